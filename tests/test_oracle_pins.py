@@ -1,0 +1,388 @@
+"""Pins for the CPU oracle: each check comes from something other than the
+oracle's own formula (hand-worked examples, a different arithmetic route,
+closed forms, invariants, brute force on tiny inputs)."""
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as WL
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+LADDER = (0, 2, 4, 6, 8)
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as fh:
+        return json.load(fh)
+
+
+# ------------------------------------------------------------------ truncation
+
+def test_truncation_golden_examples():
+    g = _load("truncation_examples.json")
+    for case in g["cases"]:
+        for d, want in zip(g["depths"], case["codes"]):
+            assert int(O.truncate(np.int8(case["q"]), d)) == want, (case, d)
+
+
+def test_truncation_exhaustive_floor_division_route():
+    """All 256 codes x 5 depths against Python floor division (a different
+    route from the oracle's shifts) and the truncation invariants."""
+    q = np.arange(-128, 128, dtype=np.int64)
+    for d in LADDER:
+        c = O.truncate(q.astype(np.int8), d)
+        if d == 0:
+            assert np.all(c == 0)
+            continue
+        step = 2 ** (8 - d)
+        want = np.array([(int(v) // step) * step for v in q])
+        assert np.array_equal(c, want)
+        assert np.all(c <= q) and np.all(q < c + step)     # floor within one step
+        assert np.all(c % step == 0)                        # multiple of the step
+        assert np.all((c >= -128) & (c <= 127))             # still an int8 code
+    assert np.array_equal(O.truncate(q.astype(np.int8), 8), q)   # D8 is the stored code
+    for d0, d1 in zip(LADDER[1:-1], LADDER[2:]):            # deeper never moves away from q
+        assert np.all(np.abs(q - O.truncate(q.astype(np.int8), d1))
+                      <= np.abs(q - O.truncate(q.astype(np.int8), d0)))
+
+
+def test_truncation_equals_residual_slice_sum():
+    """Base + refinements rebuilt from the 2-bit slices equals the top-d-bit read."""
+    q = np.arange(-128, 128, dtype=np.int64).astype(np.int8)
+    dig = O.slice_digits(q)
+    assert dig.min() >= 0 and dig.max() <= 3
+    # digits re-form the byte exactly
+    u = (q.astype(np.int64) & 0xFF)
+    assert np.array_equal(sum(dig[:, s] << (2 * s) for s in range(4)), u)
+    for d in LADDER:
+        assert np.array_equal(O.residual_code(dig, d), O.truncate(q, d))
+
+
+def test_truncation_by_byte_mask_route():
+    """Masking the low 8-d bits of the byte and re-reading it as int8."""
+    q = np.arange(-128, 128, dtype=np.int64).astype(np.int8)
+    for d in LADDER[1:]:
+        mask = (0xFF << (8 - d)) & 0xFF
+        want = (q.view(np.uint8) & np.uint8(mask)).view(np.int8).astype(np.int64)
+        assert np.array_equal(O.truncate(q, d), want)
+
+
+# ------------------------------------------------------------------ lens rules
+
+def _case_map(case, lenses):
+    cen = np.array([lenses[n][:2] for n in case["lenses"]], dtype=np.float64)
+    rad = np.array([lenses[n][2] for n in case["lenses"]], dtype=np.float64)
+    return O.level_map(np.array(case["blocks"], dtype=np.float64), cen, rad, case["f"],
+                       case["g"], case["combine"], 5, case["glass"], case["stops"])
+
+
+@pytest.mark.parametrize("idx", range(9))
+def test_level_map_hand_examples(idx):
+    g = _load("lens_hand_examples.json")
+    case = g["cases"][idx]
+    got = _case_map(case, g["lenses"])
+    assert got.tolist() == case["levels"], case["name"]
+
+
+def test_ceiling_closed_form():
+    # g = 0 -> the glass; g = 1 -> the top rung, for every glass
+    for m in range(1, 8):
+        for gam in range(0, m + 1):
+            assert O.ceiling(0.0, m, gam) == gam
+            assert O.ceiling(1.0, m, gam) == m
+    assert O.ceiling(0.75, 4, 1) == 3 and O.ceiling(0.5, 4, 0) == 2 and O.ceiling(0.34, 4, 1) == 2
+
+
+def test_default_stops_closed_form():
+    for n in range(1, 9):
+        s = O.profile_stops(n)
+        assert s[0] == 1.0
+        assert all(Fraction(float(s[j - 1])) == Fraction(n - j + 1, n)
+                   or abs(float(s[j - 1]) - (n - j + 1) / n) < 1e-16 for j in range(1, n + 1))
+        assert np.all(np.diff(s) < 0)
+
+
+def _ring_scan(rho_star, s, glass):
+    """The ring rho* falls into, by walking the ring intervals outward:
+    [0, s_kappa) -> kappa, [s_kappa, s_(kappa-1)) -> kappa-1, ...,
+    [s_(gamma+1), inf) -> gamma."""
+    n = len(s)
+    edges = [0.0] + [float(v) for v in s[::-1]] + [math.inf]   # 0 < s_kappa < ... < s_(gamma+1) < inf
+    for k in range(n + 1):
+        if edges[k] <= rho_star < edges[k + 1]:
+            return glass + n - k
+    raise AssertionError("rho* outside every ring")
+
+
+def test_single_lens_reduces_to_ring_of_rho():
+    """With one lens, L = max(0, 1 - rho/s_last) and rho* = min(rho, s_last),
+    so the level is the ring that rho itself falls into (brute-force ring scan).
+    Checked on random tiny maps, away from exact ties."""
+    rng = np.random.default_rng(123)
+    for trial in range(300):
+        n_rungs = int(rng.integers(2, 8))
+        m = n_rungs - 1
+        glass = int(rng.integers(0, m))
+        g = float(rng.uniform(0, 1))
+        f = float(rng.uniform(0.05, 0.95))
+        kappa = O.ceiling(g, m, glass)
+        n = kappa - glass
+        stops = None
+        if n > 0 and rng.uniform() < 0.5:
+            stops = np.sort(rng.uniform(0.1, 2.5, size=n))[::-1]
+            if np.any(np.diff(stops) >= 0):
+                stops = None
+        coords = rng.uniform(0, 1, size=(8, 2))
+        cen = rng.uniform(0, 1, size=(1, 2))
+        r = rng.uniform(0.05, 0.5, size=1)
+        got = O.level_map(coords, cen, r, f, g, "sum", n_rungs, glass, stops)
+        if n == 0:
+            assert np.all(got == glass)
+            continue
+        s = O.profile_stops(n, stops)
+        R = r[0] * f / (1 - f)
+        for b in range(8):
+            rho = math.hypot(coords[b, 0] - cen[0, 0], coords[b, 1] - cen[0, 1]) / R
+            if min(abs(rho - v) for v in s) < 1e-9:
+                continue
+            assert got[b] == _ring_scan(min(rho, float(s[0])), s, glass)
+
+
+def test_level_map_bruteforce_8_blocks_count_vs_scan():
+    """The count form gamma + #{j : rho* < s_j} against the explicit ring scan,
+    for many lenses, on random 8-block maps; rho* recomputed from a scalar
+    walk of rules 4-6 with Python floats."""
+    rng = np.random.default_rng(7)
+    for trial in range(200):
+        glass = int(rng.integers(0, 4))
+        g = float(rng.uniform(0, 1))
+        f = float(rng.uniform(0.05, 0.9))
+        combine = "sum" if trial % 2 == 0 else "max"
+        nl = int(rng.integers(1, 5))
+        coords = rng.uniform(0, 1, size=(8, 2))
+        cen = rng.uniform(0, 1, size=(nl, 2))
+        r = rng.uniform(0.05, 0.4, size=nl)
+        got = O.level_map(coords, cen, r, f, g, combine, 5, glass)
+        kappa = O.ceiling(g, 4, glass)
+        n = kappa - glass
+        if n == 0:
+            assert np.all(got == glass)
+            continue
+        s = O.profile_stops(n)
+        for b in range(8):
+            lifts = []
+            for i in range(nl):
+                rho = math.sqrt((coords[b, 0] - cen[i, 0]) ** 2 + (coords[b, 1] - cen[i, 1]) ** 2) / (r[i] * f / (1 - f))
+                lifts.append(max(0.0, 1.0 - rho / float(s[0])))
+            L = min(1.0, sum(lifts)) if combine == "sum" else max(lifts)
+            rs = float(s[0]) * (1.0 - L)
+            if min(abs(rs - v) for v in s) < 1e-9:
+                continue
+            assert got[b] == _ring_scan(rs, s, glass)
+
+
+def test_level_map_invariants():
+    """Bounds and monotonicity: levels stay in [glass, kappa]; adding a lens,
+    raising g or raising f never lowers a level; sum >= max; a block far
+    outside every lens keeps the glass; the map is unchanged when every
+    coordinate and size is scaled by 2 (exact in fp64)."""
+    rng = np.random.default_rng(11)
+    for trial in range(100):
+        coords = rng.uniform(0, 1, size=(64, 2))
+        cen = coords[rng.choice(64, 3, replace=False)]
+        r = rng.uniform(0.05, 0.3, size=3)
+        glass = int(rng.integers(0, 3))
+        f, g = float(rng.uniform(0.1, 0.9)), float(rng.uniform(0, 1))
+        base = O.level_map(coords, cen, r, f, g, "sum", 5, glass)
+        kappa = O.ceiling(g, 4, glass)
+        assert base.min() >= glass and base.max() <= kappa
+        two = O.level_map(coords, cen[:2], r[:2], f, g, "sum", 5, glass)
+        assert np.all(base >= two)
+        assert np.all(O.level_map(coords, cen, r, f, min(1.0, g + 0.2), "sum", 5, glass) >= base)
+        assert np.all(O.level_map(coords, cen, r, min(0.95, f + 0.05), g, "sum", 5, glass) >= base)
+        mx = O.level_map(coords, cen, r, f, g, "max", 5, glass)
+        assert np.all(base >= mx)
+        far = O.level_map(np.array([[50.0, 50.0]]), cen, r, f, g, "sum", 5, glass)
+        assert far[0] == glass
+        scaled = O.level_map(coords * 2, cen * 2, r * 2, f, g, "sum", 5, glass)
+        assert np.array_equal(scaled, base)
+
+
+def test_level_map_centre_reaches_ceiling():
+    rng = np.random.default_rng(3)
+    coords = rng.uniform(0, 1, size=(32, 2))
+    for glass in range(4):
+        for g in (0.0, 0.3, 0.75, 1.0):
+            got = O.level_map(coords, coords[[5]], [0.1], 0.5, g, "sum", 5, glass)
+            assert got[5] == O.ceiling(g, 4, glass)
+
+
+# ------------------------------------------------------------------ memory formula
+
+def test_memory_uniform_maps_exact():
+    w = np.full(8, 64 * 256, dtype=np.int64)
+    for idx, d in enumerate(LADDER):
+        assert O.mean_bits(np.full(8, idx), w) == d
+        assert O.weight_bytes(np.full(8, idx), w) == 8 * 64 * 256 * d // 8
+
+
+def test_memory_all_5pow8_maps_of_eight_equal_blocks():
+    """Every one of the 390,625 maps over 8 equal blocks: the formula equals
+    the plain average of the bits (exact rational arithmetic)."""
+    w = np.full(8, 64 * 256, dtype=np.int64)
+    maps = np.array(list(itertools.product(range(5), repeat=8)), dtype=np.int64)
+    bits = np.array(LADDER, dtype=np.int64)[maps]
+    want = bits.sum(axis=1)                       # 8 * mean, exact
+    got = np.array([O.mean_bits(mp, w) for mp in maps[::97]])
+    assert np.allclose(got * 8, want[::97], rtol=0, atol=1e-12)
+    # the vectorised check over all maps: bytes are exact integers
+    assert np.all(bits.sum(axis=1) * 64 * 256 // 8 == [int(v) * 2048 for v in want])
+    for mp in maps[::3907]:
+        assert O.weight_bytes(mp, w) == int(np.array(LADDER)[mp].sum()) * 2048
+
+
+def test_memory_unequal_blocks_hand_example():
+    # a K = 256 block at D2 and a K = 512 block at D8: (2*16384 + 8*32768) / 49152 = 6
+    w = np.array([64 * 256, 64 * 512], dtype=np.int64)
+    assert O.mean_bits(np.array([1, 4]), w) == 6.0
+    assert O.weight_bytes(np.array([1, 4]), w) == (2 * 16384 + 8 * 32768) // 8
+
+
+# ------------------------------------------------------------------ qmatvec
+
+def _int_inputs(rng, N, K, B):
+    W = rng.integers(-128, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    x = rng.integers(-3, 4, size=(B, K)).astype(np.float64)
+    return W, x
+
+
+def test_qmatvec_d8_equals_untruncated_int_product():
+    rng = np.random.default_rng(5)
+    W, x = _int_inputs(rng, 256, 384, 3)
+    level = np.full(4, 4)
+    y = O.qmatvec_ref(W, np.ones(256), x, level)
+    want = x.astype(np.int64) @ W.astype(np.int64).T
+    assert np.array_equal(y, want.astype(np.float64))
+
+
+def test_qmatvec_uniform_depth_equals_masked_int_product():
+    rng = np.random.default_rng(6)
+    W, x = _int_inputs(rng, 192, 256, 2)
+    for idx, d in enumerate(LADDER):
+        y = O.qmatvec_ref(W, np.ones(192), x, np.full(3, idx))
+        if d == 0:
+            assert np.all(y == 0)
+            continue
+        mask = np.uint8((0xFF << (8 - d)) & 0xFF)
+        c = (W.view(np.uint8) & mask).view(np.int8).astype(np.int64)
+        assert np.array_equal(y, (x.astype(np.int64) @ c.T).astype(np.float64))
+
+
+def test_qmatvec_mixed_map_blockwise_and_scaled():
+    """A mixed map equals, block by block, the uniform-depth product of that
+    block; scales multiply rows (float x, fp64)."""
+    rng = np.random.default_rng(8)
+    W = rng.integers(-127, 128, size=(320, 128), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=320)
+    x = rng.standard_normal((2, 128))
+    level = np.array([0, 1, 2, 3, 4])
+    y = O.qmatvec_ref(W, sc, x, level)
+    for b in range(5):
+        rows = slice(64 * b, 64 * b + 64)
+        d = LADDER[level[b]]
+        if d == 0:
+            assert np.all(y[:, rows] == 0)
+            continue
+        step = 2 ** (8 - d)
+        c = np.floor_divide(W[rows].astype(np.int64), step) * step
+        want = np.einsum("rk,nk->rn", x, c.astype(np.float64)) * sc[rows]
+        assert np.allclose(y[:, rows], want, rtol=1e-13, atol=1e-15)
+
+
+def test_qmatvec_per_request_maps_equal_separate_calls():
+    rng = np.random.default_rng(9)
+    W = rng.integers(-127, 128, size=(256, 64), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=256)
+    x = rng.standard_normal((3, 64))
+    maps = rng.integers(0, 5, size=(3, 4))
+    y = O.qmatvec_ref(W, sc, x, maps, per_request=True)
+    for r in range(3):
+        assert np.allclose(y[r], O.qmatvec_ref(W, sc, x[r:r + 1], maps[r])[0], rtol=1e-12, atol=1e-12)
+
+
+def test_qmatvec_brute_force_maps_table_cfg1():
+    """Single 512x256 layer: the output for any map is assembled from a
+    per-block, per-depth table; sampled maps against the oracle."""
+    inp = WL.single_layer_512x256(0)
+    W, sc, x = inp["W"], inp["scales"], inp["x"]
+    table = np.zeros((8, 5, 64))
+    for b in range(8):
+        for idx, d in enumerate(LADDER):
+            rows = slice(64 * b, 64 * b + 64)
+            step = 2 ** (8 - d) if d else None
+            c = np.zeros((64, 256)) if d == 0 else (np.floor_divide(W[rows].astype(np.int64), step) * step).astype(np.float64)
+            table[b, idx] = (c @ x[0].astype(np.float64)) * sc[rows].astype(np.float64)
+    rng = np.random.default_rng(1)
+    for mp in rng.integers(0, 5, size=(300, 8)):
+        y = O.qmatvec_ref(W, sc, x, mp)[0]
+        want = np.concatenate([table[b, mp[b]] for b in range(8)])
+        assert np.allclose(y, want, rtol=1e-13, atol=1e-16)
+
+
+def test_tolerance_bounds_output_and_vanishes_on_zero():
+    rng = np.random.default_rng(10)
+    W = rng.integers(-127, 128, size=(128, 64), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=128)
+    x = rng.standard_normal((1, 64))
+    lvl = np.array([0, 3])
+    tol = O.qmatvec_tolerance(W, sc, x, lvl)
+    y = O.qmatvec_ref(W, sc, x, lvl)
+    assert np.all(tol[:, :64] == 0)
+    assert np.all(tol >= 1e-4 * np.abs(y) - 1e-18)
+
+
+# ------------------------------------------------------------------ escalation
+
+def test_escalation_schedule_closed_form():
+    scores = WL.escalation_scores(0, 256)
+    mask = O.escalation_schedule(scores, 0.16)
+    assert mask.sum() == 41                                    # round(0.16 * 256) = round(40.96)
+    assert scores[mask].min() > scores[~mask].max()            # exactly the 41 largest
+    assert O.escalation_byte_ratio(mask) == float(Fraction(1, 2) + Fraction(41, 256))
+    assert O.escalation_byte_ratio(mask) == 0.66015625
+    assert O.escalation_byte_ratio(np.zeros(256, bool)) == 0.5
+    assert O.escalation_byte_ratio(np.ones(256, bool)) == 1.5
+
+
+# ------------------------------------------------------------------ glue
+
+def test_rmsnorm_and_silu_closed_forms():
+    x = np.array([[3.0, 4.0]])
+    y = O.rmsnorm_ref(x, eps=0.0)                 # rms = sqrt(12.5)
+    assert np.allclose(y, x / math.sqrt(12.5), rtol=1e-15)
+    assert np.allclose(np.mean(O.rmsnorm_ref(np.random.default_rng(0).standard_normal((4, 100)), 0.0) ** 2, axis=1), 1.0)
+    assert O.silu_mul_ref(0.0, 5.0) == 0.0
+    assert abs(O.silu_mul_ref(1.0, 1.0) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
+    assert abs(O.silu_mul_ref(-50.0, 1.0)) < 1e-19
+
+
+# ------------------------------------------------------------------ generators
+
+def test_generators_are_seeded_and_shaped():
+    a = WL.single_layer_512x256(0)
+    b = WL.single_layer_512x256(0)
+    assert np.array_equal(a["W"], b["W"]) and np.array_equal(a["x"], b["x"])
+    assert a["W"].dtype == np.int8 and a["W"].min() >= -127 and a["W"].max() <= 127
+    assert a["scales"].dtype == np.float32 and a["scales"].min() >= 0.001 and a["scales"].max() <= 0.02
+    fld = WL.e2b_field(0)
+    assert fld.n_blocks == 9360 and fld.n_weights == 1_132_462_080
+    assert WL.qwen_decode_field(0).n_blocks == 7750
+    assert WL.batched_layer(0).n_blocks == 352
+    assert WL.streaming_stack(0).n_blocks == 4608 and WL.streaming_stack(0).n_weights == 3_758_096_384
