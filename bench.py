@@ -1,0 +1,286 @@
+#!/usr/bin/env python
+"""Benchmark of the mixed-depth weight-read hot path on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input:
+build the per-block level map from the lens rules, then read every matrix of
+the workload at its blocks' depths (one grouped qmatvec launch for a weight
+field).  Packing is offline and untimed.  Inputs are resident in HBM before
+the timed region starts.
+
+Default workload: the Gemma-E2B-scale weight field (30 synthetic decoder
+layers, q/k/v/o 1536x1536, gate/up 6144x1536, down 1536x6144; 9,360 blocks of
+64 rows; clustered block coordinates; 5 lenses, g = 0.75, glass D2, sum;
+focus_area calibrated by the oracle to a mean of 4.0 bits/weight), batch 1.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+CALIBRATION = os.path.join(ROOT, "tests", "golden", "calibration.json")
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "query_adaptive_mixed_amd", "csrc", "qmatvec.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    try:
+        with open(COUNTERS) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = d.get(key)
+    if not ent or ent.get("kernel_sha") != kernel_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------- workloads
+
+def build_field(fld, lens, B, torch, Q, dev):
+    """Pack every matrix of a field; returns (items, algorithmic byte counts)."""
+    coords = torch.from_numpy(fld.coords).to(dev)
+    lv = Q.build_level_map(coords, lens.centres, lens.radii, lens.f, lens.g, lens.combine, lens.glass)
+    torch.cuda.synchronize()
+    lv_h = lv.cpu().numpy()
+    items, keep = [], []
+    wbytes = other = 0
+    offs = fld.block_offsets()
+    t0 = time.time()
+    for i, m in enumerate(fld.matrices):
+        W = torch.from_numpy(fld.codes(i)).to(dev)
+        sc = torch.from_numpy(fld.scales(i)).to(dev)
+        pm = Q.pack_slices(W, sc)
+        del W
+        x = torch.from_numpy(fld.x(i, B)).to(dev)
+        y = torch.empty((B, m.N), dtype=torch.float32, device=dev)
+        sub = lv[offs[i]:offs[i] + m.n_blocks]
+        items.append((pm, x, y, sub))
+        mb, wb = Q.map_weight_bytes(lv_h[offs[i]:offs[i] + m.n_blocks], m.K)
+        wbytes += wb
+        nz = int(np.count_nonzero(lv_h[offs[i]:offs[i] + m.n_blocks]))
+        other += nz * 64 * 4 + B * m.K * 4 + B * m.N * 4 + m.n_blocks
+        if i % 30 == 0:
+            log(f"  packed {i + 1}/{len(fld.matrices)} matrices ({time.time() - t0:.1f} s)")
+    torch.cuda.synchronize()
+    return coords, lv, lv_h, items, wbytes, other
+
+
+def run_field(args, torch, Q, WL):
+    dev = torch.device("cuda:0")
+    cal = json.load(open(CALIBRATION))
+    if args.workload == "e2b_field":
+        fld = WL.e2b_field(0)
+        c = cal["e2b_field"]
+        f = c["target_4.0"]["f"] if args.mean_bits == 4.0 else 0.5
+        lens = WL.e2b_lenses(fld, f=f, g=c["g"])
+        desc = "e2b_field: 30 layers x {q,k,v,o 1536x1536; gate,up 6144x1536; down 1536x6144} int8, 9360 blocks"
+    else:
+        fld = WL.streaming_stack(0)
+        c = cal["streaming_stack"][f"glass{args.glass}_target{float(args.mean_bits)}"]
+        cen, rad = WL.stack_lenses(fld)
+        lens = WL.LensParams(centres=cen, radii=rad, f=c["f"], g=1.0, combine="sum", glass=args.glass)
+        desc = "streaming_stack: 8 x {8192x28672, 28672x8192} int8, 4608 blocks"
+    log(f"workload {desc}; f={lens.f:.6f} g={lens.g} glass={lens.glass}")
+    coords, lv, lv_h, items, wbytes, other = build_field(fld, lens, args.batch, torch, Q, dev)
+    w = fld.block_weights()
+    mean_bits = float(np.sum(w * np.array(Q.LADDER_BITS)[lv_h]) / np.sum(w))
+    group = Q.GroupedQmatvec(items, device=dev)
+
+    def step():
+        Q.build_level_map(coords, lens.centres, lens.radii, lens.f, lens.g, lens.combine, lens.glass, out=lv)
+        group.run()
+
+    ev = []
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        a, b, e = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record()
+        Q.build_level_map(coords, lens.centres, lens.radii, lens.f, lens.g, lens.combine, lens.glass, out=lv)
+        b.record()
+        group.run()
+        e.record()
+        ev.append((a, b, e))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = float(np.mean([b.elapsed_time(e) for a, b, e in ev]))
+    map_ms = float(np.mean([a.elapsed_time(b) for a, b, e in ev]))
+    assert np.array_equal(lv.cpu().numpy(), lv_h), "level map changed between steps"
+    ms = wall * 1e3 / args.steps
+    return dict(desc=desc, mean_bits=mean_bits, wbytes=wbytes, other=other, ms=ms, kern_ms=kern_ms, map_ms=map_ms,
+                variant=Q.last_variant(), lens=lens, fld=fld, lv_h=lv_h, n_items=len(items),
+                key=f"{args.workload}_{args.mean_bits}_g{lens.glass}_b{args.batch}")
+
+
+# ----------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(res, args):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    fld, lens, lv_h = res["fld"], res["lens"], res["lv_h"]
+    offs = fld.block_offsets()
+    budget = args.cpu_seconds
+
+    def one_pass(limit):
+        """Map over every block, then products matrix by matrix until `limit` s."""
+        t0 = time.perf_counter()
+        O.level_map(fld.coords, lens.centres, lens.radii, lens.f, lens.g, lens.combine, 5, lens.glass)
+        t_map = time.perf_counter() - t0
+        done_bytes, t_prod, n = 0, 0.0, 0
+        for i, m in enumerate(fld.matrices):
+            W, sc, x = fld.codes(i), fld.scales(i), fld.x(i, args.batch)
+            sub = lv_h[offs[i]:offs[i] + m.n_blocks]
+            t0 = time.perf_counter()
+            O.qmatvec_ref(W, sc, x, sub)
+            t_prod += time.perf_counter() - t0
+            done_bytes += int(np.sum(64 * m.K * np.array((0, 2, 4, 6, 8))[sub]) // 8)
+            n += 1
+            if t_prod > limit:
+                break
+        return t_map, t_prod, done_bytes, n
+
+    t_map, t_prod, done_bytes, n = one_pass(budget)
+    if n == len(fld.matrices) and 4 * (t_map + t_prod) < budget:
+        # the whole pass fits: warm-up done, take the median of three full passes
+        runs = sorted((one_pass(float("inf")) for _ in range(3)), key=lambda r: r[0] + r[1])
+        t_map, t_prod, done_bytes, n = runs[1]
+        how = "median of 3 whole passes after one warm-up pass"
+    else:
+        how = "one bounded pass, scaled to the whole workload"
+    frac = done_bytes / res["wbytes"]
+    t_pass = t_map + t_prod / frac
+    gbs = res["wbytes"] / t_pass / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"level map over all {len(lv_h)} blocks + fp64 product of {n} of {len(fld.matrices)} "
+                      f"matrices ({100 * frac:.1f}% of the weight bytes; {t_map + t_prod:.2f} s per pass); {how}"}
+
+
+def copy_probe(args, torch):
+    """A plain 1 GiB device-to-device copy: the known-size reference against which
+    the FETCH_SIZE / WRITE_SIZE counters are scaled to bytes."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    print(json.dumps({"metric": "copy GB/s (read + write)", "value": round(2 * n / ms / 1e6, 2), "unit": "GB/s",
+                      "bytes_read_per_copy": n, "bytes_written_per_copy": n, "ms_per_copy": round(ms, 4)}))
+
+
+# ----------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="e2b_field", choices=["e2b_field", "streaming_stack", "copy_probe"])
+    ap.add_argument("--mean-bits", type=float, default=4.0)
+    ap.add_argument("--glass", type=int, default=1)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("this build measures one GPU only: the product is split by output-row blocks and needs no "
+               "collective within a pass, but no multi-GPU path is built; run with --gpus 1")
+        print(msg, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import query_adaptive_mixed_amd as Q
+    import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    log(f"device: {torch.cuda.get_device_name(0)}")
+    if args.workload == "copy_probe":
+        return copy_probe(args, torch)
+    res = run_field(args, torch, Q, WL)
+    gbs = res["wbytes"] / (res["ms"] * 1e-3) / 1e9
+    kern_bytes = res["wbytes"] + res["other"]
+    achieved = kern_bytes / (res["kern_ms"] * 1e-3) / 1e9
+    out = {
+        "metric": "achieved HBM GB/s (% of peak) and decode tokens/s at mean bits/weight",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 codes x fp32 activations (exact int8 dot4 on 4-limb fixed point), fp32 out",
+        "data": "synthetic (seeded codes, scales, activations, block coordinates and lenses)",
+        "config": {
+            "workload": args.workload,
+            "description": res["desc"],
+            "batch": args.batch,
+            "mean_bits": round(res["mean_bits"], 6),
+            "weight_bytes_per_step": int(res["wbytes"]),
+            "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+            "focus_area_f": res["lens"].f, "focus_strength_g": res["lens"].g, "glass_rung": res["lens"].glass,
+            "matrices_per_launch": res["n_items"],
+            "level_map_ms": round(res["map_ms"], 5),
+            "kernel": res["variant"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(res["key"]),
+            "kernel_ms": round(res["kern_ms"], 5),
+            "algorithmic_bytes_per_launch": int(kern_bytes),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(res, args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

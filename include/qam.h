@@ -1,0 +1,293 @@
+/*
+ * qam.h -- C ABI of libqam: mixed-depth reads of one stored int8 weight copy
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * One stored copy of int8 weights is kept as four residual 2-bit slices.
+ * Each block of 64 output rows is read at its own depth from the ladder
+ * ZERO < D2 < D4 < D6 < D8; a block read at d bits touches d/2 slices and a
+ * ZERO block touches nothing.  The depth of every block comes from a level
+ * map (one byte per block) built by the lens rules or set uniformly (the
+ * top-4-bit pass and its 8-bit re-run).
+ *
+ * Sources (cited by page title and section):
+ *   [FoQLens]  "FoQLens" (foqlens.sawking.tech), table "Progress" and section
+ *              "FoQZones, the mechanism".
+ *   [Lens]     "FoQLens" landing page (vovanda.github.io/FoQLens), section
+ *              "The mechanism" and the field description.
+ *   [PoD]      "Precision on Demand: Escalating Weight Bits at Uncertain
+ *              Decoding Steps in a Small Local Model" (arXiv:2611.14418 v1),
+ *              abstract.
+ *
+ * Conventions shared by every call:
+ *   - Pointers marked (device) are HIP device pointers owned by the caller;
+ *     pointers marked (host) are host memory owned by the caller and only
+ *     read during the call.  The library never allocates or frees device
+ *     memory.
+ *   - Work is enqueued on the caller's stream `s` (0 = the null stream) and
+ *     is asynchronous: outputs are ready once the stream has reached that
+ *     point.  A kernel fault surfaces at the caller's next synchronisation.
+ *   - Every argument check runs on the host before anything is enqueued.  On
+ *     failure a negative QAM_ERR_* code is returned, nothing is enqueued and
+ *     qam_last_error() describes the problem.  Nothing aborts or throws across
+ *     the ABI, and no call falls back silently to another kernel variant:
+ *     qam_last_variant() names the variant the last successful call ran.
+ *   - Calls are reentrant; the only library state is the thread-local error
+ *     and variant strings.
+ */
+#ifndef QAM_H
+#define QAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- errors */
+#define QAM_OK             0
+#define QAM_ERR_NULL      -1   /* a required pointer is NULL                      */
+#define QAM_ERR_SHAPE     -2   /* N or K not a multiple of 64, or out of range    */
+#define QAM_ERR_ARG       -3   /* a scalar argument is out of range              */
+#define QAM_ERR_LADDER    -4   /* ladder not accepted by this call                */
+#define QAM_ERR_ALIGN     -5   /* a pointer is not aligned as required            */
+#define QAM_ERR_HIP       -6   /* a HIP runtime call failed                       */
+#define QAM_ERR_WORKSPACE -7   /* workspace missing or too small                  */
+
+#define QAM_ROWS_PER_BLOCK 64
+#define QAM_MAX_K          65536      /* keeps every exact integer sum in range */
+#define QAM_MAX_LENSES     64
+#define QAM_MAX_RUNGS      16
+#define QAM_MAX_BATCH      8          /* requests per qmatvec call with a shared map */
+#define QAM_MAX_BLOCKS     65536      /* blocks per matrix (N <= 4,194,304)         */
+#define QAM_WS_COUNTER_BYTES (QAM_MAX_BLOCKS * 4)  /* workspace counter region      */
+
+#define QAM_X_F32  0
+#define QAM_X_BF16 1
+
+/* ---------------------------------------------------------------- packed weights */
+/*
+ * Slice-major layout of one packed matrix W [N][K] (int8, row-major input):
+ *
+ *   bytes [0, N*K)            four planes of N*K/4 bytes each.  Plane p holds the
+ *                             2-bit digit s = 3 - p of every code (p = 0 is the
+ *                             top digit and carries the sign), so reading depth d
+ *                             touches planes 0 .. d/2-1 only.
+ *   bytes [N*K, N*K + 4N)     the per-row fp32 scales (copied at pack time).
+ *
+ * Inside a plane: block b (rows 64b .. 64b+63) owns 16*K contiguous bytes;
+ * inside a block, tile t (columns 64t .. 64t+63) owns 1024 bytes; inside a
+ * tile, lane L (0..63) owns 16 bytes = four 32-bit words j = 0..3.  Word j
+ * holds the digits of row 16j + (L & 15), columns 16(L >> 4) + 4u + i
+ * (u, i = 0..3), the digit for (u, i) at bit (8i + 2s - 2u) mod 32.  A group
+ * of four digits therefore rotates into a byte-aligned int8x4 word with one
+ * mask per slice and one rotation.
+ */
+typedef struct qam_packed {
+    int64_t N;          /* output rows, multiple of 64            */
+    int64_t K;          /* input columns, multiple of 64, <= QAM_MAX_K */
+    int64_t n_blocks;   /* N / 64                                 */
+    void*   planes;     /* (device) qam_packed_bytes(N, K) bytes, 256-B aligned */
+    float*  scales;     /* (device) = (float*)((char*)planes + N*K)  */
+} qam_packed;
+
+/* Bytes of one packed matrix: N*K slice bytes + 4*N scale bytes. */
+size_t qam_packed_bytes(int64_t N, int64_t K);
+
+/*
+ * qam_pack_slices -- split int8 codes into the four residual 2-bit slices.
+ *   [FoQLens] "Progress": one stored stack, a base with refinements over it,
+ *   any depth read from the same copy without repacking; [Lens] "The
+ *   mechanism": one stored copy of residual slices read at 2, 4, 6 or 8 bits.
+ *
+ *   W        (device) int8 [N][K], row-major, any values (-128 allowed).
+ *   scales   (device) fp32 [N] per-row scales.
+ *   N, K     multiples of 64; K <= QAM_MAX_K.
+ *   out      (device) qam_packed_bytes(N, K) bytes, 256-byte aligned; must
+ *            not overlap W or scales.
+ *   desc_out (host)   filled with N, K, n_blocks, planes = out, scales.
+ * Packing happens once per matrix (offline); W and scales may be freed once
+ * the stream has passed this call.
+ */
+int qam_pack_slices(const int8_t* W, const float* scales, int64_t N, int64_t K,
+                    void* out, size_t out_bytes, qam_packed* desc_out, hipStream_t s);
+
+/*
+ * qam_describe_packed -- fill a descriptor for an already packed buffer.
+ */
+int qam_describe_packed(void* packed_buf, int64_t N, int64_t K, qam_packed* desc_out);
+
+/*
+ * qam_unpack_codes -- debug probe: the int8 codes the product kernels read.
+ *   Writes codes_out[n][k] = the code of W[n][k] truncated to the depth of
+ *   block n/64 in `level_map`, rebuilt from the slices by the same device
+ *   routine the product kernels use.  ZERO blocks give 0.
+ *   packed    (host)   descriptor from qam_pack_slices.
+ *   level_map (device) uint8 [n_blocks], rung indices 0..4 of {0,2,4,6,8}.
+ *   codes_out (device) int8 [N][K].
+ */
+int qam_unpack_codes(const qam_packed* packed, const uint8_t* level_map, int8_t* codes_out,
+                     hipStream_t s);
+
+/* ---------------------------------------------------------------- level maps */
+typedef struct qam_lens {
+    double cx, cy;      /* centre on the 2-D block field */
+    double r;           /* size r_i >= 0 (the radius is R_i = r_i f / (1 - f)) */
+} qam_lens;
+
+#define QAM_COMBINE_SUM 0
+#define QAM_COMBINE_MAX 1
+#define QAM_MAX_STOPS   (QAM_MAX_RUNGS - 1)
+
+typedef struct qam_lens_params {
+    double f;           /* focus_area, in [0, 1]                        */
+    double g;           /* focus_strength, in [0, 1]                    */
+    int    combine;     /* QAM_COMBINE_SUM or QAM_COMBINE_MAX           */
+    int    n_stops;     /* 0: default stops; else must equal kappa - glass */
+    double stops[QAM_MAX_STOPS]; /* s_(glass+1) > s_(glass+2) > ... > s_kappa > 0, in radii */
+} qam_lens_params;
+
+/*
+ * qam_build_level_map -- per-block rung index from the lens rules.
+ *   [Lens] "The mechanism" rules 1-6 and [FoQLens] "FoQZones, the mechanism":
+ *     R_i = r_i f / (1 - f); kappa = glass + floor(g (m - glass));
+ *     rho_i(b) = d(b, c_i) / R_i; L_i(b) = max(0, 1 - rho_i(b) / s_last);
+ *     L(b) = min(1, sum_i L_i) or max_i L_i; rho* = s_last (1 - L(b));
+ *     level = the ring rho* falls into, the glass outside every lens.
+ *   Readings: d is Euclidean on the block coordinates; s_last = s_(glass+1);
+ *   default stops s_(glass+j) = (n - j + 1) / n with n = kappa - glass; rings
+ *   are half-open (level = glass + #{j : rho* < s_(glass+j)}); f = 1 gives
+ *   R = +inf; R = 0 lifts only a block at distance 0.
+ *   One thread per block, fp64 throughout, no contraction into FMA, correctly
+ *   rounded sqrt and division: the map is bit-identical to the same rules run
+ *   in IEEE fp64 on a CPU.
+ *
+ *   coords      (device) fp64 [n_blocks][2], finite.
+ *   n_blocks    >= 0 (0 enqueues nothing).
+ *   lenses      (host) [n_lenses], n_lenses in [0, QAM_MAX_LENSES]; r >= 0.
+ *   params      (host) f, g in [0, 1]; explicit stops strictly decreasing, > 0.
+ *   ladder_bits (host) [n_rungs], ladder_bits[0] == 0, strictly increasing,
+ *               2 <= n_rungs <= QAM_MAX_RUNGS.  Only the rung count enters
+ *               the rules; the bits matter to the memory formula.
+ *   glass       rung index gamma in [0, n_rungs - 1].
+ *   level_out   (device) uint8 [n_blocks].
+ * A uniform map (every block at one rung, e.g. the all-D4 pass and its D8
+ * re-run of [PoD]) is this call with n_lenses = 0 and glass = that rung.
+ */
+int qam_build_level_map(const double* coords, int64_t n_blocks,
+                        const qam_lens* lenses, int n_lenses, const qam_lens_params* params,
+                        const uint8_t* ladder_bits, int n_rungs, int glass,
+                        uint8_t* level_out, hipStream_t s);
+
+/*
+ * qam_map_weight_bytes -- rule 7 and the bytes-read cost for a map (host).
+ *   [Lens] rule 7: bits = sum_b w_b bits(b) / sum_b w_b; [PoD]: cost counted
+ *   in weight bytes read.  w_b = 64 * K for every block of one matrix.
+ *   level (host) uint8 [n_blocks]; ladder_bits (host) [n_rungs].
+ *   Outputs (host, may be NULL): mean bits, weight bytes sum_b w_b bits(b)/8.
+ */
+int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
+                         const uint8_t* ladder_bits, int n_rungs,
+                         double* mean_bits, int64_t* weight_bytes);
+
+/* ---------------------------------------------------------------- qmatvec */
+/*
+ * qam_qmatvec -- y[r][n] = scale[n] * sum_k c[n][k] x[r][k] with c the code
+ *   of W[n][k] read at the depth of block n/64 ([FoQLens] "Progress": every
+ *   block of rows read at its own depth straight from the stored bytes inside
+ *   the pass; [PoD]: cost counted in weight bytes read).  A ZERO block loads
+ *   nothing and writes y = 0.
+ *
+ *   Arithmetic: each chunk of columns of x is put on an exact fixed-point
+ *   grid, x~ = round(x * 2^(30-e)) * 2^(e-30) with 2^(e-1) <= max|x| < 2^e
+ *   over the chunk, held as four signed int8 limbs; c . x~ is accumulated
+ *   exactly in integers (int8 dot products), chunks are summed in fp64 in a
+ *   fixed order, and y = fl32(scale * sum).  Hence
+ *     |y - y_exact| <= 2^-30 sum_chunks max_chunk|x| sum_chunk|w| + 2^-24|y|,
+ *   and results are bit-reproducible run to run.  Integer-valued x with
+ *   scale 1 gives exact integer outputs; a D8 map gives the untruncated
+ *   int8 product.  x must be finite.
+ *
+ *   x          (device) [B][K] row-major, fp32 (x_dtype QAM_X_F32) or bf16
+ *              (QAM_X_BF16); 16-byte aligned.
+ *   B          1 .. QAM_MAX_BATCH requests.
+ *   packed     (host) descriptor from qam_pack_slices.
+ *   level_map  (device) uint8 rung indices of the ladder {0,2,4,6,8}
+ *              (rung index = slices read): [n_blocks], shared by all requests.
+ *   per_request_maps  must be 0 for this entry point.
+ *   y          (device) fp32 [B][N], must not overlap x.
+ *   workspace  (device) qam_qmatvec_workspace_bytes(N, K, B) bytes (0 when
+ *              the plan needs no split of K; NULL is then accepted), 256-byte
+ *              aligned.  Its first QAM_WS_COUNTER_BYTES hold per-block arrival
+ *              counters: they must be zero before the first use, and every
+ *              call leaves them zero again, whatever the shape, so one buffer
+ *              serves calls of any shape.  The rest holds fp64 partial sums
+ *              that each call writes before it reads.  Calls that share a
+ *              workspace must be ordered (same stream or synchronised).
+ *   N          at most QAM_MAX_BLOCKS blocks of 64 rows.
+ */
+size_t qam_qmatvec_workspace_bytes(int64_t N, int64_t K, int64_t B);
+
+int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_packed* packed,
+                const uint8_t* level_map, int per_request_maps, float* y,
+                void* workspace, size_t workspace_bytes, hipStream_t s);
+
+/* ---------------------------------------------------------------- grouped qmatvec */
+/*
+ * A group runs qam_qmatvec over many matrices, each with its own x, y and
+ * level map, in ONE launch ([FoQLens] "Progress": the whole pass reads every
+ * block at its own depth).  Typical use: every matrix of a weight field, or
+ * the matrices of one layer that take different inputs.  The pointers are
+ * bound once by qam_group_init; qam_qmatvec_group then replays the product
+ * on whatever the bound buffers hold (e.g. once per decode step).
+ */
+typedef struct qam_gemv_item {
+    qam_packed     w;          /* descriptor from qam_pack_slices                    */
+    const void*    x;          /* (device) [B][w.K], fp32 or bf16, 16-byte aligned   */
+    float*         y;          /* (device) [B][w.N]                                  */
+    const uint8_t* level_map;  /* (device) [w.n_blocks], rungs of {0,2,4,6,8}, shared by the B requests */
+} qam_gemv_item;
+
+typedef struct qam_group {     /* filled by qam_group_init; treat as opaque          */
+    int     n_items;
+    int64_t B;
+    int     x_dtype;
+    int64_t n_workgroups;
+    size_t  lds_bytes;
+    void*   table;             /* (device) descriptor table inside dev_mem           */
+    void*   wg_map;            /* (device) workgroup -> item map inside dev_mem      */
+} qam_group;
+
+/* Device bytes qam_group_init needs (0 if the items are invalid). */
+size_t qam_group_bytes(const qam_gemv_item* items, int n_items, int64_t B);
+
+/*
+ * qam_group_init -- validate the items (as qam_qmatvec does for each), lay
+ *   out and upload the descriptor table, and zero the counter region.
+ *   items    (host) [n_items]; sum of blocks <= QAM_MAX_BLOCKS.
+ *   dev_mem  (device) qam_group_bytes(...) bytes, 256-byte aligned, owned by
+ *            the caller and kept alive as long as the group is used; it holds
+ *            the counters, fp64 partials, the table and the workgroup map.
+ *   Synchronises `s` before returning (one-time set-up, not for graph capture).
+ */
+int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dtype,
+                   void* dev_mem, size_t dev_bytes, qam_group* group_out, hipStream_t s);
+
+/*
+ * qam_qmatvec_group -- one launch computing y_i = the mixed-depth product of
+ *   every item i, with exactly the arithmetic of qam_qmatvec.  Enqueues one
+ *   kernel and nothing else (safe to capture in a HIP graph).  Calls on one
+ *   group must be ordered.
+ */
+int qam_qmatvec_group(const qam_group* group, hipStream_t s);
+
+/* ---------------------------------------------------------------- diagnostics */
+const char* qam_last_error(void);     /* thread-local, "" if none           */
+const char* qam_last_variant(void);   /* kernel variant of the last call     */
+const char* qam_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QAM_H */

@@ -1,0 +1,24 @@
+"""query_adaptive_mixed_amd -- mixed-depth reads of one stored int8 weight
+copy on MI355X.
+
+The compute lives in ``libqam.so`` (HIP kernels for gfx950 behind a C ABI,
+declared in ``include/qam.h``); this package is the thin Python binding.
+Importing it does not load the library; the first call does, and fails
+loudly if the library is missing.
+"""
+
+from .api import (  # noqa: F401
+    LADDER_BITS,
+    GroupedQmatvec,
+    PackedMatrix,
+    Workspace,
+    build_level_map,
+    last_variant,
+    map_weight_bytes,
+    pack_slices,
+    packed_bytes,
+    qmatvec,
+    unpack_codes,
+    workspace_bytes,
+)
+from ._lib import QamError  # noqa: F401

@@ -1,0 +1,105 @@
+"""ctypes declarations for libqam.so (the C ABI in include/qam.h).
+
+Loading fails loudly: if the library has not been built, or cannot be
+loaded, an ImportError names the problem.  There is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqam.so")
+
+QAM_OK = 0
+ERRORS = {-1: "QAM_ERR_NULL", -2: "QAM_ERR_SHAPE", -3: "QAM_ERR_ARG", -4: "QAM_ERR_LADDER",
+          -5: "QAM_ERR_ALIGN", -6: "QAM_ERR_HIP", -7: "QAM_ERR_WORKSPACE"}
+QAM_MAX_LENSES = 64
+QAM_MAX_STOPS = 15
+QAM_MAX_BATCH = 8
+QAM_MAX_K = 65536
+QAM_X_F32, QAM_X_BF16 = 0, 1
+QAM_COMBINE_SUM, QAM_COMBINE_MAX = 0, 1
+
+
+class QamPacked(C.Structure):
+    _fields_ = [("N", C.c_int64), ("K", C.c_int64), ("n_blocks", C.c_int64),
+                ("planes", C.c_void_p), ("scales", C.c_void_p)]
+
+
+class QamLens(C.Structure):
+    _fields_ = [("cx", C.c_double), ("cy", C.c_double), ("r", C.c_double)]
+
+
+class QamLensParams(C.Structure):
+    _fields_ = [("f", C.c_double), ("g", C.c_double), ("combine", C.c_int), ("n_stops", C.c_int),
+                ("stops", C.c_double * QAM_MAX_STOPS)]
+
+
+class QamGemvItem(C.Structure):
+    _fields_ = [("w", QamPacked), ("x", C.c_void_p), ("y", C.c_void_p), ("level_map", C.c_void_p)]
+
+
+class QamGroup(C.Structure):
+    _fields_ = [("n_items", C.c_int), ("B", C.c_int64), ("x_dtype", C.c_int), ("n_workgroups", C.c_int64),
+                ("lds_bytes", C.c_size_t), ("table", C.c_void_p), ("wg_map", C.c_void_p)]
+
+
+class QamError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+# (name, restype, argtypes) for every exported function declared in qam.h
+_P, _I64, _I, _SZ, _D = C.c_void_p, C.c_int64, C.c_int, C.c_size_t, C.c_double
+SIGNATURES = [
+    ("qam_packed_bytes", C.c_size_t, [_I64, _I64]),
+    ("qam_pack_slices", _I, [_P, _P, _I64, _I64, _P, _SZ, C.POINTER(QamPacked), _P]),
+    ("qam_describe_packed", _I, [_P, _I64, _I64, C.POINTER(QamPacked)]),
+    ("qam_unpack_codes", _I, [C.POINTER(QamPacked), _P, _P, _P]),
+    ("qam_build_level_map", _I, [_P, _I64, C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I, _I, _P, _P]),
+    ("qam_map_weight_bytes", _I, [_P, _I64, _I64, _P, _I, C.POINTER(_D), C.POINTER(_I64)]),
+    ("qam_qmatvec_workspace_bytes", C.c_size_t, [_I64, _I64, _I64]),
+    ("qam_qmatvec", _I, [_P, _I, _I64, C.POINTER(QamPacked), _P, _I, _P, _P, _SZ, _P]),
+    ("qam_group_bytes", C.c_size_t, [C.POINTER(QamGemvItem), _I, _I64]),
+    ("qam_group_init", _I, [C.POINTER(QamGemvItem), _I, _I64, _I, _P, _SZ, C.POINTER(QamGroup), _P]),
+    ("qam_qmatvec_group", _I, [C.POINTER(QamGroup), _P]),
+    ("qam_last_error", C.c_char_p, []),
+    ("qam_last_variant", C.c_char_p, []),
+    ("qam_version", C.c_char_p, []),
+]
+# tuning hooks that are not part of the product ABI contract
+EXTRA_SIGNATURES = [
+    ("qam_set_target_waves", _I, [_I]),
+]
+
+
+def load(path: str = LIB_PATH) -> C.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"libqam.so not built at {path}: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    try:
+        lib = C.CDLL(path)
+    except OSError as exc:
+        raise ImportError(f"cannot load {path}: {exc}") from exc
+    for name, res, args in SIGNATURES + EXTRA_SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_LIB = None
+
+
+def lib() -> C.CDLL:
+    global _LIB
+    if _LIB is None:
+        _LIB = load()
+    return _LIB
+
+
+def check(rc: int) -> None:
+    if rc != QAM_OK:
+        raise QamError(rc, lib().qam_last_error().decode())

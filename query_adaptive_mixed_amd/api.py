@@ -1,0 +1,233 @@
+"""Thin Python binding over libqam (argument marshalling only).
+
+PyTorch supplies device memory and the current HIP stream; every step of
+the computation runs in libqam's kernels.  Names follow the C ABI:
+``pack_slices``, ``build_level_map``, ``qmatvec`` plus the probes and
+helpers ``unpack_codes``, ``map_weight_bytes`` and ``workspace_bytes``.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+LADDER_BITS = (0, 2, 4, 6, 8)
+
+
+def _stream_handle() -> C.c_void_p:
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> C.c_void_p:
+    return C.c_void_p(t.data_ptr())
+
+
+def _require_cuda(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device (cuda) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class PackedMatrix:
+    """One packed matrix: the device buffer (slice planes + scales) and its descriptor."""
+    buf: torch.Tensor            # uint8 [qam_packed_bytes(N, K)]
+    desc: L.QamPacked
+
+    @property
+    def N(self) -> int:
+        return int(self.desc.N)
+
+    @property
+    def K(self) -> int:
+        return int(self.desc.K)
+
+    @property
+    def n_blocks(self) -> int:
+        return int(self.desc.n_blocks)
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return int(L.lib().qam_packed_bytes(N, K))
+
+
+def pack_slices(W: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None) -> PackedMatrix:
+    """Split int8 codes W [N, K] and fp32 scales [N] into the slice-major packed layout."""
+    _require_cuda(W, "W", torch.int8)
+    _require_cuda(scales, "scales", torch.float32)
+    N, K = W.shape
+    nbytes = packed_bytes(N, K)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    desc = L.QamPacked()
+    L.check(L.lib().qam_pack_slices(_ptr(W), _ptr(scales), N, K, _ptr(out), out.numel(), C.byref(desc),
+                                     _stream_handle()))
+    return PackedMatrix(out, desc)
+
+
+def unpack_codes(packed: PackedMatrix, level_map: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Debug probe: int8 [N, K] codes as the product kernels read them at the map's depths."""
+    _require_cuda(level_map, "level_map", torch.uint8)
+    if out is None:
+        out = torch.empty((packed.N, packed.K), dtype=torch.int8, device=packed.buf.device)
+    L.check(L.lib().qam_unpack_codes(C.byref(packed.desc), _ptr(level_map), _ptr(out), _stream_handle()))
+    return out
+
+
+def build_level_map(coords: torch.Tensor, centres, radii, f: float, g: float, combine: str = "sum",
+                    glass: int = 1, ladder_bits: Sequence[int] = LADDER_BITS, stops=None,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-block rung indices (uint8 [n_blocks]) from the lens rules.
+
+    ``coords`` is a device fp64 [n_blocks, 2] tensor; ``centres`` [n_lenses, 2]
+    and ``radii`` [n_lenses] are host sequences."""
+    _require_cuda(coords, "coords", torch.float64)
+    n_blocks = coords.shape[0]
+    centres = np.asarray(centres, dtype=np.float64).reshape(-1, 2)
+    radii = np.asarray(radii, dtype=np.float64).reshape(-1)
+    if centres.shape[0] != radii.shape[0]:
+        raise ValueError("centres and radii disagree on the lens count")
+    n_lenses = centres.shape[0]
+    lenses = (L.QamLens * max(1, n_lenses))()
+    for i in range(n_lenses):
+        lenses[i].cx, lenses[i].cy, lenses[i].r = float(centres[i, 0]), float(centres[i, 1]), float(radii[i])
+    p = L.QamLensParams()
+    p.f, p.g = float(f), float(g)
+    p.combine = {"sum": L.QAM_COMBINE_SUM, "max": L.QAM_COMBINE_MAX}[combine]
+    if stops is None:
+        p.n_stops = 0
+    else:
+        st = np.asarray(stops, dtype=np.float64).reshape(-1)
+        p.n_stops = int(st.shape[0])
+        if p.n_stops > L.QAM_MAX_STOPS:
+            raise ValueError("too many stops")
+        for j, v in enumerate(st):
+            p.stops[j] = float(v)
+    ladder = (C.c_uint8 * len(ladder_bits))(*ladder_bits)
+    if out is None:
+        out = torch.empty(n_blocks, dtype=torch.uint8, device=coords.device)
+    L.check(L.lib().qam_build_level_map(_ptr(coords), n_blocks, lenses, n_lenses, C.byref(p), C.cast(ladder, C.c_void_p),
+                                        len(ladder_bits), int(glass), _ptr(out), _stream_handle()))
+    return out
+
+
+def map_weight_bytes(level_map, K: int, ladder_bits: Sequence[int] = LADDER_BITS):
+    """(mean bits, weight bytes) of a map over one matrix with K columns (host)."""
+    lv = np.ascontiguousarray(np.asarray(level_map.cpu() if isinstance(level_map, torch.Tensor) else level_map,
+                                         dtype=np.uint8))
+    ladder = (C.c_uint8 * len(ladder_bits))(*ladder_bits)
+    mb, wb = C.c_double(), C.c_int64()
+    L.check(L.lib().qam_map_weight_bytes(lv.ctypes.data_as(C.c_void_p), lv.shape[0], K, C.cast(ladder, C.c_void_p),
+                                         len(ladder_bits), C.byref(mb), C.byref(wb)))
+    return mb.value, wb.value
+
+
+def workspace_bytes(N: int, K: int, B: int = 1) -> int:
+    return int(L.lib().qam_qmatvec_workspace_bytes(N, K, B))
+
+
+class Workspace:
+    """A device scratch buffer that grows on demand (new storage is zero-filled).
+    libqam keeps its leading counter region zero after every call, so one
+    buffer serves calls of any shape on a stream."""
+
+    def __init__(self, device="cuda"):
+        self.device = torch.device(device)
+        self.buf = torch.zeros(0, dtype=torch.uint8, device=self.device)
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 2 * self.buf.numel()), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_WS = {}
+
+
+def default_workspace(device) -> Workspace:
+    key = torch.device(device)
+    if key not in _WS:
+        _WS[key] = Workspace(key)
+    return _WS[key]
+
+
+def qmatvec(x: torch.Tensor, packed: PackedMatrix, level_map: torch.Tensor, y: Optional[torch.Tensor] = None,
+            workspace: Optional[Workspace] = None) -> torch.Tensor:
+    """y [B, N] fp32 = the mixed-depth product of x [B, K] (fp32 or bf16) with the packed matrix."""
+    _require_cuda(level_map, "level_map", torch.uint8)
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    _require_cuda(x, "x")
+    if x.dtype == torch.float32:
+        xdt = L.QAM_X_F32
+    elif x.dtype == torch.bfloat16:
+        xdt = L.QAM_X_BF16
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    B, K = x.shape
+    if K != packed.K:
+        raise ValueError(f"x has {K} columns, matrix has {packed.K}")
+    if level_map.numel() != packed.n_blocks:
+        raise ValueError("level_map must have one entry per block")
+    if y is None:
+        y = torch.empty((B, packed.N), dtype=torch.float32, device=x.device)
+    else:
+        _require_cuda(y, "y", torch.float32)
+    ws = workspace or default_workspace(x.device)
+    need = workspace_bytes(packed.N, packed.K, B)
+    wbuf = ws.get(max(need, 1))
+    L.check(L.lib().qam_qmatvec(_ptr(x), xdt, B, C.byref(packed.desc), _ptr(level_map), 0, _ptr(y), _ptr(wbuf),
+                                wbuf.numel(), _stream_handle()))
+    return y
+
+
+class GroupedQmatvec:
+    """Many matrices with their own x, y and level map, one launch per call.
+
+    ``items`` is a sequence of (PackedMatrix, x [B, K], y [B, N], level_map)
+    tuples; the tensors are bound once (keep them alive and update them in
+    place), and every ``run()`` recomputes all the y from the bound buffers."""
+
+    def __init__(self, items, device="cuda"):
+        n = len(items)
+        arr = (L.QamGemvItem * n)()
+        B = None
+        xdt = None
+        self._keep = []
+        for i, (pm, x, y, lv) in enumerate(items):
+            _require_cuda(x, "x")
+            _require_cuda(y, "y", torch.float32)
+            _require_cuda(lv, "level_map", torch.uint8)
+            b = x.shape[0] if x.dim() == 2 else 1
+            d = L.QAM_X_F32 if x.dtype == torch.float32 else (L.QAM_X_BF16 if x.dtype == torch.bfloat16 else None)
+            if d is None:
+                raise TypeError("x must be float32 or bfloat16")
+            if B is None:
+                B, xdt = b, d
+            elif (b, d) != (B, xdt):
+                raise ValueError("every item of a group needs the same batch and x dtype")
+            arr[i].w = pm.desc
+            arr[i].x, arr[i].y, arr[i].level_map = x.data_ptr(), y.data_ptr(), lv.data_ptr()
+            self._keep.append((pm, x, y, lv))
+        nbytes = int(L.lib().qam_group_bytes(arr, n, B))
+        if nbytes == 0:
+            raise L.QamError(-2, "invalid group items")
+        self.mem = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.desc = L.QamGroup()
+        L.check(L.lib().qam_group_init(arr, n, B, xdt, _ptr(self.mem), nbytes, C.byref(self.desc), _stream_handle()))
+
+    def run(self) -> None:
+        L.check(L.lib().qam_qmatvec_group(C.byref(self.desc), _stream_handle()))
+
+
+def last_variant() -> str:
+    return L.lib().qam_last_variant().decode()

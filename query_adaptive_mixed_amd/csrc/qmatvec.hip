@@ -1,0 +1,652 @@
+// Mixed-depth matrix-vector / small-batch product over the slice planes.
+//
+// Each block of 64 output rows is read at its own depth straight from the
+// stored bytes inside the pass ("FoQLens", table "Progress"); a block read at
+// d bits touches d/2 slice planes, a ZERO block nothing.  Cost is the weight
+// bytes read ("Precision on Demand", abstract).
+//
+// Work decomposition.  A workgroup is one wavefront and takes one block of
+// 64 rows and one chunk of columns (tiles_per_chunk tiles of 64).  The wave
+// first loads its chunk of x and the first half of its weight-prefetch ring,
+// then turns the chunk of x into an exact fixed-point form in LDS:
+//     v_k = rint(x_k * 2^(30-e)),   2^(e-1) <= max_chunk |x| < 2^e,
+// held as four signed int8 limbs v_k = sum_l s_l 256^l (balanced digits of
+// v_k + 0x80808080).  Each lane owns, per 64-column tile and per slice, one
+// 16-byte word group covering 4 rows x 16 columns; codes are rebuilt in
+// registers (one mask per slice and one rotate per four codes) and multiplied
+// into the limbs with v_dot4_i32_i8, exactly, in int32.  The limb sums are
+// combined into an exact integer per row and chunk, scaled by 2^(e-30) in
+// fp64 (still exact), and either written as the output (one chunk) or stored
+// as a partial; the last wavefront of a block to finish sums the partials in
+// chunk order and writes y = fl32(scale * sum).  No floating-point atomics:
+// results are bit-reproducible.
+//
+// The same kernel serves one matrix (descriptor passed by value) and a group
+// of matrices with independent inputs (descriptor table in device memory,
+// one table lookup per workgroup), so a whole weight field is one launch.
+#include <vector>
+
+#include "qam_common.h"
+
+namespace qam {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+
+// Weight loads must be global (not flat) memory operations: a flat load also
+// counts against the LDS wait counter, so every wait for the limb words in LDS
+// would drain the whole prefetch ring with it.
+__device__ __forceinline__ u32x4 load_plane(const uint8_t* p) {
+    return __builtin_nontemporal_load((global_u32x4*)(p));
+}
+
+// One matrix of a launch.
+struct Item {
+    const uint8_t* planes;
+    const float* scales;
+    const void* x;             // [B][K]
+    float* y;                  // [B][N]
+    const uint8_t* level;      // [n_blocks]
+    double* partials;          // [n_chunks][B][N] (split K only)
+    uint32_t* counters;        // [n_blocks]       (split K only)
+    int64_t plane_bytes;       // N*K/4
+    int64_t N, K;
+    int n_blocks;
+    int n_tiles;               // K / 64
+    int tpc;                   // tiles per chunk
+    int n_chunks;
+    int n_quads;               // ceil(n_blocks / 4)
+    int wg_begin;              // first workgroup of this item in a grouped launch
+};
+
+struct Common {
+    const Item* items;         // grouped launches: the descriptor table
+    const int* wg_item;        // grouped launches: item index of every workgroup
+    int B;
+    int x_bf16;
+};
+
+// ------------------------------------------------------------------ x staging
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x2 global_u32x2;
+typedef __attribute__((address_space(4))) const uint32_t const_u32;
+
+// Raw bits of four x values: fp32 (16 bytes) or bf16 (8 bytes, in .x/.y).
+// Converting later, when the values are staged, keeps the wait off this load.
+template <bool XBF16>
+__device__ __forceinline__ u32x4 load_x4_raw(const void* x, int64_t idx) {
+    if constexpr (XBF16) {
+        const u32x2 h = *(global_u32x2*)(static_cast<const uint16_t*>(x) + idx);
+        return u32x4{h.x, h.y, 0u, 0u};
+    } else {
+        return *(global_u32x4*)(static_cast<const float*>(x) + idx);
+    }
+}
+
+template <bool XBF16>
+__device__ __forceinline__ float4 x4_value(u32x4 raw) {
+    if constexpr (XBF16)
+        return make_float4(__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xFFFF0000u),
+                           __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u));
+    return make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y), __uint_as_float(raw.z), __uint_as_float(raw.w));
+}
+
+// The level byte of block b through the scalar cache: the aligned dword that
+// holds it (same page as the byte, so never a fault), waited on with the
+// scalar counter rather than the vector one.
+__device__ __forceinline__ int level_of(const uint8_t* level, int b) {
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(level + b);
+    const uint32_t word = *(const_u32*)(addr & ~(uintptr_t)3);
+    return (int)((word >> (8 * (addr & 3))) & 0xFFu);
+}
+
+// Balanced base-256 digits of the fixed-point value of one element, as four
+// signed bytes (byte l = digit l).
+__device__ __forceinline__ uint32_t limbs_of(float v, int sh) {
+    const int q = (int)rintf(ldexpf(v, sh));            // |q| <= 2^30
+    return ((uint32_t)q + 0x80808080u) ^ 0x80808080u;
+}
+
+// LDS index (in 16-byte units) of the limb words of 4-column group g of the
+// chunk: tile g/16, then the group's position u in the lane's 16 columns, then
+// the lane group (L >> 4) that owns it, so that the four lane groups reading
+// one u hit four consecutive 16-byte slots.
+__device__ __forceinline__ int limb_slot(int g) { return (g & ~15) | ((g & 3) << 2) | ((g >> 2) & 3); }
+
+// ------------------------------------------------------------------ per-wave body
+
+// Prefetch ring: two halves of H tiles each, about eight 16-byte loads in
+// flight per lane for one request (fewer when several requests' accumulators
+// take the registers).  The wait before one half is computed always follows
+// the reload of the other half, so it drains exactly the older half.
+template <int NS, int NB>
+struct Ring {
+    static constexpr int raw = 4 / (NS * NB);
+    static constexpr int H = raw >= 4 ? 4 : (raw >= 2 ? 2 : 1);   // tiles per half
+    static constexpr int PF = 2 * H;                                // tiles per ring
+};
+
+// One tile: four groups of four columns, four rows each, NB requests.
+template <int NS, int NB>
+__device__ __forceinline__ void tile_dots(const u32x4* buf, const int4* __restrict__ lt, int slots,
+                                          int (&acc)[NB][4][4]) {
+    uint32_t w[4][NS];
+#pragma unroll
+    for (int p = 0; p < NS; ++p) {
+        w[0][p] = buf[p].x;
+        w[1][p] = buf[p].y;
+        w[2][p] = buf[p].z;
+        w[3][p] = buf[p].w;
+    }
+    int4 lm[4][NB];
+#pragma unroll
+    for (int uu = 0; uu < 4; ++uu)
+#pragma unroll
+        for (int r = 0; r < NB; ++r) lm[uu][r] = lt[r * slots + uu * 4];
+#define QAM_GROUP(UU)                                                                          \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                             \
+        const int P = (int)assemble<NS, UU>(w[j]);                                              \
+        _Pragma("unroll") for (int r = 0; r < NB; ++r) {                                        \
+            acc[r][j][0] = __builtin_amdgcn_sdot4(P, lm[UU][r].x, acc[r][j][0], false);         \
+            acc[r][j][1] = __builtin_amdgcn_sdot4(P, lm[UU][r].y, acc[r][j][1], false);         \
+            acc[r][j][2] = __builtin_amdgcn_sdot4(P, lm[UU][r].z, acc[r][j][2], false);         \
+            acc[r][j][3] = __builtin_amdgcn_sdot4(P, lm[UU][r].w, acc[r][j][3], false);         \
+        }                                                                                      \
+    }
+    QAM_GROUP(0)
+    QAM_GROUP(1)
+    QAM_GROUP(2)
+    QAM_GROUP(3)
+#undef QAM_GROUP
+}
+
+template <int NS, int H>
+__device__ __forceinline__ void load_half(u32x4 (&h)[H][NS], const uint8_t* base, int64_t pb, int tile, int last) {
+#pragma unroll
+    for (int u = 0; u < H; ++u) {
+        const int t = min(tile + u, last);   // past the chunk: reload its last tile (never computed)
+#pragma unroll
+        for (int p = 0; p < NS; ++p) h[u][p] = load_plane(base + p * pb + (int64_t)t * kTileBytes);
+    }
+}
+
+// Turn this wave's chunk of x into limb words in LDS (see the file comment).
+// xv[r][i] holds the x values of group lane + 64 i of request r.
+template <int NB, int G, bool XBF16>
+__device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngroups, int slots, int L,
+                                            int4* __restrict__ lds, int (&exps)[NB], bool (&bad)[NB]) {
+    float4 xv[NB][G];
+#pragma unroll
+    for (int r = 0; r < NB; ++r)
+#pragma unroll
+        for (int i = 0; i < G; ++i) xv[r][i] = x4_value<XBF16>(xraw[r][i]);
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        float m = 0.0f;
+        int nonfinite = 0;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const float4 v = xv[r][i];
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            nonfinite |= !(fabsf(v.x) <= 3.402823466e38f) | !(fabsf(v.y) <= 3.402823466e38f) |
+                         !(fabsf(v.z) <= 3.402823466e38f) | !(fabsf(v.w) <= 3.402823466e38f);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            m = fmaxf(m, __shfl_xor(m, o));
+            nonfinite |= __shfl_xor(nonfinite, o);
+        }
+        int e = 0;
+        if (m > 0.0f) frexpf(m, &e);
+        exps[r] = __builtin_amdgcn_readfirstlane(e);
+        bad[r] = __builtin_amdgcn_readfirstlane(nonfinite) != 0;
+        const int sh = 30 - exps[r];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int g = L + 64 * i;
+            if (g >= ngroups) continue;
+            const float4 v = xv[r][i];
+            const uint32_t w0 = limbs_of(v.x, sh), w1 = limbs_of(v.y, sh);
+            const uint32_t w2 = limbs_of(v.z, sh), w3 = limbs_of(v.w, sh);
+            int4 out;
+            out.x = (int)((w0 & 0xFFu) | ((w1 & 0xFFu) << 8) | ((w2 & 0xFFu) << 16) | (w3 << 24));
+            out.y = (int)(((w0 >> 8) & 0xFFu) | (w1 & 0xFF00u) | ((w2 & 0xFF00u) << 8) | ((w3 & 0xFF00u) << 16));
+            out.z = (int)(((w0 >> 16) & 0xFFu) | ((w1 >> 8) & 0xFF00u) | (w2 & 0xFF0000u) | ((w3 & 0xFF0000u) << 8));
+            out.w = (int)((w0 >> 24) | ((w1 >> 16) & 0xFF00u) | ((w2 >> 8) & 0xFF0000u) | (w3 & 0xFF000000u));
+            lds[r * slots + limb_slot(g)] = out;
+        }
+    }
+    __syncthreads();   // the workgroup is this one wavefront: orders the LDS writes before the reads
+}
+
+// One wavefront: block b, column chunk `chunk`, read at NS slices.
+template <int NS, int NB, int G, bool XBF16>
+__device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* __restrict__ lds, int b, int chunk,
+                                          int L) {
+    constexpr int H = Ring<NS, NB>::H;
+    constexpr int PF = Ring<NS, NB>::PF;
+    const int B = c.B;
+    const int tile0 = chunk * a.tpc;
+    const int ntile = min(a.tpc, a.n_tiles - tile0);
+    const int ngroups = ntile * 16;
+    const int slots = a.tpc * 16;
+    const int64_t col0 = (int64_t)tile0 * kTileCols;
+    const uint8_t* base = a.planes + (int64_t)b * 16 * a.K + (int64_t)tile0 * kTileBytes + L * 16;
+    const int kg = L >> 4;
+    const int64_t pb = a.plane_bytes;
+
+    // Nothing of this wave is in flight here, so this wait is free; it tells the
+    // compiler's wait counting as much, which it cannot see through the merged
+    // control flow of the depth cases, and keeps every wait below exact.
+    __builtin_amdgcn_s_waitcnt(0);
+    // 1. x first, so that waiting for it never drains the weight loads issued after it
+    u32x4 xraw[NB][G];
+#pragma unroll
+    for (int r = 0; r < NB; ++r)
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            // unconditional (clamped) loads keep the wait counts exact; groups
+            // past the chunk are never written to LDS
+            const int g = min(L + 64 * i, ngroups - 1);
+            xraw[r][i] = load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + 4 * g);
+        }
+    // 2. the first ring of weight loads, straight into the ring registers
+    // 2. the first ring of weight loads, straight into the ring registers
+    //    (every load is unconditional; tiles past the chunk are clamped)
+    const int last = ntile - 1;
+    //    (first half now; the compiler tracks at most about fifteen loads in
+    //    flight precisely, and x already takes up to eight of them)
+    u32x4 A[H][NS], Bh[H][NS];
+    __builtin_amdgcn_sched_barrier(0);   // x loads go out first ...
+    load_half<NS, H>(A, base, pb, 0, last);
+    __builtin_amdgcn_sched_barrier(0);   // ... then half a ring, and only then is x used
+    // 3. the limbs of this chunk of x, while those loads are in flight
+    int exps[NB];
+    bool bad[NB];
+    stage_limbs<NB, G, XBF16>(xraw, ngroups, slots, L, lds, exps, bad);
+    load_half<NS, H>(Bh, base, pb, H, last);
+    __builtin_amdgcn_sched_barrier(0);
+
+    int acc[NB][4][4];
+#pragma unroll
+    for (int r = 0; r < NB; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int l = 0; l < 4; ++l) acc[r][j][l] = 0;
+
+    // Steady state: every tile of these rounds is in range.  The scheduling
+    // barriers keep each reload right after the half it replaces, ahead of the
+    // other half's arithmetic, so each wait drains only the older half.
+    int t = 0;
+    for (; t + PF < ntile; t += PF) {
+#pragma unroll
+        for (int u = 0; u < H; ++u) tile_dots<NS, NB>(A[u], lds + (t + u) * 16 + kg, slots, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        load_half<NS, H>(A, base, pb, t + PF, last);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < H; ++u) tile_dots<NS, NB>(Bh[u], lds + (t + H + u) * 16 + kg, slots, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        load_half<NS, H>(Bh, base, pb, t + PF + H, last);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Drain: the last ring, whose tail may run past a ragged chunk.
+#pragma unroll
+    for (int u = 0; u < H; ++u)
+        if (t + u < ntile) tile_dots<NS, NB>(A[u], lds + (t + u) * 16 + kg, slots, acc);
+#pragma unroll
+    for (int u = 0; u < H; ++u)
+        if (t + H + u < ntile) tile_dots<NS, NB>(Bh[u], lds + (t + H + u) * 16 + kg, slots, acc);
+
+    // exact per-row integers, summed over the four lane groups sharing a row
+    const int row = b * kRows + L;          // the row this lane writes: j = L >> 4
+    const float sc = a.scales[row];
+    double part[NB];
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        double d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            d[j] = (double)acc[r][j][3] * 16777216.0 + (double)acc[r][j][2] * 65536.0 +
+                   (double)acc[r][j][1] * 256.0 + (double)acc[r][j][0];
+            d[j] += __shfl_xor(d[j], 16);
+            d[j] += __shfl_xor(d[j], 32);
+        }
+        const double mine = kg == 0 ? d[0] : (kg == 1 ? d[1] : (kg == 2 ? d[2] : d[3]));
+        // a non-finite x in the chunk makes that request's outputs NaN
+        part[r] = bad[r] ? __builtin_nan("") : ldexp(mine, exps[r] - 30);
+    }
+
+    if (a.n_chunks == 1) {
+#pragma unroll
+        for (int r = 0; r < NB; ++r) a.y[(int64_t)r * a.N + row] = (float)((double)sc * part[r]);
+        return;
+    }
+    // Split K: publish this chunk's partials, then count the arrival; the last
+    // wave of the block sums the partials in chunk order.  The partials are
+    // written and read with device-scope (write-through) atomic accesses and
+    // the counter is bumped only after those stores have completed, so no
+    // cache-wide writeback or invalidate is needed: a device-scope fence here
+    // writes back and invalidates the whole L2 of the XCD, thousands of times
+    // per launch.
+#pragma unroll
+    for (int r = 0; r < NB; ++r)
+        __hip_atomic_store(&a.partials[((int64_t)chunk * B + r) * a.N + row], part[r], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);   // the partial stores are complete before the arrival is counted
+    uint32_t prev = 0;
+    if (L == 0) prev = __hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __shfl(prev, 0);
+    if (prev != (uint32_t)(a.n_chunks - 1)) return;
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        double sum = 0.0;
+        for (int cc = 0; cc < a.n_chunks; ++cc)
+            sum += __hip_atomic_load(&a.partials[((int64_t)cc * B + r) * a.N + row], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        a.y[(int64_t)r * a.N + row] = (float)((double)sc * sum);
+    }
+    if (L == 0) __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Groups of four x values one lane stages per request (tpc / 4, 64 lanes).
+// With the first half ring this keeps at most about eleven loads in flight
+// before x is used, within what the compiler's wait counting tracks exactly.
+template <int NB>
+struct Stage {
+    static constexpr int G = NB == 1 ? 6 : (NB == 2 ? 3 : (NB <= 4 ? 2 : 1));   // tpc <= 24, 12, 8, 4
+};
+
+// One workgroup = one wavefront = one (block, column chunk) of one matrix.
+template <int NB, bool GROUPED, bool XBF16>
+__global__ __launch_bounds__(64) void qmatvec_kernel(Item single, Common c) {
+    extern __shared__ int4 lds[];           // [NB][tpc * 16] limb words of this wave's chunk
+    Item a;
+    int local;
+    if constexpr (GROUPED) {
+        const int idx = c.wg_item[blockIdx.x];
+        a = c.items[idx];
+        local = (int)blockIdx.x - a.wg_begin;
+    } else {
+        a = single;
+        local = (int)blockIdx.x;
+    }
+    const int chunk = local % a.n_chunks;
+    const int b = local / a.n_chunks;
+    const int L = threadIdx.x;
+    const int lev = level_of(a.level, b);
+    const int ns = __builtin_amdgcn_readfirstlane(lev < 4 ? lev : 4);
+    constexpr int G = Stage<NB>::G;
+    switch (ns) {
+        case 0:   // ZERO: nothing read, y = 0 (written once, by the first chunk)
+            if (chunk == 0)
+#pragma unroll
+                for (int r = 0; r < NB; ++r) a.y[(int64_t)r * a.N + (int64_t)b * kRows + L] = 0.0f;
+            return;
+        case 1: wave_body<1, NB, G, XBF16>(a, c, lds, b, chunk, L); return;
+        case 2: wave_body<2, NB, G, XBF16>(a, c, lds, b, chunk, L); return;
+        case 3: wave_body<3, NB, G, XBF16>(a, c, lds, b, chunk, L); return;
+        default: wave_body<4, NB, G, XBF16>(a, c, lds, b, chunk, L); return;
+    }
+}
+
+// ------------------------------------------------------------------ host side
+
+struct Plan {
+    int tpc, n_chunks, n_quads;
+    size_t partial_bytes;
+};
+
+static int g_target_waves = 256 * 16;   // wavefronts aimed for per launch
+
+// LDS holds B x tpc x 256 bytes of limbs; one lane stages at most
+// Stage<B>::G groups of four x values, so tpc <= 4 G
+static int max_tpc_for(int64_t B) { return B > 4 ? 4 : (B > 2 ? 8 : (B > 1 ? 12 : 24)); }
+// every full chunk holds a whole number of prefetch rings (Ring<NS, B>::PF for every NS)
+static int tpc_align_for(int64_t B) { return B == 1 ? 8 : (B == 2 ? 4 : 2); }
+
+// Chunking of one matrix.  `blocks_in_launch` is the number of blocks the
+// whole launch covers (the matrix itself, or every matrix of a group): K is
+// split until the launch has about g_target_waves wavefronts, with at least
+// four tiles per chunk and at most max_tpc_for(B) (LDS budget).
+static Plan make_plan(int64_t N, int64_t K, int64_t B, int64_t blocks_in_launch) {
+    Plan p{};
+    const int n_blocks = (int)(N / kRows);
+    const int n_tiles = (int)(K / kTileCols);
+    const int max_tpc = max_tpc_for(B);
+    const int align = tpc_align_for(B);
+    long want = (long)((g_target_waves + blocks_in_launch - 1) / blocks_in_launch);
+    long max_chunks = n_tiles / align;
+    if (max_chunks < 1) max_chunks = 1;
+    if (want > max_chunks) want = max_chunks;
+    if (want < 1) want = 1;
+    int tpc = (int)((n_tiles + want - 1) / want);
+    tpc = (tpc + align - 1) / align * align;
+    if (tpc > max_tpc) tpc = max_tpc;
+    if (tpc > n_tiles) tpc = n_tiles;
+    if (tpc < 1) tpc = 1;
+    p.tpc = tpc;
+    p.n_chunks = (n_tiles + tpc - 1) / tpc;
+    p.n_quads = n_blocks;   // one wavefront-sized workgroup per block and chunk
+    p.partial_bytes = p.n_chunks > 1 ? ((size_t)p.n_chunks * B * N * sizeof(double) + 255) / 256 * 256 : 0;
+    return p;
+}
+
+template <int NB, bool GROUPED>
+static void launch_nb(const Item& it, const Common& c, int64_t grid, size_t lds, hipStream_t s) {
+    if (c.x_bf16)
+        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, true>), dim3((unsigned)grid), dim3(64), lds, s, it, c);
+    else
+        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, false>), dim3((unsigned)grid), dim3(64), lds, s, it, c);
+}
+
+template <bool GROUPED>
+static void launch(int64_t B, const Item& it, const Common& c, int64_t grid, size_t lds, hipStream_t s) {
+    switch (B) {
+        case 1: launch_nb<1, GROUPED>(it, c, grid, lds, s); break;
+        case 2: launch_nb<2, GROUPED>(it, c, grid, lds, s); break;
+        case 3: launch_nb<3, GROUPED>(it, c, grid, lds, s); break;
+        case 4: launch_nb<4, GROUPED>(it, c, grid, lds, s); break;
+        case 5: launch_nb<5, GROUPED>(it, c, grid, lds, s); break;
+        case 6: launch_nb<6, GROUPED>(it, c, grid, lds, s); break;
+        case 7: launch_nb<7, GROUPED>(it, c, grid, lds, s); break;
+        default: launch_nb<8, GROUPED>(it, c, grid, lds, s); break;
+    }
+}
+
+// Host checks shared by the single and grouped entry points.
+static int check_item(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
+                      float* y, const char* who) {
+    if (!x || !packed || !level_map || !y || !packed->planes) QAM_FAIL(QAM_ERR_NULL, "%s: null pointer", who);
+    const int64_t N = packed->N, K = packed->K;
+    if (N <= 0 || K <= 0 || N % kRows || K % kTileCols || K > QAM_MAX_K || packed->n_blocks != N / kRows ||
+        packed->n_blocks > QAM_MAX_BLOCKS)
+        QAM_FAIL(QAM_ERR_SHAPE, "%s: bad packed shape N=%lld K=%lld", who, (long long)N, (long long)K);
+    if (B < 1 || B > QAM_MAX_BATCH) QAM_FAIL(QAM_ERR_ARG, "%s: B=%lld outside [1, %d]", who, (long long)B, QAM_MAX_BATCH);
+    if (x_dtype != QAM_X_F32 && x_dtype != QAM_X_BF16) QAM_FAIL(QAM_ERR_ARG, "%s: unknown x_dtype %d", who, x_dtype);
+    if (!aligned(x, 16) || !aligned(y, 4) || !aligned(packed->planes, 256))
+        QAM_FAIL(QAM_ERR_ALIGN, "%s: x must be 16-byte and planes 256-byte aligned", who);
+    if (packed->scales != reinterpret_cast<float*>(static_cast<char*>(packed->planes) + N * K))
+        QAM_FAIL(QAM_ERR_ARG, "%s: descriptor scales do not follow the planes", who);
+    const size_t xbytes = (size_t)B * K * (x_dtype == QAM_X_BF16 ? 2 : 4);
+    const char* xc = static_cast<const char*>(x);
+    const char* yc = reinterpret_cast<const char*>(y);
+    if (xc < yc + (size_t)B * N * 4 && yc < xc + xbytes) QAM_FAIL(QAM_ERR_ARG, "%s: x and y overlap", who);
+    return QAM_OK;
+}
+
+static Item make_item(const void* x, const qam_packed* packed, const uint8_t* level_map, float* y, const Plan& p) {
+    Item it{};
+    it.planes = static_cast<const uint8_t*>(packed->planes);
+    it.scales = packed->scales;
+    it.x = x;
+    it.y = y;
+    it.level = level_map;
+    it.plane_bytes = packed->N * packed->K / 4;
+    it.N = packed->N;
+    it.K = packed->K;
+    it.n_blocks = (int)(packed->N / kRows);
+    it.n_tiles = (int)(packed->K / kTileCols);
+    it.tpc = p.tpc;
+    it.n_chunks = p.n_chunks;
+    it.n_quads = p.n_quads;
+    return it;
+}
+
+}  // namespace qam
+
+using namespace qam;
+
+extern "C" size_t qam_qmatvec_workspace_bytes(int64_t N, int64_t K, int64_t B) {
+    if (N <= 0 || K <= 0 || N % kRows || K % kTileCols || K > QAM_MAX_K || N / kRows > QAM_MAX_BLOCKS || B < 1 ||
+        B > QAM_MAX_BATCH)
+        return 0;
+    const Plan p = make_plan(N, K, B, N / kRows);
+    return p.n_chunks > 1 ? QAM_WS_COUNTER_BYTES + p.partial_bytes : 0;
+}
+
+extern "C" int qam_set_target_waves(int waves) {
+    clear_error();
+    if (waves < 64 || waves > (1 << 20)) QAM_FAIL(QAM_ERR_ARG, "set_target_waves: %d outside [64, 2^20]", waves);
+    g_target_waves = waves;
+    return QAM_OK;
+}
+
+extern "C" int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
+                           int per_request_maps, float* y, void* workspace, size_t workspace_bytes, hipStream_t s) {
+    clear_error();
+    if (int rc = check_item(x, x_dtype, B, packed, level_map, y, "qmatvec")) return rc;
+    if (per_request_maps != 0) QAM_FAIL(QAM_ERR_ARG, "qmatvec: per-request maps are not taken by this entry point");
+    const Plan p = make_plan(packed->N, packed->K, B, packed->n_blocks);
+    Item it = make_item(x, packed, level_map, y, p);
+    if (p.n_chunks > 1) {
+        const size_t need = QAM_WS_COUNTER_BYTES + p.partial_bytes;
+        if (!workspace) QAM_FAIL(QAM_ERR_WORKSPACE, "qmatvec: workspace of %zu bytes required", need);
+        if (workspace_bytes < need) QAM_FAIL(QAM_ERR_WORKSPACE, "qmatvec: workspace %zu < %zu bytes", workspace_bytes, need);
+        if (!aligned(workspace, 256)) QAM_FAIL(QAM_ERR_ALIGN, "qmatvec: workspace must be 256-byte aligned");
+        it.counters = static_cast<uint32_t*>(workspace);
+        it.partials = reinterpret_cast<double*>(static_cast<char*>(workspace) + QAM_WS_COUNTER_BYTES);
+    }
+    Common c{};
+    c.B = (int)B;
+    c.x_bf16 = x_dtype == QAM_X_BF16;
+    const int64_t grid = (int64_t)p.n_chunks * p.n_quads;
+    launch<false>(B, it, c, grid, (size_t)B * p.tpc * 16 * sizeof(int4), s);
+    QAM_HIP_CHECK(hipGetLastError());
+    char v[128];
+    snprintf(v, sizeof(v), "qmatvec_dot4 B=%lld tpc=%d chunks=%d", (long long)B, p.tpc, p.n_chunks);
+    set_variant(v);
+    return QAM_OK;
+}
+
+// ------------------------------------------------------------------ grouped launches
+
+namespace qam {
+
+struct GroupLayout {
+    std::vector<Plan> plans;
+    size_t partial_bytes = 0, table_bytes = 0, map_bytes = 0, total = 0;
+    int64_t n_wg = 0, blocks = 0;
+    int max_tpc = 0;
+};
+
+static int layout_group(const qam_gemv_item* items, int n_items, int64_t B, GroupLayout& g) {
+    if (!items || n_items < 1) QAM_FAIL(QAM_ERR_ARG, "group: need at least one item");
+    if (B < 1 || B > QAM_MAX_BATCH) QAM_FAIL(QAM_ERR_ARG, "group: B=%lld outside [1, %d]", (long long)B, QAM_MAX_BATCH);
+    for (int i = 0; i < n_items; ++i) {
+        const qam_packed& w = items[i].w;
+        if (w.N <= 0 || w.N % kRows || w.K <= 0 || w.K % kTileCols || w.K > QAM_MAX_K)
+            QAM_FAIL(QAM_ERR_SHAPE, "group: item %d has a bad shape", i);
+        g.blocks += w.N / kRows;
+    }
+    if (g.blocks > QAM_MAX_BLOCKS) QAM_FAIL(QAM_ERR_SHAPE, "group: %lld blocks > %d", (long long)g.blocks, QAM_MAX_BLOCKS);
+    for (int i = 0; i < n_items; ++i) {
+        const Plan p = make_plan(items[i].w.N, items[i].w.K, B, g.blocks);
+        g.plans.push_back(p);
+        g.partial_bytes += p.partial_bytes;
+        g.n_wg += (int64_t)p.n_chunks * p.n_quads;
+        if (p.tpc > g.max_tpc) g.max_tpc = p.tpc;
+    }
+    if (g.n_wg > 0x7FFFFFFF) QAM_FAIL(QAM_ERR_SHAPE, "group: too many workgroups");
+    g.table_bytes = ((size_t)n_items * sizeof(Item) + 255) / 256 * 256;
+    g.map_bytes = ((size_t)g.n_wg * sizeof(int) + 255) / 256 * 256;
+    g.total = QAM_WS_COUNTER_BYTES + g.partial_bytes + g.table_bytes + g.map_bytes;
+    return QAM_OK;
+}
+
+}  // namespace qam
+
+extern "C" size_t qam_group_bytes(const qam_gemv_item* items, int n_items, int64_t B) {
+    GroupLayout g;
+    if (layout_group(items, n_items, B, g) != QAM_OK) return 0;
+    return g.total;
+}
+
+extern "C" int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dtype, void* dev_mem,
+                              size_t dev_bytes, qam_group* group_out, hipStream_t s) {
+    clear_error();
+    if (!group_out || !dev_mem) QAM_FAIL(QAM_ERR_NULL, "group_init: null pointer");
+    GroupLayout g;
+    if (int rc = layout_group(items, n_items, B, g)) return rc;
+    if (dev_bytes < g.total) QAM_FAIL(QAM_ERR_WORKSPACE, "group_init: %zu < %zu bytes", dev_bytes, g.total);
+    if (!aligned(dev_mem, 256)) QAM_FAIL(QAM_ERR_ALIGN, "group_init: device memory must be 256-byte aligned");
+    char* base = static_cast<char*>(dev_mem);
+    char* partials = base + QAM_WS_COUNTER_BYTES;
+    char* table = partials + g.partial_bytes;
+    char* wgmap = table + g.table_bytes;
+    std::vector<Item> host_items(n_items);
+    std::vector<int> host_map((size_t)g.n_wg);
+    int64_t wg = 0, blk = 0;
+    size_t poff = 0;
+    for (int i = 0; i < n_items; ++i) {
+        const qam_gemv_item& gi = items[i];
+        if (int rc = check_item(gi.x, x_dtype, B, &gi.w, gi.level_map, gi.y, "group_init")) return rc;
+        const Plan& p = g.plans[i];
+        Item it = make_item(gi.x, &gi.w, gi.level_map, gi.y, p);
+        it.wg_begin = (int)wg;
+        if (p.n_chunks > 1) {
+            it.counters = reinterpret_cast<uint32_t*>(base) + blk;
+            it.partials = reinterpret_cast<double*>(partials + poff);
+            poff += p.partial_bytes;
+        }
+        blk += it.n_blocks;
+        const int64_t n = (int64_t)p.n_chunks * p.n_quads;
+        for (int64_t k = 0; k < n; ++k) host_map[(size_t)(wg + k)] = i;
+        wg += n;
+        host_items[i] = it;
+    }
+    QAM_HIP_CHECK(hipMemsetAsync(base, 0, QAM_WS_COUNTER_BYTES, s));
+    QAM_HIP_CHECK(hipMemcpyAsync(table, host_items.data(), sizeof(Item) * n_items, hipMemcpyHostToDevice, s));
+    QAM_HIP_CHECK(hipMemcpyAsync(wgmap, host_map.data(), sizeof(int) * host_map.size(), hipMemcpyHostToDevice, s));
+    QAM_HIP_CHECK(hipStreamSynchronize(s));
+    group_out->n_items = n_items;
+    group_out->B = B;
+    group_out->x_dtype = x_dtype;
+    group_out->n_workgroups = g.n_wg;
+    group_out->lds_bytes = (size_t)B * g.max_tpc * 16 * sizeof(int4);
+    group_out->table = table;
+    group_out->wg_map = wgmap;
+    return QAM_OK;
+}
+
+extern "C" int qam_qmatvec_group(const qam_group* group, hipStream_t s) {
+    clear_error();
+    if (!group || !group->table || !group->wg_map) QAM_FAIL(QAM_ERR_NULL, "qmatvec_group: uninitialised group");
+    if (group->B < 1 || group->B > QAM_MAX_BATCH || group->n_workgroups < 1)
+        QAM_FAIL(QAM_ERR_ARG, "qmatvec_group: corrupt group descriptor");
+    Common c{};
+    c.items = static_cast<const Item*>(group->table);
+    c.wg_item = static_cast<const int*>(group->wg_map);
+    c.B = (int)group->B;
+    c.x_bf16 = group->x_dtype == QAM_X_BF16;
+    Item none{};
+    launch<true>(group->B, none, c, group->n_workgroups, group->lds_bytes, s);
+    QAM_HIP_CHECK(hipGetLastError());
+    char v[128];
+    snprintf(v, sizeof(v), "qmatvec_dot4_group items=%d B=%lld wg=%lld", group->n_items, (long long)group->B,
+             (long long)group->n_workgroups);
+    set_variant(v);
+    return QAM_OK;
+}

@@ -1,0 +1,340 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: level maps and reconstructed int codes bit-exact; fp32 outputs within
+1e-4 * sum_k |w_nk| |x_k| per row (w = scale * code at the block's depth),
+so a ZERO block must give exactly 0; exact-integer special cases bit-exact.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+LADDER = (0, 2, 4, 6, 8)
+
+
+@pytest.fixture(scope="module")
+def qam():
+    import query_adaptive_mixed_amd as Q
+    return Q
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def pack(qam, W, sc):
+    return qam.pack_slices(dev(W), dev(sc.astype(np.float32)))
+
+
+def check_y(y, W, sc, x, lv, what=""):
+    ref = O.qmatvec_ref(W, sc, x, lv)
+    tol = O.qmatvec_tolerance(W, sc, x, lv)
+    err = np.abs(y.astype(np.float64) - ref)
+    bad = err > tol
+    assert not bad.any(), (what, int(bad.sum()), float((err / np.maximum(tol, 1e-300)).max()))
+    zero_rows = np.repeat(np.asarray(lv) == 0, 64)
+    assert np.all(y[:, zero_rows] == 0.0), what
+
+
+# ------------------------------------------------------------------ codes
+
+@pytest.mark.parametrize("N,K", [(64, 64), (512, 256), (192, 1088), (1024, 4096)])
+def test_unpack_codes_bit_exact_every_depth(qam, N, K):
+    rng = np.random.default_rng(N + K)
+    W = rng.integers(-128, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=N)
+    pm = pack(qam, W, sc)
+    nb = N // 64
+    for lv in [np.full(nb, d, np.uint8) for d in range(5)] + [rng.integers(0, 5, nb).astype(np.uint8)]:
+        got = host(qam.unpack_codes(pm, dev(lv)))
+        want = np.concatenate([O.truncate(W[64 * b:64 * b + 64], LADDER[lv[b]]) for b in range(nb)])
+        assert np.array_equal(got.astype(np.int64), want), lv
+    # the scales travel with the planes
+    got_sc = host(pm.buf[N * K:].view(torch.float32))
+    assert np.array_equal(got_sc, sc.astype(np.float32))
+
+
+def test_identity_batch_probe_reads_the_codes(qam):
+    """x = e_k through the real product kernel gives y = scale * c[:, k] exactly."""
+    rng = np.random.default_rng(3)
+    N, K = 256, 512
+    W = rng.integers(-128, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    sc = np.ones(N, np.float32)
+    pm = pack(qam, W, sc)
+    lv = np.array([1, 2, 3, 4], np.uint8)
+    cols = [0, 1, 63, 64, 200, 511]
+    x = np.zeros((len(cols), K), np.float32)
+    for i, k in enumerate(cols):
+        x[i, k] = 1.0
+    y = host(qam.qmatvec(dev(x), pm, dev(lv)))
+    for i, k in enumerate(cols):
+        want = np.concatenate([O.truncate(W[64 * b:64 * b + 64, k], LADDER[lv[b]]) for b in range(4)])
+        assert np.array_equal(y[i].astype(np.int64), want)
+
+
+# ------------------------------------------------------------------ level maps
+
+def _gpu_map(qam, coords, centres, radii, f, g, combine, glass, stops=None, ladder=LADDER):
+    return host(qam.build_level_map(dev(coords.astype(np.float64)), centres, radii, f, g, combine, glass,
+                                    ladder_bits=ladder, stops=stops))
+
+
+def test_level_map_hand_examples(qam):
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "lens_hand_examples.json")))
+    for case in g["cases"]:
+        cen = np.array([g["lenses"][n][:2] for n in case["lenses"]])
+        rad = np.array([g["lenses"][n][2] for n in case["lenses"]])
+        got = _gpu_map(qam, np.array(case["blocks"]), cen, rad, case["f"], case["g"], case["combine"],
+                       case["glass"], case["stops"])
+        assert got.tolist() == case["levels"], case["name"]
+
+
+def test_level_map_single_layer_workload(qam):
+    inp = WL.single_layer_512x256(0)
+    lp = inp["lens"]
+    want = O.level_map(inp["coords"], lp.centres, lp.radii, lp.f, lp.g, lp.combine, 5, lp.glass)
+    got = _gpu_map(qam, inp["coords"], lp.centres, lp.radii, lp.f, lp.g, lp.combine, lp.glass)
+    assert np.array_equal(got, want)
+
+
+def test_level_map_bit_exact_random_fields(qam):
+    rng = np.random.default_rng(17)
+    for trial in range(40):
+        n = int(rng.integers(1, 5000))
+        coords = rng.uniform(-0.2, 1.2, size=(n, 2)) if trial % 2 else WL.clustered_coords(rng, n)
+        nl = int(rng.integers(0, 12))
+        centres = coords[rng.choice(n, min(nl, n), replace=False)] if nl else np.zeros((0, 2))
+        radii = rng.uniform(0.0, 0.4, size=centres.shape[0])
+        n_rungs = int(rng.integers(2, 9))
+        ladder = tuple(range(0, 2 * n_rungs, 2))
+        glass = int(rng.integers(0, n_rungs))
+        f = float(rng.choice([0.0, 1.0, rng.uniform(0, 1), 0.5]))
+        g = float(rng.choice([0.0, 1.0, rng.uniform(0, 1)]))
+        combine = "sum" if rng.uniform() < 0.6 else "max"
+        kappa = O.ceiling(g, n_rungs - 1, glass)
+        stops = None
+        if kappa > glass and rng.uniform() < 0.4:
+            stops = np.sort(rng.uniform(0.05, 3.0, size=kappa - glass))[::-1]
+            if np.any(np.diff(stops) >= 0):
+                stops = None
+        want = O.level_map(coords, centres, radii, f, g, combine, n_rungs, glass, stops)
+        got = _gpu_map(qam, coords, centres, radii, f, g, combine, glass, stops, ladder)
+        assert np.array_equal(got, want), (trial, np.nonzero(got != want)[0][:5])
+
+
+def test_level_map_bit_exact_on_ties(qam):
+    """A dyadic grid puts many blocks exactly on ring stops and lens edges."""
+    xs = np.arange(0, 65) / 64.0
+    coords = np.array([(a, b) for a in xs for b in xs])
+    centres = np.array([[0.5, 0.5], [0.25, 0.75], [0.75, 0.25]])
+    for f, g, glass, combine in [(0.5, 1.0, 0, "sum"), (0.5, 0.75, 1, "sum"), (0.5, 1.0, 1, "max"),
+                                 (0.2, 1.0, 0, "max"), (0.8, 0.5, 0, "sum")]:
+        for radii in ([0.25, 0.125, 0.375], [0.5, 0.5, 0.5]):
+            want = O.level_map(coords, centres, radii, f, g, combine, 5, glass)
+            got = _gpu_map(qam, coords, centres, radii, f, g, combine, glass)
+            assert np.array_equal(got, want)
+
+
+def test_level_map_workload_fields(qam):
+    fld = WL.e2b_field(0)
+    lp = WL.e2b_lenses(fld)
+    want = O.level_map(fld.coords, lp.centres, lp.radii, lp.f, lp.g, lp.combine, 5, lp.glass)
+    got = _gpu_map(qam, fld.coords, lp.centres, lp.radii, lp.f, lp.g, lp.combine, lp.glass)
+    assert np.array_equal(got, want)
+    st = WL.streaming_stack(0)
+    cen, rad = WL.stack_lenses(st)
+    for glass in (0, 1):
+        for f in (0.1, 0.3, 0.6):
+            want = O.level_map(st.coords, cen, rad, f, 1.0, "sum", 5, glass)
+            got = _gpu_map(qam, st.coords, cen, rad, f, 1.0, "sum", glass)
+            assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------------------ qmatvec
+
+def test_qmatvec_single_layer_workload_all_maps_sampled(qam):
+    inp = WL.single_layer_512x256(0)
+    W, sc, x, lp = inp["W"], inp["scales"], inp["x"], inp["lens"]
+    pm = pack(qam, W, sc)
+    lv = O.level_map(inp["coords"], lp.centres, lp.radii, lp.f, lp.g, lp.combine, 5, lp.glass)
+    y = host(qam.qmatvec(dev(x), pm, dev(lv)))
+    check_y(y, W, sc, x, lv, "lens map")
+    # a per-block, per-depth table checked once; then random maps through the kernel
+    rng = np.random.default_rng(0)
+    xd = dev(x)
+    for mp in list(rng.integers(0, 5, size=(200, 8))) + [np.full(8, d) for d in range(5)]:
+        mp = mp.astype(np.uint8)
+        y = host(qam.qmatvec(xd, pm, dev(mp)))
+        check_y(y, W, sc, x, mp, str(mp))
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 8])
+@pytest.mark.parametrize("K", [256, 512, 1536, 2048, 8960])
+@pytest.mark.parametrize("N", [128, 512, 2048])
+def test_qmatvec_shape_battery(qam, N, K, B):
+    rng = np.random.default_rng(N * 7 + K * 3 + B)
+    W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+    x = rng.standard_normal((B, K)).astype(np.float32)
+    lv = rng.integers(0, 5, size=N // 64).astype(np.uint8)
+    pm = pack(qam, W, sc)
+    y = host(qam.qmatvec(dev(x), pm, dev(lv)))
+    check_y(y, W, sc, x, lv, (N, K, B))
+
+
+def test_qmatvec_exact_integer_cases(qam):
+    """Integer x in [-3, 3] with scale 1: y is an exact integer; a D8 map is
+    the untruncated int8 product (numpy int64, bit-exact)."""
+    rng = np.random.default_rng(21)
+    for N, K, B in [(512, 256, 1), (256, 8192, 2), (128, 28672, 1), (64, 65536, 1)]:
+        W = rng.integers(-128, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+        x = rng.integers(-3, 4, size=(B, K)).astype(np.float32)
+        pm = pack(qam, W, np.ones(N, np.float32))
+        for lv in (np.full(N // 64, 4, np.uint8), rng.integers(0, 5, N // 64).astype(np.uint8)):
+            y = host(qam.qmatvec(dev(x), pm, dev(lv)))
+            codes = np.concatenate([O.truncate(W[64 * b:64 * b + 64], LADDER[lv[b]]) for b in range(N // 64)])
+            want = x.astype(np.int64) @ codes.T
+            assert np.array_equal(y.astype(np.int64), want)
+            assert np.all(np.abs(want) < 2 ** 24)
+
+
+def test_qmatvec_edge_cases(qam):
+    rng = np.random.default_rng(4)
+    N, K = 256, 1024
+    W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    W[0, :] = -128
+    W[1, :] = 127
+    W[2, :] = -127
+    sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+    sc[3] = 0.0
+    x = rng.standard_normal((1, K)).astype(np.float32)
+    pm = pack(qam, W, sc)
+    for lv in (np.zeros(4, np.uint8), np.full(4, 4, np.uint8), np.array([1, 0, 4, 2], np.uint8)):
+        y = host(qam.qmatvec(dev(x), pm, dev(lv)))
+        check_y(y, W, sc, x, lv, lv)
+    y = host(qam.qmatvec(dev(x), pm, dev(np.full(4, 3, np.uint8))))
+    assert y[0, 3] == 0.0
+    # x all zero gives exact zeros
+    y = host(qam.qmatvec(dev(np.zeros((1, K), np.float32)), pm, dev(np.full(4, 4, np.uint8))))
+    assert np.all(y == 0.0)
+    # wide dynamic range of x (six decades) still meets the bound
+    xr = (rng.choice([-1, 1], size=(2, K)) * 10.0 ** rng.uniform(-3, 3, size=(2, K))).astype(np.float32)
+    lv = rng.integers(1, 5, 4).astype(np.uint8)
+    y = host(qam.qmatvec(dev(xr), pm, dev(lv)))
+    check_y(y, W, sc, xr, lv, "dynamic range")
+    # a non-finite x poisons that request's non-ZERO outputs with NaN
+    xn = x.copy()
+    xn[0, 5] = np.inf
+    y = host(qam.qmatvec(dev(xn), pm, dev(np.array([0, 4, 4, 4], np.uint8))))
+    assert np.all(y[0, :64] == 0.0) and np.all(np.isnan(y[0, 64:]))
+
+
+def test_qmatvec_bf16_activations(qam):
+    rng = np.random.default_rng(5)
+    N, K = 512, 2048
+    W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+    xb = torch.randn(2, K, generator=torch.Generator().manual_seed(0)).to(torch.bfloat16)
+    x32 = xb.float().numpy()
+    lv = rng.integers(0, 5, N // 64).astype(np.uint8)
+    pm = pack(qam, W, sc)
+    y = host(qam.qmatvec(xb.cuda(), pm, dev(lv)))
+    check_y(y, W, sc, x32, lv, "bf16")
+
+
+def test_qmatvec_deterministic_and_leaves_workspace_clean(qam):
+    rng = np.random.default_rng(6)
+    N, K = 2048, 28672
+    W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+    x = rng.standard_normal((1, K)).astype(np.float32)
+    lv = rng.integers(0, 5, N // 64).astype(np.uint8)
+    pm = pack(qam, W, sc)
+    ws = qam.Workspace("cuda")
+    xd, lvd = dev(x), dev(lv)
+    y1 = host(qam.qmatvec(xd, pm, lvd, workspace=ws))
+    y2 = host(qam.qmatvec(xd, pm, lvd, workspace=ws))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    assert int(np.abs(host(ws.buf[:4 * 65536].view(torch.int32))).sum()) == 0   # counters reset
+    check_y(y1, W, sc, x, lv, "28672")
+
+
+def test_qmatvec_one_workspace_across_shapes(qam):
+    """Calls of different shapes share one workspace: the partials one call
+    leaves behind never disturb the next call's arrival counters."""
+    rng = np.random.default_rng(12)
+    ws = qam.Workspace("cuda")
+    for N, K, B in [(2048, 8960, 8), (8192, 4096, 1), (128, 8960, 3), (4096, 28672, 1), (64, 65536, 1),
+                    (2048, 8960, 8)]:
+        W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+        sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+        x = rng.standard_normal((B, K)).astype(np.float32)
+        lv = rng.integers(0, 5, N // 64).astype(np.uint8)
+        y = host(qam.qmatvec(dev(x), pack(qam, W, sc), dev(lv), workspace=ws))
+        check_y(y, W, sc, x, lv, (N, K, B))
+        assert int(np.abs(host(ws.buf[:4 * 65536].view(torch.int32))).sum()) == 0
+
+
+def test_qmatvec_full_size_streaming_layer_sampled_rows(qam):
+    """8192 x 28672 and 28672 x 8192 at a lens map near 4 bits, in the launch
+    configuration the benchmark uses; 384 sampled rows against the oracle."""
+    st = WL.streaming_stack(0)
+    cen, rad = WL.stack_lenses(st)
+    lv_all = O.level_map(st.coords, cen, rad, 0.3, 1.0, "sum", 5, 1)
+    offs = st.block_offsets()
+    rng = np.random.default_rng(8)
+    for i in (0, 1):
+        m = st.matrices[i]
+        W = st.codes(i)
+        sc = st.scales(i)
+        x = st.x(i)
+        lv = lv_all[offs[i]:offs[i] + m.n_blocks]
+        pm = pack(qam, W, sc)
+        y = host(qam.qmatvec(dev(x), pm, dev(lv)))
+        rows = np.sort(rng.choice(m.N, 384, replace=False))
+        Wr = W[rows]
+        # oracle on the sampled rows only: each row keeps its own block's depth
+        codes = np.stack([O.truncate(Wr[j], LADDER[lv[r // 64]]) for j, r in enumerate(rows)])
+        ref = (codes.astype(np.float64) @ x[0].astype(np.float64)) * sc[rows].astype(np.float64)
+        tol = 1e-4 * (np.abs(codes).astype(np.float64) @ np.abs(x[0]).astype(np.float64)) * sc[rows]
+        err = np.abs(y[0, rows].astype(np.float64) - ref)
+        assert np.all(err <= tol), (i, float((err / np.maximum(tol, 1e-300)).max()))
+        del pm
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_grouped_qmatvec_matches_oracle(qam, B):
+    """Several matrices with their own x, y and maps in one launch."""
+    rng = np.random.default_rng(30 + B)
+    shapes = [(1536, 1536), (6144, 1536), (1536, 6144), (64, 28672), (128, 256), (512, 8960)]
+    items, host_in = [], []
+    for i, (N, K) in enumerate(shapes):
+        W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+        sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+        x = rng.standard_normal((B, K)).astype(np.float32)
+        lv = (np.zeros(N // 64) if i == 4 else rng.integers(0, 5, N // 64)).astype(np.uint8)
+        y = torch.full((B, N), float("nan"), device="cuda")
+        items.append((pack(qam, W, sc), dev(x), y, dev(lv)))
+        host_in.append((W, sc, x, lv))
+    grp = qam.GroupedQmatvec(items)
+    grp.run()
+    first = [host(it[2]).copy() for it in items]
+    for (W, sc, x, lv), y in zip(host_in, first):
+        check_y(y, W, sc, x, lv, W.shape)
+    grp.run()
+    for it, y0 in zip(items, first):
+        assert np.array_equal(host(it[2]).view(np.uint32), y0.view(np.uint32))
