@@ -199,15 +199,20 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   the pass; [PoD]: cost counted in weight bytes read).  A ZERO block loads
  *   nothing and writes y = 0.
  *
- *   Arithmetic: each chunk of columns of x is put on an exact fixed-point
- *   grid, x~ = round(x * 2^(30-e)) * 2^(e-30) with 2^(e-1) <= max|x| < 2^e
- *   over the chunk, held as four signed int8 limbs; c . x~ is accumulated
- *   exactly in integers (int8 dot products), chunks are summed in fp64 in a
- *   fixed order, and y = fl32(scale * sum).  Hence
- *     |y - y_exact| <= 2^-30 sum_chunks max_chunk|x| sum_chunk|w| + 2^-24|y|,
- *   and results are bit-reproducible run to run.  Integer-valued x with
- *   scale 1 gives exact integer outputs; a D8 map gives the untruncated
- *   int8 product.  x must be finite.
+ *   Arithmetic: x is walked in sub-chunks of columns (at most 1536 for
+ *   B = 1, 768 for B = 2, 512 for B <= 4, 256 for B <= 8); each is put on
+ *   a fixed-point grid, x~ = round(x * 2^(22-e)) * 2^(e-22) with
+ *   2^(e-1) <= max|x| < 2^e over the sub-chunk, held as three signed int8
+ *   limbs; c . x~ is accumulated exactly in integers (int8 dot products),
+ *   sub-chunks and column chunks are summed in fp64 in a fixed order, and
+ *   y = fl32(scale * sum).  Hence
+ *     |y - y_exact| <= 2^-22 sum_sub max_sub|x| sum_sub|w| + 2^-24|y| (+ fp64),
+ *   which meets 1e-4 sum|w||x| unless the |w|-weighted mean of |x| in a
+ *   sub-chunk falls below about 2.4e-3 of that sub-chunk's largest |x|;
+ *   results are bit-reproducible run to run.  Integer-valued x with
+ *   |x| < 2^22 and scale 1 gives exact integer outputs; a D8 map gives the
+ *   untruncated int8 product.  A non-finite x makes that request's
+ *   non-ZERO outputs NaN.
  *
  *   x          (device) [B][K] row-major, fp32 (x_dtype QAM_X_F32) or bf16
  *              (QAM_X_BF16); 16-byte aligned.

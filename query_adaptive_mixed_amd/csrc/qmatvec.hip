@@ -24,6 +24,7 @@
 // The same kernel serves one matrix (descriptor passed by value) and a group
 // of matrices with independent inputs (descriptor table in device memory,
 // one table lookup per workgroup), so a whole weight field is one launch.
+#include <algorithm>
 #include <vector>
 
 #include "qam_common.h"
@@ -101,17 +102,22 @@ __device__ __forceinline__ int level_of(const uint8_t* level, int b) {
     return (int)((word >> (8 * (addr & 3))) & 0xFFu);
 }
 
-// Balanced base-256 digits of the fixed-point value of one element, as four
-// signed bytes (byte l = digit l).
+// Activations are held as three signed int8 limbs of a 24-bit fixed point
+// per sub-chunk: v = rint(x * 2^(kFrac - e)), |v| <= 2^22.
+constexpr int kLimbs = 3;
+constexpr int kFrac = 22;
+
+// Balanced base-256 digits of the fixed-point value of one element, as three
+// signed bytes (byte l = digit l; the top byte is unused).
 __device__ __forceinline__ uint32_t limbs_of(float v, int sh) {
-    const int q = (int)rintf(ldexpf(v, sh));            // |q| <= 2^30
-    return ((uint32_t)q + 0x80808080u) ^ 0x80808080u;
+    const int q = (int)rintf(ldexpf(v, sh));            // |q| <= 2^22
+    return ((uint32_t)q + 0x808080u) ^ 0x808080u;
 }
 
 // LDS index (in 16-byte units) of the limb words of 4-column group g of the
-// chunk: tile g/16, then the group's position u in the lane's 16 columns, then
-// the lane group (L >> 4) that owns it, so that the four lane groups reading
-// one u hit four consecutive 16-byte slots.
+// sub-chunk: tile g/16, then the group's position u in the lane's 16 columns,
+// then the lane group (L >> 4) that owns it, so that the four lane groups
+// reading one u hit four consecutive 16-byte slots.
 __device__ __forceinline__ int limb_slot(int g) { return (g & ~15) | ((g & 3) << 2) | ((g >> 2) & 3); }
 
 // ------------------------------------------------------------------ per-wave body
@@ -127,10 +133,21 @@ struct Ring {
     static constexpr int PF = 2 * H;                                // tiles per ring
 };
 
+// x is staged in sub-chunks of S tiles: each lane loads G = S / 4 groups of
+// four values per request, which with the first half ring keeps at most about
+// eleven loads in flight before x is used (within what the compiler's wait
+// counting tracks exactly), and the limbs of a sub-chunk take NB * S * 256
+// bytes of LDS.  S is a multiple of every ring length used with NB.
+template <int NB>
+struct Stage {
+    static constexpr int S = NB == 1 ? 24 : (NB == 2 ? 12 : (NB <= 4 ? 8 : 4));
+    static constexpr int G = S / 4;
+};
+
 // One tile: four groups of four columns, four rows each, NB requests.
 template <int NS, int NB>
 __device__ __forceinline__ void tile_dots(const u32x4* buf, const int4* __restrict__ lt, int slots,
-                                          int (&acc)[NB][4][4]) {
+                                          int (&acc)[NB][4][kLimbs]) {
     uint32_t w[4][NS];
 #pragma unroll
     for (int p = 0; p < NS; ++p) {
@@ -151,7 +168,6 @@ __device__ __forceinline__ void tile_dots(const u32x4* buf, const int4* __restri
             acc[r][j][0] = __builtin_amdgcn_sdot4(P, lm[UU][r].x, acc[r][j][0], false);         \
             acc[r][j][1] = __builtin_amdgcn_sdot4(P, lm[UU][r].y, acc[r][j][1], false);         \
             acc[r][j][2] = __builtin_amdgcn_sdot4(P, lm[UU][r].z, acc[r][j][2], false);         \
-            acc[r][j][3] = __builtin_amdgcn_sdot4(P, lm[UU][r].w, acc[r][j][3], false);         \
         }                                                                                      \
     }
     QAM_GROUP(0)
@@ -165,17 +181,18 @@ template <int NS, int H>
 __device__ __forceinline__ void load_half(u32x4 (&h)[H][NS], const uint8_t* base, int64_t pb, int tile, int last) {
 #pragma unroll
     for (int u = 0; u < H; ++u) {
-        const int t = min(tile + u, last);   // past the chunk: reload its last tile (never computed)
+        const int t = min(tile + u, last);   // past the sub-chunk: reload its last tile (never computed)
 #pragma unroll
         for (int p = 0; p < NS; ++p) h[u][p] = load_plane(base + p * pb + (int64_t)t * kTileBytes);
     }
 }
 
-// Turn this wave's chunk of x into limb words in LDS (see the file comment).
-// xv[r][i] holds the x values of group lane + 64 i of request r.
+// Turn this wave's sub-chunk of x into limb words in LDS (see the file comment).
+// xraw[r][i] holds the x values of group lane + 64 i of request r.
 template <int NB, int G, bool XBF16>
 __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngroups, int slots, int L,
                                             int4* __restrict__ lds, int (&exps)[NB], bool (&bad)[NB]) {
+    __syncthreads();   // the workgroup is this one wavefront: the last sub-chunk's LDS reads are done
     float4 xv[NB][G];
 #pragma unroll
     for (int r = 0; r < NB; ++r)
@@ -201,7 +218,7 @@ __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngro
         if (m > 0.0f) frexpf(m, &e);
         exps[r] = __builtin_amdgcn_readfirstlane(e);
         bad[r] = __builtin_amdgcn_readfirstlane(nonfinite) != 0;
-        const int sh = 30 - exps[r];
+        const int sh = kFrac - exps[r];
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             const int g = L + 64 * i;
@@ -213,111 +230,129 @@ __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngro
             out.x = (int)((w0 & 0xFFu) | ((w1 & 0xFFu) << 8) | ((w2 & 0xFFu) << 16) | (w3 << 24));
             out.y = (int)(((w0 >> 8) & 0xFFu) | (w1 & 0xFF00u) | ((w2 & 0xFF00u) << 8) | ((w3 & 0xFF00u) << 16));
             out.z = (int)(((w0 >> 16) & 0xFFu) | ((w1 >> 8) & 0xFF00u) | (w2 & 0xFF0000u) | ((w3 & 0xFF0000u) << 8));
-            out.w = (int)((w0 >> 24) | ((w1 >> 16) & 0xFF00u) | ((w2 >> 8) & 0xFF0000u) | (w3 & 0xFF000000u));
+            out.w = 0;
             lds[r * slots + limb_slot(g)] = out;
         }
     }
-    __syncthreads();   // the workgroup is this one wavefront: orders the LDS writes before the reads
+    __syncthreads();   // orders the LDS writes before the reads
 }
 
-// One wavefront: block b, column chunk `chunk`, read at NS slices.
-template <int NS, int NB, int G, bool XBF16>
+// One wavefront: block b, column chunk `chunk`, read at NS slices.  The chunk
+// is walked in sub-chunks of S tiles; each sub-chunk's exact integer sums are
+// scaled into a per-row fp64 sum (exact but for fp64 rounding across
+// sub-chunks, in a fixed order).
+template <int NS, int NB, bool XBF16>
 __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* __restrict__ lds, int b, int chunk,
                                           int L) {
     constexpr int H = Ring<NS, NB>::H;
     constexpr int PF = Ring<NS, NB>::PF;
+    constexpr int S = Stage<NB>::S;
+    constexpr int G = Stage<NB>::G;
     const int B = c.B;
     const int tile0 = chunk * a.tpc;
     const int ntile = min(a.tpc, a.n_tiles - tile0);
-    const int ngroups = ntile * 16;
-    const int slots = a.tpc * 16;
-    const int64_t col0 = (int64_t)tile0 * kTileCols;
-    const uint8_t* base = a.planes + (int64_t)b * 16 * a.K + (int64_t)tile0 * kTileBytes + L * 16;
+    const uint8_t* base0 = a.planes + (int64_t)b * 16 * a.K + (int64_t)tile0 * kTileBytes + L * 16;
     const int kg = L >> 4;
+    const int slots = S * 16;
     const int64_t pb = a.plane_bytes;
 
-    // Nothing of this wave is in flight here, so this wait is free; it tells the
-    // compiler's wait counting as much, which it cannot see through the merged
-    // control flow of the depth cases, and keeps every wait below exact.
-    __builtin_amdgcn_s_waitcnt(0);
-    // 1. x first, so that waiting for it never drains the weight loads issued after it
-    u32x4 xraw[NB][G];
+    double mine[NB];
+    bool any_bad[NB];
 #pragma unroll
-    for (int r = 0; r < NB; ++r)
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            // unconditional (clamped) loads keep the wait counts exact; groups
-            // past the chunk are never written to LDS
-            const int g = min(L + 64 * i, ngroups - 1);
-            xraw[r][i] = load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + 4 * g);
-        }
-    // 2. the first ring of weight loads, straight into the ring registers
-    // 2. the first ring of weight loads, straight into the ring registers
-    //    (every load is unconditional; tiles past the chunk are clamped)
-    const int last = ntile - 1;
-    //    (first half now; the compiler tracks at most about fifteen loads in
-    //    flight precisely, and x already takes up to eight of them)
-    u32x4 A[H][NS], Bh[H][NS];
-    __builtin_amdgcn_sched_barrier(0);   // x loads go out first ...
-    load_half<NS, H>(A, base, pb, 0, last);
-    __builtin_amdgcn_sched_barrier(0);   // ... then half a ring, and only then is x used
-    // 3. the limbs of this chunk of x, while those loads are in flight
-    int exps[NB];
-    bool bad[NB];
-    stage_limbs<NB, G, XBF16>(xraw, ngroups, slots, L, lds, exps, bad);
-    load_half<NS, H>(Bh, base, pb, H, last);
-    __builtin_amdgcn_sched_barrier(0);
-
-    int acc[NB][4][4];
-#pragma unroll
-    for (int r = 0; r < NB; ++r)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int l = 0; l < 4; ++l) acc[r][j][l] = 0;
-
-    // Steady state: every tile of these rounds is in range.  The scheduling
-    // barriers keep each reload right after the half it replaces, ahead of the
-    // other half's arithmetic, so each wait drains only the older half.
-    int t = 0;
-    for (; t + PF < ntile; t += PF) {
-#pragma unroll
-        for (int u = 0; u < H; ++u) tile_dots<NS, NB>(A[u], lds + (t + u) * 16 + kg, slots, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        load_half<NS, H>(A, base, pb, t + PF, last);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < H; ++u) tile_dots<NS, NB>(Bh[u], lds + (t + H + u) * 16 + kg, slots, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        load_half<NS, H>(Bh, base, pb, t + PF + H, last);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int r = 0; r < NB; ++r) {
+        mine[r] = 0.0;
+        any_bad[r] = false;
     }
-    // Drain: the last ring, whose tail may run past a ragged chunk.
-#pragma unroll
-    for (int u = 0; u < H; ++u)
-        if (t + u < ntile) tile_dots<NS, NB>(A[u], lds + (t + u) * 16 + kg, slots, acc);
-#pragma unroll
-    for (int u = 0; u < H; ++u)
-        if (t + H + u < ntile) tile_dots<NS, NB>(Bh[u], lds + (t + H + u) * 16 + kg, slots, acc);
 
-    // exact per-row integers, summed over the four lane groups sharing a row
+    for (int t0 = 0; t0 < ntile; t0 += S) {
+        const int nt = min(S, ntile - t0);
+        const int ngroups = nt * 16;
+        const int64_t col0 = (int64_t)(tile0 + t0) * kTileCols;
+        const uint8_t* base = base0 + (int64_t)t0 * kTileBytes;
+        const int last = nt - 1;
+        // Nothing of this wave is in flight here, so this wait is free; it tells
+        // the compiler's wait counting as much (it cannot see it through the
+        // merged control flow of the depth cases and this loop), which keeps
+        // every wait below exact.
+        __builtin_amdgcn_s_waitcnt(0);
+        // 1. x first, so that waiting for it never drains the weight loads issued
+        //    after it (unconditional, clamped loads keep the wait counts exact;
+        //    groups past the sub-chunk are never written to LDS)
+        u32x4 xraw[NB][G];
+#pragma unroll
+        for (int r = 0; r < NB; ++r)
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                const int g = min(L + 64 * i, ngroups - 1);
+                xraw[r][i] = load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + 4 * g);
+            }
+        // 2. the first half ring of weight loads, straight into the ring registers
+        u32x4 A[H][NS], Bh[H][NS];
+        __builtin_amdgcn_sched_barrier(0);   // x loads go out first ...
+        load_half<NS, H>(A, base, pb, 0, last);
+        __builtin_amdgcn_sched_barrier(0);   // ... then half a ring, and only then is x used
+        // 3. the limbs of this sub-chunk of x while those loads are in flight,
+        //    then the second half ring
+        int exps[NB];
+        bool bad[NB];
+        stage_limbs<NB, G, XBF16>(xraw, ngroups, slots, L, lds, exps, bad);
+        load_half<NS, H>(Bh, base, pb, H, last);
+        __builtin_amdgcn_sched_barrier(0);
+
+        int acc[NB][4][kLimbs];
+#pragma unroll
+        for (int r = 0; r < NB; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int l = 0; l < kLimbs; ++l) acc[r][j][l] = 0;
+
+        // Steady state: every tile of these rounds is in range.  The scheduling
+        // barriers keep each reload right after the half it replaces, ahead of
+        // the other half's arithmetic, so each wait drains only the older half.
+        int t = 0;
+        for (; t + PF < nt; t += PF) {
+#pragma unroll
+            for (int u = 0; u < H; ++u) tile_dots<NS, NB>(A[u], lds + (t + u) * 16 + kg, slots, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            load_half<NS, H>(A, base, pb, t + PF, last);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < H; ++u) tile_dots<NS, NB>(Bh[u], lds + (t + H + u) * 16 + kg, slots, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            load_half<NS, H>(Bh, base, pb, t + PF + H, last);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Drain: the last ring, whose tail may run past a ragged sub-chunk.
+#pragma unroll
+        for (int u = 0; u < H; ++u)
+            if (t + u < nt) tile_dots<NS, NB>(A[u], lds + (t + u) * 16 + kg, slots, acc);
+#pragma unroll
+        for (int u = 0; u < H; ++u)
+            if (t + H + u < nt) tile_dots<NS, NB>(Bh[u], lds + (t + H + u) * 16 + kg, slots, acc);
+
+        // exact per-row integers, summed over the four lane groups sharing a
+        // row, scaled by this sub-chunk's exponent into the row's fp64 sum
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {
+            double d[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                d[j] = (double)acc[r][j][2] * 65536.0 + (double)acc[r][j][1] * 256.0 + (double)acc[r][j][0];
+                d[j] += __shfl_xor(d[j], 16);
+                d[j] += __shfl_xor(d[j], 32);
+            }
+            const double sel = kg == 0 ? d[0] : (kg == 1 ? d[1] : (kg == 2 ? d[2] : d[3]));
+            mine[r] += ldexp(sel, exps[r] - kFrac);
+            any_bad[r] = any_bad[r] || bad[r];
+        }
+    }
+
     const int row = b * kRows + L;          // the row this lane writes: j = L >> 4
     const float sc = a.scales[row];
     double part[NB];
 #pragma unroll
-    for (int r = 0; r < NB; ++r) {
-        double d[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            d[j] = (double)acc[r][j][3] * 16777216.0 + (double)acc[r][j][2] * 65536.0 +
-                   (double)acc[r][j][1] * 256.0 + (double)acc[r][j][0];
-            d[j] += __shfl_xor(d[j], 16);
-            d[j] += __shfl_xor(d[j], 32);
-        }
-        const double mine = kg == 0 ? d[0] : (kg == 1 ? d[1] : (kg == 2 ? d[2] : d[3]));
-        // a non-finite x in the chunk makes that request's outputs NaN
-        part[r] = bad[r] ? __builtin_nan("") : ldexp(mine, exps[r] - 30);
-    }
+    for (int r = 0; r < NB; ++r) part[r] = any_bad[r] ? __builtin_nan("") : mine[r];   // non-finite x: NaN
 
     if (a.n_chunks == 1) {
 #pragma unroll
@@ -351,18 +386,10 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     if (L == 0) __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Groups of four x values one lane stages per request (tpc / 4, 64 lanes).
-// With the first half ring this keeps at most about eleven loads in flight
-// before x is used, within what the compiler's wait counting tracks exactly.
-template <int NB>
-struct Stage {
-    static constexpr int G = NB == 1 ? 6 : (NB == 2 ? 3 : (NB <= 4 ? 2 : 1));   // tpc <= 24, 12, 8, 4
-};
-
 // One workgroup = one wavefront = one (block, column chunk) of one matrix.
 template <int NB, bool GROUPED, bool XBF16>
 __global__ __launch_bounds__(64) void qmatvec_kernel(Item single, Common c) {
-    extern __shared__ int4 lds[];           // [NB][tpc * 16] limb words of this wave's chunk
+    extern __shared__ int4 lds[];           // [NB][S * 16] limb words of this wave's sub-chunk
     Item a;
     int local;
     if constexpr (GROUPED) {
@@ -378,17 +405,16 @@ __global__ __launch_bounds__(64) void qmatvec_kernel(Item single, Common c) {
     const int L = threadIdx.x;
     const int lev = level_of(a.level, b);
     const int ns = __builtin_amdgcn_readfirstlane(lev < 4 ? lev : 4);
-    constexpr int G = Stage<NB>::G;
     switch (ns) {
         case 0:   // ZERO: nothing read, y = 0 (written once, by the first chunk)
             if (chunk == 0)
 #pragma unroll
                 for (int r = 0; r < NB; ++r) a.y[(int64_t)r * a.N + (int64_t)b * kRows + L] = 0.0f;
             return;
-        case 1: wave_body<1, NB, G, XBF16>(a, c, lds, b, chunk, L); return;
-        case 2: wave_body<2, NB, G, XBF16>(a, c, lds, b, chunk, L); return;
-        case 3: wave_body<3, NB, G, XBF16>(a, c, lds, b, chunk, L); return;
-        default: wave_body<4, NB, G, XBF16>(a, c, lds, b, chunk, L); return;
+        case 1: wave_body<1, NB, XBF16>(a, c, lds, b, chunk, L); return;
+        case 2: wave_body<2, NB, XBF16>(a, c, lds, b, chunk, L); return;
+        case 3: wave_body<3, NB, XBF16>(a, c, lds, b, chunk, L); return;
+        default: wave_body<4, NB, XBF16>(a, c, lds, b, chunk, L); return;
     }
 }
 
@@ -399,34 +425,31 @@ struct Plan {
     size_t partial_bytes;
 };
 
-static int g_target_waves = 256 * 16;   // wavefronts aimed for per launch
+static int64_t g_target_waves = 256 * 32;   // wavefronts aimed for per launch
 
-// LDS holds B x tpc x 256 bytes of limbs; one lane stages at most
-// Stage<B>::G groups of four x values, so tpc <= 4 G
-static int max_tpc_for(int64_t B) { return B > 4 ? 4 : (B > 2 ? 8 : (B > 1 ? 12 : 24)); }
-// every full chunk holds a whole number of prefetch rings (Ring<NS, B>::PF for every NS)
+// every chunk holds a whole number of prefetch rings (Ring<NS, B>::PF for every NS)
 static int tpc_align_for(int64_t B) { return B == 1 ? 8 : (B == 2 ? 4 : 2); }
+static int stage_tiles_for(int64_t B) { return B == 1 ? 24 : (B == 2 ? 12 : (B <= 4 ? 8 : 4)); }
+static size_t lds_bytes_for(int64_t B) { return (size_t)B * stage_tiles_for(B) * 16 * sizeof(int4); }
 
-// Chunking of one matrix.  `blocks_in_launch` is the number of blocks the
-// whole launch covers (the matrix itself, or every matrix of a group): K is
-// split until the launch has about g_target_waves wavefronts, with at least
-// four tiles per chunk and at most max_tpc_for(B) (LDS budget).
-static Plan make_plan(int64_t N, int64_t K, int64_t B, int64_t blocks_in_launch) {
+// Column chunk length (in tiles) for a launch covering `block_tiles` block x
+// tile pairs: enough chunks for about g_target_waves wavefronts of equal work.
+static int chunk_goal(int64_t block_tiles) {
+    const int64_t g = (block_tiles + g_target_waves - 1) / g_target_waves;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(g, QAM_MAX_K / kTileCols));
+}
+
+// Chunking of one matrix: K is cut into the fewest chunks of at most `goal`
+// tiles, evened out and rounded up to a whole number of prefetch rings.
+static Plan make_plan(int64_t N, int64_t K, int64_t B, int goal) {
     Plan p{};
     const int n_blocks = (int)(N / kRows);
     const int n_tiles = (int)(K / kTileCols);
-    const int max_tpc = max_tpc_for(B);
     const int align = tpc_align_for(B);
-    long want = (long)((g_target_waves + blocks_in_launch - 1) / blocks_in_launch);
-    long max_chunks = n_tiles / align;
-    if (max_chunks < 1) max_chunks = 1;
-    if (want > max_chunks) want = max_chunks;
-    if (want < 1) want = 1;
-    int tpc = (int)((n_tiles + want - 1) / want);
+    const int want = (n_tiles + goal - 1) / goal;
+    int tpc = (n_tiles + want - 1) / want;
     tpc = (tpc + align - 1) / align * align;
-    if (tpc > max_tpc) tpc = max_tpc;
     if (tpc > n_tiles) tpc = n_tiles;
-    if (tpc < 1) tpc = 1;
     p.tpc = tpc;
     p.n_chunks = (n_tiles + tpc - 1) / tpc;
     p.n_quads = n_blocks;   // one wavefront-sized workgroup per block and chunk
@@ -503,7 +526,7 @@ extern "C" size_t qam_qmatvec_workspace_bytes(int64_t N, int64_t K, int64_t B) {
     if (N <= 0 || K <= 0 || N % kRows || K % kTileCols || K > QAM_MAX_K || N / kRows > QAM_MAX_BLOCKS || B < 1 ||
         B > QAM_MAX_BATCH)
         return 0;
-    const Plan p = make_plan(N, K, B, N / kRows);
+    const Plan p = make_plan(N, K, B, chunk_goal(N / kRows * (K / kTileCols)));
     return p.n_chunks > 1 ? QAM_WS_COUNTER_BYTES + p.partial_bytes : 0;
 }
 
@@ -519,7 +542,7 @@ extern "C" int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_pack
     clear_error();
     if (int rc = check_item(x, x_dtype, B, packed, level_map, y, "qmatvec")) return rc;
     if (per_request_maps != 0) QAM_FAIL(QAM_ERR_ARG, "qmatvec: per-request maps are not taken by this entry point");
-    const Plan p = make_plan(packed->N, packed->K, B, packed->n_blocks);
+    const Plan p = make_plan(packed->N, packed->K, B, chunk_goal(packed->n_blocks * (packed->K / kTileCols)));
     Item it = make_item(x, packed, level_map, y, p);
     if (p.n_chunks > 1) {
         const size_t need = QAM_WS_COUNTER_BYTES + p.partial_bytes;
@@ -533,7 +556,7 @@ extern "C" int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_pack
     c.B = (int)B;
     c.x_bf16 = x_dtype == QAM_X_BF16;
     const int64_t grid = (int64_t)p.n_chunks * p.n_quads;
-    launch<false>(B, it, c, grid, (size_t)B * p.tpc * 16 * sizeof(int4), s);
+    launch<false>(B, it, c, grid, lds_bytes_for(B), s);
     QAM_HIP_CHECK(hipGetLastError());
     char v[128];
     snprintf(v, sizeof(v), "qmatvec_dot4 B=%lld tpc=%d chunks=%d", (long long)B, p.tpc, p.n_chunks);
@@ -548,8 +571,7 @@ namespace qam {
 struct GroupLayout {
     std::vector<Plan> plans;
     size_t partial_bytes = 0, table_bytes = 0, map_bytes = 0, total = 0;
-    int64_t n_wg = 0, blocks = 0;
-    int max_tpc = 0;
+    int64_t n_wg = 0, blocks = 0, block_tiles = 0;
 };
 
 static int layout_group(const qam_gemv_item* items, int n_items, int64_t B, GroupLayout& g) {
@@ -560,14 +582,14 @@ static int layout_group(const qam_gemv_item* items, int n_items, int64_t B, Grou
         if (w.N <= 0 || w.N % kRows || w.K <= 0 || w.K % kTileCols || w.K > QAM_MAX_K)
             QAM_FAIL(QAM_ERR_SHAPE, "group: item %d has a bad shape", i);
         g.blocks += w.N / kRows;
+        g.block_tiles += w.N / kRows * (w.K / kTileCols);
     }
     if (g.blocks > QAM_MAX_BLOCKS) QAM_FAIL(QAM_ERR_SHAPE, "group: %lld blocks > %d", (long long)g.blocks, QAM_MAX_BLOCKS);
     for (int i = 0; i < n_items; ++i) {
-        const Plan p = make_plan(items[i].w.N, items[i].w.K, B, g.blocks);
+        const Plan p = make_plan(items[i].w.N, items[i].w.K, B, chunk_goal(g.block_tiles));
         g.plans.push_back(p);
         g.partial_bytes += p.partial_bytes;
         g.n_wg += (int64_t)p.n_chunks * p.n_quads;
-        if (p.tpc > g.max_tpc) g.max_tpc = p.tpc;
     }
     if (g.n_wg > 0x7FFFFFFF) QAM_FAIL(QAM_ERR_SHAPE, "group: too many workgroups");
     g.table_bytes = ((size_t)n_items * sizeof(Item) + 255) / 256 * 256;
@@ -625,7 +647,7 @@ extern "C" int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B
     group_out->B = B;
     group_out->x_dtype = x_dtype;
     group_out->n_workgroups = g.n_wg;
-    group_out->lds_bytes = (size_t)B * g.max_tpc * 16 * sizeof(int4);
+    group_out->lds_bytes = lds_bytes_for(B);
     group_out->table = table;
     group_out->wg_map = wgmap;
     return QAM_OK;

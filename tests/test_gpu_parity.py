@@ -211,6 +211,43 @@ def test_qmatvec_exact_integer_cases(qam):
             assert np.all(np.abs(want) < 2 ** 24)
 
 
+def test_qmatvec_large_integer_x_rounds_once(qam):
+    """Integer x up to 2^21 in magnitude sits on the fixed-point grid exactly,
+    so the only rounding is the final fp32 one: y == fl32(exact int64 sum)."""
+    rng = np.random.default_rng(22)
+    for N, K, B in [(256, 4096, 1), (128, 1600 - 1600 % 64, 3), (64, 12288, 8)]:
+        W = rng.integers(-128, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+        x = rng.integers(-(2 ** 21), 2 ** 21, size=(B, K)).astype(np.float32)
+        x[:, 0] = -(2 ** 21)
+        pm = pack(qam, W, np.ones(N, np.float32))
+        lv = rng.integers(0, 5, N // 64).astype(np.uint8)
+        lv[0] = 4
+        y = host(qam.qmatvec(dev(x), pm, dev(lv)))
+        codes = np.concatenate([O.truncate(W[64 * b:64 * b + 64], LADDER[lv[b]]) for b in range(N // 64)])
+        want = (x.astype(np.int64) @ codes.T).astype(np.float32)
+        assert np.array_equal(y, want), (N, K, B)
+
+
+def test_qmatvec_error_within_fixed_point_bound(qam):
+    """Adversarial x (one huge element per row of x whose weight is zero, the
+    rest O(1)) still obeys the kernel's stated fixed-point bound
+    2^-22 max|x| sum|w| + 2^-24 |y|, the bound that holds for any x."""
+    rng = np.random.default_rng(23)
+    N, K = 128, 1024
+    W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    W[:, 7] = 0
+    sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+    x = rng.standard_normal((2, K)).astype(np.float32)
+    x[:, 7] = 3.0e4
+    lv = np.array([4, 4], np.uint8)
+    pm = pack(qam, W, sc)
+    y = host(qam.qmatvec(dev(x), pm, dev(lv)))
+    ref = O.qmatvec_ref(W, sc, x, lv)
+    aw = np.abs(W.astype(np.float64)) * sc[:, None].astype(np.float64)
+    bound = 2.0 ** -22 * np.abs(x).max(axis=1)[:, None] * aw.sum(axis=1)[None, :] + 2.0 ** -24 * np.abs(ref)
+    assert np.all(np.abs(y - ref) <= bound)
+
+
 def test_qmatvec_edge_cases(qam):
     rng = np.random.default_rng(4)
     N, K = 256, 1024
@@ -338,3 +375,56 @@ def test_grouped_qmatvec_matches_oracle(qam, B):
     grp.run()
     for it, y0 in zip(items, first):
         assert np.array_equal(host(it[2]).view(np.uint32), y0.view(np.uint32))
+
+
+def test_graph_replays_match_eager(qam):
+    """A captured step (level map + grouped product + a split-K single product)
+    replayed several times, with eager work and synchronisations between the
+    replays, gives exactly the eager result every time."""
+    rng = np.random.default_rng(40)
+    coords = rng.uniform(0, 1, size=(2 * 24 + 16, 2))
+    cen, rad = coords[[3, 40]], np.array([0.2, 0.3])
+    cd = dev(coords)
+    lv = qam.build_level_map(cd, cen, rad, 0.6, 1.0, "sum", 1)
+    mats = [(1536, 1536), (1536, 6144), (1024, 28672)]
+    items, offs, o = [], [], 0
+    for N, K in mats:
+        W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+        sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+        x = dev(rng.standard_normal((1, K)).astype(np.float32))
+        items.append((pack(qam, W, sc), x, torch.empty((1, N), device="cuda"), lv[o:o + N // 64]))
+        o += N // 64
+    grp = qam.GroupedQmatvec(items[:2])
+    single = items[2]
+    ws = qam.Workspace("cuda")
+    y_single = torch.empty((1, 1024), device="cuda")
+
+    def step():
+        qam.build_level_map(cd, cen, rad, 0.6, 1.0, "sum", 1, out=lv)
+        grp.run()
+        qam.qmatvec(single[1], single[0], single[3], y=y_single, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    want = [host(it[2]).copy() for it in items[:2]] + [host(y_single).copy()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for it in items[:2]:
+            it[2].fill_(float("nan"))
+        y_single.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host(it[2]) for it in items[:2]] + [host(y_single)]
+        for a, b in zip(got, want):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), rep
+        step()                                 # eager work between replays
+        torch.cuda.synchronize()
