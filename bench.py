@@ -162,6 +162,128 @@ def run_field(args, torch, Q, WL):
                 key=f"{args.workload}_{args.mean_bits}_g{lens.glass}_b{args.batch}")
 
 
+# ----------------------------------------------------------------- decode
+
+QWEN = dict(n_layers=28, hidden=1024, q_dim=2048, kv_dim=1024, ffn=3072, vocab=151936)
+
+
+def run_decode(args, torch, Q, WL):
+    """Qwen3-0.6B-shaped decode: T steps, each every block at D4 (top 4 bits),
+    the 16% most uncertain steps (seeded synthetic scores) run again at D8.
+    Each rung's step is one captured HIP graph of 4 x 28 + 1 fused products."""
+    from query_adaptive_mixed_amd.decode import build_decoder
+    c = QWEN
+    T = args.decode_steps
+    fld = WL.qwen_decode_field(0)
+    t0 = time.time()
+    dec = build_decoder(fld, c["n_layers"], c["hidden"], c["q_dim"], c["kv_dim"], c["ffn"], eps=1e-6,
+                        target_waves=args.decode_waves,
+                        progress=lambda l: log(f"  packed layer {l + 1}/28 ({time.time() - t0:.1f} s)") if l % 7 == 6 else None)
+    xs = torch.from_numpy(WL.decode_inputs(0, T, c["hidden"])).cuda()
+    esc = Q.escalation_schedule(WL.escalation_scores(0, T), 0.16)
+    n_esc = int(esc.sum())
+    wb = {r: sum(64 * m.K * m.n_blocks * Q.LADDER_BITS[r] // 8 for m in fld.matrices) for r in (2, 4)}
+    dec.capture(2)
+    dec.capture(4)
+    # per-rung step time: events around replays on the launch stream
+    per = {}
+    for rung in (2, 4):
+        for _ in range(5):
+            dec.hidden.copy_(xs[0])
+            dec.replay(rung)
+        ev = []
+        for i in range(30):
+            dec.hidden.copy_(xs[i % T])
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dec.replay(rung)
+            b.record()
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        per[rung] = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    # the decode run: T tokens, escalated steps re-run at D8
+    for t in range(min(T, 8)):
+        dec.hidden.copy_(xs[t])
+        dec.replay(2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(T):
+        dec.hidden.copy_(xs[t])
+        dec.replay(2)
+        if esc[t]:
+            dec.hidden.copy_(xs[t])
+            dec.replay(4)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total = T * wb[2] + n_esc * wb[4]
+    return {
+        "workload": "qwen_decode",
+        "description": "Qwen3-0.6B-shaped decode: 28 x {q|k|v 4096x1024, o 1024x2048, gate|up 6144x1024, "
+                       "down 1024x3072} + lm_head 151936x1024, int8; batch 1",
+        "steps": T,
+        "escalated_steps": n_esc,
+        "tokens_per_s": round(T / wall, 2),
+        "ms_per_token": round(wall * 1e3 / T, 5),
+        "weight_bytes_per_token": int(total // T),
+        "mean_bits_read_per_token": round(8.0 * total / T / wb[4], 6),
+        "byte_ratio_vs_all_8bit": round(total / (T * wb[4]), 8),
+        "achieved_weight_GBps": round(total / wall / 1e9, 2),
+        "d4_step_ms": round(per[2], 5), "d8_step_ms": round(per[4], 5),
+        "d4_step_GBps": round(wb[2] / per[2] / 1e6, 2), "d8_step_GBps": round(wb[4] / per[4] / 1e6, 2),
+        "launches_per_step": 4 * c["n_layers"] + 1,
+        "timing": "HIP graph per rung (captured by libqam), replayed per step; wall clock over all steps",
+        "_fld": fld, "_esc": esc, "_wb": wb,
+    }
+
+
+def decode_cpu_baseline(res, args):
+    """The oracle's decode step (fp64 products + glue) on 2 of 28 layers and the
+    head, scaled to the whole step; tokens/s at the same escalation rate."""
+    import oracle as O
+    from query_adaptive_mixed_amd.decode import interleave_gate_up, stack_rows
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    import workloads as WL
+    fld = res["_fld"]
+    c = QWEN
+    n_sample = 2
+    mats = []
+    for l in range(n_sample):
+        cc = [fld.codes(7 * l + j) for j in range(7)]
+        ss = [fld.scales(7 * l + j) for j in range(7)]
+        mats.append([(stack_rows(cc[0], cc[1], cc[2]), stack_rows(ss[0], ss[1], ss[2])), (cc[3], ss[3]),
+                     (interleave_gate_up(cc[4], cc[5]), interleave_gate_up(ss[4], ss[5])), (cc[6], ss[6])])
+    Wl, sl = fld.codes(7 * c["n_layers"]), fld.scales(7 * c["n_layers"])
+    x0 = WL.decode_inputs(0, 1, c["hidden"])
+
+    def step(rung):
+        lv = lambda W: np.full(W.shape[0] // 64, rung, np.uint8)
+        h = x0.astype(np.float64)
+        t0 = time.perf_counter()
+        for (Wq, sq), (Wo, so), (Wg, sg), (Wd, sd) in mats:
+            qkv = O.qmatvec_ref(Wq, sq, O.rmsnorm_ref(h), lv(Wq))
+            h = h + O.qmatvec_ref(Wo, so, qkv[:, :c["q_dim"]], lv(Wo))
+            gu = O.qmatvec_ref(Wg, sg, O.rmsnorm_ref(h), lv(Wg)).reshape(-1, 64)
+            m = O.silu_mul_ref(gu[:, :32].reshape(1, -1), gu[:, 32:].reshape(1, -1))
+            h = h + O.qmatvec_ref(Wd, sd, m, lv(Wd))
+        t_layers = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.qmatvec_ref(Wl, sl, O.rmsnorm_ref(h), lv(Wl))
+        t_head = time.perf_counter() - t0
+        return t_layers * c["n_layers"] / n_sample + t_head, t_layers + t_head
+
+    t4, s4 = step(2)
+    t8, s8 = step(4)
+    T, n_esc = res["steps"], res["escalated_steps"]
+    per_token = (T * t4 + n_esc * t8) / T
+    return {"value": round(1.0 / per_token, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one fp64 oracle step at D4 and one at D8 over {n_sample} of 28 layers plus the full "
+                      f"lm_head ({s4 + s8:.1f} s of CPU), scaled to 28 layers and to {n_esc} of {T} steps re-run at D8"}
+
+
 # ----------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(res, args):
@@ -235,13 +357,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="e2b_field", choices=["e2b_field", "streaming_stack", "copy_probe"])
+    ap.add_argument("--workload", default="e2b_field",
+                    choices=["e2b_field", "streaming_stack", "qwen_decode", "copy_probe"])
     ap.add_argument("--mean-bits", type=float, default=4.0)
     ap.add_argument("--glass", type=int, default=1)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a captured step")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode tokens/s leg of the default run")
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-waves", type=int, default=0, help="decoder launch width goal (0 = library default)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -261,6 +387,20 @@ def main():
     log(f"device: {torch.cuda.get_device_name(0)}")
     if args.workload == "copy_probe":
         return copy_probe(args, torch)
+    if args.workload == "qwen_decode":
+        d = run_decode(args, torch, Q, WL)
+        out = {
+            "metric": "achieved HBM GB/s (% of peak) and decode tokens/s at mean bits/weight",
+            "value": d["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": d["steps"], "warmup": 8,
+            "ms_per_step": d["ms_per_token"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "int8 codes x fp32 activations (exact int8 dot4 on 24-bit fixed-point x), fp32 out",
+            "data": "synthetic (seeded codes, scales, step inputs and escalation scores)",
+            "config": {k: v for k, v in d.items() if not k.startswith("_")},
+        }
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = decode_cpu_baseline(d, args)
+        print(json.dumps(out), flush=True)
+        return
     res = run_field(args, torch, Q, WL)
     gbs = res["wbytes"] / (res["ms"] * 1e-3) / 1e9
     kern_bytes = res["wbytes"] + res["other"]
@@ -305,6 +445,11 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(res, args)
+    if not args.no_decode and args.workload == "e2b_field" and args.batch == 1:
+        log("decode leg: Qwen3-0.6B-shaped, 256 steps ...")
+        del res
+        d = run_decode(args, torch, Q, WL)
+        out["decode"] = {k: v for k, v in d.items() if not k.startswith("_")}
     print(json.dumps(out), flush=True)
 
 

@@ -238,6 +238,46 @@ int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_packed* packed,
                 const uint8_t* level_map, int per_request_maps, float* y,
                 void* workspace, size_t workspace_bytes, hipStream_t s);
 
+/* ---------------------------------------------------------------- fused epilogues */
+/*
+ * qam_qmatvec_ep -- qam_qmatvec with the glue of a decode step folded into
+ *   the product's last stage, so a decoder layer is one launch per matrix.
+ *   None of this is from the pages: it is the plainest stand-in for the
+ *   normalisation and gated activation around the weight reads of the
+ *   decoder-only model the [PoD] abstract decodes (Qwen3-0.6B), so that a
+ *   decode step can be timed as tokens/s with no kernel other than the
+ *   mixed-depth product.
+ *
+ *   With v[r][n] = scale[n] * sum_k c[n][k] x'[r][k], where
+ *     x' = x                                 (ep->rms_norm == 0)
+ *     x' = x / sqrt(mean_k x[r][k]^2 + eps)   (ep->rms_norm == 1; the factor
+ *          is applied to the exact row sum, computed in fp64 over all K),
+ *   the output is
+ *     QAM_OUT_STORE: y[r][n] = fl32(v)
+ *     QAM_OUT_ADD:   y[r][n] = fl32(y[r][n] + v)        (residual; y is read)
+ *     QAM_OUT_GLU:   block b's rows 64b..64b+31 are gate rows and rows
+ *                    64b+32..64b+63 the up rows of features 32b..32b+31;
+ *                    y[r][32b+i] = fl32(silu(v_gate) * v_up), silu(t) =
+ *                    t / (1 + e^-t), in fp64; y is [B][N/2].
+ *   A ZERO block reads nothing: v = 0 for its rows (QAM_OUT_ADD leaves y as
+ *   it is, QAM_OUT_GLU writes 0).  Other arguments, the workspace and the
+ *   error bound (on v) are those of qam_qmatvec; y must not overlap x.
+ *   ep == NULL is qam_qmatvec with a shared map.
+ */
+#define QAM_OUT_STORE 0
+#define QAM_OUT_ADD   1
+#define QAM_OUT_GLU   2
+
+typedef struct qam_epilogue {
+    int    rms_norm;   /* 0 or 1                                  */
+    int    out_mode;   /* QAM_OUT_STORE, QAM_OUT_ADD, QAM_OUT_GLU */
+    double eps;        /* >= 0, used when rms_norm == 1           */
+} qam_epilogue;
+
+int qam_qmatvec_ep(const void* x, int x_dtype, int64_t B, const qam_packed* packed,
+                   const uint8_t* level_map, const qam_epilogue* ep, float* y,
+                   void* workspace, size_t workspace_bytes, hipStream_t s);
+
 /* ---------------------------------------------------------------- grouped qmatvec */
 /*
  * A group runs qam_qmatvec over many matrices, each with its own x, y and
@@ -286,6 +326,95 @@ int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dty
  *   group must be ordered.
  */
 int qam_qmatvec_group(const qam_group* group, hipStream_t s);
+
+/* ---------------------------------------------------------------- decode driver */
+/*
+ * A decode step of a decoder-only model in which every weight read is the
+ * mixed-depth product at one uniform depth per step ([PoD] abstract: the
+ * 8-bit weights are read with their top 4 bits, and a step whose output looks
+ * uncertain is run again at 8 bits; the cost is weight bytes read per token).
+ * The step is a chain of 4 n_layers + 1 qam_qmatvec_ep launches and nothing
+ * else; per layer, with h the hidden state [hidden]:
+ *   qkv = W_qkv rms(h)          QAM_OUT_STORE; rows: q_dim queries, then
+ *                               kv_dim keys and kv_dim values
+ *   h  += W_o qkv[0 : q_dim]    QAM_OUT_ADD; the query part stands in for the
+ *                               attention output (weights are synthetic)
+ *   m   = glu(W_gu rms(h))      QAM_OUT_GLU; W_gu rows interleaved per block:
+ *                               32 gate rows, then the 32 matching up rows
+ *   h  += W_down m              QAM_OUT_ADD
+ * and finally logits = W_lm rms(h).  rms(v) = v / sqrt(mean(v^2) + eps).
+ */
+typedef struct qam_decoder_layer {
+    qam_packed qkv;       /* [q_dim + 2 kv_dim][hidden] */
+    qam_packed o;         /* [hidden][q_dim]            */
+    qam_packed gate_up;   /* [2 ffn][hidden], interleaved per 64-row block */
+    qam_packed down;      /* [hidden][ffn]              */
+} qam_decoder_layer;
+
+typedef struct qam_decoder_desc {
+    int                      n_layers;
+    int64_t                  hidden, q_dim, kv_dim, ffn, vocab;   /* multiples of 64 (ffn of 32) */
+    const qam_decoder_layer* layers;        /* (host) [n_layers]; descriptors are copied */
+    qam_packed               lm_head;       /* [vocab][hidden] */
+    double                   eps;           /* RMS epsilon, >= 0 */
+    int                      target_waves;  /* launch width goal per matrix; 0 = 2048 */
+} qam_decoder_desc;
+
+typedef struct qam_decoder qam_decoder;     /* opaque host object */
+
+/* Device bytes qam_decoder_create needs (0 if the description is invalid). */
+size_t qam_decoder_bytes(const qam_decoder_desc* d);
+
+/*
+ * qam_decoder_create -- validate the shapes, lay out the step's buffers in
+ *   dev_mem (caller-owned, qam_decoder_bytes bytes, 256-byte aligned, kept
+ *   alive while the decoder lives): split-K workspace, h, qkv, m, logits and
+ *   one uniform level map per rung.  Fills the maps and zeroes the counters
+ *   on `s`, then synchronises `s`.  The packed weights must stay alive.
+ */
+int qam_decoder_create(const qam_decoder_desc* d, void* dev_mem, size_t dev_bytes,
+                       qam_decoder** out, hipStream_t s);
+
+/* (device) the step's buffers: QAM_DEC_H h [hidden] (the step reads its
+ * input here and leaves the final h), QAM_DEC_QKV [q_dim + 2 kv_dim],
+ * QAM_DEC_M [ffn], QAM_DEC_LOGITS [vocab]; NULL for an unknown id. */
+#define QAM_DEC_H      0
+#define QAM_DEC_QKV    1
+#define QAM_DEC_M      2
+#define QAM_DEC_LOGITS 3
+float* qam_decoder_buffer(qam_decoder* dec, int which);
+
+/* qam_decoder_step -- enqueue one step with every block read at `rung`
+ *   (0..4 of {0,2,4,6,8}; 2 = D4, 4 = D8).  Kernels only: capturable. */
+int qam_decoder_step(qam_decoder* dec, int rung, hipStream_t s);
+
+/* qam_decoder_run -- enqueue products first .. first+count-1 of the step's
+ *   chain (4 per layer in the order qkv, o, gate_up, down, then the head),
+ *   exactly as qam_decoder_step launches them; for inspecting one product's
+ *   inputs and outputs. */
+int qam_decoder_run(qam_decoder* dec, int rung, int first, int count, hipStream_t s);
+
+/* qam_decoder_capture -- capture qam_decoder_step(dec, rung) on `s` (not the
+ *   null stream) as a HIP graph kept by the decoder (replaces any earlier
+ *   graph of that rung); qam_decoder_replay launches it on any stream. */
+int qam_decoder_capture(qam_decoder* dec, int rung, hipStream_t s);
+int qam_decoder_replay(qam_decoder* dec, int rung, hipStream_t s);
+
+/* Frees the host object and its graphs (not dev_mem). */
+void qam_decoder_destroy(qam_decoder* dec);
+
+/*
+ * qam_escalation_schedule -- which of T decode steps are run again at 8 bits
+ *   ([PoD] abstract: escalate the uncertain steps).  Exactly
+ *   floor(rate * T + 0.5) steps are marked: those with the largest score,
+ *   ties going to the earlier step.  Host only.
+ *   scores        (host) fp64 [T], finite.
+ *   rate          in [0, 1].
+ *   escalate_out  (host) uint8 [T]: 1 = re-run at 8 bits.
+ *   n_out         (host, may be NULL) the number marked.
+ */
+int qam_escalation_schedule(const double* scores, int64_t T, double rate, uint8_t* escalate_out,
+                            int64_t* n_out);
 
 /* ---------------------------------------------------------------- diagnostics */
 const char* qam_last_error(void);     /* thread-local, "" if none           */

@@ -9,10 +9,12 @@ loudly if the library is missing.
 
 from .api import (  # noqa: F401
     LADDER_BITS,
+    Decoder,
     GroupedQmatvec,
     PackedMatrix,
     Workspace,
     build_level_map,
+    escalation_schedule,
     last_variant,
     map_weight_bytes,
     pack_slices,

@@ -21,6 +21,7 @@ QAM_MAX_BATCH = 8
 QAM_MAX_K = 65536
 QAM_X_F32, QAM_X_BF16 = 0, 1
 QAM_COMBINE_SUM, QAM_COMBINE_MAX = 0, 1
+QAM_OUT_STORE, QAM_OUT_ADD, QAM_OUT_GLU = 0, 1, 2
 
 
 class QamPacked(C.Structure):
@@ -46,6 +47,20 @@ class QamGroup(C.Structure):
                 ("lds_bytes", C.c_size_t), ("table", C.c_void_p), ("wg_map", C.c_void_p)]
 
 
+class QamEpilogue(C.Structure):
+    _fields_ = [("rms_norm", C.c_int), ("out_mode", C.c_int), ("eps", C.c_double)]
+
+
+class QamDecoderLayer(C.Structure):
+    _fields_ = [("qkv", QamPacked), ("o", QamPacked), ("gate_up", QamPacked), ("down", QamPacked)]
+
+
+class QamDecoderDesc(C.Structure):
+    _fields_ = [("n_layers", C.c_int), ("hidden", C.c_int64), ("q_dim", C.c_int64), ("kv_dim", C.c_int64),
+                ("ffn", C.c_int64), ("vocab", C.c_int64), ("layers", C.POINTER(QamDecoderLayer)),
+                ("lm_head", QamPacked), ("eps", C.c_double), ("target_waves", C.c_int)]
+
+
 class QamError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__(f"{ERRORS.get(code, code)}: {msg}")
@@ -63,6 +78,16 @@ SIGNATURES = [
     ("qam_map_weight_bytes", _I, [_P, _I64, _I64, _P, _I, C.POINTER(_D), C.POINTER(_I64)]),
     ("qam_qmatvec_workspace_bytes", C.c_size_t, [_I64, _I64, _I64]),
     ("qam_qmatvec", _I, [_P, _I, _I64, C.POINTER(QamPacked), _P, _I, _P, _P, _SZ, _P]),
+    ("qam_qmatvec_ep", _I, [_P, _I, _I64, C.POINTER(QamPacked), _P, C.POINTER(QamEpilogue), _P, _P, _SZ, _P]),
+    ("qam_decoder_bytes", C.c_size_t, [C.POINTER(QamDecoderDesc)]),
+    ("qam_decoder_create", _I, [C.POINTER(QamDecoderDesc), _P, _SZ, C.POINTER(_P), _P]),
+    ("qam_decoder_buffer", _P, [_P, _I]),
+    ("qam_decoder_step", _I, [_P, _I, _P]),
+    ("qam_decoder_run", _I, [_P, _I, _I, _I, _P]),
+    ("qam_decoder_capture", _I, [_P, _I, _P]),
+    ("qam_decoder_replay", _I, [_P, _I, _P]),
+    ("qam_decoder_destroy", None, [_P]),
+    ("qam_escalation_schedule", _I, [_P, _I64, _D, _P, C.POINTER(_I64)]),
     ("qam_group_bytes", C.c_size_t, [C.POINTER(QamGemvItem), _I, _I64]),
     ("qam_group_init", _I, [C.POINTER(QamGemvItem), _I, _I64, _I, _P, _SZ, C.POINTER(QamGroup), _P]),
     ("qam_qmatvec_group", _I, [C.POINTER(QamGroup), _P]),

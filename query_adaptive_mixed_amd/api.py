@@ -160,9 +160,17 @@ def default_workspace(device) -> Workspace:
     return _WS[key]
 
 
+_OUT_MODES = {"store": L.QAM_OUT_STORE, "add": L.QAM_OUT_ADD, "glu": L.QAM_OUT_GLU}
+
+
 def qmatvec(x: torch.Tensor, packed: PackedMatrix, level_map: torch.Tensor, y: Optional[torch.Tensor] = None,
-            workspace: Optional[Workspace] = None) -> torch.Tensor:
-    """y [B, N] fp32 = the mixed-depth product of x [B, K] (fp32 or bf16) with the packed matrix."""
+            workspace: Optional[Workspace] = None, rms_norm: bool = False, out_mode: str = "store",
+            eps: float = 1e-6) -> torch.Tensor:
+    """y fp32 = the mixed-depth product of x [B, K] (fp32 or bf16) with the packed matrix.
+
+    ``rms_norm`` multiplies in 1 / sqrt(mean(x^2) + eps); ``out_mode`` is
+    "store" (y [B, N]), "add" (y += product, y given) or "glu" (gate/up rows
+    interleaved 32/32 per block, y [B, N/2] = silu(gate) * up)."""
     _require_cuda(level_map, "level_map", torch.uint8)
     if x.dim() == 1:
         x = x.unsqueeze(0)
@@ -178,15 +186,25 @@ def qmatvec(x: torch.Tensor, packed: PackedMatrix, level_map: torch.Tensor, y: O
         raise ValueError(f"x has {K} columns, matrix has {packed.K}")
     if level_map.numel() != packed.n_blocks:
         raise ValueError("level_map must have one entry per block")
+    mode = _OUT_MODES[out_mode]
+    n_out = packed.N // 2 if mode == L.QAM_OUT_GLU else packed.N
     if y is None:
-        y = torch.empty((B, packed.N), dtype=torch.float32, device=x.device)
+        if mode == L.QAM_OUT_ADD:
+            raise ValueError("out_mode 'add' needs y")
+        y = torch.empty((B, n_out), dtype=torch.float32, device=x.device)
     else:
         _require_cuda(y, "y", torch.float32)
+        if y.numel() != B * n_out:
+            raise ValueError(f"y must hold {B} x {n_out} values")
     ws = workspace or default_workspace(x.device)
     need = workspace_bytes(packed.N, packed.K, B)
     wbuf = ws.get(max(need, 1))
-    L.check(L.lib().qam_qmatvec(_ptr(x), xdt, B, C.byref(packed.desc), _ptr(level_map), 0, _ptr(y), _ptr(wbuf),
-                                wbuf.numel(), _stream_handle()))
+    ep = None
+    if rms_norm or mode != L.QAM_OUT_STORE:
+        ep = L.QamEpilogue(int(bool(rms_norm)), mode, float(eps))
+    L.check(L.lib().qam_qmatvec_ep(_ptr(x), xdt, B, C.byref(packed.desc), _ptr(level_map),
+                                   C.byref(ep) if ep is not None else None, _ptr(y), _ptr(wbuf), wbuf.numel(),
+                                   _stream_handle()))
     return y
 
 
@@ -227,6 +245,84 @@ class GroupedQmatvec:
 
     def run(self) -> None:
         L.check(L.lib().qam_qmatvec_group(C.byref(self.desc), _stream_handle()))
+
+
+class Decoder:
+    """A decode step as a chain of fused mixed-depth products (libqam's decoder).
+
+    ``layers`` is a sequence of (qkv, o, gate_up, down) PackedMatrix tuples
+    (gate_up rows interleaved 32 gate / 32 up per 64-row block) and
+    ``lm_head`` a PackedMatrix.  Write the step input into ``hidden`` and call
+    ``step(rung)`` (eager) or ``capture(rung)`` once and ``replay(rung)``."""
+
+    def __init__(self, layers, lm_head: PackedMatrix, hidden: int, q_dim: int, kv_dim: int, ffn: int,
+                 eps: float = 1e-6, target_waves: int = 0, device="cuda"):
+        n = len(layers)
+        self._layers = (L.QamDecoderLayer * n)()
+        self._keep = [lm_head]
+        for i, (qkv, o, gu, down) in enumerate(layers):
+            self._layers[i].qkv, self._layers[i].o = qkv.desc, o.desc
+            self._layers[i].gate_up, self._layers[i].down = gu.desc, down.desc
+            self._keep.append((qkv, o, gu, down))
+        d = L.QamDecoderDesc()
+        d.n_layers, d.hidden, d.q_dim, d.kv_dim, d.ffn, d.vocab = n, hidden, q_dim, kv_dim, ffn, lm_head.N
+        d.layers = self._layers
+        d.lm_head = lm_head.desc
+        d.eps = float(eps)
+        d.target_waves = int(target_waves)
+        self._desc = d
+        nbytes = int(L.lib().qam_decoder_bytes(C.byref(d)))
+        if nbytes == 0:
+            raise L.QamError(-2, "invalid decoder description")
+        self.mem = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        h = C.c_void_p()
+        L.check(L.lib().qam_decoder_create(C.byref(d), _ptr(self.mem), nbytes, C.byref(h), _stream_handle()))
+        self._h = h
+        self.n_layers = n
+        self.n_ops = 4 * n + 1
+        self.hidden = self._buffer(0, hidden)
+        self.qkv = self._buffer(1, q_dim + 2 * kv_dim)
+        self.m = self._buffer(2, ffn)
+        self.logits = self._buffer(3, lm_head.N)
+        self._capture_stream = None
+
+    def _buffer(self, which: int, n: int) -> torch.Tensor:
+        off = L.lib().qam_decoder_buffer(self._h, which) - self.mem.data_ptr()
+        return self.mem[off:off + 4 * n].view(torch.float32)
+
+    def run(self, rung: int, first: int, count: int = 1) -> None:
+        """Enqueue products first .. first+count-1 of the step's chain."""
+        L.check(L.lib().qam_decoder_run(self._h, int(rung), int(first), int(count), _stream_handle()))
+
+    def step(self, rung: int) -> None:
+        L.check(L.lib().qam_decoder_step(self._h, int(rung), _stream_handle()))
+
+    def capture(self, rung: int) -> None:
+        if self._capture_stream is None:
+            self._capture_stream = torch.cuda.Stream(device=self.mem.device)
+        s = self._capture_stream
+        s.wait_stream(torch.cuda.current_stream())
+        L.check(L.lib().qam_decoder_capture(self._h, int(rung), C.c_void_p(s.cuda_stream)))
+        torch.cuda.current_stream().wait_stream(s)
+
+    def replay(self, rung: int) -> None:
+        L.check(L.lib().qam_decoder_replay(self._h, int(rung), _stream_handle()))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            L.lib().qam_decoder_destroy(h)
+            self._h = None
+
+
+def escalation_schedule(scores, rate: float) -> np.ndarray:
+    """bool [T]: the steps re-run at 8 bits (the round(rate T) largest scores, ties to the earlier step)."""
+    sc = np.ascontiguousarray(np.asarray(scores, dtype=np.float64).reshape(-1))
+    out = np.zeros(sc.shape[0], dtype=np.uint8)
+    n = C.c_int64()
+    L.check(L.lib().qam_escalation_schedule(sc.ctypes.data_as(C.c_void_p), sc.shape[0], float(rate),
+                                            out.ctypes.data_as(C.c_void_p), C.byref(n)))
+    return out.astype(bool)
 
 
 def last_variant() -> str:

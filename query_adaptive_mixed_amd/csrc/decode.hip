@@ -1,0 +1,266 @@
+// Decode driver: one step of a decoder-only model as a chain of mixed-depth
+// products with fused epilogues, eager or replayed from a HIP graph, and the
+// host-side escalation schedule.
+//
+// [PoD] "Precision on Demand" abstract: 8-bit weights are stored once, each
+// step is decoded with their top 4 bits, and a step whose output looks
+// uncertain is decoded again at 8 bits; cost is counted in weight bytes read
+// per token.  In the ladder {0,2,4,6,8} those two depths are rungs 2 and 4,
+// every block at the same rung.
+
+#include <algorithm>
+#include <cmath>
+#include <new>
+#include <numeric>
+#include <vector>
+
+#include "qmatvec_internal.h"
+
+using namespace qam;
+
+struct qam_decoder {
+    qam_decoder_desc d{};
+    std::vector<qam_decoder_layer> layers;
+    float *h = nullptr, *qkv = nullptr, *m = nullptr, *logits = nullptr;
+    uint8_t* maps[5] = {};
+    char* ws = nullptr;            // counters, then fp64 partials
+    int64_t target_waves = 2048;
+    hipGraph_t graph[5] = {};
+    hipGraphExec_t exec[5] = {};
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t up256(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// The five launches of one layer (or the lm_head) in chain order.
+struct Op {
+    const qam_packed* w;
+    const float* x;
+    float* y;
+    int rms, out_mode;
+};
+
+std::vector<Op> chain(const qam_decoder& dec) {
+    std::vector<Op> ops;
+    ops.reserve(4 * dec.layers.size() + 1);
+    for (const qam_decoder_layer& L : dec.layers) {
+        ops.push_back({&L.qkv, dec.h, dec.qkv, 1, QAM_OUT_STORE});
+        ops.push_back({&L.o, dec.qkv, dec.h, 0, QAM_OUT_ADD});
+        ops.push_back({&L.gate_up, dec.h, dec.m, 1, QAM_OUT_GLU});
+        ops.push_back({&L.down, dec.m, dec.h, 0, QAM_OUT_ADD});
+    }
+    ops.push_back({&dec.d.lm_head, dec.h, dec.logits, 1, QAM_OUT_STORE});
+    return ops;
+}
+
+Plan plan_of(const qam_packed& w, int64_t target_waves) {
+    // chunks of whole D8 rings (2 tiles) so that small matrices spread over
+    // many wavefronts: a decode step is a chain of short, latency-bound launches
+    return make_plan(w.N, w.K, 1, chunk_goal(w.n_blocks * (w.K / kTileCols), target_waves), 2);
+}
+
+bool same_shape(const qam_packed& w, int64_t N, int64_t K) {
+    return w.N == N && w.K == K && w.n_blocks == N / kRows && w.planes &&
+           w.scales == reinterpret_cast<float*>(static_cast<char*>(w.planes) + N * K);
+}
+
+struct Layout {
+    size_t ws = 0, h = 0, qkv = 0, m = 0, logits = 0, maps = 0, total = 0;
+    int64_t max_blocks = 0;
+};
+
+int layout(const qam_decoder_desc* d, Layout& lo) {
+    if (!d || !d->layers) QAM_FAIL(QAM_ERR_NULL, "decoder: null description");
+    if (d->n_layers < 1 || d->n_layers > 4096) QAM_FAIL(QAM_ERR_ARG, "decoder: n_layers=%d", d->n_layers);
+    const int64_t H = d->hidden, Q = d->q_dim, KV = d->kv_dim, F = d->ffn, V = d->vocab;
+    if (H <= 0 || Q <= 0 || KV <= 0 || F <= 0 || V <= 0 || H % 64 || Q % 64 || KV % 64 || F % 32 || V % 64 ||
+        H > QAM_MAX_K || Q > QAM_MAX_K || F > QAM_MAX_K)
+        QAM_FAIL(QAM_ERR_SHAPE, "decoder: hidden, q_dim, kv_dim, vocab must be multiples of 64 and ffn of 32");
+    if (!(d->eps >= 0.0) || d->eps > 1e300) QAM_FAIL(QAM_ERR_ARG, "decoder: eps must be finite and >= 0");
+    if (d->target_waves < 0) QAM_FAIL(QAM_ERR_ARG, "decoder: target_waves < 0");
+    const int64_t tw = d->target_waves ? d->target_waves : 2048;
+    size_t partial = 0;
+    auto need = [&](const qam_packed& w) {
+        lo.max_blocks = std::max<int64_t>(lo.max_blocks, w.n_blocks);
+        partial = std::max(partial, plan_of(w, tw).partial_bytes);
+    };
+    for (int l = 0; l < d->n_layers; ++l) {
+        const qam_decoder_layer& L = d->layers[l];
+        if (!same_shape(L.qkv, Q + 2 * KV, H) || !same_shape(L.o, H, Q) || !same_shape(L.gate_up, 2 * F, H) ||
+            !same_shape(L.down, H, F))
+            QAM_FAIL(QAM_ERR_SHAPE, "decoder: layer %d has a matrix of the wrong shape", l);
+        need(L.qkv), need(L.o), need(L.gate_up), need(L.down);
+    }
+    if (!same_shape(d->lm_head, V, H)) QAM_FAIL(QAM_ERR_SHAPE, "decoder: lm_head must be [vocab][hidden]");
+    need(d->lm_head);
+    if (lo.max_blocks > QAM_MAX_BLOCKS) QAM_FAIL(QAM_ERR_SHAPE, "decoder: a matrix has more than %d blocks", QAM_MAX_BLOCKS);
+    size_t off = 0;
+    lo.ws = off;      off += up256(QAM_WS_COUNTER_BYTES + partial);
+    lo.h = off;       off += up256((size_t)H * 4);
+    lo.qkv = off;     off += up256((size_t)(Q + 2 * KV) * 4);
+    lo.m = off;       off += up256((size_t)F * 4);
+    lo.logits = off;  off += up256((size_t)V * 4);
+    lo.maps = off;    off += 5 * up256((size_t)lo.max_blocks);
+    lo.total = off;
+    return QAM_OK;
+}
+
+int enqueue(qam_decoder* dec, int rung, int first, int count, hipStream_t s) {
+    if (rung < 0 || rung > 4) QAM_FAIL(QAM_ERR_ARG, "decoder: rung %d outside 0..4", rung);
+    const std::vector<Op> ops = chain(*dec);
+    if (first < 0 || count < 0 || first > (int)ops.size() || count > (int)ops.size() - first)
+        QAM_FAIL(QAM_ERR_ARG, "decoder: products [%d, %d) outside the chain of %zu", first, first + count, ops.size());
+    Common c{};
+    c.B = 1;
+    c.x_bf16 = 0;
+    for (int i = first; i < first + count; ++i) {
+        const Op& op = ops[(size_t)i];
+        const Plan p = plan_of(*op.w, dec->target_waves);
+        Item it = make_item(op.x, op.w, dec->maps[rung], op.y, p);
+        it.rms = op.rms;
+        it.out_mode = op.out_mode;
+        it.eps = dec->d.eps;
+        if (p.n_chunks > 1) {
+            it.counters = reinterpret_cast<uint32_t*>(dec->ws);
+            it.partials = reinterpret_cast<double*>(dec->ws + QAM_WS_COUNTER_BYTES);
+        }
+        launch_single(1, it, c, (int64_t)p.n_chunks * p.n_quads, s);
+    }
+    QAM_HIP_CHECK(hipGetLastError());
+    return QAM_OK;
+}
+
+}  // namespace
+
+extern "C" size_t qam_decoder_bytes(const qam_decoder_desc* d) {
+    Layout lo;
+    if (layout(d, lo) != QAM_OK) return 0;
+    return lo.total;
+}
+
+extern "C" int qam_decoder_create(const qam_decoder_desc* d, void* dev_mem, size_t dev_bytes, qam_decoder** out,
+                                  hipStream_t s) {
+    clear_error();
+    if (!out || !dev_mem) QAM_FAIL(QAM_ERR_NULL, "decoder_create: null pointer");
+    *out = nullptr;
+    Layout lo;
+    if (int rc = layout(d, lo)) return rc;
+    if (dev_bytes < lo.total) QAM_FAIL(QAM_ERR_WORKSPACE, "decoder_create: %zu < %zu bytes", dev_bytes, lo.total);
+    if (!aligned(dev_mem, kAlign)) QAM_FAIL(QAM_ERR_ALIGN, "decoder_create: device memory must be 256-byte aligned");
+    qam_decoder* dec = new (std::nothrow) qam_decoder();
+    if (!dec) QAM_FAIL(QAM_ERR_ARG, "decoder_create: out of host memory");
+    dec->d = *d;
+    dec->layers.assign(d->layers, d->layers + d->n_layers);
+    dec->d.layers = dec->layers.data();
+    dec->target_waves = d->target_waves ? d->target_waves : 2048;
+    char* base = static_cast<char*>(dev_mem);
+    dec->ws = base + lo.ws;
+    dec->h = reinterpret_cast<float*>(base + lo.h);
+    dec->qkv = reinterpret_cast<float*>(base + lo.qkv);
+    dec->m = reinterpret_cast<float*>(base + lo.m);
+    dec->logits = reinterpret_cast<float*>(base + lo.logits);
+    hipError_t e = hipMemsetAsync(dec->ws, 0, QAM_WS_COUNTER_BYTES, s);
+    for (int r = 0; r < 5 && e == hipSuccess; ++r) {
+        dec->maps[r] = reinterpret_cast<uint8_t*>(base + lo.maps + r * up256((size_t)lo.max_blocks));
+        e = hipMemsetAsync(dec->maps[r], r, (size_t)lo.max_blocks, s);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        delete dec;
+        QAM_FAIL(QAM_ERR_HIP, "decoder_create: %s", hipGetErrorString(e));
+    }
+    *out = dec;
+    return QAM_OK;
+}
+
+extern "C" float* qam_decoder_buffer(qam_decoder* dec, int which) {
+    if (!dec) return nullptr;
+    switch (which) {
+        case QAM_DEC_H: return dec->h;
+        case QAM_DEC_QKV: return dec->qkv;
+        case QAM_DEC_M: return dec->m;
+        case QAM_DEC_LOGITS: return dec->logits;
+        default: return nullptr;
+    }
+}
+
+extern "C" int qam_decoder_step(qam_decoder* dec, int rung, hipStream_t s) {
+    clear_error();
+    if (!dec) QAM_FAIL(QAM_ERR_NULL, "decoder_step: null decoder");
+    if (int rc = enqueue(dec, rung, 0, 4 * dec->d.n_layers + 1, s)) return rc;
+    char v[96];
+    snprintf(v, sizeof(v), "decoder_step rung=%d launches=%d", rung, 4 * dec->d.n_layers + 1);
+    set_variant(v);
+    return QAM_OK;
+}
+
+extern "C" int qam_decoder_run(qam_decoder* dec, int rung, int first, int count, hipStream_t s) {
+    clear_error();
+    if (!dec) QAM_FAIL(QAM_ERR_NULL, "decoder_run: null decoder");
+    return enqueue(dec, rung, first, count, s);
+}
+
+extern "C" int qam_decoder_capture(qam_decoder* dec, int rung, hipStream_t s) {
+    clear_error();
+    if (!dec) QAM_FAIL(QAM_ERR_NULL, "decoder_capture: null decoder");
+    if (!s) QAM_FAIL(QAM_ERR_ARG, "decoder_capture: the null stream cannot be captured");
+    if (rung < 0 || rung > 4) QAM_FAIL(QAM_ERR_ARG, "decoder_capture: rung %d outside 0..4", rung);
+    QAM_HIP_CHECK(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    const int rc = enqueue(dec, rung, 0, 4 * dec->d.n_layers + 1, s);
+    hipGraph_t g = nullptr;
+    const hipError_t e = hipStreamEndCapture(s, &g);
+    if (rc != QAM_OK) {
+        if (g) (void)hipGraphDestroy(g);
+        return rc;
+    }
+    if (e != hipSuccess) QAM_FAIL(QAM_ERR_HIP, "decoder_capture: %s", hipGetErrorString(e));
+    hipGraphExec_t x = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    if (ei != hipSuccess) {
+        (void)hipGraphDestroy(g);
+        QAM_FAIL(QAM_ERR_HIP, "decoder_capture: instantiate: %s", hipGetErrorString(ei));
+    }
+    if (dec->exec[rung]) (void)hipGraphExecDestroy(dec->exec[rung]);
+    if (dec->graph[rung]) (void)hipGraphDestroy(dec->graph[rung]);
+    dec->graph[rung] = g;
+    dec->exec[rung] = x;
+    return QAM_OK;
+}
+
+extern "C" int qam_decoder_replay(qam_decoder* dec, int rung, hipStream_t s) {
+    clear_error();
+    if (!dec) QAM_FAIL(QAM_ERR_NULL, "decoder_replay: null decoder");
+    if (rung < 0 || rung > 4 || !dec->exec[rung]) QAM_FAIL(QAM_ERR_ARG, "decoder_replay: rung %d was not captured", rung);
+    QAM_HIP_CHECK(hipGraphLaunch(dec->exec[rung], s));
+    return QAM_OK;
+}
+
+extern "C" void qam_decoder_destroy(qam_decoder* dec) {
+    if (!dec) return;
+    for (int r = 0; r < 5; ++r) {
+        if (dec->exec[r]) (void)hipGraphExecDestroy(dec->exec[r]);
+        if (dec->graph[r]) (void)hipGraphDestroy(dec->graph[r]);
+    }
+    delete dec;
+}
+
+extern "C" int qam_escalation_schedule(const double* scores, int64_t T, double rate, uint8_t* escalate_out,
+                                       int64_t* n_out) {
+    clear_error();
+    if (!scores || !escalate_out) QAM_FAIL(QAM_ERR_NULL, "escalation_schedule: null pointer");
+    if (T < 0) QAM_FAIL(QAM_ERR_ARG, "escalation_schedule: T < 0");
+    if (!(rate >= 0.0 && rate <= 1.0)) QAM_FAIL(QAM_ERR_ARG, "escalation_schedule: rate outside [0, 1]");
+    for (int64_t t = 0; t < T; ++t)
+        if (!std::isfinite(scores[t])) QAM_FAIL(QAM_ERR_ARG, "escalation_schedule: score %lld not finite", (long long)t);
+    const int64_t n = (int64_t)std::floor(rate * (double)T + 0.5);
+    std::vector<int64_t> order((size_t)T);
+    std::iota(order.begin(), order.end(), (int64_t)0);
+    // largest score first; equal scores keep step order (the earlier step wins)
+    std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b) { return scores[a] > scores[b]; });
+    std::fill(escalate_out, escalate_out + T, (uint8_t)0);
+    for (int64_t i = 0; i < n; ++i) escalate_out[order[(size_t)i]] = 1;
+    if (n_out) *n_out = n;
+    return QAM_OK;
+}

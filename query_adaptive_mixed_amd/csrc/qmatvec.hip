@@ -27,7 +27,7 @@
 #include <algorithm>
 #include <vector>
 
-#include "qam_common.h"
+#include "qmatvec_internal.h"
 
 namespace qam {
 
@@ -40,32 +40,6 @@ typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
 __device__ __forceinline__ u32x4 load_plane(const uint8_t* p) {
     return __builtin_nontemporal_load((global_u32x4*)(p));
 }
-
-// One matrix of a launch.
-struct Item {
-    const uint8_t* planes;
-    const float* scales;
-    const void* x;             // [B][K]
-    float* y;                  // [B][N]
-    const uint8_t* level;      // [n_blocks]
-    double* partials;          // [n_chunks][B][N] (split K only)
-    uint32_t* counters;        // [n_blocks]       (split K only)
-    int64_t plane_bytes;       // N*K/4
-    int64_t N, K;
-    int n_blocks;
-    int n_tiles;               // K / 64
-    int tpc;                   // tiles per chunk
-    int n_chunks;
-    int n_quads;               // ceil(n_blocks / 4)
-    int wg_begin;              // first workgroup of this item in a grouped launch
-};
-
-struct Common {
-    const Item* items;         // grouped launches: the descriptor table
-    const int* wg_item;        // grouped launches: item index of every workgroup
-    int B;
-    int x_bf16;
-};
 
 // ------------------------------------------------------------------ x staging
 
@@ -237,6 +211,65 @@ __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngro
     __syncthreads();   // orders the LDS writes before the reads
 }
 
+// ------------------------------------------------------------------ epilogue
+
+// sum_k x[r][k]^2 in fp64, in a fixed order: lane partials over a stride of
+// 256 columns, then a butterfly (every lane ends with the same value).
+template <bool XBF16>
+__device__ double sum_squares(const void* x, int64_t K, int r, int L) {
+    double s = 0.0;
+    for (int64_t k = 4 * L; k < K; k += 256) {
+        const float4 v = x4_value<XBF16>(load_x4_raw<XBF16>(x, (int64_t)r * K + k));
+        s += (double)v.x * (double)v.x;
+        s += (double)v.y * (double)v.y;
+        s += (double)v.z * (double)v.z;
+        s += (double)v.w * (double)v.w;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
+    return s;
+}
+
+// Writes the block's outputs from the exact row sums sum[r] = c_n . x_r:
+// v = scale * sum (divided by the RMS of x_r when the item asks for an
+// RMS-normalised input), then y = fl32(v) (store), y = fl32(y + v) (residual
+// add) or, for rows interleaved 32 gate / 32 up per block, one output per
+// pair: fl32(silu(gate) * up) with silu(t) = t / (1 + e^-t), all in fp64.
+template <int NB, bool XBF16>
+__device__ __forceinline__ void finish(const Item& a, int b, int L, const double (&sum)[NB]) {
+    const int row = b * kRows + L;
+    const double sc = (double)a.scales[row];
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        double v = sc * sum[r];
+        if (a.rms) v = v / sqrt(sum_squares<XBF16>(a.x, a.K, r, L) / (double)a.K + a.eps);
+        if (a.out_mode == QAM_OUT_GLU) {
+            const double up = __shfl(v, (L + 32) & 63);
+            if (L < 32) a.y[(int64_t)r * (a.N / 2) + b * 32 + L] = (float)(v / (1.0 + exp(-v)) * up);
+        } else if (a.out_mode == QAM_OUT_ADD) {
+            float* yp = a.y + (int64_t)r * a.N + row;
+            *yp = (float)((double)*yp + v);
+        } else {
+            a.y[(int64_t)r * a.N + row] = (float)v;
+        }
+    }
+}
+
+// A ZERO block: every row's sum is 0, so y = 0 (store), y unchanged (add) or
+// silu(0) * 0 = 0 (gated pairs); nothing of the block is read.
+template <int NB>
+__device__ __forceinline__ void finish_zero(const Item& a, int b, int L) {
+    if (a.out_mode == QAM_OUT_ADD) return;
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+        if (a.out_mode == QAM_OUT_GLU) {
+            if (L < 32) a.y[(int64_t)r * (a.N / 2) + b * 32 + L] = 0.0f;
+        } else {
+            a.y[(int64_t)r * a.N + (int64_t)b * kRows + L] = 0.0f;
+        }
+    }
+}
+
 // One wavefront: block b, column chunk `chunk`, read at NS slices.  The chunk
 // is walked in sub-chunks of S tiles; each sub-chunk's exact integer sums are
 // scaled into a per-row fp64 sum (exact but for fp64 rounding across
@@ -349,14 +382,12 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     }
 
     const int row = b * kRows + L;          // the row this lane writes: j = L >> 4
-    const float sc = a.scales[row];
     double part[NB];
 #pragma unroll
     for (int r = 0; r < NB; ++r) part[r] = any_bad[r] ? __builtin_nan("") : mine[r];   // non-finite x: NaN
 
     if (a.n_chunks == 1) {
-#pragma unroll
-        for (int r = 0; r < NB; ++r) a.y[(int64_t)r * a.N + row] = (float)((double)sc * part[r]);
+        finish<NB, XBF16>(a, b, L, part);
         return;
     }
     // Split K: publish this chunk's partials, then count the arrival; the last
@@ -375,15 +406,16 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     if (L == 0) prev = __hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = __shfl(prev, 0);
     if (prev != (uint32_t)(a.n_chunks - 1)) return;
+    double sum[NB];
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
-        double sum = 0.0;
+        sum[r] = 0.0;
         for (int cc = 0; cc < a.n_chunks; ++cc)
-            sum += __hip_atomic_load(&a.partials[((int64_t)cc * B + r) * a.N + row], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-        a.y[(int64_t)r * a.N + row] = (float)((double)sc * sum);
+            sum[r] += __hip_atomic_load(&a.partials[((int64_t)cc * B + r) * a.N + row], __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
     }
     if (L == 0) __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    finish<NB, XBF16>(a, b, L, sum);
 }
 
 // One workgroup = one wavefront = one (block, column chunk) of one matrix.
@@ -407,9 +439,7 @@ __global__ __launch_bounds__(64) void qmatvec_kernel(Item single, Common c) {
     const int ns = __builtin_amdgcn_readfirstlane(lev < 4 ? lev : 4);
     switch (ns) {
         case 0:   // ZERO: nothing read, y = 0 (written once, by the first chunk)
-            if (chunk == 0)
-#pragma unroll
-                for (int r = 0; r < NB; ++r) a.y[(int64_t)r * a.N + (int64_t)b * kRows + L] = 0.0f;
+            if (chunk == 0) finish_zero<NB>(a, b, L);
             return;
         case 1: wave_body<1, NB, XBF16>(a, c, lds, b, chunk, L); return;
         case 2: wave_body<2, NB, XBF16>(a, c, lds, b, chunk, L); return;
@@ -420,32 +450,28 @@ __global__ __launch_bounds__(64) void qmatvec_kernel(Item single, Common c) {
 
 // ------------------------------------------------------------------ host side
 
-struct Plan {
-    int tpc, n_chunks, n_quads;
-    size_t partial_bytes;
-};
-
 static int64_t g_target_waves = 256 * 32;   // wavefronts aimed for per launch
 
 // every chunk holds a whole number of prefetch rings (Ring<NS, B>::PF for every NS)
-static int tpc_align_for(int64_t B) { return B == 1 ? 8 : (B == 2 ? 4 : 2); }
-static int stage_tiles_for(int64_t B) { return B == 1 ? 24 : (B == 2 ? 12 : (B <= 4 ? 8 : 4)); }
-static size_t lds_bytes_for(int64_t B) { return (size_t)B * stage_tiles_for(B) * 16 * sizeof(int4); }
+int tpc_align_for(int64_t B) { return B == 1 ? 8 : (B == 2 ? 4 : 2); }
+int stage_tiles_for(int64_t B) { return B == 1 ? 24 : (B == 2 ? 12 : (B <= 4 ? 8 : 4)); }
+size_t lds_bytes_for(int64_t B) { return (size_t)B * stage_tiles_for(B) * 16 * sizeof(int4); }
 
 // Column chunk length (in tiles) for a launch covering `block_tiles` block x
 // tile pairs: enough chunks for about g_target_waves wavefronts of equal work.
-static int chunk_goal(int64_t block_tiles) {
-    const int64_t g = (block_tiles + g_target_waves - 1) / g_target_waves;
+int chunk_goal(int64_t block_tiles, int64_t target_waves) {
+    if (target_waves <= 0) target_waves = g_target_waves;
+    const int64_t g = (block_tiles + target_waves - 1) / target_waves;
     return (int)std::max<int64_t>(1, std::min<int64_t>(g, QAM_MAX_K / kTileCols));
 }
 
 // Chunking of one matrix: K is cut into the fewest chunks of at most `goal`
 // tiles, evened out and rounded up to a whole number of prefetch rings.
-static Plan make_plan(int64_t N, int64_t K, int64_t B, int goal) {
+Plan make_plan(int64_t N, int64_t K, int64_t B, int goal, int align) {
     Plan p{};
     const int n_blocks = (int)(N / kRows);
     const int n_tiles = (int)(K / kTileCols);
-    const int align = tpc_align_for(B);
+    if (align <= 0) align = tpc_align_for(B);
     const int want = (n_tiles + goal - 1) / goal;
     int tpc = (n_tiles + want - 1) / want;
     tpc = (tpc + align - 1) / align * align;
@@ -479,9 +505,13 @@ static void launch(int64_t B, const Item& it, const Common& c, int64_t grid, siz
     }
 }
 
+void launch_single(int64_t B, const Item& it, const Common& c, int64_t grid, hipStream_t s) {
+    launch<false>(B, it, c, grid, lds_bytes_for(B), s);
+}
+
 // Host checks shared by the single and grouped entry points.
-static int check_item(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
-                      float* y, const char* who) {
+int check_item(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
+               float* y, const char* who, int out_mode) {
     if (!x || !packed || !level_map || !y || !packed->planes) QAM_FAIL(QAM_ERR_NULL, "%s: null pointer", who);
     const int64_t N = packed->N, K = packed->K;
     if (N <= 0 || K <= 0 || N % kRows || K % kTileCols || K > QAM_MAX_K || packed->n_blocks != N / kRows ||
@@ -496,11 +526,12 @@ static int check_item(const void* x, int x_dtype, int64_t B, const qam_packed* p
     const size_t xbytes = (size_t)B * K * (x_dtype == QAM_X_BF16 ? 2 : 4);
     const char* xc = static_cast<const char*>(x);
     const char* yc = reinterpret_cast<const char*>(y);
-    if (xc < yc + (size_t)B * N * 4 && yc < xc + xbytes) QAM_FAIL(QAM_ERR_ARG, "%s: x and y overlap", who);
+    const size_t ybytes = (size_t)B * (out_mode == QAM_OUT_GLU ? N / 2 : N) * 4;
+    if (xc < yc + ybytes && yc < xc + xbytes) QAM_FAIL(QAM_ERR_ARG, "%s: x and y overlap", who);
     return QAM_OK;
 }
 
-static Item make_item(const void* x, const qam_packed* packed, const uint8_t* level_map, float* y, const Plan& p) {
+Item make_item(const void* x, const qam_packed* packed, const uint8_t* level_map, float* y, const Plan& p) {
     Item it{};
     it.planes = static_cast<const uint8_t*>(packed->planes);
     it.scales = packed->scales;
@@ -526,7 +557,7 @@ extern "C" size_t qam_qmatvec_workspace_bytes(int64_t N, int64_t K, int64_t B) {
     if (N <= 0 || K <= 0 || N % kRows || K % kTileCols || K > QAM_MAX_K || N / kRows > QAM_MAX_BLOCKS || B < 1 ||
         B > QAM_MAX_BATCH)
         return 0;
-    const Plan p = make_plan(N, K, B, chunk_goal(N / kRows * (K / kTileCols)));
+    const Plan p = make_plan(N, K, B, chunk_goal(N / kRows * (K / kTileCols), 0));
     return p.n_chunks > 1 ? QAM_WS_COUNTER_BYTES + p.partial_bytes : 0;
 }
 
@@ -537,13 +568,29 @@ extern "C" int qam_set_target_waves(int waves) {
     return QAM_OK;
 }
 
-extern "C" int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
-                           int per_request_maps, float* y, void* workspace, size_t workspace_bytes, hipStream_t s) {
+static int check_epilogue(const qam_epilogue* ep, const char* who) {
+    if (!ep) return QAM_OK;
+    if (ep->rms_norm != 0 && ep->rms_norm != 1) QAM_FAIL(QAM_ERR_ARG, "%s: rms_norm must be 0 or 1", who);
+    if (ep->out_mode != QAM_OUT_STORE && ep->out_mode != QAM_OUT_ADD && ep->out_mode != QAM_OUT_GLU)
+        QAM_FAIL(QAM_ERR_ARG, "%s: unknown out_mode %d", who, ep->out_mode);
+    if (!(ep->eps >= 0.0) || ep->eps > 1e300) QAM_FAIL(QAM_ERR_ARG, "%s: eps must be finite and >= 0", who);
+    return QAM_OK;
+}
+
+extern "C" int qam_qmatvec_ep(const void* x, int x_dtype, int64_t B, const qam_packed* packed,
+                              const uint8_t* level_map, const qam_epilogue* ep, float* y, void* workspace,
+                              size_t workspace_bytes, hipStream_t s) {
     clear_error();
-    if (int rc = check_item(x, x_dtype, B, packed, level_map, y, "qmatvec")) return rc;
-    if (per_request_maps != 0) QAM_FAIL(QAM_ERR_ARG, "qmatvec: per-request maps are not taken by this entry point");
-    const Plan p = make_plan(packed->N, packed->K, B, chunk_goal(packed->n_blocks * (packed->K / kTileCols)));
+    if (int rc = check_epilogue(ep, "qmatvec")) return rc;
+    const int out_mode = ep ? ep->out_mode : QAM_OUT_STORE;
+    if (int rc = check_item(x, x_dtype, B, packed, level_map, y, "qmatvec", out_mode)) return rc;
+    const Plan p = make_plan(packed->N, packed->K, B, chunk_goal(packed->n_blocks * (packed->K / kTileCols), 0));
     Item it = make_item(x, packed, level_map, y, p);
+    if (ep) {
+        it.rms = ep->rms_norm;
+        it.out_mode = ep->out_mode;
+        it.eps = ep->eps;
+    }
     if (p.n_chunks > 1) {
         const size_t need = QAM_WS_COUNTER_BYTES + p.partial_bytes;
         if (!workspace) QAM_FAIL(QAM_ERR_WORKSPACE, "qmatvec: workspace of %zu bytes required", need);
@@ -556,12 +603,19 @@ extern "C" int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_pack
     c.B = (int)B;
     c.x_bf16 = x_dtype == QAM_X_BF16;
     const int64_t grid = (int64_t)p.n_chunks * p.n_quads;
-    launch<false>(B, it, c, grid, lds_bytes_for(B), s);
+    launch_single(B, it, c, grid, s);
     QAM_HIP_CHECK(hipGetLastError());
     char v[128];
     snprintf(v, sizeof(v), "qmatvec_dot4 B=%lld tpc=%d chunks=%d", (long long)B, p.tpc, p.n_chunks);
     set_variant(v);
     return QAM_OK;
+}
+
+extern "C" int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
+                           int per_request_maps, float* y, void* workspace, size_t workspace_bytes, hipStream_t s) {
+    clear_error();
+    if (per_request_maps != 0) QAM_FAIL(QAM_ERR_ARG, "qmatvec: per-request maps are not taken by this entry point");
+    return qam_qmatvec_ep(x, x_dtype, B, packed, level_map, nullptr, y, workspace, workspace_bytes, s);
 }
 
 // ------------------------------------------------------------------ grouped launches
@@ -586,7 +640,7 @@ static int layout_group(const qam_gemv_item* items, int n_items, int64_t B, Grou
     }
     if (g.blocks > QAM_MAX_BLOCKS) QAM_FAIL(QAM_ERR_SHAPE, "group: %lld blocks > %d", (long long)g.blocks, QAM_MAX_BLOCKS);
     for (int i = 0; i < n_items; ++i) {
-        const Plan p = make_plan(items[i].w.N, items[i].w.K, B, chunk_goal(g.block_tiles));
+        const Plan p = make_plan(items[i].w.N, items[i].w.K, B, chunk_goal(g.block_tiles, 0));
         g.plans.push_back(p);
         g.partial_bytes += p.partial_bytes;
         g.n_wg += (int64_t)p.n_chunks * p.n_quads;
@@ -624,7 +678,7 @@ extern "C" int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B
     size_t poff = 0;
     for (int i = 0; i < n_items; ++i) {
         const qam_gemv_item& gi = items[i];
-        if (int rc = check_item(gi.x, x_dtype, B, &gi.w, gi.level_map, gi.y, "group_init")) return rc;
+        if (int rc = check_item(gi.x, x_dtype, B, &gi.w, gi.level_map, gi.y, "group_init", QAM_OUT_STORE)) return rc;
         const Plan& p = g.plans[i];
         Item it = make_item(gi.x, &gi.w, gi.level_map, gi.y, p);
         it.wg_begin = (int)wg;

@@ -146,3 +146,115 @@ def test_map_weight_bytes_matches_the_oracle_memory_formula(lib):
         assert abs(mb.value - O.mean_bits(lv, w)) < 1e-12
     bad = np.array([5], dtype=np.uint8)
     assert lib.qam_map_weight_bytes(bad.ctypes.data_as(C.c_void_p), 1, 64, lad, 5, None, None) == -3
+
+
+# ------------------------------------------------------------------ escalation schedule (host)
+
+def _schedule(lib, scores, rate):
+    sc = np.ascontiguousarray(np.asarray(scores, dtype=np.float64))
+    out = np.zeros(sc.shape[0], dtype=np.uint8)
+    n = C.c_int64(-1)
+    rc = lib.qam_escalation_schedule(sc.ctypes.data_as(C.c_void_p), sc.shape[0], rate,
+                                     out.ctypes.data_as(C.c_void_p), C.byref(n))
+    return rc, out.astype(bool), n.value
+
+
+@pytest.mark.parametrize("T", [0, 1, 7, 256, 1000])
+@pytest.mark.parametrize("rate", [0.0, 0.16, 0.5, 1.0])
+def test_escalation_schedule_matches_oracle(lib, T, rate):
+    rng = np.random.default_rng(T * 10 + int(rate * 100))
+    for scores in (rng.beta(2.0, 5.0, size=T), rng.integers(0, 4, size=T).astype(np.float64)):  # ties too
+        rc, got, n = _schedule(lib, scores, rate)
+        assert rc == 0
+        want = O.escalation_schedule(scores, rate)
+        assert np.array_equal(got, want)
+        assert n == int(want.sum())
+
+
+def test_escalation_schedule_decode_workload(lib):
+    import workloads as WL
+    scores = WL.escalation_scores(0, 256)
+    rc, got, n = _schedule(lib, scores, 0.16)
+    assert rc == 0 and n == 41
+    assert np.array_equal(got, O.escalation_schedule(scores, 0.16))
+    assert O.escalation_byte_ratio(got) == 0.66015625
+
+
+def test_escalation_schedule_rejects(lib):
+    assert _schedule(lib, [0.1, float("nan")], 0.5)[0] == -3
+    assert _schedule(lib, [0.1, 0.2], 1.5)[0] == -3
+    assert _schedule(lib, [0.1, 0.2], -0.1)[0] == -3
+
+
+# ------------------------------------------------------------------ fused epilogue and decoder (host checks)
+
+def _fake_packed(N, K, base=0x100000):
+    d = L.QamPacked()
+    d.N, d.K, d.n_blocks = N, K, N // 64
+    d.planes = base
+    d.scales = base + N * K
+    return d
+
+
+@pytest.mark.parametrize("ep,code", [
+    ((2, 0, 1e-6), -3), ((0, 3, 1e-6), -3), ((1, 0, -1.0), -3), ((1, 0, float("nan")), -3),
+])
+def test_qmatvec_ep_rejects_bad_epilogue(lib, ep, code):
+    e = L.QamEpilogue(*ep)
+    w = _fake_packed(128, 256)
+    rc = lib.qam_qmatvec_ep(FAKE, 0, 1, C.byref(w), FAKE, C.byref(e), FAKE, None, 0, None)
+    assert rc == code
+    assert lib.qam_last_error().decode()
+
+
+def _decoder_desc(n_layers=2, H=256, Q=512, KV=128, F=384, V=1024, tweak=None):
+    layers = (L.QamDecoderLayer * n_layers)()
+    base = 0x10000000
+    for i in range(n_layers):
+        layers[i].qkv = _fake_packed(Q + 2 * KV, H, base)
+        layers[i].o = _fake_packed(H, Q, base)
+        layers[i].gate_up = _fake_packed(2 * F, H, base)
+        layers[i].down = _fake_packed(H, F, base)
+    d = L.QamDecoderDesc()
+    d.n_layers, d.hidden, d.q_dim, d.kv_dim, d.ffn, d.vocab = n_layers, H, Q, KV, F, V
+    d.layers = layers
+    d.lm_head = _fake_packed(V, H, base)
+    d.eps = 1e-6
+    if tweak:
+        tweak(d, layers)
+    return d, layers
+
+
+def test_decoder_bytes_layout(lib):
+    d, keep = _decoder_desc()
+    nb = lib.qam_decoder_bytes(C.byref(d))
+    # workspace counters + h + qkv + m + logits + 5 maps, each 256-byte aligned
+    floor = (64 * 1024 * 4 + 256 * 4 + (512 + 256) * 4 + 384 * 4 + 1024 * 4 + 5 * 256)
+    assert nb >= floor and nb % 256 == 0
+
+
+@pytest.mark.parametrize("tweak", [
+    lambda d, l: setattr(d, "ffn", 100),
+    lambda d, l: setattr(d, "hidden", 250),
+    lambda d, l: setattr(l[1], "o", _fake_packed(256, 256, 0x10000000)),
+    lambda d, l: setattr(d, "lm_head", _fake_packed(960, 256, 0x10000000)),
+    lambda d, l: setattr(d, "n_layers", 0),
+    lambda d, l: setattr(d, "eps", -1.0),
+])
+def test_decoder_rejects_bad_descriptions(lib, tweak):
+    d, keep = _decoder_desc(tweak=tweak)
+    assert lib.qam_decoder_bytes(C.byref(d)) == 0
+    h = C.c_void_p()
+    assert lib.qam_decoder_create(C.byref(d), FAKE, 1 << 30, C.byref(h), None) in (-2, -3)
+    assert not h.value
+
+
+def test_decoder_create_checks_memory_before_any_launch(lib):
+    d, keep = _decoder_desc()
+    nb = lib.qam_decoder_bytes(C.byref(d))
+    h = C.c_void_p()
+    assert lib.qam_decoder_create(C.byref(d), FAKE, nb - 1, C.byref(h), None) == -7
+    assert lib.qam_decoder_create(C.byref(d), C.c_void_p(0x1010), nb, C.byref(h), None) == -5
+    assert lib.qam_decoder_create(C.byref(d), None, nb, C.byref(h), None) == -1
+    assert lib.qam_decoder_step(None, 2, None) == -1
+    assert lib.qam_decoder_replay(None, 2, None) == -1

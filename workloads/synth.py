@@ -199,16 +199,26 @@ QWEN_LAYER = (("q", 2048, 1024), ("k", 1024, 1024), ("v", 1024, 1024), ("o", 102
 QWEN_VOCAB = 151936
 
 
+def decoder_field(seed: int, n_layers: int, hidden: int, q_dim: int, kv_dim: int, ffn: int, vocab: int,
+                  name: str = "decoder") -> Field:
+    """Matrices of a decoder-only model, per layer q [q_dim, hidden],
+    k and v [kv_dim, hidden], o [hidden, q_dim], gate and up [ffn, hidden],
+    down [hidden, ffn], then a [vocab, hidden] head; int8 codes."""
+    shapes = (("q", q_dim, hidden), ("k", kv_dim, hidden), ("v", kv_dim, hidden), ("o", hidden, q_dim),
+              ("gate", ffn, hidden), ("up", ffn, hidden), ("down", hidden, ffn))
+    mats, i = [], 0
+    for layer in range(n_layers):
+        for nm, N, K in shapes:
+            mats.append(Matrix(f"L{layer}.{nm}", N, K, i))
+            i += 1
+    mats.append(Matrix("lm_head", vocab, hidden, i))
+    return Field(name, seed, mats)
+
+
 def qwen_decode_field(seed: int = 0, n_layers: int = 28) -> Field:
     """28 layers (hidden 1024; 16 Q heads / 8 KV heads of dim 128; FFN 3072)
     plus the tied 151936x1024 head, int8 weights."""
-    mats, i = [], 0
-    for layer in range(n_layers):
-        for name, N, K in QWEN_LAYER:
-            mats.append(Matrix(f"L{layer}.{name}", N, K, i))
-            i += 1
-    mats.append(Matrix("lm_head", QWEN_VOCAB, QWEN_HIDDEN, i))
-    return Field("qwen_decode", seed, mats)
+    return decoder_field(seed, n_layers, QWEN_HIDDEN, 2048, 1024, 3072, QWEN_VOCAB, "qwen_decode")
 
 
 def decode_inputs(seed: int, n_steps: int, hidden: int = QWEN_HIDDEN) -> np.ndarray:
