@@ -59,7 +59,8 @@ extern "C" {
 #define QAM_MAX_K          65536      /* keeps every exact integer sum in range */
 #define QAM_MAX_LENSES     64
 #define QAM_MAX_RUNGS      16
-#define QAM_MAX_BATCH      8          /* requests per qmatvec call with a shared map */
+#define QAM_MAX_BATCH      8          /* requests per call on the dot-product route   */
+#define QAM_MAX_BATCH_MFMA 32         /* requests per qam_qmatvec call (matrix cores) */
 #define QAM_MAX_BLOCKS     65536      /* blocks per matrix (N <= 4,194,304)         */
 #define QAM_WS_COUNTER_BYTES (QAM_MAX_BLOCKS * 4)  /* workspace counter region      */
 
@@ -214,23 +215,40 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   untruncated int8 product.  A non-finite x makes that request's
  *   non-ZERO outputs NaN.
  *
+ *   Routes.  Batches of 1 (and small batches with a shared map) run on the
+ *   vector ALUs: each 16-byte slice word becomes four int8x4 code words
+ *   multiplied by the limbs with v_dot4.  Batches of QAM_MAX_BATCH+1 .. 32,
+ *   per-request maps, and shared-map batches from a tunable threshold (4)
+ *   run on the matrix cores: a pre-pass writes the limbs of x per column
+ *   chunk as MFMA B operands, and v_mfma_i32_16x16x64_i8 multiplies the
+ *   codes (16 rows x 64 columns per lane group of words) with 16 requests
+ *   of one limb at a time.  With per-request maps a block is read once, to
+ *   the deepest slice any request needs, and each request gets the codes at
+ *   its own depth, built from the same words (the residual slices make the
+ *   code at depth d the sum of the first d/2 slices).  Both routes have the
+ *   arithmetic and bound above (the matrix-core route's fixed point is per
+ *   column chunk).
+ *
  *   x          (device) [B][K] row-major, fp32 (x_dtype QAM_X_F32) or bf16
  *              (QAM_X_BF16); 16-byte aligned.
- *   B          1 .. QAM_MAX_BATCH requests.
+ *   B          1 .. QAM_MAX_BATCH_MFMA requests.
  *   packed     (host) descriptor from qam_pack_slices.
  *   level_map  (device) uint8 rung indices of the ladder {0,2,4,6,8}
- *              (rung index = slices read): [n_blocks], shared by all requests.
- *   per_request_maps  must be 0 for this entry point.
+ *              (rung index = slices read): [n_blocks] shared by all requests
+ *              (per_request_maps = 0) or [B][n_blocks], one map per request
+ *              (per_request_maps = 1).
  *   y          (device) fp32 [B][N], must not overlap x.
- *   workspace  (device) qam_qmatvec_workspace_bytes(N, K, B) bytes (0 when
- *              the plan needs no split of K; NULL is then accepted), 256-byte
- *              aligned.  Its first QAM_WS_COUNTER_BYTES hold per-block arrival
- *              counters: they must be zero before the first use, and every
- *              call leaves them zero again, whatever the shape, so one buffer
- *              serves calls of any shape.  The rest holds fp64 partial sums
- *              that each call writes before it reads.  Calls that share a
- *              workspace must be ordered (same stream or synchronised).
- *   N          at most QAM_MAX_BLOCKS blocks of 64 rows.
+ *   workspace  (device) qam_qmatvec_workspace_bytes(N, K, B) bytes (enough
+ *              for either route; 0 when no route needs any, NULL is then
+ *              accepted), 256-byte aligned.  Its first QAM_WS_COUNTER_BYTES
+ *              hold per-block arrival counters: they must be zero before the
+ *              first use, and every call leaves them zero again, whatever
+ *              the shape, so one buffer serves calls of any shape.  The rest
+ *              holds fp64 partial sums and limbs that each call writes before
+ *              it reads.  Calls that share a workspace must be ordered (same
+ *              stream or synchronised).
+ *   N          at most QAM_MAX_BLOCKS blocks of 64 rows (half that for
+ *              B > 16 on the matrix-core route).
  */
 size_t qam_qmatvec_workspace_bytes(int64_t N, int64_t K, int64_t B);
 
@@ -261,8 +279,9 @@ int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_packed* packed,
  *                    t / (1 + e^-t), in fp64; y is [B][N/2].
  *   A ZERO block reads nothing: v = 0 for its rows (QAM_OUT_ADD leaves y as
  *   it is, QAM_OUT_GLU writes 0).  Other arguments, the workspace and the
- *   error bound (on v) are those of qam_qmatvec; y must not overlap x.
- *   ep == NULL is qam_qmatvec with a shared map.
+ *   error bound (on v) are those of qam_qmatvec's dot-product route; y must
+ *   not overlap x.  B <= QAM_MAX_BATCH, shared map; ep == NULL is that route
+ *   of qam_qmatvec.
  */
 #define QAM_OUT_STORE 0
 #define QAM_OUT_ADD   1
@@ -357,7 +376,7 @@ typedef struct qam_decoder_desc {
     const qam_decoder_layer* layers;        /* (host) [n_layers]; descriptors are copied */
     qam_packed               lm_head;       /* [vocab][hidden] */
     double                   eps;           /* RMS epsilon, >= 0 */
-    int                      target_waves;  /* launch width goal per matrix; 0 = 2048 */
+    int                      target_waves;  /* launch width goal per matrix; 0 = 96 */
 } qam_decoder_desc;
 
 typedef struct qam_decoder qam_decoder;     /* opaque host object */

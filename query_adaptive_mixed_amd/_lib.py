@@ -18,6 +18,7 @@ ERRORS = {-1: "QAM_ERR_NULL", -2: "QAM_ERR_SHAPE", -3: "QAM_ERR_ARG", -4: "QAM_E
 QAM_MAX_LENSES = 64
 QAM_MAX_STOPS = 15
 QAM_MAX_BATCH = 8
+QAM_MAX_BATCH_MFMA = 32
 QAM_MAX_K = 65536
 QAM_X_F32, QAM_X_BF16 = 0, 1
 QAM_COMBINE_SUM, QAM_COMBINE_MAX = 0, 1
@@ -98,6 +99,8 @@ SIGNATURES = [
 # tuning hooks that are not part of the product ABI contract
 EXTRA_SIGNATURES = [
     ("qam_set_target_waves", _I, [_I]),
+    ("qam_set_mfma_target_waves", _I, [_I]),
+    ("qam_set_mfma_min_batch", _I, [_I]),
 ]
 
 

@@ -168,9 +168,12 @@ def qmatvec(x: torch.Tensor, packed: PackedMatrix, level_map: torch.Tensor, y: O
             eps: float = 1e-6) -> torch.Tensor:
     """y fp32 = the mixed-depth product of x [B, K] (fp32 or bf16) with the packed matrix.
 
-    ``rms_norm`` multiplies in 1 / sqrt(mean(x^2) + eps); ``out_mode`` is
-    "store" (y [B, N]), "add" (y += product, y given) or "glu" (gate/up rows
-    interleaved 32/32 per block, y [B, N/2] = silu(gate) * up)."""
+    ``level_map`` is uint8 [n_blocks] (shared by the B requests) or
+    [B, n_blocks] (one map per request).  ``rms_norm`` multiplies in
+    1 / sqrt(mean(x^2) + eps); ``out_mode`` is "store" (y [B, N]), "add"
+    (y += product, y given) or "glu" (gate/up rows interleaved 32/32 per
+    block, y [B, N/2] = silu(gate) * up); the last two and ``rms_norm`` take a
+    shared map and B <= 8."""
     _require_cuda(level_map, "level_map", torch.uint8)
     if x.dim() == 1:
         x = x.unsqueeze(0)
@@ -184,7 +187,11 @@ def qmatvec(x: torch.Tensor, packed: PackedMatrix, level_map: torch.Tensor, y: O
     B, K = x.shape
     if K != packed.K:
         raise ValueError(f"x has {K} columns, matrix has {packed.K}")
-    if level_map.numel() != packed.n_blocks:
+    per_request = level_map.dim() == 2
+    if per_request:
+        if tuple(level_map.shape) != (B, packed.n_blocks):
+            raise ValueError("a per-request level_map must be [B, n_blocks]")
+    elif level_map.numel() != packed.n_blocks:
         raise ValueError("level_map must have one entry per block")
     mode = _OUT_MODES[out_mode]
     n_out = packed.N // 2 if mode == L.QAM_OUT_GLU else packed.N
@@ -199,12 +206,15 @@ def qmatvec(x: torch.Tensor, packed: PackedMatrix, level_map: torch.Tensor, y: O
     ws = workspace or default_workspace(x.device)
     need = workspace_bytes(packed.N, packed.K, B)
     wbuf = ws.get(max(need, 1))
-    ep = None
     if rms_norm or mode != L.QAM_OUT_STORE:
+        if per_request:
+            raise ValueError("fused epilogues take a shared level map")
         ep = L.QamEpilogue(int(bool(rms_norm)), mode, float(eps))
-    L.check(L.lib().qam_qmatvec_ep(_ptr(x), xdt, B, C.byref(packed.desc), _ptr(level_map),
-                                   C.byref(ep) if ep is not None else None, _ptr(y), _ptr(wbuf), wbuf.numel(),
-                                   _stream_handle()))
+        L.check(L.lib().qam_qmatvec_ep(_ptr(x), xdt, B, C.byref(packed.desc), _ptr(level_map), C.byref(ep), _ptr(y),
+                                       _ptr(wbuf), wbuf.numel(), _stream_handle()))
+    else:
+        L.check(L.lib().qam_qmatvec(_ptr(x), xdt, B, C.byref(packed.desc), _ptr(level_map), int(per_request),
+                                    _ptr(y), _ptr(wbuf), wbuf.numel(), _stream_handle()))
     return y
 
 

@@ -24,7 +24,7 @@ struct qam_decoder {
     float *h = nullptr, *qkv = nullptr, *m = nullptr, *logits = nullptr;
     uint8_t* maps[5] = {};
     char* ws = nullptr;            // counters, then fp64 partials
-    int64_t target_waves = 2048;
+    int64_t target_waves = 96;
     hipGraph_t graph[5] = {};
     hipGraphExec_t exec[5] = {};
 };
@@ -80,7 +80,7 @@ int layout(const qam_decoder_desc* d, Layout& lo) {
         QAM_FAIL(QAM_ERR_SHAPE, "decoder: hidden, q_dim, kv_dim, vocab must be multiples of 64 and ffn of 32");
     if (!(d->eps >= 0.0) || d->eps > 1e300) QAM_FAIL(QAM_ERR_ARG, "decoder: eps must be finite and >= 0");
     if (d->target_waves < 0) QAM_FAIL(QAM_ERR_ARG, "decoder: target_waves < 0");
-    const int64_t tw = d->target_waves ? d->target_waves : 2048;
+    const int64_t tw = d->target_waves ? d->target_waves : 96;
     size_t partial = 0;
     auto need = [&](const qam_packed& w) {
         lo.max_blocks = std::max<int64_t>(lo.max_blocks, w.n_blocks);
@@ -154,7 +154,7 @@ extern "C" int qam_decoder_create(const qam_decoder_desc* d, void* dev_mem, size
     dec->d = *d;
     dec->layers.assign(d->layers, d->layers + d->n_layers);
     dec->d.layers = dec->layers.data();
-    dec->target_waves = d->target_waves ? d->target_waves : 2048;
+    dec->target_waves = d->target_waves ? d->target_waves : 96;
     char* base = static_cast<char*>(dev_mem);
     dec->ws = base + lo.ws;
     dec->h = reinterpret_cast<float*>(base + lo.h);

@@ -31,62 +31,7 @@
 
 namespace qam {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
-
-// Weight loads must be global (not flat) memory operations: a flat load also
-// counts against the LDS wait counter, so every wait for the limb words in LDS
-// would drain the whole prefetch ring with it.
-__device__ __forceinline__ u32x4 load_plane(const uint8_t* p) {
-    return __builtin_nontemporal_load((global_u32x4*)(p));
-}
-
 // ------------------------------------------------------------------ x staging
-
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(1))) const u32x2 global_u32x2;
-typedef __attribute__((address_space(4))) const uint32_t const_u32;
-
-// Raw bits of four x values: fp32 (16 bytes) or bf16 (8 bytes, in .x/.y).
-// Converting later, when the values are staged, keeps the wait off this load.
-template <bool XBF16>
-__device__ __forceinline__ u32x4 load_x4_raw(const void* x, int64_t idx) {
-    if constexpr (XBF16) {
-        const u32x2 h = *(global_u32x2*)(static_cast<const uint16_t*>(x) + idx);
-        return u32x4{h.x, h.y, 0u, 0u};
-    } else {
-        return *(global_u32x4*)(static_cast<const float*>(x) + idx);
-    }
-}
-
-template <bool XBF16>
-__device__ __forceinline__ float4 x4_value(u32x4 raw) {
-    if constexpr (XBF16)
-        return make_float4(__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xFFFF0000u),
-                           __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u));
-    return make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y), __uint_as_float(raw.z), __uint_as_float(raw.w));
-}
-
-// The level byte of block b through the scalar cache: the aligned dword that
-// holds it (same page as the byte, so never a fault), waited on with the
-// scalar counter rather than the vector one.
-__device__ __forceinline__ int level_of(const uint8_t* level, int b) {
-    const uintptr_t addr = reinterpret_cast<uintptr_t>(level + b);
-    const uint32_t word = *(const_u32*)(addr & ~(uintptr_t)3);
-    return (int)((word >> (8 * (addr & 3))) & 0xFFu);
-}
-
-// Activations are held as three signed int8 limbs of a 24-bit fixed point
-// per sub-chunk: v = rint(x * 2^(kFrac - e)), |v| <= 2^22.
-constexpr int kLimbs = 3;
-constexpr int kFrac = 22;
-
-// Balanced base-256 digits of the fixed-point value of one element, as three
-// signed bytes (byte l = digit l; the top byte is unused).
-__device__ __forceinline__ uint32_t limbs_of(float v, int sh) {
-    const int q = (int)rintf(ldexpf(v, sh));            // |q| <= 2^22
-    return ((uint32_t)q + 0x808080u) ^ 0x808080u;
-}
 
 // LDS index (in 16-byte units) of the limb words of 4-column group g of the
 // sub-chunk: tile g/16, then the group's position u in the lane's 16 columns,
@@ -165,7 +110,8 @@ __device__ __forceinline__ void load_half(u32x4 (&h)[H][NS], const uint8_t* base
 // xraw[r][i] holds the x values of group lane + 64 i of request r.
 template <int NB, int G, bool XBF16>
 __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngroups, int slots, int L,
-                                            int4* __restrict__ lds, int (&exps)[NB], bool (&bad)[NB]) {
+                                            int4* __restrict__ lds, int (&exps)[NB], bool (&bad)[NB],
+                                            bool want_ssq, double (&ssq)[NB]) {
     __syncthreads();   // the workgroup is this one wavefront: the last sub-chunk's LDS reads are done
     float4 xv[NB][G];
 #pragma unroll
@@ -198,6 +144,12 @@ __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngro
             const int g = L + 64 * i;
             if (g >= ngroups) continue;
             const float4 v = xv[r][i];
+            if (want_ssq) {   // this lane's share of sum x^2 (an RMS-normalised input, one column chunk)
+                ssq[r] += (double)v.x * (double)v.x;
+                ssq[r] += (double)v.y * (double)v.y;
+                ssq[r] += (double)v.z * (double)v.z;
+                ssq[r] += (double)v.w * (double)v.w;
+            }
             const uint32_t w0 = limbs_of(v.x, sh), w1 = limbs_of(v.y, sh);
             const uint32_t w2 = limbs_of(v.z, sh), w3 = limbs_of(v.w, sh);
             int4 out;
@@ -230,19 +182,23 @@ __device__ double sum_squares(const void* x, int64_t K, int r, int L) {
     return s;
 }
 
-// Writes the block's outputs from the exact row sums sum[r] = c_n . x_r:
+// Writes the block's outputs from the exact row sums sum[r] = c_n . x_r
+// (ssq: sum_k x_r[k]^2 when the caller already has it, else NULL):
 // v = scale * sum (divided by the RMS of x_r when the item asks for an
 // RMS-normalised input), then y = fl32(v) (store), y = fl32(y + v) (residual
 // add) or, for rows interleaved 32 gate / 32 up per block, one output per
 // pair: fl32(silu(gate) * up) with silu(t) = t / (1 + e^-t), all in fp64.
 template <int NB, bool XBF16>
-__device__ __forceinline__ void finish(const Item& a, int b, int L, const double (&sum)[NB]) {
+__device__ __forceinline__ void finish(const Item& a, int b, int L, const double (&sum)[NB], const double* ssq) {
     const int row = b * kRows + L;
     const double sc = (double)a.scales[row];
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
         double v = sc * sum[r];
-        if (a.rms) v = v / sqrt(sum_squares<XBF16>(a.x, a.K, r, L) / (double)a.K + a.eps);
+        if (a.rms) {
+            const double ss = ssq ? ssq[r] : sum_squares<XBF16>(a.x, a.K, r, L);
+            v = v / sqrt(ss / (double)a.K + a.eps);
+        }
         if (a.out_mode == QAM_OUT_GLU) {
             const double up = __shfl(v, (L + 32) & 63);
             if (L < 32) a.y[(int64_t)r * (a.N / 2) + b * 32 + L] = (float)(v / (1.0 + exp(-v)) * up);
@@ -291,10 +247,14 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
 
     double mine[NB];
     bool any_bad[NB];
+    double ssq[NB];
+    // an unsplit RMS-normalised product sees all of x while staging it
+    const bool want_ssq = a.rms && a.n_chunks == 1;
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
         mine[r] = 0.0;
         any_bad[r] = false;
+        ssq[r] = 0.0;
     }
 
     for (int t0 = 0; t0 < ntile; t0 += S) {
@@ -328,7 +288,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
         //    then the second half ring
         int exps[NB];
         bool bad[NB];
-        stage_limbs<NB, G, XBF16>(xraw, ngroups, slots, L, lds, exps, bad);
+        stage_limbs<NB, G, XBF16>(xraw, ngroups, slots, L, lds, exps, bad, want_ssq, ssq);
         load_half<NS, H>(Bh, base, pb, H, last);
         __builtin_amdgcn_sched_barrier(0);
 
@@ -387,7 +347,13 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     for (int r = 0; r < NB; ++r) part[r] = any_bad[r] ? __builtin_nan("") : mine[r];   // non-finite x: NaN
 
     if (a.n_chunks == 1) {
-        finish<NB, XBF16>(a, b, L, part);
+        if (want_ssq) {
+#pragma unroll
+            for (int r = 0; r < NB; ++r)
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) ssq[r] += __shfl_xor(ssq[r], o);
+        }
+        finish<NB, XBF16>(a, b, L, part, want_ssq ? ssq : nullptr);
         return;
     }
     // Split K: publish this chunk's partials, then count the arrival; the last
@@ -415,7 +381,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
                                         __HIP_MEMORY_SCOPE_AGENT);
     }
     if (L == 0) __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    finish<NB, XBF16>(a, b, L, sum);
+    finish<NB, XBF16>(a, b, L, sum, nullptr);
 }
 
 // One workgroup = one wavefront = one (block, column chunk) of one matrix.
@@ -517,7 +483,8 @@ int check_item(const void* x, int x_dtype, int64_t B, const qam_packed* packed, 
     if (N <= 0 || K <= 0 || N % kRows || K % kTileCols || K > QAM_MAX_K || packed->n_blocks != N / kRows ||
         packed->n_blocks > QAM_MAX_BLOCKS)
         QAM_FAIL(QAM_ERR_SHAPE, "%s: bad packed shape N=%lld K=%lld", who, (long long)N, (long long)K);
-    if (B < 1 || B > QAM_MAX_BATCH) QAM_FAIL(QAM_ERR_ARG, "%s: B=%lld outside [1, %d]", who, (long long)B, QAM_MAX_BATCH);
+    if (B < 1 || B > QAM_MAX_BATCH_MFMA)
+        QAM_FAIL(QAM_ERR_ARG, "%s: B=%lld outside [1, %d]", who, (long long)B, QAM_MAX_BATCH_MFMA);
     if (x_dtype != QAM_X_F32 && x_dtype != QAM_X_BF16) QAM_FAIL(QAM_ERR_ARG, "%s: unknown x_dtype %d", who, x_dtype);
     if (!aligned(x, 16) || !aligned(y, 4) || !aligned(packed->planes, 256))
         QAM_FAIL(QAM_ERR_ALIGN, "%s: x must be 16-byte and planes 256-byte aligned", who);
@@ -555,10 +522,15 @@ using namespace qam;
 
 extern "C" size_t qam_qmatvec_workspace_bytes(int64_t N, int64_t K, int64_t B) {
     if (N <= 0 || K <= 0 || N % kRows || K % kTileCols || K > QAM_MAX_K || N / kRows > QAM_MAX_BLOCKS || B < 1 ||
-        B > QAM_MAX_BATCH)
+        B > QAM_MAX_BATCH_MFMA)
         return 0;
-    const Plan p = make_plan(N, K, B, chunk_goal(N / kRows * (K / kTileCols), 0));
-    return p.n_chunks > 1 ? QAM_WS_COUNTER_BYTES + p.partial_bytes : 0;
+    size_t need = 0;
+    if (B <= QAM_MAX_BATCH) {   // the dot4 route
+        const Plan p = make_plan(N, K, B, chunk_goal(N / kRows * (K / kTileCols), 0));
+        need = p.n_chunks > 1 ? QAM_WS_COUNTER_BYTES + p.partial_bytes : 0;
+    }
+    if (B > 1) need = std::max(need, qam_mfma_workspace_bytes(N, K, B));   // the matrix-core route
+    return need;
 }
 
 extern "C" int qam_set_target_waves(int waves) {
@@ -584,6 +556,8 @@ extern "C" int qam_qmatvec_ep(const void* x, int x_dtype, int64_t B, const qam_p
     if (int rc = check_epilogue(ep, "qmatvec")) return rc;
     const int out_mode = ep ? ep->out_mode : QAM_OUT_STORE;
     if (int rc = check_item(x, x_dtype, B, packed, level_map, y, "qmatvec", out_mode)) return rc;
+    if (B > QAM_MAX_BATCH)
+        QAM_FAIL(QAM_ERR_ARG, "qmatvec: B=%lld outside [1, %d] for this entry point", (long long)B, QAM_MAX_BATCH);
     const Plan p = make_plan(packed->N, packed->K, B, chunk_goal(packed->n_blocks * (packed->K / kTileCols), 0));
     Item it = make_item(x, packed, level_map, y, p);
     if (ep) {
@@ -611,11 +585,28 @@ extern "C" int qam_qmatvec_ep(const void* x, int x_dtype, int64_t B, const qam_p
     return QAM_OK;
 }
 
+// Smallest batch with a shared map that takes the matrix-core route.
+static int g_mfma_min_batch = 4;
+
+static bool mfma_route(int64_t B, int per_request_maps) {
+    return (per_request_maps && B > 1) || B > QAM_MAX_BATCH || B >= g_mfma_min_batch;
+}
+
+extern "C" int qam_set_mfma_min_batch(int b) {
+    clear_error();
+    if (b < 2 || b > QAM_MAX_BATCH + 1) QAM_FAIL(QAM_ERR_ARG, "set_mfma_min_batch: %d outside [2, %d]", b, QAM_MAX_BATCH + 1);
+    g_mfma_min_batch = b;
+    return QAM_OK;
+}
+
 extern "C" int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
                            int per_request_maps, float* y, void* workspace, size_t workspace_bytes, hipStream_t s) {
     clear_error();
-    if (per_request_maps != 0) QAM_FAIL(QAM_ERR_ARG, "qmatvec: per-request maps are not taken by this entry point");
-    return qam_qmatvec_ep(x, x_dtype, B, packed, level_map, nullptr, y, workspace, workspace_bytes, s);
+    if (per_request_maps != 0 && per_request_maps != 1) QAM_FAIL(QAM_ERR_ARG, "qmatvec: per_request_maps must be 0 or 1");
+    if (!mfma_route(B, per_request_maps) || B < 1)
+        return qam_qmatvec_ep(x, x_dtype, B, packed, level_map, nullptr, y, workspace, workspace_bytes, s);
+    if (int rc = check_item(x, x_dtype, B, packed, level_map, y, "qmatvec", QAM_OUT_STORE)) return rc;
+    return qmatvec_mfma(x, x_dtype, B, packed, level_map, per_request_maps, y, workspace, workspace_bytes, s);
 }
 
 // ------------------------------------------------------------------ grouped launches

@@ -6,6 +6,65 @@
 
 namespace qam {
 
+// ---------------------------------------------------------------- device helpers
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+
+// Weight loads must be global (not flat) memory operations: a flat load also
+// counts against the LDS wait counter, so every wait for the limb words in LDS
+// would drain the whole prefetch ring with it.
+__device__ __forceinline__ u32x4 load_plane(const uint8_t* p) {
+    return __builtin_nontemporal_load((global_u32x4*)(p));
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x2 global_u32x2;
+typedef __attribute__((address_space(4))) const uint32_t const_u32;
+
+// Raw bits of four x values: fp32 (16 bytes) or bf16 (8 bytes, in .x/.y).
+// Converting later, when the values are staged, keeps the wait off this load.
+template <bool XBF16>
+__device__ __forceinline__ u32x4 load_x4_raw(const void* x, int64_t idx) {
+    if constexpr (XBF16) {
+        const u32x2 h = *(global_u32x2*)(static_cast<const uint16_t*>(x) + idx);
+        return u32x4{h.x, h.y, 0u, 0u};
+    } else {
+        return *(global_u32x4*)(static_cast<const float*>(x) + idx);
+    }
+}
+
+template <bool XBF16>
+__device__ __forceinline__ float4 x4_value(u32x4 raw) {
+    if constexpr (XBF16)
+        return make_float4(__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xFFFF0000u),
+                           __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u));
+    return make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y), __uint_as_float(raw.z), __uint_as_float(raw.w));
+}
+
+// The level byte of block b through the scalar cache: the aligned dword that
+// holds it (same page as the byte, so never a fault), waited on with the
+// scalar counter rather than the vector one.
+__device__ __forceinline__ int level_of(const uint8_t* level, int b) {
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(level + b);
+    const uint32_t word = *(const_u32*)(addr & ~(uintptr_t)3);
+    return (int)((word >> (8 * (addr & 3))) & 0xFFu);
+}
+
+// Activations are held as three signed int8 limbs of a 24-bit fixed point
+// per sub-chunk: v = rint(x * 2^(kFrac - e)), |v| <= 2^22.
+constexpr int kLimbs = 3;
+constexpr int kFrac = 22;
+
+// Balanced base-256 digits of the fixed-point value of one element, as three
+// signed bytes (byte l = digit l; the top byte is unused).
+__device__ __forceinline__ uint32_t limbs_of(float v, int sh) {
+    const int q = (int)rintf(ldexpf(v, sh));            // |q| <= 2^22
+    return ((uint32_t)q + 0x808080u) ^ 0x808080u;
+}
+
+// ---------------------------------------------------------------- launch descriptors
+
 // One matrix of a launch.
 struct Item {
     const uint8_t* planes;
@@ -21,7 +80,7 @@ struct Item {
     int n_tiles;               // K / 64
     int tpc;                   // tiles per chunk
     int n_chunks;
-    int n_quads;               // ceil(n_blocks / 4)
+    int n_quads;               // workgroups per chunk (one per block)
     int wg_begin;              // first workgroup of this item in a grouped launch
     int rms;                   // 1: y uses x / sqrt(mean(x^2) + eps)
     int out_mode;              // QAM_OUT_STORE / _ADD / _GLU
@@ -54,6 +113,10 @@ Plan make_plan(int64_t N, int64_t K, int64_t B, int goal, int align = 0);
 Item make_item(const void* x, const qam_packed* packed, const uint8_t* level_map, float* y, const Plan& p);
 int check_item(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map, float* y,
                const char* who, int out_mode);
+// Matrix-core route of qam_qmatvec (batches up to 32, per-request maps).
+size_t qam_mfma_workspace_bytes(int64_t N, int64_t K, int64_t B);
+int qmatvec_mfma(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
+                 int per_request_maps, float* y, void* workspace, size_t workspace_bytes, hipStream_t s);
 // Enqueues one single-matrix product launch (grid = n_chunks * n_quads).
 void launch_single(int64_t B, const Item& it, const Common& c, int64_t grid, hipStream_t s);
 

@@ -1,0 +1,422 @@
+// Batched mixed-depth product on the matrix cores: up to 32 requests, with
+// one level map shared by all of them or one map per request.
+//
+// [FoQLens] "Progress": every 64-row block is read at its own depth from the
+// one stored copy inside the pass (the pages' batched decode reads 32
+// requests per step).  With a map per request, block b is read once, to the
+// deepest slice any request needs, and every request gets the block's codes
+// at its own depth: the residual slices make the code at depth d the sum of
+// the first d/2 slices, so the codes for each depth present in the batch are
+// built incrementally from the same loaded words.
+//
+// Arithmetic (exact, as in the batch-1 kernel): a pre-pass turns each
+// request's x, per column chunk, into a 24-bit fixed point held as three int8
+// limbs, laid out as the B operands of v_mfma_i32_16x16x64_i8 (16 columns =
+// 16 requests of one limb); codes are the A operands (16 rows x 64 columns,
+// exactly the words a lane loads); i32 accumulation is exact; limbs are
+// combined in fp64 at the end of the chunk.
+//
+// Wavefront h of a workgroup serves requests 16h .. 16h+15 of one (block,
+// column chunk); MFMA output lane L holds rows 4(L>>4)+i (i = 0..3) of each
+// 16-row group and request 16h + (L & 15).
+
+#include <algorithm>
+#include <vector>
+
+#include "qmatvec_internal.h"
+
+namespace qam {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const v4i global_v4i;
+
+constexpr int kBadExp = 0x7FFFFFFF;   // exponent marker of a chunk of x with a non-finite value
+
+struct MItem {
+    const uint8_t* planes;
+    const float* scales;
+    const void* x;             // [B][K]
+    float* y;                  // [B][N]
+    const uint8_t* level;      // [B][n_blocks] (per request) or [n_blocks]
+    int64_t level_stride;      // n_blocks (per request) or 0
+    v4i* limbs;                // [n_tiles][NH][3][64] 16-byte B operands
+    int* exps;                 // [n_chunks][16 NH]
+    double* partials;          // [n_chunks][B][N] (split K only)
+    uint32_t* counters;        // [n_blocks][NH]   (split K only)
+    int64_t plane_bytes;
+    int64_t N, K;
+    int n_blocks, n_tiles, tpc, n_chunks;
+};
+
+// ------------------------------------------------------------------ x -> limbs
+
+// One wavefront per (column chunk, request slot r < 16 NH): the chunk's
+// largest |x| sets the exponent; padding slots r >= B get zero limbs.
+template <bool XBF16>
+__global__ __launch_bounds__(64) void limbs_kernel(MItem a, int B, int NH) {
+    const int slots = 16 * NH;
+    const int chunk = blockIdx.x / slots;
+    const int r = blockIdx.x % slots;
+    const int L = threadIdx.x;
+    const int t0 = chunk * a.tpc;
+    const int ncol = min(a.tpc, a.n_tiles - t0) * 64;
+    const int64_t col0 = (int64_t)t0 * 64;
+    const bool live = r < B;
+    float m = 0.0f;
+    int nonfinite = 0;
+    if (live)
+        for (int k = 4 * L; k < ncol; k += 256) {
+            const float4 v = x4_value<XBF16>(load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + k));
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            nonfinite |= !(fabsf(v.x) <= 3.402823466e38f) | !(fabsf(v.y) <= 3.402823466e38f) |
+                         !(fabsf(v.z) <= 3.402823466e38f) | !(fabsf(v.w) <= 3.402823466e38f);
+        }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        m = fmaxf(m, __shfl_xor(m, o));
+        nonfinite |= __shfl_xor(nonfinite, o);
+    }
+    int e = 0;
+    if (m > 0.0f) frexpf(m, &e);
+    if (L == 0) a.exps[chunk * slots + r] = nonfinite ? kBadExp : e;
+    const int sh = kFrac - e;
+    const int h = r >> 4, n = r & 15;
+    uint8_t* lb = reinterpret_cast<uint8_t*>(a.limbs);
+    for (int k = 4 * L; k < ncol; k += 256) {
+        uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+        if (live && !nonfinite) {
+            const float4 v = x4_value<XBF16>(load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + k));
+            w0 = limbs_of(v.x, sh), w1 = limbs_of(v.y, sh), w2 = limbs_of(v.z, sh), w3 = limbs_of(v.w, sh);
+        }
+        const int64_t kk = col0 + k;   // columns kk .. kk+3: one tile, one 16-column slice
+        const int64_t t = kk >> 6;
+        const int kg = (int)((kk & 63) >> 4);
+        const int byte = (int)(kk & 15);
+#pragma unroll
+        for (int l = 0; l < kLimbs; ++l) {
+            const uint32_t word = ((w0 >> (8 * l)) & 0xFFu) | (((w1 >> (8 * l)) & 0xFFu) << 8) |
+                                  (((w2 >> (8 * l)) & 0xFFu) << 16) | (((w3 >> (8 * l)) & 0xFFu) << 24);
+            const int64_t unit = ((t * NH + h) * kLimbs + l) * 64 + kg * 16 + n;
+            *reinterpret_cast<uint32_t*>(lb + unit * 16 + byte) = word;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ product
+
+// Tiles in flight: two halves of H tiles, each tile NS weight loads and three
+// limb loads per lane.
+template <int NS>
+struct MRing {
+    static constexpr int H = NS <= 2 ? 2 : 1;
+    static constexpr int PF = 2 * H;
+};
+
+template <int NS, int H>
+__device__ __forceinline__ void mload(u32x4 (&w)[H][NS], v4i (&x)[H][kLimbs], const uint8_t* wbase, int64_t pb,
+                                      const v4i* xbase, int64_t xstride, int tile, int last) {
+#pragma unroll
+    for (int u = 0; u < H; ++u) {
+        const int t = min(tile + u, last);
+#pragma unroll
+        for (int p = 0; p < NS; ++p) w[u][p] = load_plane(wbase + p * pb + (int64_t)t * kTileBytes);
+#pragma unroll
+        for (int l = 0; l < kLimbs; ++l) x[u][l] = *(global_v4i*)(xbase + t * xstride + l * 64);
+    }
+}
+
+// One tile: for each depth d present among the wave's requests (bit d of
+// `dmask`), the codes at depth d times the limbs of the requests reading d.
+template <int NS, bool PER_REQ>
+__device__ __forceinline__ void mtile(const u32x4 (&w)[NS], const v4i (&xl)[kLimbs], int m_lane, uint32_t dmask,
+                                      v4i (&acc)[4][kLimbs]) {
+    uint32_t q[4][4];   // [j][u]: masked slice bits so far, unrotated
+#pragma unroll
+    for (int p = 0; p < NS; ++p) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t mk = slice_mask(3 - p, u);
+            if (p == 0) {
+                q[0][u] = w[0].x & mk;
+                q[1][u] = w[0].y & mk;
+                q[2][u] = w[0].z & mk;
+                q[3][u] = w[0].w & mk;
+            } else {
+                q[0][u] |= w[p].x & mk;
+                q[1][u] |= w[p].y & mk;
+                q[2][u] |= w[p].z & mk;
+                q[3][u] |= w[p].w & mk;
+            }
+        }
+        const bool use = PER_REQ ? ((dmask >> (p + 1)) & 1u) != 0 : p == NS - 1;
+        if (use) {
+            v4i bm[kLimbs];
+#pragma unroll
+            for (int l = 0; l < kLimbs; ++l) {
+                if constexpr (PER_REQ) {
+                    const bool mine = m_lane == p + 1;
+                    bm[l] = v4i{mine ? xl[l].x : 0, mine ? xl[l].y : 0, mine ? xl[l].z : 0, mine ? xl[l].w : 0};
+                } else {
+                    bm[l] = xl[l];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const v4i A = v4i{(int)q[j][0], (int)rotl32(q[j][1], 2), (int)rotl32(q[j][2], 4),
+                                  (int)rotl32(q[j][3], 6)};
+#pragma unroll
+                for (int l = 0; l < kLimbs; ++l)
+                    acc[j][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bm[l], acc[j][l], 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <int NS, bool PER_REQ>
+__device__ __forceinline__ void mwave(const MItem& a, int B, int NH, int b, int chunk, int h, int L, int m_lane,
+                                      uint32_t dmask) {
+    constexpr int H = MRing<NS>::H;
+    constexpr int PF = MRing<NS>::PF;
+    const int t0 = chunk * a.tpc;
+    const int nt = min(a.tpc, a.n_tiles - t0);
+    const int last = nt - 1;
+    const uint8_t* wbase = a.planes + (int64_t)b * 16 * a.K + (int64_t)t0 * kTileBytes + L * 16;
+    const int64_t xstride = (int64_t)NH * kLimbs * 64;   // v4i units per tile
+    const v4i* xbase = a.limbs + (int64_t)t0 * xstride + (int64_t)h * kLimbs * 64 + L;
+    const int64_t pb = a.plane_bytes;
+
+    v4i acc[4][kLimbs];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int l = 0; l < kLimbs; ++l) acc[j][l] = v4i{0, 0, 0, 0};
+
+    __builtin_amdgcn_s_waitcnt(0);
+    u32x4 wa[H][NS], wb[H][NS];
+    v4i xa[H][kLimbs], xb[H][kLimbs];
+    mload<NS, H>(wa, xa, wbase, pb, xbase, xstride, 0, last);
+    __builtin_amdgcn_sched_barrier(0);
+    mload<NS, H>(wb, xb, wbase, pb, xbase, xstride, H, last);
+    __builtin_amdgcn_sched_barrier(0);
+    int t = 0;
+    for (; t + PF < nt; t += PF) {
+#pragma unroll
+        for (int u = 0; u < H; ++u) mtile<NS, PER_REQ>(wa[u], xa[u], m_lane, dmask, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        mload<NS, H>(wa, xa, wbase, pb, xbase, xstride, t + PF, last);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < H; ++u) mtile<NS, PER_REQ>(wb[u], xb[u], m_lane, dmask, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        mload<NS, H>(wb, xb, wbase, pb, xbase, xstride, t + PF + H, last);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = 0; u < H; ++u)
+        if (t + u < nt) mtile<NS, PER_REQ>(wa[u], xa[u], m_lane, dmask, acc);
+#pragma unroll
+    for (int u = 0; u < H; ++u)
+        if (t + H + u < nt) mtile<NS, PER_REQ>(wb[u], xb[u], m_lane, dmask, acc);
+
+    // exact row sums for this lane's request: rows 16j + 4(L>>4) + i
+    const int slots = 16 * NH;
+    const int r = 16 * h + (L & 15);
+    const int e = a.exps[chunk * slots + r];
+    double v[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const double d = (double)acc[j][2][i] * 65536.0 + (double)acc[j][1][i] * 256.0 + (double)acc[j][0][i];
+            v[j][i] = m_lane == 0 ? 0.0 : (e == kBadExp ? __builtin_nan("") : ldexp(d, e - kFrac));
+        }
+    const int row0 = b * kRows + 4 * (L >> 4);
+    const bool live = r < B;
+    // the 16 scales first, all in flight together (y may alias nothing, but
+    // the compiler cannot know that, so loads interleaved with the y stores
+    // would each wait for the one before)
+    float sc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[j][i] = a.scales[row0 + 16 * j + i];
+    if (a.n_chunks == 1) {
+        if (live)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a.y[(int64_t)r * a.N + row0 + 16 * j + i] = (float)((double)sc[j][i] * v[j][i]);
+        return;
+    }
+    // split K: the protocol of the batch-1 kernel, one counter per (block, wave)
+    if (live)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __hip_atomic_store(&a.partials[((int64_t)chunk * B + r) * a.N + row0 + 16 * j + i], v[j][i],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    uint32_t prev = 0;
+    uint32_t* ctr = a.counters + (int64_t)b * NH + h;
+    if (L == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __shfl(prev, 0);
+    if (prev != (uint32_t)(a.n_chunks - 1)) return;
+    if (live) {
+        double s[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[j][i] = 0.0;
+        for (int cc = 0; cc < a.n_chunks; ++cc) {
+            const double* pp = a.partials + ((int64_t)cc * B + r) * a.N + row0;
+            double t[4][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    t[j][i] = __hip_atomic_load(pp + 16 * j + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[j][i] += t[j][i];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a.y[(int64_t)r * a.N + row0 + 16 * j + i] = (float)((double)sc[j][i] * s[j][i]);
+    }
+    if (L == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup = NH wavefronts = one (block, column chunk); wave h serves
+// requests 16h .. 16h+15.
+template <bool PER_REQ>
+__global__ __launch_bounds__(128) void qmm_kernel(MItem a, int B, int NH) {
+    const int chunk = (int)blockIdx.x % a.n_chunks;
+    const int b = (int)blockIdx.x / a.n_chunks;
+    const int h = (int)threadIdx.x >> 6;
+    const int L = (int)threadIdx.x & 63;
+    const int r = 16 * h + (L & 15);
+    // depth (slices read) of this lane's request; padding requests read nothing
+    int m = 0;
+    if (r < B) {
+        const int lev = PER_REQ ? (int)a.level[(int64_t)r * a.level_stride + b] : level_of(a.level, b);
+        m = lev < 4 ? lev : 4;
+    }
+    // which depths the wave's requests read (bit d), and the deepest
+    uint32_t dm = 1u << m;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) dm |= __shfl_xor(dm, o);
+    dm = __builtin_amdgcn_readfirstlane(dm);
+    const int ns = 31 - __builtin_clz(dm);
+    switch (ns) {
+        case 0:   // every request of this wave reads nothing of the block: y = 0
+            if (chunk == 0 && r < B)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        a.y[(int64_t)r * a.N + b * kRows + 16 * j + 4 * (L >> 4) + i] = 0.0f;
+            return;
+        case 1: mwave<1, PER_REQ>(a, B, NH, b, chunk, h, L, m, dm); return;
+        case 2: mwave<2, PER_REQ>(a, B, NH, b, chunk, h, L, m, dm); return;
+        case 3: mwave<3, PER_REQ>(a, B, NH, b, chunk, h, L, m, dm); return;
+        default: mwave<4, PER_REQ>(a, B, NH, b, chunk, h, L, m, dm); return;
+    }
+}
+
+// ------------------------------------------------------------------ host side
+
+struct MPlan {
+    int NH, tpc, n_chunks;
+    size_t counters, partials, limbs, exps, total;
+};
+
+static int64_t g_mfma_target_waves = 256 * 8;
+
+static MPlan mplan(int64_t N, int64_t K, int64_t B) {
+    MPlan p{};
+    p.NH = B > 16 ? 2 : 1;
+    const int n_blocks = (int)(N / kRows);
+    const int n_tiles = (int)(K / kTileCols);
+    const int goal = chunk_goal((int64_t)n_blocks * n_tiles * p.NH, g_mfma_target_waves);
+    const int want = (n_tiles + goal - 1) / goal;
+    int tpc = (n_tiles + want - 1) / want;
+    tpc = (tpc + 3) / 4 * 4;
+    if (tpc > n_tiles) tpc = n_tiles;
+    p.tpc = tpc;
+    p.n_chunks = (n_tiles + tpc - 1) / tpc;
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    p.counters = QAM_WS_COUNTER_BYTES;
+    p.partials = p.n_chunks > 1 ? up((size_t)p.n_chunks * B * N * sizeof(double)) : 0;
+    p.limbs = up((size_t)n_tiles * p.NH * kLimbs * 64 * 16);
+    p.exps = up((size_t)p.n_chunks * 16 * p.NH * sizeof(int));
+    p.total = p.counters + p.partials + p.limbs + p.exps;
+    return p;
+}
+
+// Workspace of the matrix-core route (0 for bad shapes).
+size_t qam_mfma_workspace_bytes(int64_t N, int64_t K, int64_t B) {
+    if (N <= 0 || K <= 0 || N % kRows || K % kTileCols || K > QAM_MAX_K || B < 1 || B > QAM_MAX_BATCH_MFMA) return 0;
+    if (N / kRows * (B > 16 ? 2 : 1) > QAM_MAX_BLOCKS) return 0;
+    return mplan(N, K, B).total;
+}
+
+// The matrix-core route of qam_qmatvec (arguments already checked by the caller).
+int qmatvec_mfma(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
+                 int per_request_maps, float* y, void* workspace, size_t workspace_bytes, hipStream_t s) {
+    const MPlan p = mplan(packed->N, packed->K, B);
+    if ((packed->n_blocks * p.NH) > QAM_MAX_BLOCKS)
+        QAM_FAIL(QAM_ERR_SHAPE, "qmatvec: %lld blocks x %d waves exceed the counter region", (long long)packed->n_blocks, p.NH);
+    if (!workspace) QAM_FAIL(QAM_ERR_WORKSPACE, "qmatvec: workspace of %zu bytes required", p.total);
+    if (workspace_bytes < p.total) QAM_FAIL(QAM_ERR_WORKSPACE, "qmatvec: workspace %zu < %zu bytes", workspace_bytes, p.total);
+    if (!aligned(workspace, 256)) QAM_FAIL(QAM_ERR_ALIGN, "qmatvec: workspace must be 256-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    MItem it{};
+    it.planes = static_cast<const uint8_t*>(packed->planes);
+    it.scales = packed->scales;
+    it.x = x;
+    it.y = y;
+    it.level = level_map;
+    it.level_stride = per_request_maps ? packed->n_blocks : 0;
+    it.counters = reinterpret_cast<uint32_t*>(ws);
+    it.partials = p.partials ? reinterpret_cast<double*>(ws + p.counters) : nullptr;
+    it.limbs = reinterpret_cast<v4i*>(ws + p.counters + p.partials);
+    it.exps = reinterpret_cast<int*>(ws + p.counters + p.partials + p.limbs);
+    it.plane_bytes = packed->N * packed->K / 4;
+    it.N = packed->N;
+    it.K = packed->K;
+    it.n_blocks = (int)packed->n_blocks;
+    it.n_tiles = (int)(packed->K / kTileCols);
+    it.tpc = p.tpc;
+    it.n_chunks = p.n_chunks;
+    const unsigned pre = (unsigned)(p.n_chunks * 16 * p.NH);
+    if (x_dtype == QAM_X_BF16)
+        hipLaunchKernelGGL((limbs_kernel<true>), dim3(pre), dim3(64), 0, s, it, (int)B, p.NH);
+    else
+        hipLaunchKernelGGL((limbs_kernel<false>), dim3(pre), dim3(64), 0, s, it, (int)B, p.NH);
+    const unsigned grid = (unsigned)((int64_t)it.n_blocks * p.n_chunks);
+    if (per_request_maps)
+        hipLaunchKernelGGL((qmm_kernel<true>), dim3(grid), dim3(64 * p.NH), 0, s, it, (int)B, p.NH);
+    else
+        hipLaunchKernelGGL((qmm_kernel<false>), dim3(grid), dim3(64 * p.NH), 0, s, it, (int)B, p.NH);
+    QAM_HIP_CHECK(hipGetLastError());
+    char v[128];
+    snprintf(v, sizeof(v), "qmatvec_mfma B=%lld maps=%s tpc=%d chunks=%d waves/wg=%d", (long long)B,
+             per_request_maps ? "per-request" : "shared", p.tpc, p.n_chunks, p.NH);
+    set_variant(v);
+    return QAM_OK;
+}
+
+}  // namespace qam
+
+extern "C" int qam_set_mfma_target_waves(int waves) {
+    qam::clear_error();
+    if (waves < 64 || waves > (1 << 20)) QAM_FAIL(QAM_ERR_ARG, "set_mfma_target_waves: %d outside [64, 2^20]", waves);
+    qam::g_mfma_target_waves = waves;
+    return QAM_OK;
+}
+

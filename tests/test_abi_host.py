@@ -110,9 +110,12 @@ def test_qmatvec_rejects_bad_arguments(lib):
     assert d.n_blocks == 2 and d.scales == 0x100000 + 128 * 256
     X, Y, M = C.c_void_p(0x200000), C.c_void_p(0x300000), C.c_void_p(0x400000)
     assert lib.qam_qmatvec(X, 0, 0, C.byref(d), M, 0, Y, None, 0, None) == -3        # B = 0
-    assert lib.qam_qmatvec(X, 0, 9, C.byref(d), M, 0, Y, None, 0, None) == -3        # B > 8
+    assert lib.qam_qmatvec(X, 0, 33, C.byref(d), M, 0, Y, None, 0, None) == -3       # B > 32
+    assert lib.qam_qmatvec(X, 0, 9, C.byref(d), M, 0, Y, None, 0, None) == -7        # matrix cores: workspace
+    assert lib.qam_qmatvec(X, 0, 2, C.byref(d), M, 1, Y, None, 0, None) == -7        # per-request maps too
     assert lib.qam_qmatvec(X, 5, 1, C.byref(d), M, 0, Y, None, 0, None) == -3        # dtype
-    assert lib.qam_qmatvec(X, 0, 1, C.byref(d), M, 1, Y, None, 0, None) == -3        # per-request maps
+    assert lib.qam_qmatvec(X, 5, 16, C.byref(d), M, 1, Y, None, 0, None) == -3       # dtype, matrix cores
+    assert lib.qam_qmatvec(X, 0, 1, C.byref(d), M, 2, Y, None, 0, None) == -3        # per_request_maps flag
     assert lib.qam_qmatvec(None, 0, 1, C.byref(d), M, 0, Y, None, 0, None) == -1
     assert lib.qam_qmatvec(C.c_void_p(0x200004), 0, 1, C.byref(d), M, 0, Y, None, 0, None) == -5
     assert lib.qam_qmatvec(X, 0, 1, C.byref(d), M, 0, C.c_void_p(0x200000 + 64), None, 0, None) == -3  # overlap
@@ -131,6 +134,11 @@ def test_workspace_size_is_zero_for_bad_shapes_and_grows_with_batch(lib):
     assert lib.qam_qmatvec_workspace_bytes(100, 64, 1) == 0
     assert lib.qam_qmatvec_workspace_bytes(64, 64, 0) == 0
     assert lib.qam_qmatvec_workspace_bytes(8192, 28672, 8) >= lib.qam_qmatvec_workspace_bytes(8192, 28672, 1)
+    assert lib.qam_qmatvec_workspace_bytes(8192, 28672, 32) > 0
+    assert lib.qam_qmatvec_workspace_bytes(8192, 28672, 33) == 0
+    # matrix-core route: the limb operands of every tile of x for 16 (32) request slots
+    assert lib.qam_qmatvec_workspace_bytes(64, 4096, 16) >= 64 * 3 * 1024
+    assert lib.qam_qmatvec_workspace_bytes(64, 4096, 32) >= 64 * 6 * 1024
 
 
 def test_map_weight_bytes_matches_the_oracle_memory_formula(lib):
