@@ -218,7 +218,7 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   Routes.  Batches of 1 (and small batches with a shared map) run on the
  *   vector ALUs: each 16-byte slice word becomes four int8x4 code words
  *   multiplied by the limbs with v_dot4.  Batches of QAM_MAX_BATCH+1 .. 32,
- *   per-request maps, and shared-map batches from a tunable threshold (4)
+ *   per-request maps, and shared-map batches from a tunable threshold (2)
  *   run on the matrix cores: a pre-pass writes the limbs of x per column
  *   chunk as MFMA B operands, and v_mfma_i32_16x16x64_i8 multiplies the
  *   codes (16 rows x 64 columns per lane group of words) with 16 requests
@@ -310,7 +310,8 @@ typedef struct qam_gemv_item {
     qam_packed     w;          /* descriptor from qam_pack_slices                    */
     const void*    x;          /* (device) [B][w.K], fp32 or bf16, 16-byte aligned   */
     float*         y;          /* (device) [B][w.N]                                  */
-    const uint8_t* level_map;  /* (device) [w.n_blocks], rungs of {0,2,4,6,8}, shared by the B requests */
+    const uint8_t* level_map;  /* (device) rungs of {0,2,4,6,8}: [w.n_blocks] shared by
+                                  the B requests, or [B][w.n_blocks] per request       */
 } qam_gemv_item;
 
 typedef struct qam_group {     /* filled by qam_group_init; treat as opaque          */
@@ -321,10 +322,15 @@ typedef struct qam_group {     /* filled by qam_group_init; treat as opaque     
     size_t  lds_bytes;
     void*   table;             /* (device) descriptor table inside dev_mem           */
     void*   wg_map;            /* (device) workgroup -> item map inside dev_mem      */
+    int     route;             /* 0: dot-product route, 1: matrix-core route         */
+    int     per_request_maps;
+    int64_t n_pre_workgroups;  /* matrix-core route: limb pre-pass workgroups        */
+    void*   pre_map;           /* (device) pre-pass workgroup -> item map            */
 } qam_group;
 
-/* Device bytes qam_group_init needs (0 if the items are invalid). */
-size_t qam_group_bytes(const qam_gemv_item* items, int n_items, int64_t B);
+/* Device bytes qam_group_init needs (0 if the items are invalid).  The route
+ * is chosen as by qam_qmatvec from B and per_request_maps. */
+size_t qam_group_bytes(const qam_gemv_item* items, int n_items, int64_t B, int per_request_maps);
 
 /*
  * qam_group_init -- validate the items (as qam_qmatvec does for each), lay
@@ -336,12 +342,14 @@ size_t qam_group_bytes(const qam_gemv_item* items, int n_items, int64_t B);
  *   Synchronises `s` before returning (one-time set-up, not for graph capture).
  */
 int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dtype,
-                   void* dev_mem, size_t dev_bytes, qam_group* group_out, hipStream_t s);
+                   int per_request_maps, void* dev_mem, size_t dev_bytes, qam_group* group_out,
+                   hipStream_t s);
 
 /*
- * qam_qmatvec_group -- one launch computing y_i = the mixed-depth product of
- *   every item i, with exactly the arithmetic of qam_qmatvec.  Enqueues one
- *   kernel and nothing else (safe to capture in a HIP graph).  Calls on one
+ * qam_qmatvec_group -- one launch (two on the matrix-core route: the limb
+ *   pre-pass, then the product) computing y_i = the mixed-depth product of
+ *   every item i, with exactly the arithmetic of qam_qmatvec.  Enqueues
+ *   kernels and nothing else (safe to capture in a HIP graph).  Calls on one
  *   group must be ordered.
  */
 int qam_qmatvec_group(const qam_group* group, hipStream_t s);

@@ -45,7 +45,8 @@ class QamGemvItem(C.Structure):
 
 class QamGroup(C.Structure):
     _fields_ = [("n_items", C.c_int), ("B", C.c_int64), ("x_dtype", C.c_int), ("n_workgroups", C.c_int64),
-                ("lds_bytes", C.c_size_t), ("table", C.c_void_p), ("wg_map", C.c_void_p)]
+                ("lds_bytes", C.c_size_t), ("table", C.c_void_p), ("wg_map", C.c_void_p), ("route", C.c_int),
+                ("per_request_maps", C.c_int), ("n_pre_workgroups", C.c_int64), ("pre_map", C.c_void_p)]
 
 
 class QamEpilogue(C.Structure):
@@ -89,8 +90,8 @@ SIGNATURES = [
     ("qam_decoder_replay", _I, [_P, _I, _P]),
     ("qam_decoder_destroy", None, [_P]),
     ("qam_escalation_schedule", _I, [_P, _I64, _D, _P, C.POINTER(_I64)]),
-    ("qam_group_bytes", C.c_size_t, [C.POINTER(QamGemvItem), _I, _I64]),
-    ("qam_group_init", _I, [C.POINTER(QamGemvItem), _I, _I64, _I, _P, _SZ, C.POINTER(QamGroup), _P]),
+    ("qam_group_bytes", C.c_size_t, [C.POINTER(QamGemvItem), _I, _I64, _I]),
+    ("qam_group_init", _I, [C.POINTER(QamGemvItem), _I, _I64, _I, _I, _P, _SZ, C.POINTER(QamGroup), _P]),
     ("qam_qmatvec_group", _I, [C.POINTER(QamGroup), _P]),
     ("qam_last_error", C.c_char_p, []),
     ("qam_last_variant", C.c_char_p, []),

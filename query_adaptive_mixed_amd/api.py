@@ -219,17 +219,21 @@ def qmatvec(x: torch.Tensor, packed: PackedMatrix, level_map: torch.Tensor, y: O
 
 
 class GroupedQmatvec:
-    """Many matrices with their own x, y and level map, one launch per call.
+    """Many matrices with their own x, y and level map, one launch per call
+    (two on the matrix-core route).
 
     ``items`` is a sequence of (PackedMatrix, x [B, K], y [B, N], level_map)
-    tuples; the tensors are bound once (keep them alive and update them in
-    place), and every ``run()`` recomputes all the y from the bound buffers."""
+    tuples, the maps all [n_blocks] (shared by the B requests) or all
+    [B, n_blocks] (per request); the tensors are bound once (keep them alive
+    and update them in place), and every ``run()`` recomputes all the y from
+    the bound buffers."""
 
     def __init__(self, items, device="cuda"):
         n = len(items)
         arr = (L.QamGemvItem * n)()
         B = None
         xdt = None
+        per_request = None
         self._keep = []
         for i, (pm, x, y, lv) in enumerate(items):
             _require_cuda(x, "x")
@@ -239,19 +243,27 @@ class GroupedQmatvec:
             d = L.QAM_X_F32 if x.dtype == torch.float32 else (L.QAM_X_BF16 if x.dtype == torch.bfloat16 else None)
             if d is None:
                 raise TypeError("x must be float32 or bfloat16")
+            pr = lv.dim() == 2
             if B is None:
-                B, xdt = b, d
-            elif (b, d) != (B, xdt):
-                raise ValueError("every item of a group needs the same batch and x dtype")
+                B, xdt, per_request = b, d, pr
+            elif (b, d, pr) != (B, xdt, per_request):
+                raise ValueError("every item of a group needs the same batch, x dtype and map kind")
+            if pr and tuple(lv.shape) != (B, pm.n_blocks):
+                raise ValueError("a per-request level_map must be [B, n_blocks]")
             arr[i].w = pm.desc
             arr[i].x, arr[i].y, arr[i].level_map = x.data_ptr(), y.data_ptr(), lv.data_ptr()
             self._keep.append((pm, x, y, lv))
-        nbytes = int(L.lib().qam_group_bytes(arr, n, B))
+        nbytes = int(L.lib().qam_group_bytes(arr, n, B, int(per_request)))
         if nbytes == 0:
             raise L.QamError(-2, "invalid group items")
         self.mem = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         self.desc = L.QamGroup()
-        L.check(L.lib().qam_group_init(arr, n, B, xdt, _ptr(self.mem), nbytes, C.byref(self.desc), _stream_handle()))
+        L.check(L.lib().qam_group_init(arr, n, B, xdt, int(per_request), _ptr(self.mem), nbytes, C.byref(self.desc),
+                                       _stream_handle()))
+
+    @property
+    def route(self) -> str:
+        return "mfma" if self.desc.route == 1 else "dot4"
 
     def run(self) -> None:
         L.check(L.lib().qam_qmatvec_group(C.byref(self.desc), _stream_handle()))

@@ -586,9 +586,9 @@ extern "C" int qam_qmatvec_ep(const void* x, int x_dtype, int64_t B, const qam_p
 }
 
 // Smallest batch with a shared map that takes the matrix-core route.
-static int g_mfma_min_batch = 4;
+static int g_mfma_min_batch = 2;
 
-static bool mfma_route(int64_t B, int per_request_maps) {
+bool qam::mfma_route(int64_t B, int per_request_maps) {
     return (per_request_maps && B > 1) || B > QAM_MAX_BATCH || B >= g_mfma_min_batch;
 }
 
@@ -645,16 +645,21 @@ static int layout_group(const qam_gemv_item* items, int n_items, int64_t B, Grou
 
 }  // namespace qam
 
-extern "C" size_t qam_group_bytes(const qam_gemv_item* items, int n_items, int64_t B) {
+extern "C" size_t qam_group_bytes(const qam_gemv_item* items, int n_items, int64_t B, int per_request_maps) {
+    if (per_request_maps != 0 && per_request_maps != 1) return 0;
+    if (mfma_route(B, per_request_maps)) return mfma_group_bytes(items, n_items, B);
     GroupLayout g;
     if (layout_group(items, n_items, B, g) != QAM_OK) return 0;
     return g.total;
 }
 
-extern "C" int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dtype, void* dev_mem,
-                              size_t dev_bytes, qam_group* group_out, hipStream_t s) {
+extern "C" int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dtype, int per_request_maps,
+                              void* dev_mem, size_t dev_bytes, qam_group* group_out, hipStream_t s) {
     clear_error();
     if (!group_out || !dev_mem) QAM_FAIL(QAM_ERR_NULL, "group_init: null pointer");
+    if (per_request_maps != 0 && per_request_maps != 1) QAM_FAIL(QAM_ERR_ARG, "group_init: per_request_maps must be 0 or 1");
+    if (mfma_route(B, per_request_maps))
+        return mfma_group_init(items, n_items, B, x_dtype, per_request_maps, dev_mem, dev_bytes, group_out, s);
     GroupLayout g;
     if (int rc = layout_group(items, n_items, B, g)) return rc;
     if (dev_bytes < g.total) QAM_FAIL(QAM_ERR_WORKSPACE, "group_init: %zu < %zu bytes", dev_bytes, g.total);
@@ -695,13 +700,22 @@ extern "C" int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B
     group_out->lds_bytes = lds_bytes_for(B);
     group_out->table = table;
     group_out->wg_map = wgmap;
+    group_out->route = 0;
+    group_out->per_request_maps = 0;
+    group_out->n_pre_workgroups = 0;
+    group_out->pre_map = nullptr;
     return QAM_OK;
 }
 
 extern "C" int qam_qmatvec_group(const qam_group* group, hipStream_t s) {
     clear_error();
     if (!group || !group->table || !group->wg_map) QAM_FAIL(QAM_ERR_NULL, "qmatvec_group: uninitialised group");
-    if (group->B < 1 || group->B > QAM_MAX_BATCH || group->n_workgroups < 1)
+    if (group->route == 1) {
+        if (!group->pre_map || group->B < 2 || group->B > QAM_MAX_BATCH_MFMA || group->n_workgroups < 1)
+            QAM_FAIL(QAM_ERR_ARG, "qmatvec_group: corrupt group descriptor");
+        return mfma_group_run(group, s);
+    }
+    if (group->route != 0 || group->B < 1 || group->B > QAM_MAX_BATCH || group->n_workgroups < 1)
         QAM_FAIL(QAM_ERR_ARG, "qmatvec_group: corrupt group descriptor");
     Common c{};
     c.items = static_cast<const Item*>(group->table);

@@ -117,6 +117,11 @@ int check_item(const void* x, int x_dtype, int64_t B, const qam_packed* packed, 
 size_t qam_mfma_workspace_bytes(int64_t N, int64_t K, int64_t B);
 int qmatvec_mfma(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
                  int per_request_maps, float* y, void* workspace, size_t workspace_bytes, hipStream_t s);
+size_t mfma_group_bytes(const qam_gemv_item* items, int n_items, int64_t B);
+int mfma_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dtype, int per_request_maps,
+                    void* dev_mem, size_t dev_bytes, qam_group* out, hipStream_t s);
+int mfma_group_run(const qam_group* g, hipStream_t s);
+bool mfma_route(int64_t B, int per_request_maps);
 // Enqueues one single-matrix product launch (grid = n_chunks * n_quads).
 void launch_single(int64_t B, const Item& it, const Common& c, int64_t grid, hipStream_t s);
 

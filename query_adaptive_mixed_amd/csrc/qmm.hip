@@ -46,17 +46,37 @@ struct MItem {
     int64_t plane_bytes;
     int64_t N, K;
     int n_blocks, n_tiles, tpc, n_chunks;
+    int wg_begin;              // grouped launches: first product workgroup of this item
+    int pre_begin;             // grouped launches: first pre-pass workgroup of this item
+};
+
+struct MCommon {
+    const MItem* items;        // grouped launches: the descriptor table
+    const int* wg_item;        // grouped launches: item of every product workgroup
+    const int* pre_item;       // grouped launches: item of every pre-pass workgroup
+    int B;
+    int NH;
 };
 
 // ------------------------------------------------------------------ x -> limbs
 
 // One wavefront per (column chunk, request slot r < 16 NH): the chunk's
 // largest |x| sets the exponent; padding slots r >= B get zero limbs.
-template <bool XBF16>
-__global__ __launch_bounds__(64) void limbs_kernel(MItem a, int B, int NH) {
+template <bool XBF16, bool GROUPED>
+__global__ __launch_bounds__(64) void limbs_kernel(MItem single, MCommon c) {
+    MItem a;
+    int local;
+    if constexpr (GROUPED) {
+        a = c.items[c.pre_item[blockIdx.x]];
+        local = (int)blockIdx.x - a.pre_begin;
+    } else {
+        a = single;
+        local = (int)blockIdx.x;
+    }
+    const int B = c.B, NH = c.NH;
     const int slots = 16 * NH;
-    const int chunk = blockIdx.x / slots;
-    const int r = blockIdx.x % slots;
+    const int chunk = local / slots;
+    const int r = local % slots;
     const int L = threadIdx.x;
     const int t0 = chunk * a.tpc;
     const int ncol = min(a.tpc, a.n_tiles - t0) * 64;
@@ -293,10 +313,20 @@ __device__ __forceinline__ void mwave(const MItem& a, int B, int NH, int b, int 
 
 // Workgroup = NH wavefronts = one (block, column chunk); wave h serves
 // requests 16h .. 16h+15.
-template <bool PER_REQ>
-__global__ __launch_bounds__(128) void qmm_kernel(MItem a, int B, int NH) {
-    const int chunk = (int)blockIdx.x % a.n_chunks;
-    const int b = (int)blockIdx.x / a.n_chunks;
+template <bool PER_REQ, bool GROUPED>
+__global__ __launch_bounds__(128) void qmm_kernel(MItem single, MCommon c) {
+    MItem a;
+    int local;
+    if constexpr (GROUPED) {
+        a = c.items[c.wg_item[blockIdx.x]];
+        local = (int)blockIdx.x - a.wg_begin;
+    } else {
+        a = single;
+        local = (int)blockIdx.x;
+    }
+    const int B = c.B, NH = c.NH;
+    const int chunk = local % a.n_chunks;
+    const int b = local / a.n_chunks;
     const int h = (int)threadIdx.x >> 6;
     const int L = (int)threadIdx.x & 63;
     const int r = 16 * h + (L & 15);
@@ -330,19 +360,34 @@ __global__ __launch_bounds__(128) void qmm_kernel(MItem a, int B, int NH) {
 
 // ------------------------------------------------------------------ host side
 
+template <bool GROUPED>
+static void launch_mfma(const MItem& it, const MCommon& c, bool xbf16, bool per_req, int64_t pre_grid, int64_t grid,
+                        hipStream_t s) {
+    const dim3 blk(64 * c.NH);
+    if (xbf16)
+        hipLaunchKernelGGL((limbs_kernel<true, GROUPED>), dim3((unsigned)pre_grid), dim3(64), 0, s, it, c);
+    else
+        hipLaunchKernelGGL((limbs_kernel<false, GROUPED>), dim3((unsigned)pre_grid), dim3(64), 0, s, it, c);
+    if (per_req)
+        hipLaunchKernelGGL((qmm_kernel<true, GROUPED>), dim3((unsigned)grid), blk, 0, s, it, c);
+    else
+        hipLaunchKernelGGL((qmm_kernel<false, GROUPED>), dim3((unsigned)grid), blk, 0, s, it, c);
+}
+
 struct MPlan {
     int NH, tpc, n_chunks;
     size_t counters, partials, limbs, exps, total;
 };
 
-static int64_t g_mfma_target_waves = 256 * 8;
+static int64_t g_mfma_target_waves = 256 * 32;
 
-static MPlan mplan(int64_t N, int64_t K, int64_t B) {
+static int mfma_waves_per_wg(int64_t B) { return B > 16 ? 2 : 1; }
+
+// Chunking of one matrix on the matrix-core route, for a chunk length goal.
+static MPlan mplan_goal(int64_t N, int64_t K, int64_t B, int goal) {
     MPlan p{};
-    p.NH = B > 16 ? 2 : 1;
-    const int n_blocks = (int)(N / kRows);
+    p.NH = mfma_waves_per_wg(B);
     const int n_tiles = (int)(K / kTileCols);
-    const int goal = chunk_goal((int64_t)n_blocks * n_tiles * p.NH, g_mfma_target_waves);
     const int want = (n_tiles + goal - 1) / goal;
     int tpc = (n_tiles + want - 1) / want;
     tpc = (tpc + 3) / 4 * 4;
@@ -356,6 +401,30 @@ static MPlan mplan(int64_t N, int64_t K, int64_t B) {
     p.exps = up((size_t)p.n_chunks * 16 * p.NH * sizeof(int));
     p.total = p.counters + p.partials + p.limbs + p.exps;
     return p;
+}
+
+static MPlan mplan(int64_t N, int64_t K, int64_t B) {
+    const int64_t block_tiles = N / kRows * (K / kTileCols) * mfma_waves_per_wg(B);
+    return mplan_goal(N, K, B, chunk_goal(block_tiles, g_mfma_target_waves));
+}
+
+static MItem make_mitem(const void* x, const qam_packed* w, const uint8_t* level_map, float* y, int per_request,
+                        const MPlan& p) {
+    MItem it{};
+    it.planes = static_cast<const uint8_t*>(w->planes);
+    it.scales = w->scales;
+    it.x = x;
+    it.y = y;
+    it.level = level_map;
+    it.level_stride = per_request ? w->n_blocks : 0;
+    it.plane_bytes = w->N * w->K / 4;
+    it.N = w->N;
+    it.K = w->K;
+    it.n_blocks = (int)w->n_blocks;
+    it.n_tiles = (int)(w->K / kTileCols);
+    it.tpc = p.tpc;
+    it.n_chunks = p.n_chunks;
+    return it;
 }
 
 // Workspace of the matrix-core route (0 for bad shapes).
@@ -375,38 +444,145 @@ int qmatvec_mfma(const void* x, int x_dtype, int64_t B, const qam_packed* packed
     if (workspace_bytes < p.total) QAM_FAIL(QAM_ERR_WORKSPACE, "qmatvec: workspace %zu < %zu bytes", workspace_bytes, p.total);
     if (!aligned(workspace, 256)) QAM_FAIL(QAM_ERR_ALIGN, "qmatvec: workspace must be 256-byte aligned");
     char* ws = static_cast<char*>(workspace);
-    MItem it{};
-    it.planes = static_cast<const uint8_t*>(packed->planes);
-    it.scales = packed->scales;
-    it.x = x;
-    it.y = y;
-    it.level = level_map;
-    it.level_stride = per_request_maps ? packed->n_blocks : 0;
+    MItem it = make_mitem(x, packed, level_map, y, per_request_maps, p);
     it.counters = reinterpret_cast<uint32_t*>(ws);
     it.partials = p.partials ? reinterpret_cast<double*>(ws + p.counters) : nullptr;
     it.limbs = reinterpret_cast<v4i*>(ws + p.counters + p.partials);
     it.exps = reinterpret_cast<int*>(ws + p.counters + p.partials + p.limbs);
-    it.plane_bytes = packed->N * packed->K / 4;
-    it.N = packed->N;
-    it.K = packed->K;
-    it.n_blocks = (int)packed->n_blocks;
-    it.n_tiles = (int)(packed->K / kTileCols);
-    it.tpc = p.tpc;
-    it.n_chunks = p.n_chunks;
-    const unsigned pre = (unsigned)(p.n_chunks * 16 * p.NH);
-    if (x_dtype == QAM_X_BF16)
-        hipLaunchKernelGGL((limbs_kernel<true>), dim3(pre), dim3(64), 0, s, it, (int)B, p.NH);
-    else
-        hipLaunchKernelGGL((limbs_kernel<false>), dim3(pre), dim3(64), 0, s, it, (int)B, p.NH);
-    const unsigned grid = (unsigned)((int64_t)it.n_blocks * p.n_chunks);
-    if (per_request_maps)
-        hipLaunchKernelGGL((qmm_kernel<true>), dim3(grid), dim3(64 * p.NH), 0, s, it, (int)B, p.NH);
-    else
-        hipLaunchKernelGGL((qmm_kernel<false>), dim3(grid), dim3(64 * p.NH), 0, s, it, (int)B, p.NH);
+    MCommon c{};
+    c.B = (int)B;
+    c.NH = p.NH;
+    launch_mfma<false>(it, c, x_dtype == QAM_X_BF16, per_request_maps != 0, (int64_t)p.n_chunks * 16 * p.NH,
+                       (int64_t)it.n_blocks * p.n_chunks, s);
     QAM_HIP_CHECK(hipGetLastError());
     char v[128];
     snprintf(v, sizeof(v), "qmatvec_mfma B=%lld maps=%s tpc=%d chunks=%d waves/wg=%d", (long long)B,
              per_request_maps ? "per-request" : "shared", p.tpc, p.n_chunks, p.NH);
+    set_variant(v);
+    return QAM_OK;
+}
+
+// ------------------------------------------------------------------ grouped launches
+
+struct MGroupLayout {
+    std::vector<MPlan> plans;
+    size_t partials = 0, limbs = 0, exps = 0, table = 0, wgmap = 0, premap = 0, total = 0;
+    int64_t n_wg = 0, n_pre = 0, blocks = 0;
+    int NH = 1;
+};
+
+static int mfma_layout(const qam_gemv_item* items, int n_items, int64_t B, MGroupLayout& g) {
+    if (!items || n_items < 1) QAM_FAIL(QAM_ERR_ARG, "group: need at least one item");
+    if (B < 2 || B > QAM_MAX_BATCH_MFMA) QAM_FAIL(QAM_ERR_ARG, "group: B=%lld outside [2, %d]", (long long)B, QAM_MAX_BATCH_MFMA);
+    g.NH = mfma_waves_per_wg(B);
+    int64_t block_tiles = 0;
+    for (int i = 0; i < n_items; ++i) {
+        const qam_packed& w = items[i].w;
+        if (w.N <= 0 || w.N % kRows || w.K <= 0 || w.K % kTileCols || w.K > QAM_MAX_K)
+            QAM_FAIL(QAM_ERR_SHAPE, "group: item %d has a bad shape", i);
+        g.blocks += w.N / kRows;
+        block_tiles += w.N / kRows * (w.K / kTileCols) * g.NH;
+    }
+    if (g.blocks * g.NH > QAM_MAX_BLOCKS)
+        QAM_FAIL(QAM_ERR_SHAPE, "group: %lld blocks x %d waves exceed %d", (long long)g.blocks, g.NH, QAM_MAX_BLOCKS);
+    const int goal = chunk_goal(block_tiles, g_mfma_target_waves);
+    for (int i = 0; i < n_items; ++i) {
+        const MPlan p = mplan_goal(items[i].w.N, items[i].w.K, B, goal);
+        g.plans.push_back(p);
+        g.partials += p.partials;
+        g.limbs += p.limbs;
+        g.exps += p.exps;
+        g.n_wg += (int64_t)(items[i].w.N / kRows) * p.n_chunks;
+        g.n_pre += (int64_t)p.n_chunks * 16 * g.NH;
+    }
+    if (g.n_wg > 0x7FFFFFFF || g.n_pre > 0x7FFFFFFF) QAM_FAIL(QAM_ERR_SHAPE, "group: too many workgroups");
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    g.table = up((size_t)n_items * sizeof(MItem));
+    g.wgmap = up((size_t)g.n_wg * sizeof(int));
+    g.premap = up((size_t)g.n_pre * sizeof(int));
+    g.total = QAM_WS_COUNTER_BYTES + g.partials + g.limbs + g.exps + g.table + g.wgmap + g.premap;
+    return QAM_OK;
+}
+
+size_t mfma_group_bytes(const qam_gemv_item* items, int n_items, int64_t B) {
+    MGroupLayout g;
+    if (mfma_layout(items, n_items, B, g) != QAM_OK) return 0;
+    return g.total;
+}
+
+int mfma_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dtype, int per_request_maps,
+                    void* dev_mem, size_t dev_bytes, qam_group* out, hipStream_t s) {
+    MGroupLayout g;
+    if (int rc = mfma_layout(items, n_items, B, g)) return rc;
+    if (dev_bytes < g.total) QAM_FAIL(QAM_ERR_WORKSPACE, "group_init: %zu < %zu bytes", dev_bytes, g.total);
+    if (!aligned(dev_mem, 256)) QAM_FAIL(QAM_ERR_ALIGN, "group_init: device memory must be 256-byte aligned");
+    char* base = static_cast<char*>(dev_mem);
+    char* partials = base + QAM_WS_COUNTER_BYTES;
+    char* limbs = partials + g.partials;
+    char* exps = limbs + g.limbs;
+    char* table = exps + g.exps;
+    char* wgmap = table + g.table;
+    char* premap = wgmap + g.wgmap;
+    std::vector<MItem> host_items(n_items);
+    std::vector<int> hw((size_t)g.n_wg), hp((size_t)g.n_pre);
+    int64_t wg = 0, pre = 0, blk = 0;
+    size_t po = 0, lo = 0, eo = 0;
+    for (int i = 0; i < n_items; ++i) {
+        const qam_gemv_item& gi = items[i];
+        if (int rc = check_item(gi.x, x_dtype, B, &gi.w, gi.level_map, gi.y, "group_init", QAM_OUT_STORE)) return rc;
+        const MPlan& p = g.plans[i];
+        MItem it = make_mitem(gi.x, &gi.w, gi.level_map, gi.y, per_request_maps, p);
+        it.counters = reinterpret_cast<uint32_t*>(base) + blk * g.NH;
+        it.partials = p.partials ? reinterpret_cast<double*>(partials + po) : nullptr;
+        it.limbs = reinterpret_cast<v4i*>(limbs + lo);
+        it.exps = reinterpret_cast<int*>(exps + eo);
+        po += p.partials;
+        lo += p.limbs;
+        eo += p.exps;
+        blk += it.n_blocks;
+        it.wg_begin = (int)wg;
+        it.pre_begin = (int)pre;
+        const int64_t n = (int64_t)it.n_blocks * p.n_chunks;
+        for (int64_t k = 0; k < n; ++k) hw[(size_t)(wg + k)] = i;
+        wg += n;
+        const int64_t np = (int64_t)p.n_chunks * 16 * g.NH;
+        for (int64_t k = 0; k < np; ++k) hp[(size_t)(pre + k)] = i;
+        pre += np;
+        host_items[i] = it;
+    }
+    QAM_HIP_CHECK(hipMemsetAsync(base, 0, QAM_WS_COUNTER_BYTES, s));
+    QAM_HIP_CHECK(hipMemcpyAsync(table, host_items.data(), sizeof(MItem) * n_items, hipMemcpyHostToDevice, s));
+    QAM_HIP_CHECK(hipMemcpyAsync(wgmap, hw.data(), sizeof(int) * hw.size(), hipMemcpyHostToDevice, s));
+    QAM_HIP_CHECK(hipMemcpyAsync(premap, hp.data(), sizeof(int) * hp.size(), hipMemcpyHostToDevice, s));
+    QAM_HIP_CHECK(hipStreamSynchronize(s));
+    out->n_items = n_items;
+    out->B = B;
+    out->x_dtype = x_dtype;
+    out->n_workgroups = g.n_wg;
+    out->lds_bytes = 0;
+    out->table = table;
+    out->wg_map = wgmap;
+    out->route = 1;
+    out->per_request_maps = per_request_maps;
+    out->n_pre_workgroups = g.n_pre;
+    out->pre_map = premap;
+    return QAM_OK;
+}
+
+int mfma_group_run(const qam_group* g, hipStream_t s) {
+    MCommon c{};
+    c.items = static_cast<const MItem*>(g->table);
+    c.wg_item = static_cast<const int*>(g->wg_map);
+    c.pre_item = static_cast<const int*>(g->pre_map);
+    c.B = (int)g->B;
+    c.NH = mfma_waves_per_wg(g->B);
+    MItem dummy{};
+    launch_mfma<true>(dummy, c, g->x_dtype == QAM_X_BF16, g->per_request_maps != 0, g->n_pre_workgroups,
+                      g->n_workgroups, s);
+    QAM_HIP_CHECK(hipGetLastError());
+    char v[128];
+    snprintf(v, sizeof(v), "qmatvec_mfma_group items=%d B=%lld maps=%s wg=%lld", g->n_items, (long long)g->B,
+             g->per_request_maps ? "per-request" : "shared", (long long)g->n_workgroups);
     set_variant(v);
     return QAM_OK;
 }

@@ -163,3 +163,42 @@ def test_batched_layer_workload(qam):
         blocks = np.sort(rng.choice(m.n_blocks, 12, replace=False))
         rows = np.concatenate([np.arange(64 * b, 64 * b + 64) for b in blocks])
         check(y[:, rows], W[rows], sc[rows], x, lv[:, blocks], True, m.name)
+
+
+@pytest.mark.parametrize("B,per_request", [(16, True), (32, True), (8, False), (3, True)])
+def test_grouped_matrix_cores(qam, B, per_request):
+    """Several matrices in one grouped launch (pre-pass + product), each
+    checked against the oracle; replays of a captured group agree bit for bit."""
+    rng = np.random.default_rng(40 + B)
+    shapes = [(256, 1024), (512, 4096), (128, 14336), (64, 64)]
+    mats, items = [], []
+    for N, K in shapes:
+        W = rng.integers(-128, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+        sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+        x = rng.standard_normal((B, K)).astype(np.float32)
+        lv = rng.integers(0, 5, size=(B, N // 64) if per_request else N // 64).astype(np.uint8)
+        pm = qam.pack_slices(dev(W), dev(sc))
+        y = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+        mats.append((W, sc, x, lv))
+        items.append((pm, dev(x), y, dev(lv)))
+    g = qam.GroupedQmatvec(items)
+    assert g.route == "mfma"
+    g.run()
+    first = [host(it[2]).copy() for it in items]
+    for (W, sc, x, lv), y in zip(mats, first):
+        check(y, W, sc, x, lv, per_request, (W.shape, B))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g.run()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.run()
+    for rep in range(3):
+        for it in items:
+            it[2].fill_(float("nan"))
+        graph.replay()
+        for it, want in zip(items, first):
+            assert np.array_equal(host(it[2]), want), rep
+        qam.qmatvec(items[0][1], items[0][0], items[0][3])   # eager work between replays

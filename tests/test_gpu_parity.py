@@ -193,6 +193,16 @@ def test_qmatvec_shape_battery(qam, N, K, B):
     pm = pack(qam, W, sc)
     y = host(qam.qmatvec(dev(x), pm, dev(lv)))
     check_y(y, W, sc, x, lv, (N, K, B))
+    if B > 1:
+        # the same batch on the dot-product route (the matrix cores take it by default)
+        from query_adaptive_mixed_amd import _lib as L
+        assert L.lib().qam_set_mfma_min_batch(9) == 0
+        try:
+            y = host(qam.qmatvec(dev(x), pm, dev(lv)))
+            assert "dot4" in qam.last_variant()
+        finally:
+            assert L.lib().qam_set_mfma_min_batch(2) == 0
+        check_y(y, W, sc, x, lv, ("dot4", N, K, B))
 
 
 def test_qmatvec_exact_integer_cases(qam):
