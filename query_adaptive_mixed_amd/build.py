@@ -33,6 +33,12 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-file extras.  The matrix-core kernels keep their MFMA accumulators in
+# ordinary VGPRs: with AGPR accumulators the register allocator rotates them
+# through copies on every ring step of the unrolled loop.
+EXTRA_FLAGS = {
+    "qmm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def hipcc() -> str:
@@ -44,7 +50,7 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *CFLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *CFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -11,14 +11,17 @@
 //
 // Arithmetic (exact, as in the batch-1 kernel): a pre-pass turns each
 // request's x, per column chunk, into a 24-bit fixed point held as three int8
-// limbs, laid out as the B operands of v_mfma_i32_16x16x64_i8 (16 columns =
-// 16 requests of one limb); codes are the A operands (16 rows x 64 columns,
-// exactly the words a lane loads); i32 accumulation is exact; limbs are
-// combined in fp64 at the end of the chunk.
+// limbs, laid out as B operands of v_mfma_i32_16x16x64_i8: column c = 3 rr + l
+// of a set of 16 requests holds limb l of request rr, 16 columns per MFMA
+// (NCG column groups per set: 1 for up to 5 requests, 2 up to 10, 3 up to
+// 16).  Codes are the A operands (16 rows x 64 columns, exactly the words a
+// lane loads); i32 accumulation is exact; the limbs of a request are combined
+// in fp64 after the chunk, through an LDS table of the block's 64 x 16 NCG
+// integer sums.
 //
-// Wavefront h of a workgroup serves requests 16h .. 16h+15 of one (block,
-// column chunk); MFMA output lane L holds rows 4(L>>4)+i (i = 0..3) of each
-// 16-row group and request 16h + (L & 15).
+// A workgroup is one (block, column chunk): wave (ks, h) serves request set
+// h on the chunk's tiles ks, ks + KS, ...; the KS tables of a set are summed
+// when the outputs are formed, one row per lane, so y is written coalesced.
 
 #include <algorithm>
 #include <vector>
@@ -39,10 +42,10 @@ struct MItem {
     float* y;                  // [B][N]
     const uint8_t* level;      // [B][n_blocks] (per request) or [n_blocks]
     int64_t level_stride;      // n_blocks (per request) or 0
-    v4i* limbs;                // [n_tiles][NH][3][64] 16-byte B operands
+    v4i* limbs;                // [n_tiles][NH][NCG][64] 16-byte B operands
     int* exps;                 // [n_chunks][16 NH]
     double* partials;          // [n_chunks][B][N] (split K only)
-    uint32_t* counters;        // [n_blocks][NH]   (split K only)
+    uint32_t* counters;        // [n_blocks]       (split K only)
     int64_t plane_bytes;
     int64_t N, K;
     int n_blocks, n_tiles, tpc, n_chunks;
@@ -55,13 +58,22 @@ struct MCommon {
     const int* wg_item;        // grouped launches: item of every product workgroup
     const int* pre_item;       // grouped launches: item of every pre-pass workgroup
     int B;
-    int NH;
+    int NH;                    // request sets of 16 per workgroup
+    int KS;                    // waves per request set splitting a chunk's tiles
+    int NCG;                   // 16-column groups per request set
 };
+
+// Depth (slices read, 0..4) of request r in block b.
+template <bool PER_REQ>
+__device__ __forceinline__ int depth_of(const MItem& a, int r, int b) {
+    const int lev = PER_REQ ? (int)a.level[(int64_t)r * a.level_stride + b] : level_of(a.level, b);
+    return lev < 4 ? lev : 4;
+}
 
 // ------------------------------------------------------------------ x -> limbs
 
 // One wavefront per (column chunk, request slot r < 16 NH): the chunk's
-// largest |x| sets the exponent; padding slots r >= B get zero limbs.
+// largest |x| sets the exponent; slots r >= B get zero limbs.
 template <bool XBF16, bool GROUPED>
 __global__ __launch_bounds__(64) void limbs_kernel(MItem single, MCommon c) {
     MItem a;
@@ -73,7 +85,7 @@ __global__ __launch_bounds__(64) void limbs_kernel(MItem single, MCommon c) {
         a = single;
         local = (int)blockIdx.x;
     }
-    const int B = c.B, NH = c.NH;
+    const int B = c.B, NH = c.NH, NCG = c.NCG;
     const int slots = 16 * NH;
     const int chunk = local / slots;
     const int r = local % slots;
@@ -100,7 +112,7 @@ __global__ __launch_bounds__(64) void limbs_kernel(MItem single, MCommon c) {
     if (m > 0.0f) frexpf(m, &e);
     if (L == 0) a.exps[chunk * slots + r] = nonfinite ? kBadExp : e;
     const int sh = kFrac - e;
-    const int h = r >> 4, n = r & 15;
+    const int h = r >> 4, rr = r & 15;
     uint8_t* lb = reinterpret_cast<uint8_t*>(a.limbs);
     for (int k = 4 * L; k < ncol; k += 256) {
         uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
@@ -114,9 +126,11 @@ __global__ __launch_bounds__(64) void limbs_kernel(MItem single, MCommon c) {
         const int byte = (int)(kk & 15);
 #pragma unroll
         for (int l = 0; l < kLimbs; ++l) {
+            const int col = 3 * rr + l;          // B-operand column of this limb
+            if (col >= 16 * NCG) break;          // beyond the set's columns (padding slots only)
             const uint32_t word = ((w0 >> (8 * l)) & 0xFFu) | (((w1 >> (8 * l)) & 0xFFu) << 8) |
                                   (((w2 >> (8 * l)) & 0xFFu) << 16) | (((w3 >> (8 * l)) & 0xFFu) << 24);
-            const int64_t unit = ((t * NH + h) * kLimbs + l) * 64 + kg * 16 + n;
+            const int64_t unit = ((t * NH + h) * NCG + (col >> 4)) * 64 + kg * 16 + (col & 15);
             *reinterpret_cast<uint32_t*>(lb + unit * 16 + byte) = word;
         }
     }
@@ -124,32 +138,33 @@ __global__ __launch_bounds__(64) void limbs_kernel(MItem single, MCommon c) {
 
 // ------------------------------------------------------------------ product
 
-// Tiles in flight: two halves of H tiles, each tile NS weight loads and three
+// Tiles in flight: two halves of H tiles, each tile NS weight loads and NCG
 // limb loads per lane.
-template <int NS>
+template <int NS, int NCG>
 struct MRing {
-    static constexpr int H = NS <= 2 ? 2 : 1;
+    static constexpr int H = NS + NCG <= 4 ? 2 : 1;
     static constexpr int PF = 2 * H;
 };
 
-template <int NS, int H>
-__device__ __forceinline__ void mload(u32x4 (&w)[H][NS], v4i (&x)[H][kLimbs], const uint8_t* wbase, int64_t pb,
-                                      const v4i* xbase, int64_t xstride, int tile, int last) {
+template <int NS, int NCG, int H>
+__device__ __forceinline__ void mload(u32x4 (&w)[H][NS], v4i (&x)[H][NCG], const uint8_t* wbase, int64_t pb,
+                                      int64_t wstride, const v4i* xbase, int64_t xstride, int tile, int last) {
 #pragma unroll
     for (int u = 0; u < H; ++u) {
         const int t = min(tile + u, last);
 #pragma unroll
-        for (int p = 0; p < NS; ++p) w[u][p] = load_plane(wbase + p * pb + (int64_t)t * kTileBytes);
+        for (int p = 0; p < NS; ++p) w[u][p] = load_plane(wbase + p * pb + (int64_t)t * wstride);
 #pragma unroll
-        for (int l = 0; l < kLimbs; ++l) x[u][l] = *(global_v4i*)(xbase + t * xstride + l * 64);
+        for (int g = 0; g < NCG; ++g) x[u][g] = *(global_v4i*)(xbase + t * xstride + g * 64);
     }
 }
 
-// One tile: for each depth d present among the wave's requests (bit d of
-// `dmask`), the codes at depth d times the limbs of the requests reading d.
-template <int NS, bool PER_REQ>
-__device__ __forceinline__ void mtile(const u32x4 (&w)[NS], const v4i (&xl)[kLimbs], int m_lane, uint32_t dmask,
-                                      v4i (&acc)[4][kLimbs]) {
+// One tile: for each depth d present among the set's requests (bit d of
+// `dmask`), the codes at depth d times the limbs of the requests reading d
+// (mcol[g]: depth of the request owning this lane's column in group g).
+template <int NS, int NCG, bool PER_REQ>
+__device__ __forceinline__ void mtile(const u32x4 (&w)[NS], const v4i (&xl)[NCG], const int (&mcol)[NCG],
+                                      uint32_t dmask, v4i (&acc)[4][NCG]) {
     uint32_t q[4][4];   // [j][u]: masked slice bits so far, unrotated
 #pragma unroll
     for (int p = 0; p < NS; ++p) {
@@ -170,14 +185,14 @@ __device__ __forceinline__ void mtile(const u32x4 (&w)[NS], const v4i (&xl)[kLim
         }
         const bool use = PER_REQ ? ((dmask >> (p + 1)) & 1u) != 0 : p == NS - 1;
         if (use) {
-            v4i bm[kLimbs];
+            v4i bm[NCG];
 #pragma unroll
-            for (int l = 0; l < kLimbs; ++l) {
+            for (int g = 0; g < NCG; ++g) {
                 if constexpr (PER_REQ) {
-                    const bool mine = m_lane == p + 1;
-                    bm[l] = v4i{mine ? xl[l].x : 0, mine ? xl[l].y : 0, mine ? xl[l].z : 0, mine ? xl[l].w : 0};
+                    const bool mine = mcol[g] == p + 1;
+                    bm[g] = v4i{mine ? xl[g].x : 0, mine ? xl[g].y : 0, mine ? xl[g].z : 0, mine ? xl[g].w : 0};
                 } else {
-                    bm[l] = xl[l];
+                    bm[g] = xl[g];
                 }
             }
 #pragma unroll
@@ -185,136 +200,78 @@ __device__ __forceinline__ void mtile(const u32x4 (&w)[NS], const v4i (&xl)[kLim
                 const v4i A = v4i{(int)q[j][0], (int)rotl32(q[j][1], 2), (int)rotl32(q[j][2], 4),
                                   (int)rotl32(q[j][3], 6)};
 #pragma unroll
-                for (int l = 0; l < kLimbs; ++l)
-                    acc[j][l] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bm[l], acc[j][l], 0, 0, 0);
+                for (int g = 0; g < NCG; ++g)
+                    acc[j][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bm[g], acc[j][g], 0, 0, 0);
             }
         }
     }
 }
 
-template <int NS, bool PER_REQ>
-__device__ __forceinline__ void mwave(const MItem& a, int B, int NH, int b, int chunk, int h, int L, int m_lane,
-                                      uint32_t dmask) {
-    constexpr int H = MRing<NS>::H;
-    constexpr int PF = MRing<NS>::PF;
-    const int t0 = chunk * a.tpc;
-    const int nt = min(a.tpc, a.n_tiles - t0);
+// The product over this wave's tiles of the chunk: tiles ks, ks + KS, ...
+template <int NS, int NCG, bool PER_REQ>
+__device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, int chunk, int h, int ks, int L,
+                                         const int (&mcol)[NCG], uint32_t dmask, v4i (&acc)[4][NCG]) {
+    constexpr int H = MRing<NS, NCG>::H;
+    constexpr int PF = MRing<NS, NCG>::PF;
+    const int t0 = chunk * a.tpc + ks;
+    const int nt_all = min(a.tpc, a.n_tiles - chunk * a.tpc);
+    const int nt = nt_all > ks ? (nt_all - ks + KS - 1) / KS : 0;
+    if (nt == 0) return;
     const int last = nt - 1;
     const uint8_t* wbase = a.planes + (int64_t)b * 16 * a.K + (int64_t)t0 * kTileBytes + L * 16;
-    const int64_t xstride = (int64_t)NH * kLimbs * 64;   // v4i units per tile
-    const v4i* xbase = a.limbs + (int64_t)t0 * xstride + (int64_t)h * kLimbs * 64 + L;
+    const int64_t wstride = (int64_t)KS * kTileBytes;
+    const int64_t xunit = (int64_t)NH * NCG * 64;        // v4i units per tile
+    const v4i* xbase = a.limbs + (int64_t)t0 * xunit + (int64_t)h * NCG * 64 + L;
+    const int64_t xstride = xunit * KS;
     const int64_t pb = a.plane_bytes;
-
-    v4i acc[4][kLimbs];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int l = 0; l < kLimbs; ++l) acc[j][l] = v4i{0, 0, 0, 0};
 
     __builtin_amdgcn_s_waitcnt(0);
     u32x4 wa[H][NS], wb[H][NS];
-    v4i xa[H][kLimbs], xb[H][kLimbs];
-    mload<NS, H>(wa, xa, wbase, pb, xbase, xstride, 0, last);
+    v4i xa[H][NCG], xb[H][NCG];
+    mload<NS, NCG, H>(wa, xa, wbase, pb, wstride, xbase, xstride, 0, last);
     __builtin_amdgcn_sched_barrier(0);
-    mload<NS, H>(wb, xb, wbase, pb, xbase, xstride, H, last);
+    mload<NS, NCG, H>(wb, xb, wbase, pb, wstride, xbase, xstride, H, last);
     __builtin_amdgcn_sched_barrier(0);
     int t = 0;
     for (; t + PF < nt; t += PF) {
 #pragma unroll
-        for (int u = 0; u < H; ++u) mtile<NS, PER_REQ>(wa[u], xa[u], m_lane, dmask, acc);
+        for (int u = 0; u < H; ++u) mtile<NS, NCG, PER_REQ>(wa[u], xa[u], mcol, dmask, acc);
         __builtin_amdgcn_sched_barrier(0);
-        mload<NS, H>(wa, xa, wbase, pb, xbase, xstride, t + PF, last);
+        mload<NS, NCG, H>(wa, xa, wbase, pb, wstride, xbase, xstride, t + PF, last);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < H; ++u) mtile<NS, PER_REQ>(wb[u], xb[u], m_lane, dmask, acc);
+        for (int u = 0; u < H; ++u) mtile<NS, NCG, PER_REQ>(wb[u], xb[u], mcol, dmask, acc);
         __builtin_amdgcn_sched_barrier(0);
-        mload<NS, H>(wb, xb, wbase, pb, xbase, xstride, t + PF + H, last);
+        mload<NS, NCG, H>(wb, xb, wbase, pb, wstride, xbase, xstride, t + PF + H, last);
         __builtin_amdgcn_sched_barrier(0);
     }
+    // Drain: the last ring, whose tail may run past the wave's tiles.  Tiles
+    // past them were loaded (clamped to the last one) but are multiplied by
+    // zero limbs, so the accumulators see the same straight-line code as in
+    // the loop.
 #pragma unroll
-    for (int u = 0; u < H; ++u)
-        if (t + u < nt) mtile<NS, PER_REQ>(wa[u], xa[u], m_lane, dmask, acc);
+    for (int u = 0; u < H; ++u) {
+        const bool in = t + u < nt;
+        v4i z[NCG];
 #pragma unroll
-    for (int u = 0; u < H; ++u)
-        if (t + H + u < nt) mtile<NS, PER_REQ>(wb[u], xb[u], m_lane, dmask, acc);
-
-    // exact row sums for this lane's request: rows 16j + 4(L>>4) + i
-    const int slots = 16 * NH;
-    const int r = 16 * h + (L & 15);
-    const int e = a.exps[chunk * slots + r];
-    double v[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const double d = (double)acc[j][2][i] * 65536.0 + (double)acc[j][1][i] * 256.0 + (double)acc[j][0][i];
-            v[j][i] = m_lane == 0 ? 0.0 : (e == kBadExp ? __builtin_nan("") : ldexp(d, e - kFrac));
-        }
-    const int row0 = b * kRows + 4 * (L >> 4);
-    const bool live = r < B;
-    // the 16 scales first, all in flight together (y may alias nothing, but
-    // the compiler cannot know that, so loads interleaved with the y stores
-    // would each wait for the one before)
-    float sc[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[j][i] = a.scales[row0 + 16 * j + i];
-    if (a.n_chunks == 1) {
-        if (live)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a.y[(int64_t)r * a.N + row0 + 16 * j + i] = (float)((double)sc[j][i] * v[j][i]);
-        return;
+        for (int g = 0; g < NCG; ++g) z[g] = in ? xa[u][g] : v4i{0, 0, 0, 0};
+        mtile<NS, NCG, PER_REQ>(wa[u], z, mcol, dmask, acc);
     }
-    // split K: the protocol of the batch-1 kernel, one counter per (block, wave)
-    if (live)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+    for (int u = 0; u < H; ++u) {
+        const bool in = t + H + u < nt;
+        v4i z[NCG];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __hip_atomic_store(&a.partials[((int64_t)chunk * B + r) * a.N + row0 + 16 * j + i], v[j][i],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
-    uint32_t prev = 0;
-    uint32_t* ctr = a.counters + (int64_t)b * NH + h;
-    if (L == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = __shfl(prev, 0);
-    if (prev != (uint32_t)(a.n_chunks - 1)) return;
-    if (live) {
-        double s[4][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s[j][i] = 0.0;
-        for (int cc = 0; cc < a.n_chunks; ++cc) {
-            const double* pp = a.partials + ((int64_t)cc * B + r) * a.N + row0;
-            double t[4][4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    t[j][i] = __hip_atomic_load(pp + 16 * j + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s[j][i] += t[j][i];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a.y[(int64_t)r * a.N + row0 + 16 * j + i] = (float)((double)sc[j][i] * s[j][i]);
+        for (int g = 0; g < NCG; ++g) z[g] = in ? xb[u][g] : v4i{0, 0, 0, 0};
+        mtile<NS, NCG, PER_REQ>(wb[u], z, mcol, dmask, acc);
     }
-    if (L == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Workgroup = NH wavefronts = one (block, column chunk); wave h serves
-// requests 16h .. 16h+15.
-template <bool PER_REQ, bool GROUPED>
-__global__ __launch_bounds__(128) void qmm_kernel(MItem single, MCommon c) {
+// One workgroup = KS x NH wavefronts = one (block, column chunk).
+template <int NCG, bool PER_REQ, bool GROUPED>
+__global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
+    extern __shared__ int tab[];   // [KS NH][64 rows][16 NCG + 1] integer sums, then one flag
+    constexpr int TW = 16 * NCG + 1;
     MItem a;
     int local;
     if constexpr (GROUPED) {
@@ -324,70 +281,160 @@ __global__ __launch_bounds__(128) void qmm_kernel(MItem single, MCommon c) {
         a = single;
         local = (int)blockIdx.x;
     }
-    const int B = c.B, NH = c.NH;
+    const int B = c.B, NH = c.NH, KS = c.KS;
     const int chunk = local % a.n_chunks;
     const int b = local / a.n_chunks;
-    const int h = (int)threadIdx.x >> 6;
+    const int wave = (int)threadIdx.x >> 6;
+    const int h = wave % NH;
+    const int ks = wave / NH;
     const int L = (int)threadIdx.x & 63;
-    const int r = 16 * h + (L & 15);
-    // depth (slices read) of this lane's request; padding requests read nothing
-    int m = 0;
-    if (r < B) {
-        const int lev = PER_REQ ? (int)a.level[(int64_t)r * a.level_stride + b] : level_of(a.level, b);
-        m = lev < 4 ? lev : 4;
+
+    // depth of request L (lanes < B), then of the set's requests and columns
+    const int m_all = L < B ? depth_of<PER_REQ>(a, L, b) : 0;
+    uint32_t dm_all = 1u << m_all;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) dm_all |= __shfl_xor(dm_all, o);
+    dm_all = __builtin_amdgcn_readfirstlane(dm_all);
+    if (dm_all == 1u) {   // no request reads any of the block: y = 0, written once, by the first chunk
+        if (chunk == 0)
+            for (int r = wave; r < B; r += NH * KS) a.y[(int64_t)r * a.N + (int64_t)b * kRows + L] = 0.0f;
+        return;
     }
-    // which depths the wave's requests read (bit d), and the deepest
-    uint32_t dm = 1u << m;
+    const int m_set = __shfl(m_all, (16 * h + (L & 15)) & 63);   // depth of request 16h + (L & 15)
+    uint32_t dm = (L < 16 && 16 * h + L < B) ? (1u << m_set) : 1u;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) dm |= __shfl_xor(dm, o);
     dm = __builtin_amdgcn_readfirstlane(dm);
     const int ns = 31 - __builtin_clz(dm);
-    switch (ns) {
-        case 0:   // every request of this wave reads nothing of the block: y = 0
-            if (chunk == 0 && r < B)
+    int mcol[NCG];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        a.y[(int64_t)r * a.N + b * kRows + 16 * j + 4 * (L >> 4) + i] = 0.0f;
-            return;
-        case 1: mwave<1, PER_REQ>(a, B, NH, b, chunk, h, L, m, dm); return;
-        case 2: mwave<2, PER_REQ>(a, B, NH, b, chunk, h, L, m, dm); return;
-        case 3: mwave<3, PER_REQ>(a, B, NH, b, chunk, h, L, m, dm); return;
-        default: mwave<4, PER_REQ>(a, B, NH, b, chunk, h, L, m, dm); return;
+    for (int g = 0; g < NCG; ++g) {
+        const int rr = (16 * g + (L & 15)) / 3;                 // request (within the set) owning this column
+        const int md = __shfl(m_set, rr & 15);                   // its depth (lane rr holds it)
+        mcol[g] = (rr < 16 && 16 * h + rr < B) ? md : 0;
     }
+    v4i acc[4][NCG];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < NCG; ++g) acc[j][g] = v4i{0, 0, 0, 0};
+    switch (ns) {
+        case 0: break;   // no request of this set reads the block
+        case 1: mproduct<1, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, dm, acc); break;
+        case 2: mproduct<2, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, dm, acc); break;
+        case 3: mproduct<3, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, dm, acc); break;
+        default: mproduct<4, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, dm, acc); break;
+    }
+    // the wave's 64 x 16 NCG integer sums into its table
+    int* mine = tab + (ks * NH + h) * 64 * TW;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < NCG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mine[(16 * j + 4 * (L >> 4) + i) * TW + 16 * g + (L & 15)] = acc[j][g][i];
+    __syncthreads();
+
+    // outputs: one row per lane, requests spread over the waves; the limbs of
+    // request r are columns 3 (r mod 16) + l of set r / 16, summed over the KS
+    // tables (exact integers), then scaled into fp64
+    const int row = L;
+    const double sc = (double)a.scales[b * kRows + row];
+    const int slots = 16 * NH;
+    const bool split = a.n_chunks > 1;
+    for (int r = wave; r < B; r += NH * KS) {
+        const int hs = r >> 4, c0 = 3 * (r & 15);
+        int64_t s0 = 0, s1 = 0, s2 = 0;
+        for (int k2 = 0; k2 < KS; ++k2) {
+            const int* t2 = tab + (k2 * NH + hs) * 64 * TW + row * TW + c0;
+            s0 += t2[0];
+            s1 += t2[1];
+            s2 += t2[2];
+        }
+        const double d = (double)s2 * 65536.0 + (double)s1 * 256.0 + (double)s0;
+        const int e = a.exps[chunk * slots + r];
+        const int mr = __shfl(m_all, r & 63);
+        const double v = mr == 0 ? 0.0 : (e == kBadExp ? __builtin_nan("") : ldexp(d, e - kFrac));
+        if (!split)
+            a.y[(int64_t)r * a.N + (int64_t)b * kRows + row] = (float)(sc * v);
+        else   // split K: publish the partial with a device-scope write-through store
+            __hip_atomic_store(&a.partials[((int64_t)chunk * B + r) * a.N + (int64_t)b * kRows + row], v,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!split) return;
+    // Once the whole workgroup's partial stores are complete, one thread
+    // counts the arrival; the last workgroup of the block sums the partials
+    // in chunk order.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int* flag = tab + KS * NH * 64 * TW;
+    if (threadIdx.x == 0)
+        *flag = (int)__hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*flag != a.n_chunks - 1) return;
+    for (int r = wave; r < B; r += NH * KS) {
+        double sum = 0.0;
+        for (int cc = 0; cc < a.n_chunks; ++cc)
+            sum += __hip_atomic_load(&a.partials[((int64_t)cc * B + r) * a.N + (int64_t)b * kRows + row],
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        a.y[(int64_t)r * a.N + (int64_t)b * kRows + row] = (float)(sc * sum);
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ host side
 
+template <int NCG, bool GROUPED>
+static void launch_product(const MItem& it, const MCommon& c, bool per_req, int64_t grid, hipStream_t s) {
+    const dim3 blk(64 * c.NH * c.KS);
+    const size_t lds = ((size_t)c.KS * c.NH * 64 * (16 * NCG + 1) + 4) * sizeof(int);
+    if (per_req)
+        hipLaunchKernelGGL((qmm_kernel<NCG, true, GROUPED>), dim3((unsigned)grid), blk, lds, s, it, c);
+    else
+        hipLaunchKernelGGL((qmm_kernel<NCG, false, GROUPED>), dim3((unsigned)grid), blk, lds, s, it, c);
+}
+
 template <bool GROUPED>
 static void launch_mfma(const MItem& it, const MCommon& c, bool xbf16, bool per_req, int64_t pre_grid, int64_t grid,
                         hipStream_t s) {
-    const dim3 blk(64 * c.NH);
     if (xbf16)
         hipLaunchKernelGGL((limbs_kernel<true, GROUPED>), dim3((unsigned)pre_grid), dim3(64), 0, s, it, c);
     else
         hipLaunchKernelGGL((limbs_kernel<false, GROUPED>), dim3((unsigned)pre_grid), dim3(64), 0, s, it, c);
-    if (per_req)
-        hipLaunchKernelGGL((qmm_kernel<true, GROUPED>), dim3((unsigned)grid), blk, 0, s, it, c);
-    else
-        hipLaunchKernelGGL((qmm_kernel<false, GROUPED>), dim3((unsigned)grid), blk, 0, s, it, c);
+    switch (c.NCG) {
+        case 1: launch_product<1, GROUPED>(it, c, per_req, grid, s); break;
+        case 2: launch_product<2, GROUPED>(it, c, per_req, grid, s); break;
+        default: launch_product<3, GROUPED>(it, c, per_req, grid, s); break;
+    }
 }
 
 struct MPlan {
-    int NH, tpc, n_chunks;
+    int NH, NCG, KS, tpc, n_chunks;
     size_t counters, partials, limbs, exps, total;
 };
 
 static int64_t g_mfma_target_waves = 256 * 32;
+// Shortest column chunk, in tiles per request of the batch: a split of K
+// writes B fp64 partials per row and chunk, which must stay small next to
+// the chunk's weight bytes (64 B per row per tile and 2 bits of depth).
+static int g_mfma_tiles_per_request = 2;
+// Waves per request group splitting each chunk's tiles inside a workgroup.
+static int g_mfma_ksplit = 2;
 
-static int mfma_waves_per_wg(int64_t B) { return B > 16 ? 2 : 1; }
+static int mfma_sets(int64_t B) { return B > 16 ? 2 : 1; }
+// 16-column groups per set of up to 16 requests (three limb columns each)
+static int mfma_ncg(int64_t B) { return (int)((3 * std::min<int64_t>(B, 16) + 15) / 16); }
+// waves per set splitting a chunk: at most four waves per workgroup
+static int mfma_ks(int64_t B) { return std::max(1, std::min(g_mfma_ksplit, 4 / mfma_sets(B))); }
 
 // Chunking of one matrix on the matrix-core route, for a chunk length goal.
 static MPlan mplan_goal(int64_t N, int64_t K, int64_t B, int goal) {
     MPlan p{};
-    p.NH = mfma_waves_per_wg(B);
+    p.NH = mfma_sets(B);
+    p.NCG = mfma_ncg(B);
+    p.KS = mfma_ks(B);
     const int n_tiles = (int)(K / kTileCols);
+    goal = std::max<int>(goal, (int)std::min<int64_t>(4096, (int64_t)g_mfma_tiles_per_request * B));
     const int want = (n_tiles + goal - 1) / goal;
     int tpc = (n_tiles + want - 1) / want;
     tpc = (tpc + 3) / 4 * 4;
@@ -397,14 +444,14 @@ static MPlan mplan_goal(int64_t N, int64_t K, int64_t B, int goal) {
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     p.counters = QAM_WS_COUNTER_BYTES;
     p.partials = p.n_chunks > 1 ? up((size_t)p.n_chunks * B * N * sizeof(double)) : 0;
-    p.limbs = up((size_t)n_tiles * p.NH * kLimbs * 64 * 16);
+    p.limbs = up((size_t)n_tiles * p.NH * p.NCG * 64 * 16);
     p.exps = up((size_t)p.n_chunks * 16 * p.NH * sizeof(int));
     p.total = p.counters + p.partials + p.limbs + p.exps;
     return p;
 }
 
 static MPlan mplan(int64_t N, int64_t K, int64_t B) {
-    const int64_t block_tiles = N / kRows * (K / kTileCols) * mfma_waves_per_wg(B);
+    const int64_t block_tiles = N / kRows * (K / kTileCols) * mfma_sets(B) * mfma_ks(B);
     return mplan_goal(N, K, B, chunk_goal(block_tiles, g_mfma_target_waves));
 }
 
@@ -430,7 +477,7 @@ static MItem make_mitem(const void* x, const qam_packed* w, const uint8_t* level
 // Workspace of the matrix-core route (0 for bad shapes).
 size_t qam_mfma_workspace_bytes(int64_t N, int64_t K, int64_t B) {
     if (N <= 0 || K <= 0 || N % kRows || K % kTileCols || K > QAM_MAX_K || B < 1 || B > QAM_MAX_BATCH_MFMA) return 0;
-    if (N / kRows * (B > 16 ? 2 : 1) > QAM_MAX_BLOCKS) return 0;
+    if (N / kRows > QAM_MAX_BLOCKS) return 0;
     return mplan(N, K, B).total;
 }
 
@@ -438,8 +485,6 @@ size_t qam_mfma_workspace_bytes(int64_t N, int64_t K, int64_t B) {
 int qmatvec_mfma(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
                  int per_request_maps, float* y, void* workspace, size_t workspace_bytes, hipStream_t s) {
     const MPlan p = mplan(packed->N, packed->K, B);
-    if ((packed->n_blocks * p.NH) > QAM_MAX_BLOCKS)
-        QAM_FAIL(QAM_ERR_SHAPE, "qmatvec: %lld blocks x %d waves exceed the counter region", (long long)packed->n_blocks, p.NH);
     if (!workspace) QAM_FAIL(QAM_ERR_WORKSPACE, "qmatvec: workspace of %zu bytes required", p.total);
     if (workspace_bytes < p.total) QAM_FAIL(QAM_ERR_WORKSPACE, "qmatvec: workspace %zu < %zu bytes", workspace_bytes, p.total);
     if (!aligned(workspace, 256)) QAM_FAIL(QAM_ERR_ALIGN, "qmatvec: workspace must be 256-byte aligned");
@@ -452,12 +497,14 @@ int qmatvec_mfma(const void* x, int x_dtype, int64_t B, const qam_packed* packed
     MCommon c{};
     c.B = (int)B;
     c.NH = p.NH;
+    c.KS = p.KS;
+    c.NCG = p.NCG;
     launch_mfma<false>(it, c, x_dtype == QAM_X_BF16, per_request_maps != 0, (int64_t)p.n_chunks * 16 * p.NH,
                        (int64_t)it.n_blocks * p.n_chunks, s);
     QAM_HIP_CHECK(hipGetLastError());
     char v[128];
-    snprintf(v, sizeof(v), "qmatvec_mfma B=%lld maps=%s tpc=%d chunks=%d waves/wg=%d", (long long)B,
-             per_request_maps ? "per-request" : "shared", p.tpc, p.n_chunks, p.NH);
+    snprintf(v, sizeof(v), "qmatvec_mfma B=%lld maps=%s tpc=%d chunks=%d sets=%d colgroups=%d ksplit=%d", (long long)B,
+             per_request_maps ? "per-request" : "shared", p.tpc, p.n_chunks, p.NH, p.NCG, p.KS);
     set_variant(v);
     return QAM_OK;
 }
@@ -468,23 +515,24 @@ struct MGroupLayout {
     std::vector<MPlan> plans;
     size_t partials = 0, limbs = 0, exps = 0, table = 0, wgmap = 0, premap = 0, total = 0;
     int64_t n_wg = 0, n_pre = 0, blocks = 0;
-    int NH = 1;
+    int NH = 1, NCG = 1, KS = 1;
 };
 
 static int mfma_layout(const qam_gemv_item* items, int n_items, int64_t B, MGroupLayout& g) {
     if (!items || n_items < 1) QAM_FAIL(QAM_ERR_ARG, "group: need at least one item");
     if (B < 2 || B > QAM_MAX_BATCH_MFMA) QAM_FAIL(QAM_ERR_ARG, "group: B=%lld outside [2, %d]", (long long)B, QAM_MAX_BATCH_MFMA);
-    g.NH = mfma_waves_per_wg(B);
+    g.NH = mfma_sets(B);
+    g.NCG = mfma_ncg(B);
+    g.KS = mfma_ks(B);
     int64_t block_tiles = 0;
     for (int i = 0; i < n_items; ++i) {
         const qam_packed& w = items[i].w;
         if (w.N <= 0 || w.N % kRows || w.K <= 0 || w.K % kTileCols || w.K > QAM_MAX_K)
             QAM_FAIL(QAM_ERR_SHAPE, "group: item %d has a bad shape", i);
         g.blocks += w.N / kRows;
-        block_tiles += w.N / kRows * (w.K / kTileCols) * g.NH;
+        block_tiles += w.N / kRows * (w.K / kTileCols) * g.NH * g.KS;
     }
-    if (g.blocks * g.NH > QAM_MAX_BLOCKS)
-        QAM_FAIL(QAM_ERR_SHAPE, "group: %lld blocks x %d waves exceed %d", (long long)g.blocks, g.NH, QAM_MAX_BLOCKS);
+    if (g.blocks > QAM_MAX_BLOCKS) QAM_FAIL(QAM_ERR_SHAPE, "group: %lld blocks > %d", (long long)g.blocks, QAM_MAX_BLOCKS);
     const int goal = chunk_goal(block_tiles, g_mfma_target_waves);
     for (int i = 0; i < n_items; ++i) {
         const MPlan p = mplan_goal(items[i].w.N, items[i].w.K, B, goal);
@@ -532,7 +580,7 @@ int mfma_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dt
         if (int rc = check_item(gi.x, x_dtype, B, &gi.w, gi.level_map, gi.y, "group_init", QAM_OUT_STORE)) return rc;
         const MPlan& p = g.plans[i];
         MItem it = make_mitem(gi.x, &gi.w, gi.level_map, gi.y, per_request_maps, p);
-        it.counters = reinterpret_cast<uint32_t*>(base) + blk * g.NH;
+        it.counters = reinterpret_cast<uint32_t*>(base) + blk;
         it.partials = p.partials ? reinterpret_cast<double*>(partials + po) : nullptr;
         it.limbs = reinterpret_cast<v4i*>(limbs + lo);
         it.exps = reinterpret_cast<int*>(exps + eo);
@@ -575,7 +623,9 @@ int mfma_group_run(const qam_group* g, hipStream_t s) {
     c.wg_item = static_cast<const int*>(g->wg_map);
     c.pre_item = static_cast<const int*>(g->pre_map);
     c.B = (int)g->B;
-    c.NH = mfma_waves_per_wg(g->B);
+    c.NH = mfma_sets(g->B);
+    c.KS = mfma_ks(g->B);
+    c.NCG = mfma_ncg(g->B);
     MItem dummy{};
     launch_mfma<true>(dummy, c, g->x_dtype == QAM_X_BF16, g->per_request_maps != 0, g->n_pre_workgroups,
                       g->n_workgroups, s);
@@ -588,6 +638,20 @@ int mfma_group_run(const qam_group* g, hipStream_t s) {
 }
 
 }  // namespace qam
+
+extern "C" int qam_set_mfma_ksplit(int ks) {
+    qam::clear_error();
+    if (ks != 1 && ks != 2 && ks != 4) QAM_FAIL(QAM_ERR_ARG, "set_mfma_ksplit: %d not 1, 2 or 4", ks);
+    qam::g_mfma_ksplit = ks;
+    return QAM_OK;
+}
+
+extern "C" int qam_set_mfma_tiles_per_request(int t) {
+    qam::clear_error();
+    if (t < 0 || t > 64) QAM_FAIL(QAM_ERR_ARG, "set_mfma_tiles_per_request: %d outside [0, 64]", t);
+    qam::g_mfma_tiles_per_request = t;
+    return QAM_OK;
+}
 
 extern "C" int qam_set_mfma_target_waves(int waves) {
     qam::clear_error();
