@@ -200,7 +200,7 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   the pass; [PoD]: cost counted in weight bytes read).  A ZERO block loads
  *   nothing and writes y = 0.
  *
- *   Arithmetic: x is walked in sub-chunks of columns (at most 1536 for
+ *   Arithmetic: x is walked in sub-chunks of columns (at most 1024 for
  *   B = 1, 768 for B = 2, 512 for B <= 4, 256 for B <= 8); each is put on
  *   a fixed-point grid, x~ = round(x * 2^(22-e)) * 2^(e-22) with
  *   2^(e-1) <= max|x| < 2^e over the sub-chunk, held as three signed int8

@@ -41,25 +41,24 @@ __device__ __forceinline__ int limb_slot(int g) { return (g & ~15) | ((g & 3) <<
 
 // ------------------------------------------------------------------ per-wave body
 
-// Prefetch ring: two halves of H tiles each, about eight 16-byte loads in
-// flight per lane for one request (fewer when several requests' accumulators
-// take the registers).  The wait before one half is computed always follows
+// Prefetch ring: two halves of H tiles each, up to sixteen 16-byte loads in
+// flight per lane for one request (eight or fewer when several requests'
+// accumulators take the registers).  The wait before one half is computed always follows
 // the reload of the other half, so it drains exactly the older half.
 template <int NS, int NB>
 struct Ring {
-    static constexpr int raw = 4 / (NS * NB);
+    static constexpr int raw = (NB == 1 ? 8 : 4) / (NS * NB);
     static constexpr int H = raw >= 4 ? 4 : (raw >= 2 ? 2 : 1);   // tiles per half
     static constexpr int PF = 2 * H;                                // tiles per ring
 };
 
 // x is staged in sub-chunks of S tiles: each lane loads G = S / 4 groups of
-// four values per request, which with the first half ring keeps at most about
-// eleven loads in flight before x is used (within what the compiler's wait
-// counting tracks exactly), and the limbs of a sub-chunk take NB * S * 256
-// bytes of LDS.  S is a multiple of every ring length used with NB.
+// four values per request, issued before the first half ring so that waiting
+// for x never drains weight loads, and the limbs of a sub-chunk take
+// NB * S * 256 bytes of LDS.  S is a multiple of every ring length used with NB.
 template <int NB>
 struct Stage {
-    static constexpr int S = NB == 1 ? 24 : (NB == 2 ? 12 : (NB <= 4 ? 8 : 4));
+    static constexpr int S = NB == 1 ? 16 : (NB == 2 ? 12 : (NB <= 4 ? 8 : 4));
     static constexpr int G = S / 4;
 };
 
@@ -420,7 +419,7 @@ static int64_t g_target_waves = 256 * 32;   // wavefronts aimed for per launch
 
 // every chunk holds a whole number of prefetch rings (Ring<NS, B>::PF for every NS)
 int tpc_align_for(int64_t B) { return B == 1 ? 8 : (B == 2 ? 4 : 2); }
-int stage_tiles_for(int64_t B) { return B == 1 ? 24 : (B == 2 ? 12 : (B <= 4 ? 8 : 4)); }
+int stage_tiles_for(int64_t B) { return B == 1 ? 16 : (B == 2 ? 12 : (B <= 4 ? 8 : 4)); }
 size_t lds_bytes_for(int64_t B) { return (size_t)B * stage_tiles_for(B) * 16 * sizeof(int4); }
 
 // Column chunk length (in tiles) for a launch covering `block_tiles` block x
