@@ -100,6 +100,7 @@ SIGNATURES = [
 # tuning hooks that are not part of the product ABI contract
 EXTRA_SIGNATURES = [
     ("qam_set_target_waves", _I, [_I]),
+    ("qam_set_max_chunk_tiles", _I, [_I]),
     ("qam_set_mfma_target_waves", _I, [_I]),
     ("qam_set_mfma_min_batch", _I, [_I]),
     ("qam_set_mfma_tiles_per_request", _I, [_I]),

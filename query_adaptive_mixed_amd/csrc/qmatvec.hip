@@ -120,24 +120,27 @@ __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngro
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
         float m = 0.0f;
-        int nonfinite = 0;
+        float poison = 0.0f;   // 0 * x summed: NaN exactly when some x is not finite
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             const float4 v = xv[r][i];
             m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-            nonfinite |= !(fabsf(v.x) <= 3.402823466e38f) | !(fabsf(v.y) <= 3.402823466e38f) |
-                         !(fabsf(v.z) <= 3.402823466e38f) | !(fabsf(v.w) <= 3.402823466e38f);
+            poison = __builtin_fmaf(v.x, 0.0f, poison);
+            poison = __builtin_fmaf(v.y, 0.0f, poison);
+            poison = __builtin_fmaf(v.z, 0.0f, poison);
+            poison = __builtin_fmaf(v.w, 0.0f, poison);
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
             m = fmaxf(m, __shfl_xor(m, o));
-            nonfinite |= __shfl_xor(nonfinite, o);
+            poison += __shfl_xor(poison, o);
         }
         int e = 0;
         if (m > 0.0f) frexpf(m, &e);
         exps[r] = __builtin_amdgcn_readfirstlane(e);
-        bad[r] = __builtin_amdgcn_readfirstlane(nonfinite) != 0;
+        bad[r] = __builtin_amdgcn_readfirstlane((int)(poison != 0.0f)) != 0;   // NaN != 0
         const int sh = kFrac - exps[r];
+        const float scale = __uint_as_float((uint32_t)(sh + 127) << 23);     // 2^sh when sh <= 126
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             const int g = L + 64 * i;
@@ -149,14 +152,14 @@ __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngro
                 ssq[r] += (double)v.z * (double)v.z;
                 ssq[r] += (double)v.w * (double)v.w;
             }
-            const uint32_t w0 = limbs_of(v.x, sh), w1 = limbs_of(v.y, sh);
-            const uint32_t w2 = limbs_of(v.z, sh), w3 = limbs_of(v.w, sh);
-            int4 out;
-            out.x = (int)((w0 & 0xFFu) | ((w1 & 0xFFu) << 8) | ((w2 & 0xFFu) << 16) | (w3 << 24));
-            out.y = (int)(((w0 >> 8) & 0xFFu) | (w1 & 0xFF00u) | ((w2 & 0xFF00u) << 8) | ((w3 & 0xFF00u) << 16));
-            out.z = (int)(((w0 >> 16) & 0xFFu) | ((w1 >> 8) & 0xFF00u) | (w2 & 0xFF0000u) | ((w3 & 0xFF0000u) << 8));
-            out.w = 0;
-            lds[r * slots + limb_slot(g)] = out;
+            uint32_t w0, w1, w2, w3;
+            if (sh <= 126) {
+                w0 = limbs_fast(v.x, scale), w1 = limbs_fast(v.y, scale);
+                w2 = limbs_fast(v.z, scale), w3 = limbs_fast(v.w, scale);
+            } else {   // every |x| of the sub-chunk below 2^-104
+                w0 = limbs_of(v.x, sh), w1 = limbs_of(v.y, sh), w2 = limbs_of(v.z, sh), w3 = limbs_of(v.w, sh);
+            }
+            lds[r * slots + limb_slot(g)] = limb_words(w0, w1, w2, w3);
         }
     }
     __syncthreads();   // orders the LDS writes before the reads
@@ -416,6 +419,7 @@ __global__ __launch_bounds__(64) void qmatvec_kernel(Item single, Common c) {
 // ------------------------------------------------------------------ host side
 
 static int64_t g_target_waves = 256 * 32;   // wavefronts aimed for per launch
+static int64_t g_max_chunk_tiles = 64;       // longest column chunk of the batch-1 launches
 
 // every chunk holds a whole number of prefetch rings (Ring<NS, B>::PF for every NS)
 int tpc_align_for(int64_t B) { return B == 1 ? 8 : (B == 2 ? 4 : 2); }
@@ -425,8 +429,10 @@ size_t lds_bytes_for(int64_t B) { return (size_t)B * stage_tiles_for(B) * 16 * s
 // Column chunk length (in tiles) for a launch covering `block_tiles` block x
 // tile pairs: enough chunks for about g_target_waves wavefronts of equal work.
 int chunk_goal(int64_t block_tiles, int64_t target_waves) {
-    if (target_waves <= 0) target_waves = g_target_waves;
-    const int64_t g = (block_tiles + target_waves - 1) / target_waves;
+    const bool dflt = target_waves <= 0;
+    if (dflt) target_waves = g_target_waves;
+    int64_t g = (block_tiles + target_waves - 1) / target_waves;
+    if (dflt) g = std::min<int64_t>(g, g_max_chunk_tiles);   // long waves leave a long tail
     return (int)std::max<int64_t>(1, std::min<int64_t>(g, QAM_MAX_K / kTileCols));
 }
 
@@ -530,6 +536,13 @@ extern "C" size_t qam_qmatvec_workspace_bytes(int64_t N, int64_t K, int64_t B) {
     }
     if (B > 1) need = std::max(need, qam_mfma_workspace_bytes(N, K, B));   // the matrix-core route
     return need;
+}
+
+extern "C" int qam_set_max_chunk_tiles(int t) {
+    clear_error();
+    if (t < 1 || t > QAM_MAX_K / kTileCols) QAM_FAIL(QAM_ERR_ARG, "set_max_chunk_tiles: %d outside [1, %d]", t, QAM_MAX_K / kTileCols);
+    g_max_chunk_tiles = t;
+    return QAM_OK;
 }
 
 extern "C" int qam_set_target_waves(int waves) {

@@ -63,6 +63,31 @@ __device__ __forceinline__ uint32_t limbs_of(float v, int sh) {
     return ((uint32_t)q + 0x808080u) ^ 0x808080u;
 }
 
+// The same digits when 2^sh is a normal float (sh <= 126, the usual case):
+// fma(v, 2^sh, 1.5 * 2^23) rounds v * 2^sh to the nearest integer q (ties to
+// even, as rintf) because the sum's ulp is 1 for |q| <= 2^22, and the float's
+// bits are 0x4B400000 + q.
+__device__ __forceinline__ uint32_t limbs_fast(float v, float scale) {
+    const uint32_t bits = __float_as_uint(__builtin_fmaf(v, scale, 12582912.0f));
+    return (bits + (0x808080u - 0x4B400000u)) ^ 0x808080u;
+}
+
+// Limb words of four consecutive elements (digit words w0..w3): word l holds
+// digit l of the four elements, element i in byte i.
+__device__ __forceinline__ int4 limb_words(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+    // byte selectors of v_perm_b32: 0-3 pick the second operand's bytes, 4-7 the first's
+    const uint32_t lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);   // w0.0 w1.0 w0.1 w1.1
+    const uint32_t hi = __builtin_amdgcn_perm(w3, w2, 0x05010400u);   // w2.0 w3.0 w2.1 w3.1
+    const uint32_t lo2 = __builtin_amdgcn_perm(w1, w0, 0x00000602u);  // w0.2 w1.2
+    const uint32_t hi2 = __builtin_amdgcn_perm(w3, w2, 0x00000602u);  // w2.2 w3.2
+    int4 out;
+    out.x = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    out.y = (int)__builtin_amdgcn_perm(hi, lo, 0x07060302u);
+    out.z = (int)__builtin_amdgcn_perm(hi2, lo2, 0x05040100u);
+    out.w = 0;
+    return out;
+}
+
 // ---------------------------------------------------------------- launch descriptors
 
 // One matrix of a launch.

@@ -95,30 +95,39 @@ __global__ __launch_bounds__(64) void limbs_kernel(MItem single, MCommon c) {
     const int64_t col0 = (int64_t)t0 * 64;
     const bool live = r < B;
     float m = 0.0f;
-    int nonfinite = 0;
+    float poison = 0.0f;   // 0 * x summed: NaN exactly when some x is not finite
     if (live)
         for (int k = 4 * L; k < ncol; k += 256) {
             const float4 v = x4_value<XBF16>(load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + k));
             m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-            nonfinite |= !(fabsf(v.x) <= 3.402823466e38f) | !(fabsf(v.y) <= 3.402823466e38f) |
-                         !(fabsf(v.z) <= 3.402823466e38f) | !(fabsf(v.w) <= 3.402823466e38f);
+            poison = __builtin_fmaf(v.x, 0.0f, poison);
+            poison = __builtin_fmaf(v.y, 0.0f, poison);
+            poison = __builtin_fmaf(v.z, 0.0f, poison);
+            poison = __builtin_fmaf(v.w, 0.0f, poison);
         }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         m = fmaxf(m, __shfl_xor(m, o));
-        nonfinite |= __shfl_xor(nonfinite, o);
+        poison += __shfl_xor(poison, o);
     }
+    const bool nonfinite = poison != 0.0f;   // NaN compares unequal
     int e = 0;
     if (m > 0.0f) frexpf(m, &e);
     if (L == 0) a.exps[chunk * slots + r] = nonfinite ? kBadExp : e;
     const int sh = kFrac - e;
+    const float scale = __uint_as_float((uint32_t)(sh + 127) << 23);   // 2^sh when sh <= 126
     const int h = r >> 4, rr = r & 15;
     uint8_t* lb = reinterpret_cast<uint8_t*>(a.limbs);
     for (int k = 4 * L; k < ncol; k += 256) {
         uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
         if (live && !nonfinite) {
             const float4 v = x4_value<XBF16>(load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + k));
-            w0 = limbs_of(v.x, sh), w1 = limbs_of(v.y, sh), w2 = limbs_of(v.z, sh), w3 = limbs_of(v.w, sh);
+            if (sh <= 126) {
+                w0 = limbs_fast(v.x, scale), w1 = limbs_fast(v.y, scale);
+                w2 = limbs_fast(v.z, scale), w3 = limbs_fast(v.w, scale);
+            } else {   // every |x| of the chunk below 2^-104
+                w0 = limbs_of(v.x, sh), w1 = limbs_of(v.y, sh), w2 = limbs_of(v.z, sh), w3 = limbs_of(v.w, sh);
+            }
         }
         const int64_t kk = col0 + k;   // columns kk .. kk+3: one tile, one 16-column slice
         const int64_t t = kk >> 6;

@@ -438,3 +438,19 @@ def test_graph_replays_match_eager(qam):
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), rep
         step()                                 # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("scale", [1e-30, 1e-36, 1e-40, 1e30])
+@pytest.mark.parametrize("B", [1, 4])
+def test_qmatvec_extreme_magnitudes(qam, scale, B):
+    """x far from 1 (down to the subnormal range, where 2^sh no longer fits a
+    normal float, and near the top of the range) on both routes."""
+    rng = np.random.default_rng(int(-np.log10(scale) * 10) + B if scale < 1 else B)
+    N, K = 256, 2048
+    W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+    x = (rng.standard_normal((B, K)) * scale).astype(np.float32)
+    lv = np.array([1, 2, 3, 4], np.uint8)
+    pm = pack(qam, W, sc)
+    y = host(qam.qmatvec(dev(x), pm, dev(lv)))
+    check_y(y, W, sc, x, lv, (scale, B))
