@@ -185,20 +185,21 @@ __device__ double sum_squares(const void* x, int64_t K, int r, int L) {
 }
 
 // Writes the block's outputs from the exact row sums sum[r] = c_n . x_r
-// (ssq: sum_k x_r[k]^2 when the caller already has it, else NULL):
+// (ssq: sum_k x_r[k]^2 when have_ssq, else taken here):
 // v = scale * sum (divided by the RMS of x_r when the item asks for an
 // RMS-normalised input), then y = fl32(v) (store), y = fl32(y + v) (residual
 // add) or, for rows interleaved 32 gate / 32 up per block, one output per
 // pair: fl32(silu(gate) * up) with silu(t) = t / (1 + e^-t), all in fp64.
 template <int NB, bool XBF16>
-__device__ __forceinline__ void finish(const Item& a, int b, int L, const double (&sum)[NB], const double* ssq) {
+__device__ __forceinline__ void finish(const Item& a, int b, int L, const double (&sum)[NB], bool have_ssq,
+                                       const double (&ssq)[NB]) {
     const int row = b * kRows + L;
     const double sc = (double)a.scales[row];
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
         double v = sc * sum[r];
         if (a.rms) {
-            const double ss = ssq ? ssq[r] : sum_squares<XBF16>(a.x, a.K, r, L);
+            const double ss = have_ssq ? ssq[r] : sum_squares<XBF16>(a.x, a.K, r, L);
             v = v / sqrt(ss / (double)a.K + a.eps);
         }
         if (a.out_mode == QAM_OUT_GLU) {
@@ -355,7 +356,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
 #pragma unroll
                 for (int o = 1; o < 64; o <<= 1) ssq[r] += __shfl_xor(ssq[r], o);
         }
-        finish<NB, XBF16>(a, b, L, part, want_ssq ? ssq : nullptr);
+        finish<NB, XBF16>(a, b, L, part, want_ssq, ssq);
         return;
     }
     // Split K: publish this chunk's partials, then count the arrival; the last
@@ -383,7 +384,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
                                         __HIP_MEMORY_SCOPE_AGENT);
     }
     if (L == 0) __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    finish<NB, XBF16>(a, b, L, sum, nullptr);
+    finish<NB, XBF16>(a, b, L, sum, false, ssq);
 }
 
 // One workgroup = one wavefront = one (block, column chunk) of one matrix.
