@@ -384,7 +384,9 @@ typedef struct qam_decoder_desc {
     const qam_decoder_layer* layers;        /* (host) [n_layers]; descriptors are copied */
     qam_packed               lm_head;       /* [vocab][hidden] */
     double                   eps;           /* RMS epsilon, >= 0 */
-    int                      target_waves;  /* launch width goal per matrix; 0 = 96 */
+    int                      target_waves;  /* launch width goal per matrix (workgroups); 0 = 16 */
+    int                      waves_per_block; /* 1, 2, 4 or 8 wavefronts split each block's chunk
+                                               of columns inside a workgroup; 0 = 4 */
 } qam_decoder_desc;
 
 typedef struct qam_decoder qam_decoder;     /* opaque host object */

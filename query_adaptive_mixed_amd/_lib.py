@@ -60,7 +60,8 @@ class QamDecoderLayer(C.Structure):
 class QamDecoderDesc(C.Structure):
     _fields_ = [("n_layers", C.c_int), ("hidden", C.c_int64), ("q_dim", C.c_int64), ("kv_dim", C.c_int64),
                 ("ffn", C.c_int64), ("vocab", C.c_int64), ("layers", C.POINTER(QamDecoderLayer)),
-                ("lm_head", QamPacked), ("eps", C.c_double), ("target_waves", C.c_int)]
+                ("lm_head", QamPacked), ("eps", C.c_double), ("target_waves", C.c_int),
+                ("waves_per_block", C.c_int)]
 
 
 class QamError(RuntimeError):

@@ -278,7 +278,7 @@ class Decoder:
     ``step(rung)`` (eager) or ``capture(rung)`` once and ``replay(rung)``."""
 
     def __init__(self, layers, lm_head: PackedMatrix, hidden: int, q_dim: int, kv_dim: int, ffn: int,
-                 eps: float = 1e-6, target_waves: int = 0, device="cuda"):
+                 eps: float = 1e-6, target_waves: int = 0, waves_per_block: int = 0, device="cuda"):
         n = len(layers)
         self._layers = (L.QamDecoderLayer * n)()
         self._keep = [lm_head]
@@ -292,6 +292,7 @@ class Decoder:
         d.lm_head = lm_head.desc
         d.eps = float(eps)
         d.target_waves = int(target_waves)
+        d.waves_per_block = int(waves_per_block)
         self._desc = d
         nbytes = int(L.lib().qam_decoder_bytes(C.byref(d)))
         if nbytes == 0:

@@ -24,7 +24,8 @@ struct qam_decoder {
     float *h = nullptr, *qkv = nullptr, *m = nullptr, *logits = nullptr;
     uint8_t* maps[5] = {};
     char* ws = nullptr;            // counters, then fp64 partials
-    int64_t target_waves = 96;
+    int64_t target_waves = 16;
+    int ksplit = 4;
     hipGraph_t graph[5] = {};
     hipGraphExec_t exec[5] = {};
 };
@@ -80,7 +81,10 @@ int layout(const qam_decoder_desc* d, Layout& lo) {
         QAM_FAIL(QAM_ERR_SHAPE, "decoder: hidden, q_dim, kv_dim, vocab must be multiples of 64 and ffn of 32");
     if (!(d->eps >= 0.0) || d->eps > 1e300) QAM_FAIL(QAM_ERR_ARG, "decoder: eps must be finite and >= 0");
     if (d->target_waves < 0) QAM_FAIL(QAM_ERR_ARG, "decoder: target_waves < 0");
-    const int64_t tw = d->target_waves ? d->target_waves : 96;
+    if (d->waves_per_block != 0 && d->waves_per_block != 1 && d->waves_per_block != 2 && d->waves_per_block != 4 &&
+        d->waves_per_block != 8)
+        QAM_FAIL(QAM_ERR_ARG, "decoder: waves_per_block must be 0, 1, 2, 4 or 8");
+    const int64_t tw = d->target_waves ? d->target_waves : 16;
     size_t partial = 0;
     auto need = [&](const qam_packed& w) {
         lo.max_blocks = std::max<int64_t>(lo.max_blocks, w.n_blocks);
@@ -118,6 +122,7 @@ int enqueue(qam_decoder* dec, int rung, int first, int count, hipStream_t s) {
     for (int i = first; i < first + count; ++i) {
         const Op& op = ops[(size_t)i];
         const Plan p = plan_of(*op.w, dec->target_waves);
+        c.KS = dec->ksplit;   // waves per (block, chunk)
         Item it = make_item(op.x, op.w, dec->maps[rung], op.y, p);
         it.rms = op.rms;
         it.out_mode = op.out_mode;
@@ -154,7 +159,8 @@ extern "C" int qam_decoder_create(const qam_decoder_desc* d, void* dev_mem, size
     dec->d = *d;
     dec->layers.assign(d->layers, d->layers + d->n_layers);
     dec->d.layers = dec->layers.data();
-    dec->target_waves = d->target_waves ? d->target_waves : 96;
+    dec->target_waves = d->target_waves ? d->target_waves : 16;
+    dec->ksplit = d->waves_per_block ? d->waves_per_block : 4;
     char* base = static_cast<char*>(dev_mem);
     dec->ws = base + lo.ws;
     dec->h = reinterpret_cast<float*>(base + lo.h);

@@ -96,13 +96,23 @@ __device__ __forceinline__ void tile_dots(const u32x4* buf, const int4* __restri
 }
 
 template <int NS, int H>
-__device__ __forceinline__ void load_half(u32x4 (&h)[H][NS], const uint8_t* base, int64_t pb, int tile, int last) {
+__device__ __forceinline__ void load_half(u32x4 (&h)[H][NS], const uint8_t* base, int64_t pb, int64_t tstride,
+                                          int tile, int last) {
 #pragma unroll
     for (int u = 0; u < H; ++u) {
         const int t = min(tile + u, last);   // past the sub-chunk: reload its last tile (never computed)
 #pragma unroll
-        for (int p = 0; p < NS; ++p) h[u][p] = load_plane(base + p * pb + (int64_t)t * kTileBytes);
+        for (int p = 0; p < NS; ++p) h[u][p] = load_plane(base + p * pb + (int64_t)t * tstride);
     }
+}
+
+// Orders this wavefront's own LDS accesses: the limb area is private to the
+// wave and a wave's LDS instructions execute in issue order, so it is enough
+// to keep the compiler from moving accesses across this point (no workgroup
+// barrier: the waves of a workgroup run different numbers of sub-chunks).
+__device__ __forceinline__ void lds_order() {
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only: vector loads stay in flight
 }
 
 // Turn this wave's sub-chunk of x into limb words in LDS (see the file comment).
@@ -111,7 +121,7 @@ template <int NB, int G, bool XBF16>
 __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngroups, int slots, int L,
                                             int4* __restrict__ lds, int (&exps)[NB], bool (&bad)[NB],
                                             bool want_ssq, double (&ssq)[NB]) {
-    __syncthreads();   // the workgroup is this one wavefront: the last sub-chunk's LDS reads are done
+    lds_order();   // the last sub-chunk's limb reads come before these writes
     float4 xv[NB][G];
 #pragma unroll
     for (int r = 0; r < NB; ++r)
@@ -162,7 +172,7 @@ __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngro
             lds[r * slots + limb_slot(g)] = limb_words(w0, w1, w2, w3);
         }
     }
-    __syncthreads();   // orders the LDS writes before the reads
+    lds_order();   // the writes come before the tile loop's reads
 }
 
 // ------------------------------------------------------------------ epilogue
@@ -235,15 +245,18 @@ __device__ __forceinline__ void finish_zero(const Item& a, int b, int L) {
 // sub-chunks, in a fixed order).
 template <int NS, int NB, bool XBF16>
 __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* __restrict__ lds, int b, int chunk,
-                                          int L) {
+                                          int L, int ks, int KS, double* red) {
     constexpr int H = Ring<NS, NB>::H;
     constexpr int PF = Ring<NS, NB>::PF;
     constexpr int S = Stage<NB>::S;
     constexpr int G = Stage<NB>::G;
     const int B = c.B;
     const int tile0 = chunk * a.tpc;
-    const int ntile = min(a.tpc, a.n_tiles - tile0);
-    const uint8_t* base0 = a.planes + (int64_t)b * 16 * a.K + (int64_t)tile0 * kTileBytes + L * 16;
+    // the chunk's tiles ks, ks + KS, ... are this wave's (KS waves share a chunk)
+    const int ntile_all = min(a.tpc, a.n_tiles - tile0);
+    const int ntile = ntile_all > ks ? (ntile_all - ks + KS - 1) / KS : 0;
+    const int64_t tstride = (int64_t)KS * kTileBytes;
+    const uint8_t* base0 = a.planes + (int64_t)b * 16 * a.K + (int64_t)(tile0 + ks) * kTileBytes + L * 16;
     const int kg = L >> 4;
     const int slots = S * 16;
     const int64_t pb = a.plane_bytes;
@@ -263,8 +276,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     for (int t0 = 0; t0 < ntile; t0 += S) {
         const int nt = min(S, ntile - t0);
         const int ngroups = nt * 16;
-        const int64_t col0 = (int64_t)(tile0 + t0) * kTileCols;
-        const uint8_t* base = base0 + (int64_t)t0 * kTileBytes;
+        const uint8_t* base = base0 + (int64_t)t0 * tstride;
         const int last = nt - 1;
         // Nothing of this wave is in flight here, so this wait is free; it tells
         // the compiler's wait counting as much (it cannot see it through the
@@ -280,19 +292,20 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
 #pragma unroll
             for (int i = 0; i < G; ++i) {
                 const int g = min(L + 64 * i, ngroups - 1);
-                xraw[r][i] = load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + 4 * g);
+                const int64_t col = (int64_t)(tile0 + ks + KS * (t0 + (g >> 4))) * kTileCols + 4 * (g & 15);
+                xraw[r][i] = load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col);
             }
         // 2. the first half ring of weight loads, straight into the ring registers
         u32x4 A[H][NS], Bh[H][NS];
         __builtin_amdgcn_sched_barrier(0);   // x loads go out first ...
-        load_half<NS, H>(A, base, pb, 0, last);
+        load_half<NS, H>(A, base, pb, tstride, 0, last);
         __builtin_amdgcn_sched_barrier(0);   // ... then half a ring, and only then is x used
         // 3. the limbs of this sub-chunk of x while those loads are in flight,
         //    then the second half ring
         int exps[NB];
         bool bad[NB];
         stage_limbs<NB, G, XBF16>(xraw, ngroups, slots, L, lds, exps, bad, want_ssq, ssq);
-        load_half<NS, H>(Bh, base, pb, H, last);
+        load_half<NS, H>(Bh, base, pb, tstride, H, last);
         __builtin_amdgcn_sched_barrier(0);
 
         int acc[NB][4][kLimbs];
@@ -311,12 +324,12 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
 #pragma unroll
             for (int u = 0; u < H; ++u) tile_dots<NS, NB>(A[u], lds + (t + u) * 16 + kg, slots, acc);
             __builtin_amdgcn_sched_barrier(0);
-            load_half<NS, H>(A, base, pb, t + PF, last);
+            load_half<NS, H>(A, base, pb, tstride, t + PF, last);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < H; ++u) tile_dots<NS, NB>(Bh[u], lds + (t + H + u) * 16 + kg, slots, acc);
             __builtin_amdgcn_sched_barrier(0);
-            load_half<NS, H>(Bh, base, pb, t + PF + H, last);
+            load_half<NS, H>(Bh, base, pb, tstride, t + PF + H, last);
             __builtin_amdgcn_sched_barrier(0);
         }
         // Drain: the last ring, whose tail may run past a ragged sub-chunk.
@@ -348,6 +361,23 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     double part[NB];
 #pragma unroll
     for (int r = 0; r < NB; ++r) part[r] = any_bad[r] ? __builtin_nan("") : mine[r];   // non-finite x: NaN
+    if (KS > 1) {   // the chunk's other waves hand over their row sums; wave 0 adds them in order
+        if (ks > 0) {
+#pragma unroll
+            for (int r = 0; r < NB; ++r) {
+                red[((ks * NB + r) * 2 + 0) * 64 + L] = part[r];
+                red[((ks * NB + r) * 2 + 1) * 64 + L] = ssq[r];
+            }
+        }
+        __syncthreads();
+        if (ks > 0) return;
+        for (int k2 = 1; k2 < KS; ++k2)
+#pragma unroll
+            for (int r = 0; r < NB; ++r) {
+                part[r] += red[((k2 * NB + r) * 2 + 0) * 64 + L];
+                ssq[r] += red[((k2 * NB + r) * 2 + 1) * 64 + L];
+            }
+    }
 
     if (a.n_chunks == 1) {
         if (want_ssq) {
@@ -387,10 +417,13 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     finish<NB, XBF16>(a, b, L, sum, false, ssq);
 }
 
-// One workgroup = one wavefront = one (block, column chunk) of one matrix.
-template <int NB, bool GROUPED, bool XBF16>
-__global__ __launch_bounds__(64) void qmatvec_kernel(Item single, Common c) {
-    extern __shared__ int4 lds[];           // [NB][S * 16] limb words of this wave's sub-chunk
+// One workgroup = c.KS wavefronts (at most MAXW) = one (block, column chunk)
+// of one matrix; wave k takes the chunk's tiles k, k + KS, ...
+template <int NB, bool GROUPED, bool XBF16, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void qmatvec_kernel(Item single, Common c) {
+    // per wave: [NB][S * 16] limb words of its sub-chunk; then, with several
+    // waves, [KS][NB][2][64] fp64 row sums handed to wave 0
+    extern __shared__ int4 lds[];
     Item a;
     int local;
     if constexpr (GROUPED) {
@@ -401,19 +434,24 @@ __global__ __launch_bounds__(64) void qmatvec_kernel(Item single, Common c) {
         a = single;
         local = (int)blockIdx.x;
     }
+    const int KS = MAXW == 1 ? 1 : c.KS;
+    const int ks = MAXW == 1 ? 0 : (int)(threadIdx.x >> 6);
+    const int region = NB * Stage<NB>::S * 16;   // int4 per wave
+    int4* mylds = lds + ks * region;
+    double* red = reinterpret_cast<double*>(lds + KS * region);
     const int chunk = local % a.n_chunks;
     const int b = local / a.n_chunks;
-    const int L = threadIdx.x;
+    const int L = threadIdx.x & 63;
     const int lev = level_of(a.level, b);
     const int ns = __builtin_amdgcn_readfirstlane(lev < 4 ? lev : 4);
-    switch (ns) {
-        case 0:   // ZERO: nothing read, y = 0 (written once, by the first chunk)
-            if (chunk == 0) finish_zero<NB>(a, b, L);
+    switch (ns) {   // uniform over the workgroup: one block
+        case 0:   // ZERO: nothing read, y = 0 (written once, by the first chunk's first wave)
+            if (chunk == 0 && ks == 0) finish_zero<NB>(a, b, L);
             return;
-        case 1: wave_body<1, NB, XBF16>(a, c, lds, b, chunk, L); return;
-        case 2: wave_body<2, NB, XBF16>(a, c, lds, b, chunk, L); return;
-        case 3: wave_body<3, NB, XBF16>(a, c, lds, b, chunk, L); return;
-        default: wave_body<4, NB, XBF16>(a, c, lds, b, chunk, L); return;
+        case 1: wave_body<1, NB, XBF16>(a, c, mylds, b, chunk, L, ks, KS, red); return;
+        case 2: wave_body<2, NB, XBF16>(a, c, mylds, b, chunk, L, ks, KS, red); return;
+        case 3: wave_body<3, NB, XBF16>(a, c, mylds, b, chunk, L, ks, KS, red); return;
+        default: wave_body<4, NB, XBF16>(a, c, mylds, b, chunk, L, ks, KS, red); return;
     }
 }
 
@@ -458,9 +496,9 @@ Plan make_plan(int64_t N, int64_t K, int64_t B, int goal, int align) {
 template <int NB, bool GROUPED>
 static void launch_nb(const Item& it, const Common& c, int64_t grid, size_t lds, hipStream_t s) {
     if (c.x_bf16)
-        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, true>), dim3((unsigned)grid), dim3(64), lds, s, it, c);
+        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, true, 1>), dim3((unsigned)grid), dim3(64), lds, s, it, c);
     else
-        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, false>), dim3((unsigned)grid), dim3(64), lds, s, it, c);
+        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, false, 1>), dim3((unsigned)grid), dim3(64), lds, s, it, c);
 }
 
 template <bool GROUPED>
@@ -478,6 +516,15 @@ static void launch(int64_t B, const Item& it, const Common& c, int64_t grid, siz
 }
 
 void launch_single(int64_t B, const Item& it, const Common& c, int64_t grid, hipStream_t s) {
+    if (B == 1 && c.KS > 1) {   // several waves per (block, chunk): batch 1 only
+        const size_t lds = (size_t)c.KS * lds_bytes_for(1) + (size_t)c.KS * 2 * 64 * sizeof(double);
+        if (c.x_bf16)
+            hipLaunchKernelGGL((qmatvec_kernel<1, false, true, 8>), dim3((unsigned)grid), dim3(64 * c.KS), lds, s, it, c);
+        else
+            hipLaunchKernelGGL((qmatvec_kernel<1, false, false, 8>), dim3((unsigned)grid), dim3(64 * c.KS), lds, s, it,
+                               c);
+        return;
+    }
     launch<false>(B, it, c, grid, lds_bytes_for(B), s);
 }
 
@@ -589,6 +636,7 @@ extern "C" int qam_qmatvec_ep(const void* x, int x_dtype, int64_t B, const qam_p
     Common c{};
     c.B = (int)B;
     c.x_bf16 = x_dtype == QAM_X_BF16;
+    c.KS = 1;
     const int64_t grid = (int64_t)p.n_chunks * p.n_quads;
     launch_single(B, it, c, grid, s);
     QAM_HIP_CHECK(hipGetLastError());
@@ -735,6 +783,7 @@ extern "C" int qam_qmatvec_group(const qam_group* group, hipStream_t s) {
     c.wg_item = static_cast<const int*>(group->wg_map);
     c.B = (int)group->B;
     c.x_bf16 = group->x_dtype == QAM_X_BF16;
+    c.KS = 1;
     Item none{};
     launch<true>(group->B, none, c, group->n_workgroups, group->lds_bytes, s);
     QAM_HIP_CHECK(hipGetLastError());

@@ -117,6 +117,7 @@ struct Common {
     const int* wg_item;        // grouped launches: item index of every workgroup
     int B;
     int x_bf16;
+    int KS;                    // waves per (block, chunk), 1..8 (batch 1, single launches)
 };
 
 // Chunking of one matrix: tiles per chunk, chunks, workgroups per chunk and
@@ -147,7 +148,8 @@ int mfma_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dt
                     void* dev_mem, size_t dev_bytes, qam_group* out, hipStream_t s);
 int mfma_group_run(const qam_group* g, hipStream_t s);
 bool mfma_route(int64_t B, int per_request_maps);
-// Enqueues one single-matrix product launch (grid = n_chunks * n_quads).
+// Enqueues one single-matrix product launch (grid = n_chunks * n_quads
+// workgroups of c.KS wavefronts; c.KS > 1 only for B == 1).
 void launch_single(int64_t B, const Item& it, const Common& c, int64_t grid, hipStream_t s);
 
 }  // namespace qam
