@@ -72,10 +72,15 @@ __device__ __forceinline__ int depth_of(const MItem& a, int r, int b) {
 
 // ------------------------------------------------------------------ x -> limbs
 
-// One wavefront per (column chunk, request slot r < 16 NH): the chunk's
-// largest |x| sets the exponent; slots r >= B get zero limbs.
+// One workgroup of four wavefronts per (column chunk, request slot
+// r < 16 NH): the chunk's largest |x| sets the exponent; slots r >= B get zero
+// limbs.
+constexpr int kPreThreads = 256;
+
 template <bool XBF16, bool GROUPED>
-__global__ __launch_bounds__(64) void limbs_kernel(MItem single, MCommon c) {
+__global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommon c) {
+    __shared__ float red_m[kPreThreads / 64];
+    __shared__ float red_p[kPreThreads / 64];
     MItem a;
     int local;
     if constexpr (GROUPED) {
@@ -89,7 +94,7 @@ __global__ __launch_bounds__(64) void limbs_kernel(MItem single, MCommon c) {
     const int slots = 16 * NH;
     const int chunk = local / slots;
     const int r = local % slots;
-    const int L = threadIdx.x;
+    const int T = threadIdx.x;
     const int t0 = chunk * a.tpc;
     const int ncol = min(a.tpc, a.n_tiles - t0) * 64;
     const int64_t col0 = (int64_t)t0 * 64;
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(64) void limbs_kernel(MItem single, MCommon c) {
     float m = 0.0f;
     float poison = 0.0f;   // 0 * x summed: NaN exactly when some x is not finite
     if (live)
-        for (int k = 4 * L; k < ncol; k += 256) {
+        for (int k = 4 * T; k < ncol; k += 4 * kPreThreads) {
             const float4 v = x4_value<XBF16>(load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + k));
             m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
             poison = __builtin_fmaf(v.x, 0.0f, poison);
@@ -110,15 +115,27 @@ __global__ __launch_bounds__(64) void limbs_kernel(MItem single, MCommon c) {
         m = fmaxf(m, __shfl_xor(m, o));
         poison += __shfl_xor(poison, o);
     }
+    if ((T & 63) == 0) {
+        red_m[T >> 6] = m;
+        red_p[T >> 6] = poison;
+    }
+    __syncthreads();
+    m = red_m[0];
+    poison = red_p[0];
+#pragma unroll
+    for (int w = 1; w < kPreThreads / 64; ++w) {
+        m = fmaxf(m, red_m[w]);
+        poison += red_p[w];
+    }
     const bool nonfinite = poison != 0.0f;   // NaN compares unequal
     int e = 0;
     if (m > 0.0f) frexpf(m, &e);
-    if (L == 0) a.exps[chunk * slots + r] = nonfinite ? kBadExp : e;
+    if (T == 0) a.exps[chunk * slots + r] = nonfinite ? kBadExp : e;
     const int sh = kFrac - e;
     const float scale = __uint_as_float((uint32_t)(sh + 127) << 23);   // 2^sh when sh <= 126
     const int h = r >> 4, rr = r & 15;
     uint8_t* lb = reinterpret_cast<uint8_t*>(a.limbs);
-    for (int k = 4 * L; k < ncol; k += 256) {
+    for (int k = 4 * T; k < ncol; k += 4 * kPreThreads) {
         uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
         if (live && !nonfinite) {
             const float4 v = x4_value<XBF16>(load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + k));
@@ -220,6 +237,7 @@ __device__ __forceinline__ void mtile(const u32x4 (&w)[NS], const v4i (&xl)[NCG]
 template <int NS, int NCG, bool PER_REQ>
 __device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, int chunk, int h, int ks, int L,
                                          const int (&mcol)[NCG], uint32_t dmask, v4i (&acc)[4][NCG]) {
+
     constexpr int H = MRing<NS, NCG>::H;
     constexpr int PF = MRing<NS, NCG>::PF;
     const int t0 = chunk * a.tpc + ks;
@@ -407,9 +425,9 @@ template <bool GROUPED>
 static void launch_mfma(const MItem& it, const MCommon& c, bool xbf16, bool per_req, int64_t pre_grid, int64_t grid,
                         hipStream_t s) {
     if (xbf16)
-        hipLaunchKernelGGL((limbs_kernel<true, GROUPED>), dim3((unsigned)pre_grid), dim3(64), 0, s, it, c);
+        hipLaunchKernelGGL((limbs_kernel<true, GROUPED>), dim3((unsigned)pre_grid), dim3(kPreThreads), 0, s, it, c);
     else
-        hipLaunchKernelGGL((limbs_kernel<false, GROUPED>), dim3((unsigned)pre_grid), dim3(64), 0, s, it, c);
+        hipLaunchKernelGGL((limbs_kernel<false, GROUPED>), dim3((unsigned)pre_grid), dim3(kPreThreads), 0, s, it, c);
     switch (c.NCG) {
         case 1: launch_product<1, GROUPED>(it, c, per_req, grid, s); break;
         case 2: launch_product<2, GROUPED>(it, c, per_req, grid, s); break;
