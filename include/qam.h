@@ -182,6 +182,22 @@ int qam_build_level_map(const double* coords, int64_t n_blocks,
                         uint8_t* level_out, hipStream_t s);
 
 /*
+ * qam_build_level_maps -- one level map per request, n_maps of them, each by
+ *   the rules of qam_build_level_map with its own lenses and parameters (the
+ *   per-request maps of a batch).  Maps are computed in launches of up to 8
+ *   maps (fewer when the maps' lenses would exceed QAM_MAX_LENSES).
+ *   lenses     (host) [n_maps][n_lenses], map k's lenses at k * n_lenses.
+ *   params     (host) [n_maps].
+ *   n_maps     1 .. QAM_MAX_BATCH_MFMA.
+ *   level_out  (device) uint8 [n_maps][n_blocks].
+ *   Other arguments and the numerics as qam_build_level_map; each map is
+ *   bit-identical to a qam_build_level_map call with its lenses and params.
+ */
+int qam_build_level_maps(const double* coords, int64_t n_blocks, const qam_lens* lenses, int n_lenses,
+                         const qam_lens_params* params, const uint8_t* ladder_bits, int n_rungs,
+                         int glass, int n_maps, uint8_t* level_out, hipStream_t s);
+
+/*
  * qam_map_weight_bytes -- rule 7 and the bytes-read cost for a map (host).
  *   [Lens] rule 7: bits = sum_b w_b bits(b) / sum_b w_b; [PoD]: cost counted
  *   in weight bytes read.  w_b = 64 * K for every block of one matrix.
@@ -311,7 +327,10 @@ typedef struct qam_gemv_item {
     const void*    x;          /* (device) [B][w.K], fp32 or bf16, 16-byte aligned   */
     float*         y;          /* (device) [B][w.N]                                  */
     const uint8_t* level_map;  /* (device) rungs of {0,2,4,6,8}: [w.n_blocks] shared by
-                                  the B requests, or [B][w.n_blocks] per request       */
+                                  the B requests, or per request B rows of w.n_blocks */
+    int64_t        level_stride; /* per-request maps: bytes from one request's row to the
+                                  next (0: w.n_blocks), e.g. the block count of a whole
+                                  field whose maps are stored [B][field blocks]        */
 } qam_gemv_item;
 
 typedef struct qam_group {     /* filled by qam_group_init; treat as opaque          */

@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     PackedMatrix,
     Workspace,
     build_level_map,
+    build_level_maps,
     escalation_schedule,
     last_variant,
     map_weight_bytes,

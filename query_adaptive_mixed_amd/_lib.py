@@ -40,7 +40,8 @@ class QamLensParams(C.Structure):
 
 
 class QamGemvItem(C.Structure):
-    _fields_ = [("w", QamPacked), ("x", C.c_void_p), ("y", C.c_void_p), ("level_map", C.c_void_p)]
+    _fields_ = [("w", QamPacked), ("x", C.c_void_p), ("y", C.c_void_p), ("level_map", C.c_void_p),
+                ("level_stride", C.c_int64)]
 
 
 class QamGroup(C.Structure):
@@ -78,6 +79,8 @@ SIGNATURES = [
     ("qam_describe_packed", _I, [_P, _I64, _I64, C.POINTER(QamPacked)]),
     ("qam_unpack_codes", _I, [C.POINTER(QamPacked), _P, _P, _P]),
     ("qam_build_level_map", _I, [_P, _I64, C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I, _I, _P, _P]),
+    ("qam_build_level_maps", _I, [_P, _I64, C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I, _I, _I, _P,
+                                  _P]),
     ("qam_map_weight_bytes", _I, [_P, _I64, _I64, _P, _I, C.POINTER(_D), C.POINTER(_I64)]),
     ("qam_qmatvec_workspace_bytes", C.c_size_t, [_I64, _I64, _I64]),
     ("qam_qmatvec", _I, [_P, _I, _I64, C.POINTER(QamPacked), _P, _I, _P, _P, _SZ, _P]),

@@ -120,6 +120,44 @@ def build_level_map(coords: torch.Tensor, centres, radii, f: float, g: float, co
     return out
 
 
+def build_level_maps(coords: torch.Tensor, lens_sets, f, g: float = 1.0, combine: str = "sum", glass: int = 1,
+                     ladder_bits: Sequence[int] = LADDER_BITS, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One map per request (uint8 [n_maps, n_blocks]): ``lens_sets`` is a
+    sequence of (centres [n_lenses, 2], radii [n_lenses]) pairs, all with the
+    same lens count; ``f`` a scalar or one value per map."""
+    _require_cuda(coords, "coords", torch.float64)
+    n_blocks = coords.shape[0]
+    n_maps = len(lens_sets)
+    fs = np.broadcast_to(np.asarray(f, dtype=np.float64), (n_maps,))
+    n_lenses = None
+    lenses = None
+    params = (L.QamLensParams * n_maps)()
+    for k, (centres, radii) in enumerate(lens_sets):
+        centres = np.asarray(centres, dtype=np.float64).reshape(-1, 2)
+        radii = np.asarray(radii, dtype=np.float64).reshape(-1)
+        if centres.shape[0] != radii.shape[0]:
+            raise ValueError("centres and radii disagree on the lens count")
+        if n_lenses is None:
+            n_lenses = centres.shape[0]
+            lenses = (L.QamLens * max(1, n_maps * n_lenses))()
+        elif centres.shape[0] != n_lenses:
+            raise ValueError("every map needs the same lens count")
+        for i in range(n_lenses):
+            l = lenses[k * n_lenses + i]
+            l.cx, l.cy, l.r = float(centres[i, 0]), float(centres[i, 1]), float(radii[i])
+        params[k].f, params[k].g = float(fs[k]), float(g)
+        params[k].combine = {"sum": L.QAM_COMBINE_SUM, "max": L.QAM_COMBINE_MAX}[combine]
+        params[k].n_stops = 0
+    ladder = (C.c_uint8 * len(ladder_bits))(*ladder_bits)
+    if out is None:
+        out = torch.empty((n_maps, n_blocks), dtype=torch.uint8, device=coords.device)
+    else:
+        _require_cuda(out, "out", torch.uint8)
+    L.check(L.lib().qam_build_level_maps(_ptr(coords), n_blocks, lenses, n_lenses, params, C.cast(ladder, C.c_void_p),
+                                         len(ladder_bits), int(glass), n_maps, _ptr(out), _stream_handle()))
+    return out
+
+
 def map_weight_bytes(level_map, K: int, ladder_bits: Sequence[int] = LADDER_BITS):
     """(mean bits, weight bytes) of a map over one matrix with K columns (host)."""
     lv = np.ascontiguousarray(np.asarray(level_map.cpu() if isinstance(level_map, torch.Tensor) else level_map,
@@ -238,7 +276,8 @@ class GroupedQmatvec:
         for i, (pm, x, y, lv) in enumerate(items):
             _require_cuda(x, "x")
             _require_cuda(y, "y", torch.float32)
-            _require_cuda(lv, "level_map", torch.uint8)
+            if not isinstance(lv, torch.Tensor) or not lv.is_cuda or lv.dtype != torch.uint8:
+                raise TypeError("level_map must be a uint8 device tensor")
             b = x.shape[0] if x.dim() == 2 else 1
             d = L.QAM_X_F32 if x.dtype == torch.float32 else (L.QAM_X_BF16 if x.dtype == torch.bfloat16 else None)
             if d is None:
@@ -248,10 +287,17 @@ class GroupedQmatvec:
                 B, xdt, per_request = b, d, pr
             elif (b, d, pr) != (B, xdt, per_request):
                 raise ValueError("every item of a group needs the same batch, x dtype and map kind")
-            if pr and tuple(lv.shape) != (B, pm.n_blocks):
-                raise ValueError("a per-request level_map must be [B, n_blocks]")
+            stride = 0
+            if pr:
+                # [B, n_blocks], possibly a column slice of a [B, field blocks] array
+                if tuple(lv.shape) != (B, pm.n_blocks) or lv.stride(1) != 1:
+                    raise ValueError("a per-request level_map must be [B, n_blocks] with unit column stride")
+                stride = lv.stride(0)
+            else:
+                _require_cuda(lv, "level_map")
             arr[i].w = pm.desc
             arr[i].x, arr[i].y, arr[i].level_map = x.data_ptr(), y.data_ptr(), lv.data_ptr()
+            arr[i].level_stride = stride
             self._keep.append((pm, x, y, lv))
         nbytes = int(L.lib().qam_group_bytes(arr, n, B, int(per_request)))
         if nbytes == 0:

@@ -606,7 +606,10 @@ int mfma_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dt
         const qam_gemv_item& gi = items[i];
         if (int rc = check_item(gi.x, x_dtype, B, &gi.w, gi.level_map, gi.y, "group_init", QAM_OUT_STORE)) return rc;
         const MPlan& p = g.plans[i];
+        if (gi.level_stride < 0 || (gi.level_stride > 0 && gi.level_stride < gi.w.n_blocks))
+            QAM_FAIL(QAM_ERR_ARG, "group_init: item %d level_stride %lld < n_blocks", i, (long long)gi.level_stride);
         MItem it = make_mitem(gi.x, &gi.w, gi.level_map, gi.y, per_request_maps, p);
+        if (per_request_maps && gi.level_stride > 0) it.level_stride = gi.level_stride;
         it.counters = reinterpret_cast<uint32_t*>(base) + blk;
         it.partials = p.partials ? reinterpret_cast<double*>(partials + po) : nullptr;
         it.limbs = reinterpret_cast<v4i*>(limbs + lo);

@@ -266,3 +266,23 @@ def test_decoder_create_checks_memory_before_any_launch(lib):
     assert lib.qam_decoder_create(C.byref(d), None, nb, C.byref(h), None) == -1
     assert lib.qam_decoder_step(None, 2, None) == -1
     assert lib.qam_decoder_replay(None, 2, None) == -1
+
+
+def test_build_level_maps_rejects(lib):
+    lad, keep = _ladder()
+    n_maps, n_lenses = 3, 2
+    lenses = (L.QamLens * (n_maps * n_lenses))()
+    for i in range(n_maps * n_lenses):
+        lenses[i].cx, lenses[i].cy, lenses[i].r = 0.5, 0.5, 0.2
+    params = (L.QamLensParams * n_maps)()
+    for k in range(n_maps):
+        params[k].f, params[k].g = 0.5, 1.0
+    assert lib.qam_build_level_maps(FAKE, 8, lenses, n_lenses, params, lad, 5, 1, 0, FAKE, None) == -3
+    assert lib.qam_build_level_maps(FAKE, 8, lenses, n_lenses, params, lad, 5, 1, 33, FAKE, None) == -3
+    assert lib.qam_build_level_maps(FAKE, 8, lenses, n_lenses, params, lad, 5, 1, 3, None, None) == -1
+    params[2].f = 1.5
+    assert lib.qam_build_level_maps(FAKE, 8, lenses, n_lenses, params, lad, 5, 1, 3, FAKE, None) == -3
+    params[2].f = 0.5
+    lenses[5].r = -1.0
+    assert lib.qam_build_level_maps(FAKE, 8, lenses, n_lenses, params, lad, 5, 1, 3, FAKE, None) == -3
+    assert lib.qam_build_level_maps(FAKE, 8, lenses, 65, params, lad, 5, 1, 3, FAKE, None) == -3

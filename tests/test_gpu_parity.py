@@ -163,6 +163,25 @@ def test_level_map_workload_fields(qam):
             assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("n_lenses", [1, 3, 9, 21])
+def test_level_maps_batched_bit_exact(qam, n_lenses):
+    """One map per request in one call (launches of up to 8 maps, fewer when
+    their lenses fill the table), every map bit-identical to the oracle."""
+    rng = np.random.default_rng(70 + n_lenses)
+    n_blocks, n_maps = 700, 32
+    coords = rng.uniform(0, 1, size=(n_blocks, 2))
+    sets = []
+    for k in range(n_maps):
+        idx = rng.choice(n_blocks, n_lenses, replace=False)
+        sets.append((coords[idx], rng.uniform(0.05, 0.3, size=n_lenses)))
+    fs = rng.uniform(0.0, 0.95, size=n_maps)
+    for combine, glass, g in (("sum", 1, 1.0), ("max", 0, 0.75)):
+        got = host(qam.build_level_maps(dev(coords), sets, fs, g=g, combine=combine, glass=glass))
+        for k, (c, r) in enumerate(sets):
+            want = O.level_map(coords, c, r, fs[k], g, combine, 5, glass)
+            assert np.array_equal(got[k], want), (k, combine)
+
+
 # ------------------------------------------------------------------ qmatvec
 
 def test_qmatvec_single_layer_workload_all_maps_sampled(qam):

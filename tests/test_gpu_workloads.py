@@ -122,11 +122,11 @@ def test_batched_layer_grouped_launch(qam, B, xdt):
     cal = CAL["batched_layer"]
     fld = WL.batched_layer(0)
     reqs = WL.request_lenses(fld, B)
-    coords = dev(fld.coords)
-    maps = torch.empty((B, fld.n_blocks), dtype=torch.uint8, device="cuda")
-    for r, (cc, rr) in enumerate(reqs):
-        qam.build_level_map(coords, cc, rr, cal["requests"][r]["f"], 1.0, "sum", 1, out=maps[r])
+    fs = [cal["requests"][r]["f"] for r in range(B)]
+    maps = qam.build_level_maps(dev(fld.coords), reqs, fs, g=1.0, combine="sum", glass=1)
     lv = host(maps)
+    for r, (cc, rr) in enumerate(reqs):
+        assert np.array_equal(lv[r], O.level_map(fld.coords, cc, rr, fs[r], 1.0, "sum", 5, 1))
     offs = fld.block_offsets()
     items, xs = [], []
     for i, m in enumerate(fld.matrices):
