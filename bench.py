@@ -107,11 +107,32 @@ def run_field(args, torch, Q, WL):
     log(f"workload {desc}; f={lens.f:.6f} g={lens.g} glass={lens.glass}")
     coords, lv, lv_h, items, wbytes, other = build_field(fld, lens, args.batch, torch, Q, dev)
     w = fld.block_weights()
+    if args.uniform_map:
+        # the same mean bits with every block at one depth (3 bits: D2 and D4
+        # alternating by block parity, every matrix having an even block count)
+        mb = float(args.mean_bits)
+        if mb == 3.0:
+            u = np.where(np.arange(fld.n_blocks) % 2 == 0, 1, 2).astype(np.uint8)
+        else:
+            u = np.full(fld.n_blocks, int(mb) // 2, np.uint8)
+        lv.copy_(torch.from_numpy(u).to(dev))
+        lv_h = u
+        offs = fld.block_offsets()
+        wbytes = other = 0
+        for i, m in enumerate(fld.matrices):
+            ui = u[offs[i]:offs[i] + m.n_blocks]
+            wbytes += Q.map_weight_bytes(ui, m.K)[1]
+            other += int(np.count_nonzero(ui)) * 64 * 4 + args.batch * (m.K + m.N) * 4 + m.n_blocks
+        desc += f"; uniform map at {mb:g} bits (no lenses)"
     mean_bits = float(np.sum(w * np.array(Q.LADDER_BITS)[lv_h]) / np.sum(w))
     group = Q.GroupedQmatvec(items, device=dev)
 
+    def build_map():
+        if not args.uniform_map:
+            Q.build_level_map(coords, lens.centres, lens.radii, lens.f, lens.g, lens.combine, lens.glass, out=lv)
+
     def step():
-        Q.build_level_map(coords, lens.centres, lens.radii, lens.f, lens.g, lens.combine, lens.glass, out=lv)
+        build_map()
         group.run()
 
     # Kernel durations: events around each launch on the stream the kernels run on.
@@ -122,7 +143,7 @@ def run_field(args, torch, Q, WL):
     for _ in range(args.steps):
         a, b, e = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         a.record()
-        Q.build_level_map(coords, lens.centres, lens.radii, lens.f, lens.g, lens.combine, lens.glass, out=lv)
+        build_map()
         b.record()
         group.run()
         e.record()
@@ -159,7 +180,7 @@ def run_field(args, torch, Q, WL):
     ms = wall * 1e3 / args.steps
     return dict(desc=desc, mean_bits=mean_bits, wbytes=wbytes, other=other, ms=ms, kern_ms=kern_ms, map_ms=map_ms,
                 variant=Q.last_variant(), lens=lens, fld=fld, lv_h=lv_h, n_items=len(items),
-                key=f"{args.workload}_{args.mean_bits}_g{lens.glass}_b{args.batch}")
+                key=f"{args.workload}_{args.mean_bits}_g{lens.glass}_b{args.batch}" + ("_uniform" if args.uniform_map else ""))
 
 
 # ----------------------------------------------------------------- batched per-request layer
@@ -452,6 +473,8 @@ def main():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--x-dtype", default="f32", choices=["f32", "bf16"], help="activations (batched_layer)")
+    ap.add_argument("--uniform-map", action="store_true",
+                    help="streaming_stack: every block at one depth, the same mean bits as the lens map")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a captured step")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode tokens/s leg of the default run")
@@ -549,6 +572,7 @@ def main():
             "mean_bits": round(res["mean_bits"], 6),
             "weight_bytes_per_step": int(res["wbytes"]),
             "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+            "map": "uniform" if args.uniform_map else "lens",
             "focus_area_f": res["lens"].f, "focus_strength_g": res["lens"].g, "glass_rung": res["lens"].glass,
             "matrices_per_launch": res["n_items"],
             "level_map_ms": round(res["map_ms"], 5),
