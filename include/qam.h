@@ -231,9 +231,13 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   untruncated int8 product.  A non-finite x makes that request's
  *   non-ZERO outputs NaN.
  *
- *   Routes.  Batches of 1 (and small batches with a shared map) run on the
- *   vector ALUs: each 16-byte slice word becomes four int8x4 code words
- *   multiplied by the limbs with v_dot4.  Batches of QAM_MAX_BATCH+1 .. 32,
+ *   Routes.  Batch 1 stages each sub-chunk's limbs in LDS and multiplies
+ *   the rebuilt codes (four int8x4 words per 16-byte slice word, 16 rows x
+ *   64 columns per lane group) by them with v_mfma_i32_16x16x64_i8, the
+ *   three limbs being columns 0-2 of the B operand; its dot4 form (the same
+ *   integers, so the same bits) serves small shared-map batches on the
+ *   vector ALUs when the matrix-core threshold below is raised.  Batches of
+ *   QAM_MAX_BATCH+1 .. 32,
  *   per-request maps, and shared-map batches from a tunable threshold (2)
  *   run on the matrix cores: a pre-pass writes the limbs of x per column
  *   chunk as MFMA B operands, and v_mfma_i32_16x16x64_i8 multiplies the

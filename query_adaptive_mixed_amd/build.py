@@ -38,6 +38,7 @@ CFLAGS = [
 # through copies on every ring step of the unrolled loop.
 EXTRA_FLAGS = {
     "qmm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "qmatvec.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

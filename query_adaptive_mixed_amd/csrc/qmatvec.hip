@@ -5,20 +5,26 @@
 // d bits touches d/2 slice planes, a ZERO block nothing.  Cost is the weight
 // bytes read ("Precision on Demand", abstract).
 //
-// Work decomposition.  A workgroup is one wavefront and takes one block of
-// 64 rows and one chunk of columns (tiles_per_chunk tiles of 64).  The wave
-// first loads its chunk of x and the first half of its weight-prefetch ring,
-// then turns the chunk of x into an exact fixed-point form in LDS:
-//     v_k = rint(x_k * 2^(30-e)),   2^(e-1) <= max_chunk |x| < 2^e,
-// held as four signed int8 limbs v_k = sum_l s_l 256^l (balanced digits of
-// v_k + 0x80808080).  Each lane owns, per 64-column tile and per slice, one
-// 16-byte word group covering 4 rows x 16 columns; codes are rebuilt in
-// registers (one mask per slice and one rotate per four codes) and multiplied
-// into the limbs with v_dot4_i32_i8, exactly, in int32.  The limb sums are
-// combined into an exact integer per row and chunk, scaled by 2^(e-30) in
-// fp64 (still exact), and either written as the output (one chunk) or stored
-// as a partial; the last wavefront of a block to finish sums the partials in
-// chunk order and writes y = fl32(scale * sum).  No floating-point atomics:
+// Work decomposition.  A workgroup is one wavefront (or, for batch 1, up to
+// eight splitting a chunk's tiles) and takes one block of 64 rows and one
+// chunk of columns (tiles_per_chunk tiles of 64).  The wave walks its chunk in
+// sub-chunks of at most 16 tiles: it loads the sub-chunk's x and the first half
+// of its weight-prefetch ring, then turns that x into an exact fixed-point
+// form in LDS:
+//     v_k = rint(x_k * 2^(22-e)),   2^(e-1) <= max_sub-chunk |x| < 2^e,
+// held as three signed int8 limbs v_k = sum_l s_l 256^l (balanced digits).
+// Each lane owns, per 64-column tile and per slice, one 16-byte word group
+// covering 4 rows x 16 columns; codes are rebuilt in registers (one mask per
+// slice and one rotate per four codes) and multiplied into the limbs exactly,
+// in int32: with v_dot4_i32_i8 on the vector ALUs (every batch up to 8), or,
+// at batch 1, with v_mfma_i32_16x16x64_i8 on the matrix cores, the rebuilt
+// words being the A operand as they stand and the three limbs columns 0-2 of
+// the B operand (columns 3-15 zero).  The limb sums are combined into an
+// exact integer per row and sub-chunk, scaled by 2^(e-22) into an fp64 row
+// sum, and either written as the output (one chunk) or stored as a partial;
+// the last wavefront of a block to finish sums the partials in chunk order and
+// writes y = fl32(scale * sum).  Both inner products give the same integers,
+// so the two batch-1 forms give the same bits.  No floating-point atomics:
 // results are bit-reproducible.
 //
 // The same kernel serves one matrix (descriptor passed by value) and a group
@@ -95,6 +101,31 @@ __device__ __forceinline__ void tile_dots(const u32x4* buf, const int4* __restri
 #undef QAM_GROUP
 }
 
+// One tile on the matrix cores (batch 1): for each 16-row group j, the
+// rebuilt codes of the lane (row 16j + (L & 15), columns 16(L >> 4) + 0..15)
+// are the A operand; bm holds the lane's B operand: limb (L & 15) of the
+// same 16 columns for L & 15 < 3, zero otherwise.  acc[j] gets the 16 x 16
+// int32 product: lane L holds limb column L & 15 of rows 16j + 4(L >> 4) + i.
+template <int NS>
+__device__ __forceinline__ void tile_mfma(const u32x4* buf, const int4* __restrict__ lt, v4i (&acc)[4]) {
+    const int4 b4 = *lt;
+    const v4i bm = v4i{b4.x, b4.y, b4.z, b4.w};
+    uint32_t w[4][NS];
+#pragma unroll
+    for (int p = 0; p < NS; ++p) {
+        w[0][p] = buf[p].x;
+        w[1][p] = buf[p].y;
+        w[2][p] = buf[p].z;
+        w[3][p] = buf[p].w;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const v4i A = v4i{(int)assemble<NS, 0>(w[j]), (int)assemble<NS, 1>(w[j]), (int)assemble<NS, 2>(w[j]),
+                          (int)assemble<NS, 3>(w[j])};
+        acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bm, acc[j], 0, 0, 0);
+    }
+}
+
 template <int NS, int H>
 __device__ __forceinline__ void load_half(u32x4 (&h)[H][NS], const uint8_t* base, int64_t pb, int64_t tstride,
                                           int tile, int last) {
@@ -117,7 +148,11 @@ __device__ __forceinline__ void lds_order() {
 
 // Turn this wave's sub-chunk of x into limb words in LDS (see the file comment).
 // xraw[r][i] holds the x values of group lane + 64 i of request r.
-template <int NB, int G, bool XBF16>
+// Limb layouts: for the dot4 product, group g's limb words as one 16-byte
+// slot (limb_slot); for the matrix-core product (MF, batch 1), per tile 16
+// slots of 16 bytes, slot 4l + k holding limb l of the tile's columns
+// 16k .. 16k + 15 (the B operand of lane 16k + l), slots 12-15 zero.
+template <int NB, int G, bool XBF16, bool MF>
 __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngroups, int slots, int L,
                                             int4* __restrict__ lds, int (&exps)[NB], bool (&bad)[NB],
                                             bool want_ssq, double (&ssq)[NB]) {
@@ -169,7 +204,15 @@ __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngro
             } else {   // every |x| of the sub-chunk below 2^-104
                 w0 = limbs_of(v.x, sh), w1 = limbs_of(v.y, sh), w2 = limbs_of(v.z, sh), w3 = limbs_of(v.w, sh);
             }
-            lds[r * slots + limb_slot(g)] = limb_words(w0, w1, w2, w3);
+            const int4 lw = limb_words(w0, w1, w2, w3);
+            if constexpr (MF) {
+                int* wl = reinterpret_cast<int*>(lds) + (g >> 4) * 64 + (g & 15);
+                wl[0] = lw.x;
+                wl[16] = lw.y;
+                wl[32] = lw.z;
+            } else {
+                lds[r * slots + limb_slot(g)] = lw;
+            }
         }
     }
     lds_order();   // the writes come before the tile loop's reads
@@ -243,9 +286,10 @@ __device__ __forceinline__ void finish_zero(const Item& a, int b, int L) {
 // is walked in sub-chunks of S tiles; each sub-chunk's exact integer sums are
 // scaled into a per-row fp64 sum (exact but for fp64 rounding across
 // sub-chunks, in a fixed order).
-template <int NS, int NB, bool XBF16>
+template <int NS, int NB, bool XBF16, bool MF>
 __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* __restrict__ lds, int b, int chunk,
                                           int L, int ks, int KS, double* red) {
+    static_assert(!MF || NB == 1, "the matrix-core inner product serves batch 1");
     constexpr int H = Ring<NS, NB>::H;
     constexpr int PF = Ring<NS, NB>::PF;
     constexpr int S = Stage<NB>::S;
@@ -260,6 +304,15 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     const int kg = L >> 4;
     const int slots = S * 16;
     const int64_t pb = a.plane_bytes;
+
+    // MF: this lane's B-operand slot, and the zero slots 12-15 of every tile
+    // (written once; staging never touches them)
+    int kslot = 0;
+    if constexpr (MF) {
+        kslot = (L & 15) < kLimbs ? (L & 15) * 4 + kg : 12 + kg;
+        lds[(L >> 2) * 16 + 12 + (L & 3)] = int4{0, 0, 0, 0};
+    }
+    int* tab = reinterpret_cast<int*>(lds + S * 16);   // MF: [3 limbs][64 rows] sums of a sub-chunk
 
     double mine[NB];
     bool any_bad[NB];
@@ -304,17 +357,25 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
         //    then the second half ring
         int exps[NB];
         bool bad[NB];
-        stage_limbs<NB, G, XBF16>(xraw, ngroups, slots, L, lds, exps, bad, want_ssq, ssq);
+        stage_limbs<NB, G, XBF16, MF>(xraw, ngroups, slots, L, lds, exps, bad, want_ssq, ssq);
         load_half<NS, H>(Bh, base, pb, tstride, H, last);
         __builtin_amdgcn_sched_barrier(0);
 
         int acc[NB][4][kLimbs];
+        v4i macc[4];
 #pragma unroll
         for (int r = 0; r < NB; ++r)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int l = 0; l < kLimbs; ++l) acc[r][j][l] = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) macc[j] = v4i{0, 0, 0, 0};
+#define QAM_TILE(BUF, TT)                                                   \
+    do {                                                                    \
+        if constexpr (MF) tile_mfma<NS>(BUF, lds + (TT) * 16 + kslot, macc); \
+        else tile_dots<NS, NB>(BUF, lds + (TT) * 16 + kg, slots, acc);     \
+    } while (0)
 
         // Steady state: every tile of these rounds is in range.  The scheduling
         // barriers keep each reload right after the half it replaces, ahead of
@@ -322,12 +383,12 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
         int t = 0;
         for (; t + PF < nt; t += PF) {
 #pragma unroll
-            for (int u = 0; u < H; ++u) tile_dots<NS, NB>(A[u], lds + (t + u) * 16 + kg, slots, acc);
+            for (int u = 0; u < H; ++u) QAM_TILE(A[u], t + u);
             __builtin_amdgcn_sched_barrier(0);
             load_half<NS, H>(A, base, pb, tstride, t + PF, last);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < H; ++u) tile_dots<NS, NB>(Bh[u], lds + (t + H + u) * 16 + kg, slots, acc);
+            for (int u = 0; u < H; ++u) QAM_TILE(Bh[u], t + H + u);
             __builtin_amdgcn_sched_barrier(0);
             load_half<NS, H>(Bh, base, pb, tstride, t + PF + H, last);
             __builtin_amdgcn_sched_barrier(0);
@@ -335,10 +396,25 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
         // Drain: the last ring, whose tail may run past a ragged sub-chunk.
 #pragma unroll
         for (int u = 0; u < H; ++u)
-            if (t + u < nt) tile_dots<NS, NB>(A[u], lds + (t + u) * 16 + kg, slots, acc);
+            if (t + u < nt) QAM_TILE(A[u], t + u);
 #pragma unroll
         for (int u = 0; u < H; ++u)
-            if (t + H + u < nt) tile_dots<NS, NB>(Bh[u], lds + (t + H + u) * 16 + kg, slots, acc);
+            if (t + H + u < nt) QAM_TILE(Bh[u], t + H + u);
+#undef QAM_TILE
+
+        if constexpr (MF) {
+            // the three limb columns of every row through LDS, then row L's
+            // exact integer on lane L (the same value the dot4 form reaches)
+            if ((L & 15) < kLimbs) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(tab + (L & 15) * 64 + 16 * j + 4 * kg) = macc[j];
+            }
+            lds_order();
+            const double d = (double)tab[128 + L] * 65536.0 + (double)tab[64 + L] * 256.0 + (double)tab[L];
+            mine[0] += ldexp(d, exps[0] - kFrac);
+            any_bad[0] = any_bad[0] || bad[0];
+            continue;
+        }
 
         // exact per-row integers, summed over the four lane groups sharing a
         // row, scaled by this sub-chunk's exponent into the row's fp64 sum
@@ -419,10 +495,11 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
 
 // One workgroup = c.KS wavefronts (at most MAXW) = one (block, column chunk)
 // of one matrix; wave k takes the chunk's tiles k, k + KS, ...
-template <int NB, bool GROUPED, bool XBF16, int MAXW>
+template <int NB, bool GROUPED, bool XBF16, int MAXW, bool MF>
 __global__ __launch_bounds__(64 * MAXW) void qmatvec_kernel(Item single, Common c) {
-    // per wave: [NB][S * 16] limb words of its sub-chunk; then, with several
-    // waves, [KS][NB][2][64] fp64 row sums handed to wave 0
+    // per wave: [NB][S * 16] limb words of its sub-chunk (batch 1: then 3 x 64
+    // int32 sums); then, with several waves, [KS][NB][2][64] fp64 row sums
+    // handed to wave 0
     extern __shared__ int4 lds[];
     Item a;
     int local;
@@ -436,7 +513,7 @@ __global__ __launch_bounds__(64 * MAXW) void qmatvec_kernel(Item single, Common 
     }
     const int KS = MAXW == 1 ? 1 : c.KS;
     const int ks = MAXW == 1 ? 0 : (int)(threadIdx.x >> 6);
-    const int region = NB * Stage<NB>::S * 16;   // int4 per wave
+    const int region = NB * Stage<NB>::S * 16 + (NB == 1 ? 48 : 0);   // int4 per wave
     int4* mylds = lds + ks * region;
     double* red = reinterpret_cast<double*>(lds + KS * region);
     const int chunk = local % a.n_chunks;
@@ -448,10 +525,10 @@ __global__ __launch_bounds__(64 * MAXW) void qmatvec_kernel(Item single, Common 
         case 0:   // ZERO: nothing read, y = 0 (written once, by the first chunk's first wave)
             if (chunk == 0 && ks == 0) finish_zero<NB>(a, b, L);
             return;
-        case 1: wave_body<1, NB, XBF16>(a, c, mylds, b, chunk, L, ks, KS, red); return;
-        case 2: wave_body<2, NB, XBF16>(a, c, mylds, b, chunk, L, ks, KS, red); return;
-        case 3: wave_body<3, NB, XBF16>(a, c, mylds, b, chunk, L, ks, KS, red); return;
-        default: wave_body<4, NB, XBF16>(a, c, mylds, b, chunk, L, ks, KS, red); return;
+        case 1: wave_body<1, NB, XBF16, MF>(a, c, mylds, b, chunk, L, ks, KS, red); return;
+        case 2: wave_body<2, NB, XBF16, MF>(a, c, mylds, b, chunk, L, ks, KS, red); return;
+        case 3: wave_body<3, NB, XBF16, MF>(a, c, mylds, b, chunk, L, ks, KS, red); return;
+        default: wave_body<4, NB, XBF16, MF>(a, c, mylds, b, chunk, L, ks, KS, red); return;
     }
 }
 
@@ -463,7 +540,12 @@ static int64_t g_max_chunk_tiles = 64;       // longest column chunk of the batc
 // every chunk holds a whole number of prefetch rings (Ring<NS, B>::PF for every NS)
 int tpc_align_for(int64_t B) { return B == 1 ? 8 : (B == 2 ? 4 : 2); }
 int stage_tiles_for(int64_t B) { return B == 1 ? 16 : (B == 2 ? 12 : (B <= 4 ? 8 : 4)); }
-size_t lds_bytes_for(int64_t B) { return (size_t)B * stage_tiles_for(B) * 16 * sizeof(int4); }
+size_t lds_bytes_for(int64_t B) {
+    return ((size_t)B * stage_tiles_for(B) * 16 + (B == 1 ? 48 : 0)) * sizeof(int4);
+}
+
+// Batch 1 inner product: 1 = matrix cores, 0 = dot4 on the vector ALUs.
+static int g_b1_mfma = 1;
 
 // Column chunk length (in tiles) for a launch covering `block_tiles` block x
 // tile pairs: enough chunks for about g_target_waves wavefronts of equal work.
@@ -493,12 +575,25 @@ Plan make_plan(int64_t N, int64_t K, int64_t B, int goal, int align) {
     return p;
 }
 
+template <int NB, bool GROUPED, int MAXW, bool MF>
+static void launch_k(const Item& it, const Common& c, int64_t grid, int threads, size_t lds, hipStream_t s) {
+    if (c.x_bf16)
+        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, true, MAXW, MF>), dim3((unsigned)grid), dim3(threads), lds, s,
+                           it, c);
+    else
+        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, false, MAXW, MF>), dim3((unsigned)grid), dim3(threads), lds, s,
+                           it, c);
+}
+
 template <int NB, bool GROUPED>
 static void launch_nb(const Item& it, const Common& c, int64_t grid, size_t lds, hipStream_t s) {
-    if (c.x_bf16)
-        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, true, 1>), dim3((unsigned)grid), dim3(64), lds, s, it, c);
-    else
-        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, false, 1>), dim3((unsigned)grid), dim3(64), lds, s, it, c);
+    if constexpr (NB == 1) {
+        if (g_b1_mfma) {
+            launch_k<1, GROUPED, 1, true>(it, c, grid, 64, lds, s);
+            return;
+        }
+    }
+    launch_k<NB, GROUPED, 1, false>(it, c, grid, 64, lds, s);
 }
 
 template <bool GROUPED>
@@ -518,11 +613,10 @@ static void launch(int64_t B, const Item& it, const Common& c, int64_t grid, siz
 void launch_single(int64_t B, const Item& it, const Common& c, int64_t grid, hipStream_t s) {
     if (B == 1 && c.KS > 1) {   // several waves per (block, chunk): batch 1 only
         const size_t lds = (size_t)c.KS * lds_bytes_for(1) + (size_t)c.KS * 2 * 64 * sizeof(double);
-        if (c.x_bf16)
-            hipLaunchKernelGGL((qmatvec_kernel<1, false, true, 8>), dim3((unsigned)grid), dim3(64 * c.KS), lds, s, it, c);
+        if (g_b1_mfma)
+            launch_k<1, false, 8, true>(it, c, grid, 64 * c.KS, lds, s);
         else
-            hipLaunchKernelGGL((qmatvec_kernel<1, false, false, 8>), dim3((unsigned)grid), dim3(64 * c.KS), lds, s, it,
-                               c);
+            launch_k<1, false, 8, false>(it, c, grid, 64 * c.KS, lds, s);
         return;
     }
     launch<false>(B, it, c, grid, lds_bytes_for(B), s);
@@ -593,6 +687,15 @@ extern "C" int qam_set_max_chunk_tiles(int t) {
     return QAM_OK;
 }
 
+static const char* b1_route_name(int64_t B) { return B == 1 && g_b1_mfma ? "qmatvec_mfma1" : "qmatvec_dot4"; }
+
+extern "C" int qam_set_b1_mfma(int on) {
+    clear_error();
+    if (on != 0 && on != 1) QAM_FAIL(QAM_ERR_ARG, "set_b1_mfma: %d is not 0 or 1", on);
+    g_b1_mfma = on;
+    return QAM_OK;
+}
+
 extern "C" int qam_set_target_waves(int waves) {
     clear_error();
     if (waves < 64 || waves > (1 << 20)) QAM_FAIL(QAM_ERR_ARG, "set_target_waves: %d outside [64, 2^20]", waves);
@@ -641,7 +744,7 @@ extern "C" int qam_qmatvec_ep(const void* x, int x_dtype, int64_t B, const qam_p
     launch_single(B, it, c, grid, s);
     QAM_HIP_CHECK(hipGetLastError());
     char v[128];
-    snprintf(v, sizeof(v), "qmatvec_dot4 B=%lld tpc=%d chunks=%d", (long long)B, p.tpc, p.n_chunks);
+    snprintf(v, sizeof(v), "%s B=%lld tpc=%d chunks=%d", b1_route_name(B), (long long)B, p.tpc, p.n_chunks);
     set_variant(v);
     return QAM_OK;
 }
@@ -788,8 +891,8 @@ extern "C" int qam_qmatvec_group(const qam_group* group, hipStream_t s) {
     launch<true>(group->B, none, c, group->n_workgroups, group->lds_bytes, s);
     QAM_HIP_CHECK(hipGetLastError());
     char v[128];
-    snprintf(v, sizeof(v), "qmatvec_dot4_group items=%d B=%lld wg=%lld", group->n_items, (long long)group->B,
-             (long long)group->n_workgroups);
+    snprintf(v, sizeof(v), "%s_group items=%d B=%lld wg=%lld", b1_route_name(group->B), group->n_items,
+             (long long)group->B, (long long)group->n_workgroups);
     set_variant(v);
     return QAM_OK;
 }

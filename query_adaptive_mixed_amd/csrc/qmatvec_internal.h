@@ -9,6 +9,7 @@ namespace qam {
 // ---------------------------------------------------------------- device helpers
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
 
 // Weight loads must be global (not flat) memory operations: a flat load also

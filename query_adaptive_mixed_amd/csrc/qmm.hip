@@ -30,7 +30,6 @@
 
 namespace qam {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const v4i global_v4i;
 
 constexpr int kBadExp = 0x7FFFFFFF;   // exponent marker of a chunk of x with a non-finite value

@@ -212,9 +212,20 @@ def test_qmatvec_shape_battery(qam, N, K, B):
     pm = pack(qam, W, sc)
     y = host(qam.qmatvec(dev(x), pm, dev(lv)))
     check_y(y, W, sc, x, lv, (N, K, B))
+    from query_adaptive_mixed_amd import _lib as L
+    if B == 1:
+        # batch 1 runs on the matrix cores; the dot4 form of the same kernel
+        # reaches the same integers, so the same bits
+        assert "mfma1" in qam.last_variant()
+        assert L.lib().qam_set_b1_mfma(0) == 0
+        try:
+            y2 = host(qam.qmatvec(dev(x), pm, dev(lv)))
+            assert "dot4" in qam.last_variant()
+        finally:
+            assert L.lib().qam_set_b1_mfma(1) == 0
+        assert np.array_equal(y2.view(np.uint32), y.view(np.uint32)), (N, K)
     if B > 1:
         # the same batch on the dot-product route (the matrix cores take it by default)
-        from query_adaptive_mixed_amd import _lib as L
         assert L.lib().qam_set_mfma_min_batch(9) == 0
         try:
             y = host(qam.qmatvec(dev(x), pm, dev(lv)))

@@ -76,20 +76,34 @@ def test_e2b_field_grouped_launch(qam):
     items = field_items(qam, fld, lv_dev, 1)
     grp = qam.GroupedQmatvec(items)
     grp.run()
-    assert "dot4_group" in qam.last_variant()
+    assert "mfma1_group" in qam.last_variant()
     rng = np.random.default_rng(11)
     offs = fld.block_offsets()
+    ys = []
     for i, m in enumerate(fld.matrices):
         blocks = np.sort(rng.choice(m.n_blocks, 3, replace=False))
         y = host(items[i][2])
+        ys.append(y.copy())
         check_blocks(y, fld.codes(i), fld.scales(i), fld.x(i, 1), lv[offs[i]:offs[i] + m.n_blocks], blocks, False,
                      m.name)
+    # the dot4 form of the batch-1 kernel gives the same bits on every row
+    from query_adaptive_mixed_amd import _lib as L
+    assert L.lib().qam_set_b1_mfma(0) == 0
+    try:
+        grp = qam.GroupedQmatvec(items)
+        grp.run()
+        assert "dot4_group" in qam.last_variant()
+    finally:
+        assert L.lib().qam_set_b1_mfma(1) == 0
+    for i, m in enumerate(fld.matrices):
+        assert np.array_equal(host(items[i][2]).view(np.uint32), ys[i].view(np.uint32)), m.name
 
 
 @pytest.mark.parametrize("B", [1, 8])
 def test_streaming_stack_grouped_launch(qam, B):
     """The streaming stack at 4.0 mean bits (glass D2), all 16 matrices in one
-    grouped launch (dot4 at batch 1, matrix cores at batch 8)."""
+    grouped launch (the batch-1 kernel's matrix-core form at batch 1, the
+    batched matrix-core route at batch 8)."""
     fld = WL.streaming_stack(0)
     c = CAL["streaming_stack"]["glass1_target4.0"]
     cen, rad = WL.stack_lenses(fld)
@@ -106,7 +120,7 @@ def test_streaming_stack_grouped_launch(qam, B):
         items.append((pm, x, y, lv_dev[offs[i]:offs[i] + m.n_blocks]))
     grp = qam.GroupedQmatvec(items)
     grp.run()
-    assert ("mfma" in qam.last_variant()) == (B > 1)
+    assert ("mfma1_group" if B == 1 else "mfma_group") in qam.last_variant()
     for i, m in enumerate(fld.matrices):
         blocks = np.sort(rng.choice(m.n_blocks, 3, replace=False))
         check_blocks(host(items[i][2]), fld.codes(i), fld.scales(i), fld.x(i, B),
