@@ -243,7 +243,7 @@ __device__ double sum_squares(const void* x, int64_t K, int r, int L) {
 // RMS-normalised input), then y = fl32(v) (store), y = fl32(y + v) (residual
 // add) or, for rows interleaved 32 gate / 32 up per block, one output per
 // pair: fl32(silu(gate) * up) with silu(t) = t / (1 + e^-t), all in fp64.
-template <int NB, bool XBF16>
+template <int NB, bool XBF16, bool EPI>
 __device__ __forceinline__ void finish(const Item& a, int b, int L, const double (&sum)[NB], bool have_ssq,
                                        const double (&ssq)[NB]) {
     const int row = b * kRows + L;
@@ -251,14 +251,14 @@ __device__ __forceinline__ void finish(const Item& a, int b, int L, const double
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
         double v = sc * sum[r];
-        if (a.rms) {
+        if (EPI && a.rms) {
             const double ss = have_ssq ? ssq[r] : sum_squares<XBF16>(a.x, a.K, r, L);
             v = v / sqrt(ss / (double)a.K + a.eps);
         }
-        if (a.out_mode == QAM_OUT_GLU) {
+        if (EPI && a.out_mode == QAM_OUT_GLU) {
             const double up = __shfl(v, (L + 32) & 63);
             if (L < 32) a.y[(int64_t)r * (a.N / 2) + b * 32 + L] = (float)(v / (1.0 + exp(-v)) * up);
-        } else if (a.out_mode == QAM_OUT_ADD) {
+        } else if (EPI && a.out_mode == QAM_OUT_ADD) {
             float* yp = a.y + (int64_t)r * a.N + row;
             *yp = (float)((double)*yp + v);
         } else {
@@ -269,12 +269,12 @@ __device__ __forceinline__ void finish(const Item& a, int b, int L, const double
 
 // A ZERO block: every row's sum is 0, so y = 0 (store), y unchanged (add) or
 // silu(0) * 0 = 0 (gated pairs); nothing of the block is read.
-template <int NB>
+template <int NB, bool EPI>
 __device__ __forceinline__ void finish_zero(const Item& a, int b, int L) {
-    if (a.out_mode == QAM_OUT_ADD) return;
+    if (EPI && a.out_mode == QAM_OUT_ADD) return;
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
-        if (a.out_mode == QAM_OUT_GLU) {
+        if (EPI && a.out_mode == QAM_OUT_GLU) {
             if (L < 32) a.y[(int64_t)r * (a.N / 2) + b * 32 + L] = 0.0f;
         } else {
             a.y[(int64_t)r * a.N + (int64_t)b * kRows + L] = 0.0f;
@@ -286,7 +286,7 @@ __device__ __forceinline__ void finish_zero(const Item& a, int b, int L) {
 // is walked in sub-chunks of S tiles; each sub-chunk's exact integer sums are
 // scaled into a per-row fp64 sum (exact but for fp64 rounding across
 // sub-chunks, in a fixed order).
-template <int NS, int NB, bool XBF16, bool MF>
+template <int NS, int NB, bool XBF16, bool MF, bool EPI>
 __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* __restrict__ lds, int b, int chunk,
                                           int L, int ks, int KS, double* red) {
     static_assert(!MF || NB == 1, "the matrix-core inner product serves batch 1");
@@ -318,7 +318,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     bool any_bad[NB];
     double ssq[NB];
     // an unsplit RMS-normalised product sees all of x while staging it
-    const bool want_ssq = a.rms && a.n_chunks == 1;
+    const bool want_ssq = EPI && a.rms && a.n_chunks == 1;
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
         mine[r] = 0.0;
@@ -326,43 +326,28 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
         ssq[r] = 0.0;
     }
 
-    for (int t0 = 0; t0 < ntile; t0 += S) {
-        const int nt = min(S, ntile - t0);
-        const int ngroups = nt * 16;
-        const uint8_t* base = base0 + (int64_t)t0 * tstride;
-        const int last = nt - 1;
-        // Nothing of this wave is in flight here, so this wait is free; it tells
-        // the compiler's wait counting as much (it cannot see it through the
-        // merged control flow of the depth cases and this loop), which keeps
-        // every wait below exact.
-        __builtin_amdgcn_s_waitcnt(0);
-        // 1. x first, so that waiting for it never drains the weight loads issued
-        //    after it (unconditional, clamped loads keep the wait counts exact;
-        //    groups past the sub-chunk are never written to LDS)
-        u32x4 xraw[NB][G];
+    // x of sub-chunk `sub`, raw, G groups of four values per lane and request
+    // (lanes past the sub-chunk reload its last group, never staged)
+    u32x4 xraw[NB][G];
+    auto load_x = [&](int sub) {
+        const int ngroups = min(S, ntile - sub * S) * 16;
 #pragma unroll
         for (int r = 0; r < NB; ++r)
 #pragma unroll
             for (int i = 0; i < G; ++i) {
                 const int g = min(L + 64 * i, ngroups - 1);
-                const int64_t col = (int64_t)(tile0 + ks + KS * (t0 + (g >> 4))) * kTileCols + 4 * (g & 15);
+                const int64_t col = (int64_t)(tile0 + ks + KS * (sub * S + (g >> 4))) * kTileCols + 4 * (g & 15);
                 xraw[r][i] = load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col);
             }
-        // 2. the first half ring of weight loads, straight into the ring registers
-        u32x4 A[H][NS], Bh[H][NS];
-        __builtin_amdgcn_sched_barrier(0);   // x loads go out first ...
-        load_half<NS, H>(A, base, pb, tstride, 0, last);
-        __builtin_amdgcn_sched_barrier(0);   // ... then half a ring, and only then is x used
-        // 3. the limbs of this sub-chunk of x while those loads are in flight,
-        //    then the second half ring
-        int exps[NB];
-        bool bad[NB];
-        stage_limbs<NB, G, XBF16, MF>(xraw, ngroups, slots, L, lds, exps, bad, want_ssq, ssq);
-        load_half<NS, H>(Bh, base, pb, tstride, H, last);
-        __builtin_amdgcn_sched_barrier(0);
-
-        int acc[NB][4][kLimbs];
-        v4i macc[4];
+    };
+    int exps[NB];
+    bool bad[NB];
+    auto stage = [&](int sub) {
+        stage_limbs<NB, G, XBF16, MF>(xraw, min(S, ntile - sub * S) * 16, slots, L, lds, exps, bad, want_ssq, ssq);
+    };
+    int acc[NB][4][kLimbs];
+    v4i macc[4];
+    auto clear_acc = [&]() {
 #pragma unroll
         for (int r = 0; r < NB; ++r)
 #pragma unroll
@@ -371,40 +356,13 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
                 for (int l = 0; l < kLimbs; ++l) acc[r][j][l] = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) macc[j] = v4i{0, 0, 0, 0};
-#define QAM_TILE(BUF, TT)                                                   \
-    do {                                                                    \
-        if constexpr (MF) tile_mfma<NS>(BUF, lds + (TT) * 16 + kslot, macc); \
-        else tile_dots<NS, NB>(BUF, lds + (TT) * 16 + kg, slots, acc);     \
-    } while (0)
-
-        // Steady state: every tile of these rounds is in range.  The scheduling
-        // barriers keep each reload right after the half it replaces, ahead of
-        // the other half's arithmetic, so each wait drains only the older half.
-        int t = 0;
-        for (; t + PF < nt; t += PF) {
-#pragma unroll
-            for (int u = 0; u < H; ++u) QAM_TILE(A[u], t + u);
-            __builtin_amdgcn_sched_barrier(0);
-            load_half<NS, H>(A, base, pb, tstride, t + PF, last);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < H; ++u) QAM_TILE(Bh[u], t + H + u);
-            __builtin_amdgcn_sched_barrier(0);
-            load_half<NS, H>(Bh, base, pb, tstride, t + PF + H, last);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // Drain: the last ring, whose tail may run past a ragged sub-chunk.
-#pragma unroll
-        for (int u = 0; u < H; ++u)
-            if (t + u < nt) QAM_TILE(A[u], t + u);
-#pragma unroll
-        for (int u = 0; u < H; ++u)
-            if (t + H + u < nt) QAM_TILE(Bh[u], t + H + u);
-#undef QAM_TILE
-
+    };
+    // The sub-chunk's exact per-row integers, scaled by its exponent into the
+    // row's fp64 sum.  dot4: summed over the four lane groups sharing a row;
+    // MF: the three limb columns of every row through LDS, then row L's
+    // integer on lane L (the same value either way).
+    auto flush = [&]() {
         if constexpr (MF) {
-            // the three limb columns of every row through LDS, then row L's
-            // exact integer on lane L (the same value the dot4 form reaches)
             if ((L & 15) < kLimbs) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(tab + (L & 15) * 64 + 16 * j + 4 * kg) = macc[j];
@@ -413,25 +371,84 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
             const double d = (double)tab[128 + L] * 65536.0 + (double)tab[64 + L] * 256.0 + (double)tab[L];
             mine[0] += ldexp(d, exps[0] - kFrac);
             any_bad[0] = any_bad[0] || bad[0];
-            continue;
-        }
-
-        // exact per-row integers, summed over the four lane groups sharing a
-        // row, scaled by this sub-chunk's exponent into the row's fp64 sum
+        } else {
 #pragma unroll
-        for (int r = 0; r < NB; ++r) {
-            double d[4];
+            for (int r = 0; r < NB; ++r) {
+                double d[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                d[j] = (double)acc[r][j][2] * 65536.0 + (double)acc[r][j][1] * 256.0 + (double)acc[r][j][0];
-                d[j] += __shfl_xor(d[j], 16);
-                d[j] += __shfl_xor(d[j], 32);
+                for (int j = 0; j < 4; ++j) {
+                    d[j] = (double)acc[r][j][2] * 65536.0 + (double)acc[r][j][1] * 256.0 + (double)acc[r][j][0];
+                    d[j] += __shfl_xor(d[j], 16);
+                    d[j] += __shfl_xor(d[j], 32);
+                }
+                const double sel = kg == 0 ? d[0] : (kg == 1 ? d[1] : (kg == 2 ? d[2] : d[3]));
+                mine[r] += ldexp(sel, exps[r] - kFrac);
+                any_bad[r] = any_bad[r] || bad[r];
             }
-            const double sel = kg == 0 ? d[0] : (kg == 1 ? d[1] : (kg == 2 ? d[2] : d[3]));
-            mine[r] += ldexp(sel, exps[r] - kFrac);
-            any_bad[r] = any_bad[r] || bad[r];
         }
+    };
+#define QAM_TILE(BUF, TT)                                                   \
+    do {                                                                    \
+        if constexpr (MF) tile_mfma<NS>(BUF, lds + (TT) * 16 + kslot, macc); \
+        else tile_dots<NS, NB>(BUF, lds + (TT) * 16 + kg, slots, acc);     \
+    } while (0)
+
+    // One prefetch ring runs through the whole chunk: two halves of H tiles,
+    // each reloaded PF tiles ahead right after it is used.  A round that ends
+    // a sub-chunk loads the next sub-chunk's x before its first reload and,
+    // once its last tile is done, flushes the sums and stages the new limbs,
+    // all inside the round (no x kept in registers from one round to the
+    // next), so a sub-chunk boundary never drains the weight loads in flight.
+    // Every wait below drains only the older half (and x loaded before it).
+    static_assert(S % PF == 0, "sub-chunks hold whole ring rounds");
+    if (ntile > 0) {
+        const int last = ntile - 1;
+        // nothing of this wave is in flight here: this wait is free, and it
+        // keeps the compiler's wait counting exact through the loop below
+        __builtin_amdgcn_s_waitcnt(0);
+        load_x(0);
+        u32x4 A[H][NS], Bh[H][NS];
+        __builtin_amdgcn_sched_barrier(0);   // x loads go out first ...
+        load_half<NS, H>(A, base0, pb, tstride, 0, last);
+        __builtin_amdgcn_sched_barrier(0);   // ... then half a ring, and only then is x used
+        stage(0);
+        load_half<NS, H>(Bh, base0, pb, tstride, H, last);
+        __builtin_amdgcn_sched_barrier(0);
+        clear_acc();
+        int t = 0;
+        // steady rounds: every tile of the round is in range and so is the next round's first
+        for (; t + PF < ntile; t += PF) {
+            const int tl = t % S;
+            const bool ends_sub = tl + PF == S;
+            if (ends_sub) load_x((t + PF) / S);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < H; ++u) QAM_TILE(A[u], tl + u);
+            __builtin_amdgcn_sched_barrier(0);
+            load_half<NS, H>(A, base0, pb, tstride, t + PF, last);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < H; ++u) QAM_TILE(Bh[u], tl + H + u);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ends_sub) {
+                flush();
+                stage((t + PF) / S);
+                clear_acc();
+            }
+            load_half<NS, H>(Bh, base0, pb, tstride, t + PF + H, last);   // past the end: clamped, never used
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the last round, possibly ragged
+        const int tl = t % S;
+#pragma unroll
+        for (int u = 0; u < H; ++u)
+            if (t + u < ntile) QAM_TILE(A[u], tl + u);
+#pragma unroll
+        for (int u = 0; u < H; ++u)
+            if (t + H + u < ntile) QAM_TILE(Bh[u], tl + H + u);
+        flush();
     }
+#undef QAM_TILE
 
     const int row = b * kRows + L;          // the row this lane writes: j = L >> 4
     double part[NB];
@@ -462,7 +479,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
 #pragma unroll
                 for (int o = 1; o < 64; o <<= 1) ssq[r] += __shfl_xor(ssq[r], o);
         }
-        finish<NB, XBF16>(a, b, L, part, want_ssq, ssq);
+        finish<NB, XBF16, EPI>(a, b, L, part, want_ssq, ssq);
         return;
     }
     // Split K: publish this chunk's partials, then count the arrival; the last
@@ -490,45 +507,65 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
                                         __HIP_MEMORY_SCOPE_AGENT);
     }
     if (L == 0) __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    finish<NB, XBF16>(a, b, L, sum, false, ssq);
+    finish<NB, XBF16, EPI>(a, b, L, sum, false, ssq);
 }
 
-// One workgroup = c.KS wavefronts (at most MAXW) = one (block, column chunk)
-// of one matrix; wave k takes the chunk's tiles k, k + KS, ...
-template <int NB, bool GROUPED, bool XBF16, int MAXW, bool MF>
-__global__ __launch_bounds__(64 * MAXW) void qmatvec_kernel(Item single, Common c) {
+// One (block, column chunk) unit of item a, `local` being its index within
+// the item, run by c.KS wavefronts (at most MAXW); wave k takes the chunk's
+// tiles k, k + KS, ...
+template <int NB, bool XBF16, int MAXW, bool MF, bool EPI>
+__device__ __forceinline__ void run_unit(const Item& a, const Common& c, int local, int4* lds, int tid) {
     // per wave: [NB][S * 16] limb words of its sub-chunk (batch 1: then 3 x 64
     // int32 sums); then, with several waves, [KS][NB][2][64] fp64 row sums
     // handed to wave 0
-    extern __shared__ int4 lds[];
-    Item a;
-    int local;
-    if constexpr (GROUPED) {
-        const int idx = c.wg_item[blockIdx.x];
-        a = c.items[idx];
-        local = (int)blockIdx.x - a.wg_begin;
-    } else {
-        a = single;
-        local = (int)blockIdx.x;
-    }
     const int KS = MAXW == 1 ? 1 : c.KS;
-    const int ks = MAXW == 1 ? 0 : (int)(threadIdx.x >> 6);
+    const int ks = MAXW == 1 ? 0 : tid >> 6;
     const int region = NB * Stage<NB>::S * 16 + (NB == 1 ? 48 : 0);   // int4 per wave
     int4* mylds = lds + ks * region;
     double* red = reinterpret_cast<double*>(lds + KS * region);
     const int chunk = local % a.n_chunks;
     const int b = local / a.n_chunks;
-    const int L = threadIdx.x & 63;
+    const int L = tid & 63;
     const int lev = level_of(a.level, b);
     const int ns = __builtin_amdgcn_readfirstlane(lev < 4 ? lev : 4);
     switch (ns) {   // uniform over the workgroup: one block
         case 0:   // ZERO: nothing read, y = 0 (written once, by the first chunk's first wave)
-            if (chunk == 0 && ks == 0) finish_zero<NB>(a, b, L);
+            if (chunk == 0 && ks == 0) finish_zero<NB, EPI>(a, b, L);
             return;
-        case 1: wave_body<1, NB, XBF16, MF>(a, c, mylds, b, chunk, L, ks, KS, red); return;
-        case 2: wave_body<2, NB, XBF16, MF>(a, c, mylds, b, chunk, L, ks, KS, red); return;
-        case 3: wave_body<3, NB, XBF16, MF>(a, c, mylds, b, chunk, L, ks, KS, red); return;
-        default: wave_body<4, NB, XBF16, MF>(a, c, mylds, b, chunk, L, ks, KS, red); return;
+        case 1: wave_body<1, NB, XBF16, MF, EPI>(a, c, mylds, b, chunk, L, ks, KS, red); return;
+        case 2: wave_body<2, NB, XBF16, MF, EPI>(a, c, mylds, b, chunk, L, ks, KS, red); return;
+        case 3: wave_body<3, NB, XBF16, MF, EPI>(a, c, mylds, b, chunk, L, ks, KS, red); return;
+        default: wave_body<4, NB, XBF16, MF, EPI>(a, c, mylds, b, chunk, L, ks, KS, red); return;
+    }
+}
+
+// The descriptor of grouped unit u.  The table and the unit map do not change
+// while a launch runs, so they are read through the constant address space:
+// scalar loads, even after the kernel has stored to global memory.
+typedef __attribute__((address_space(4))) const int const_int;
+__device__ __forceinline__ Item unit_item(const Common& c, int u) {
+    static_assert(sizeof(Item) % 4 == 0, "descriptor in whole dwords");
+    const int idx = *(const_int*)(c.wg_item + u);
+    const const_u32* src = (const const_u32*)(c.items + idx);
+    uint32_t w[sizeof(Item) / 4];
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(Item) / 4); ++i) w[i] = src[i];
+    Item a;
+    __builtin_memcpy(&a, w, sizeof(Item));
+    return a;
+}
+
+// One workgroup per unit: a single matrix (descriptor by value; with its
+// epilogue) or a group (descriptor table, one lookup per workgroup; plain
+// stores, the only output a group's items have).
+template <int NB, bool GROUPED, bool XBF16, int MAXW, bool MF>
+__global__ __launch_bounds__(64 * MAXW) void qmatvec_kernel(Item single, Common c) {
+    extern __shared__ int4 lds[];
+    if constexpr (GROUPED) {
+        const Item a = unit_item(c, (int)blockIdx.x);
+        run_unit<NB, XBF16, MAXW, MF, false>(a, c, (int)blockIdx.x - a.wg_begin, lds, (int)threadIdx.x);
+    } else {
+        run_unit<NB, XBF16, MAXW, MF, true>(single, c, (int)blockIdx.x, lds, (int)threadIdx.x);
     }
 }
 
@@ -887,10 +924,10 @@ extern "C" int qam_qmatvec_group(const qam_group* group, hipStream_t s) {
     c.B = (int)group->B;
     c.x_bf16 = group->x_dtype == QAM_X_BF16;
     c.KS = 1;
+    char v[128];
     Item none{};
     launch<true>(group->B, none, c, group->n_workgroups, group->lds_bytes, s);
     QAM_HIP_CHECK(hipGetLastError());
-    char v[128];
     snprintf(v, sizeof(v), "%s_group items=%d B=%lld wg=%lld", b1_route_name(group->B), group->n_items,
              (long long)group->B, (long long)group->n_workgroups);
     set_variant(v);
