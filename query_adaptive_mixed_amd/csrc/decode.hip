@@ -124,6 +124,7 @@ int enqueue(qam_decoder* dec, int rung, int first, int count, hipStream_t s) {
         const Plan p = plan_of(*op.w, dec->target_waves);
         c.KS = dec->ksplit;   // waves per (block, chunk)
         Item it = make_item(op.x, op.w, dec->maps[rung], op.y, p);
+        it.fixed_level = rung;   // the map is uniform: the kernel takes the rung, not the map bytes
         it.rms = op.rms;
         it.out_mode = op.out_mode;
         it.eps = dec->d.eps;

@@ -526,7 +526,7 @@ __device__ __forceinline__ void run_unit(const Item& a, const Common& c, int loc
     const int chunk = local % a.n_chunks;
     const int b = local / a.n_chunks;
     const int L = tid & 63;
-    const int lev = level_of(a.level, b);
+    const int lev = a.fixed_level >= 0 ? a.fixed_level : level_of(a.level, b);
     const int ns = __builtin_amdgcn_readfirstlane(lev < 4 ? lev : 4);
     switch (ns) {   // uniform over the workgroup: one block
         case 0:   // ZERO: nothing read, y = 0 (written once, by the first chunk's first wave)
@@ -697,6 +697,7 @@ Item make_item(const void* x, const qam_packed* packed, const uint8_t* level_map
     it.tpc = p.tpc;
     it.n_chunks = p.n_chunks;
     it.n_quads = p.n_quads;
+    it.fixed_level = -1;
     return it;
 }
 
@@ -814,6 +815,9 @@ extern "C" int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_pack
 
 namespace qam {
 
+static int g_tail_pct = 15;   // share of a group's block tiles planned with short chunks
+static int g_tail_div = 2;    // how much shorter
+
 struct GroupLayout {
     std::vector<Plan> plans;
     size_t partial_bytes = 0, table_bytes = 0, map_bytes = 0, total = 0;
@@ -831,8 +835,16 @@ static int layout_group(const qam_gemv_item* items, int n_items, int64_t B, Grou
         g.block_tiles += w.N / kRows * (w.K / kTileCols);
     }
     if (g.blocks > QAM_MAX_BLOCKS) QAM_FAIL(QAM_ERR_SHAPE, "group: %lld blocks > %d", (long long)g.blocks, QAM_MAX_BLOCKS);
+    // Items are dispatched in order, so the last ones run while the chip
+    // drains: those covering the last g_tail_pct percent of the block tiles
+    // take chunks g_tail_div times shorter, so that the final wavefronts are short.
+    const int goal = chunk_goal(g.block_tiles, 0);
+    int64_t before = 0;
     for (int i = 0; i < n_items; ++i) {
-        const Plan p = make_plan(items[i].w.N, items[i].w.K, B, chunk_goal(g.block_tiles, 0));
+        const int64_t bt = items[i].w.N / kRows * (items[i].w.K / kTileCols);
+        const bool tail = g_tail_pct > 0 && (before + bt) * 100 > g.block_tiles * (100 - g_tail_pct);
+        before += bt;
+        const Plan p = make_plan(items[i].w.N, items[i].w.K, B, tail ? std::max(1, goal / g_tail_div) : goal);
         g.plans.push_back(p);
         g.partial_bytes += p.partial_bytes;
         g.n_wg += (int64_t)p.n_chunks * p.n_quads;
@@ -845,6 +857,14 @@ static int layout_group(const qam_gemv_item* items, int n_items, int64_t B, Grou
 }
 
 }  // namespace qam
+
+extern "C" int qam_set_tail_split(int pct, int div) {
+    clear_error();
+    if (pct < 0 || pct > 100 || div < 1 || div > 64) QAM_FAIL(QAM_ERR_ARG, "set_tail_split: pct %d / div %d out of range", pct, div);
+    g_tail_pct = pct;
+    g_tail_div = div;
+    return QAM_OK;
+}
 
 extern "C" size_t qam_group_bytes(const qam_gemv_item* items, int n_items, int64_t B, int per_request_maps) {
     if (per_request_maps != 0 && per_request_maps != 1) return 0;

@@ -108,6 +108,7 @@ struct Item {
     int n_chunks;
     int n_quads;               // workgroups per chunk (one per block)
     int wg_begin;              // first workgroup of this item in a grouped launch
+    int fixed_level;           // >= 0: every block at this rung, `level` not read (uniform maps)
     int rms;                   // 1: y uses x / sqrt(mean(x^2) + eps)
     int out_mode;              // QAM_OUT_STORE / _ADD / _GLU
     double eps;
