@@ -506,7 +506,7 @@ def main():
             "metric": "achieved HBM GB/s (% of peak) and decode tokens/s at mean bits/weight",
             "value": d["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": d["steps"], "warmup": 8,
             "ms_per_step": d["ms_per_token"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "int8 codes x fp32 activations (exact int8 dot4 on 24-bit fixed-point x), fp32 out",
+            "dtype": "int8 codes x fp32 activations (exact i8 MFMA on 24-bit fixed-point x in 3 int8 limbs), fp32 out",
             "data": "synthetic (seeded codes, scales, step inputs and escalation scores)",
             "config": {k: v for k, v in d.items() if not k.startswith("_")},
         }
@@ -563,7 +563,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 codes x fp32 activations (exact int8 dot4 on 24-bit fixed-point x, 3 int8 limbs), fp32 out",
+        "dtype": "int8 codes x fp32 activations (exact i8 MFMA on 24-bit fixed-point x in 3 int8 limbs), fp32 out",
         "data": "synthetic (seeded codes, scales, activations, block coordinates and lenses)",
         "config": {
             "workload": args.workload,
