@@ -183,12 +183,12 @@ def _check_chain_against_oracle(qam, dec, fld, cfg, rung, x0, head_rows=None):
     return host(dec.logits).copy(), host(dec.hidden).copy()
 
 
-@pytest.mark.parametrize("wpb,tw", [(0, 0), (1, 0), (2, 0), (4, 512)])
+@pytest.mark.parametrize("wpb,tw", [(0, 0), (1, 0), (2, 0), (8, 0), (4, 512)])
 @pytest.mark.parametrize("rung", [2, 4, 1, 0])
 def test_decoder_products_match_oracle(qam, rung, wpb, tw):
-    """Every product of the chain against the oracle, for 1, 2 and 4 waves per
-    block (uneven tile shares: 4, 6 and 8 tiles over the waves) and with a
-    wide launch that also splits K across workgroups."""
+    """Every product of the chain against the oracle, for 1, 2, 4 and 8 waves
+    per block (uneven tile shares: 4, 6 and 8 tiles over the waves) and with
+    a wide launch that also splits K across workgroups."""
     fld, dec = _make_decoder(qam, SMALL, target_waves=tw, waves_per_block=wpb)
     x0 = WL.decode_inputs(0, 1, SMALL["hidden"])[0]
     logits, h = _check_chain_against_oracle(qam, dec, fld, SMALL, rung, x0)
