@@ -59,7 +59,7 @@ extern "C" {
 #define QAM_MAX_K          65536      /* keeps every exact integer sum in range */
 #define QAM_MAX_LENSES     64
 #define QAM_MAX_RUNGS      16
-#define QAM_MAX_BATCH      8          /* requests per call on the dot-product route   */
+#define QAM_MAX_BATCH      8          /* requests per call on the staged-limb route   */
 #define QAM_MAX_BATCH_MFMA 32         /* requests per qam_qmatvec call (matrix cores) */
 #define QAM_MAX_BLOCKS     65536      /* blocks per matrix (N <= 4,194,304)         */
 #define QAM_WS_COUNTER_BYTES (QAM_MAX_BLOCKS * 4)  /* workspace counter region      */
@@ -231,23 +231,23 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   untruncated int8 product.  A non-finite x makes that request's
  *   non-ZERO outputs NaN.
  *
- *   Routes.  Batch 1 stages each sub-chunk's limbs in LDS and multiplies
- *   the rebuilt codes (four int8x4 words per 16-byte slice word, 16 rows x
- *   64 columns per lane group) by them with v_mfma_i32_16x16x64_i8, the
- *   three limbs being columns 0-2 of the B operand; its dot4 form (the same
- *   integers, so the same bits) serves small shared-map batches on the
- *   vector ALUs when the matrix-core threshold below is raised.  Batches of
- *   QAM_MAX_BATCH+1 .. 32,
- *   per-request maps, and shared-map batches from a tunable threshold (2)
- *   run on the matrix cores: a pre-pass writes the limbs of x per column
- *   chunk as MFMA B operands, and v_mfma_i32_16x16x64_i8 multiplies the
- *   codes (16 rows x 64 columns per lane group of words) with 16 requests
- *   of one limb at a time.  With per-request maps a block is read once, to
- *   the deepest slice any request needs, and each request gets the codes at
- *   its own depth, built from the same words (the residual slices make the
- *   code at depth d the sum of the first d/2 slices).  Both routes have the
- *   arithmetic and bound above (the matrix-core route's fixed point is per
- *   column chunk).
+ *   Routes.  The staged-limb route (batch 1, and shared-map batches up to
+ *   QAM_MAX_BATCH below a tunable threshold) stages each sub-chunk's limbs
+ *   in LDS inside the product kernel.  At batch 1 it multiplies the rebuilt
+ *   codes (four int8x4 words per 16-byte slice word, 16 rows x 64 columns
+ *   per lane group) by them with v_mfma_i32_16x16x64_i8, the three limbs
+ *   being columns 0-2 of the B operand; its batches of 2-8 (and batch 1
+ *   when asked) use v_dot4 on the vector ALUs, which reaches the same
+ *   integers, so the same bits.  The pre-pass route (batches of
+ *   QAM_MAX_BATCH+1 .. 32, per-request maps, and shared-map batches from
+ *   the threshold, 2 by default) runs a pre-pass that writes the limbs of x
+ *   per column chunk as MFMA B operands, then v_mfma_i32_16x16x64_i8
+ *   multiplies the codes with 16 requests of one limb at a time.  With
+ *   per-request maps a block is read once, to the deepest slice any request
+ *   needs, and each request gets the codes at its own depth, built from the
+ *   same words (the residual slices make the code at depth d the sum of the
+ *   first d/2 slices).  Both routes have the arithmetic and bound above (the
+ *   pre-pass route's fixed point is per column chunk).
  *
  *   x          (device) [B][K] row-major, fp32 (x_dtype QAM_X_F32) or bf16
  *              (QAM_X_BF16); 16-byte aligned.
@@ -268,7 +268,7 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *              it reads.  Calls that share a workspace must be ordered (same
  *              stream or synchronised).
  *   N          at most QAM_MAX_BLOCKS blocks of 64 rows (half that for
- *              B > 16 on the matrix-core route).
+ *              B > 16 on the pre-pass route).
  */
 size_t qam_qmatvec_workspace_bytes(int64_t N, int64_t K, int64_t B);
 
@@ -299,7 +299,7 @@ int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_packed* packed,
  *                    t / (1 + e^-t), in fp64; y is [B][N/2].
  *   A ZERO block reads nothing: v = 0 for its rows (QAM_OUT_ADD leaves y as
  *   it is, QAM_OUT_GLU writes 0).  Other arguments, the workspace and the
- *   error bound (on v) are those of qam_qmatvec's dot-product route; y must
+ *   error bound (on v) are those of qam_qmatvec's staged-limb route; y must
  *   not overlap x.  B <= QAM_MAX_BATCH, shared map; ep == NULL is that route
  *   of qam_qmatvec.
  */
@@ -345,9 +345,9 @@ typedef struct qam_group {     /* filled by qam_group_init; treat as opaque     
     size_t  lds_bytes;
     void*   table;             /* (device) descriptor table inside dev_mem           */
     void*   wg_map;            /* (device) workgroup -> item map inside dev_mem      */
-    int     route;             /* 0: dot-product route, 1: matrix-core route         */
+    int     route;             /* 0: staged-limb route, 1: pre-pass route            */
     int     per_request_maps;
-    int64_t n_pre_workgroups;  /* matrix-core route: limb pre-pass workgroups        */
+    int64_t n_pre_workgroups;  /* pre-pass route: limb pre-pass workgroups           */
     void*   pre_map;           /* (device) pre-pass workgroup -> item map            */
 } qam_group;
 
@@ -369,7 +369,7 @@ int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dty
                    hipStream_t s);
 
 /*
- * qam_qmatvec_group -- one launch (two on the matrix-core route: the limb
+ * qam_qmatvec_group -- one launch (two on the pre-pass route: the limb
  *   pre-pass, then the product) computing y_i = the mixed-depth product of
  *   every item i, with exactly the arithmetic of qam_qmatvec.  Enqueues
  *   kernels and nothing else (safe to capture in a HIP graph).  Calls on one

@@ -258,7 +258,7 @@ def qmatvec(x: torch.Tensor, packed: PackedMatrix, level_map: torch.Tensor, y: O
 
 class GroupedQmatvec:
     """Many matrices with their own x, y and level map, one launch per call
-    (two on the matrix-core route).
+    (two on the pre-pass route).
 
     ``items`` is a sequence of (PackedMatrix, x [B, K], y [B, N], level_map)
     tuples, the maps all [n_blocks] (shared by the B requests) or all
@@ -309,7 +309,8 @@ class GroupedQmatvec:
 
     @property
     def route(self) -> str:
-        return "mfma" if self.desc.route == 1 else "dot4"
+        """"staged" (limbs staged inside the product kernel) or "prepass" (a limb pre-pass, then the product)."""
+        return "prepass" if self.desc.route == 1 else "staged"
 
     def run(self) -> None:
         L.check(L.lib().qam_qmatvec_group(C.byref(self.desc), _stream_handle()))

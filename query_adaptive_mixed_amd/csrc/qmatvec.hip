@@ -710,11 +710,11 @@ extern "C" size_t qam_qmatvec_workspace_bytes(int64_t N, int64_t K, int64_t B) {
         B > QAM_MAX_BATCH_MFMA)
         return 0;
     size_t need = 0;
-    if (B <= QAM_MAX_BATCH) {   // the dot4 route
+    if (B <= QAM_MAX_BATCH) {   // the staged-limb route
         const Plan p = make_plan(N, K, B, chunk_goal(N / kRows * (K / kTileCols), 0));
         need = p.n_chunks > 1 ? QAM_WS_COUNTER_BYTES + p.partial_bytes : 0;
     }
-    if (B > 1) need = std::max(need, qam_mfma_workspace_bytes(N, K, B));   // the matrix-core route
+    if (B > 1) need = std::max(need, qam_mfma_workspace_bytes(N, K, B));   // the pre-pass route
     return need;
 }
 
@@ -787,7 +787,7 @@ extern "C" int qam_qmatvec_ep(const void* x, int x_dtype, int64_t B, const qam_p
     return QAM_OK;
 }
 
-// Smallest batch with a shared map that takes the matrix-core route.
+// Smallest batch with a shared map that takes the pre-pass route.
 static int g_mfma_min_batch = 2;
 
 bool qam::mfma_route(int64_t B, int per_request_maps) {

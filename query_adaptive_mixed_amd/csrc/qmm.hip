@@ -453,7 +453,7 @@ static int mfma_ncg(int64_t B) { return (int)((3 * std::min<int64_t>(B, 16) + 15
 // waves per set splitting a chunk: at most four waves per workgroup
 static int mfma_ks(int64_t B) { return std::max(1, std::min(g_mfma_ksplit, 4 / mfma_sets(B))); }
 
-// Chunking of one matrix on the matrix-core route, for a chunk length goal.
+// Chunking of one matrix on the pre-pass route, for a chunk length goal.
 static MPlan mplan_goal(int64_t N, int64_t K, int64_t B, int goal) {
     MPlan p{};
     p.NH = mfma_sets(B);
@@ -500,14 +500,14 @@ static MItem make_mitem(const void* x, const qam_packed* w, const uint8_t* level
     return it;
 }
 
-// Workspace of the matrix-core route (0 for bad shapes).
+// Workspace of the pre-pass route (0 for bad shapes).
 size_t qam_mfma_workspace_bytes(int64_t N, int64_t K, int64_t B) {
     if (N <= 0 || K <= 0 || N % kRows || K % kTileCols || K > QAM_MAX_K || B < 1 || B > QAM_MAX_BATCH_MFMA) return 0;
     if (N / kRows > QAM_MAX_BLOCKS) return 0;
     return mplan(N, K, B).total;
 }
 
-// The matrix-core route of qam_qmatvec (arguments already checked by the caller).
+// The pre-pass route of qam_qmatvec (arguments already checked by the caller).
 int qmatvec_mfma(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
                  int per_request_maps, float* y, void* workspace, size_t workspace_bytes, hipStream_t s) {
     const MPlan p = mplan(packed->N, packed->K, B);

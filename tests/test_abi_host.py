@@ -136,7 +136,7 @@ def test_workspace_size_is_zero_for_bad_shapes_and_grows_with_batch(lib):
     assert lib.qam_qmatvec_workspace_bytes(8192, 28672, 8) >= lib.qam_qmatvec_workspace_bytes(8192, 28672, 1)
     assert lib.qam_qmatvec_workspace_bytes(8192, 28672, 32) > 0
     assert lib.qam_qmatvec_workspace_bytes(8192, 28672, 33) == 0
-    # matrix-core route: the limb operands of every tile of x for 16 (32) request slots
+    # pre-pass route: the limb operands of every tile of x for 16 (32) request slots
     assert lib.qam_qmatvec_workspace_bytes(64, 4096, 16) >= 64 * 3 * 1024
     assert lib.qam_qmatvec_workspace_bytes(64, 4096, 32) >= 64 * 6 * 1024
 

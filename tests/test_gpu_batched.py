@@ -1,4 +1,4 @@
-"""GPU parity of the matrix-core route (batches up to 32, shared or
+"""GPU parity of the pre-pass route (batches up to 32, shared or
 per-request level maps) against the CPU oracle, through the C ABI."""
 
 import json
@@ -182,7 +182,7 @@ def test_grouped_matrix_cores(qam, B, per_request):
         mats.append((W, sc, x, lv))
         items.append((pm, dev(x), y, dev(lv)))
     g = qam.GroupedQmatvec(items)
-    assert g.route == "mfma"
+    assert g.route == "prepass"
     g.run()
     first = [host(it[2]).copy() for it in items]
     for (W, sc, x, lv), y in zip(mats, first):

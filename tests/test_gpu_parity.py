@@ -225,7 +225,7 @@ def test_qmatvec_shape_battery(qam, N, K, B):
             assert L.lib().qam_set_b1_mfma(1) == 0
         assert np.array_equal(y2.view(np.uint32), y.view(np.uint32)), (N, K)
     if B > 1:
-        # the same batch on the dot-product route (the matrix cores take it by default)
+        # the same batch on the staged-limb route's dot4 form (the pre-pass route takes it by default)
         assert L.lib().qam_set_mfma_min_batch(9) == 0
         try:
             y = host(qam.qmatvec(dev(x), pm, dev(lv)))

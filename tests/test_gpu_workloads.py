@@ -103,7 +103,7 @@ def test_e2b_field_grouped_launch(qam):
 def test_streaming_stack_grouped_launch(qam, B):
     """The streaming stack at 4.0 mean bits (glass D2), all 16 matrices in one
     grouped launch (the batch-1 kernel's matrix-core form at batch 1, the
-    batched matrix-core route at batch 8)."""
+    pre-pass route at batch 8)."""
     fld = WL.streaming_stack(0)
     c = CAL["streaming_stack"]["glass1_target4.0"]
     cen, rad = WL.stack_lenses(fld)
