@@ -493,8 +493,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        msg = ("this build measures one GPU only: the product is split by output-row blocks and needs no "
-               "collective within a pass, but no multi-GPU path is built; run with --gpus 1")
+        msg = ("bench.py measures one GPU only: the product would split by output-row blocks with no "
+               "collective within a pass, but no multi-GPU path exists; run with --gpus 1")
         print(msg, file=sys.stderr)
         sys.exit(2)
 
