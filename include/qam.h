@@ -217,7 +217,7 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   nothing and writes y = 0.
  *
  *   Arithmetic: x is walked in sub-chunks of columns (at most 1024 for
- *   B = 1, 768 for B = 2, 512 for B <= 4, 256 for B <= 8); each is put on
+ *   B <= 2, 512 for B <= 5, 256 for B <= 8); each is put on
  *   a fixed-point grid, x~ = round(x * 2^(22-e)) * 2^(e-22) with
  *   2^(e-1) <= max|x| < 2^e over the sub-chunk, held as three signed int8
  *   limbs; c . x~ is accumulated exactly in integers (int8 dot products),
@@ -233,14 +233,14 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *
  *   Routes.  The staged-limb route (batch 1, and shared-map batches up to
  *   QAM_MAX_BATCH below a tunable threshold) stages each sub-chunk's limbs
- *   in LDS inside the product kernel.  At batch 1 it multiplies the rebuilt
- *   codes (four int8x4 words per 16-byte slice word, 16 rows x 64 columns
- *   per lane group) by them with v_mfma_i32_16x16x64_i8, the three limbs
- *   being columns 0-2 of the B operand; its batches of 2-8 (and batch 1
- *   when asked) use v_dot4 on the vector ALUs, which reaches the same
- *   integers, so the same bits.  The pre-pass route (batches of
+ *   in LDS inside the product kernel and multiplies the rebuilt codes (four
+ *   int8x4 words per 16-byte slice word, 16 rows x 64 columns per lane
+ *   group) by them with v_mfma_i32_16x16x64_i8, B-operand column 3 r + l
+ *   holding limb l of request r (one group of 16 columns up to 5 requests,
+ *   two up to 8); its dot4 form on the vector ALUs (qam_set_staged_mfma(0))
+ *   reaches the same integers, so the same bits.  The pre-pass route (batches of
  *   QAM_MAX_BATCH+1 .. 32, per-request maps, and shared-map batches from
- *   the threshold, 2 by default) runs a pre-pass that writes the limbs of x
+ *   the threshold, 3 by default) runs a pre-pass that writes the limbs of x
  *   per column chunk as MFMA B operands, then v_mfma_i32_16x16x64_i8
  *   multiplies the codes with 16 requests of one limb at a time.  With
  *   per-request maps a block is read once, to the deepest slice any request

@@ -107,7 +107,7 @@ EXTRA_SIGNATURES = [
     ("qam_set_max_chunk_tiles", _I, [_I]),
     ("qam_set_mfma_target_waves", _I, [_I]),
     ("qam_set_mfma_min_batch", _I, [_I]),
-    ("qam_set_b1_mfma", _I, [_I]),
+    ("qam_set_staged_mfma", _I, [_I]),
     ("qam_set_tail_split", _I, [_I, _I]),
     ("qam_set_mfma_tiles_per_request", _I, [_I]),
     ("qam_set_mfma_ksplit", _I, [_I]),

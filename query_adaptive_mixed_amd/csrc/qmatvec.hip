@@ -47,26 +47,53 @@ __device__ __forceinline__ int limb_slot(int g) { return (g & ~15) | ((g & 3) <<
 
 // ------------------------------------------------------------------ per-wave body
 
-// Prefetch ring: two halves of H tiles each, up to sixteen 16-byte loads in
-// flight per lane for one request (eight or fewer when several requests'
-// accumulators take the registers).  The wait before one half is computed always follows
-// the reload of the other half, so it drains exactly the older half.
-template <int NS, int NB>
-struct Ring {
-    static constexpr int raw = (NB == 1 ? 8 : 4) / (NS * NB);
-    static constexpr int H = raw >= 4 ? 4 : (raw >= 2 ? 2 : 1);   // tiles per half
-    static constexpr int PF = 2 * H;                                // tiles per ring
-};
-
-// x is staged in sub-chunks of S tiles: each lane loads G = S / 4 groups of
-// four values per request, issued before the first half ring so that waiting
-// for x never drains weight loads, and the limbs of a sub-chunk take
-// NB * S * 256 bytes of LDS.  S is a multiple of every ring length used with NB.
+// x is staged in sub-chunks of S tiles (the same for both inner products, so
+// that they reach the same integers): each lane loads G = S / 4 groups of four
+// values per request.  S is a multiple of every ring length used with NB.
 template <int NB>
 struct Stage {
-    static constexpr int S = NB == 1 ? 16 : (NB == 2 ? 12 : (NB <= 4 ? 8 : 4));
+    static constexpr int S = NB <= 2 ? 16 : (NB <= 5 ? 8 : 4);
     static constexpr int G = S / 4;
 };
+
+// Prefetch ring: two halves of H tiles each, up to sixteen 16-byte loads in
+// flight per lane (fewer when a dot4 form's per-request accumulators take the
+// registers, or beyond four requests on the matrix cores).  The wait before
+// one half is computed always follows the reload of the other half, so it
+// drains exactly the older half.
+template <int NS, int NB, bool MF>
+struct Ring {
+    static constexpr int raw = MF ? (NB <= 4 ? 8 : 4) / NS : (NB == 1 ? 8 : 4) / (NS * NB);
+    static constexpr int Hr = raw >= 4 ? 4 : (raw >= 2 ? 2 : 1);
+    static constexpr int H = Hr > Stage<NB>::S / 2 ? Stage<NB>::S / 2 : Hr;   // tiles per half
+    static constexpr int PF = 2 * H;                                           // tiles per ring
+};
+
+// Matrix-core limb layout for NB requests: B-operand column 3 r + l holds
+// limb l of request r, in NCG groups of 16 columns.  Per tile and group there
+// is one 16-byte slot per (real column c, lane group k), at 4 c + k, then,
+// when the group has columns past the requests, 4 zero slots that every such
+// column reads.
+template <int NB>
+struct MFLayout {
+    static constexpr int cols = 3 * NB;
+    static constexpr int NCG = (cols + 15) / 16;
+    static constexpr int ncol(int g) { return cols - 16 * g < 16 ? cols - 16 * g : 16; }
+    static constexpr int gslots(int g) { return 4 * (ncol(g) + (ncol(g) < 16 ? 1 : 0)); }
+    static constexpr int goff(int g) { return g == 0 ? 0 : goff(g - 1) + gslots(g - 1); }
+    static constexpr int stride = goff(NCG);                                   // int4 slots per tile
+    static constexpr int zero = goff(NCG - 1) + 4 * ncol(NCG - 1);             // zero slots of the last group
+    static constexpr bool padded = ncol(NCG - 1) < 16;
+};
+
+// int4 of LDS per wave: the larger of the dot4 layout (NB S 16) and the
+// matrix-core one (S x stride, then 3 NB x 64 int32 sums).
+template <int NB>
+constexpr int region_int4() {
+    constexpr int d4 = NB * Stage<NB>::S * 16;
+    constexpr int mf = Stage<NB>::S * MFLayout<NB>::stride + 3 * NB * 16;
+    return d4 > mf ? d4 : mf;
+}
 
 // One tile: four groups of four columns, four rows each, NB requests.
 template <int NS, int NB>
@@ -101,15 +128,22 @@ __device__ __forceinline__ void tile_dots(const u32x4* buf, const int4* __restri
 #undef QAM_GROUP
 }
 
-// One tile on the matrix cores (batch 1): for each 16-row group j, the
-// rebuilt codes of the lane (row 16j + (L & 15), columns 16(L >> 4) + 0..15)
-// are the A operand; bm holds the lane's B operand: limb (L & 15) of the
-// same 16 columns for L & 15 < 3, zero otherwise.  acc[j] gets the 16 x 16
-// int32 product: lane L holds limb column L & 15 of rows 16j + 4(L >> 4) + i.
-template <int NS>
-__device__ __forceinline__ void tile_mfma(const u32x4* buf, const int4* __restrict__ lt, v4i (&acc)[4]) {
-    const int4 b4 = *lt;
-    const v4i bm = v4i{b4.x, b4.y, b4.z, b4.w};
+// One tile on the matrix cores: for each 16-row group j, the rebuilt codes
+// of the lane (row 16j + (L & 15), columns 16(L >> 4) + 0..15) are the A
+// operand; B operand g of the lane is column 16 g + (L & 15) of the limbs
+// (slot bslot[g] of the tile).  acc[g][j] gets the 16 x 16 int32 product:
+// lane L holds column 16 g + (L & 15) of rows 16j + 4(L >> 4) + i.
+template <int NS, int NB>
+__device__ __forceinline__ void tile_mfma(const u32x4* buf, const int4* __restrict__ lt,
+                                          const int (&bslot)[MFLayout<NB>::NCG],
+                                          v4i (&acc)[MFLayout<NB>::NCG][4]) {
+    constexpr int NCG = MFLayout<NB>::NCG;
+    v4i bm[NCG];
+#pragma unroll
+    for (int g = 0; g < NCG; ++g) {
+        const int4 b4 = lt[bslot[g]];
+        bm[g] = v4i{b4.x, b4.y, b4.z, b4.w};
+    }
     uint32_t w[4][NS];
 #pragma unroll
     for (int p = 0; p < NS; ++p) {
@@ -122,7 +156,8 @@ __device__ __forceinline__ void tile_mfma(const u32x4* buf, const int4* __restri
     for (int j = 0; j < 4; ++j) {
         const v4i A = v4i{(int)assemble<NS, 0>(w[j]), (int)assemble<NS, 1>(w[j]), (int)assemble<NS, 2>(w[j]),
                           (int)assemble<NS, 3>(w[j])};
-        acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bm, acc[j], 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < NCG; ++g) acc[g][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bm[g], acc[g][j], 0, 0, 0);
     }
 }
 
@@ -149,9 +184,9 @@ __device__ __forceinline__ void lds_order() {
 // Turn this wave's sub-chunk of x into limb words in LDS (see the file comment).
 // xraw[r][i] holds the x values of group lane + 64 i of request r.
 // Limb layouts: for the dot4 product, group g's limb words as one 16-byte
-// slot (limb_slot); for the matrix-core product (MF, batch 1), per tile 16
-// slots of 16 bytes, slot 4l + k holding limb l of the tile's columns
-// 16k .. 16k + 15 (the B operand of lane 16k + l), slots 12-15 zero.
+// slot (limb_slot); for the matrix-core product (MF), MFLayout: the limb
+// words of request r, limb l and the tile's columns 16k + 4u .. +3 go to word
+// u of slot 4 c + k of the group holding column 3 r + l.
 template <int NB, int G, bool XBF16, bool MF>
 __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngroups, int slots, int L,
                                             int4* __restrict__ lds, int (&exps)[NB], bool (&bad)[NB],
@@ -206,10 +241,13 @@ __device__ __forceinline__ void stage_limbs(const u32x4 (&xraw)[NB][G], int ngro
             }
             const int4 lw = limb_words(w0, w1, w2, w3);
             if constexpr (MF) {
-                int* wl = reinterpret_cast<int*>(lds) + (g >> 4) * 64 + (g & 15);
-                wl[0] = lw.x;
-                wl[16] = lw.y;
-                wl[32] = lw.z;
+                using Y = MFLayout<NB>;
+                // (4 c + k) * 4 + u with k = (g & 15) >> 2, u = g & 3 is 16 c + (g & 15)
+                int* wl = reinterpret_cast<int*>(lds) + (g >> 4) * Y::stride * 4 + (g & 15);
+                const int c0 = 3 * r, c1 = 3 * r + 1, c2 = 3 * r + 2;
+                wl[4 * Y::goff(c0 >> 4) + 16 * (c0 & 15)] = lw.x;
+                wl[4 * Y::goff(c1 >> 4) + 16 * (c1 & 15)] = lw.y;
+                wl[4 * Y::goff(c2 >> 4) + 16 * (c2 & 15)] = lw.z;
             } else {
                 lds[r * slots + limb_slot(g)] = lw;
             }
@@ -289,9 +327,10 @@ __device__ __forceinline__ void finish_zero(const Item& a, int b, int L) {
 template <int NS, int NB, bool XBF16, bool MF, bool EPI>
 __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* __restrict__ lds, int b, int chunk,
                                           int L, int ks, int KS, double* red) {
-    static_assert(!MF || NB == 1, "the matrix-core inner product serves batch 1");
-    constexpr int H = Ring<NS, NB>::H;
-    constexpr int PF = Ring<NS, NB>::PF;
+    constexpr int H = Ring<NS, NB, MF>::H;
+    constexpr int PF = Ring<NS, NB, MF>::PF;
+    using Y = MFLayout<NB>;
+    constexpr int NCG = Y::NCG;
     constexpr int S = Stage<NB>::S;
     constexpr int G = Stage<NB>::G;
     const int B = c.B;
@@ -305,14 +344,18 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     const int slots = S * 16;
     const int64_t pb = a.plane_bytes;
 
-    // MF: this lane's B-operand slot, and the zero slots 12-15 of every tile
-    // (written once; staging never touches them)
-    int kslot = 0;
-    if constexpr (MF) {
-        kslot = (L & 15) < kLimbs ? (L & 15) * 4 + kg : 12 + kg;
-        lds[(L >> 2) * 16 + 12 + (L & 3)] = int4{0, 0, 0, 0};
+    // MF: this lane's B-operand slot per column group, and the zero slots of
+    // every tile (written once; staging never touches them)
+    int bslot[NCG];
+#pragma unroll
+    for (int g = 0; g < NCG; ++g) {
+        const int cc = L & 15;
+        bslot[g] = Y::goff(g) + 4 * (cc < Y::ncol(g) ? cc : Y::ncol(g)) + kg;
     }
-    int* tab = reinterpret_cast<int*>(lds + S * 16);   // MF: [3 limbs][64 rows] sums of a sub-chunk
+    if constexpr (MF && Y::padded) {
+        if ((L >> 2) < S) lds[(L >> 2) * Y::stride + Y::zero + (L & 3)] = int4{0, 0, 0, 0};
+    }
+    int* tab = reinterpret_cast<int*>(lds + S * Y::stride);   // MF: [3 NB][64 rows] sums of a sub-chunk
 
     double mine[NB];
     bool any_bad[NB];
@@ -346,7 +389,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
         stage_limbs<NB, G, XBF16, MF>(xraw, min(S, ntile - sub * S) * 16, slots, L, lds, exps, bad, want_ssq, ssq);
     };
     int acc[NB][4][kLimbs];
-    v4i macc[4];
+    v4i macc[NCG][4];
     auto clear_acc = [&]() {
 #pragma unroll
         for (int r = 0; r < NB; ++r)
@@ -355,7 +398,9 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
 #pragma unroll
                 for (int l = 0; l < kLimbs; ++l) acc[r][j][l] = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) macc[j] = v4i{0, 0, 0, 0};
+        for (int g = 0; g < NCG; ++g)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) macc[g][j] = v4i{0, 0, 0, 0};
     };
     // The sub-chunk's exact per-row integers, scaled by its exponent into the
     // row's fp64 sum.  dot4: summed over the four lane groups sharing a row;
@@ -363,14 +408,22 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     // integer on lane L (the same value either way).
     auto flush = [&]() {
         if constexpr (MF) {
-            if ((L & 15) < kLimbs) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(tab + (L & 15) * 64 + 16 * j + 4 * kg) = macc[j];
+            for (int g = 0; g < NCG; ++g) {
+                const int gc = 16 * g + (L & 15);
+                if (gc < 3 * NB) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(tab + gc * 64 + 16 * j + 4 * kg) = macc[g][j];
+                }
             }
             lds_order();
-            const double d = (double)tab[128 + L] * 65536.0 + (double)tab[64 + L] * 256.0 + (double)tab[L];
-            mine[0] += ldexp(d, exps[0] - kFrac);
-            any_bad[0] = any_bad[0] || bad[0];
+#pragma unroll
+            for (int r = 0; r < NB; ++r) {
+                const double d = (double)tab[(3 * r + 2) * 64 + L] * 65536.0 + (double)tab[(3 * r + 1) * 64 + L] * 256.0 +
+                                 (double)tab[3 * r * 64 + L];
+                mine[r] += ldexp(d, exps[r] - kFrac);
+                any_bad[r] = any_bad[r] || bad[r];
+            }
         } else {
 #pragma unroll
             for (int r = 0; r < NB; ++r) {
@@ -389,7 +442,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     };
 #define QAM_TILE(BUF, TT)                                                   \
     do {                                                                    \
-        if constexpr (MF) tile_mfma<NS>(BUF, lds + (TT) * 16 + kslot, macc); \
+        if constexpr (MF) tile_mfma<NS, NB>(BUF, lds + (TT) * Y::stride, bslot, macc); \
         else tile_dots<NS, NB>(BUF, lds + (TT) * 16 + kg, slots, acc);     \
     } while (0)
 
@@ -520,7 +573,7 @@ __device__ __forceinline__ void run_unit(const Item& a, const Common& c, int loc
     // handed to wave 0
     const int KS = MAXW == 1 ? 1 : c.KS;
     const int ks = MAXW == 1 ? 0 : tid >> 6;
-    const int region = NB * Stage<NB>::S * 16 + (NB == 1 ? 48 : 0);   // int4 per wave
+    const int region = region_int4<NB>();   // int4 per wave
     int4* mylds = lds + ks * region;
     double* red = reinterpret_cast<double*>(lds + KS * region);
     const int chunk = local % a.n_chunks;
@@ -574,15 +627,27 @@ __global__ __launch_bounds__(64 * MAXW) void qmatvec_kernel(Item single, Common 
 static int64_t g_target_waves = 256 * 32;   // wavefronts aimed for per launch
 static int64_t g_max_chunk_tiles = 64;       // longest column chunk of the batch-1 launches
 
-// every chunk holds a whole number of prefetch rings (Ring<NS, B>::PF for every NS)
-int tpc_align_for(int64_t B) { return B == 1 ? 8 : (B == 2 ? 4 : 2); }
-int stage_tiles_for(int64_t B) { return B == 1 ? 16 : (B == 2 ? 12 : (B <= 4 ? 8 : 4)); }
+// every chunk holds a whole number of prefetch rings (Ring<NS, B, MF>::PF for every NS and form)
+int tpc_align_for(int64_t B) { return B <= 4 ? 8 : 4; }
+int stage_tiles_for(int64_t B) { return B <= 2 ? 16 : (B <= 5 ? 8 : 4); }
 size_t lds_bytes_for(int64_t B) {
-    return ((size_t)B * stage_tiles_for(B) * 16 + (B == 1 ? 48 : 0)) * sizeof(int4);
+    int r = 0;
+    switch (B) {
+        case 1: r = region_int4<1>(); break;
+        case 2: r = region_int4<2>(); break;
+        case 3: r = region_int4<3>(); break;
+        case 4: r = region_int4<4>(); break;
+        case 5: r = region_int4<5>(); break;
+        case 6: r = region_int4<6>(); break;
+        case 7: r = region_int4<7>(); break;
+        default: r = region_int4<8>(); break;
+    }
+    return (size_t)r * sizeof(int4);
 }
 
-// Batch 1 inner product: 1 = matrix cores, 0 = dot4 on the vector ALUs.
-static int g_b1_mfma = 1;
+// Inner product of the staged-limb route: 1 = matrix cores, 0 = dot4 on the
+// vector ALUs (the same integers, so the same bits).
+static int g_staged_mfma = 1;
 
 // Column chunk length (in tiles) for a launch covering `block_tiles` block x
 // tile pairs: enough chunks for about g_target_waves wavefronts of equal work.
@@ -624,13 +689,8 @@ static void launch_k(const Item& it, const Common& c, int64_t grid, int threads,
 
 template <int NB, bool GROUPED>
 static void launch_nb(const Item& it, const Common& c, int64_t grid, size_t lds, hipStream_t s) {
-    if constexpr (NB == 1) {
-        if (g_b1_mfma) {
-            launch_k<1, GROUPED, 1, true>(it, c, grid, 64, lds, s);
-            return;
-        }
-    }
-    launch_k<NB, GROUPED, 1, false>(it, c, grid, 64, lds, s);
+    if (g_staged_mfma) launch_k<NB, GROUPED, 1, true>(it, c, grid, 64, lds, s);
+    else launch_k<NB, GROUPED, 1, false>(it, c, grid, 64, lds, s);
 }
 
 template <bool GROUPED>
@@ -650,7 +710,7 @@ static void launch(int64_t B, const Item& it, const Common& c, int64_t grid, siz
 void launch_single(int64_t B, const Item& it, const Common& c, int64_t grid, hipStream_t s) {
     if (B == 1 && c.KS > 1) {   // several waves per (block, chunk): batch 1 only
         const size_t lds = (size_t)c.KS * lds_bytes_for(1) + (size_t)c.KS * 2 * 64 * sizeof(double);
-        if (g_b1_mfma)
+        if (g_staged_mfma)
             launch_k<1, false, 8, true>(it, c, grid, 64 * c.KS, lds, s);
         else
             launch_k<1, false, 8, false>(it, c, grid, 64 * c.KS, lds, s);
@@ -725,12 +785,12 @@ extern "C" int qam_set_max_chunk_tiles(int t) {
     return QAM_OK;
 }
 
-static const char* b1_route_name(int64_t B) { return B == 1 && g_b1_mfma ? "qmatvec_mfma1" : "qmatvec_dot4"; }
+static const char* staged_name() { return g_staged_mfma ? "qmatvec_staged_mfma" : "qmatvec_staged_dot4"; }
 
-extern "C" int qam_set_b1_mfma(int on) {
+extern "C" int qam_set_staged_mfma(int on) {
     clear_error();
-    if (on != 0 && on != 1) QAM_FAIL(QAM_ERR_ARG, "set_b1_mfma: %d is not 0 or 1", on);
-    g_b1_mfma = on;
+    if (on != 0 && on != 1) QAM_FAIL(QAM_ERR_ARG, "set_staged_mfma: %d is not 0 or 1", on);
+    g_staged_mfma = on;
     return QAM_OK;
 }
 
@@ -782,13 +842,15 @@ extern "C" int qam_qmatvec_ep(const void* x, int x_dtype, int64_t B, const qam_p
     launch_single(B, it, c, grid, s);
     QAM_HIP_CHECK(hipGetLastError());
     char v[128];
-    snprintf(v, sizeof(v), "%s B=%lld tpc=%d chunks=%d", b1_route_name(B), (long long)B, p.tpc, p.n_chunks);
+    snprintf(v, sizeof(v), "%s B=%lld tpc=%d chunks=%d", staged_name(), (long long)B, p.tpc, p.n_chunks);
     set_variant(v);
     return QAM_OK;
 }
 
-// Smallest batch with a shared map that takes the pre-pass route.
-static int g_mfma_min_batch = 2;
+// Smallest batch with a shared map that takes the pre-pass route (below it,
+// staging the limbs in every row block's wave costs less than the pre-pass
+// launch and the limb loads; from 3 requests on it costs more).
+static int g_mfma_min_batch = 3;
 
 bool qam::mfma_route(int64_t B, int per_request_maps) {
     return (per_request_maps && B > 1) || B > QAM_MAX_BATCH || B >= g_mfma_min_batch;
@@ -948,8 +1010,8 @@ extern "C" int qam_qmatvec_group(const qam_group* group, hipStream_t s) {
     Item none{};
     launch<true>(group->B, none, c, group->n_workgroups, group->lds_bytes, s);
     QAM_HIP_CHECK(hipGetLastError());
-    snprintf(v, sizeof(v), "%s_group items=%d B=%lld wg=%lld", b1_route_name(group->B), group->n_items,
-             (long long)group->B, (long long)group->n_workgroups);
+    snprintf(v, sizeof(v), "%s_group items=%d B=%lld wg=%lld", staged_name(), group->n_items, (long long)group->B,
+             (long long)group->n_workgroups);
     set_variant(v);
     return QAM_OK;
 }

@@ -200,7 +200,7 @@ def test_qmatvec_single_layer_workload_all_maps_sampled(qam):
         check_y(y, W, sc, x, mp, str(mp))
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 8])
+@pytest.mark.parametrize("B", [1, 2, 3, 5, 6, 8])
 @pytest.mark.parametrize("K", [256, 512, 1536, 2048, 8960])
 @pytest.mark.parametrize("N", [128, 512, 2048])
 def test_qmatvec_shape_battery(qam, N, K, B):
@@ -213,26 +213,25 @@ def test_qmatvec_shape_battery(qam, N, K, B):
     y = host(qam.qmatvec(dev(x), pm, dev(lv)))
     check_y(y, W, sc, x, lv, (N, K, B))
     from query_adaptive_mixed_amd import _lib as L
+    # the staged-limb route (batch 1 by default; every batch up to 8 once the
+    # pre-pass threshold is raised): matrix cores, then its dot4 form, which
+    # reaches the same integers, so the same bits
+    assert L.lib().qam_set_mfma_min_batch(9) == 0
+    try:
+        ys = host(qam.qmatvec(dev(x), pm, dev(lv)))
+        assert "staged_mfma" in qam.last_variant()
+        assert L.lib().qam_set_staged_mfma(0) == 0
+        try:
+            yd = host(qam.qmatvec(dev(x), pm, dev(lv)))
+            assert "staged_dot4" in qam.last_variant()
+        finally:
+            assert L.lib().qam_set_staged_mfma(1) == 0
+    finally:
+        assert L.lib().qam_set_mfma_min_batch(3) == 0
+    check_y(ys, W, sc, x, lv, ("staged", N, K, B))
+    assert np.array_equal(yd.view(np.uint32), ys.view(np.uint32)), (N, K, B)
     if B == 1:
-        # batch 1 runs on the matrix cores; the dot4 form of the same kernel
-        # reaches the same integers, so the same bits
-        assert "mfma1" in qam.last_variant()
-        assert L.lib().qam_set_b1_mfma(0) == 0
-        try:
-            y2 = host(qam.qmatvec(dev(x), pm, dev(lv)))
-            assert "dot4" in qam.last_variant()
-        finally:
-            assert L.lib().qam_set_b1_mfma(1) == 0
-        assert np.array_equal(y2.view(np.uint32), y.view(np.uint32)), (N, K)
-    if B > 1:
-        # the same batch on the staged-limb route's dot4 form (the pre-pass route takes it by default)
-        assert L.lib().qam_set_mfma_min_batch(9) == 0
-        try:
-            y = host(qam.qmatvec(dev(x), pm, dev(lv)))
-            assert "dot4" in qam.last_variant()
-        finally:
-            assert L.lib().qam_set_mfma_min_batch(2) == 0
-        check_y(y, W, sc, x, lv, ("dot4", N, K, B))
+        assert np.array_equal(ys.view(np.uint32), y.view(np.uint32)), (N, K)
 
 
 def test_qmatvec_exact_integer_cases(qam):

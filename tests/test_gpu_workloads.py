@@ -76,7 +76,7 @@ def test_e2b_field_grouped_launch(qam):
     items = field_items(qam, fld, lv_dev, 1)
     grp = qam.GroupedQmatvec(items)
     grp.run()
-    assert "mfma1_group" in qam.last_variant()
+    assert "staged_mfma_group" in qam.last_variant()
     rng = np.random.default_rng(11)
     offs = fld.block_offsets()
     ys = []
@@ -88,13 +88,13 @@ def test_e2b_field_grouped_launch(qam):
                      m.name)
     # the dot4 form of the batch-1 kernel gives the same bits on every row
     from query_adaptive_mixed_amd import _lib as L
-    assert L.lib().qam_set_b1_mfma(0) == 0
+    assert L.lib().qam_set_staged_mfma(0) == 0
     try:
         grp = qam.GroupedQmatvec(items)
         grp.run()
-        assert "dot4_group" in qam.last_variant()
+        assert "staged_dot4_group" in qam.last_variant()
     finally:
-        assert L.lib().qam_set_b1_mfma(1) == 0
+        assert L.lib().qam_set_staged_mfma(1) == 0
     for i, m in enumerate(fld.matrices):
         assert np.array_equal(host(items[i][2]).view(np.uint32), ys[i].view(np.uint32)), m.name
 
@@ -120,7 +120,7 @@ def test_streaming_stack_grouped_launch(qam, B):
         items.append((pm, x, y, lv_dev[offs[i]:offs[i] + m.n_blocks]))
     grp = qam.GroupedQmatvec(items)
     grp.run()
-    assert ("mfma1_group" if B == 1 else "mfma_group") in qam.last_variant()
+    assert ("staged_mfma_group" if B == 1 else "qmatvec_mfma_group") in qam.last_variant()
     for i, m in enumerate(fld.matrices):
         blocks = np.sort(rng.choice(m.n_blocks, 3, replace=False))
         check_blocks(host(items[i][2]), fld.codes(i), fld.scales(i), fld.x(i, B),
