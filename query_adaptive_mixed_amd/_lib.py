@@ -108,6 +108,7 @@ EXTRA_SIGNATURES = [
     ("qam_set_mfma_target_waves", _I, [_I]),
     ("qam_set_mfma_min_batch", _I, [_I]),
     ("qam_set_staged_mfma", _I, [_I]),
+    ("qam_group_launch_times", _I, [C.POINTER(QamGroup), _I, _P, _P]),
     ("qam_set_tail_split", _I, [_I, _I]),
     ("qam_set_mfma_tiles_per_request", _I, [_I]),
     ("qam_set_mfma_ksplit", _I, [_I]),

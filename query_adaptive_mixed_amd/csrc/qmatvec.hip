@@ -30,6 +30,8 @@
 // The same kernel serves one matrix (descriptor passed by value) and a group
 // of matrices with independent inputs (descriptor table in device memory,
 // one table lookup per workgroup), so a whole weight field is one launch.
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <vector>
 
@@ -677,33 +679,46 @@ Plan make_plan(int64_t N, int64_t K, int64_t B, int goal, int align) {
     return p;
 }
 
+// With events, the launch records them at the kernel's own start and end
+// (hipExtLaunchKernel), which times the kernel alone.
 template <int NB, bool GROUPED, int MAXW, bool MF>
-static void launch_k(const Item& it, const Common& c, int64_t grid, int threads, size_t lds, hipStream_t s) {
+static void launch_k(const Item& it, const Common& c, int64_t grid, int threads, size_t lds, hipStream_t s,
+                     hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+    const dim3 g((unsigned)grid), b((unsigned)threads);
+    if (e0 || e1) {
+        if (c.x_bf16)
+            hipExtLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, true, MAXW, MF>), g, b, (uint32_t)lds, s, e0, e1, 0u,
+                                  it, c);
+        else
+            hipExtLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, false, MAXW, MF>), g, b, (uint32_t)lds, s, e0, e1, 0u,
+                                  it, c);
+        return;
+    }
     if (c.x_bf16)
-        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, true, MAXW, MF>), dim3((unsigned)grid), dim3(threads), lds, s,
-                           it, c);
+        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, true, MAXW, MF>), g, b, lds, s, it, c);
     else
-        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, false, MAXW, MF>), dim3((unsigned)grid), dim3(threads), lds, s,
-                           it, c);
+        hipLaunchKernelGGL((qmatvec_kernel<NB, GROUPED, false, MAXW, MF>), g, b, lds, s, it, c);
 }
 
 template <int NB, bool GROUPED>
-static void launch_nb(const Item& it, const Common& c, int64_t grid, size_t lds, hipStream_t s) {
-    if (g_staged_mfma) launch_k<NB, GROUPED, 1, true>(it, c, grid, 64, lds, s);
-    else launch_k<NB, GROUPED, 1, false>(it, c, grid, 64, lds, s);
+static void launch_nb(const Item& it, const Common& c, int64_t grid, size_t lds, hipStream_t s, hipEvent_t e0,
+                      hipEvent_t e1) {
+    if (g_staged_mfma) launch_k<NB, GROUPED, 1, true>(it, c, grid, 64, lds, s, e0, e1);
+    else launch_k<NB, GROUPED, 1, false>(it, c, grid, 64, lds, s, e0, e1);
 }
 
 template <bool GROUPED>
-static void launch(int64_t B, const Item& it, const Common& c, int64_t grid, size_t lds, hipStream_t s) {
+static void launch(int64_t B, const Item& it, const Common& c, int64_t grid, size_t lds, hipStream_t s,
+                   hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
     switch (B) {
-        case 1: launch_nb<1, GROUPED>(it, c, grid, lds, s); break;
-        case 2: launch_nb<2, GROUPED>(it, c, grid, lds, s); break;
-        case 3: launch_nb<3, GROUPED>(it, c, grid, lds, s); break;
-        case 4: launch_nb<4, GROUPED>(it, c, grid, lds, s); break;
-        case 5: launch_nb<5, GROUPED>(it, c, grid, lds, s); break;
-        case 6: launch_nb<6, GROUPED>(it, c, grid, lds, s); break;
-        case 7: launch_nb<7, GROUPED>(it, c, grid, lds, s); break;
-        default: launch_nb<8, GROUPED>(it, c, grid, lds, s); break;
+        case 1: launch_nb<1, GROUPED>(it, c, grid, lds, s, e0, e1); break;
+        case 2: launch_nb<2, GROUPED>(it, c, grid, lds, s, e0, e1); break;
+        case 3: launch_nb<3, GROUPED>(it, c, grid, lds, s, e0, e1); break;
+        case 4: launch_nb<4, GROUPED>(it, c, grid, lds, s, e0, e1); break;
+        case 5: launch_nb<5, GROUPED>(it, c, grid, lds, s, e0, e1); break;
+        case 6: launch_nb<6, GROUPED>(it, c, grid, lds, s, e0, e1); break;
+        case 7: launch_nb<7, GROUPED>(it, c, grid, lds, s, e0, e1); break;
+        default: launch_nb<8, GROUPED>(it, c, grid, lds, s, e0, e1); break;
     }
 }
 
@@ -987,6 +1002,37 @@ extern "C" int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B
     group_out->per_request_maps = 0;
     group_out->n_pre_workgroups = 0;
     group_out->pre_map = nullptr;
+    return QAM_OK;
+}
+
+// Benchmark hook: runs a staged-limb group `n` times back to back on `s`,
+// timing each launch with HIP events recorded at the kernel's own start and
+// end; writes the n durations (ms) and synchronises `s`.
+extern "C" int qam_group_launch_times(const qam_group* group, int n, float* ms_out, hipStream_t s) {
+    clear_error();
+    if (!group || !group->table || !group->wg_map || !ms_out) QAM_FAIL(QAM_ERR_NULL, "group_launch_times: null pointer");
+    if (group->route != 0 || group->B < 1 || group->B > QAM_MAX_BATCH || group->n_workgroups < 1)
+        QAM_FAIL(QAM_ERR_ARG, "group_launch_times: only staged-limb groups are timed here");
+    if (n < 1 || n > 4096) QAM_FAIL(QAM_ERR_ARG, "group_launch_times: n=%d outside [1, 4096]", n);
+    Common c{};
+    c.items = static_cast<const Item*>(group->table);
+    c.wg_item = static_cast<const int*>(group->wg_map);
+    c.B = (int)group->B;
+    c.x_bf16 = group->x_dtype == QAM_X_BF16;
+    c.KS = 1;
+    Item none{};
+    std::vector<hipEvent_t> ev((size_t)2 * n, nullptr);
+    hipError_t e = hipSuccess;
+    for (size_t i = 0; i < ev.size() && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+    for (int i = 0; i < n && e == hipSuccess; ++i) {
+        launch<true>(group->B, none, c, group->n_workgroups, group->lds_bytes, s, ev[2 * i], ev[2 * i + 1]);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    for (int i = 0; i < n && e == hipSuccess; ++i) e = hipEventElapsedTime(&ms_out[i], ev[2 * i], ev[2 * i + 1]);
+    for (hipEvent_t x : ev)
+        if (x) (void)hipEventDestroy(x);
+    if (e != hipSuccess) QAM_FAIL(QAM_ERR_HIP, "group_launch_times: %s", hipGetErrorString(e));
     return QAM_OK;
 }
 
