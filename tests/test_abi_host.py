@@ -286,3 +286,20 @@ def test_build_level_maps_rejects(lib):
     lenses[5].r = -1.0
     assert lib.qam_build_level_maps(FAKE, 8, lenses, n_lenses, params, lad, 5, 1, 3, FAKE, None) == -3
     assert lib.qam_build_level_maps(FAKE, 8, lenses, 65, params, lad, 5, 1, 3, FAKE, None) == -3
+
+
+def test_group_calls_reject_bad_descriptors_before_any_launch(lib):
+    assert lib.qam_qmatvec_group(None, None) == -1
+    g = L.QamGroup()          # zeroed: no table, no map
+    assert lib.qam_qmatvec_group(C.byref(g), None) == -1
+    out = (C.c_float * 4)()
+    assert lib.qam_group_launch_times(None, 4, C.cast(out, C.c_void_p), None) == -1
+    assert lib.qam_group_launch_times(C.byref(g), 4, C.cast(out, C.c_void_p), None) == -1
+    g.table, g.wg_map, g.n_workgroups, g.B = 0x10000000, 0x10001000, 8, 1
+    g.route = 1               # the timing hook serves staged-limb groups only
+    assert lib.qam_group_launch_times(C.byref(g), 4, C.cast(out, C.c_void_p), None) == -3
+    g.route = 0
+    assert lib.qam_group_launch_times(C.byref(g), 0, C.cast(out, C.c_void_p), None) == -3
+    assert lib.qam_group_launch_times(C.byref(g), 4, None, None) == -1
+    g.B = 9                   # beyond the staged-limb route
+    assert lib.qam_qmatvec_group(C.byref(g), None) == -3
