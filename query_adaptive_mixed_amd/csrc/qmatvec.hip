@@ -1,4 +1,5 @@
-// Mixed-depth matrix-vector / small-batch product over the slice planes.
+// Mixed-depth matrix-vector / small-batch product over the slice planes
+// (the staged-limb route: up to 8 requests sharing one level map).
 //
 // Each block of 64 output rows is read at its own depth straight from the
 // stored bytes inside the pass ("FoQLens", table "Progress"); a block read at
@@ -8,28 +9,28 @@
 // Work decomposition.  A workgroup is one wavefront (or, for batch 1, up to
 // eight splitting a chunk's tiles) and takes one block of 64 rows and one
 // chunk of columns (tiles_per_chunk tiles of 64).  The wave walks its chunk in
-// sub-chunks of at most 16 tiles: it loads the sub-chunk's x and the first half
-// of its weight-prefetch ring, then turns that x into an exact fixed-point
-// form in LDS:
+// sub-chunks of 16, 8 or 4 tiles (by batch); the ring of weight loads runs
+// through the whole chunk, and each sub-chunk's x is turned into an exact
+// fixed-point form in LDS:
 //     v_k = rint(x_k * 2^(22-e)),   2^(e-1) <= max_sub-chunk |x| < 2^e,
 // held as three signed int8 limbs v_k = sum_l s_l 256^l (balanced digits).
 // Each lane owns, per 64-column tile and per slice, one 16-byte word group
 // covering 4 rows x 16 columns; codes are rebuilt in registers (one mask per
 // slice and one rotate per four codes) and multiplied into the limbs exactly,
-// in int32: with v_dot4_i32_i8 on the vector ALUs (every batch up to 8), or,
-// at batch 1, with v_mfma_i32_16x16x64_i8 on the matrix cores, the rebuilt
-// words being the A operand as they stand and the three limbs columns 0-2 of
-// the B operand (columns 3-15 zero).  The limb sums are combined into an
-// exact integer per row and sub-chunk, scaled by 2^(e-22) into an fp64 row
+// in int32, with v_mfma_i32_16x16x64_i8 on the matrix cores: the rebuilt
+// words are the A operand as they stand, and B-operand column 3 r + l holds
+// limb l of request r (the dot4 form, v_dot4_i32_i8 on the vector ALUs,
+// reaches the same integers).  The limb sums are combined into an exact
+// integer per row, request and sub-chunk, scaled by 2^(e-22) into an fp64 row
 // sum, and either written as the output (one chunk) or stored as a partial;
 // the last wavefront of a block to finish sums the partials in chunk order and
-// writes y = fl32(scale * sum).  Both inner products give the same integers,
-// so the two batch-1 forms give the same bits.  No floating-point atomics:
-// results are bit-reproducible.
+// writes y = fl32(scale * sum).  No floating-point atomics: results are
+// bit-reproducible, and the two inner products give the same bits.
 //
-// The same kernel serves one matrix (descriptor passed by value) and a group
-// of matrices with independent inputs (descriptor table in device memory,
-// one table lookup per workgroup), so a whole weight field is one launch.
+// The same kernel serves one matrix (descriptor passed by value, with its
+// fused epilogue) and a group of matrices with independent inputs (descriptor
+// table in device memory, one table lookup per workgroup), so a whole weight
+// field is one launch.
 #include <hip/hip_ext.h>
 
 #include <algorithm>
@@ -570,7 +571,8 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
 // tiles k, k + KS, ...
 template <int NB, bool XBF16, int MAXW, bool MF, bool EPI>
 __device__ __forceinline__ void run_unit(const Item& a, const Common& c, int local, int4* lds, int tid) {
-    // per wave: [NB][S * 16] limb words of its sub-chunk (batch 1: then 3 x 64
+    // per wave: region_int4<NB>() int4 (the sub-chunk's limb words in the
+    // layout of the inner product in use; for the matrix cores then 3 NB x 64
     // int32 sums); then, with several waves, [KS][NB][2][64] fp64 row sums
     // handed to wave 0
     const int KS = MAXW == 1 ? 1 : c.KS;
@@ -627,7 +629,7 @@ __global__ __launch_bounds__(64 * MAXW) void qmatvec_kernel(Item single, Common 
 // ------------------------------------------------------------------ host side
 
 static int64_t g_target_waves = 256 * 32;   // wavefronts aimed for per launch
-static int64_t g_max_chunk_tiles = 64;       // longest column chunk of the batch-1 launches
+static int64_t g_max_chunk_tiles = 64;       // longest column chunk of the staged-limb launches
 
 // every chunk holds a whole number of prefetch rings (Ring<NS, B, MF>::PF for every NS and form)
 int tpc_align_for(int64_t B) { return B <= 4 ? 8 : 4; }
