@@ -1,4 +1,4 @@
-// Level map from the lens rules: one thread per block, fp64.
+// Level map from the lens rules: a group of lanes per block (one per lens), fp64.
 //
 // Rules 1-6 of the FoQLens landing page (vovanda.github.io/FoQLens), section
 // "The mechanism", which repeat the rule list of "FoQZones, the mechanism" on
@@ -29,77 +29,74 @@ namespace qam {
 
 constexpr int kMapsPerLaunch = 8;
 
-// One map's rule parameters (its lenses are [first, first + n_lenses) of the
-// launch's lens table).
+// One map's rules as the kernel takes them: rules 1-3 are per map and per
+// lens, not per block, so the host evaluates them (the same IEEE operations
+// in the same order, hence the same values) and the kernel runs rules 4-6.
 struct MapParams {
-    double stops[QAM_MAX_STOPS];
-    double f, g;
+    double stops[QAM_MAX_STOPS];   // rule 3: s_(gamma+1) > ... > s_kappa, n of them
+    int n;                         // kappa - gamma (0: every block at the glass)
     int combine;
-    int n_stops;     // 0: default spacing
-    int first;
+    int first;                     // the map's lenses: [first, first + n_lenses)
     int n_lenses;
 };
 
 struct LensArgs {
     double cx[QAM_MAX_LENSES];
     double cy[QAM_MAX_LENSES];
-    double r[QAM_MAX_LENSES];
+    double R[QAM_MAX_LENSES];      // rule 1: R_i, +inf at f = 1
     MapParams maps[kMapsPerLaunch];
-    int n_rungs;
     int glass;
-    int64_t out_stride;   // bytes between the maps of one launch
+    int lanes_log2;                // log2 of the lanes per block: >= log2(n_lenses), <= 6
+    int64_t out_stride;            // bytes between the maps of one launch
 };
 
-// grid.y = map of the launch; one thread per block of that map.
+// grid.y = map of the launch.  Each block is taken by a group of 2^lanes_log2
+// lanes of one wavefront, lane j of the group computing lens j's lift (rule
+// 4); the lifts are then combined in lens order (rule 5) through lane
+// shuffles, so the sum is the same left-to-right fp64 sum as one thread
+// walking the lenses, and the group's first lane writes the level (rule 6).
 __global__ __launch_bounds__(256) void levelmap_kernel(const double* __restrict__ coords, int64_t n_blocks,
                                                        LensArgs a, uint8_t* __restrict__ out) {
-    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= n_blocks) return;
     const MapParams& p = a.maps[blockIdx.y];
     uint8_t* o = out + (int64_t)blockIdx.y * a.out_stride;
-    const int m = a.n_rungs - 1;
-    // rule 2: ceiling
-    const int kappa = a.glass + (int)floor(p.g * (double)(m - a.glass));
-    const int n = kappa - a.glass;
-    if (n <= 0 || p.n_lenses == 0) {
-        o[b] = (uint8_t)a.glass;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t b_raw = t >> a.lanes_log2;
+    const int j = (int)(t & ((1 << a.lanes_log2) - 1));
+    const bool live = b_raw < n_blocks;
+    const int64_t b = live ? b_raw : n_blocks - 1;   // past the end: a valid block, nothing written
+    if (p.n <= 0 || p.n_lenses == 0) {               // uniform over the launch's map
+        if (live && j == 0) o[b] = (uint8_t)a.glass;
         return;
     }
-    // rule 3: stops, s[j-1] = s_(gamma+j)
-    double s[QAM_MAX_STOPS];
-#pragma unroll
-    for (int j = 0; j < QAM_MAX_STOPS; ++j) {
-        if (p.n_stops) s[j] = p.stops[j];
-        else s[j] = (double)(n - j) / (double)n;
-    }
-    const double s_last = s[0];
-    const double bx = coords[2 * b];
-    const double by = coords[2 * b + 1];
-    double acc = 0.0;
-    for (int i = p.first; i < p.first + p.n_lenses; ++i) {
-        // rule 1: radius
-        const double R = (p.f == 1.0) ? INFINITY : (a.r[i] * p.f) / (1.0 - p.f);
-        // rule 4: distance in radii, then the lift
-        const double dx = bx - a.cx[i];
-        const double dy = by - a.cy[i];
+    const double s_last = p.stops[0];
+    double lift = 0.0;
+    if (j < p.n_lenses) {
+        const int i = p.first + j;
+        const double dx = coords[2 * b] - a.cx[i];
+        const double dy = coords[2 * b + 1] - a.cy[i];
         const double dist = sqrt(dx * dx + dy * dy);
+        const double R = a.R[i];
         double rho;
         if (R == 0.0) rho = (dist == 0.0) ? 0.0 : INFINITY;
         else rho = dist / R;
-        const double t = 1.0 - rho / s_last;
-        const double lift = t > 0.0 ? t : 0.0;
-        // rule 5: combine (sum in lens order, or max)
-        if (p.combine == QAM_COMBINE_SUM) acc = acc + lift;
-        else acc = acc > lift ? acc : lift;
+        const double tt = 1.0 - rho / s_last;
+        lift = tt > 0.0 ? tt : 0.0;
+    }
+    // rule 5 in lens order: lane base + k holds lens k of this block
+    const int base = (int)(threadIdx.x & 63) & ~((1 << a.lanes_log2) - 1);
+    double acc = 0.0;
+    for (int k = 0; k < p.n_lenses; ++k) {
+        const double v = __shfl(lift, base + k, 64);
+        if (p.combine == QAM_COMBINE_SUM) acc = acc + v;
+        else acc = acc > v ? acc : v;
     }
     const double L = (p.combine == QAM_COMBINE_SUM) ? (acc < 1.0 ? acc : 1.0) : acc;
     // rule 6: the ring rho* falls into
     const double rho_star = s_last * (1.0 - L);
     int count = 0;
-#pragma unroll
-    for (int j = 0; j < QAM_MAX_STOPS; ++j)
-        if (j < n && rho_star < s[j]) ++count;
-    o[b] = (uint8_t)(a.glass + count);
+    for (int k = 0; k < p.n; ++k)
+        if (rho_star < p.stops[k]) ++count;
+    if (live && j == 0) o[b] = (uint8_t)(a.glass + count);
 }
 
 // Host checks of one map's parameters and lenses (error text names `who`).
@@ -117,6 +114,7 @@ static int check_map(const qam_lens* lenses, int n_lenses, const qam_lens_params
     const int kappa = glass + (int)floor(g * (double)(m - glass));
     const int n = kappa - glass;
     mp = MapParams{};
+    mp.n = n;
     if (params->n_stops != 0) {
         if (params->n_stops != n)
             QAM_FAIL(QAM_ERR_ARG, "%s: %d stops given, kappa - glass = %d", who, params->n_stops, n);
@@ -127,16 +125,32 @@ static int check_map(const qam_lens* lenses, int n_lenses, const qam_lens_params
                 QAM_FAIL(QAM_ERR_ARG, "%s: stops not strictly decreasing", who);
             mp.stops[j] = params->stops[j];
         }
+    } else {
+        for (int j = 0; j < n; ++j) mp.stops[j] = (double)(n - j) / (double)n;   // default spacing
     }
     for (int i = 0; i < n_lenses; ++i)
         if (!isfinite(lenses[i].cx) || !isfinite(lenses[i].cy) || !(lenses[i].r >= 0.0) || !isfinite(lenses[i].r))
             QAM_FAIL(QAM_ERR_ARG, "%s: lens %d has a non-finite centre or a bad size", who, i);
-    mp.f = f;
-    mp.g = g;
     mp.combine = params->combine;
-    mp.n_stops = params->n_stops;
     mp.n_lenses = n_lenses;
     return QAM_OK;
+}
+
+// Rule 1 for one lens, as the oracle and the pages write it: (r f) / (1 - f).
+static double lens_R(double r, double f) { return f == 1.0 ? INFINITY : (r * f) / (1.0 - f); }
+
+// Lanes per block: the least power of two holding the launch's lens count.
+static int lanes_log2_for(int n_lenses) {
+    int l = 0;
+    while ((1 << l) < n_lenses) ++l;
+    return l;
+}
+
+static void launch_maps(const double* coords, int64_t n_blocks, const LensArgs& a, int cnt, uint8_t* out,
+                        hipStream_t s) {
+    const int64_t threads = n_blocks << a.lanes_log2;
+    const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)cnt);
+    hipLaunchKernelGGL(levelmap_kernel, grid, dim3(256), 0, s, coords, n_blocks, a, out);
 }
 
 static int check_ladder(const uint8_t* ladder_bits, int n_rungs, int glass, const char* who) {
@@ -171,6 +185,9 @@ extern "C" int qam_build_level_maps(const double* coords, int64_t n_blocks, cons
                                glass, mps[(size_t)k], "build_level_maps"))
             return rc;
     if (n_blocks == 0) return QAM_OK;
+    if (n_blocks > (INT64_C(1) << 31) >> lanes_log2_for(n_lenses))
+        QAM_FAIL(QAM_ERR_SHAPE, "build_level_maps: %lld blocks of %d lenses exceed one launch", (long long)n_blocks,
+                 n_lenses);
     // as many maps per launch as the lens table (and the map slots) hold
     const int per = std::max(1, std::min(kMapsPerLaunch, n_lenses ? QAM_MAX_LENSES / n_lenses : kMapsPerLaunch));
     for (int k0 = 0; k0 < n_maps; k0 += per) {
@@ -183,14 +200,13 @@ extern "C" int qam_build_level_maps(const double* coords, int64_t n_blocks, cons
                 const qam_lens& l = lenses[(int64_t)(k0 + k) * n_lenses + i];
                 a.cx[k * n_lenses + i] = l.cx;
                 a.cy[k * n_lenses + i] = l.cy;
-                a.r[k * n_lenses + i] = l.r;
+                a.R[k * n_lenses + i] = lens_R(l.r, params[k0 + k].f);
             }
         }
-        a.n_rungs = n_rungs;
         a.glass = glass;
+        a.lanes_log2 = lanes_log2_for(n_lenses);
         a.out_stride = n_blocks;
-        const dim3 grid((unsigned)((n_blocks + 255) / 256), (unsigned)cnt);
-        hipLaunchKernelGGL(levelmap_kernel, grid, dim3(256), 0, s, coords, n_blocks, a, level_out + (int64_t)k0 * n_blocks);
+        launch_maps(coords, n_blocks, a, cnt, level_out + (int64_t)k0 * n_blocks, s);
         QAM_HIP_CHECK(hipGetLastError());
     }
     set_variant("levelmap_fp64");
@@ -208,18 +224,20 @@ extern "C" int qam_build_level_map(const double* coords, int64_t n_blocks, const
     MapParams mp;
     if (int rc = check_map(lenses, n_lenses, params, n_rungs, glass, mp, "build_level_map")) return rc;
     if (n_blocks == 0) return QAM_OK;
+    if (n_blocks > (INT64_C(1) << 31) >> lanes_log2_for(n_lenses))
+        QAM_FAIL(QAM_ERR_SHAPE, "build_level_map: %lld blocks of %d lenses exceed one launch", (long long)n_blocks,
+                 n_lenses);
     LensArgs a = {};
     a.maps[0] = mp;
     for (int i = 0; i < n_lenses; ++i) {
         a.cx[i] = lenses[i].cx;
         a.cy[i] = lenses[i].cy;
-        a.r[i] = lenses[i].r;
+        a.R[i] = lens_R(lenses[i].r, params->f);
     }
-    a.n_rungs = n_rungs;
     a.glass = glass;
+    a.lanes_log2 = lanes_log2_for(n_lenses);
     a.out_stride = n_blocks;
-    const int64_t grid = (n_blocks + 255) / 256;
-    hipLaunchKernelGGL(levelmap_kernel, dim3((unsigned)grid, 1), dim3(256), 0, s, coords, n_blocks, a, level_out);
+    launch_maps(coords, n_blocks, a, 1, level_out, s);
     QAM_HIP_CHECK(hipGetLastError());
     set_variant("levelmap_fp64");
     return QAM_OK;

@@ -135,6 +135,34 @@ def test_level_map_bit_exact_random_fields(qam):
         assert np.array_equal(got, want), (trial, np.nonzero(got != want)[0][:5])
 
 
+@pytest.mark.parametrize("n_lenses", [16, 33, 64])
+def test_level_map_many_lenses_and_rungs(qam, n_lenses):
+    """Up to the lens-table limit (a whole wavefront of lenses per block) and
+    the longest ladder: every map bit-identical to the oracle, also for a
+    block count that leaves a ragged last workgroup."""
+    rng = np.random.default_rng(300 + n_lenses)
+    for trial in range(6):
+        n = int(rng.integers(1, 3000))
+        coords = rng.uniform(0, 1, size=(n, 2))
+        centres = rng.uniform(-0.1, 1.1, size=(n_lenses, 2))
+        radii = rng.uniform(0.0, 0.2, size=n_lenses)
+        n_rungs = 16 if trial % 2 == 0 else int(rng.integers(2, 16))
+        ladder = tuple(range(0, 2 * n_rungs, 2))
+        glass = int(rng.integers(0, n_rungs))
+        f = float(rng.choice([0.0, 1.0, rng.uniform(0, 1)]))
+        g = float(rng.choice([1.0, rng.uniform(0, 1)]))
+        combine = "sum" if trial % 3 else "max"
+        kappa = O.ceiling(g, n_rungs - 1, glass)
+        stops = None
+        if kappa > glass and trial % 2:
+            stops = np.sort(rng.uniform(0.05, 3.0, size=kappa - glass))[::-1]
+            if np.any(np.diff(stops) >= 0):
+                stops = None
+        want = O.level_map(coords, centres, radii, f, g, combine, n_rungs, glass, stops)
+        got = _gpu_map(qam, coords, centres, radii, f, g, combine, glass, stops, ladder)
+        assert np.array_equal(got, want), (trial, np.nonzero(got != want)[0][:5])
+
+
 def test_level_map_bit_exact_on_ties(qam):
     """A dyadic grid puts many blocks exactly on ring stops and lens edges."""
     xs = np.arange(0, 65) / 64.0
