@@ -78,7 +78,7 @@ def build_field(fld, lens, B, torch, Q, dev):
         x = torch.from_numpy(fld.x(i, B)).to(dev)
         y = torch.empty((B, m.N), dtype=torch.float32, device=dev)
         sub = lv[offs[i]:offs[i] + m.n_blocks]
-        items.append((pm, x, y, sub))
+        items.append((pm, x, y, sub, coords[offs[i]:offs[i] + m.n_blocks]))
         mb, wb = Q.map_weight_bytes(lv_h[offs[i]:offs[i] + m.n_blocks], m.K)
         wbytes += wb
         nz = int(np.count_nonzero(lv_h[offs[i]:offs[i] + m.n_blocks]))
@@ -126,14 +126,24 @@ def run_field(args, torch, Q, WL):
         desc += f"; uniform map at {mb:g} bits (no lenses)"
     mean_bits = float(np.sum(w * np.array(Q.LADDER_BITS)[lv_h]) / np.sum(w))
     group = Q.GroupedQmatvec(items, device=dev)
+    rules = Q.LensRules(lens.centres, lens.radii, lens.f, lens.g, lens.combine, lens.glass)
+    # a lens map on the staged route is built inside the product launch (one
+    # launch per step): each block's coordinates are read (16 bytes) and its
+    # rung written, in place of reading the rung
+    fused = not args.uniform_map and not args.separate_map and group.route == "staged"
+    if fused:
+        other += 16 * fld.n_blocks
 
     def build_map():
         if not args.uniform_map:
-            Q.build_level_map(coords, lens.centres, lens.radii, lens.f, lens.g, lens.combine, lens.glass, out=lv)
+            Q.build_level_map(coords, None, None, None, None, out=lv, rules=rules)
 
     def step():
-        build_map()
-        group.run()
+        if fused:
+            group.run_lens(rules)
+        else:
+            build_map()
+            group.run()
 
     # Kernel durations from HIP events on the stream the kernels run on: the
     # map launch alone (events around it), and the product launch from events
@@ -152,10 +162,19 @@ def run_field(args, torch, Q, WL):
         ev.append((a, b))
     torch.cuda.synchronize()
     map_ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
-    if group.route == "staged":
+    import ctypes as C
+    from query_adaptive_mixed_amd import _lib as L
+    if fused:
+        times = (C.c_float * args.steps)()
+        L.check(L.lib().qam_group_lens_launch_times(
+            C.byref(group.desc), rules.lenses, rules.n_lenses, C.byref(rules.params), C.cast(rules.ladder, C.c_void_p),
+            rules.n_rungs, rules.glass, args.steps, C.cast(times, C.c_void_p),
+            C.c_void_p(torch.cuda.current_stream().cuda_stream)))
+        kern_ms = float(np.median(list(times)))
+        kern_timing = ("median over launches of HIP events recorded at the kernel's start and end "
+                       "(hipExtLaunchKernel); the launch builds the level map and runs the product")
+    elif group.route == "staged":
         # HIP events recorded at the kernel's own start and end (one launch each)
-        import ctypes as C
-        from query_adaptive_mixed_amd import _lib as L
         times = (C.c_float * args.steps)()
         L.check(L.lib().qam_group_launch_times(C.byref(group.desc), args.steps, C.cast(times, C.c_void_p),
                                                 C.c_void_p(torch.cuda.current_stream().cuda_stream)))
@@ -203,9 +222,10 @@ def run_field(args, torch, Q, WL):
     assert np.array_equal(lv.cpu().numpy(), lv_h), "level map changed between steps"
     ms = wall * 1e3 / args.steps
     return dict(desc=desc, mean_bits=mean_bits, wbytes=wbytes, other=other, ms=ms, kern_ms=kern_ms, map_ms=map_ms,
-                kern_timing=kern_timing,
+                kern_timing=kern_timing, fused=fused,
                 variant=Q.last_variant(), lens=lens, fld=fld, lv_h=lv_h, n_items=len(items),
-                key=f"{args.workload}_{args.mean_bits}_g{lens.glass}_b{args.batch}" + ("_uniform" if args.uniform_map else ""))
+                key=f"{args.workload}_{args.mean_bits}_g{lens.glass}_b{args.batch}" + ("_uniform" if args.uniform_map else "")
+                + ("_lens" if fused else ""))
 
 
 # ----------------------------------------------------------------- batched per-request layer
@@ -502,6 +522,8 @@ def main():
                     help="streaming_stack: every block at one depth, the same mean bits as the lens map")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time replays of a captured step instead of eager launches")
+    ap.add_argument("--separate-map", action="store_true",
+                    help="build the lens map with its own launch before the product (else inside the product launch)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode tokens/s leg of the default run")
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-waves", type=int, default=0, help="decoder launch width goal (0 = library default)")
@@ -600,7 +622,8 @@ def main():
             "map": "uniform" if args.uniform_map else "lens",
             "focus_area_f": res["lens"].f, "focus_strength_g": res["lens"].g, "glass_rung": res["lens"].glass,
             "matrices_per_launch": res["n_items"],
-            "level_map_ms": round(res["map_ms"], 5),
+            "level_map": ("built inside the product launch" if res["fused"] else "own launch before the product"),
+            "level_map_alone_ms": round(res["map_ms"], 5),
             "step_timing": "HIP graph replay of one step" if args.graph else "eager launches, wall clock",
             "kernel": res["variant"],
         },

@@ -335,6 +335,9 @@ typedef struct qam_gemv_item {
     int64_t        level_stride; /* per-request maps: bytes from one request's row to the
                                   next (0: w.n_blocks), e.g. the block count of a whole
                                   field whose maps are stored [B][field blocks]        */
+    const double*  coords;     /* (device) fp64 [w.n_blocks][2] block coordinates on the
+                                  field, e.g. rows of the field's coordinate array; only
+                                  qam_qmatvec_group_lens reads them (may be NULL)     */
 } qam_gemv_item;
 
 typedef struct qam_group {     /* filled by qam_group_init; treat as opaque          */
@@ -349,6 +352,7 @@ typedef struct qam_group {     /* filled by qam_group_init; treat as opaque     
     int     per_request_maps;
     int64_t n_pre_workgroups;  /* pre-pass route: limb pre-pass workgroups           */
     void*   pre_map;           /* (device) pre-pass workgroup -> item map            */
+    int     lens_ready;        /* 1: staged-limb route with every item's coords bound */
 } qam_group;
 
 /* Device bytes qam_group_init needs (0 if the items are invalid).  The route
@@ -376,6 +380,29 @@ int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dty
  *   group must be ordered.
  */
 int qam_qmatvec_group(const qam_group* group, hipStream_t s);
+
+/*
+ * qam_qmatvec_group_lens -- qam_qmatvec_group with the level maps built in
+ *   the same launch: every item's map is computed from the lens rules of
+ *   qam_build_level_map ([Lens] "The mechanism" rules 1-6, the same readings
+ *   and numerics, hence bit-identical to qam_build_level_map over the item's
+ *   coords), written to the item's level_map and used for its product.  Each
+ *   wavefront computes the rung of its own block, one lane per lens, before
+ *   reading the block's planes: the map costs no launch of its own and the
+ *   planes read are those of the map.
+ *   group      from qam_group_init on the staged-limb route with B <= 2
+ *              and a shared map, every item's coords bound
+ *              (group->lens_ready); else QAM_ERR_ARG, nothing enqueued.
+ *   lenses, n_lenses, params, glass   as qam_build_level_map; one map rule
+ *              set for every item (the items are blocks of one field).
+ *   ladder_bits/n_rungs  must be the product ladder {0, 2, 4, 6, 8}
+ *              (QAM_ERR_LADDER otherwise).
+ *   Outputs: every item's y, as qam_qmatvec_group with that map, and its
+ *   level_map.  Enqueues one kernel and nothing else (safe to capture).
+ */
+int qam_qmatvec_group_lens(const qam_group* group, const qam_lens* lenses, int n_lenses,
+                           const qam_lens_params* params, const uint8_t* ladder_bits, int n_rungs,
+                           int glass, hipStream_t s);
 
 /* ---------------------------------------------------------------- decode driver */
 /*

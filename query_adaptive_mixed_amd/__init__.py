@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     LADDER_BITS,
     Decoder,
     GroupedQmatvec,
+    LensRules,
     PackedMatrix,
     Workspace,
     build_level_map,

@@ -41,13 +41,14 @@ class QamLensParams(C.Structure):
 
 class QamGemvItem(C.Structure):
     _fields_ = [("w", QamPacked), ("x", C.c_void_p), ("y", C.c_void_p), ("level_map", C.c_void_p),
-                ("level_stride", C.c_int64)]
+                ("level_stride", C.c_int64), ("coords", C.c_void_p)]
 
 
 class QamGroup(C.Structure):
     _fields_ = [("n_items", C.c_int), ("B", C.c_int64), ("x_dtype", C.c_int), ("n_workgroups", C.c_int64),
                 ("lds_bytes", C.c_size_t), ("table", C.c_void_p), ("wg_map", C.c_void_p), ("route", C.c_int),
-                ("per_request_maps", C.c_int), ("n_pre_workgroups", C.c_int64), ("pre_map", C.c_void_p)]
+                ("per_request_maps", C.c_int), ("n_pre_workgroups", C.c_int64), ("pre_map", C.c_void_p),
+                ("lens_ready", C.c_int)]
 
 
 class QamEpilogue(C.Structure):
@@ -97,6 +98,8 @@ SIGNATURES = [
     ("qam_group_bytes", C.c_size_t, [C.POINTER(QamGemvItem), _I, _I64, _I]),
     ("qam_group_init", _I, [C.POINTER(QamGemvItem), _I, _I64, _I, _I, _P, _SZ, C.POINTER(QamGroup), _P]),
     ("qam_qmatvec_group", _I, [C.POINTER(QamGroup), _P]),
+    ("qam_qmatvec_group_lens", _I, [C.POINTER(QamGroup), C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I,
+                                    _I, _P]),
     ("qam_last_error", C.c_char_p, []),
     ("qam_last_variant", C.c_char_p, []),
     ("qam_version", C.c_char_p, []),
@@ -109,6 +112,8 @@ EXTRA_SIGNATURES = [
     ("qam_set_mfma_min_batch", _I, [_I]),
     ("qam_set_staged_mfma", _I, [_I]),
     ("qam_group_launch_times", _I, [C.POINTER(QamGroup), _I, _P, _P]),
+    ("qam_group_lens_launch_times", _I, [C.POINTER(QamGroup), C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P,
+                                         _I, _I, _I, _P, _P]),
     ("qam_set_tail_split", _I, [_I, _I]),
     ("qam_set_mfma_tiles_per_request", _I, [_I]),
     ("qam_set_mfma_ksplit", _I, [_I]),

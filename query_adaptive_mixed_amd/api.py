@@ -83,40 +83,57 @@ def unpack_codes(packed: PackedMatrix, level_map: torch.Tensor, out: Optional[to
     return out
 
 
+class LensRules:
+    """One map's lens-rule arguments, marshalled once for the C ABI:
+    ``centres`` [n_lenses, 2] and ``radii`` [n_lenses] (host sequences), the
+    focus area ``f`` and strength ``g``, ``combine`` ('sum' or 'max'), the
+    ``glass`` rung, optional explicit ``stops`` and the ladder."""
+
+    def __init__(self, centres, radii, f: float, g: float, combine: str = "sum", glass: int = 1, stops=None,
+                 ladder_bits: Sequence[int] = LADDER_BITS):
+        centres = np.asarray(centres, dtype=np.float64).reshape(-1, 2)
+        radii = np.asarray(radii, dtype=np.float64).reshape(-1)
+        if centres.shape[0] != radii.shape[0]:
+            raise ValueError("centres and radii disagree on the lens count")
+        self.n_lenses = centres.shape[0]
+        self.lenses = (L.QamLens * max(1, self.n_lenses))()
+        for i in range(self.n_lenses):
+            self.lenses[i].cx, self.lenses[i].cy = float(centres[i, 0]), float(centres[i, 1])
+            self.lenses[i].r = float(radii[i])
+        p = L.QamLensParams()
+        p.f, p.g = float(f), float(g)
+        p.combine = {"sum": L.QAM_COMBINE_SUM, "max": L.QAM_COMBINE_MAX}[combine]
+        if stops is None:
+            p.n_stops = 0
+        else:
+            st = np.asarray(stops, dtype=np.float64).reshape(-1)
+            p.n_stops = int(st.shape[0])
+            if p.n_stops > L.QAM_MAX_STOPS:
+                raise ValueError("too many stops")
+            for j, v in enumerate(st):
+                p.stops[j] = float(v)
+        self.params = p
+        self.n_rungs = len(ladder_bits)
+        self.ladder = (C.c_uint8 * self.n_rungs)(*ladder_bits)
+        self.glass = int(glass)
+
+
 def build_level_map(coords: torch.Tensor, centres, radii, f: float, g: float, combine: str = "sum",
                     glass: int = 1, ladder_bits: Sequence[int] = LADDER_BITS, stops=None,
-                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    out: Optional[torch.Tensor] = None, rules: Optional[LensRules] = None) -> torch.Tensor:
     """Per-block rung indices (uint8 [n_blocks]) from the lens rules.
 
     ``coords`` is a device fp64 [n_blocks, 2] tensor; ``centres`` [n_lenses, 2]
-    and ``radii`` [n_lenses] are host sequences."""
+    and ``radii`` [n_lenses] are host sequences (or pass ``rules``, a
+    LensRules, with centres = radii = None)."""
     _require_cuda(coords, "coords", torch.float64)
     n_blocks = coords.shape[0]
-    centres = np.asarray(centres, dtype=np.float64).reshape(-1, 2)
-    radii = np.asarray(radii, dtype=np.float64).reshape(-1)
-    if centres.shape[0] != radii.shape[0]:
-        raise ValueError("centres and radii disagree on the lens count")
-    n_lenses = centres.shape[0]
-    lenses = (L.QamLens * max(1, n_lenses))()
-    for i in range(n_lenses):
-        lenses[i].cx, lenses[i].cy, lenses[i].r = float(centres[i, 0]), float(centres[i, 1]), float(radii[i])
-    p = L.QamLensParams()
-    p.f, p.g = float(f), float(g)
-    p.combine = {"sum": L.QAM_COMBINE_SUM, "max": L.QAM_COMBINE_MAX}[combine]
-    if stops is None:
-        p.n_stops = 0
-    else:
-        st = np.asarray(stops, dtype=np.float64).reshape(-1)
-        p.n_stops = int(st.shape[0])
-        if p.n_stops > L.QAM_MAX_STOPS:
-            raise ValueError("too many stops")
-        for j, v in enumerate(st):
-            p.stops[j] = float(v)
-    ladder = (C.c_uint8 * len(ladder_bits))(*ladder_bits)
+    r = rules if rules is not None else LensRules(centres, radii, f, g, combine, glass, stops, ladder_bits)
     if out is None:
         out = torch.empty(n_blocks, dtype=torch.uint8, device=coords.device)
-    L.check(L.lib().qam_build_level_map(_ptr(coords), n_blocks, lenses, n_lenses, C.byref(p), C.cast(ladder, C.c_void_p),
-                                        len(ladder_bits), int(glass), _ptr(out), _stream_handle()))
+    L.check(L.lib().qam_build_level_map(_ptr(coords), n_blocks, r.lenses, r.n_lenses, C.byref(r.params),
+                                        C.cast(r.ladder, C.c_void_p), r.n_rungs, r.glass, _ptr(out),
+                                        _stream_handle()))
     return out
 
 
@@ -264,7 +281,9 @@ class GroupedQmatvec:
     tuples, the maps all [n_blocks] (shared by the B requests) or all
     [B, n_blocks] (per request); the tensors are bound once (keep them alive
     and update them in place), and every ``run()`` recomputes all the y from
-    the bound buffers."""
+    the bound buffers.  A fifth element, the item's block coordinates (device
+    fp64 [n_blocks, 2]), lets ``run_lens`` build the maps in the product
+    launch (staged route, shared maps)."""
 
     def __init__(self, items, device="cuda"):
         n = len(items)
@@ -273,7 +292,9 @@ class GroupedQmatvec:
         xdt = None
         per_request = None
         self._keep = []
-        for i, (pm, x, y, lv) in enumerate(items):
+        for i, item in enumerate(items):
+            pm, x, y, lv = item[:4]
+            cd = item[4] if len(item) > 4 else None
             _require_cuda(x, "x")
             _require_cuda(y, "y", torch.float32)
             if not isinstance(lv, torch.Tensor) or not lv.is_cuda or lv.dtype != torch.uint8:
@@ -298,7 +319,12 @@ class GroupedQmatvec:
             arr[i].w = pm.desc
             arr[i].x, arr[i].y, arr[i].level_map = x.data_ptr(), y.data_ptr(), lv.data_ptr()
             arr[i].level_stride = stride
-            self._keep.append((pm, x, y, lv))
+            if cd is not None:
+                _require_cuda(cd, "coords", torch.float64)
+                if tuple(cd.shape) != (pm.n_blocks, 2) or cd.stride() != (2, 1):
+                    raise ValueError("coords must be a contiguous fp64 [n_blocks, 2] tensor")
+                arr[i].coords = cd.data_ptr()
+            self._keep.append((pm, x, y, lv, cd))
         nbytes = int(L.lib().qam_group_bytes(arr, n, B, int(per_request)))
         if nbytes == 0:
             raise L.QamError(-2, "invalid group items")
@@ -314,6 +340,13 @@ class GroupedQmatvec:
 
     def run(self) -> None:
         L.check(L.lib().qam_qmatvec_group(C.byref(self.desc), _stream_handle()))
+
+    def run_lens(self, rules: LensRules) -> None:
+        """One launch: every item's level map from ``rules`` (a LensRules) over
+        its bound coordinates, written to its level_map, and its product."""
+        L.check(L.lib().qam_qmatvec_group_lens(C.byref(self.desc), rules.lenses, rules.n_lenses,
+                                               C.byref(rules.params), C.cast(rules.ladder, C.c_void_p),
+                                               rules.n_rungs, rules.glass, _stream_handle()))
 
 
 class Decoder:

@@ -1,18 +1,11 @@
-// Level map from the lens rules: a group of lanes per block (one per lens), fp64.
-//
-// Rules 1-6 of the FoQLens landing page (vovanda.github.io/FoQLens), section
-// "The mechanism", which repeat the rule list of "FoQZones, the mechanism" on
-// foqlens.sawking.tech with the per-lens radius R_i = r_i f / (1 - f):
-//   1 radius   R_i = r_i f / (1 - f)
-//   2 ceiling  kappa = gamma + floor(g (m - gamma))
-//   3 stops    s_kappa < ... < s_(gamma+1), ring ends in radii
-//   4 lift     rho_i = d(b, c_i) / R_i,  L_i = max(0, 1 - rho_i / s_last)
-//   5 combine  L = min(1, sum L_i)  or  max L_i
-//   6 level    rho* = s_last (1 - L); the ring rho* falls into; else the glass
-// Readings where the pages are open: Euclidean distance on the block field,
-// s_last = s_(gamma+1), default stops evenly spaced with the outermost at 1,
-// half-open rings (level = gamma + #{j : rho* < s_(gamma+j)}), R = +inf at
-// f = 1, and a radius of 0 lifting only a block at distance 0.
+// Level maps from the lens rules of the FoQLens landing page
+// (vovanda.github.io/FoQLens), section "The mechanism", which repeat the rule
+// list of "FoQZones, the mechanism" on foqlens.sawking.tech with the per-lens
+// radius R_i = r_i f / (1 - f).  The rules and the readings taken where the
+// pages are open are stated in lens_rules.h, with the device code this file
+// and the grouped product share.  Here: the host checks, rules 1-3 on the
+// host, and a kernel that runs rules 4-6 with a group of lanes per block (one
+// lane per lens).
 //
 // The file is compiled with -ffp-contract=off: every product and sum is a
 // separate correctly rounded IEEE operation, as is sqrt (an FMA-corrected
@@ -23,27 +16,15 @@
 #include <algorithm>
 #include <vector>
 
-#include "qam_common.h"
+#include "lens_rules.h"
 
 namespace qam {
 
 constexpr int kMapsPerLaunch = 8;
 
-// One map's rules as the kernel takes them: rules 1-3 are per map and per
-// lens, not per block, so the host evaluates them (the same IEEE operations
-// in the same order, hence the same values) and the kernel runs rules 4-6.
-struct MapParams {
-    double stops[QAM_MAX_STOPS];   // rule 3: s_(gamma+1) > ... > s_kappa, n of them
-    int n;                         // kappa - gamma (0: every block at the glass)
-    int combine;
-    int first;                     // the map's lenses: [first, first + n_lenses)
-    int n_lenses;
-};
-
+// Up to kMapsPerLaunch maps of one launch over a shared lens table.
 struct LensArgs {
-    double cx[QAM_MAX_LENSES];
-    double cy[QAM_MAX_LENSES];
-    double R[QAM_MAX_LENSES];      // rule 1: R_i, +inf at f = 1
+    LensTable t;
     MapParams maps[kMapsPerLaunch];
     int glass;
     int lanes_log2;                // log2 of the lanes per block: >= log2(n_lenses), <= 6
@@ -68,40 +49,18 @@ __global__ __launch_bounds__(256) void levelmap_kernel(const double* __restrict_
         if (live && j == 0) o[b] = (uint8_t)a.glass;
         return;
     }
-    const double s_last = p.stops[0];
     double lift = 0.0;
     if (j < p.n_lenses) {
         const int i = p.first + j;
-        const double dx = coords[2 * b] - a.cx[i];
-        const double dy = coords[2 * b + 1] - a.cy[i];
-        const double dist = sqrt(dx * dx + dy * dy);
-        const double R = a.R[i];
-        double rho;
-        if (R == 0.0) rho = (dist == 0.0) ? 0.0 : INFINITY;
-        else rho = dist / R;
-        const double tt = 1.0 - rho / s_last;
-        lift = tt > 0.0 ? tt : 0.0;
+        lift = lens_lift(coords[2 * b], coords[2 * b + 1], a.t.cx[i], a.t.cy[i], a.t.R[i], p.stops[0]);
     }
-    // rule 5 in lens order: lane base + k holds lens k of this block
     const int base = (int)(threadIdx.x & 63) & ~((1 << a.lanes_log2) - 1);
-    double acc = 0.0;
-    for (int k = 0; k < p.n_lenses; ++k) {
-        const double v = __shfl(lift, base + k, 64);
-        if (p.combine == QAM_COMBINE_SUM) acc = acc + v;
-        else acc = acc > v ? acc : v;
-    }
-    const double L = (p.combine == QAM_COMBINE_SUM) ? (acc < 1.0 ? acc : 1.0) : acc;
-    // rule 6: the ring rho* falls into
-    const double rho_star = s_last * (1.0 - L);
-    int count = 0;
-    for (int k = 0; k < p.n; ++k)
-        if (rho_star < p.stops[k]) ++count;
-    if (live && j == 0) o[b] = (uint8_t)(a.glass + count);
+    const int rung = lens_rung(lift, base, p, a.glass);
+    if (live && j == 0) o[b] = (uint8_t)rung;
 }
 
-// Host checks of one map's parameters and lenses (error text names `who`).
-static int check_map(const qam_lens* lenses, int n_lenses, const qam_lens_params* params, int n_rungs, int glass,
-                     MapParams& mp, const char* who) {
+int lens_check_map(const qam_lens* lenses, int n_lenses, const qam_lens_params* params, int n_rungs, int glass,
+                   MapParams& mp, const char* who) {
     if (n_lenses < 0 || n_lenses > QAM_MAX_LENSES)
         QAM_FAIL(QAM_ERR_ARG, "%s: n_lenses=%d outside [0, %d]", who, n_lenses, QAM_MAX_LENSES);
     if (n_lenses > 0 && !lenses) QAM_FAIL(QAM_ERR_NULL, "%s: null lenses", who);
@@ -111,11 +70,11 @@ static int check_map(const qam_lens* lenses, int n_lenses, const qam_lens_params
     if (params->combine != QAM_COMBINE_SUM && params->combine != QAM_COMBINE_MAX)
         QAM_FAIL(QAM_ERR_ARG, "%s: combine must be SUM or MAX", who);
     const int m = n_rungs - 1;
-    const int kappa = glass + (int)floor(g * (double)(m - glass));
+    const int kappa = glass + (int)floor(g * (double)(m - glass));   // rule 2
     const int n = kappa - glass;
     mp = MapParams{};
     mp.n = n;
-    if (params->n_stops != 0) {
+    if (params->n_stops != 0) {   // rule 3, given
         if (params->n_stops != n)
             QAM_FAIL(QAM_ERR_ARG, "%s: %d stops given, kappa - glass = %d", who, params->n_stops, n);
         for (int j = 0; j < n; ++j) {
@@ -125,8 +84,8 @@ static int check_map(const qam_lens* lenses, int n_lenses, const qam_lens_params
                 QAM_FAIL(QAM_ERR_ARG, "%s: stops not strictly decreasing", who);
             mp.stops[j] = params->stops[j];
         }
-    } else {
-        for (int j = 0; j < n; ++j) mp.stops[j] = (double)(n - j) / (double)n;   // default spacing
+    } else {                      // rule 3, default spacing
+        for (int j = 0; j < n; ++j) mp.stops[j] = (double)(n - j) / (double)n;
     }
     for (int i = 0; i < n_lenses; ++i)
         if (!isfinite(lenses[i].cx) || !isfinite(lenses[i].cy) || !(lenses[i].r >= 0.0) || !isfinite(lenses[i].r))
@@ -136,8 +95,17 @@ static int check_map(const qam_lens* lenses, int n_lenses, const qam_lens_params
     return QAM_OK;
 }
 
-// Rule 1 for one lens, as the oracle and the pages write it: (r f) / (1 - f).
-static double lens_R(double r, double f) { return f == 1.0 ? INFINITY : (r * f) / (1.0 - f); }
+double lens_radius(double r, double f) { return f == 1.0 ? INFINITY : (r * f) / (1.0 - f); }
+
+int lens_check_ladder(const uint8_t* ladder_bits, int n_rungs, int glass, const char* who) {
+    if (n_rungs < 2 || n_rungs > QAM_MAX_RUNGS)
+        QAM_FAIL(QAM_ERR_LADDER, "%s: n_rungs=%d outside [2, %d]", who, n_rungs, QAM_MAX_RUNGS);
+    if (ladder_bits[0] != 0) QAM_FAIL(QAM_ERR_LADDER, "%s: ladder must start at ZERO", who);
+    for (int i = 1; i < n_rungs; ++i)
+        if (ladder_bits[i] <= ladder_bits[i - 1]) QAM_FAIL(QAM_ERR_LADDER, "%s: ladder not increasing", who);
+    if (glass < 0 || glass >= n_rungs) QAM_FAIL(QAM_ERR_ARG, "%s: glass=%d not a rung", who, glass);
+    return QAM_OK;
+}
 
 // Lanes per block: the least power of two holding the launch's lens count.
 static int lanes_log2_for(int n_lenses) {
@@ -153,16 +121,6 @@ static void launch_maps(const double* coords, int64_t n_blocks, const LensArgs& 
     hipLaunchKernelGGL(levelmap_kernel, grid, dim3(256), 0, s, coords, n_blocks, a, out);
 }
 
-static int check_ladder(const uint8_t* ladder_bits, int n_rungs, int glass, const char* who) {
-    if (n_rungs < 2 || n_rungs > QAM_MAX_RUNGS)
-        QAM_FAIL(QAM_ERR_LADDER, "%s: n_rungs=%d outside [2, %d]", who, n_rungs, QAM_MAX_RUNGS);
-    if (ladder_bits[0] != 0) QAM_FAIL(QAM_ERR_LADDER, "%s: ladder must start at ZERO", who);
-    for (int i = 1; i < n_rungs; ++i)
-        if (ladder_bits[i] <= ladder_bits[i - 1]) QAM_FAIL(QAM_ERR_LADDER, "%s: ladder not increasing", who);
-    if (glass < 0 || glass >= n_rungs) QAM_FAIL(QAM_ERR_ARG, "%s: glass=%d not a rung", who, glass);
-    return QAM_OK;
-}
-
 }  // namespace qam
 
 using namespace qam;
@@ -176,12 +134,12 @@ extern "C" int qam_build_level_maps(const double* coords, int64_t n_blocks, cons
     if (n_maps < 1 || n_maps > QAM_MAX_BATCH_MFMA)
         QAM_FAIL(QAM_ERR_ARG, "build_level_maps: n_maps=%d outside [1, %d]", n_maps, QAM_MAX_BATCH_MFMA);
     if (n_blocks > 0 && (!coords || !level_out)) QAM_FAIL(QAM_ERR_NULL, "build_level_maps: null coords/output");
-    if (int rc = check_ladder(ladder_bits, n_rungs, glass, "build_level_maps")) return rc;
+    if (int rc = lens_check_ladder(ladder_bits, n_rungs, glass, "build_level_maps")) return rc;
     if (n_lenses < 0 || n_lenses > QAM_MAX_LENSES)
         QAM_FAIL(QAM_ERR_ARG, "build_level_maps: n_lenses=%d outside [0, %d]", n_lenses, QAM_MAX_LENSES);
     std::vector<MapParams> mps((size_t)n_maps);
     for (int k = 0; k < n_maps; ++k)
-        if (int rc = check_map(n_lenses ? lenses + (int64_t)k * n_lenses : nullptr, n_lenses, params + k, n_rungs,
+        if (int rc = lens_check_map(n_lenses ? lenses + (int64_t)k * n_lenses : nullptr, n_lenses, params + k, n_rungs,
                                glass, mps[(size_t)k], "build_level_maps"))
             return rc;
     if (n_blocks == 0) return QAM_OK;
@@ -198,9 +156,9 @@ extern "C" int qam_build_level_maps(const double* coords, int64_t n_blocks, cons
             a.maps[k].first = k * n_lenses;
             for (int i = 0; i < n_lenses; ++i) {
                 const qam_lens& l = lenses[(int64_t)(k0 + k) * n_lenses + i];
-                a.cx[k * n_lenses + i] = l.cx;
-                a.cy[k * n_lenses + i] = l.cy;
-                a.R[k * n_lenses + i] = lens_R(l.r, params[k0 + k].f);
+                a.t.cx[k * n_lenses + i] = l.cx;
+                a.t.cy[k * n_lenses + i] = l.cy;
+                a.t.R[k * n_lenses + i] = lens_radius(l.r, params[k0 + k].f);
             }
         }
         a.glass = glass;
@@ -220,9 +178,9 @@ extern "C" int qam_build_level_map(const double* coords, int64_t n_blocks, const
     if (n_blocks < 0) QAM_FAIL(QAM_ERR_SHAPE, "build_level_map: n_blocks < 0");
     if (!params || !ladder_bits) QAM_FAIL(QAM_ERR_NULL, "build_level_map: null params/ladder");
     if (n_blocks > 0 && (!coords || !level_out)) QAM_FAIL(QAM_ERR_NULL, "build_level_map: null coords/output");
-    if (int rc = check_ladder(ladder_bits, n_rungs, glass, "build_level_map")) return rc;
+    if (int rc = lens_check_ladder(ladder_bits, n_rungs, glass, "build_level_map")) return rc;
     MapParams mp;
-    if (int rc = check_map(lenses, n_lenses, params, n_rungs, glass, mp, "build_level_map")) return rc;
+    if (int rc = lens_check_map(lenses, n_lenses, params, n_rungs, glass, mp, "build_level_map")) return rc;
     if (n_blocks == 0) return QAM_OK;
     if (n_blocks > (INT64_C(1) << 31) >> lanes_log2_for(n_lenses))
         QAM_FAIL(QAM_ERR_SHAPE, "build_level_map: %lld blocks of %d lenses exceed one launch", (long long)n_blocks,
@@ -230,9 +188,9 @@ extern "C" int qam_build_level_map(const double* coords, int64_t n_blocks, const
     LensArgs a = {};
     a.maps[0] = mp;
     for (int i = 0; i < n_lenses; ++i) {
-        a.cx[i] = lenses[i].cx;
-        a.cy[i] = lenses[i].cy;
-        a.R[i] = lens_R(lenses[i].r, params->f);
+        a.t.cx[i] = lenses[i].cx;
+        a.t.cy[i] = lenses[i].cy;
+        a.t.R[i] = lens_radius(lenses[i].r, params->f);
     }
     a.glass = glass;
     a.lanes_log2 = lanes_log2_for(n_lenses);

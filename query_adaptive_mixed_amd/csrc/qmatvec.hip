@@ -36,6 +36,7 @@
 #include <algorithm>
 #include <vector>
 
+#include "lens_rules.h"
 #include "qmatvec_internal.h"
 
 namespace qam {
@@ -568,9 +569,12 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
 
 // One (block, column chunk) unit of item a, `local` being its index within
 // the item, run by c.KS wavefronts (at most MAXW); wave k takes the chunk's
-// tiles k, k + KS, ...
-template <int NB, bool XBF16, int MAXW, bool MF, bool EPI>
-__device__ __forceinline__ void run_unit(const Item& a, const Common& c, int local, int4* lds, int tid) {
+// tiles k, k + KS, ...  With a lens map lm (one wavefront per unit), the
+// block's rung comes from the lens rules and the chunk-0 unit writes it to
+// the item's map; else it is read from the map (or fixed).
+template <int NB, bool XBF16, int MAXW, bool MF, bool EPI, bool LENS = false>
+__device__ __forceinline__ void run_unit(const Item& a, const Common& c, int local, int4* lds, int tid,
+                                         const LensMap* lm = nullptr) {
     // per wave: region_int4<NB>() int4 (the sub-chunk's limb words in the
     // layout of the inner product in use; for the matrix cores then 3 NB x 64
     // int32 sums); then, with several waves, [KS][NB][2][64] fp64 row sums
@@ -583,7 +587,14 @@ __device__ __forceinline__ void run_unit(const Item& a, const Common& c, int loc
     const int chunk = local % a.n_chunks;
     const int b = local / a.n_chunks;
     const int L = tid & 63;
-    const int lev = a.fixed_level >= 0 ? a.fixed_level : level_of(a.level, b);
+    int lev;
+    if constexpr (LENS) {
+        static_assert(MAXW == 1, "one wavefront per unit computes the rung");
+        lev = lens_block_rung(a.coords, b, L, *lm);
+        if (chunk == 0 && L == 0) const_cast<uint8_t*>(a.level)[b] = (uint8_t)lev;
+    } else {
+        lev = a.fixed_level >= 0 ? a.fixed_level : level_of(a.level, b);
+    }
     const int ns = __builtin_amdgcn_readfirstlane(lev < 4 ? lev : 4);
     switch (ns) {   // uniform over the workgroup: one block
         case 0:   // ZERO: nothing read, y = 0 (written once, by the first chunk's first wave)
@@ -624,6 +635,15 @@ __global__ __launch_bounds__(64 * MAXW) void qmatvec_kernel(Item single, Common 
     } else {
         run_unit<NB, XBF16, MAXW, MF, true>(single, c, (int)blockIdx.x, lds, (int)threadIdx.x);
     }
+}
+
+// A group whose maps are built in the same launch: every unit computes its
+// block's rung from the lens map (kernel argument) before its planes.
+template <int NB, bool XBF16, bool MF>
+__global__ __launch_bounds__(64) void qmatvec_lens_kernel(Common c, LensMap lm) {
+    extern __shared__ int4 lds[];
+    const Item a = unit_item(c, (int)blockIdx.x);
+    run_unit<NB, XBF16, 1, MF, false, true>(a, c, (int)blockIdx.x - a.wg_begin, lds, (int)threadIdx.x, &lm);
 }
 
 // ------------------------------------------------------------------ host side
@@ -970,6 +990,7 @@ extern "C" int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B
     char* wgmap = table + g.table_bytes;
     std::vector<Item> host_items(n_items);
     std::vector<int> host_map((size_t)g.n_wg);
+    int lens_ready = 1;
     int64_t wg = 0, blk = 0;
     size_t poff = 0;
     for (int i = 0; i < n_items; ++i) {
@@ -978,6 +999,9 @@ extern "C" int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B
         const Plan& p = g.plans[i];
         Item it = make_item(gi.x, &gi.w, gi.level_map, gi.y, p);
         it.wg_begin = (int)wg;
+        it.coords = gi.coords;
+        if (!gi.coords) lens_ready = 0;
+        else if (!aligned(gi.coords, 8)) QAM_FAIL(QAM_ERR_ALIGN, "group_init: item %d coords not 8-byte aligned", i);
         if (p.n_chunks > 1) {
             it.counters = reinterpret_cast<uint32_t*>(base) + blk;
             it.partials = reinterpret_cast<double*>(partials + poff);
@@ -1004,6 +1028,121 @@ extern "C" int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B
     group_out->per_request_maps = 0;
     group_out->n_pre_workgroups = 0;
     group_out->pre_map = nullptr;
+    group_out->lens_ready = lens_ready;
+    return QAM_OK;
+}
+
+namespace qam {
+
+template <int NB, bool MF>
+static void launch_lens_k(const Common& c, const LensMap& lm, int64_t grid, size_t lds, hipStream_t s,
+                          hipEvent_t e0, hipEvent_t e1) {
+    const dim3 g((unsigned)grid), b(64u);
+    if (c.x_bf16)
+        hipExtLaunchKernelGGL((qmatvec_lens_kernel<NB, true, MF>), g, b, (uint32_t)lds, s, e0, e1, 0u, c, lm);
+    else
+        hipExtLaunchKernelGGL((qmatvec_lens_kernel<NB, false, MF>), g, b, (uint32_t)lds, s, e0, e1, 0u, c, lm);
+}
+
+template <int NB>
+static void launch_lens_nb(const Common& c, const LensMap& lm, int64_t grid, size_t lds, hipStream_t s,
+                           hipEvent_t e0, hipEvent_t e1) {
+    if (g_staged_mfma) launch_lens_k<NB, true>(c, lm, grid, lds, s, e0, e1);
+    else launch_lens_k<NB, false>(c, lm, grid, lds, s, e0, e1);
+}
+
+// Checks of a group and its lens rules for a launch that builds the maps;
+// fills the launch arguments.
+static int lens_group_setup(const qam_group* group, const qam_lens* lenses, int n_lenses,
+                            const qam_lens_params* params, const uint8_t* ladder_bits, int n_rungs, int glass,
+                            Common& c, LensMap& lm, const char* who) {
+    if (!group || !group->table || !group->wg_map) QAM_FAIL(QAM_ERR_NULL, "%s: uninitialised group", who);
+    if (!params || !ladder_bits) QAM_FAIL(QAM_ERR_NULL, "%s: null params/ladder", who);
+    if (group->route != 0 || group->per_request_maps != 0 || group->B < 1 || group->B > QAM_MAX_BATCH ||
+        group->n_workgroups < 1)
+        QAM_FAIL(QAM_ERR_ARG, "%s: the map is built in the launch on the staged-limb route only (shared map)", who);
+    if (!group->lens_ready) QAM_FAIL(QAM_ERR_ARG, "%s: the group's items have no block coordinates", who);
+    static const uint8_t kProductLadder[5] = {0, 2, 4, 6, 8};
+    if (n_rungs != 5) QAM_FAIL(QAM_ERR_LADDER, "%s: the product ladder has 5 rungs, got %d", who, n_rungs);
+    if (int rc = lens_check_ladder(ladder_bits, n_rungs, glass, who)) return rc;
+    for (int i = 0; i < 5; ++i)
+        if (ladder_bits[i] != kProductLadder[i]) QAM_FAIL(QAM_ERR_LADDER, "%s: ladder must be {0,2,4,6,8}", who);
+    lm = LensMap{};
+    if (int rc = lens_check_map(lenses, n_lenses, params, n_rungs, glass, lm.p, who)) return rc;
+    for (int i = 0; i < n_lenses; ++i) {
+        lm.t.cx[i] = lenses[i].cx;
+        lm.t.cy[i] = lenses[i].cy;
+        lm.t.R[i] = lens_radius(lenses[i].r, params->f);
+    }
+    lm.glass = glass;
+    c = Common{};
+    c.items = static_cast<const Item*>(group->table);
+    c.wg_item = static_cast<const int*>(group->wg_map);
+    c.B = (int)group->B;
+    c.x_bf16 = group->x_dtype == QAM_X_BF16;
+    c.KS = 1;
+    return QAM_OK;
+}
+
+static void launch_lens(const qam_group* group, const Common& c, const LensMap& lm, hipStream_t s,
+                        hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+    const int64_t grid = group->n_workgroups;
+    const size_t lds = group->lds_bytes;
+    switch (group->B) {
+        case 1: launch_lens_nb<1>(c, lm, grid, lds, s, e0, e1); break;
+        default: launch_lens_nb<2>(c, lm, grid, lds, s, e0, e1); break;
+    }
+}
+
+}  // namespace qam
+
+extern "C" int qam_qmatvec_group_lens(const qam_group* group, const qam_lens* lenses, int n_lenses,
+                                      const qam_lens_params* params, const uint8_t* ladder_bits, int n_rungs,
+                                      int glass, hipStream_t s) {
+    clear_error();
+    Common c;
+    LensMap lm;
+    if (int rc = lens_group_setup(group, lenses, n_lenses, params, ladder_bits, n_rungs, glass, c, lm,
+                                  "qmatvec_group_lens"))
+        return rc;
+    if (group->B > 2)
+        QAM_FAIL(QAM_ERR_ARG, "qmatvec_group_lens: B=%lld; the map is built in the launch for B <= 2",
+                 (long long)group->B);
+    launch_lens(group, c, lm, s);
+    QAM_HIP_CHECK(hipGetLastError());
+    char v[128];
+    snprintf(v, sizeof(v), "%s_group_lens items=%d B=%lld wg=%lld", staged_name(), group->n_items,
+             (long long)group->B, (long long)group->n_workgroups);
+    set_variant(v);
+    return QAM_OK;
+}
+
+// Benchmark hook: qam_qmatvec_group_lens run `n` times back to back on `s`,
+// each launch timed as by qam_group_launch_times.
+extern "C" int qam_group_lens_launch_times(const qam_group* group, const qam_lens* lenses, int n_lenses,
+                                           const qam_lens_params* params, const uint8_t* ladder_bits, int n_rungs,
+                                           int glass, int n, float* ms_out, hipStream_t s) {
+    clear_error();
+    Common c;
+    LensMap lm;
+    if (int rc = lens_group_setup(group, lenses, n_lenses, params, ladder_bits, n_rungs, glass, c, lm,
+                                  "group_lens_launch_times"))
+        return rc;
+    if (group->B > 2) QAM_FAIL(QAM_ERR_ARG, "group_lens_launch_times: B=%lld > 2", (long long)group->B);
+    if (!ms_out) QAM_FAIL(QAM_ERR_NULL, "group_lens_launch_times: null output");
+    if (n < 1 || n > 4096) QAM_FAIL(QAM_ERR_ARG, "group_lens_launch_times: n=%d outside [1, 4096]", n);
+    std::vector<hipEvent_t> ev((size_t)2 * n, nullptr);
+    hipError_t e = hipSuccess;
+    for (size_t i = 0; i < ev.size() && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+    for (int i = 0; i < n && e == hipSuccess; ++i) {
+        launch_lens(group, c, lm, s, ev[2 * i], ev[2 * i + 1]);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    for (int i = 0; i < n && e == hipSuccess; ++i) e = hipEventElapsedTime(&ms_out[i], ev[2 * i], ev[2 * i + 1]);
+    for (hipEvent_t x : ev)
+        if (x) (void)hipEventDestroy(x);
+    if (e != hipSuccess) QAM_FAIL(QAM_ERR_HIP, "group_lens_launch_times: %s", hipGetErrorString(e));
     return QAM_OK;
 }
 

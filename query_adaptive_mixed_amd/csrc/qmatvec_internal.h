@@ -97,7 +97,8 @@ struct Item {
     const float* scales;
     const void* x;             // [B][K]
     float* y;                  // [B][N]
-    const uint8_t* level;      // [n_blocks]
+    const uint8_t* level;      // [n_blocks] (written by grouped launches that build the map)
+    const double* coords;      // [n_blocks][2] block coordinates (grouped launches that build the map)
     double* partials;          // [n_chunks][B][N] (split K only)
     uint32_t* counters;        // [n_blocks]       (split K only)
     int64_t plane_bytes;       // N*K/4

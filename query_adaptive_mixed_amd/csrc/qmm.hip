@@ -643,6 +643,7 @@ int mfma_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dt
     out->per_request_maps = per_request_maps;
     out->n_pre_workgroups = g.n_pre;
     out->pre_map = premap;
+    out->lens_ready = 0;
     return QAM_OK;
 }
 

@@ -303,3 +303,49 @@ def test_group_calls_reject_bad_descriptors_before_any_launch(lib):
     assert lib.qam_group_launch_times(C.byref(g), 4, None, None) == -1
     g.B = 9                   # beyond the staged-limb route
     assert lib.qam_qmatvec_group(C.byref(g), None) == -3
+
+
+def test_group_lens_rejects_before_any_launch(lib):
+    """The launch that builds the maps checks the group, the ladder and the
+    lens rules on the host; every rejection returns before any HIP call."""
+    lens = (L.QamLens * 1)()
+    lens[0].cx, lens[0].cy, lens[0].r = 0.5, 0.5, 0.2
+    p = L.QamLensParams()
+    p.f, p.g, p.combine = 0.5, 1.0, L.QAM_COMBINE_SUM
+    lad = (C.c_uint8 * 5)(0, 2, 4, 6, 8)
+    ladp = C.cast(lad, C.c_void_p)
+    out = (C.c_float * 4)()
+
+    def run(g, n_lenses=1, params=p, ladder=ladp, n_rungs=5, glass=1):
+        return lib.qam_qmatvec_group_lens(C.byref(g) if g is not None else None, lens, n_lenses, C.byref(params),
+                                          ladder, n_rungs, glass, None)
+
+    assert run(None) == -1
+    g = L.QamGroup()                      # zeroed: no table, no map
+    assert run(g) == -1
+    g.table, g.wg_map, g.n_workgroups, g.B = 0x10000000, 0x10001000, 8, 1
+    assert run(g) == -3                   # no coordinates bound
+    g.lens_ready = 1
+    g.route = 1                           # pre-pass route: maps are not built in its launch
+    assert run(g) == -3
+    g.route, g.per_request_maps = 0, 1
+    assert run(g) == -3
+    g.per_request_maps = 0
+    g.B = 3                               # the fused launch serves B <= 2
+    assert run(g) == -3
+    g.B = 1
+    assert run(g, ladder=None) == -1
+    assert run(g, n_rungs=4) == -4        # the product ladder only
+    lad2 = (C.c_uint8 * 5)(0, 2, 4, 6, 10)
+    assert run(g, ladder=C.cast(lad2, C.c_void_p)) == -4
+    assert run(g, glass=5) == -3
+    assert run(g, n_lenses=65) == -3
+    bad = L.QamLensParams()
+    bad.f, bad.g, bad.combine = 1.5, 1.0, L.QAM_COMBINE_SUM
+    assert run(g, params=bad) == -3
+    assert lib.qam_group_lens_launch_times(C.byref(g), lens, 1, C.byref(p), ladp, 5, 1, 0,
+                                           C.cast(out, C.c_void_p), None) == -3
+    assert lib.qam_group_lens_launch_times(C.byref(g), lens, 1, C.byref(p), ladp, 5, 1, 4, None, None) == -1
+    g.lens_ready = 0
+    assert lib.qam_group_lens_launch_times(C.byref(g), lens, 1, C.byref(p), ladp, 5, 1, 4,
+                                           C.cast(out, C.c_void_p), None) == -3

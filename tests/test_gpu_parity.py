@@ -444,6 +444,94 @@ def test_grouped_qmatvec_matches_oracle(qam, B):
         assert np.array_equal(host(it[2]).view(np.uint32), y0.view(np.uint32))
 
 
+def _lens_field(rng, shapes, B, bf16=False):
+    """A small field of matrices with block coordinates and random lenses."""
+    n_blocks = sum(N // 64 for N, _ in shapes)
+    coords = WL.clustered_coords(rng, n_blocks) if n_blocks > 8 else rng.uniform(0, 1, size=(n_blocks, 2))
+    mats = []
+    for N, K in shapes:
+        W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+        sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+        x = rng.standard_normal((B, K)).astype(np.float32)
+        if bf16:
+            x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+        mats.append((W, sc, x))
+    return coords, mats
+
+
+def _lens_group(qam, coords, mats, bf16=False):
+    cd = dev(coords)
+    lv = torch.full((coords.shape[0],), 0xEE, dtype=torch.uint8, device="cuda")   # stale: every rung is written
+    items, o = [], 0
+    for W, sc, x in mats:
+        N = W.shape[0]
+        xt = dev(x).to(torch.bfloat16) if bf16 else dev(x)
+        y = torch.full((x.shape[0], N), float("nan"), device="cuda")
+        items.append((pack(qam, W, sc), xt, y, lv[o:o + N // 64], cd[o:o + N // 64]))
+        o += N // 64
+    return qam.GroupedQmatvec(items), items, lv, cd
+
+
+@pytest.mark.parametrize("B,bf16", [(1, False), (2, False), (1, True)])
+def test_group_lens_builds_the_maps_in_the_launch(qam, B, bf16):
+    """The launch that builds the level maps writes every item's map
+    bit-identical to the oracle's lens rules over the whole field, and its
+    outputs are bit-identical to the map launch followed by the plain grouped
+    product (hence within the tolerance of the oracle)."""
+    rng = np.random.default_rng(500 + B + 10 * bf16)
+    shapes = [(1536, 1536), (6144, 1536), (1536, 6144), (64, 28672), (128, 256), (512, 8960), (192, 64)]
+    coords, mats = _lens_field(rng, shapes, B, bf16)
+    grp, items, lv, cd = _lens_group(qam, coords, mats, bf16)
+    assert grp.route == "staged"
+    for trial, (n_lenses, f, g, combine, glass) in enumerate(
+            [(5, 0.5, 0.75, "sum", 1), (9, 0.35, 1.0, "max", 0), (1, 1.0, 1.0, "sum", 2), (0, 0.5, 1.0, "sum", 3),
+             (64, 0.1, 1.0, "sum", 0), (3, 0.0, 1.0, "sum", 1), (4, 0.6, 0.0, "sum", 2)]):
+        cen = coords[rng.choice(coords.shape[0], n_lenses, replace=False)].copy()
+        rad = rng.uniform(0.02, 0.4, size=n_lenses)
+        if trial == 5:
+            rad[0] = 0.0
+            cen[0] = coords[7]          # radius 0: lifts only the block at its centre
+        rules = qam.LensRules(cen, rad, f, g, combine, glass)
+        want_map = O.level_map(coords, cen, rad, f, g, combine, 5, glass)
+        lv.fill_(0xEE)
+        grp.run_lens(rules)
+        assert "group_lens" in qam.last_variant()
+        assert np.array_equal(host(lv), want_map), trial
+        fused = [host(it[2]).copy() for it in items]
+        lv.fill_(0xEE)
+        qam.build_level_map(cd, cen, rad, f, g, combine, glass, out=lv)
+        grp.run()
+        o = 0
+        for (W, sc, x), it, yf in zip(mats, items, fused):
+            N = W.shape[0]
+            y = host(it[2])
+            assert np.array_equal(y.view(np.uint32), yf.view(np.uint32)), (trial, W.shape)
+            check_y(yf, W, sc, x, want_map[o:o + N // 64], (trial, W.shape))
+            o += N // 64
+
+
+def test_group_lens_needs_coordinates_and_the_staged_route(qam):
+    rng = np.random.default_rng(520)
+    coords, mats = _lens_field(rng, [(256, 512), (128, 256)], 1)
+    cd = dev(coords)
+    lv = torch.zeros(coords.shape[0], dtype=torch.uint8, device="cuda")
+    W, sc, x = mats[0]
+    no_coords = qam.GroupedQmatvec([(pack(qam, W, sc), dev(x), torch.empty((1, 256), device="cuda"), lv[:4])])
+    rules = qam.LensRules(coords[:2], [0.2, 0.3], 0.5, 1.0)
+    with pytest.raises(qam.QamError):
+        no_coords.run_lens(rules)
+    x3 = dev(np.repeat(x, 3, axis=0))
+    pre = qam.GroupedQmatvec([(pack(qam, W, sc), x3, torch.empty((3, 256), device="cuda"), lv[:4], cd[:4])])
+    assert pre.route == "prepass"
+    with pytest.raises(qam.QamError):
+        pre.run_lens(rules)
+    ok = qam.GroupedQmatvec([(pack(qam, W, sc), dev(x), torch.empty((1, 256), device="cuda"), lv[:4], cd[:4])])
+    with pytest.raises(qam.QamError):
+        ok.run_lens(qam.LensRules(coords[:2], [0.2, 0.3], 0.5, 1.0, ladder_bits=(0, 2, 4, 8)))
+    ok.run_lens(rules)
+    assert np.array_equal(host(lv[:4]), O.level_map(coords[:4], coords[:2], [0.2, 0.3], 0.5, 1.0, "sum", 5, 1))
+
+
 def test_graph_replays_match_eager(qam):
     """A captured step (level map + grouped product + a split-K single product)
     replayed several times, with eager work and synchronisations between the
