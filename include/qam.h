@@ -246,8 +246,12 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   per-request maps a block is read once, to the deepest slice any request
  *   needs, and each request gets the codes at its own depth, built from the
  *   same words (the residual slices make the code at depth d the sum of the
- *   first d/2 slices).  Both routes have the arithmetic and bound above (the
- *   pre-pass route's fixed point is per column chunk).
+ *   first d/2 slices): up to 8 requests each slice plane is multiplied by
+ *   every request's limbs and each request adds the planes it reads; above,
+ *   the codes at each depth present are multiplied by the limbs of the
+ *   requests at that depth.  Both sum the same integers.  Both routes have the
+ *   arithmetic and bound above (the pre-pass route's fixed point is per
+ *   column chunk).
  *
  *   x          (device) [B][K] row-major, fp32 (x_dtype QAM_X_F32) or bf16
  *              (QAM_X_BF16); 16-byte aligned.
@@ -353,6 +357,9 @@ typedef struct qam_group {     /* filled by qam_group_init; treat as opaque     
     int64_t n_pre_workgroups;  /* pre-pass route: limb pre-pass workgroups           */
     void*   pre_map;           /* (device) pre-pass workgroup -> item map            */
     int     lens_ready;        /* 1: staged-limb route with every item's coords bound */
+    int     sets;              /* pre-pass route: request sets per workgroup          */
+    int     set_size;          /* pre-pass route: requests per set                    */
+    int     col_groups;        /* pre-pass route: 16-column groups per set            */
 } qam_group;
 
 /* Device bytes qam_group_init needs (0 if the items are invalid).  The route

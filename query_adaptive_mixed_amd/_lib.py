@@ -48,7 +48,7 @@ class QamGroup(C.Structure):
     _fields_ = [("n_items", C.c_int), ("B", C.c_int64), ("x_dtype", C.c_int), ("n_workgroups", C.c_int64),
                 ("lds_bytes", C.c_size_t), ("table", C.c_void_p), ("wg_map", C.c_void_p), ("route", C.c_int),
                 ("per_request_maps", C.c_int), ("n_pre_workgroups", C.c_int64), ("pre_map", C.c_void_p),
-                ("lens_ready", C.c_int)]
+                ("lens_ready", C.c_int), ("sets", C.c_int), ("set_size", C.c_int), ("col_groups", C.c_int)]
 
 
 class QamEpilogue(C.Structure):
@@ -117,6 +117,8 @@ EXTRA_SIGNATURES = [
     ("qam_set_tail_split", _I, [_I, _I]),
     ("qam_set_mfma_tiles_per_request", _I, [_I]),
     ("qam_set_mfma_ksplit", _I, [_I]),
+    ("qam_set_mfma_set_max", _I, [_I]),
+    ("qam_set_mfma_per_slice_max", _I, [_I]),
 ]
 
 

@@ -57,7 +57,8 @@ struct MCommon {
     const int* wg_item;        // grouped launches: item of every product workgroup
     const int* pre_item;       // grouped launches: item of every pre-pass workgroup
     int B;
-    int NH;                    // request sets of 16 per workgroup
+    int NH;                    // request sets per workgroup
+    int SS;                    // requests per set (<= 16; 3 SS limb columns in NCG groups of 16)
     int KS;                    // waves per request set splitting a chunk's tiles
     int NCG;                   // 16-column groups per request set
 };
@@ -72,7 +73,7 @@ __device__ __forceinline__ int depth_of(const MItem& a, int r, int b) {
 // ------------------------------------------------------------------ x -> limbs
 
 // One workgroup of four wavefronts per (column chunk, request slot
-// r < 16 NH): the chunk's largest |x| sets the exponent; slots r >= B get zero
+// r < SS NH): the chunk's largest |x| sets the exponent; slots r >= B get zero
 // limbs.
 constexpr int kPreThreads = 256;
 
@@ -89,8 +90,8 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
         a = single;
         local = (int)blockIdx.x;
     }
-    const int B = c.B, NH = c.NH, NCG = c.NCG;
-    const int slots = 16 * NH;
+    const int B = c.B, NH = c.NH, NCG = c.NCG, SS = c.SS;
+    const int slots = SS * NH;
     const int chunk = local / slots;
     const int r = local % slots;
     const int T = threadIdx.x;
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
     if (T == 0) a.exps[chunk * slots + r] = nonfinite ? kBadExp : e;
     const int sh = kFrac - e;
     const float scale = __uint_as_float((uint32_t)(sh + 127) << 23);   // 2^sh when sh <= 126
-    const int h = r >> 4, rr = r & 15;
+    const int h = r / SS, rr = r % SS;
     uint8_t* lb = reinterpret_cast<uint8_t*>(a.limbs);
     for (int k = 4 * T; k < ncol; k += 4 * kPreThreads) {
         uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
         a = single;
         local = (int)blockIdx.x;
     }
-    const int B = c.B, NH = c.NH, KS = c.KS;
+    const int B = c.B, NH = c.NH, KS = c.KS, SS = c.SS;
     const int chunk = local % a.n_chunks;
     const int b = local / a.n_chunks;
     const int wave = (int)threadIdx.x >> 6;
@@ -326,8 +327,8 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
             for (int r = wave; r < B; r += NH * KS) a.y[(int64_t)r * a.N + (int64_t)b * kRows + L] = 0.0f;
         return;
     }
-    const int m_set = __shfl(m_all, (16 * h + (L & 15)) & 63);   // depth of request 16h + (L & 15)
-    uint32_t dm = (L < 16 && 16 * h + L < B) ? (1u << m_set) : 1u;
+    const int m_set = __shfl(m_all, (SS * h + (L & 15)) & 63);   // depth of request SS h + (L & 15)
+    uint32_t dm = (L < SS && SS * h + L < B) ? (1u << m_set) : 1u;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) dm |= __shfl_xor(dm, o);
     dm = __builtin_amdgcn_readfirstlane(dm);
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
     for (int g = 0; g < NCG; ++g) {
         const int rr = (16 * g + (L & 15)) / 3;                 // request (within the set) owning this column
         const int md = __shfl(m_set, rr & 15);                   // its depth (lane rr holds it)
-        mcol[g] = (rr < 16 && 16 * h + rr < B) ? md : 0;
+        mcol[g] = (rr < SS && SS * h + rr < B) ? md : 0;
     }
     v4i acc[4][NCG];
 #pragma unroll
@@ -366,10 +367,10 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
     // tables (exact integers), then scaled into fp64
     const int row = L;
     const double sc = (double)a.scales[b * kRows + row];
-    const int slots = 16 * NH;
+    const int slots = SS * NH;
     const bool split = a.n_chunks > 1;
     for (int r = wave; r < B; r += NH * KS) {
-        const int hs = r >> 4, c0 = 3 * (r & 15);
+        const int hs = r / SS, c0 = 3 * (r % SS);
         int64_t s0 = 0, s1 = 0, s2 = 0;
         for (int k2 = 0; k2 < KS; ++k2) {
             const int* t2 = tab + (k2 * NH + hs) * 64 * TW + row * TW + c0;
@@ -408,10 +409,226 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
     if (threadIdx.x == 0) __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------------------------ per-slice partials
+
+// Per-request maps, the per-slice form: the masked bytes of slice plane p
+// (digit 3 - p of every code, in place: bits 7-6 as a signed byte, bits 5-4,
+// 3-2 or 1-0 as an unsigned one) add up, over the planes a request reads, to
+// its code at its depth, so P_p = plane p's bytes times every request's limbs
+// needs no masking, and request r's sum is that of P_p over p < d_r(b).  Wave
+// p of a set takes plane p over the chunk's tiles; each plane's partials are
+// exact int32, so the order of the sum does not matter.
+
+template <int NCG>
+struct PRing {
+    static constexpr int H = NCG <= 2 ? 2 : 1;   // tiles per half: 4 + 4 NCG registers each
+    static constexpr int PF = 2 * H;
+};
+
+template <int NCG, int H>
+__device__ __forceinline__ void pload(u32x4 (&w)[H], v4i (&x)[H][NCG], const uint8_t* wbase, const v4i* xbase,
+                                      int64_t xunit, int tile, int last) {
+#pragma unroll
+    for (int u = 0; u < H; ++u) {
+        const int t = min(tile + u, last);
+        w[u] = load_plane(wbase + (int64_t)t * kTileBytes);
+#pragma unroll
+        for (int g = 0; g < NCG; ++g) x[u][g] = *(global_v4i*)(xbase + t * xunit + g * 64);
+    }
+}
+
+template <int P, int NCG>
+__device__ __forceinline__ void ptile(const u32x4& w, const v4i (&xl)[NCG], v4i (&acc)[4][NCG]) {
+    const uint32_t wj[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const v4i A = v4i{(int)(wj[j] & slice_mask(3 - P, 0)), (int)rotl32(wj[j] & slice_mask(3 - P, 1), 2),
+                          (int)rotl32(wj[j] & slice_mask(3 - P, 2), 4), (int)rotl32(wj[j] & slice_mask(3 - P, 3), 6)};
+#pragma unroll
+        for (int g = 0; g < NCG; ++g) acc[j][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, xl[g], acc[j][g], 0, 0, 0);
+    }
+}
+
+// Plane P of block b over the chunk's tiles, for request set h.
+template <int P, int NCG>
+__device__ __forceinline__ void pproduct(const MItem& a, int NH, int b, int chunk, int h, int L, v4i (&acc)[4][NCG]) {
+    constexpr int H = PRing<NCG>::H;
+    constexpr int PF = PRing<NCG>::PF;
+    const int t0 = chunk * a.tpc;
+    const int nt = min(a.tpc, a.n_tiles - t0);
+    const int last = nt - 1;
+    const uint8_t* wbase = a.planes + (int64_t)P * a.plane_bytes + (int64_t)b * 16 * a.K + (int64_t)t0 * kTileBytes +
+                           L * 16;
+    const int64_t xunit = (int64_t)NH * NCG * 64;
+    const v4i* xbase = a.limbs + (int64_t)t0 * xunit + (int64_t)h * NCG * 64 + L;
+    __builtin_amdgcn_s_waitcnt(0);
+    u32x4 wa[H], wb[H];
+    v4i xa[H][NCG], xb[H][NCG];
+    pload<NCG, H>(wa, xa, wbase, xbase, xunit, 0, last);
+    __builtin_amdgcn_sched_barrier(0);
+    pload<NCG, H>(wb, xb, wbase, xbase, xunit, H, last);
+    __builtin_amdgcn_sched_barrier(0);
+    int t = 0;
+    for (; t + PF < nt; t += PF) {
+#pragma unroll
+        for (int u = 0; u < H; ++u) ptile<P, NCG>(wa[u], xa[u], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        pload<NCG, H>(wa, xa, wbase, xbase, xunit, t + PF, last);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < H; ++u) ptile<P, NCG>(wb[u], xb[u], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        pload<NCG, H>(wb, xb, wbase, xbase, xunit, t + PF + H, last);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // the last ring: tiles past the chunk were loaded (clamped) and are multiplied by zero limbs
+#pragma unroll
+    for (int u = 0; u < H; ++u) {
+        v4i z[NCG];
+#pragma unroll
+        for (int g = 0; g < NCG; ++g) z[g] = t + u < nt ? xa[u][g] : v4i{0, 0, 0, 0};
+        ptile<P, NCG>(wa[u], z, acc);
+    }
+#pragma unroll
+    for (int u = 0; u < H; ++u) {
+        v4i z[NCG];
+#pragma unroll
+        for (int g = 0; g < NCG; ++g) z[g] = t + H + u < nt ? xb[u][g] : v4i{0, 0, 0, 0};
+        ptile<P, NCG>(wb[u], z, acc);
+    }
+}
+
+// One workgroup = 4 NH wavefronts = one (block, column chunk); wave 4h + p
+// takes plane p for request set h.  Each wave keeps only the columns of the
+// requests that read its plane and adds them into the set's table (LDS
+// integer adds: exact, in any order); then one row per lane, as in qmm_kernel.
+template <int NCG, bool GROUPED>
+__global__ __launch_bounds__(512) void qmm_plane_kernel(MItem single, MCommon c) {
+    extern __shared__ int tab[];   // [NH][64 rows][16 NCG + 1] integer sums, then one flag
+    constexpr int TW = 16 * NCG + 1;
+    MItem a;
+    int local;
+    if constexpr (GROUPED) {
+        a = c.items[c.wg_item[blockIdx.x]];
+        local = (int)blockIdx.x - a.wg_begin;
+    } else {
+        a = single;
+        local = (int)blockIdx.x;
+    }
+    const int B = c.B, NH = c.NH, SS = c.SS;
+    const int chunk = local % a.n_chunks;
+    const int b = local / a.n_chunks;
+    const int wave = (int)threadIdx.x >> 6;
+    const int p = wave & 3;
+    const int h = wave >> 2;
+    const int L = (int)threadIdx.x & 63;
+    const int nw = 4 * NH;
+
+    const int m_all = L < B ? depth_of<true>(a, L, b) : 0;   // slices request L reads
+    int dmax = m_all;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) dmax = max(dmax, __shfl_xor(dmax, o));
+    dmax = __builtin_amdgcn_readfirstlane(dmax);
+    if (dmax == 0) {   // no request reads any of the block: y = 0, written once, by the first chunk
+        if (chunk == 0)
+            for (int r = wave; r < B; r += nw) a.y[(int64_t)r * a.N + (int64_t)b * kRows + L] = 0.0f;
+        return;
+    }
+    // deepest read in this wave's set, and whether the request owning each of
+    // this lane's columns reads plane p
+    const int m_set = __shfl(m_all, (SS * h + (L & 15)) & 63);
+    int dset = (L < SS && SS * h + L < B) ? m_set : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) dset = max(dset, __shfl_xor(dset, o));
+    dset = __builtin_amdgcn_readfirstlane(dset);
+    bool keep[NCG];
+#pragma unroll
+    for (int g = 0; g < NCG; ++g) {
+        const int rr = (16 * g + (L & 15)) / 3;
+        const int md = __shfl(m_set, rr & 15);
+        keep[g] = rr < SS && SS * h + rr < B && md > p;
+    }
+    for (int i = (int)threadIdx.x; i < NH * 64 * TW; i += (int)blockDim.x) tab[i] = 0;
+    v4i acc[4][NCG];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < NCG; ++g) acc[j][g] = v4i{0, 0, 0, 0};
+    if (p < dset) {
+        switch (p) {
+            case 0: pproduct<0, NCG>(a, NH, b, chunk, h, L, acc); break;
+            case 1: pproduct<1, NCG>(a, NH, b, chunk, h, L, acc); break;
+            case 2: pproduct<2, NCG>(a, NH, b, chunk, h, L, acc); break;
+            default: pproduct<3, NCG>(a, NH, b, chunk, h, L, acc); break;
+        }
+    }
+    __syncthreads();   // the tables are clear
+    if (p < dset) {
+        int* mine = tab + h * 64 * TW;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < NCG; ++g)
+                if (keep[g])
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        atomicAdd(&mine[(16 * j + 4 * (L >> 4) + i) * TW + 16 * g + (L & 15)], acc[j][g][i]);
+    }
+    __syncthreads();
+
+    const int row = L;
+    const double sc = (double)a.scales[b * kRows + row];
+    const int slots = SS * NH;
+    const bool split = a.n_chunks > 1;
+    for (int r = wave; r < B; r += nw) {
+        const int* t2 = tab + (r / SS) * 64 * TW + row * TW + 3 * (r % SS);
+        const double d = (double)t2[2] * 65536.0 + (double)t2[1] * 256.0 + (double)t2[0];
+        const int e = a.exps[chunk * slots + r];
+        const int mr = __shfl(m_all, r & 63);
+        const double v = mr == 0 ? 0.0 : (e == kBadExp ? __builtin_nan("") : ldexp(d, e - kFrac));
+        if (!split)
+            a.y[(int64_t)r * a.N + (int64_t)b * kRows + row] = (float)(sc * v);
+        else
+            __hip_atomic_store(&a.partials[((int64_t)chunk * B + r) * a.N + (int64_t)b * kRows + row], v,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!split) return;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int* flag = tab + NH * 64 * TW;
+    if (threadIdx.x == 0)
+        *flag = (int)__hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*flag != a.n_chunks - 1) return;
+    for (int r = wave; r < B; r += nw) {
+        double sum = 0.0;
+        for (int cc = 0; cc < a.n_chunks; ++cc)
+            sum += __hip_atomic_load(&a.partials[((int64_t)cc * B + r) * a.N + (int64_t)b * kRows + row],
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        a.y[(int64_t)r * a.N + (int64_t)b * kRows + row] = (float)(sc * sum);
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------------ host side
+
+// Per-request maps take the per-slice form up to this many requests, the
+// per-depth form above (measured on the batched layer: per-slice 42 / 50 /
+// 57 us at 4 / 8 / 16 requests against per-depth 56 / 59 / 56 us, and
+// 108 us against 84 us at 32 requests, where the two sets' eight waves share
+// one workgroup).
+static int g_mfma_per_slice_max = 8;
+
+
+static bool per_slice_form(int64_t B, bool per_req, int NH) { return per_req && B <= g_mfma_per_slice_max && NH <= 2; }
 
 template <int NCG, bool GROUPED>
 static void launch_product(const MItem& it, const MCommon& c, bool per_req, int64_t grid, hipStream_t s) {
+    if (per_slice_form(c.B, per_req, c.NH)) {
+        const size_t lds = ((size_t)c.NH * 64 * (16 * NCG + 1) + 4) * sizeof(int);
+        hipLaunchKernelGGL((qmm_plane_kernel<NCG, GROUPED>), dim3((unsigned)grid), dim3(256 * c.NH), lds, s, it, c);
+        return;
+    }
     const dim3 blk(64 * c.NH * c.KS);
     const size_t lds = ((size_t)c.KS * c.NH * 64 * (16 * NCG + 1) + 4) * sizeof(int);
     if (per_req)
@@ -435,7 +652,7 @@ static void launch_mfma(const MItem& it, const MCommon& c, bool xbf16, bool per_
 }
 
 struct MPlan {
-    int NH, NCG, KS, tpc, n_chunks;
+    int NH, SS, NCG, KS, tpc, n_chunks;
     size_t counters, partials, limbs, exps, total;
 };
 
@@ -447,9 +664,14 @@ static int g_mfma_tiles_per_request = 2;
 // Waves per request group splitting each chunk's tiles inside a workgroup.
 static int g_mfma_ksplit = 2;
 
-static int mfma_sets(int64_t B) { return B > 16 ? 2 : 1; }
-// 16-column groups per set of up to 16 requests (three limb columns each)
-static int mfma_ncg(int64_t B) { return (int)((3 * std::min<int64_t>(B, 16) + 15) / 16); }
+// Most requests per set (three limb columns each, in 16-column groups).
+static int g_mfma_set_max = 0;   // 0: the default below; else 8..16
+static int mfma_set_max(int64_t) { return g_mfma_set_max ? g_mfma_set_max : 16; }
+// request sets, as even as possible
+static int mfma_sets(int64_t B) { return (int)((B + mfma_set_max(B) - 1) / mfma_set_max(B)); }
+static int mfma_ss(int64_t B) { return (int)((B + mfma_sets(B) - 1) / mfma_sets(B)); }
+// 16-column groups per set (three limb columns per request)
+static int mfma_ncg(int64_t B) { return (3 * mfma_ss(B) + 15) / 16; }
 // waves per set splitting a chunk: at most four waves per workgroup
 static int mfma_ks(int64_t B) { return std::max(1, std::min(g_mfma_ksplit, 4 / mfma_sets(B))); }
 
@@ -457,6 +679,7 @@ static int mfma_ks(int64_t B) { return std::max(1, std::min(g_mfma_ksplit, 4 / m
 static MPlan mplan_goal(int64_t N, int64_t K, int64_t B, int goal) {
     MPlan p{};
     p.NH = mfma_sets(B);
+    p.SS = mfma_ss(B);
     p.NCG = mfma_ncg(B);
     p.KS = mfma_ks(B);
     const int n_tiles = (int)(K / kTileCols);
@@ -471,7 +694,7 @@ static MPlan mplan_goal(int64_t N, int64_t K, int64_t B, int goal) {
     p.counters = QAM_WS_COUNTER_BYTES;
     p.partials = p.n_chunks > 1 ? up((size_t)p.n_chunks * B * N * sizeof(double)) : 0;
     p.limbs = up((size_t)n_tiles * p.NH * p.NCG * 64 * 16);
-    p.exps = up((size_t)p.n_chunks * 16 * p.NH * sizeof(int));
+    p.exps = up((size_t)p.n_chunks * p.SS * p.NH * sizeof(int));
     p.total = p.counters + p.partials + p.limbs + p.exps;
     return p;
 }
@@ -523,14 +746,16 @@ int qmatvec_mfma(const void* x, int x_dtype, int64_t B, const qam_packed* packed
     MCommon c{};
     c.B = (int)B;
     c.NH = p.NH;
+    c.SS = p.SS;
     c.KS = p.KS;
     c.NCG = p.NCG;
-    launch_mfma<false>(it, c, x_dtype == QAM_X_BF16, per_request_maps != 0, (int64_t)p.n_chunks * 16 * p.NH,
+    launch_mfma<false>(it, c, x_dtype == QAM_X_BF16, per_request_maps != 0, (int64_t)p.n_chunks * p.SS * p.NH,
                        (int64_t)it.n_blocks * p.n_chunks, s);
     QAM_HIP_CHECK(hipGetLastError());
     char v[128];
-    snprintf(v, sizeof(v), "qmatvec_mfma B=%lld maps=%s tpc=%d chunks=%d sets=%d colgroups=%d ksplit=%d", (long long)B,
-             per_request_maps ? "per-request" : "shared", p.tpc, p.n_chunks, p.NH, p.NCG, p.KS);
+    snprintf(v, sizeof(v), "qmatvec_mfma B=%lld maps=%s form=%s tpc=%d chunks=%d sets=%d colgroups=%d ksplit=%d",
+             (long long)B, per_request_maps ? "per-request" : "shared",
+             per_slice_form(B, per_request_maps != 0, p.NH) ? "slice" : "depth", p.tpc, p.n_chunks, p.NH, p.NCG, p.KS);
     set_variant(v);
     return QAM_OK;
 }
@@ -541,13 +766,14 @@ struct MGroupLayout {
     std::vector<MPlan> plans;
     size_t partials = 0, limbs = 0, exps = 0, table = 0, wgmap = 0, premap = 0, total = 0;
     int64_t n_wg = 0, n_pre = 0, blocks = 0;
-    int NH = 1, NCG = 1, KS = 1;
+    int NH = 1, SS = 16, NCG = 1, KS = 1;
 };
 
 static int mfma_layout(const qam_gemv_item* items, int n_items, int64_t B, MGroupLayout& g) {
     if (!items || n_items < 1) QAM_FAIL(QAM_ERR_ARG, "group: need at least one item");
     if (B < 2 || B > QAM_MAX_BATCH_MFMA) QAM_FAIL(QAM_ERR_ARG, "group: B=%lld outside [2, %d]", (long long)B, QAM_MAX_BATCH_MFMA);
     g.NH = mfma_sets(B);
+    g.SS = mfma_ss(B);
     g.NCG = mfma_ncg(B);
     g.KS = mfma_ks(B);
     int64_t block_tiles = 0;
@@ -567,7 +793,7 @@ static int mfma_layout(const qam_gemv_item* items, int n_items, int64_t B, MGrou
         g.limbs += p.limbs;
         g.exps += p.exps;
         g.n_wg += (int64_t)(items[i].w.N / kRows) * p.n_chunks;
-        g.n_pre += (int64_t)p.n_chunks * 16 * g.NH;
+        g.n_pre += (int64_t)p.n_chunks * g.SS * g.NH;
     }
     if (g.n_wg > 0x7FFFFFFF || g.n_pre > 0x7FFFFFFF) QAM_FAIL(QAM_ERR_SHAPE, "group: too many workgroups");
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
@@ -622,7 +848,7 @@ int mfma_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dt
         const int64_t n = (int64_t)it.n_blocks * p.n_chunks;
         for (int64_t k = 0; k < n; ++k) hw[(size_t)(wg + k)] = i;
         wg += n;
-        const int64_t np = (int64_t)p.n_chunks * 16 * g.NH;
+        const int64_t np = (int64_t)p.n_chunks * g.SS * g.NH;
         for (int64_t k = 0; k < np; ++k) hp[(size_t)(pre + k)] = i;
         pre += np;
         host_items[i] = it;
@@ -644,30 +870,53 @@ int mfma_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dt
     out->n_pre_workgroups = g.n_pre;
     out->pre_map = premap;
     out->lens_ready = 0;
+    out->sets = g.NH;
+    out->set_size = g.SS;
+    out->col_groups = g.NCG;
     return QAM_OK;
 }
 
 int mfma_group_run(const qam_group* g, hipStream_t s) {
+    if (g->sets < 1 || g->sets > 4 || g->set_size < 1 || g->set_size > 16 || (int64_t)g->sets * g->set_size < g->B ||
+        g->col_groups < 1 || g->col_groups > 3 || 3 * g->set_size > 16 * g->col_groups)
+        QAM_FAIL(QAM_ERR_ARG, "qmatvec_group: corrupt group descriptor");
     MCommon c{};
     c.items = static_cast<const MItem*>(g->table);
     c.wg_item = static_cast<const int*>(g->wg_map);
     c.pre_item = static_cast<const int*>(g->pre_map);
     c.B = (int)g->B;
-    c.NH = mfma_sets(g->B);
-    c.KS = mfma_ks(g->B);
-    c.NCG = mfma_ncg(g->B);
+    c.NH = g->sets;
+    c.SS = g->set_size;
+    c.NCG = g->col_groups;
+    c.KS = std::max(1, std::min(g_mfma_ksplit, 4 / c.NH));
     MItem dummy{};
     launch_mfma<true>(dummy, c, g->x_dtype == QAM_X_BF16, g->per_request_maps != 0, g->n_pre_workgroups,
                       g->n_workgroups, s);
     QAM_HIP_CHECK(hipGetLastError());
     char v[128];
-    snprintf(v, sizeof(v), "qmatvec_mfma_group items=%d B=%lld maps=%s wg=%lld", g->n_items, (long long)g->B,
-             g->per_request_maps ? "per-request" : "shared", (long long)g->n_workgroups);
+    snprintf(v, sizeof(v), "qmatvec_mfma_group items=%d B=%lld maps=%s form=%s wg=%lld", g->n_items, (long long)g->B,
+             g->per_request_maps ? "per-request" : "shared",
+             per_slice_form(g->B, g->per_request_maps != 0, g->sets) ? "slice" : "depth", (long long)g->n_workgroups);
     set_variant(v);
     return QAM_OK;
 }
 
 }  // namespace qam
+
+extern "C" int qam_set_mfma_per_slice_max(int b) {
+    qam::clear_error();
+    if (b < 0 || b > QAM_MAX_BATCH_MFMA) QAM_FAIL(QAM_ERR_ARG, "set_mfma_per_slice_max: %d outside [0, %d]", b,
+                                                  QAM_MAX_BATCH_MFMA);
+    qam::g_mfma_per_slice_max = b;
+    return QAM_OK;
+}
+
+extern "C" int qam_set_mfma_set_max(int n) {
+    qam::clear_error();
+    if (n != 0 && (n < 8 || n > 16)) QAM_FAIL(QAM_ERR_ARG, "set_mfma_set_max: %d not 0 or in [8, 16]", n);
+    qam::g_mfma_set_max = n;
+    return QAM_OK;
+}
 
 extern "C" int qam_set_mfma_ksplit(int ks) {
     qam::clear_error();
