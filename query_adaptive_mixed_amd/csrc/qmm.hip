@@ -614,10 +614,10 @@ __global__ __launch_bounds__(512) void qmm_plane_kernel(MItem single, MCommon c)
 
 // Per-request maps take the per-slice form up to this many requests, the
 // per-depth form above (measured on the batched layer: per-slice 42 / 50 /
-// 57 us at 4 / 8 / 16 requests against per-depth 56 / 59 / 56 us, and
-// 108 us against 84 us at 32 requests, where the two sets' eight waves share
-// one workgroup).
-static int g_mfma_per_slice_max = 8;
+// 60 / 57 us at 4 / 8 / 12 / 16 requests against per-depth 56 / 59 / 67 /
+// 56 us, and 108 us against 84 us at 32 requests, where the two sets' eight
+// waves share one workgroup).
+static int g_mfma_per_slice_max = 12;
 
 
 static bool per_slice_form(int64_t B, bool per_req, int NH) { return per_req && B <= g_mfma_per_slice_max && NH <= 2; }
