@@ -25,6 +25,8 @@ from .qam_oracle import (  # noqa: F401
     qmatvec_tolerance,
     escalation_schedule,
     escalation_byte_ratio,
+    uncertainty,
+    gate,
     rmsnorm_ref,
     silu_mul_ref,
 )

@@ -334,6 +334,53 @@ def escalation_schedule(scores, rate: float) -> np.ndarray:
     return mask
 
 
+def uncertainty(logits):
+    """Entropy and top-two margin of the low pass's output distribution
+    ([PoD] abstract: a step is redone at 8 bits when the low-precision output
+    distribution looks uncertain, entropy above a threshold or a small
+    top-two margin).
+
+    Readings taken where the abstract is open: the distribution is the
+    softmax of the logits, p_i = exp(z_i) / sum_j exp(z_j), evaluated in fp64
+    as exp(z_i - max z) / sum; the entropy is in nats, H = -sum_i p_i ln p_i
+    with 0 ln 0 = 0 (a logit of -inf is a token of probability 0); the
+    margin is between the two largest probabilities, p_(1) - p_(2), the top
+    two taken by value, ties to the lower index.  Logits holding a NaN or a
+    +inf, or all -inf, give no distribution: entropy and margin are NaN.
+
+    Returns dict(entropy, margin, top1, top2, p1, p2).
+    """
+    z = np.asarray(logits, dtype=np.float64).reshape(-1)
+    V = z.shape[0]
+    if V < 2:
+        raise ValueError("need at least two logits")
+    order = np.lexsort((np.arange(V), -z))         # by value, descending; ties to the lower index
+    top1, top2 = int(order[0]), int(order[1])
+    if np.any(np.isnan(z)) or np.any(z == np.inf) or np.all(z == -np.inf):
+        nan = float("nan")
+        return dict(entropy=nan, margin=nan, top1=top1, top2=top2, p1=nan, p2=nan)
+    m = z.max()
+    e = np.exp(z - m)
+    p = e / np.sum(e)
+    plogp = np.zeros(V)
+    nz = p > 0.0
+    plogp[nz] = p[nz] * np.log(p[nz])
+    H = -np.sum(plogp)
+    return dict(entropy=float(H), margin=float(p[top1] - p[top2]), top1=top1, top2=top2,
+                p1=float(p[top1]), p2=float(p[top2]))
+
+
+def gate(logits, tau_entropy: float, tau_margin: float) -> bool:
+    """The escalation gate ([PoD] abstract): redo the step when the entropy
+    exceeds ``tau_entropy`` or the top-two margin falls below ``tau_margin``
+    (+inf / -inf switch either test off).  No distribution (NaN) escalates."""
+    u = uncertainty(logits)
+    H, mg = u["entropy"], u["margin"]
+    if np.isnan(H):
+        return True
+    return bool(H > tau_entropy or mg < tau_margin)
+
+
 def escalation_byte_ratio(mask, low_bits: int = 4, high_bits: int = 8) -> float:
     """Weight bytes read by the gated schedule over the all-high schedule.
 

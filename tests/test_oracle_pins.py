@@ -386,3 +386,80 @@ def test_generators_are_seeded_and_shaped():
     assert WL.qwen_decode_field(0).n_blocks == 7750
     assert WL.batched_layer(0).n_blocks == 352
     assert WL.streaming_stack(0).n_blocks == 4608 and WL.streaming_stack(0).n_weights == 3_758_096_384
+
+
+# ---------------------------------------------------------------- the escalation gate's uncertainty
+
+def test_uncertainty_closed_forms():
+    """Uniform logits: H = ln V and margin 0; two logits a, b: the binary
+    entropy of q = 1 / (1 + e^(b - a)); one logit L above V - 1 zeros: the
+    two-level entropy; every case written from its closed form, not the
+    oracle's formula."""
+    for V in (2, 7, 151936):
+        u = O.uncertainty(np.full(V, 3.25))
+        assert abs(u["entropy"] - math.log(V)) <= 1e-12 * math.log(V)
+        assert u["margin"] == 0.0 and (u["top1"], u["top2"]) == (0, 1)
+    for a, b in ((0.0, 0.0), (2.0, -1.0), (-5.5, 7.25), (30.0, 0.0)):
+        q = 1.0 / (1.0 + math.exp(b - a))
+        want = -(q * math.log(q) + (1.0 - q) * math.log1p(-q)) if 0.0 < q < 1.0 else 0.0
+        u = O.uncertainty([a, b])
+        assert abs(u["entropy"] - want) <= 1e-12, (a, b)
+        assert abs(u["margin"] - abs(2.0 * q - 1.0)) <= 1e-12
+    V, L = 1000, 6.0
+    d = math.exp(L) + (V - 1)
+    p1, po = math.exp(L) / d, 1.0 / d
+    want = -(p1 * math.log(p1) + (V - 1) * po * math.log(po))
+    z = np.zeros(V)
+    z[417] = L
+    u = O.uncertainty(z)
+    assert abs(u["entropy"] - want) <= 1e-12 and abs(u["margin"] - (p1 - po)) <= 1e-12
+    assert (u["top1"], u["top2"]) == (417, 0)
+
+
+def test_uncertainty_against_scipy_and_invariants():
+    """Random logits: entropy equals scipy's entropy of scipy's softmax;
+    shifting or permuting the logits changes nothing; -inf logits are tokens
+    of probability 0 (the same as leaving them out)."""
+    from scipy.special import softmax
+    from scipy.stats import entropy
+    rng = np.random.default_rng(31)
+    for V in (3, 100, 5000):
+        z = rng.standard_normal(V) * rng.uniform(0.1, 8.0)
+        u = O.uncertainty(z)
+        assert abs(u["entropy"] - entropy(softmax(z))) <= 1e-10
+        p = np.sort(softmax(z))[::-1]
+        assert abs(u["margin"] - (p[0] - p[1])) <= 1e-12
+        assert 0.0 <= u["entropy"] <= math.log(V) + 1e-12 and 0.0 <= u["margin"] <= 1.0
+        us = O.uncertainty(z + 123.5)
+        assert abs(us["entropy"] - u["entropy"]) <= 1e-10 and abs(us["margin"] - u["margin"]) <= 1e-12
+        perm = rng.permutation(V)
+        up = O.uncertainty(z[perm])
+        assert abs(up["entropy"] - u["entropy"]) <= 1e-10
+        assert perm[up["top1"]] == u["top1"]
+        zi = np.concatenate([z, np.full(17, -np.inf)])
+        ui = O.uncertainty(zi)
+        assert abs(ui["entropy"] - u["entropy"]) <= 1e-12 and ui["top1"] == u["top1"]
+
+
+def test_uncertainty_ties_and_no_distribution():
+    z = np.array([1.0, 4.0, 2.0, 4.0, 4.0])
+    u = O.uncertainty(z)
+    assert (u["top1"], u["top2"]) == (1, 3) and u["margin"] == 0.0
+    for bad in ([0.0, np.nan, 1.0], [0.0, np.inf], [-np.inf, -np.inf]):
+        u = O.uncertainty(bad)
+        assert math.isnan(u["entropy"]) and math.isnan(u["margin"])
+        assert O.gate(bad, 10.0, -1.0)
+
+
+def test_gate_rules():
+    """Entropy above its threshold, or margin below its threshold, escalates;
+    +inf / -inf thresholds switch a test off."""
+    sharp = np.zeros(50)
+    sharp[3] = 20.0                      # H ~ 0, margin ~ 1
+    flat = np.zeros(50)                  # H = ln 50, margin 0
+    assert not O.gate(sharp, 1.0, 0.1)
+    assert O.gate(flat, 1.0, 0.1)
+    assert O.gate(flat, math.inf, 0.1)           # the margin alone
+    assert O.gate(flat, 1.0, -math.inf)          # the entropy alone
+    assert not O.gate(flat, math.inf, -math.inf)
+    assert not O.gate(flat, math.log(50) + 1e-9, -math.inf)
