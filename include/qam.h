@@ -502,6 +502,39 @@ void qam_decoder_destroy(qam_decoder* dec);
 int qam_escalation_schedule(const double* scores, int64_t T, double rate, uint8_t* escalate_out,
                             int64_t* n_out);
 
+/*
+ * qam_gate -- the escalation gate on the device ([PoD] abstract: a step is
+ *   redone at 8 bits when the low-precision output distribution looks
+ *   uncertain, entropy above a threshold or a small top-two margin).  Over
+ *   the V logits z of the low pass, in fp64: p = softmax(z); entropy
+ *   H = -sum p ln p in nats (0 ln 0 = 0: a -inf logit is a token of
+ *   probability 0); margin = p_(1) - p_(2), the two largest probabilities
+ *   (ties to the lower index).  escalate = H > tau_entropy or
+ *   margin < tau_margin (+inf / -inf switch a test off).  Logits holding a
+ *   NaN or +inf, or all -inf, give no distribution: H, margin, p1 and p2
+ *   are NaN and escalate = 1.  One launch; the partials of its workgroups
+ *   are merged in a fixed order, so the result is the same bits on every
+ *   call (within ~1e-12 of the same formulas evaluated in fp64 on a CPU).
+ *   logits     (device) fp32 [V], V >= 2.
+ *   out        (device) one qam_uncertainty, written by the launch.
+ *   workspace  (device) qam_gate_workspace_bytes(V) bytes, 256-byte aligned,
+ *              zero-filled before its first use; every call leaves its
+ *              counter at zero again.  Calls sharing a workspace must be
+ *              ordered.
+ */
+typedef struct qam_uncertainty {
+    double  entropy;     /* nats                                       */
+    double  margin;      /* p1 - p2                                    */
+    double  p1, p2;      /* the two largest probabilities              */
+    int64_t top1, top2;  /* their token indices                        */
+    int32_t escalate;    /* 1: redo the step at the high depth         */
+    int32_t reserved;
+} qam_uncertainty;
+
+size_t qam_gate_workspace_bytes(int64_t V);
+int qam_gate(const float* logits, int64_t V, double tau_entropy, double tau_margin,
+             qam_uncertainty* out, void* workspace, size_t workspace_bytes, hipStream_t s);
+
 /* ---------------------------------------------------------------- diagnostics */
 const char* qam_last_error(void);     /* thread-local, "" if none           */
 const char* qam_last_variant(void);   /* kernel variant of the last call     */

@@ -10,6 +10,7 @@ loudly if the library is missing.
 from .api import (  # noqa: F401
     LADDER_BITS,
     Decoder,
+    Gate,
     GroupedQmatvec,
     LensRules,
     PackedMatrix,

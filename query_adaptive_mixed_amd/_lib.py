@@ -51,6 +51,11 @@ class QamGroup(C.Structure):
                 ("lens_ready", C.c_int), ("sets", C.c_int), ("set_size", C.c_int), ("col_groups", C.c_int)]
 
 
+class QamUncertainty(C.Structure):
+    _fields_ = [("entropy", C.c_double), ("margin", C.c_double), ("p1", C.c_double), ("p2", C.c_double),
+                ("top1", C.c_int64), ("top2", C.c_int64), ("escalate", C.c_int32), ("reserved", C.c_int32)]
+
+
 class QamEpilogue(C.Structure):
     _fields_ = [("rms_norm", C.c_int), ("out_mode", C.c_int), ("eps", C.c_double)]
 
@@ -100,6 +105,8 @@ SIGNATURES = [
     ("qam_qmatvec_group", _I, [C.POINTER(QamGroup), _P]),
     ("qam_qmatvec_group_lens", _I, [C.POINTER(QamGroup), C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I,
                                     _I, _P]),
+    ("qam_gate_workspace_bytes", C.c_size_t, [_I64]),
+    ("qam_gate", _I, [_P, _I64, C.c_double, C.c_double, _P, _P, _SZ, _P]),
     ("qam_last_error", C.c_char_p, []),
     ("qam_last_variant", C.c_char_p, []),
     ("qam_version", C.c_char_p, []),

@@ -349,6 +349,35 @@ class GroupedQmatvec:
                                                rules.n_rungs, rules.glass, _stream_handle()))
 
 
+class Gate:
+    """The escalation gate on the device: softmax entropy (nats) and top-two
+    margin of a logits vector of length ``V``, and the decision
+    entropy > tau_entropy or margin < tau_margin; one launch per ``run``.
+    ``result()`` copies the outcome to the host (a synchronisation)."""
+
+    def __init__(self, V: int, device="cuda"):
+        n = int(L.lib().qam_gate_workspace_bytes(int(V)))
+        if n == 0:
+            raise ValueError("the gate needs at least two logits")
+        self.V = int(V)
+        self.ws = torch.zeros(n, dtype=torch.uint8, device=device)
+        self.out = torch.zeros(C.sizeof(L.QamUncertainty), dtype=torch.uint8, device=device)
+
+    def run(self, logits: torch.Tensor, tau_entropy: float = float("inf"),
+            tau_margin: float = float("-inf")) -> None:
+        _require_cuda(logits, "logits", torch.float32)
+        if logits.numel() != self.V:
+            raise ValueError(f"logits must hold {self.V} values")
+        L.check(L.lib().qam_gate(_ptr(logits), self.V, float(tau_entropy), float(tau_margin), _ptr(self.out),
+                                 _ptr(self.ws), self.ws.numel(), _stream_handle()))
+
+    def result(self) -> dict:
+        raw = self.out.cpu().numpy().tobytes()
+        u = L.QamUncertainty.from_buffer_copy(raw)
+        return dict(entropy=u.entropy, margin=u.margin, p1=u.p1, p2=u.p2, top1=int(u.top1), top2=int(u.top2),
+                    escalate=bool(u.escalate))
+
+
 class Decoder:
     """A decode step as a chain of fused mixed-depth products (libqam's decoder).
 

@@ -1,0 +1,231 @@
+// The escalation gate on the device: entropy and top-two margin of the low
+// pass's output distribution ("Precision on Demand: Escalating Weight Bits at
+// Uncertain Decoding Steps in a Small Local Model", abstract: redo a step at
+// 8 bits when the low-precision output looks uncertain, entropy above a
+// threshold or a small top-two margin).
+//
+// With m = max z, e_i = exp(z_i - m), S = sum e_i and T = sum e_i (z_i - m),
+// the softmax entropy -sum p ln p is ln S - T / S, and the largest
+// probability is 1 / S.  Each workgroup reduces its slice of the logits to
+// (m_g, S_g, T_g, its top two) relative to its own maximum; the last
+// workgroup to finish rescales them to the global maximum, in slice order,
+// and writes the result.  Every sum has a fixed order, so the result is the
+// same bits on every call.
+#include <math.h>
+
+#include "qam_common.h"
+
+namespace qam {
+
+constexpr int kGateThreads = 256;
+constexpr int kGateMaxGroups = 256;
+constexpr int64_t kGatePerGroup = 4096;   // logits per workgroup (fewer groups for short vectors)
+
+struct GatePartial {
+    double m, S, T;        // max of the slice, sum of exp(z - m), sum of exp(z - m) (z - m)
+    float v1, v2;          // the slice's two largest logits ...
+    int64_t i1, i2;        // ... and their indices (ties to the lower index)
+    int32_t bad;           // a NaN or +inf in the slice
+    int32_t pad;
+};
+
+static_assert(sizeof(GatePartial) == 56, "partial layout");
+
+// (v, i) ranks ahead of (w, j): larger value, or equal value and lower index.
+__device__ __forceinline__ bool ahead(float v, int64_t i, float w, int64_t j) { return v > w || (v == w && i < j); }
+
+// Merge the top two (a1, a2) with (b1, b2) into (a1, a2).
+__device__ __forceinline__ void merge2(float& a1, int64_t& ai1, float& a2, int64_t& ai2, float b1, int64_t bi1,
+                                       float b2, int64_t bi2) {
+    if (ahead(b1, bi1, a1, ai1)) {
+        // b1 leads; the runner-up is the better of a1 and b2
+        if (ahead(a1, ai1, b2, bi2)) {
+            a2 = a1;
+            ai2 = ai1;
+        } else {
+            a2 = b2;
+            ai2 = bi2;
+        }
+        a1 = b1;
+        ai1 = bi1;
+    } else if (ahead(b1, bi1, a2, ai2)) {
+        a2 = b1;
+        ai2 = bi1;
+    }
+}
+
+// Sum over the workgroup in a fixed tree order; every thread gets the sum.
+__device__ __forceinline__ double block_sum(double v, double* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    double s = red[0];
+    for (int k = 1; k < kGateThreads / 64; ++k) s += red[k];
+    return s;
+}
+
+__global__ __launch_bounds__(kGateThreads) void gate_kernel(const float* __restrict__ z, int64_t V, int64_t per,
+                                                            double tau_h, double tau_m, GatePartial* parts,
+                                                            uint32_t* counter, qam_uncertainty* out) {
+    constexpr int NW = kGateThreads / 64;
+    __shared__ double red[NW];
+    __shared__ float tv1[NW], tv2[NW];
+    __shared__ int64_t ti1[NW], ti2[NW];
+    __shared__ int badw[NW];
+    __shared__ int last;
+    __shared__ GatePartial lp[kGateMaxGroups];
+    const int g = blockIdx.x;
+    const int64_t lo = (int64_t)g * per;
+    const int64_t hi = min(V, lo + per);
+    const int T = threadIdx.x;
+    const int w = T >> 6;
+
+    // pass 1: the slice's top two (the first is its maximum) and whether it
+    // holds a NaN or +inf
+    float v1 = -INFINITY, v2 = -INFINITY;
+    int64_t i1 = INT64_MAX, i2 = INT64_MAX;
+    int bad = 0;
+    for (int64_t k = lo + T; k < hi; k += kGateThreads) {
+        const float v = z[k];
+        if (isnan(v) || v == INFINITY) bad = 1;
+        merge2(v1, i1, v2, i2, v, k, -INFINITY, INT64_MAX);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float b1 = __shfl_xor(v1, o), b2 = __shfl_xor(v2, o);
+        const int64_t bi1 = __shfl_xor(i1, o), bi2 = __shfl_xor(i2, o);
+        merge2(v1, i1, v2, i2, b1, bi1, b2, bi2);
+        bad |= __shfl_xor(bad, o);
+    }
+    if ((T & 63) == 0) {
+        tv1[w] = v1, tv2[w] = v2, ti1[w] = i1, ti2[w] = i2;
+        badw[w] = bad;
+    }
+    __syncthreads();
+    v1 = tv1[0], v2 = tv2[0], i1 = ti1[0], i2 = ti2[0];
+    bad = badw[0];
+    for (int k = 1; k < NW; ++k) {
+        merge2(v1, i1, v2, i2, tv1[k], ti1[k], tv2[k], ti2[k]);
+        bad |= badw[k];
+    }
+
+    // pass 2: sums relative to the slice's maximum (-inf logits add nothing)
+    const double md = (double)v1;
+    double S = 0.0, Tt = 0.0;
+    if (v1 != -INFINITY && !bad) {
+        for (int64_t k = lo + T; k < hi; k += kGateThreads) {
+            const double d = (double)z[k] - md;
+            if (d != -INFINITY) {
+                const double e = exp(d);
+                S += e;
+                Tt += e * d;
+            }
+        }
+    }
+    S = block_sum(S, red);
+    Tt = block_sum(Tt, red);
+
+    if (T == 0) {
+        GatePartial* pp = parts + g;
+        __hip_atomic_store(&pp->m, md, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&pp->S, S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&pp->T, Tt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&pp->v1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&pp->v2, v2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&pp->i1, i1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&pp->i2, i2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&pp->bad, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);   // the partial is stored before it is counted
+        last = (int)(__hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     gridDim.x - 1);
+    }
+    __syncthreads();
+    if (!last) return;
+
+    // the last workgroup: every partial is in; its threads fetch them, then
+    // one thread merges them in slice order
+    const int G = (int)gridDim.x;
+    for (int k = T; k < G; k += kGateThreads) {
+        const GatePartial* pp = parts + k;
+        lp[k].m = __hip_atomic_load(&pp->m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lp[k].S = __hip_atomic_load(&pp->S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lp[k].T = __hip_atomic_load(&pp->T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lp[k].v1 = __hip_atomic_load(&pp->v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lp[k].v2 = __hip_atomic_load(&pp->v2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lp[k].i1 = __hip_atomic_load(&pp->i1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lp[k].i2 = __hip_atomic_load(&pp->i2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lp[k].bad = __hip_atomic_load(&pp->bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (T != 0) return;
+    double M = -INFINITY;
+    int anybad = 0;
+    float b1 = -INFINITY, b2 = -INFINITY;
+    int64_t bi1 = INT64_MAX, bi2 = INT64_MAX;
+    for (int k = 0; k < G; ++k) {
+        M = fmax(M, lp[k].m);
+        anybad |= lp[k].bad;
+        merge2(b1, bi1, b2, bi2, lp[k].v1, lp[k].i1, lp[k].v2, lp[k].i2);
+    }
+    qam_uncertainty r{};
+    r.top1 = bi1;
+    r.top2 = bi2;
+    if (anybad || M == -INFINITY) {
+        r.entropy = r.margin = r.p1 = r.p2 = __builtin_nan("");
+        r.escalate = 1;
+    } else {
+        double Sa = 0.0, Ta = 0.0;
+        for (int k = 0; k < G; ++k) {
+            if (lp[k].m == -INFINITY) continue;   // an all -inf slice adds nothing
+            const double sh = lp[k].m - M;        // <= 0
+            const double f = exp(sh);
+            Sa += f * lp[k].S;
+            Ta += f * (lp[k].T + sh * lp[k].S);
+        }
+        r.entropy = log(Sa) - Ta / Sa;
+        r.p1 = 1.0 / Sa;
+        r.p2 = exp((double)b2 - M) / Sa;
+        r.margin = r.p1 - r.p2;
+        r.escalate = (r.entropy > tau_h || r.margin < tau_m) ? 1 : 0;
+    }
+    *out = r;
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+static int gate_groups(int64_t V) {
+    const int64_t g = (V + kGatePerGroup - 1) / kGatePerGroup;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(kGateMaxGroups, g));
+}
+
+}  // namespace qam
+
+using namespace qam;
+
+extern "C" size_t qam_gate_workspace_bytes(int64_t V) {
+    if (V < 2) return 0;
+    return 256 + (size_t)gate_groups(V) * sizeof(GatePartial);
+}
+
+extern "C" int qam_gate(const float* logits, int64_t V, double tau_entropy, double tau_margin, qam_uncertainty* out,
+                        void* workspace, size_t workspace_bytes, hipStream_t s) {
+    clear_error();
+    if (!logits || !out || !workspace) QAM_FAIL(QAM_ERR_NULL, "gate: null pointer");
+    if (V < 2) QAM_FAIL(QAM_ERR_SHAPE, "gate: V=%lld < 2", (long long)V);
+    if (isnan(tau_entropy) || isnan(tau_margin)) QAM_FAIL(QAM_ERR_ARG, "gate: NaN threshold");
+    const size_t need = qam_gate_workspace_bytes(V);
+    if (workspace_bytes < need) QAM_FAIL(QAM_ERR_WORKSPACE, "gate: workspace %zu < %zu bytes", workspace_bytes, need);
+    if (!aligned(workspace, 256) || !aligned(logits, 4) || !aligned(out, 8))
+        QAM_FAIL(QAM_ERR_ALIGN, "gate: workspace must be 256-byte, logits 4-byte and out 8-byte aligned");
+    const int G = gate_groups(V);
+    const int64_t per = (V + G - 1) / G;
+    uint32_t* counter = static_cast<uint32_t*>(workspace);
+    GatePartial* parts = reinterpret_cast<GatePartial*>(static_cast<char*>(workspace) + 256);
+    hipLaunchKernelGGL(gate_kernel, dim3((unsigned)G), dim3(kGateThreads), 0, s, logits, V, per, tau_entropy,
+                       tau_margin, parts, counter, out);
+    QAM_HIP_CHECK(hipGetLastError());
+    set_variant("gate_fp64");
+    return QAM_OK;
+}
