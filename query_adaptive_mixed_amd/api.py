@@ -362,6 +362,7 @@ class Gate:
         self.V = int(V)
         self.ws = torch.zeros(n, dtype=torch.uint8, device=device)
         self.out = torch.zeros(C.sizeof(L.QamUncertainty), dtype=torch.uint8, device=device)
+        self._host = torch.empty(C.sizeof(L.QamUncertainty), dtype=torch.uint8, pin_memory=True)
 
     def run(self, logits: torch.Tensor, tau_entropy: float = float("inf"),
             tau_margin: float = float("-inf")) -> None:
@@ -372,8 +373,9 @@ class Gate:
                                  _ptr(self.ws), self.ws.numel(), _stream_handle()))
 
     def result(self) -> dict:
-        raw = self.out.cpu().numpy().tobytes()
-        u = L.QamUncertainty.from_buffer_copy(raw)
+        self._host.copy_(self.out, non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        u = L.QamUncertainty.from_buffer_copy(self._host.numpy().tobytes())
         return dict(entropy=u.entropy, margin=u.margin, p1=u.p1, p2=u.p2, top1=int(u.top1), top2=int(u.top2),
                     escalate=bool(u.escalate))
 
