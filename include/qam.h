@@ -515,7 +515,7 @@ int qam_escalation_schedule(const double* scores, int64_t T, double rate, uint8_
  *   are NaN and escalate = 1.  One launch; the partials of its workgroups
  *   are merged in a fixed order, so the result is the same bits on every
  *   call (within ~1e-12 of the same formulas evaluated in fp64 on a CPU).
- *   logits     (device) fp32 [V], V >= 2.
+ *   logits     (device) fp32 [V], 2 <= V <= 2^31 - 2.
  *   out        (device) one qam_uncertainty, written by the launch.
  *   workspace  (device) qam_gate_workspace_bytes(V) bytes, 256-byte aligned,
  *              zero-filled before its first use; every call leaves its

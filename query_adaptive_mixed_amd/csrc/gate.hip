@@ -18,25 +18,26 @@
 namespace qam {
 
 constexpr int kGateThreads = 256;
-constexpr int kGateMaxGroups = 256;
-constexpr int64_t kGatePerGroup = 4096;   // logits per workgroup (fewer groups for short vectors)
+constexpr int kGateMaxGroups = 256;   // at most one partial per thread of the merging workgroup
+constexpr int64_t kGatePerGroup = 1024;   // logits per workgroup (at most kGateMaxGroups groups)
+constexpr int kGateBatch = 4;             // loads a thread has in flight
 
 struct GatePartial {
     double m, S, T;        // max of the slice, sum of exp(z - m), sum of exp(z - m) (z - m)
     float v1, v2;          // the slice's two largest logits ...
-    int64_t i1, i2;        // ... and their indices (ties to the lower index)
+    int32_t i1, i2;        // ... and their indices (ties to the lower index)
     int32_t bad;           // a NaN or +inf in the slice
     int32_t pad;
 };
 
-static_assert(sizeof(GatePartial) == 56, "partial layout");
+static_assert(sizeof(GatePartial) == 48, "partial layout");
+static_assert(kGateMaxGroups <= kGateThreads, "the merge takes one partial per thread");
 
 // (v, i) ranks ahead of (w, j): larger value, or equal value and lower index.
-__device__ __forceinline__ bool ahead(float v, int64_t i, float w, int64_t j) { return v > w || (v == w && i < j); }
+__device__ __forceinline__ bool ahead(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
 
 // Merge the top two (a1, a2) with (b1, b2) into (a1, a2).
-__device__ __forceinline__ void merge2(float& a1, int64_t& ai1, float& a2, int64_t& ai2, float b1, int64_t bi1,
-                                       float b2, int64_t bi2) {
+__device__ __forceinline__ void merge2(float& a1, int& ai1, float& a2, int& ai2, float b1, int bi1, float b2, int bi2) {
     if (ahead(b1, bi1, a1, ai1)) {
         // b1 leads; the runner-up is the better of a1 and b2
         if (ahead(a1, ai1, b2, bi2)) {
@@ -67,61 +68,102 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
     return s;
 }
 
+// Maximum over the workgroup; every thread gets it.
+__device__ __forceinline__ double block_max(double v, double* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    double s = red[0];
+    for (int k = 1; k < kGateThreads / 64; ++k) s = fmax(s, red[k]);
+    return s;
+}
+
+// The top two (and the NaN / +inf flag) over the workgroup; every thread gets them.
+struct Top2 {
+    float v1, v2;
+    int i1, i2;
+    int bad;
+};
+__device__ __forceinline__ void block_top2(Top2& t, Top2* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float b1 = __shfl_xor(t.v1, o), b2 = __shfl_xor(t.v2, o);
+        const int bi1 = __shfl_xor(t.i1, o), bi2 = __shfl_xor(t.i2, o);
+        merge2(t.v1, t.i1, t.v2, t.i2, b1, bi1, b2, bi2);
+        t.bad |= __shfl_xor(t.bad, o);
+    }
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = t;
+    __syncthreads();
+    t = red[0];
+    for (int k = 1; k < kGateThreads / 64; ++k) {
+        merge2(t.v1, t.i1, t.v2, t.i2, red[k].v1, red[k].i1, red[k].v2, red[k].i2);
+        t.bad |= red[k].bad;
+    }
+}
+
 __global__ __launch_bounds__(kGateThreads) void gate_kernel(const float* __restrict__ z, int64_t V, int64_t per,
                                                             double tau_h, double tau_m, GatePartial* parts,
                                                             uint32_t* counter, qam_uncertainty* out) {
     constexpr int NW = kGateThreads / 64;
     __shared__ double red[NW];
-    __shared__ float tv1[NW], tv2[NW];
-    __shared__ int64_t ti1[NW], ti2[NW];
-    __shared__ int badw[NW];
+    __shared__ Top2 tred[NW];
     __shared__ int last;
-    __shared__ GatePartial lp[kGateMaxGroups];
     const int g = blockIdx.x;
     const int64_t lo = (int64_t)g * per;
     const int64_t hi = min(V, lo + per);
     const int T = threadIdx.x;
-    const int w = T >> 6;
 
     // pass 1: the slice's top two (the first is its maximum) and whether it
     // holds a NaN or +inf
     float v1 = -INFINITY, v2 = -INFINITY;
-    int64_t i1 = INT64_MAX, i2 = INT64_MAX;
+    int i1 = INT32_MAX, i2 = INT32_MAX;
     int bad = 0;
-    for (int64_t k = lo + T; k < hi; k += kGateThreads) {
-        const float v = z[k];
-        if (isnan(v) || v == INFINITY) bad = 1;
-        merge2(v1, i1, v2, i2, v, k, -INFINITY, INT64_MAX);
-    }
+    float keep[kGateBatch];   // the first batch, reused by pass 2 (the whole slice when it fits)
+    for (int64_t k0 = lo + T; k0 < hi; k0 += kGateBatch * kGateThreads) {
+        float v[kGateBatch];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float b1 = __shfl_xor(v1, o), b2 = __shfl_xor(v2, o);
-        const int64_t bi1 = __shfl_xor(i1, o), bi2 = __shfl_xor(i2, o);
-        merge2(v1, i1, v2, i2, b1, bi1, b2, bi2);
-        bad |= __shfl_xor(bad, o);
+        for (int j = 0; j < kGateBatch; ++j) {   // the batch's loads go out together
+            const int64_t k = k0 + (int64_t)j * kGateThreads;
+            v[j] = k < hi ? z[k] : -INFINITY;
+        }
+#pragma unroll
+        for (int j = 0; j < kGateBatch; ++j) {
+            const int64_t k = k0 + (int64_t)j * kGateThreads;
+            if (k < hi) {
+                if (isnan(v[j]) || v[j] == INFINITY) bad = 1;
+                merge2(v1, i1, v2, i2, v[j], (int)k, -INFINITY, INT32_MAX);
+            }
+            if (k0 == lo + T) keep[j] = v[j];
+        }
     }
-    if ((T & 63) == 0) {
-        tv1[w] = v1, tv2[w] = v2, ti1[w] = i1, ti2[w] = i2;
-        badw[w] = bad;
-    }
-    __syncthreads();
-    v1 = tv1[0], v2 = tv2[0], i1 = ti1[0], i2 = ti2[0];
-    bad = badw[0];
-    for (int k = 1; k < NW; ++k) {
-        merge2(v1, i1, v2, i2, tv1[k], ti1[k], tv2[k], ti2[k]);
-        bad |= badw[k];
-    }
+    Top2 tp{v1, v2, i1, i2, bad};
+    block_top2(tp, tred);
+    v1 = tp.v1, v2 = tp.v2, i1 = tp.i1, i2 = tp.i2, bad = tp.bad;
 
     // pass 2: sums relative to the slice's maximum (-inf logits add nothing)
     const double md = (double)v1;
     double S = 0.0, Tt = 0.0;
     if (v1 != -INFINITY && !bad) {
-        for (int64_t k = lo + T; k < hi; k += kGateThreads) {
-            const double d = (double)z[k] - md;
-            if (d != -INFINITY) {
-                const double e = exp(d);
-                S += e;
-                Tt += e * d;
+        for (int64_t k0 = lo + T; k0 < hi; k0 += kGateBatch * kGateThreads) {
+            float v[kGateBatch];
+#pragma unroll
+            for (int j = 0; j < kGateBatch; ++j) {
+                const int64_t k = k0 + (int64_t)j * kGateThreads;
+                v[j] = k0 == lo + T ? keep[j] : (k < hi ? z[k] : -INFINITY);
+            }
+#pragma unroll
+            for (int j = 0; j < kGateBatch; ++j) {   // in index order, as loaded
+                const double d = (double)v[j] - md;
+                if (d != -INFINITY) {
+                    const double e = exp(d);
+                    S += e;
+                    Tt += e * d;
+                }
             }
         }
     }
@@ -145,49 +187,46 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(const float* __restr
     __syncthreads();
     if (!last) return;
 
-    // the last workgroup: every partial is in; its threads fetch them, then
-    // one thread merges them in slice order
+    // the last workgroup: every partial is in; thread k takes partial k
+    // (G <= the workgroup size) and the workgroup reduces them in a fixed
+    // tree order
     const int G = (int)gridDim.x;
-    for (int k = T; k < G; k += kGateThreads) {
-        const GatePartial* pp = parts + k;
-        lp[k].m = __hip_atomic_load(&pp->m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lp[k].S = __hip_atomic_load(&pp->S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lp[k].T = __hip_atomic_load(&pp->T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lp[k].v1 = __hip_atomic_load(&pp->v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lp[k].v2 = __hip_atomic_load(&pp->v2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lp[k].i1 = __hip_atomic_load(&pp->i1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lp[k].i2 = __hip_atomic_load(&pp->i2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lp[k].bad = __hip_atomic_load(&pp->bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    double mk = -INFINITY, Sk = 0.0, Tk = 0.0;
+    Top2 tk{-INFINITY, -INFINITY, INT32_MAX, INT32_MAX, 0};
+    if (T < G) {
+        const GatePartial* pp = parts + T;
+        mk = __hip_atomic_load(&pp->m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        Sk = __hip_atomic_load(&pp->S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        Tk = __hip_atomic_load(&pp->T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tk.v1 = __hip_atomic_load(&pp->v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tk.v2 = __hip_atomic_load(&pp->v2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tk.i1 = __hip_atomic_load(&pp->i1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tk.i2 = __hip_atomic_load(&pp->i2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tk.bad = __hip_atomic_load(&pp->bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();
+    const double M = block_max(mk, red);
+    block_top2(tk, tred);
+    // each slice's sums rescaled to the global maximum (an all -inf slice adds nothing)
+    double Sc = 0.0, Tc = 0.0;
+    if (T < G && mk != -INFINITY && M != -INFINITY && !tk.bad) {
+        const double sh = mk - M;   // <= 0
+        const double f = exp(sh);
+        Sc = f * Sk;
+        Tc = f * (Tk + sh * Sk);
+    }
+    const double Sa = block_sum(Sc, red);
+    const double Ta = block_sum(Tc, red);
     if (T != 0) return;
-    double M = -INFINITY;
-    int anybad = 0;
-    float b1 = -INFINITY, b2 = -INFINITY;
-    int64_t bi1 = INT64_MAX, bi2 = INT64_MAX;
-    for (int k = 0; k < G; ++k) {
-        M = fmax(M, lp[k].m);
-        anybad |= lp[k].bad;
-        merge2(b1, bi1, b2, bi2, lp[k].v1, lp[k].i1, lp[k].v2, lp[k].i2);
-    }
     qam_uncertainty r{};
-    r.top1 = bi1;
-    r.top2 = bi2;
-    if (anybad || M == -INFINITY) {
+    r.top1 = tk.i1;
+    r.top2 = tk.i2;
+    if (tk.bad || M == -INFINITY) {
         r.entropy = r.margin = r.p1 = r.p2 = __builtin_nan("");
         r.escalate = 1;
     } else {
-        double Sa = 0.0, Ta = 0.0;
-        for (int k = 0; k < G; ++k) {
-            if (lp[k].m == -INFINITY) continue;   // an all -inf slice adds nothing
-            const double sh = lp[k].m - M;        // <= 0
-            const double f = exp(sh);
-            Sa += f * lp[k].S;
-            Ta += f * (lp[k].T + sh * lp[k].S);
-        }
         r.entropy = log(Sa) - Ta / Sa;
         r.p1 = 1.0 / Sa;
-        r.p2 = exp((double)b2 - M) / Sa;
+        r.p2 = exp((double)tk.v2 - M) / Sa;
         r.margin = r.p1 - r.p2;
         r.escalate = (r.entropy > tau_h || r.margin < tau_m) ? 1 : 0;
     }
@@ -205,7 +244,7 @@ static int gate_groups(int64_t V) {
 using namespace qam;
 
 extern "C" size_t qam_gate_workspace_bytes(int64_t V) {
-    if (V < 2) return 0;
+    if (V < 2 || V > INT32_MAX - 1) return 0;
     return 256 + (size_t)gate_groups(V) * sizeof(GatePartial);
 }
 
@@ -213,7 +252,7 @@ extern "C" int qam_gate(const float* logits, int64_t V, double tau_entropy, doub
                         void* workspace, size_t workspace_bytes, hipStream_t s) {
     clear_error();
     if (!logits || !out || !workspace) QAM_FAIL(QAM_ERR_NULL, "gate: null pointer");
-    if (V < 2) QAM_FAIL(QAM_ERR_SHAPE, "gate: V=%lld < 2", (long long)V);
+    if (V < 2 || V > INT32_MAX - 1) QAM_FAIL(QAM_ERR_SHAPE, "gate: V=%lld outside [2, 2^31 - 2]", (long long)V);
     if (isnan(tau_entropy) || isnan(tau_margin)) QAM_FAIL(QAM_ERR_ARG, "gate: NaN threshold");
     const size_t need = qam_gate_workspace_bytes(V);
     if (workspace_bytes < need) QAM_FAIL(QAM_ERR_WORKSPACE, "gate: workspace %zu < %zu bytes", workspace_bytes, need);

@@ -355,10 +355,12 @@ def test_gate_rejects_before_any_launch(lib):
     FAKEW = 0x20000000            # 256-byte aligned stand-ins, never dereferenced
     assert lib.qam_gate_workspace_bytes(1) == 0
     need = lib.qam_gate_workspace_bytes(151936)
-    assert need >= 256 + 38 * 56
+    assert need >= 256 + 149 * 48
     assert lib.qam_gate(None, 100, 1.0, 0.1, FAKEW, FAKEW, need, None) == -1
     assert lib.qam_gate(FAKEW, 100, 1.0, 0.1, None, FAKEW, need, None) == -1
     assert lib.qam_gate(FAKEW, 1, 1.0, 0.1, FAKEW, FAKEW, need, None) == -2
+    assert lib.qam_gate(FAKEW, 1 << 31, 1.0, 0.1, FAKEW, FAKEW, need, None) == -2
+    assert lib.qam_gate_workspace_bytes(1 << 31) == 0
     assert lib.qam_gate(FAKEW, 100, float("nan"), 0.1, FAKEW, FAKEW, need, None) == -3
     assert lib.qam_gate(FAKEW, 151936, 1.0, 0.1, FAKEW, FAKEW, need - 1, None) == -7
     assert lib.qam_gate(FAKEW, 100, 1.0, 0.1, FAKEW, FAKEW + 8, need, None) == -5
