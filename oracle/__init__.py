@@ -21,6 +21,7 @@ from .qam_oracle import (  # noqa: F401
     level_map,
     mean_bits,
     weight_bytes,
+    fit_focus_area,
     qmatvec_ref,
     qmatvec_tolerance,
     escalation_schedule,

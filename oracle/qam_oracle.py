@@ -313,6 +313,43 @@ def qmatvec_tolerance(W, scales, x, level, ladder_bits=LADDER_BITS, per_request=
     return rel * t
 
 
+def fit_focus_area(coords, centres, radii, g: float, combine: str, n_rungs: int, glass: int,
+                   block_weights, budget_bytes: int, iters: int = 40, ladder_bits=LADDER_BITS, stops=None):
+    """The byte-budget regulator: the largest focus area f in [0, 1] whose
+    lens map reads at most ``budget_bytes`` of weights.
+
+    [Lens] "The mechanism": memory is what the lenses cost (rule 7, bytes
+    sum_b w_b bits(b) / 8), and focus_area is the control that widens every
+    lens.  The pages set no budget rule; the reading taken: bytes never
+    decrease as f grows (a wider lens lifts no block less), so f is found by
+    bisection on [0, 1], ``iters`` halvings, keeping the end that fits.  If
+    f = 1 fits, f = 1; if not even f = 0 fits, f = 0 (and the returned
+    bytes exceed the budget).  Exact integers decide every step.
+
+    Returns (f, bytes at f, level map at f).
+    """
+    def at(f):
+        lv = level_map(coords, centres, radii, f, g, combine, n_rungs, glass, stops)
+        return weight_bytes(lv, block_weights, ladder_bits), lv
+
+    b1, lv1 = at(1.0)
+    if b1 <= budget_bytes:
+        return 1.0, b1, lv1
+    b0, lv0 = at(0.0)
+    if b0 > budget_bytes:
+        return 0.0, b0, lv0
+    lo, hi = 0.0, 1.0
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        b, _ = at(mid)
+        if b <= budget_bytes:
+            lo = mid
+        else:
+            hi = mid
+    b, lv = at(lo)
+    return lo, b, lv
+
+
 # --------------------------------------------------------------------------
 # Escalation: top-4-bit decode with a gated 8-bit re-run
 # --------------------------------------------------------------------------

@@ -463,3 +463,44 @@ def test_gate_rules():
     assert O.gate(flat, 1.0, -math.inf)          # the entropy alone
     assert not O.gate(flat, math.inf, -math.inf)
     assert not O.gate(flat, math.log(50) + 1e-9, -math.inf)
+
+
+# ---------------------------------------------------------------- the byte-budget regulator
+
+def _field(seed, n=60, n_lenses=3):
+    rng = np.random.default_rng(seed)
+    coords = rng.uniform(0, 1, size=(n, 2))
+    cen = coords[rng.choice(n, n_lenses, replace=False)]
+    rad = rng.uniform(0.05, 0.3, size=n_lenses)
+    w = 64 * rng.choice([256, 1024, 4096], size=n)
+    return coords, cen, rad, w
+
+
+def test_fit_focus_area_against_a_fine_scan():
+    """On small fields the regulator's f is the edge a brute-force scan finds:
+    the map at f fits the budget, the map 2^-iters above it does not, and no
+    f on a fine grid below the edge has more bytes than the budget."""
+    for seed in range(6):
+        coords, cen, rad, w = _field(seed)
+        full = O.weight_bytes(O.level_map(coords, cen, rad, 1.0, 1.0, "sum", 5, 1), w)
+        low = O.weight_bytes(O.level_map(coords, cen, rad, 0.0, 1.0, "sum", 5, 1), w)
+        for frac in (0.2, 0.5, 0.8):
+            budget = int(low + frac * (full - low))
+            f, b, lv = O.fit_focus_area(coords, cen, rad, 1.0, "sum", 5, 1, w, budget, iters=30)
+            assert b <= budget and b == O.weight_bytes(lv, w)
+            above = O.weight_bytes(O.level_map(coords, cen, rad, min(1.0, f + 2.0 ** -30), 1.0, "sum", 5, 1), w)
+            assert above > budget
+            grid = np.linspace(0.0, f, 257)
+            assert max(O.weight_bytes(O.level_map(coords, cen, rad, x, 1.0, "sum", 5, 1), w) for x in grid) <= budget
+
+
+def test_fit_focus_area_ends_and_monotone():
+    coords, cen, rad, w = _field(9)
+    full = O.weight_bytes(O.level_map(coords, cen, rad, 1.0, 0.75, "max", 5, 1), w)
+    low = O.weight_bytes(O.level_map(coords, cen, rad, 0.0, 0.75, "max", 5, 1), w)
+    assert O.fit_focus_area(coords, cen, rad, 0.75, "max", 5, 1, w, full)[0] == 1.0
+    f0, b0, _ = O.fit_focus_area(coords, cen, rad, 0.75, "max", 5, 1, w, low - 1)
+    assert f0 == 0.0 and b0 == low > low - 1
+    fs = [O.fit_focus_area(coords, cen, rad, 0.75, "max", 5, 1, w, low + k * (full - low) // 7, iters=24)[0]
+          for k in range(8)]
+    assert all(a <= b for a, b in zip(fs, fs[1:])) and fs[-1] == 1.0
