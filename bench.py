@@ -192,6 +192,19 @@ def run_field(args, torch, Q, WL):
         kern_ms = float(np.median([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]))
         kern_timing = "median spacing of HIP events recorded after each of back-to-back launches"
 
+    # The byte-budget regulator on this field (outside the timed step): the
+    # largest focus area whose map reads at most the bytes of a 4-bit mean.
+    regulator = None
+    if not args.uniform_map:
+        wt = torch.from_numpy(fld.block_weights().astype(np.int64)).to(dev)
+        budget = int(np.sum(fld.block_weights())) * 4 // 8
+        torch.cuda.synchronize()
+        r0 = time.perf_counter()
+        f_fit, b_fit, _ = Q.fit_focus_area(coords, wt, lens.centres, lens.radii, lens.g, budget,
+                                           combine=lens.combine, glass=lens.glass, iters=40)
+        regulator = {"budget_bytes": budget, "focus_area_f": f_fit, "bytes": b_fit, "bisection_steps": 40,
+                     "ms": round((time.perf_counter() - r0) * 1e3, 3)}
+
     # Whole-step throughput: wall clock over K steps issued from the host (map
     # + grouped product each), so the host's per-call overhead is inside the
     # timed region wherever the host falls behind the GPU.  With --graph, one
@@ -223,7 +236,7 @@ def run_field(args, torch, Q, WL):
     assert np.array_equal(lv.cpu().numpy(), lv_h), "level map changed between steps"
     ms = wall * 1e3 / args.steps
     return dict(desc=desc, mean_bits=mean_bits, wbytes=wbytes, other=other, ms=ms, kern_ms=kern_ms, map_ms=map_ms,
-                kern_timing=kern_timing, fused=fused,
+                kern_timing=kern_timing, fused=fused, regulator=regulator,
                 variant=Q.last_variant(), lens=lens, fld=fld, lv_h=lv_h, n_items=len(items),
                 key=f"{args.workload}_{args.mean_bits}_g{lens.glass}_b{args.batch}" + ("_uniform" if args.uniform_map else "")
                 + ("_lens" if fused else ""))
@@ -664,6 +677,7 @@ def main():
             "matrices_per_launch": res["n_items"],
             "level_map": ("built inside the product launch" if res["fused"] else "own launch before the product"),
             "level_map_alone_ms": round(res["map_ms"], 5),
+            "regulator": res["regulator"],
             "step_timing": "HIP graph replay of one step" if args.graph else "eager launches, wall clock",
             "kernel": res["variant"],
         },

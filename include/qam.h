@@ -198,6 +198,36 @@ int qam_build_level_maps(const double* coords, int64_t n_blocks, const qam_lens*
                          int glass, int n_maps, uint8_t* level_out, hipStream_t s);
 
 /*
+ * qam_fit_focus_area -- the byte-budget regulator: the largest focus area f
+ *   in [0, 1] whose lens map reads at most budget_bytes of weights
+ *   ([Lens] "The mechanism": memory is what the lenses cost, rule 7 bytes
+ *   sum_b w_b bits(b) / 8; focus_area widens every lens).  Bytes never
+ *   decrease as f grows, so f is found by bisection: f = 1 if it fits, else
+ *   f = 0 if even that does not fit (then *bytes_out > budget_bytes), else
+ *   `iters` halvings of [0, 1] keeping the end that fits.  Each step builds
+ *   the map on the device (the kernel of qam_build_level_map, so the maps
+ *   are those of the rules) and sums its bytes exactly in int64; the host
+ *   reads the sum (one synchronisation of `s` per step).  Every decision is
+ *   an integer comparison: f is the same double as the same bisection
+ *   evaluated on a CPU.
+ *   coords, n_blocks, lenses, n_lenses, ladder_bits, n_rungs, glass
+ *               as qam_build_level_map; params: g, combine and stops (its f
+ *               is not read).
+ *   block_weights (device) int64 [n_blocks], w_b >= 0 (64 K for a block of
+ *               a K-column matrix); sum_b w_b bits(b) must fit in int64.
+ *   iters       0 .. 60.
+ *   level_out   (device) uint8 [n_blocks]: the map at the returned f.
+ *   workspace   (device) 256 bytes, 256-byte aligned.
+ *   f_out, bytes_out  (host) the focus area and its bytes.
+ *   Host-synchronous; not for graph capture.
+ */
+int qam_fit_focus_area(const double* coords, int64_t n_blocks, const int64_t* block_weights,
+                       const qam_lens* lenses, int n_lenses, const qam_lens_params* params,
+                       const uint8_t* ladder_bits, int n_rungs, int glass, int64_t budget_bytes,
+                       int iters, uint8_t* level_out, void* workspace, size_t workspace_bytes,
+                       double* f_out, int64_t* bytes_out, hipStream_t s);
+
+/*
  * qam_map_weight_bytes -- rule 7 and the bytes-read cost for a map (host).
  *   [Lens] rule 7: bits = sum_b w_b bits(b) / sum_b w_b; [PoD]: cost counted
  *   in weight bytes read.  w_b = 64 * K for every block of one matrix.

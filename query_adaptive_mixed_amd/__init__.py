@@ -18,6 +18,7 @@ from .api import (  # noqa: F401
     build_level_map,
     build_level_maps,
     escalation_schedule,
+    fit_focus_area,
     last_variant,
     map_weight_bytes,
     pack_slices,

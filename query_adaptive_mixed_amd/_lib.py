@@ -105,6 +105,8 @@ SIGNATURES = [
     ("qam_qmatvec_group", _I, [C.POINTER(QamGroup), _P]),
     ("qam_qmatvec_group_lens", _I, [C.POINTER(QamGroup), C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I,
                                     _I, _P]),
+    ("qam_fit_focus_area", _I, [_P, _I64, _P, C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I, _I, _I64,
+                                _I, _P, _P, _SZ, C.POINTER(C.c_double), C.POINTER(C.c_int64), _P]),
     ("qam_gate_workspace_bytes", C.c_size_t, [_I64]),
     ("qam_gate", _I, [_P, _I64, C.c_double, C.c_double, _P, _P, _SZ, _P]),
     ("qam_last_error", C.c_char_p, []),

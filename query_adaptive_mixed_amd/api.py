@@ -137,6 +137,30 @@ def build_level_map(coords: torch.Tensor, centres, radii, f: float, g: float, co
     return out
 
 
+def fit_focus_area(coords: torch.Tensor, block_weights: torch.Tensor, centres, radii, g: float, budget_bytes: int,
+                   combine: str = "sum", glass: int = 1, iters: int = 40, stops=None,
+                   ladder_bits: Sequence[int] = LADDER_BITS, out: Optional[torch.Tensor] = None):
+    """The byte-budget regulator: the largest focus area f whose lens map
+    reads at most ``budget_bytes`` of weights (bisection, ``iters`` halvings).
+    ``block_weights`` is a device int64 [n_blocks] tensor of w_b.  Returns
+    (f, bytes, level map uint8 [n_blocks] at f)."""
+    _require_cuda(coords, "coords", torch.float64)
+    _require_cuda(block_weights, "block_weights", torch.int64)
+    n_blocks = coords.shape[0]
+    if block_weights.numel() != n_blocks:
+        raise ValueError("one weight per block")
+    r = LensRules(centres, radii, 0.0, g, combine, glass, stops, ladder_bits)
+    if out is None:
+        out = torch.empty(n_blocks, dtype=torch.uint8, device=coords.device)
+    ws = torch.zeros(256, dtype=torch.uint8, device=coords.device)
+    f, b = C.c_double(), C.c_int64()
+    L.check(L.lib().qam_fit_focus_area(_ptr(coords), n_blocks, _ptr(block_weights), r.lenses, r.n_lenses,
+                                       C.byref(r.params), C.cast(r.ladder, C.c_void_p), r.n_rungs, r.glass,
+                                       int(budget_bytes), int(iters), _ptr(out), _ptr(ws), 256, C.byref(f),
+                                       C.byref(b), _stream_handle()))
+    return f.value, b.value, out
+
+
 def build_level_maps(coords: torch.Tensor, lens_sets, f, g: float = 1.0, combine: str = "sum", glass: int = 1,
                      ladder_bits: Sequence[int] = LADDER_BITS, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One map per request (uint8 [n_maps, n_blocks]): ``lens_sets`` is a

@@ -22,6 +22,11 @@ namespace qam {
 
 constexpr int kMapsPerLaunch = 8;
 
+// The bits of every rung of a ladder, by value for the byte-sum kernel.
+struct LadderBits {
+    uint32_t v[QAM_MAX_RUNGS];
+};
+
 // Up to kMapsPerLaunch maps of one launch over a shared lens table.
 struct LensArgs {
     LensTable t;
@@ -121,6 +126,19 @@ static void launch_maps(const double* coords, int64_t n_blocks, const LensArgs& 
     hipLaunchKernelGGL(levelmap_kernel, grid, dim3(256), 0, s, coords, n_blocks, a, out);
 }
 
+// Rule 7 bytes of a map, summed exactly: sum_b w_b bits(level_b) into *acc
+// (int64 adds, so the order does not matter).
+__global__ __launch_bounds__(256) void map_bits_kernel(const uint8_t* __restrict__ level,
+                                                       const int64_t* __restrict__ w, int64_t n_blocks,
+                                                       LadderBits bits, unsigned long long* acc) {
+    unsigned long long sum = 0;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < n_blocks; b += (int64_t)gridDim.x * blockDim.x)
+        sum += (unsigned long long)w[b] * bits.v[level[b]];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    if ((threadIdx.x & 63) == 0 && sum) atomicAdd(acc, sum);
+}
+
 }  // namespace qam
 
 using namespace qam;
@@ -198,5 +216,82 @@ extern "C" int qam_build_level_map(const double* coords, int64_t n_blocks, const
     launch_maps(coords, n_blocks, a, 1, level_out, s);
     QAM_HIP_CHECK(hipGetLastError());
     set_variant("levelmap_fp64");
+    return QAM_OK;
+}
+
+extern "C" int qam_fit_focus_area(const double* coords, int64_t n_blocks, const int64_t* block_weights,
+                                  const qam_lens* lenses, int n_lenses, const qam_lens_params* params,
+                                  const uint8_t* ladder_bits, int n_rungs, int glass, int64_t budget_bytes, int iters,
+                                  uint8_t* level_out, void* workspace, size_t workspace_bytes, double* f_out,
+                                  int64_t* bytes_out, hipStream_t s) {
+    clear_error();
+    if (!params || !ladder_bits || !f_out || !bytes_out) QAM_FAIL(QAM_ERR_NULL, "fit_focus_area: null pointer");
+    if (n_blocks < 1) QAM_FAIL(QAM_ERR_SHAPE, "fit_focus_area: n_blocks < 1");
+    if (!coords || !block_weights || !level_out || !workspace) QAM_FAIL(QAM_ERR_NULL, "fit_focus_area: null pointer");
+    if (iters < 0 || iters > 60) QAM_FAIL(QAM_ERR_ARG, "fit_focus_area: iters=%d outside [0, 60]", iters);
+    if (budget_bytes < 0) QAM_FAIL(QAM_ERR_ARG, "fit_focus_area: negative budget");
+    if (workspace_bytes < 256) QAM_FAIL(QAM_ERR_WORKSPACE, "fit_focus_area: workspace %zu < 256 bytes", workspace_bytes);
+    if (!aligned(workspace, 256) || !aligned(block_weights, 8) || !aligned(coords, 8))
+        QAM_FAIL(QAM_ERR_ALIGN, "fit_focus_area: workspace 256-byte, weights and coords 8-byte aligned");
+    if (int rc = lens_check_ladder(ladder_bits, n_rungs, glass, "fit_focus_area")) return rc;
+    if (n_blocks > (INT64_C(1) << 31) >> lanes_log2_for(n_lenses))
+        QAM_FAIL(QAM_ERR_SHAPE, "fit_focus_area: %lld blocks of %d lenses exceed one launch", (long long)n_blocks,
+                 n_lenses);
+    qam_lens_params p = *params;
+    LensArgs a = {};
+    LadderBits lb = {};
+    for (int i = 0; i < n_rungs; ++i) lb.v[i] = ladder_bits[i];
+    unsigned long long* acc = static_cast<unsigned long long*>(workspace);
+    unsigned long long host = 0;
+    // the map at f and its byte count (host-synchronous)
+    auto at = [&](double f, int64_t& bytes) -> int {
+        p.f = f;
+        if (int rc = lens_check_map(lenses, n_lenses, &p, n_rungs, glass, a.maps[0], "fit_focus_area")) return rc;
+        for (int i = 0; i < n_lenses; ++i) {
+            a.t.cx[i] = lenses[i].cx;
+            a.t.cy[i] = lenses[i].cy;
+            a.t.R[i] = lens_radius(lenses[i].r, f);
+        }
+        a.glass = glass;
+        a.lanes_log2 = lanes_log2_for(n_lenses);
+        a.out_stride = n_blocks;
+        launch_maps(coords, n_blocks, a, 1, level_out, s);
+        QAM_HIP_CHECK(hipGetLastError());
+        QAM_HIP_CHECK(hipMemsetAsync(acc, 0, sizeof(unsigned long long), s));
+        const int64_t grid = std::min<int64_t>(1024, (n_blocks + 255) / 256);
+        hipLaunchKernelGGL(map_bits_kernel, dim3((unsigned)grid), dim3(256), 0, s, level_out, block_weights, n_blocks,
+                           lb, acc);
+        QAM_HIP_CHECK(hipGetLastError());
+        QAM_HIP_CHECK(hipMemcpyAsync(&host, acc, sizeof(unsigned long long), hipMemcpyDeviceToHost, s));
+        QAM_HIP_CHECK(hipStreamSynchronize(s));
+        if (host % 8) QAM_FAIL(QAM_ERR_ARG, "fit_focus_area: weight bits not a whole number of bytes");
+        bytes = (int64_t)(host / 8);
+        return QAM_OK;
+    };
+    int rc = QAM_OK;
+    double f = 1.0;
+    int64_t b = 0;
+    do {
+        if ((rc = at(1.0, b))) break;
+        if (b <= budget_bytes) break;
+        f = 0.0;
+        if ((rc = at(0.0, b))) break;
+        if (b > budget_bytes) break;
+        double lo = 0.0, hi = 1.0;
+        for (int k = 0; k < iters; ++k) {
+            const double mid = 0.5 * (lo + hi);
+            int64_t bm = 0;
+            if ((rc = at(mid, bm))) break;
+            if (bm <= budget_bytes) lo = mid;
+            else hi = mid;
+        }
+        if (rc) break;
+        f = lo;
+        rc = at(lo, b);   // the returned map is the one at f
+    } while (false);
+    if (rc) return rc;
+    *f_out = f;
+    *bytes_out = b;
+    set_variant("fit_focus_area");
     return QAM_OK;
 }

@@ -365,3 +365,30 @@ def test_gate_rejects_before_any_launch(lib):
     assert lib.qam_gate(FAKEW, 151936, 1.0, 0.1, FAKEW, FAKEW, need - 1, None) == -7
     assert lib.qam_gate(FAKEW, 100, 1.0, 0.1, FAKEW, FAKEW + 8, need, None) == -5
     assert lib.qam_gate(FAKEW + 2, 100, 1.0, 0.1, FAKEW, FAKEW, need, None) == -5
+
+
+def test_fit_focus_area_rejects_before_any_launch(lib):
+    FAKEW = 0x20000000
+    lens = (L.QamLens * 1)()
+    lens[0].cx, lens[0].cy, lens[0].r = 0.5, 0.5, 0.2
+    p = L.QamLensParams()
+    p.f, p.g, p.combine = 0.0, 1.0, L.QAM_COMBINE_SUM
+    lad = (C.c_uint8 * 5)(0, 2, 4, 6, 8)
+    f, b = C.c_double(), C.c_int64()
+
+    def call(n=8, coords=FAKEW, w=FAKEW, params=p, ladder=lad, n_rungs=5, glass=1, budget=100, iters=10,
+             out=FAKEW, ws=FAKEW, ws_bytes=256, fo=True):
+        return lib.qam_fit_focus_area(coords, n, w, lens, 1, C.byref(params) if params is not None else None,
+                                      C.cast(ladder, C.c_void_p) if ladder is not None else None, n_rungs, glass,
+                                      budget, iters, out, ws, ws_bytes, C.byref(f) if fo else None, C.byref(b), None)
+
+    assert call(params=None) == -1
+    assert call(fo=False) == -1
+    assert call(coords=None) == -1
+    assert call(n=0) == -2
+    assert call(iters=61) == -3
+    assert call(budget=-1) == -3
+    assert call(ws_bytes=255) == -7
+    assert call(ws=FAKEW + 8) == -5
+    assert call(n_rungs=1) == -4
+    assert call(glass=7) == -3
