@@ -3,9 +3,12 @@
 
 A step is one pass of the hot path over one batch of synthetic input:
 build the per-block level map from the lens rules, then read every matrix of
-the workload at its blocks' depths (one grouped qmatvec launch for a weight
-field).  Packing is offline and untimed.  Inputs are resident in HBM before
-the timed region starts.
+the workload at its blocks' depths.  For a weight field both happen in one
+grouped launch (every wavefront computes its block's rung, writes it to the
+map and reads the block at that depth); --separate-map gives the map its own
+launch first.  Steps are issued eagerly and timed by the wall clock.
+Packing is offline and untimed.  Inputs are resident in HBM before the timed
+region starts.
 
 Default workload: the Gemma-E2B-scale weight field (30 synthetic decoder
 layers, q/k/v/o 1536x1536, gate/up 6144x1536, down 1536x6144; 9,360 blocks of

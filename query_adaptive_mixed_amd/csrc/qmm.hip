@@ -6,22 +6,28 @@
 // requests per step).  With a map per request, block b is read once, to the
 // deepest slice any request needs, and every request gets the block's codes
 // at its own depth: the residual slices make the code at depth d the sum of
-// the first d/2 slices, so the codes for each depth present in the batch are
-// built incrementally from the same loaded words.
+// the first d/2 slices.  Two forms use that: the per-depth form builds the
+// codes for each depth present in the batch incrementally from the same
+// loaded words and multiplies them by the limbs of the requests at that
+// depth; the per-slice form (up to 12 requests by default) multiplies each
+// slice plane alone by every request's limbs and lets each request add the
+// planes it reads.
 //
 // Arithmetic (exact, as in the batch-1 kernel): a pre-pass turns each
 // request's x, per column chunk, into a 24-bit fixed point held as three int8
 // limbs, laid out as B operands of v_mfma_i32_16x16x64_i8: column c = 3 rr + l
-// of a set of 16 requests holds limb l of request rr, 16 columns per MFMA
-// (NCG column groups per set: 1 for up to 5 requests, 2 up to 10, 3 up to
-// 16).  Codes are the A operands (16 rows x 64 columns, exactly the words a
-// lane loads); i32 accumulation is exact; the limbs of a request are combined
-// in fp64 after the chunk, through an LDS table of the block's 64 x 16 NCG
-// integer sums.
+// of a request set (16 requests at most, SS by the plan) holds limb l of
+// request rr, 16 columns per MFMA (NCG column groups per set: 1 for up to 5
+// requests, 2 up to 10, 3 up to 16).  Codes are the A operands (16 rows x 64
+// columns, exactly the words a lane loads); i32 accumulation is exact; the
+// limbs of a request are combined in fp64 after the chunk, through an LDS
+// table of the block's 64 x 16 NCG integer sums.
 //
-// A workgroup is one (block, column chunk): wave (ks, h) serves request set
-// h on the chunk's tiles ks, ks + KS, ...; the KS tables of a set are summed
-// when the outputs are formed, one row per lane, so y is written coalesced.
+// A workgroup is one (block, column chunk).  Per-depth form: wave (ks, h)
+// serves request set h on the chunk's tiles ks, ks + KS, ...; the KS tables
+// of a set are summed when the outputs are formed.  Per-slice form: wave
+// (h, p) takes plane p of the chunk for set h.  Either way one row per lane
+// forms the outputs, so y is written coalesced.
 
 #include <algorithm>
 #include <vector>
