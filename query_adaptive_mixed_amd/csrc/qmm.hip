@@ -663,12 +663,16 @@ struct MPlan {
 };
 
 static int64_t g_mfma_target_waves = 256 * 32;
-// Shortest column chunk, in tiles per request of the batch: a split of K
-// writes B fp64 partials per row and chunk, which must stay small next to
-// the chunk's weight bytes (64 B per row per tile and 2 bits of depth).
-static int g_mfma_tiles_per_request = 2;
-// Waves per request group splitting each chunk's tiles inside a workgroup.
-static int g_mfma_ksplit = 2;
+// Shortest column chunk, in tiles per request of the batch (0: by form, see
+// mfma_min_tiles): a split of K writes B fp64 partials per row and chunk and
+// reads them back, 16 B bytes per row against 64 bytes per row and tile of
+// weights at D8, so chunks shorter than a few B tiles spend a large share of
+// the traffic on partials.
+static int g_mfma_tiles_per_request = 0;
+// Waves per request set splitting each chunk's tiles inside a workgroup (at
+// most four waves per workgroup): a split inside the workgroup is reduced in
+// LDS, one across workgroups through partials in memory.
+static int g_mfma_ksplit = 4;
 
 // Most requests per set (three limb columns each, in 16-column groups).
 static int g_mfma_set_max = 0;   // 0: the default below; else 8..16
@@ -681,15 +685,29 @@ static int mfma_ncg(int64_t B) { return (3 * mfma_ss(B) + 15) / 16; }
 // waves per set splitting a chunk: at most four waves per workgroup
 static int mfma_ks(int64_t B) { return std::max(1, std::min(g_mfma_ksplit, 4 / mfma_sets(B))); }
 
+static bool per_slice_form(int64_t B, bool per_req, int NH);
+
+// Shortest column chunk in tiles.  Measured on the batched layer (4096 and
+// 14336 columns) and the streaming stack: per-request maps take chunks of at
+// least 32 tiles in the per-slice form (42 us against 50 us at 8 requests
+// with 16) and 96 in the per-depth form (45 us against 56 us at 16
+// requests with 32; 75 us against 90 us at 32 requests); shared maps 3 B
+// tiles (404 us against 430 us at 8 requests on the stack).
+static int mfma_min_tiles(int64_t B, bool per_req) {
+    if (g_mfma_tiles_per_request > 0) return (int)std::min<int64_t>(4096, (int64_t)g_mfma_tiles_per_request * B);
+    if (!per_req) return (int)(3 * B);
+    return per_slice_form(B, true, mfma_sets(B)) ? 32 : 96;
+}
+
 // Chunking of one matrix on the pre-pass route, for a chunk length goal.
-static MPlan mplan_goal(int64_t N, int64_t K, int64_t B, int goal) {
+static MPlan mplan_goal(int64_t N, int64_t K, int64_t B, int goal, bool per_req) {
     MPlan p{};
     p.NH = mfma_sets(B);
     p.SS = mfma_ss(B);
     p.NCG = mfma_ncg(B);
     p.KS = mfma_ks(B);
     const int n_tiles = (int)(K / kTileCols);
-    goal = std::max<int>(goal, (int)std::min<int64_t>(4096, (int64_t)g_mfma_tiles_per_request * B));
+    goal = std::max<int>(goal, mfma_min_tiles(B, per_req));
     const int want = (n_tiles + goal - 1) / goal;
     int tpc = (n_tiles + want - 1) / want;
     tpc = (tpc + 3) / 4 * 4;
@@ -705,9 +723,9 @@ static MPlan mplan_goal(int64_t N, int64_t K, int64_t B, int goal) {
     return p;
 }
 
-static MPlan mplan(int64_t N, int64_t K, int64_t B) {
+static MPlan mplan(int64_t N, int64_t K, int64_t B, bool per_req) {
     const int64_t block_tiles = N / kRows * (K / kTileCols) * mfma_sets(B) * mfma_ks(B);
-    return mplan_goal(N, K, B, chunk_goal(block_tiles, g_mfma_target_waves));
+    return mplan_goal(N, K, B, chunk_goal(block_tiles, g_mfma_target_waves), per_req);
 }
 
 static MItem make_mitem(const void* x, const qam_packed* w, const uint8_t* level_map, float* y, int per_request,
@@ -733,13 +751,13 @@ static MItem make_mitem(const void* x, const qam_packed* w, const uint8_t* level
 size_t qam_mfma_workspace_bytes(int64_t N, int64_t K, int64_t B) {
     if (N <= 0 || K <= 0 || N % kRows || K % kTileCols || K > QAM_MAX_K || B < 1 || B > QAM_MAX_BATCH_MFMA) return 0;
     if (N / kRows > QAM_MAX_BLOCKS) return 0;
-    return mplan(N, K, B).total;
+    return std::max(mplan(N, K, B, false).total, mplan(N, K, B, true).total);   // either kind of map
 }
 
 // The pre-pass route of qam_qmatvec (arguments already checked by the caller).
 int qmatvec_mfma(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
                  int per_request_maps, float* y, void* workspace, size_t workspace_bytes, hipStream_t s) {
-    const MPlan p = mplan(packed->N, packed->K, B);
+    const MPlan p = mplan(packed->N, packed->K, B, per_request_maps != 0);
     if (!workspace) QAM_FAIL(QAM_ERR_WORKSPACE, "qmatvec: workspace of %zu bytes required", p.total);
     if (workspace_bytes < p.total) QAM_FAIL(QAM_ERR_WORKSPACE, "qmatvec: workspace %zu < %zu bytes", workspace_bytes, p.total);
     if (!aligned(workspace, 256)) QAM_FAIL(QAM_ERR_ALIGN, "qmatvec: workspace must be 256-byte aligned");
@@ -775,7 +793,7 @@ struct MGroupLayout {
     int NH = 1, SS = 16, NCG = 1, KS = 1;
 };
 
-static int mfma_layout(const qam_gemv_item* items, int n_items, int64_t B, MGroupLayout& g) {
+static int mfma_layout(const qam_gemv_item* items, int n_items, int64_t B, bool per_req, MGroupLayout& g) {
     if (!items || n_items < 1) QAM_FAIL(QAM_ERR_ARG, "group: need at least one item");
     if (B < 2 || B > QAM_MAX_BATCH_MFMA) QAM_FAIL(QAM_ERR_ARG, "group: B=%lld outside [2, %d]", (long long)B, QAM_MAX_BATCH_MFMA);
     g.NH = mfma_sets(B);
@@ -793,7 +811,7 @@ static int mfma_layout(const qam_gemv_item* items, int n_items, int64_t B, MGrou
     if (g.blocks > QAM_MAX_BLOCKS) QAM_FAIL(QAM_ERR_SHAPE, "group: %lld blocks > %d", (long long)g.blocks, QAM_MAX_BLOCKS);
     const int goal = chunk_goal(block_tiles, g_mfma_target_waves);
     for (int i = 0; i < n_items; ++i) {
-        const MPlan p = mplan_goal(items[i].w.N, items[i].w.K, B, goal);
+        const MPlan p = mplan_goal(items[i].w.N, items[i].w.K, B, goal, per_req);
         g.plans.push_back(p);
         g.partials += p.partials;
         g.limbs += p.limbs;
@@ -810,16 +828,20 @@ static int mfma_layout(const qam_gemv_item* items, int n_items, int64_t B, MGrou
     return QAM_OK;
 }
 
+// Device bytes of a group on the pre-pass route: enough for either kind of map.
 size_t mfma_group_bytes(const qam_gemv_item* items, int n_items, int64_t B) {
+    MGroupLayout g2;
+    if (mfma_layout(items, n_items, B, true, g2) != QAM_OK) return 0;
     MGroupLayout g;
-    if (mfma_layout(items, n_items, B, g) != QAM_OK) return 0;
+    if (mfma_layout(items, n_items, B, false, g) != QAM_OK) return 0;
+    g.total = std::max(g.total, g2.total);
     return g.total;
 }
 
 int mfma_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dtype, int per_request_maps,
                     void* dev_mem, size_t dev_bytes, qam_group* out, hipStream_t s) {
     MGroupLayout g;
-    if (int rc = mfma_layout(items, n_items, B, g)) return rc;
+    if (int rc = mfma_layout(items, n_items, B, per_request_maps != 0, g)) return rc;
     if (dev_bytes < g.total) QAM_FAIL(QAM_ERR_WORKSPACE, "group_init: %zu < %zu bytes", dev_bytes, g.total);
     if (!aligned(dev_mem, 256)) QAM_FAIL(QAM_ERR_ALIGN, "group_init: device memory must be 256-byte aligned");
     char* base = static_cast<char*>(dev_mem);

@@ -212,6 +212,7 @@ def test_request_set_sizes(qam, set_max):
     from query_adaptive_mixed_amd import _lib as L
     lib = L.lib()
     try:
+        L.check(lib.qam_set_mfma_tiles_per_request(4))   # the same column chunks whatever the sets
         for B, per_request in ((16, True), (20, True), (32, True), (24, False)):
             rng, W, sc, x = problem(900 + B + set_max, 512, 4096, B)
             lv = rng.integers(0, 5, size=(B, 8) if per_request else 8).astype(np.uint8)
@@ -233,6 +234,7 @@ def test_request_set_sizes(qam, set_max):
             assert np.array_equal(host(g16._keep[0][2]).view(np.uint32), y16.view(np.uint32)), (B, "g16")
     finally:
         L.check(lib.qam_set_mfma_set_max(0))
+        L.check(lib.qam_set_mfma_tiles_per_request(0))
 
 
 @pytest.mark.parametrize("B", [3, 8, 16, 32])
@@ -240,7 +242,8 @@ def test_per_slice_and_per_depth_forms_agree(qam, B):
     """Per-request maps: the per-slice form (each plane times every request's
     limbs, then each request adds the planes it reads) and the per-depth form
     (codes at each depth times the limbs of the requests at that depth) sum
-    the same integers, so their outputs agree bit for bit, single and grouped."""
+    the same integers, so with the same column chunks (the fixed point of x is
+    per chunk) their outputs agree bit for bit, single and grouped."""
     from query_adaptive_mixed_amd import _lib as L
     lib = L.lib()
     rng, W, sc, x = problem(1200 + B, 768, 6144, B)
@@ -251,6 +254,7 @@ def test_per_slice_and_per_depth_forms_agree(qam, B):
     pm = qam.pack_slices(dev(W), dev(sc))
     out = {}
     try:
+        L.check(lib.qam_set_mfma_tiles_per_request(4))   # the same chunks for both forms
         for form, mx in (("slice", 32), ("depth", 0)):
             L.check(lib.qam_set_mfma_per_slice_max(mx))
             out[form] = host(qam.qmatvec(dev(x), pm, dev(lv)))
@@ -262,5 +266,6 @@ def test_per_slice_and_per_depth_forms_agree(qam, B):
             assert np.array_equal(host(yg).view(np.uint32), out[form].view(np.uint32)), (form, "group")
     finally:
         L.check(lib.qam_set_mfma_per_slice_max(12))
+        L.check(lib.qam_set_mfma_tiles_per_request(0))
     assert np.array_equal(out["slice"].view(np.uint32), out["depth"].view(np.uint32))
     check(out["slice"], W, sc, x, lv, True, B)
