@@ -25,14 +25,18 @@
  *     memory.
  *   - Work is enqueued on the caller's stream `s` (0 = the null stream) and
  *     is asynchronous: outputs are ready once the stream has reached that
- *     point.  A kernel fault surfaces at the caller's next synchronisation.
+ *     point (calls whose description says they synchronise `s` return with
+ *     their work done).  A kernel fault surfaces at the caller's next
+ *     synchronisation.
  *   - Every argument check runs on the host before anything is enqueued.  On
  *     failure a negative QAM_ERR_* code is returned, nothing is enqueued and
  *     qam_last_error() describes the problem.  Nothing aborts or throws across
  *     the ABI, and no call falls back silently to another kernel variant:
  *     qam_last_variant() names the variant the last successful call ran.
- *   - Calls are reentrant; the only library state is the thread-local error
- *     and variant strings.
+ *   - Calls are reentrant; the library's state is the thread-local error and
+ *     variant strings, plus the process-wide launch parameters that the
+ *     library's tuning hooks set (qam_set_*, exported for benchmarks and not
+ *     declared here): a call racing with a tuning hook is undefined.
  */
 #ifndef QAM_H
 #define QAM_H
