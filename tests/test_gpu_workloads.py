@@ -1,5 +1,6 @@
 """GPU parity at the benchmark's full sizes, in the launch configurations
-bench.py times: the whole E2B-shaped field in one grouped launch, the
+bench.py times: the whole E2B-shaped field in one grouped launch (with and
+without the level map built inside it), the
 streaming stack (batch 1 and 8), the batched per-request layer (16 and 32
 requests) and the full 28-layer Qwen3-0.6B-shaped decode step.  Outputs are
 checked against the oracle on sampled blocks (every row of a sampled block,
@@ -97,6 +98,37 @@ def test_e2b_field_grouped_launch(qam):
         assert L.lib().qam_set_staged_mfma(1) == 0
     for i, m in enumerate(fld.matrices):
         assert np.array_equal(host(items[i][2]).view(np.uint32), ys[i].view(np.uint32)), m.name
+
+
+def test_e2b_field_map_built_in_the_launch(qam):
+    """The launch bench.py times by default: one grouped launch over all 210
+    matrices that builds the level map itself.  Its map is the oracle's, bit
+    for bit, and its outputs are those of the map launch followed by the
+    plain grouped product, bit for bit."""
+    fld = WL.e2b_field(0)
+    c = CAL["e2b_field"]
+    lens = WL.e2b_lenses(fld, f=c["target_4.0"]["f"], g=c["g"])
+    want = O.level_map(fld.coords, lens.centres, lens.radii, lens.f, lens.g, lens.combine, 5, lens.glass)
+    cd = dev(fld.coords)
+    lv_dev = torch.full((fld.n_blocks,), 0xEE, dtype=torch.uint8, device="cuda")
+    items = field_items(qam, fld, lv_dev, 1)
+    offs = fld.block_offsets()
+    items = [it + (cd[offs[i]:offs[i] + m.n_blocks],) for i, (it, m) in enumerate(zip(items, fld.matrices))]
+    grp = qam.GroupedQmatvec(items)
+    grp.run_lens(qam.LensRules(lens.centres, lens.radii, lens.f, lens.g, lens.combine, lens.glass))
+    assert "staged_mfma_group_lens" in qam.last_variant()
+    assert np.array_equal(host(lv_dev), want)
+    fused = [host(it[2]).copy() for it in items]
+    lv_dev.fill_(0xEE)
+    qam.build_level_map(cd, lens.centres, lens.radii, lens.f, lens.g, lens.combine, lens.glass, out=lv_dev)
+    grp.run()
+    rng = np.random.default_rng(12)
+    for i, m in enumerate(fld.matrices):
+        assert np.array_equal(host(items[i][2]).view(np.uint32), fused[i].view(np.uint32)), m.name
+        if i % 7 == 0:
+            blocks = np.sort(rng.choice(m.n_blocks, 3, replace=False))
+            check_blocks(fused[i], fld.codes(i), fld.scales(i), fld.x(i, 1), want[offs[i]:offs[i] + m.n_blocks],
+                         blocks, False, m.name)
 
 
 @pytest.mark.parametrize("B", [1, 8])
