@@ -153,10 +153,22 @@ def test_streaming_stack_grouped_launch(qam, B):
     grp = qam.GroupedQmatvec(items)
     grp.run()
     assert ("staged_mfma_group" if B == 1 else "qmatvec_mfma_group") in qam.last_variant()
+    ys = []
     for i, m in enumerate(fld.matrices):
         blocks = np.sort(rng.choice(m.n_blocks, 3, replace=False))
-        check_blocks(host(items[i][2]), fld.codes(i), fld.scales(i), fld.x(i, B),
+        ys.append(host(items[i][2]).copy())
+        check_blocks(ys[-1], fld.codes(i), fld.scales(i), fld.x(i, B),
                      lv[offs[i]:offs[i] + m.n_blocks], blocks, False, (m.name, B))
+    if B == 1:   # bench.py's launch at batch 1: the map built inside it, the same map and bits
+        cd = dev(fld.coords)
+        items = [it + (cd[offs[i]:offs[i] + m.n_blocks],) for i, (it, m) in enumerate(zip(items, fld.matrices))]
+        grp = qam.GroupedQmatvec(items)
+        lv_dev.fill_(0xEE)
+        grp.run_lens(qam.LensRules(cen, rad, c["f"], 1.0, "sum", 1))
+        assert "staged_mfma_group_lens" in qam.last_variant()
+        assert np.array_equal(host(lv_dev), lv)
+        for i, m in enumerate(fld.matrices):
+            assert np.array_equal(host(items[i][2]).view(np.uint32), ys[i].view(np.uint32)), m.name
     del items, grp
     torch.cuda.empty_cache()
 
