@@ -280,10 +280,10 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   per-request maps a block is read once, to the deepest slice any request
  *   needs, and each request gets the codes at its own depth, built from the
  *   same words (the residual slices make the code at depth d the sum of the
- *   first d/2 slices): up to 12 requests each slice plane is multiplied by
- *   every request's limbs and each request adds the planes it reads; above,
- *   the codes at each depth present are multiplied by the limbs of the
- *   requests at that depth.  Both sum the same integers.  Both routes have the
+ *   first d/2 slices): the codes at each depth present are multiplied by
+ *   the limbs of the requests at that depth (or, selected by a tuning hook,
+ *   each slice plane by every request's limbs, each request adding the
+ *   planes it reads: the same integers).  Both routes have the
  *   arithmetic and bound above (the pre-pass route's fixed point is per
  *   column chunk).
  *

@@ -9,7 +9,7 @@
 // the first d/2 slices.  Two forms use that: the per-depth form builds the
 // codes for each depth present in the batch incrementally from the same
 // loaded words and multiplies them by the limbs of the requests at that
-// depth; the per-slice form (up to 12 requests by default) multiplies each
+// depth; the per-slice form (selectable by a tuning hook) multiplies each
 // slice plane alone by every request's limbs and lets each request add the
 // planes it reads.
 //
@@ -619,11 +619,12 @@ __global__ __launch_bounds__(512) void qmm_plane_kernel(MItem single, MCommon c)
 // ------------------------------------------------------------------ host side
 
 // Per-request maps take the per-slice form up to this many requests, the
-// per-depth form above (measured on the batched layer: per-slice 42 / 50 /
-// 60 / 57 us at 4 / 8 / 12 / 16 requests against per-depth 56 / 59 / 67 /
-// 56 us, and 108 us against 84 us at 32 requests, where the two sets' eight
-// waves share one workgroup).
-static int g_mfma_per_slice_max = 12;
+// per-depth form above.  0 by default: with 96-tile chunks and four waves
+// per set the per-depth form is ahead at every batch measured (4 / 8 / 12 /
+// 16 requests: 30 / 36 / 43 / 45 us against 31 / 42 / 48 / 50 us for the
+// per-slice form); the per-slice form stays selectable (tuning hook) and
+// gives the same bits with the same chunks.
+static int g_mfma_per_slice_max = 0;
 
 
 static bool per_slice_form(int64_t B, bool per_req, int NH) { return per_req && B <= g_mfma_per_slice_max && NH <= 2; }
@@ -685,18 +686,14 @@ static int mfma_ncg(int64_t B) { return (3 * mfma_ss(B) + 15) / 16; }
 // waves per set splitting a chunk: at most four waves per workgroup
 static int mfma_ks(int64_t B) { return std::max(1, std::min(g_mfma_ksplit, 4 / mfma_sets(B))); }
 
-static bool per_slice_form(int64_t B, bool per_req, int NH);
-
 // Shortest column chunk in tiles.  Measured on the batched layer (4096 and
 // 14336 columns) and the streaming stack: per-request maps take chunks of at
-// least 32 tiles in the per-slice form (42 us against 50 us at 8 requests
-// with 16) and 96 in the per-depth form (45 us against 56 us at 16
-// requests with 32; 75 us against 90 us at 32 requests); shared maps 3 B
-// tiles (404 us against 430 us at 8 requests on the stack).
+// least 96 tiles (per-depth form, 4 / 8 / 12 / 16 / 32 requests: 30 / 36 /
+// 43 / 45 / 75 us, against 35 / 42 / 52 / 56 / 90 us with 32-tile chunks);
+// shared maps 3 B tiles (404 us against 430 us at 8 requests on the stack).
 static int mfma_min_tiles(int64_t B, bool per_req) {
     if (g_mfma_tiles_per_request > 0) return (int)std::min<int64_t>(4096, (int64_t)g_mfma_tiles_per_request * B);
-    if (!per_req) return (int)(3 * B);
-    return per_slice_form(B, true, mfma_sets(B)) ? 32 : 96;
+    return per_req ? 96 : (int)(3 * B);
 }
 
 // Chunking of one matrix on the pre-pass route, for a chunk length goal.

@@ -265,7 +265,7 @@ def test_per_slice_and_per_depth_forms_agree(qam, B):
             assert f"form={form}" in qam.last_variant(), qam.last_variant()
             assert np.array_equal(host(yg).view(np.uint32), out[form].view(np.uint32)), (form, "group")
     finally:
-        L.check(lib.qam_set_mfma_per_slice_max(12))
+        L.check(lib.qam_set_mfma_per_slice_max(0))
         L.check(lib.qam_set_mfma_tiles_per_request(0))
     assert np.array_equal(out["slice"].view(np.uint32), out["depth"].view(np.uint32))
     check(out["slice"], W, sc, x, lv, True, B)
