@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     Gate,
     GroupedQmatvec,
     LensRules,
+    LensSets,
     PackedMatrix,
     Workspace,
     build_level_map,

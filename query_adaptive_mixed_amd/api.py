@@ -161,41 +161,55 @@ def fit_focus_area(coords: torch.Tensor, block_weights: torch.Tensor, centres, r
     return f.value, b.value, out
 
 
-def build_level_maps(coords: torch.Tensor, lens_sets, f, g: float = 1.0, combine: str = "sum", glass: int = 1,
-                     ladder_bits: Sequence[int] = LADDER_BITS, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """One map per request (uint8 [n_maps, n_blocks]): ``lens_sets`` is a
-    sequence of (centres [n_lenses, 2], radii [n_lenses]) pairs, all with the
-    same lens count; ``f`` a scalar or one value per map."""
+class LensSets:
+    """The lens-rule arguments of one map per request, marshalled once for the
+    C ABI: ``lens_sets`` is a sequence of (centres [n_lenses, 2], radii
+    [n_lenses]) pairs, all with the same lens count; ``f`` a scalar or one
+    value per map."""
+
+    def __init__(self, lens_sets, f, g: float = 1.0, combine: str = "sum", glass: int = 1,
+                 ladder_bits: Sequence[int] = LADDER_BITS):
+        self.n_maps = len(lens_sets)
+        fs = np.broadcast_to(np.asarray(f, dtype=np.float64), (self.n_maps,))
+        self.n_lenses = None
+        self.lenses = None
+        self.params = (L.QamLensParams * self.n_maps)()
+        for k, (centres, radii) in enumerate(lens_sets):
+            centres = np.asarray(centres, dtype=np.float64).reshape(-1, 2)
+            radii = np.asarray(radii, dtype=np.float64).reshape(-1)
+            if centres.shape[0] != radii.shape[0]:
+                raise ValueError("centres and radii disagree on the lens count")
+            if self.n_lenses is None:
+                self.n_lenses = centres.shape[0]
+                self.lenses = (L.QamLens * max(1, self.n_maps * self.n_lenses))()
+            elif centres.shape[0] != self.n_lenses:
+                raise ValueError("every map needs the same lens count")
+            for i in range(self.n_lenses):
+                lens = self.lenses[k * self.n_lenses + i]
+                lens.cx, lens.cy, lens.r = float(centres[i, 0]), float(centres[i, 1]), float(radii[i])
+            self.params[k].f, self.params[k].g = float(fs[k]), float(g)
+            self.params[k].combine = {"sum": L.QAM_COMBINE_SUM, "max": L.QAM_COMBINE_MAX}[combine]
+            self.params[k].n_stops = 0
+        self.n_rungs = len(ladder_bits)
+        self.ladder = (C.c_uint8 * self.n_rungs)(*ladder_bits)
+        self.glass = int(glass)
+
+
+def build_level_maps(coords: torch.Tensor, lens_sets=None, f=None, g: float = 1.0, combine: str = "sum",
+                     glass: int = 1, ladder_bits: Sequence[int] = LADDER_BITS, out: Optional[torch.Tensor] = None,
+                     sets: Optional[LensSets] = None) -> torch.Tensor:
+    """One map per request (uint8 [n_maps, n_blocks]) from ``lens_sets`` and
+    ``f`` as LensSets takes them, or from ``sets``, a LensSets."""
     _require_cuda(coords, "coords", torch.float64)
     n_blocks = coords.shape[0]
-    n_maps = len(lens_sets)
-    fs = np.broadcast_to(np.asarray(f, dtype=np.float64), (n_maps,))
-    n_lenses = None
-    lenses = None
-    params = (L.QamLensParams * n_maps)()
-    for k, (centres, radii) in enumerate(lens_sets):
-        centres = np.asarray(centres, dtype=np.float64).reshape(-1, 2)
-        radii = np.asarray(radii, dtype=np.float64).reshape(-1)
-        if centres.shape[0] != radii.shape[0]:
-            raise ValueError("centres and radii disagree on the lens count")
-        if n_lenses is None:
-            n_lenses = centres.shape[0]
-            lenses = (L.QamLens * max(1, n_maps * n_lenses))()
-        elif centres.shape[0] != n_lenses:
-            raise ValueError("every map needs the same lens count")
-        for i in range(n_lenses):
-            l = lenses[k * n_lenses + i]
-            l.cx, l.cy, l.r = float(centres[i, 0]), float(centres[i, 1]), float(radii[i])
-        params[k].f, params[k].g = float(fs[k]), float(g)
-        params[k].combine = {"sum": L.QAM_COMBINE_SUM, "max": L.QAM_COMBINE_MAX}[combine]
-        params[k].n_stops = 0
-    ladder = (C.c_uint8 * len(ladder_bits))(*ladder_bits)
+    st = sets if sets is not None else LensSets(lens_sets, f, g, combine, glass, ladder_bits)
     if out is None:
-        out = torch.empty((n_maps, n_blocks), dtype=torch.uint8, device=coords.device)
+        out = torch.empty((st.n_maps, n_blocks), dtype=torch.uint8, device=coords.device)
     else:
         _require_cuda(out, "out", torch.uint8)
-    L.check(L.lib().qam_build_level_maps(_ptr(coords), n_blocks, lenses, n_lenses, params, C.cast(ladder, C.c_void_p),
-                                         len(ladder_bits), int(glass), n_maps, _ptr(out), _stream_handle()))
+    L.check(L.lib().qam_build_level_maps(_ptr(coords), n_blocks, st.lenses, st.n_lenses, st.params,
+                                         C.cast(st.ladder, C.c_void_p), st.n_rungs, st.glass, st.n_maps, _ptr(out),
+                                         _stream_handle()))
     return out
 
 
