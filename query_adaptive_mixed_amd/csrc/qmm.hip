@@ -663,7 +663,10 @@ struct MPlan {
     size_t counters, partials, limbs, exps, total;
 };
 
-static int64_t g_mfma_target_waves = 256 * 32;
+// Wavefronts aimed for per launch (with four waves per set: on the streaming
+// stack, two chunks per 28672-column matrix; 337 / 405 us at 4 / 8 requests
+// against 370 / 430 us at half the target).
+static int64_t g_mfma_target_waves = 256 * 64;
 // Shortest column chunk, in tiles per request of the batch (0: by form, see
 // mfma_min_tiles): a split of K writes B fp64 partials per row and chunk and
 // reads them back, 16 B bytes per row against 64 bytes per row and tile of
