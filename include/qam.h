@@ -523,6 +523,8 @@ int qam_decoder_replay(qam_decoder* dec, int rung, hipStream_t s);
 /* Frees the host object and its graphs (not dev_mem). */
 void qam_decoder_destroy(qam_decoder* dec);
 
+/* qam_decoder_decode_gated is declared after qam_gate below. */
+
 /*
  * qam_escalation_schedule -- which of T decode steps are run again at 8 bits
  *   ([PoD] abstract: escalate the uncertain steps).  Exactly
@@ -568,6 +570,31 @@ typedef struct qam_uncertainty {
 size_t qam_gate_workspace_bytes(int64_t V);
 int qam_gate(const float* logits, int64_t V, double tau_entropy, double tau_margin,
              qam_uncertainty* out, void* workspace, size_t workspace_bytes, hipStream_t s);
+
+/*
+ * qam_decoder_decode_gated -- T decode steps with the escalation gate decided
+ *   on the device ([PoD] abstract: decode with the top bits, redo the step at
+ *   8 bits when the gate fires).  Per step t: h <- inputs[t], replay the
+ *   rung_low graph, qam_gate over the logits, read its result into
+ *   host_result (one synchronisation of `s`), and if it fired h <- inputs[t]
+ *   again and replay the rung_high graph.  Both rungs must have been
+ *   captured (qam_decoder_capture).
+ *   inputs         (device) fp32 [T][hidden].
+ *   gate_workspace (device) qam_gate_workspace_bytes(vocab) bytes, as for
+ *                  qam_gate; gate_out (device) one qam_uncertainty.
+ *   host_result    (host, pinned memory for speed) one qam_uncertainty.
+ *   escalated_out  (host) uint8 [T]: 1 where the step was redone.
+ *   Host-synchronous; not for graph capture.  Outputs of the last step stay
+ *   in the decoder's buffers.
+ *   Errors: QAM_ERR_NULL, QAM_ERR_ARG (T < 0, a rung not captured),
+ *   QAM_ERR_ALIGN, QAM_ERR_WORKSPACE, and whatever qam_gate returns; on an
+ *   error part way, the steps before it have run and escalated_out holds
+ *   their flags.
+ */
+int qam_decoder_decode_gated(qam_decoder* dec, const float* inputs, int64_t T, int rung_low, int rung_high,
+                             double tau_entropy, double tau_margin, void* gate_workspace,
+                             size_t gate_workspace_bytes, qam_uncertainty* gate_out,
+                             qam_uncertainty* host_result, uint8_t* escalated_out, hipStream_t s);
 
 /* ---------------------------------------------------------------- diagnostics */
 const char* qam_last_error(void);     /* thread-local, "" if none           */

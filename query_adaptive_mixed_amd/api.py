@@ -480,6 +480,25 @@ class Decoder:
     def replay(self, rung: int) -> None:
         L.check(L.lib().qam_decoder_replay(self._h, int(rung), _stream_handle()))
 
+    def decode_gated(self, inputs: torch.Tensor, gate: "Gate", tau_entropy: float = float("inf"),
+                     tau_margin: float = float("-inf"), rung_low: int = 2, rung_high: int = 4) -> np.ndarray:
+        """T steps (inputs [T, hidden] fp32 on the device) with the escalation
+        gate decided on the device each step, looped inside the library; both
+        rungs must be captured.  Returns uint8 [T], 1 where a step was redone
+        at ``rung_high``."""
+        _require_cuda(inputs, "inputs", torch.float32)
+        T = inputs.shape[0]
+        if inputs.dim() != 2 or inputs.shape[1] != self.hidden.numel():
+            raise ValueError("inputs must be [T, hidden]")
+        if gate.V != self.logits.numel():
+            raise ValueError("the gate must take the vocabulary's logits")
+        esc = np.zeros(T, dtype=np.uint8)
+        L.check(L.lib().qam_decoder_decode_gated(
+            self._h, _ptr(inputs), T, int(rung_low), int(rung_high), float(tau_entropy), float(tau_margin),
+            _ptr(gate.ws), gate.ws.numel(), _ptr(gate.out), C.c_void_p(gate._host.data_ptr()),
+            esc.ctypes.data_as(C.c_void_p), _stream_handle()))
+        return esc
+
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None and h.value:

@@ -244,6 +244,41 @@ extern "C" int qam_decoder_replay(qam_decoder* dec, int rung, hipStream_t s) {
     return QAM_OK;
 }
 
+extern "C" int qam_decoder_decode_gated(qam_decoder* dec, const float* inputs, int64_t T, int rung_low,
+                                        int rung_high, double tau_entropy, double tau_margin, void* gate_workspace,
+                                        size_t gate_workspace_bytes, qam_uncertainty* gate_out,
+                                        qam_uncertainty* host_result, uint8_t* escalated_out, hipStream_t s) {
+    clear_error();
+    if (!dec || !gate_out || !host_result || ((!inputs || !escalated_out) && T > 0))
+        QAM_FAIL(QAM_ERR_NULL, "decoder_decode_gated: null pointer");
+    if (T < 0) QAM_FAIL(QAM_ERR_ARG, "decoder_decode_gated: T < 0");
+    for (int r : {rung_low, rung_high})
+        if (r < 0 || r > 4 || !dec->exec[r]) QAM_FAIL(QAM_ERR_ARG, "decoder_decode_gated: rung %d was not captured", r);
+    if (!aligned(inputs, 4)) QAM_FAIL(QAM_ERR_ALIGN, "decoder_decode_gated: inputs not 4-byte aligned");
+    const int64_t H = dec->d.hidden, V = dec->d.vocab;
+    if (gate_workspace_bytes < qam_gate_workspace_bytes(V))
+        QAM_FAIL(QAM_ERR_WORKSPACE, "decoder_decode_gated: gate workspace %zu < %zu bytes", gate_workspace_bytes,
+                 qam_gate_workspace_bytes(V));
+    for (int64_t t = 0; t < T; ++t) {
+        const float* x = inputs + t * H;
+        QAM_HIP_CHECK(hipMemcpyAsync(dec->h, x, H * sizeof(float), hipMemcpyDeviceToDevice, s));
+        QAM_HIP_CHECK(hipGraphLaunch(dec->exec[rung_low], s));
+        if (int rc = qam_gate(dec->logits, V, tau_entropy, tau_margin, gate_out, gate_workspace,
+                              gate_workspace_bytes, s))
+            return rc;
+        QAM_HIP_CHECK(hipMemcpyAsync(host_result, gate_out, sizeof(qam_uncertainty), hipMemcpyDeviceToHost, s));
+        QAM_HIP_CHECK(hipStreamSynchronize(s));
+        escalated_out[t] = host_result->escalate ? 1 : 0;
+        if (host_result->escalate) {
+            QAM_HIP_CHECK(hipMemcpyAsync(dec->h, x, H * sizeof(float), hipMemcpyDeviceToDevice, s));
+            QAM_HIP_CHECK(hipGraphLaunch(dec->exec[rung_high], s));
+        }
+    }
+    QAM_HIP_CHECK(hipStreamSynchronize(s));
+    set_variant("decoder_decode_gated");
+    return QAM_OK;
+}
+
 extern "C" void qam_decoder_destroy(qam_decoder* dec) {
     if (!dec) return;
     for (int r = 0; r < 5; ++r) {

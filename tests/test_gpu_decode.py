@@ -6,6 +6,8 @@ one-product-at-a-time chain and HIP-graph replays must then agree bit for
 bit, since they launch the same kernels with the same chunking.
 """
 
+import math
+
 import numpy as np
 import pytest
 
@@ -243,3 +245,49 @@ def test_escalation_schedule_product_matches_oracle(qam):
     got = qam.escalation_schedule(scores, 0.16)
     assert np.array_equal(got, O.escalation_schedule(scores, 0.16))
     assert int(got.sum()) == 41
+
+
+def test_decode_gated_matches_step_by_step_loop(qam):
+    """The library's gated loop takes the same decisions, and leaves the same
+    bits in the decoder's buffers, as the loop driven step by step from the
+    host (replay the low rung, gate, replay the high rung on escalation)."""
+    fld, dec = _make_decoder(qam, SMALL)
+    T = 12
+    xs = dev(WL.decode_inputs(5, T, SMALL["hidden"]))
+    gate = qam.Gate(SMALL["vocab"])
+    with pytest.raises(qam.QamError):                 # rungs not captured yet
+        dec.decode_gated(xs, gate, 1.0)
+    dec.capture(2)
+    dec.capture(4)
+    ent = []
+    for t in range(T):
+        dec.hidden.copy_(xs[t])
+        dec.replay(2)
+        gate.run(dec.logits)
+        ent.append(gate.result()["entropy"])
+    srt = sorted(ent)
+    tau = 0.5 * (srt[T // 2 - 1] + srt[T // 2])       # fires on half the steps
+    want, last = [], None
+    for t in range(T):
+        dec.hidden.copy_(xs[t])
+        dec.replay(2)
+        gate.run(dec.logits, tau)
+        esc = gate.result()["escalate"]
+        if esc:
+            dec.hidden.copy_(xs[t])
+            dec.replay(4)
+        want.append(int(esc))
+        last = (host(dec.logits).copy(), host(dec.hidden).copy())
+    assert sum(want) == T // 2
+    for rep in range(2):
+        dec.hidden.zero_()
+        got = dec.decode_gated(xs, gate, tau)
+        assert got.tolist() == want, rep
+        assert np.array_equal(host(dec.logits), last[0]) and np.array_equal(host(dec.hidden), last[1]), rep
+    assert dec.decode_gated(xs[:0], gate, tau).size == 0
+    assert dec.decode_gated(xs, gate, math.inf, -math.inf).sum() == 0      # never fires
+    assert dec.decode_gated(xs, gate, -1.0).sum() == T                     # always fires (H >= 0 > -1)
+    with pytest.raises(ValueError):
+        dec.decode_gated(xs, qam.Gate(SMALL["vocab"] + 1), tau)
+    with pytest.raises(qam.QamError):
+        dec.decode_gated(xs, gate, tau, rung_low=1)
