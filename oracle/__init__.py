@@ -22,6 +22,9 @@ from .qam_oracle import (  # noqa: F401
     mean_bits,
     weight_bytes,
     fit_focus_area,
+    layer_scores,
+    layer_levels_threshold,
+    layer_levels_share,
     qmatvec_ref,
     qmatvec_tolerance,
     escalation_schedule,

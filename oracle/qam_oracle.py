@@ -351,6 +351,88 @@ def fit_focus_area(coords, centres, radii, g: float, combine: str, n_rungs: int,
 
 
 # --------------------------------------------------------------------------
+# Layer decides: per-block levels from the layer's own base read
+# --------------------------------------------------------------------------
+
+def layer_scores(y_base, scales, K: int) -> np.ndarray:
+    """Reduced draft scores, one per (request, block): fp64 [B, n_blocks].
+
+    [FoQLens] "FoQZones, the mechanism", the variant in which the layer
+    decides: the "draft" score of a unit is the squared norm of its output
+    read at the base depth times the square of its quantisation step,
+    s_c = |y_c(base)|^2 Delta_c^2, and the reduced score divides in the
+    step once more and the block's weights, s^_c = s_c Delta_c^2 / w_c.
+
+    Readings where the page is open: the unit c is a block of 64 output
+    rows; y_c(base) are its 64 outputs of the product at the base depth;
+    Delta_c^2 is the mean over the block's rows of the squared row scale
+    (the step of the stored 8-bit codes); w_c is the number of weights in
+    the block, 64 K.  Sums run over the block's rows in order, in fp64
+    (squares of fp32 values are exact there), and the reduced score is
+    ((|y_c|^2 Delta_c^2) Delta_c^2) / w_c, evaluated left to right.
+    """
+    y = np.asarray(y_base, dtype=np.float32).astype(np.float64)
+    y = y.reshape(-1, y.shape[-1])
+    B, N = y.shape
+    if N % ROWS_PER_BLOCK:
+        raise ValueError("N must be a multiple of 64")
+    nb = N // ROWS_PER_BLOCK
+    sc = np.asarray(scales, dtype=np.float32).astype(np.float64).reshape(nb, ROWS_PER_BLOCK)
+    yb = y.reshape(B, nb, ROWS_PER_BLOCK)
+    energy = np.zeros((B, nb))
+    step2 = np.zeros(nb)
+    for i in range(ROWS_PER_BLOCK):          # row by row, in order
+        energy = energy + yb[:, :, i] * yb[:, :, i]
+        step2 = step2 + sc[:, i] * sc[:, i]
+    step2 = step2 / ROWS_PER_BLOCK
+    w = np.float64(ROWS_PER_BLOCK * K)
+    draft = energy * step2[None, :]
+    return (draft * step2[None, :]) / w
+
+
+def layer_levels_threshold(shat, n_rungs: int, glass: int, g: float, lam: float) -> np.ndarray:
+    """Rung per block from its reduced score: uint8, the shape of ``shat``.
+
+    [FoQLens] "FoQZones, the mechanism", layer-decides variant:
+    level = gamma + #{j >= 1 : s^ >= lambda 16^j}, capped at the ceiling
+    kappa = gamma + floor(g (m - gamma)) (``ceiling``), m = n_rungs - 1.
+    The page leaves lambda open: it is the caller's parameter.  With the
+    cap, j runs over 1 .. kappa - gamma; 16^j is exact in fp64.  A NaN score
+    meets no threshold and stays at the glass.
+    """
+    shat = np.asarray(shat, dtype=np.float64)
+    kappa = ceiling(g, n_rungs - 1, glass)
+    level = np.full(shat.shape, glass, dtype=np.int64)
+    for j in range(1, kappa - glass + 1):
+        level = level + (shat >= np.float64(lam) * np.float64(16.0 ** j))
+    return level.astype(np.uint8)
+
+
+def layer_levels_share(shat, n_rungs: int, glass: int, g: float, share: float) -> np.ndarray:
+    """Rung per block by share: uint8, the shape of ``shat`` ([B, n_blocks]).
+
+    [FoQLens] "FoQZones, the mechanism", layer-decides variant, "by share":
+    the top f of the layer by reduced score rise and the rest stays at the
+    base.  Readings: per request, the floor(f n_blocks) blocks of largest
+    score rise to the ceiling kappa (``ceiling``); equal scores are ordered
+    by block index, the lower first; a NaN score ranks below every number
+    and never rises.
+    """
+    shat = np.asarray(shat, dtype=np.float64)
+    sh = shat.reshape(-1, shat.shape[-1])
+    B, nb = sh.shape
+    kappa = ceiling(g, n_rungs - 1, glass)
+    k = int(np.floor(np.float64(share) * np.float64(nb)))
+    level = np.full((B, nb), glass, dtype=np.uint8)
+    for r in range(B):
+        numbers = [c for c in range(nb) if not np.isnan(sh[r, c])]
+        order = sorted(numbers, key=lambda c: (-sh[r, c], c))
+        for c in order[:k]:
+            level[r, c] = kappa
+    return level.reshape(shat.shape)
+
+
+# --------------------------------------------------------------------------
 # Escalation: top-4-bit decode with a gated 8-bit re-run
 # --------------------------------------------------------------------------
 

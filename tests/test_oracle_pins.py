@@ -504,3 +504,105 @@ def test_fit_focus_area_ends_and_monotone():
     fs = [O.fit_focus_area(coords, cen, rad, 0.75, "max", 5, 1, w, low + k * (full - low) // 7, iters=24)[0]
           for k in range(8)]
     assert all(a <= b for a, b in zip(fs, fs[1:])) and fs[-1] == 1.0
+
+
+# ---------------------------------------------------------------- layer decides
+
+def test_layer_scores_hand_values():
+    """[FoQLens] "FoQZones, the mechanism", layer-decides variant: reduced
+    draft score |y_c|^2 Delta_c^2 Delta_c^2 / w_c, worked by hand."""
+    K = 64
+    y = np.zeros(192, np.float32)
+    y[:64] = 1.0                      # block 0: |y|^2 = 64
+    y[64 + 7] = 3.0                   # block 1: |y|^2 = 9
+    sc = np.full(192, 0.5, np.float32)
+    sc[64:128] = np.where(np.arange(64) % 2 == 0, 1.0, 3.0).astype(np.float32)   # mean scale^2 = 5
+    sc[128:] = 2.0                    # block 2: y = 0
+    got = O.layer_scores(y, sc, K)
+    assert got.shape == (1, 3)
+    # block 0: 64 * 0.25 * 0.25 / 4096 = 2^-10; block 1: 9 * 5 * 5 / 4096
+    assert got[0, 0] == 2.0 ** -10
+    assert got[0, 1] == 225.0 / 4096.0
+    assert got[0, 2] == 0.0
+
+
+def test_layer_scores_scaling_laws():
+    """Exact powers of two move the score by exact factors: outputs x4 give
+    x16 (the square of the output), scales x2 give x16 (the step enters
+    squared, twice), K x2 halves it (weights of the block); each block is
+    scored on its own rows only."""
+    rng = np.random.default_rng(3)
+    B, N, K = 3, 64 * 9, 128
+    y = rng.standard_normal((B, N)).astype(np.float32)
+    sc = rng.uniform(0.01, 0.2, N).astype(np.float32)
+    base = O.layer_scores(y, sc, K)
+    assert np.array_equal(O.layer_scores(y * 4, sc, K), base * 16)
+    assert np.array_equal(O.layer_scores(y, sc * 2, K), base * 16)
+    assert np.array_equal(O.layer_scores(y, sc, 2 * K), base / 2)
+    y2 = y.copy()
+    y2[1, 64 * 4:64 * 5] *= 4          # one block of one request
+    got = O.layer_scores(y2, sc, K)
+    want = base.copy()
+    want[1, 4] *= 16
+    assert np.array_equal(got, want)
+    sc2 = sc.copy()
+    sc2[64 * 6:64 * 7] *= 2            # one block's scales
+    want = base.copy()
+    want[:, 6] *= 16
+    assert np.array_equal(O.layer_scores(y, sc2, K), want)
+    # against a brute-force sum per block (in the same row order)
+    for r in range(B):
+        for c in range(N // 64):
+            e = 0.0
+            d = 0.0
+            for i in range(64):
+                e += float(y[r, 64 * c + i]) ** 2
+                d += float(sc[64 * c + i]) ** 2
+            d /= 64
+            assert base[r, c] == (e * d * d) / (64 * K)
+
+
+def test_layer_levels_threshold_rules():
+    """level = glass + #{j >= 1 : s >= lambda 16^j}, capped at kappa."""
+    lv = lambda s, g=1.0, lam=1.0, glass=1: O.layer_levels_threshold(np.array(s, np.float64), 5, glass, g, lam)
+    assert lv([0.0, 15.999, 16.0, 255.0, 256.0, 4096.0, 65536.0, 1e300]).tolist() == [1, 1, 2, 2, 3, 4, 4, 4]
+    assert lv([16.0, 256.0, 4096.0], g=0.7).tolist() == [2, 3, 3]        # kappa = 1 + floor(0.7 * 3) = 3
+    assert lv([16.0, 256.0, 4096.0], g=0.5).tolist() == [2, 2, 2]        # kappa = 1 + floor(0.5 * 3) = 2
+    assert lv([16.0, 4096.0], g=0.0).tolist() == [1, 1]                   # kappa = glass
+    assert lv([0.5, 8.0, 128.0], lam=0.5).tolist() == [1, 2, 3]           # 0.5*16 = 8, 0.5*256 = 128
+    assert lv([np.nan, np.inf], glass=0).tolist() == [0, 4]
+    assert lv([1.0], lam=0.0).tolist() == [4]                              # every threshold is 0
+    # scores x16 climb exactly one rung until the cap, once at or above
+    # lambda (j starts at 1: below lambda 16 a block stays at the glass)
+    rng = np.random.default_rng(4)
+    s = np.exp(rng.uniform(-5, 12, 2000))
+    a = lv(s, glass=0)
+    b = lv(s * 16, glass=0)
+    assert np.array_equal(b, np.minimum(a + (s >= 1.0), 4))
+    assert np.array_equal(a[s < 16.0], np.zeros(int(np.sum(s < 16.0)), np.uint8))
+
+
+def test_layer_levels_share_invariants():
+    """Per request exactly floor(f n) blocks rise to kappa, every one of them
+    scores at least every block left at the glass, and equal scores go in
+    block order."""
+    rng = np.random.default_rng(5)
+    B, nb = 4, 77
+    s = np.round(rng.uniform(0, 6, (B, nb)), 0)          # many ties
+    s[2, 10] = np.nan
+    for f in (0.0, 0.1, 0.5, 0.99, 1.0):
+        lv = O.layer_levels_share(s, 5, 1, 1.0, f)
+        for r in range(B):
+            risen = np.nonzero(lv[r] == 4)[0]
+            stay = np.nonzero(lv[r] == 1)[0]
+            assert len(risen) + len(stay) == nb
+            finite = int(np.sum(~np.isnan(s[r])))
+            assert len(risen) == min(int(np.floor(f * nb)), finite)
+            for a in risen:
+                assert not np.isnan(s[r, a])
+                for b in stay:
+                    if np.isnan(s[r, b]):
+                        continue
+                    assert s[r, a] > s[r, b] or (s[r, a] == s[r, b] and a < b)
+    lv = O.layer_levels_share(s, 5, 2, 0.5, 0.3)        # kappa = 2 + floor(0.5 * 2) = 3
+    assert set(np.unique(lv).tolist()) == {2, 3}
