@@ -232,6 +232,46 @@ int qam_fit_focus_area(const double* coords, int64_t n_blocks, const int64_t* bl
                        double* f_out, int64_t* bytes_out, hipStream_t s);
 
 /*
+ * qam_layer_levels -- level maps decided by the layer from its own read at
+ *   the base depth ([FoQLens] "FoQZones, the mechanism", the variant in which
+ *   the layer decides; scores and levels stay on the device).  Per request r
+ *   and block c (64 output rows):
+ *     s^ = ((|y_c|^2 Delta_c^2) Delta_c^2) / w_c   (the reduced draft score),
+ *   y_c the block's 64 values of y_base, Delta_c^2 the mean over its rows of
+ *   the squared row scale, w_c = 64 K; rows summed in order in fp64 (the
+ *   oracle's sums, bit for bit).  kappa = glass + floor(g (m - glass)),
+ *   m = n_rungs - 1.  Rung:
+ *     QAM_LAYER_THRESHOLD: glass + #{j in 1 .. kappa - glass : s^ >= lambda 16^j}
+ *       (lambda is left open by the page: the caller's; a NaN score stays
+ *       at the glass);
+ *     QAM_LAYER_SHARE: the floor(share n_blocks) blocks of largest s^ rise
+ *       to kappa (equal scores in block order, NaN scores never), the rest
+ *       stay at the glass.  Cost O(n_blocks^2) comparisons per request.
+ *   y_base     (device) fp32 [B][N], 16-byte aligned: the product at the
+ *              base depth (a uniform map at `glass`), as qam_qmatvec writes it.
+ *   B          0 .. 65535 requests (0: nothing is launched).
+ *   w          (host) the packed matrix; only N, K and its scales are read.
+ *   rule       (host) mode, lambda (not NaN), share in [0, 1], g in [0, 1].
+ *   shat_out   (device) fp64 [B][n_blocks]: the scores (written in both modes).
+ *   level_out  (device) uint8 [B][n_blocks]: the maps, as qam_qmatvec takes
+ *              per-request maps (row r is request r's map).
+ *   Errors: QAM_ERR_NULL, QAM_ERR_SHAPE, QAM_ERR_ARG, QAM_ERR_LADDER (glass
+ *   outside the ladder), QAM_ERR_ALIGN.  Asynchronous on `s`.
+ */
+#define QAM_LAYER_THRESHOLD 0
+#define QAM_LAYER_SHARE     1
+typedef struct qam_layer_rule {
+    int    mode;        /* QAM_LAYER_THRESHOLD or QAM_LAYER_SHARE */
+    int    reserved;
+    double lambda;      /* threshold mode: the lambda of lambda 16^j */
+    double share;       /* share mode: the share f of the blocks that rise */
+    double g;           /* focus strength: the ceiling kappa */
+} qam_layer_rule;
+
+int qam_layer_levels(const float* y_base, int64_t B, const qam_packed* w, const qam_layer_rule* rule,
+                     int n_rungs, int glass, double* shat_out, uint8_t* level_out, hipStream_t s);
+
+/*
  * qam_map_weight_bytes -- rule 7 and the bytes-read cost for a map (host).
  *   [Lens] rule 7: bits = sum_b w_b bits(b) / sum_b w_b; [PoD]: cost counted
  *   in weight bytes read.  w_b = 64 * K for every block of one matrix.

@@ -12,6 +12,9 @@ from .api import (  # noqa: F401
     Decoder,
     Gate,
     GroupedQmatvec,
+    LayerDecides,
+    LayerDecidesGroup,
+    LayerRule,
     LensRules,
     LensSets,
     PackedMatrix,
@@ -21,6 +24,7 @@ from .api import (  # noqa: F401
     escalation_schedule,
     fit_focus_area,
     last_variant,
+    layer_levels,
     map_weight_bytes,
     pack_slices,
     packed_bytes,

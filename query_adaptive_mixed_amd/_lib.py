@@ -39,6 +39,15 @@ class QamLensParams(C.Structure):
                 ("stops", C.c_double * QAM_MAX_STOPS)]
 
 
+QAM_LAYER_THRESHOLD = 0
+QAM_LAYER_SHARE = 1
+
+
+class QamLayerRule(C.Structure):
+    _fields_ = [("mode", C.c_int), ("reserved", C.c_int), ("lam", C.c_double), ("share", C.c_double),
+                ("g", C.c_double)]
+
+
 class QamGemvItem(C.Structure):
     _fields_ = [("w", QamPacked), ("x", C.c_void_p), ("y", C.c_void_p), ("level_map", C.c_void_p),
                 ("level_stride", C.c_int64), ("coords", C.c_void_p)]
@@ -105,6 +114,7 @@ SIGNATURES = [
     ("qam_qmatvec_group", _I, [C.POINTER(QamGroup), _P]),
     ("qam_qmatvec_group_lens", _I, [C.POINTER(QamGroup), C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I,
                                     _I, _P]),
+    ("qam_layer_levels", _I, [_P, _I64, C.POINTER(QamPacked), C.POINTER(QamLayerRule), _I, _I, _P, _P, _P]),
     ("qam_fit_focus_area", _I, [_P, _I64, _P, C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I, _I, _I64,
                                 _I, _P, _P, _SZ, C.POINTER(C.c_double), C.POINTER(C.c_int64), _P]),
     ("qam_decoder_decode_gated", _I, [_P, _P, _I64, _I, _I, C.c_double, C.c_double, _P, _SZ, _P, _P, _P, _P]),

@@ -387,6 +387,109 @@ class GroupedQmatvec:
                                                rules.n_rungs, rules.glass, _stream_handle()))
 
 
+class LayerRule:
+    """The rule by which a layer sets its blocks' rungs from its own base read
+    (libqam's ``qam_layer_levels``): ``lam`` for the lambda 16^j thresholds
+    or ``share`` for the top share, exactly one of them; ``g`` the focus
+    strength (ceiling), ``glass`` the base rung, ``n_rungs`` the ladder
+    length."""
+
+    def __init__(self, lam: Optional[float] = None, share: Optional[float] = None, g: float = 1.0, glass: int = 1,
+                 n_rungs: int = len(LADDER_BITS)):
+        if (lam is None) == (share is None):
+            raise ValueError("give exactly one of lam and share")
+        r = L.QamLayerRule()
+        r.mode = L.QAM_LAYER_THRESHOLD if share is None else L.QAM_LAYER_SHARE
+        r.lam = float(lam) if lam is not None else 0.0
+        r.share = float(share) if share is not None else 0.0
+        r.g = float(g)
+        self.rule = r
+        self.glass = int(glass)
+        self.n_rungs = int(n_rungs)
+
+
+def layer_levels(y_base: torch.Tensor, packed: PackedMatrix, rule: LayerRule, shat: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None):
+    """Per-request level maps uint8 [B, n_blocks] and the reduced scores fp64
+    [B, n_blocks] from the product at the base depth ``y_base`` fp32 [B, N]."""
+    _require_cuda(y_base, "y_base", torch.float32)
+    if y_base.dim() == 1:
+        y_base = y_base.unsqueeze(0)
+    B, N = y_base.shape
+    if N != packed.N:
+        raise ValueError(f"y_base has {N} columns, the matrix {packed.N} rows")
+    nb = packed.n_blocks
+    if shat is None:
+        shat = torch.empty((B, nb), dtype=torch.float64, device=y_base.device)
+    if out is None:
+        out = torch.empty((B, nb), dtype=torch.uint8, device=y_base.device)
+    _require_cuda(shat, "shat", torch.float64)
+    _require_cuda(out, "out", torch.uint8)
+    if shat.numel() != B * nb or out.numel() != B * nb:
+        raise ValueError("shat and out must hold B x n_blocks values")
+    L.check(L.lib().qam_layer_levels(_ptr(y_base), B, C.byref(packed.desc), C.byref(rule.rule), rule.n_rungs,
+                                     rule.glass, _ptr(shat), _ptr(out), _stream_handle()))
+    return out, shat
+
+
+class LayerDecides:
+    """One layer that decides its own depths: the product at the base rung
+    (a uniform map), the scores and levels on the device, then the product
+    at those levels (a map per request; one shared map at B = 1).  Buffers
+    are allocated once; ``run(x)`` returns y fp32 [B, N]."""
+
+    def __init__(self, packed: PackedMatrix, B: int, rule: LayerRule, device="cuda"):
+        self.packed, self.B, self.rule = packed, int(B), rule
+        nb = packed.n_blocks
+        self.base_map = torch.full((nb,), rule.glass, dtype=torch.uint8, device=device)
+        self.y_base = torch.empty((self.B, packed.N), dtype=torch.float32, device=device)
+        self.y = torch.empty((self.B, packed.N), dtype=torch.float32, device=device)
+        self.shat = torch.empty((self.B, nb), dtype=torch.float64, device=device)
+        self.levels = torch.empty((self.B, nb), dtype=torch.uint8, device=device)
+
+    def run(self, x: torch.Tensor) -> torch.Tensor:
+        qmatvec(x, self.packed, self.base_map, y=self.y_base)
+        layer_levels(self.y_base, self.packed, self.rule, shat=self.shat, out=self.levels)
+        qmatvec(x, self.packed, self.levels[0] if self.B == 1 else self.levels, y=self.y)
+        return self.y
+
+
+class LayerDecidesGroup:
+    """Several matrices that decide their own depths, grouped: one grouped
+    product at the glass (a uniform map), the scores and levels of each
+    matrix on the device, one grouped product at those maps (per request;
+    shared at B = 1).  ``items`` are (PackedMatrix, x [B, K], y [B, N])
+    tuples, bound once like GroupedQmatvec's; ``run()`` recomputes every y,
+    ``levels[i]`` holds matrix i's maps [B, n_blocks] afterwards."""
+
+    def __init__(self, items, rule: LayerRule, device="cuda"):
+        self.rule = rule
+        base_items, second_items, self.parts = [], [], []
+        for pm, x, y in items:
+            B = x.shape[0] if x.dim() == 2 else 1
+            nb = pm.n_blocks
+            base_map = torch.full((nb,), rule.glass, dtype=torch.uint8, device=device)
+            y_base = torch.empty((B, pm.N), dtype=torch.float32, device=device)
+            shat = torch.empty((B, nb), dtype=torch.float64, device=device)
+            lv = torch.empty((B, nb), dtype=torch.uint8, device=device)
+            base_items.append((pm, x, y_base, base_map))
+            second_items.append((pm, x, y, lv[0] if B == 1 else lv))
+            self.parts.append((pm, y_base, shat, lv))
+        self.base = GroupedQmatvec(base_items, device=device)
+        self.second = GroupedQmatvec(second_items, device=device)
+        self.levels = [p[3] for p in self.parts]
+
+    def decide(self) -> None:
+        """The scores and levels from the base outputs of the last run."""
+        for pm, y_base, shat, lv in self.parts:
+            layer_levels(y_base, pm, self.rule, shat=shat, out=lv)
+
+    def run(self) -> None:
+        self.base.run()
+        self.decide()
+        self.second.run()
+
+
 class Gate:
     """The escalation gate on the device: softmax entropy (nats) and top-two
     margin of a logits vector of length ``V``, and the decision

@@ -392,3 +392,36 @@ def test_fit_focus_area_rejects_before_any_launch(lib):
     assert call(ws=FAKEW + 8) == -5
     assert call(n_rungs=1) == -4
     assert call(glass=7) == -3
+
+
+def test_layer_levels_rejects_before_any_launch(lib):
+    FAKEW = 0x20000000            # 256-byte aligned stand-ins, never dereferenced
+    w = L.QamPacked(N=640, K=128, n_blocks=10, planes=FAKEW, scales=FAKEW + 640 * 128)
+
+    def rule(mode=L.QAM_LAYER_THRESHOLD, lam=1.0, share=0.5, g=1.0):
+        return L.QamLayerRule(mode=mode, reserved=0, lam=lam, share=share, g=g)
+
+    def call(y=FAKEW, B=2, ww=w, r=None, n_rungs=5, glass=1, shat=FAKEW, out=FAKEW):
+        r = rule() if r is None else r
+        return lib.qam_layer_levels(y, B, C.byref(ww) if ww is not None else None, C.byref(r), n_rungs, glass,
+                                    shat, out, None)
+
+    assert call(y=None) == -1
+    assert call(shat=None) == -1
+    assert call(out=None) == -1
+    assert call(ww=None) == -1
+    assert call(ww=L.QamPacked(N=640, K=128, n_blocks=9, planes=FAKEW, scales=FAKEW)) == -2
+    assert call(ww=L.QamPacked(N=600, K=128, n_blocks=9, planes=FAKEW, scales=FAKEW)) == -2
+    assert call(B=-1) == -3
+    assert call(B=65536) == -3
+    assert call(glass=5) == -4
+    assert call(n_rungs=0, glass=0) == -4
+    assert call(r=rule(mode=2)) == -3
+    assert call(r=rule(g=1.5)) == -3
+    assert call(r=rule(g=float("nan"))) == -3
+    assert call(r=rule(lam=float("nan"))) == -3
+    assert call(r=rule(mode=L.QAM_LAYER_SHARE, share=-0.1)) == -3
+    assert call(r=rule(mode=L.QAM_LAYER_SHARE, share=float("nan"))) == -3
+    assert call(y=FAKEW + 4) == -5
+    assert call(shat=FAKEW + 4) == -5
+    assert call(B=0, y=None, shat=None, out=None) == 0          # nothing to do, nothing launched

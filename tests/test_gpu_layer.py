@@ -1,0 +1,189 @@
+"""GPU parity of the layer-decides level maps (FoQLens, "FoQZones, the
+mechanism", the variant in which the layer decides) against the CPU oracle,
+through the C ABI: the reduced draft scores and both rules bit for bit on the
+same seeded base outputs, then the whole layer (base product, levels,
+product at the levels) against the oracle's product, its maps checked
+against the oracle's score bounds."""
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+TAG = 9100
+
+
+@pytest.fixture(scope="module")
+def qam():
+    import query_adaptive_mixed_amd as Q
+    return Q
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def packed(qam, seed, N, K):
+    W = WL.int8_codes(WL.stream(seed, TAG, 0), N, K)
+    sc = WL.row_scales(WL.stream(seed, TAG, 1), N)
+    return W, sc, qam.pack_slices(dev(W), dev(sc))
+
+
+def base_outputs(seed, B, N, spread=4.0):
+    """fp32 [B, N]: normal values with a per-block magnitude spread over a few
+    powers of 16, so the scores fall on several rungs."""
+    rng = WL.stream(seed, TAG, 2)
+    y = WL.activations(rng, B, N)
+    mag = np.exp2(rng.uniform(-spread, spread, (B, N // 64))).astype(np.float32)
+    return (y.reshape(B, N // 64, 64) * mag[:, :, None]).reshape(B, N)
+
+
+def device_levels(qam, y, pm, rule):
+    lv, sh = qam.layer_levels(dev(y), pm, rule)
+    torch.cuda.synchronize()
+    return lv.cpu().numpy(), sh.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,N,K", [(1, 64, 64), (3, 64 * 37, 128), (32, 64 * 300, 4096), (5, 64 * 1000, 64),
+                                   (2, 64 * 4099, 256)])
+def test_scores_and_threshold_levels_bit_exact(qam, B, N, K):
+    _, sc, pm = packed(qam, N + K, N, K)
+    y = base_outputs(B + N, B, N)
+    want_s = O.layer_scores(y, sc, K)
+    med = float(np.median(want_s))
+    for glass, g, lam in ((1, 1.0, med / 16), (0, 1.0, med / 256), (2, 0.5, med), (1, 0.75, want_s.flat[0] / 16),
+                          (1, 1.0, 0.0), (1, 1.0, np.inf), (1, 1.0, -1.0)):
+        lv, sh = device_levels(qam, y, pm, qam.LayerRule(lam=lam, g=g, glass=glass))
+        assert np.array_equal(sh, want_s), (glass, g, lam)
+        want = O.layer_levels_threshold(want_s, 5, glass, g, lam)
+        assert np.array_equal(lv, want), (glass, g, lam, np.bincount(lv.ravel()), np.bincount(want.ravel()))
+    assert len(np.unique(O.layer_levels_threshold(want_s, 5, 1, 1.0, med / 16))) >= min(3, want_s.size)
+
+
+@pytest.mark.parametrize("B,nb", [(1, 1), (4, 77), (32, 300), (1, 512), (2, 513), (2, 2374), (3, 1000)])
+def test_share_levels_bit_exact_with_ties_and_nan(qam, B, nb):
+    N, K = 64 * nb, 128
+    _, sc, pm = packed(qam, nb, N, K)
+    y = base_outputs(nb, B, N)
+    y3 = y.reshape(B, nb, 64)
+    if nb > 4:
+        y3[:, 3] = y3[:, 1]                               # equal scores when the scales agree too
+        y3[0, 2, 5] = np.nan                              # a NaN score never rises
+    y = y3.reshape(B, N)
+    sc3 = sc.reshape(nb, 64)
+    if nb > 4:
+        sc3[3] = sc3[1]
+    sc = sc3.reshape(N)
+    pm = qam.pack_slices(dev(WL.int8_codes(WL.stream(nb, TAG, 0), N, K)), dev(sc))
+    want_s = O.layer_scores(y, sc, K)
+    for f, g, glass in ((0.0, 1.0, 1), (0.1, 1.0, 1), (0.5, 0.5, 1), (0.999, 1.0, 0), (1.0, 1.0, 2)):
+        lv, sh = device_levels(qam, y, pm, qam.LayerRule(share=f, g=g, glass=glass))
+        assert np.array_equal(sh, want_s, equal_nan=True)
+        want = O.layer_levels_share(want_s, 5, glass, g, f)
+        assert np.array_equal(lv, want), (f, g, glass)
+
+
+def test_all_equal_scores_rise_in_block_order(qam):
+    nb, K = 513, 64
+    N = 64 * nb
+    pm = qam.pack_slices(dev(np.ones((N, K), np.int8)), dev(np.full(N, 0.01, np.float32)))
+    y = np.ones((2, N), np.float32)
+    lv, _ = device_levels(qam, y, pm, qam.LayerRule(share=0.25, glass=1))
+    k = int(np.floor(0.25 * nb))
+    assert np.array_equal(lv[0], np.r_[np.full(k, 4), np.full(nb - k, 1)].astype(np.uint8))
+    assert np.array_equal(lv[1], lv[0])
+
+
+def score_bounds(y_ref, tol, sc, K):
+    """The oracle's scores at the ends of each output's tolerance interval:
+    a device output within tol of y_ref gives a score between these."""
+    lo = np.maximum(np.abs(y_ref) - tol, 0.0)
+    hi = np.abs(y_ref) + tol
+    return O.layer_scores(lo, sc, K), O.layer_scores(hi, sc, K)
+
+
+@pytest.mark.parametrize("B", [1, 4, 32])
+def test_layer_decides_end_to_end(qam, B):
+    """Base product at the glass, levels on the device, product at the levels:
+    each block's rung lies between the oracle's rungs at its score bounds (and
+    equals them where they agree); the output matches the oracle's product
+    with that map."""
+    N, K = 64 * 96, 1024
+    W, sc, pm = packed(qam, 77, N, K)
+    x = WL.activations(WL.stream(77, TAG, 3), B, K)
+    glass = 1
+    ld = None
+    y_ref = O.qmatvec_ref(W, sc, x, np.full(N // 64, glass, np.uint8))
+    tol = O.qmatvec_tolerance(W, sc, x, np.full(N // 64, glass, np.uint8))
+    s_lo, s_hi = score_bounds(y_ref, tol, sc, K)
+    med = float(np.median(O.layer_scores(y_ref, sc, K)))
+    for rule_kw in (dict(lam=med / 16), dict(lam=med / 300), dict(share=0.3)):
+        rule = qam.LayerRule(glass=glass, **rule_kw)
+        ld = qam.LayerDecides(pm, B, rule)
+        y = ld.run(dev(x)).cpu().numpy()
+        lv = ld.levels.cpu().numpy()
+        if "lam" in rule_kw:
+            a = O.layer_levels_threshold(s_lo, 5, glass, 1.0, rule_kw["lam"])
+            b = O.layer_levels_threshold(s_hi, 5, glass, 1.0, rule_kw["lam"])
+            assert np.all((a <= lv) & (lv <= b)), rule_kw
+            assert np.mean(a == b) > 0.9
+        else:
+            k = int(np.floor(0.3 * (N // 64)))
+            for r in range(B):
+                risen, stay = lv[r] == 4, lv[r] == glass
+                assert risen.sum() == k and (risen | stay).all()
+                assert s_hi[r][risen].min() >= s_lo[r][stay].max()
+        ref = O.qmatvec_ref(W, sc, x, lv, per_request=True)
+        err = np.abs(y.astype(np.float64) - ref)
+        assert np.all(err <= O.qmatvec_tolerance(W, sc, x, lv, per_request=True)), rule_kw
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_layer_decides_group(qam, B):
+    """The grouped form over three matrices of different shapes: every map
+    between the oracle's maps at the score bounds, every output within the
+    tolerance of the oracle's product at that map; a second run repeats the
+    first bit for bit."""
+    shapes = [(64 * 40, 512), (64 * 17, 1024), (64 * 64, 256)]
+    mats, items, xs = [], [], []
+    for i, (N, K) in enumerate(shapes):
+        W, sc, pm = packed(qam, 300 + i, N, K)
+        x = WL.activations(WL.stream(300 + i, TAG, 3), B, K)
+        mats.append((W, sc))
+        xs.append(x)
+        items.append((pm, dev(x), torch.empty((B, N), dtype=torch.float32, device="cuda")))
+    glass = 1
+    for rule_kw in (dict(lam=None), dict(share=0.25)):
+        if rule_kw.get("lam", 0) is None:
+            W, sc = mats[0]
+            y_ref = O.qmatvec_ref(W, sc, xs[0], np.full(W.shape[0] // 64, glass, np.uint8))
+            rule_kw = dict(lam=float(np.median(O.layer_scores(y_ref, sc, W.shape[1]))) / 16)
+        grp = qam.LayerDecidesGroup(items, qam.LayerRule(glass=glass, **rule_kw))
+        grp.run()
+        first = [it[2].cpu().numpy().copy() for it in items]
+        for i, ((W, sc), x) in enumerate(zip(mats, xs)):
+            N, K = W.shape
+            lv = grp.levels[i].cpu().numpy()
+            uni = np.full(N // 64, glass, np.uint8)
+            s_lo, s_hi = score_bounds(O.qmatvec_ref(W, sc, x, uni), O.qmatvec_tolerance(W, sc, x, uni), sc, K)
+            if "lam" in rule_kw:
+                a = O.layer_levels_threshold(s_lo, 5, glass, 1.0, rule_kw["lam"])
+                b = O.layer_levels_threshold(s_hi, 5, glass, 1.0, rule_kw["lam"])
+                assert np.all((a <= lv) & (lv <= b)), (i, rule_kw)
+            else:
+                k = int(np.floor(0.25 * (N // 64)))
+                for r in range(B):
+                    risen, stay = lv[r] == 4, lv[r] == glass
+                    assert risen.sum() == k and (risen | stay).all()
+                    assert s_hi[r][risen].min() >= s_lo[r][stay].max()
+            ref = O.qmatvec_ref(W, sc, x, lv, per_request=True)
+            assert np.all(np.abs(first[i].astype(np.float64) - ref)
+                          <= O.qmatvec_tolerance(W, sc, x, lv, per_request=True)), (i, rule_kw)
+        grp.run()
+        for i, it in enumerate(items):
+            assert np.array_equal(it[2].cpu().numpy(), first[i]), i
