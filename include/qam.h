@@ -272,6 +272,30 @@ int qam_layer_levels(const float* y_base, int64_t B, const qam_packed* w, const 
                      int n_rungs, int glass, double* shat_out, uint8_t* level_out, hipStream_t s);
 
 /*
+ * qam_layer_levels_group -- qam_layer_levels for up to QAM_LAYER_GROUP_MAX
+ *   matrices of one layer in one launch (same rule, glass and batch B; the
+ *   same scores and maps, bit for bit, as one qam_layer_levels call per
+ *   item).  A workgroup per (item, request) scores the request's blocks
+ *   and, in share mode, ranks them in LDS, so every item must have at most
+ *   512 blocks (QAM_ERR_SHAPE otherwise; call qam_layer_levels for larger
+ *   ones).
+ *   items   (host) [n_items], 1 <= n_items <= QAM_LAYER_GROUP_MAX: each
+ *           item's base outputs, packed matrix, scores and maps, laid out
+ *           and aligned as in qam_layer_levels.
+ *   Errors: as qam_layer_levels, naming the item.  Asynchronous on `s`.
+ */
+#define QAM_LAYER_GROUP_MAX 16
+typedef struct qam_layer_item {
+    const float* y_base;   /* (device) fp32 [B][N] */
+    qam_packed   w;        /* N, K and the scales are read */
+    double*      shat_out; /* (device) fp64 [B][n_blocks] */
+    uint8_t*     level_out;/* (device) uint8 [B][n_blocks] */
+} qam_layer_item;
+
+int qam_layer_levels_group(const qam_layer_item* items, int n_items, int64_t B, const qam_layer_rule* rule,
+                           int n_rungs, int glass, hipStream_t s);
+
+/*
  * qam_map_weight_bytes -- rule 7 and the bytes-read cost for a map (host).
  *   [Lens] rule 7: bits = sum_b w_b bits(b) / sum_b w_b; [PoD]: cost counted
  *   in weight bytes read.  w_b = 64 * K for every block of one matrix.

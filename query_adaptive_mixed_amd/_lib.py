@@ -48,6 +48,13 @@ class QamLayerRule(C.Structure):
                 ("g", C.c_double)]
 
 
+QAM_LAYER_GROUP_MAX = 16
+
+
+class QamLayerItem(C.Structure):
+    _fields_ = [("y_base", C.c_void_p), ("w", QamPacked), ("shat_out", C.c_void_p), ("level_out", C.c_void_p)]
+
+
 class QamGemvItem(C.Structure):
     _fields_ = [("w", QamPacked), ("x", C.c_void_p), ("y", C.c_void_p), ("level_map", C.c_void_p),
                 ("level_stride", C.c_int64), ("coords", C.c_void_p)]
@@ -115,6 +122,7 @@ SIGNATURES = [
     ("qam_qmatvec_group_lens", _I, [C.POINTER(QamGroup), C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I,
                                     _I, _P]),
     ("qam_layer_levels", _I, [_P, _I64, C.POINTER(QamPacked), C.POINTER(QamLayerRule), _I, _I, _P, _P, _P]),
+    ("qam_layer_levels_group", _I, [C.POINTER(QamLayerItem), _I, _I64, C.POINTER(QamLayerRule), _I, _I, _P]),
     ("qam_fit_focus_area", _I, [_P, _I64, _P, C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I, _I, _I64,
                                 _I, _P, _P, _SZ, C.POINTER(C.c_double), C.POINTER(C.c_int64), _P]),
     ("qam_decoder_decode_gated", _I, [_P, _P, _I64, _I, _I, C.c_double, C.c_double, _P, _SZ, _P, _P, _P, _P]),

@@ -460,7 +460,8 @@ class LayerDecidesGroup:
     matrix on the device, one grouped product at those maps (per request;
     shared at B = 1).  ``items`` are (PackedMatrix, x [B, K], y [B, N])
     tuples, bound once like GroupedQmatvec's; ``run()`` recomputes every y,
-    ``levels[i]`` holds matrix i's maps [B, n_blocks] afterwards."""
+    ``levels[i]`` holds matrix i's maps [B, n_blocks] afterwards.  Up to 16
+    matrices of at most 512 blocks each share one level launch."""
 
     def __init__(self, items, rule: LayerRule, device="cuda"):
         self.rule = rule
@@ -478,9 +479,22 @@ class LayerDecidesGroup:
         self.base = GroupedQmatvec(base_items, device=device)
         self.second = GroupedQmatvec(second_items, device=device)
         self.levels = [p[3] for p in self.parts]
+        # one launch for every matrix when each has at most 512 blocks
+        self._table = None
+        n = len(self.parts)
+        if n <= L.QAM_LAYER_GROUP_MAX and all(p[0].n_blocks <= 512 for p in self.parts):
+            self._table = (L.QamLayerItem * n)()
+            for i, (pm, y_base, shat, lv) in enumerate(self.parts):
+                self._table[i].y_base, self._table[i].w = y_base.data_ptr(), pm.desc
+                self._table[i].shat_out, self._table[i].level_out = shat.data_ptr(), lv.data_ptr()
+            self._B = self.parts[0][1].shape[0]
 
     def decide(self) -> None:
         """The scores and levels from the base outputs of the last run."""
+        if self._table is not None:
+            L.check(L.lib().qam_layer_levels_group(self._table, len(self.parts), self._B, C.byref(self.rule.rule),
+                                                   self.rule.n_rungs, self.rule.glass, _stream_handle()))
+            return
         for pm, y_base, shat, lv in self.parts:
             layer_levels(y_base, pm, self.rule, shat=shat, out=lv)
 

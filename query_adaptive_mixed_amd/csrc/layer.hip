@@ -133,30 +133,81 @@ layer_share_kernel(const double* __restrict__ shat, int64_t nb, int64_t k, int g
     if (c < nb) level[r * nb + c] = (uint8_t)((!isnan(key) && rank < k) ? kappa : glass);
 }
 
+// One matrix of a grouped call, as the kernel sees it.
+struct LayerItem {
+    const float* y;
+    const float* scales;
+    double* shat;
+    uint8_t* level;
+    int64_t N, nb;
+    double w;
+    int64_t k;            // share mode: blocks that rise per request
+};
+
+struct LayerGroupArgs {
+    LayerItem items[QAM_LAYER_GROUP_MAX];
+    int64_t B;
+    int mode, glass, lifts, kappa;
+    double lambda;
+};
+
+// Every matrix of a group in one launch: a workgroup per (item, request),
+// each scoring that request's blocks (at most kLayerFusedMax) and, in share
+// mode, ranking them in LDS; the same arithmetic as the single-matrix kernels.
+__global__ void __launch_bounds__(kLayerThreads) layer_group_kernel(LayerGroupArgs g) {
+    __shared__ double sc[kLayerFusedMax];
+    const int64_t item = blockIdx.x / g.B, r = blockIdx.x - item * g.B;
+    const LayerItem& it = g.items[item];
+    const int64_t nb = it.nb;
+    for (int64_t c = threadIdx.x; c < nb; c += kLayerThreads) {
+        const double score = block_score(it.y, it.scales, r, c, it.N, it.w);
+        it.shat[r * nb + c] = score;
+        if (g.mode == QAM_LAYER_THRESHOLD) it.level[r * nb + c] = (uint8_t)threshold_rung(score, g.lambda, g.glass, g.lifts);
+        else sc[c] = score;
+    }
+    if (g.mode == QAM_LAYER_THRESHOLD) return;
+    __syncthreads();
+    for (int64_t c = threadIdx.x; c < nb; c += kLayerThreads) {
+        const double key = sc[c];
+        int64_t rank = 0;
+        for (int64_t b = 0; b < nb; ++b) rank += ranks_ahead(sc[b], b, key, c);
+        it.level[r * nb + c] = (uint8_t)((!isnan(key) && rank < it.k) ? g.kappa : g.glass);
+    }
+}
+
 }  // namespace qam
 
 using namespace qam;
 
+// Checks shared by the entry points (error text names `who`).
+static int check_layer(const qam_packed* w, int64_t B, const qam_layer_rule* rule, int n_rungs, int glass,
+                       const char* who) {
+    const int64_t N = w->N, K = w->K, nb = w->n_blocks;
+    if (!w->scales) QAM_FAIL(QAM_ERR_NULL, "%s: null scales", who);
+    if (N <= 0 || K <= 0 || N % 64 || K % 64 || K > QAM_MAX_K || nb != N / 64 || nb > QAM_MAX_BLOCKS)
+        QAM_FAIL(QAM_ERR_SHAPE, "%s: bad packed shape N=%lld K=%lld", who, (long long)N, (long long)K);
+    if (B < 0 || B > 65535) QAM_FAIL(QAM_ERR_ARG, "%s: B=%lld outside [0, 65535]", who, (long long)B);
+    if (n_rungs < 1 || n_rungs > QAM_MAX_RUNGS || glass < 0 || glass >= n_rungs)
+        QAM_FAIL(QAM_ERR_LADDER, "%s: glass %d outside a ladder of %d rungs", who, glass, n_rungs);
+    if (rule->mode != QAM_LAYER_THRESHOLD && rule->mode != QAM_LAYER_SHARE)
+        QAM_FAIL(QAM_ERR_ARG, "%s: unknown mode %d", who, rule->mode);
+    if (!(rule->g >= 0.0 && rule->g <= 1.0)) QAM_FAIL(QAM_ERR_ARG, "%s: g outside [0, 1]", who);
+    if (rule->mode == QAM_LAYER_THRESHOLD && isnan(rule->lambda)) QAM_FAIL(QAM_ERR_ARG, "%s: lambda is NaN", who);
+    if (rule->mode == QAM_LAYER_SHARE && !(rule->share >= 0.0 && rule->share <= 1.0))
+        QAM_FAIL(QAM_ERR_ARG, "%s: share outside [0, 1]", who);
+    if (!aligned(w->scales, 16)) QAM_FAIL(QAM_ERR_ALIGN, "%s: scales must be 16-byte aligned", who);
+    return QAM_OK;
+}
+
 extern "C" int qam_layer_levels(const float* y_base, int64_t B, const qam_packed* w, const qam_layer_rule* rule,
                                 int n_rungs, int glass, double* shat_out, uint8_t* level_out, hipStream_t s) {
     clear_error();
-    if (!w || !rule || !w->scales || ((!y_base || !shat_out || !level_out) && B > 0))
+    if (!w || !rule || ((!y_base || !shat_out || !level_out) && B > 0))
         QAM_FAIL(QAM_ERR_NULL, "layer_levels: null pointer");
+    if (int rc = check_layer(w, B, rule, n_rungs, glass, "layer_levels")) return rc;
+    if (!aligned(y_base, 16) || !aligned(shat_out, 8))
+        QAM_FAIL(QAM_ERR_ALIGN, "layer_levels: y_base must be 16-byte, shat_out 8-byte aligned");
     const int64_t N = w->N, K = w->K, nb = w->n_blocks;
-    if (N <= 0 || K <= 0 || N % 64 || K % 64 || K > QAM_MAX_K || nb != N / 64 || nb > QAM_MAX_BLOCKS)
-        QAM_FAIL(QAM_ERR_SHAPE, "layer_levels: bad packed shape N=%lld K=%lld", (long long)N, (long long)K);
-    if (B < 0 || B > 65535) QAM_FAIL(QAM_ERR_ARG, "layer_levels: B=%lld outside [0, 65535]", (long long)B);
-    if (n_rungs < 1 || n_rungs > QAM_MAX_RUNGS || glass < 0 || glass >= n_rungs)
-        QAM_FAIL(QAM_ERR_LADDER, "layer_levels: glass %d outside a ladder of %d rungs", glass, n_rungs);
-    if (rule->mode != QAM_LAYER_THRESHOLD && rule->mode != QAM_LAYER_SHARE)
-        QAM_FAIL(QAM_ERR_ARG, "layer_levels: unknown mode %d", rule->mode);
-    if (!(rule->g >= 0.0 && rule->g <= 1.0)) QAM_FAIL(QAM_ERR_ARG, "layer_levels: g outside [0, 1]");
-    if (rule->mode == QAM_LAYER_THRESHOLD && isnan(rule->lambda))
-        QAM_FAIL(QAM_ERR_ARG, "layer_levels: lambda is NaN");
-    if (rule->mode == QAM_LAYER_SHARE && !(rule->share >= 0.0 && rule->share <= 1.0))
-        QAM_FAIL(QAM_ERR_ARG, "layer_levels: share outside [0, 1]");
-    if (!aligned(y_base, 16) || !aligned(w->scales, 16) || !aligned(shat_out, 8))
-        QAM_FAIL(QAM_ERR_ALIGN, "layer_levels: y_base and scales must be 16-byte, shat_out 8-byte aligned");
     const int m = n_rungs - 1;
     const int kappa = glass + (int)floor(rule->g * (double)(m - glass));
     if (B == 0) {
@@ -185,5 +236,47 @@ extern "C" int qam_layer_levels(const float* y_base, int64_t B, const qam_packed
         QAM_HIP_CHECK(hipGetLastError());
     }
     set_variant(rule->mode == QAM_LAYER_SHARE ? "layer_levels_share" : "layer_levels_threshold");
+    return QAM_OK;
+}
+
+extern "C" int qam_layer_levels_group(const qam_layer_item* items, int n_items, int64_t B,
+                                      const qam_layer_rule* rule, int n_rungs, int glass, hipStream_t s) {
+    clear_error();
+    if (!items || !rule) QAM_FAIL(QAM_ERR_NULL, "layer_levels_group: null pointer");
+    if (n_items < 1 || n_items > QAM_LAYER_GROUP_MAX)
+        QAM_FAIL(QAM_ERR_ARG, "layer_levels_group: %d items outside [1, %d]", n_items, QAM_LAYER_GROUP_MAX);
+    LayerGroupArgs g{};
+    for (int i = 0; i < n_items; ++i) {
+        const qam_layer_item& q = items[i];
+        if ((!q.y_base || !q.shat_out || !q.level_out) && B > 0)
+            QAM_FAIL(QAM_ERR_NULL, "layer_levels_group: item %d: null pointer", i);
+        if (int rc = check_layer(&q.w, B, rule, n_rungs, glass, "layer_levels_group")) return rc;
+        if (q.w.n_blocks > kLayerFusedMax)
+            QAM_FAIL(QAM_ERR_SHAPE, "layer_levels_group: item %d has %lld blocks, more than %lld", i,
+                     (long long)q.w.n_blocks, (long long)kLayerFusedMax);
+        if (!aligned(q.y_base, 16) || !aligned(q.shat_out, 8))
+            QAM_FAIL(QAM_ERR_ALIGN, "layer_levels_group: item %d: y_base must be 16-byte, shat_out 8-byte aligned", i);
+        LayerItem& it = g.items[i];
+        it.y = q.y_base;
+        it.scales = q.w.scales;
+        it.shat = q.shat_out;
+        it.level = q.level_out;
+        it.N = q.w.N;
+        it.nb = q.w.n_blocks;
+        it.w = (double)(64 * q.w.K);
+        it.k = (int64_t)floor(rule->share * (double)q.w.n_blocks);
+    }
+    const int kappa = glass + (int)floor(rule->g * (double)(n_rungs - 1 - glass));
+    g.B = B;
+    g.mode = rule->mode;
+    g.glass = glass;
+    g.lifts = kappa - glass;
+    g.kappa = kappa;
+    g.lambda = rule->lambda;
+    if (B > 0) {
+        hipLaunchKernelGGL(layer_group_kernel, dim3((unsigned)(n_items * B)), dim3(kLayerThreads), 0, s, g);
+        QAM_HIP_CHECK(hipGetLastError());
+    }
+    set_variant("layer_levels_group");
     return QAM_OK;
 }

@@ -425,3 +425,27 @@ def test_layer_levels_rejects_before_any_launch(lib):
     assert call(y=FAKEW + 4) == -5
     assert call(shat=FAKEW + 4) == -5
     assert call(B=0, y=None, shat=None, out=None) == 0          # nothing to do, nothing launched
+
+
+def test_layer_levels_group_rejects_before_any_launch(lib):
+    FAKEW = 0x20000000
+
+    def item(nb=10, y=FAKEW, shat=FAKEW, out=FAKEW):
+        w = L.QamPacked(N=64 * nb, K=128, n_blocks=nb, planes=FAKEW, scales=FAKEW + 64 * nb * 128)
+        return L.QamLayerItem(y_base=y, w=w, shat_out=shat, level_out=out)
+
+    rule = L.QamLayerRule(mode=L.QAM_LAYER_SHARE, reserved=0, lam=1.0, share=0.5, g=1.0)
+
+    def call(items, n=None, B=2, r=rule, glass=1):
+        arr = (L.QamLayerItem * max(1, len(items)))(*items)
+        return lib.qam_layer_levels_group(arr, len(items) if n is None else n, B, C.byref(r), 5, glass, None)
+
+    assert lib.qam_layer_levels_group(None, 1, 2, C.byref(rule), 5, 1, None) == -1
+    assert call([item()], n=0) == -3
+    assert call([item()] * 17) == -3
+    assert call([item(), item(y=None)]) == -1
+    assert call([item(), item(nb=513)]) == -2
+    assert call([item(), item(y=FAKEW + 4)]) == -5
+    assert call([item()], glass=5) == -4
+    assert call([item()], r=L.QamLayerRule(mode=L.QAM_LAYER_SHARE, reserved=0, lam=1.0, share=2.0, g=1.0)) == -3
+    assert call([item(y=None, shat=None, out=None)], B=0) == 0      # nothing to do, nothing launched

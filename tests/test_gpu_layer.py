@@ -187,3 +187,36 @@ def test_layer_decides_group(qam, B):
         grp.run()
         for i, it in enumerate(items):
             assert np.array_equal(it[2].cpu().numpy(), first[i]), i
+
+
+@pytest.mark.parametrize("B", [1, 5])
+def test_group_call_bit_exact(qam, B):
+    """One launch for several matrices gives each matrix the scores and maps
+    of the oracle, bit for bit, in both modes."""
+    from query_adaptive_mixed_amd import _lib as L
+    import ctypes as C
+    nbs, K = (1, 77, 512, 200), 128
+    tabs = []
+    arr = (L.QamLayerItem * len(nbs))()
+    for i, nb in enumerate(nbs):
+        _, sc, pm = packed(qam, 500 + i, 64 * nb, K)
+        y = base_outputs(500 + i, B, 64 * nb)
+        if nb > 4:
+            y.reshape(B, nb, 64)[:, 3] = y.reshape(B, nb, 64)[:, 1]
+        yd = dev(y)
+        sh = torch.empty((B, nb), dtype=torch.float64, device="cuda")
+        lv = torch.empty((B, nb), dtype=torch.uint8, device="cuda")
+        arr[i].y_base, arr[i].w, arr[i].shat_out, arr[i].level_out = yd.data_ptr(), pm.desc, sh.data_ptr(), lv.data_ptr()
+        tabs.append((y, sc, pm, yd, sh, lv))
+    for kw in (dict(share=0.3), dict(share=1.0, g=0.5), dict(lam=1e-9), dict(lam=0.0, glass=2)):
+        rule = qam.LayerRule(**kw)
+        L.check(L.lib().qam_layer_levels_group(arr, len(nbs), B, C.byref(rule.rule), rule.n_rungs, rule.glass, None))
+        torch.cuda.synchronize()
+        for y, sc, pm, yd, sh, lv in tabs:
+            want_s = O.layer_scores(y, sc, K)
+            assert np.array_equal(sh.cpu().numpy(), want_s), kw
+            if "share" in kw:
+                want = O.layer_levels_share(want_s, 5, rule.glass, kw.get("g", 1.0), kw["share"])
+            else:
+                want = O.layer_levels_threshold(want_s, 5, rule.glass, 1.0, kw["lam"])
+            assert np.array_equal(lv.cpu().numpy(), want), (kw, pm.n_blocks)
