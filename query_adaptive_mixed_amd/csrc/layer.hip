@@ -71,6 +71,22 @@ __device__ __forceinline__ bool ranks_ahead(double v, int64_t b, double key, int
     return v > key || (v == key && b < c);
 }
 
+// Blocks of sc[0, nb) ahead of (key, c), nb <= kLayerFusedMax: four
+// independent counts (integer, so their order does not matter), so that
+// several LDS reads are in flight at once.
+__device__ __forceinline__ int64_t count_ahead(const double* sc, int nb, double key, int c) {
+    int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+    int b = 0;
+    for (; b + 4 <= nb; b += 4) {
+        r0 += ranks_ahead(sc[b], b, key, c);
+        r1 += ranks_ahead(sc[b + 1], b + 1, key, c);
+        r2 += ranks_ahead(sc[b + 2], b + 2, key, c);
+        r3 += ranks_ahead(sc[b + 3], b + 3, key, c);
+    }
+    for (; b < nb; ++b) r0 += ranks_ahead(sc[b], b, key, c);
+    return (int64_t)r0 + r1 + r2 + r3;
+}
+
 // One thread per (request, block): the score and, in threshold mode, the rung.
 __global__ void __launch_bounds__(kLayerThreads)
 layer_score_kernel(const float* __restrict__ y, const float* __restrict__ scales, int64_t B, int64_t nb,
@@ -101,8 +117,7 @@ layer_share_fused_kernel(const float* __restrict__ y, const float* __restrict__ 
     __syncthreads();
     for (int64_t c = threadIdx.x; c < nb; c += kLayerThreads) {
         const double key = sc[c];
-        int64_t rank = 0;
-        for (int64_t b = 0; b < nb; ++b) rank += ranks_ahead(sc[b], b, key, c);
+        const int64_t rank = count_ahead(sc, (int)nb, key, (int)c);
         level[r * nb + c] = (uint8_t)((!isnan(key) && rank < k) ? kappa : glass);
     }
 }
@@ -169,8 +184,7 @@ __global__ void __launch_bounds__(kLayerThreads) layer_group_kernel(LayerGroupAr
     __syncthreads();
     for (int64_t c = threadIdx.x; c < nb; c += kLayerThreads) {
         const double key = sc[c];
-        int64_t rank = 0;
-        for (int64_t b = 0; b < nb; ++b) rank += ranks_ahead(sc[b], b, key, c);
+        const int64_t rank = count_ahead(sc, (int)nb, key, (int)c);
         it.level[r * nb + c] = (uint8_t)((!isnan(key) && rank < it.k) ? g.kappa : g.glass);
     }
 }
