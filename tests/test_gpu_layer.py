@@ -65,7 +65,7 @@ def test_scores_and_threshold_levels_bit_exact(qam, B, N, K):
     assert len(np.unique(O.layer_levels_threshold(want_s, 5, 1, 1.0, med / 16))) >= min(3, want_s.size)
 
 
-@pytest.mark.parametrize("B,nb", [(1, 1), (4, 77), (32, 300), (1, 512), (2, 513), (2, 2374), (3, 1000)])
+@pytest.mark.parametrize("B,nb", [(1, 1), (4, 77), (32, 300), (1, 512), (2, 513), (2, 2374), (3, 1000), (1, 16384)])
 def test_share_levels_bit_exact_with_ties_and_nan(qam, B, nb):
     N, K = 64 * nb, 128
     _, sc, pm = packed(qam, nb, N, K)
@@ -220,3 +220,41 @@ def test_group_call_bit_exact(qam, B):
             else:
                 want = O.layer_levels_threshold(want_s, 5, rule.glass, 1.0, kw["lam"])
             assert np.array_equal(lv.cpu().numpy(), want), (kw, pm.n_blocks)
+
+
+def test_group_step_graph_replays_match_eager(qam):
+    """The grouped layer step captured in a HIP graph: every replay, with
+    eager work and synchronisations between them, leaves the same outputs
+    and maps as the eager step."""
+    B = 4
+    items = []
+    for i, (N, K) in enumerate([(64 * 40, 512), (64 * 224, 256)]):
+        _, _, pm = packed(qam, 700 + i, N, K)
+        x = dev(WL.activations(WL.stream(700 + i, TAG, 3), B, K))
+        items.append((pm, x, torch.empty((B, N), dtype=torch.float32, device="cuda")))
+    grp = qam.LayerDecidesGroup(items, qam.LayerRule(share=1.0 / 3.0, glass=1))
+    grp.run()
+    torch.cuda.synchronize()
+    want_y = [it[2].cpu().numpy().copy() for it in items]
+    want_lv = [lv.cpu().numpy().copy() for lv in grp.levels]
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        grp.run()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        grp.run()
+    for rep in range(3):
+        for it in items:
+            it[2].fill_(float("nan"))
+        for lv in grp.levels:
+            lv.fill_(0xEE)
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, it in enumerate(items):
+            assert np.array_equal(it[2].cpu().numpy(), want_y[i]), (rep, i)
+            assert np.array_equal(grp.levels[i].cpu().numpy(), want_lv[i]), (rep, i)
+        grp.second.run()                       # eager work between replays
+        torch.cuda.synchronize()
