@@ -382,7 +382,7 @@ def run_layer(args, torch, Q, WL):
 
     step_ms = wall(step)
     lv = [l.cpu().numpy() for l in grp.levels]
-    fixed_ms = wall(fixed)
+    grp.base.run()            # the base outputs again (the refinement adds into them)
     ev = []
     for _ in range(args.steps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -393,14 +393,16 @@ def run_layer(args, torch, Q, WL):
     torch.cuda.synchronize()
     levels_ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
     assert all(np.array_equal(a.cpu().numpy(), l) for a, l in zip(grp.levels, lv)), "maps changed"
+    fixed_ms = wall(fixed)
     bits = np.array(Q.LADDER_BITS)
     base_bytes = sum(m.N * m.K * 2 // 8 for m in fld.matrices)
     union = sum(int(np.sum(64 * m.K * bits[l.max(axis=0)]) // 8) for m, l in zip(fld.matrices, lv))
+    above = sum(int(np.sum(64 * m.K * (bits[l.max(axis=0)] - bits[1])) // 8) for m, l in zip(fld.matrices, lv))
     w = fld.block_weights()
     allv = np.concatenate(lv, axis=1)
     mean_req = float(np.mean([np.sum(w * bits[allv[r]]) / np.sum(w) for r in range(B)]))
     return dict(step_ms=step_ms, fixed_ms=fixed_ms, levels_ms=levels_ms, base_bytes=base_bytes,
-                union_bytes=union, mean_bits_per_request=mean_req,
+                union_bytes=above if grp.refine else union, fixed_bytes=union, refine=grp.refine, mean_bits_per_request=mean_req,
                 mean_bits_union=float(np.sum(w * bits[allv.max(axis=0)]) / np.sum(w)))
 
 
@@ -705,7 +707,7 @@ def main():
         return
     if args.workload == "layer_decides":
         res = run_layer(args, torch, Q, WL)
-        step_bytes = res["base_bytes"] + res["union_bytes"]
+        step_bytes = res["base_bytes"] + res["union_bytes"]   # the second read: slices above the glass if refined
         gbs = step_bytes / (res["step_ms"] * 1e-3) / 1e9
         out = {
             "metric": "achieved HBM GB/s (% of peak) and decode tokens/s at mean bits/weight",
@@ -724,7 +726,10 @@ def main():
                 "mean_bits_per_request": round(res["mean_bits_per_request"], 6),
                 "mean_bits_union": round(res["mean_bits_union"], 6),
                 "weight_bytes_base_pass": int(res["base_bytes"]),
+                "second_pass": "lifted blocks' slices above the glass, added to the base outputs"
+                               if res["refine"] else "full product at the per-request maps",
                 "weight_bytes_second_pass_union": int(res["union_bytes"]),
+                "weight_bytes_fixed_map_products": int(res["fixed_bytes"]),
                 "step_ms": round(res["step_ms"], 5),
                 "fixed_map_products_ms": round(res["fixed_ms"], 5),
                 "layer_decides_over_fixed": round(res["step_ms"] / res["fixed_ms"], 4),

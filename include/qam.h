@@ -487,6 +487,24 @@ int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dty
 int qam_qmatvec_group(const qam_group* group, hipStream_t s);
 
 /*
+ * qam_qmatvec_group_refine -- the group's product from slice first_slice
+ *   on, added to y: for every request and block whose depth d (in slices)
+ *   exceeds first_slice, y += scale * (code at d - code at first_slice) . x,
+ *   reading only slices first_slice .. d - 1; other blocks leave y as it is.
+ *   With y holding the product at a uniform depth first_slice, y becomes the
+ *   product at the group's maps ([FoQLens] "FoQZones, the mechanism": the
+ *   layer read once, its lifted blocks read deeper after it decides).  The
+ *   sum is formed in fp64 from the fp32 y and rounded once.
+ *   group        initialised by qam_group_init on the pre-pass route (B >= 2,
+ *                the route qam_group_init takes from 3 requests by default)
+ *                and not in the per-slice form.
+ *   first_slice  1 .. 3.
+ *   Errors: QAM_ERR_NULL (uninitialised group), QAM_ERR_ARG (another route,
+ *   the per-slice form, first_slice out of range).  Asynchronous on `s`.
+ */
+int qam_qmatvec_group_refine(const qam_group* group, int first_slice, hipStream_t s);
+
+/*
  * qam_qmatvec_group_lens -- qam_qmatvec_group with the level maps built in
  *   the same launch: every item's map is computed from the lens rules of
  *   qam_build_level_map ([Lens] "The mechanism" rules 1-6, the same readings

@@ -123,6 +123,7 @@ SIGNATURES = [
                                     _I, _P]),
     ("qam_layer_levels", _I, [_P, _I64, C.POINTER(QamPacked), C.POINTER(QamLayerRule), _I, _I, _P, _P, _P]),
     ("qam_layer_levels_group", _I, [C.POINTER(QamLayerItem), _I, _I64, C.POINTER(QamLayerRule), _I, _I, _P]),
+    ("qam_qmatvec_group_refine", _I, [_P, _I, _P]),
     ("qam_fit_focus_area", _I, [_P, _I64, _P, C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I, _I, _I64,
                                 _I, _P, _P, _SZ, C.POINTER(C.c_double), C.POINTER(C.c_int64), _P]),
     ("qam_decoder_decode_gated", _I, [_P, _P, _I64, _I, _I, C.c_double, C.c_double, _P, _SZ, _P, _P, _P, _P]),

@@ -461,16 +461,24 @@ class LayerDecidesGroup:
     shared at B = 1).  ``items`` are (PackedMatrix, x [B, K], y [B, N])
     tuples, bound once like GroupedQmatvec's; ``run()`` recomputes every y,
     ``levels[i]`` holds matrix i's maps [B, n_blocks] afterwards.  Up to 16
-    matrices of at most 512 blocks each share one level launch."""
+    matrices of at most 512 blocks each share one level launch.  With
+    ``refine`` (taken where the second product runs on the pre-pass route,
+    from 3 requests, and the glass is D2-D6), the base product is written
+    into y and the second product only adds the lifted blocks' slices above
+    the glass (``qam_qmatvec_group_refine``): every block is read once to
+    the glass and the lifted ones on from there; ``self.refine`` says which
+    form runs."""
 
-    def __init__(self, items, rule: LayerRule, device="cuda"):
+    def __init__(self, items, rule: LayerRule, device="cuda", refine: bool = True):
         self.rule = rule
+        B0 = items[0][1].shape[0] if items[0][1].dim() == 2 else 1
+        refine = bool(refine) and B0 >= 3 and 1 <= rule.glass <= 3 and rule.n_rungs == len(LADDER_BITS)
         base_items, second_items, self.parts = [], [], []
         for pm, x, y in items:
             B = x.shape[0] if x.dim() == 2 else 1
             nb = pm.n_blocks
             base_map = torch.full((nb,), rule.glass, dtype=torch.uint8, device=device)
-            y_base = torch.empty((B, pm.N), dtype=torch.float32, device=device)
+            y_base = y if refine else torch.empty((B, pm.N), dtype=torch.float32, device=device)
             shat = torch.empty((B, nb), dtype=torch.float64, device=device)
             lv = torch.empty((B, nb), dtype=torch.uint8, device=device)
             base_items.append((pm, x, y_base, base_map))
@@ -478,6 +486,10 @@ class LayerDecidesGroup:
             self.parts.append((pm, y_base, shat, lv))
         self.base = GroupedQmatvec(base_items, device=device)
         self.second = GroupedQmatvec(second_items, device=device)
+        self.refine = refine and self.second.route == "prepass"
+        if refine and not self.refine:
+            # the second product runs on the staged route: a full product at the maps, into y
+            raise ValueError("refinement needs the pre-pass route for the second product")
         self.levels = [p[3] for p in self.parts]
         # one launch for every matrix when each has at most 512 blocks
         self._table = None
@@ -498,10 +510,17 @@ class LayerDecidesGroup:
         for pm, y_base, shat, lv in self.parts:
             layer_levels(y_base, pm, self.rule, shat=shat, out=lv)
 
+    def refine_run(self) -> None:
+        """The lifted blocks' slices above the glass, added to y."""
+        L.check(L.lib().qam_qmatvec_group_refine(C.byref(self.second.desc), self.rule.glass, _stream_handle()))
+
     def run(self) -> None:
         self.base.run()
         self.decide()
-        self.second.run()
+        if self.refine:
+            self.refine_run()
+        else:
+            self.second.run()
 
 
 class Gate:

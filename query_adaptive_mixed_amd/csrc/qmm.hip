@@ -67,6 +67,7 @@ struct MCommon {
     int SS;                    // requests per set (<= 16; 3 SS limb columns in NCG groups of 16)
     int KS;                    // waves per request set splitting a chunk's tiles
     int NCG;                   // 16-column groups per request set
+    int first;                 // refinement launches: slices below this are not read, and y is added to
 };
 
 // Depth (slices read, 0..4) of request r in block b.
@@ -180,12 +181,14 @@ struct MRing {
 
 template <int NS, int NCG, int H>
 __device__ __forceinline__ void mload(u32x4 (&w)[H][NS], v4i (&x)[H][NCG], const uint8_t* wbase, int64_t pb,
-                                      int64_t wstride, const v4i* xbase, int64_t xstride, int tile, int last) {
+                                      int64_t wstride, const v4i* xbase, int64_t xstride, int tile, int last,
+                                      int first) {
 #pragma unroll
     for (int u = 0; u < H; ++u) {
         const int t = min(tile + u, last);
 #pragma unroll
-        for (int p = 0; p < NS; ++p) w[u][p] = load_plane(wbase + p * pb + (int64_t)t * wstride);
+        for (int p = 0; p < NS; ++p)
+            w[u][p] = p < first ? u32x4{0u, 0u, 0u, 0u} : load_plane(wbase + p * pb + (int64_t)t * wstride);
 #pragma unroll
         for (int g = 0; g < NCG; ++g) x[u][g] = *(global_v4i*)(xbase + t * xstride + g * 64);
     }
@@ -242,7 +245,7 @@ __device__ __forceinline__ void mtile(const u32x4 (&w)[NS], const v4i (&xl)[NCG]
 // The product over this wave's tiles of the chunk: tiles ks, ks + KS, ...
 template <int NS, int NCG, bool PER_REQ>
 __device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, int chunk, int h, int ks, int L,
-                                         const int (&mcol)[NCG], uint32_t dmask, v4i (&acc)[4][NCG]) {
+                                         const int (&mcol)[NCG], uint32_t dmask, int first, v4i (&acc)[4][NCG]) {
 
     constexpr int H = MRing<NS, NCG>::H;
     constexpr int PF = MRing<NS, NCG>::PF;
@@ -261,21 +264,21 @@ __device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, 
     __builtin_amdgcn_s_waitcnt(0);
     u32x4 wa[H][NS], wb[H][NS];
     v4i xa[H][NCG], xb[H][NCG];
-    mload<NS, NCG, H>(wa, xa, wbase, pb, wstride, xbase, xstride, 0, last);
+    mload<NS, NCG, H>(wa, xa, wbase, pb, wstride, xbase, xstride, 0, last, first);
     __builtin_amdgcn_sched_barrier(0);
-    mload<NS, NCG, H>(wb, xb, wbase, pb, wstride, xbase, xstride, H, last);
+    mload<NS, NCG, H>(wb, xb, wbase, pb, wstride, xbase, xstride, H, last, first);
     __builtin_amdgcn_sched_barrier(0);
     int t = 0;
     for (; t + PF < nt; t += PF) {
 #pragma unroll
         for (int u = 0; u < H; ++u) mtile<NS, NCG, PER_REQ>(wa[u], xa[u], mcol, dmask, acc);
         __builtin_amdgcn_sched_barrier(0);
-        mload<NS, NCG, H>(wa, xa, wbase, pb, wstride, xbase, xstride, t + PF, last);
+        mload<NS, NCG, H>(wa, xa, wbase, pb, wstride, xbase, xstride, t + PF, last, first);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < H; ++u) mtile<NS, NCG, PER_REQ>(wb[u], xb[u], mcol, dmask, acc);
         __builtin_amdgcn_sched_barrier(0);
-        mload<NS, NCG, H>(wb, xb, wbase, pb, wstride, xbase, xstride, t + PF + H, last);
+        mload<NS, NCG, H>(wb, xb, wbase, pb, wstride, xbase, xstride, t + PF + H, last, first);
         __builtin_amdgcn_sched_barrier(0);
     }
     // Drain: the last ring, whose tail may run past the wave's tiles.  Tiles
@@ -301,7 +304,9 @@ __device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, 
 }
 
 // One workgroup = KS x NH wavefronts = one (block, column chunk).
-template <int NCG, bool PER_REQ, bool GROUPED>
+// REFINE: a refinement launch (c.first > 0); without it `first` is the
+// constant 0 and the code is that of the plain product.
+template <int NCG, bool PER_REQ, bool GROUPED, bool REFINE>
 __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
     extern __shared__ int tab[];   // [KS NH][64 rows][16 NCG + 1] integer sums, then one flag
     constexpr int TW = 16 * NCG + 1;
@@ -315,6 +320,7 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
         local = (int)blockIdx.x;
     }
     const int B = c.B, NH = c.NH, KS = c.KS, SS = c.SS;
+    const int first = REFINE ? c.first : 0;
     const int chunk = local % a.n_chunks;
     const int b = local / a.n_chunks;
     const int wave = (int)threadIdx.x >> 6;
@@ -322,14 +328,16 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
     const int ks = wave / NH;
     const int L = (int)threadIdx.x & 63;
 
-    // depth of request L (lanes < B), then of the set's requests and columns
-    const int m_all = L < B ? depth_of<PER_REQ>(a, L, b) : 0;
+    // depth of request L (lanes < B), then of the set's requests and columns;
+    // a refinement launch reads nothing for a request at or below its first slice
+    const int m_req = L < B ? depth_of<PER_REQ>(a, L, b) : 0;
+    const int m_all = m_req > first ? m_req : 0;
     uint32_t dm_all = 1u << m_all;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) dm_all |= __shfl_xor(dm_all, o);
     dm_all = __builtin_amdgcn_readfirstlane(dm_all);
-    if (dm_all == 1u) {   // no request reads any of the block: y = 0, written once, by the first chunk
-        if (chunk == 0)
+    if (dm_all == 1u) {   // no request reads any of the block: y = 0 (unchanged when refining), by the first chunk
+        if (chunk == 0 && !REFINE)
             for (int r = wave; r < B; r += NH * KS) a.y[(int64_t)r * a.N + (int64_t)b * kRows + L] = 0.0f;
         return;
     }
@@ -353,10 +361,10 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
         for (int g = 0; g < NCG; ++g) acc[j][g] = v4i{0, 0, 0, 0};
     switch (ns) {
         case 0: break;   // no request of this set reads the block
-        case 1: mproduct<1, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, dm, acc); break;
-        case 2: mproduct<2, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, dm, acc); break;
-        case 3: mproduct<3, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, dm, acc); break;
-        default: mproduct<4, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, dm, acc); break;
+        case 1: mproduct<1, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, dm, first, acc); break;
+        case 2: mproduct<2, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, dm, first, acc); break;
+        case 3: mproduct<3, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, dm, first, acc); break;
+        default: mproduct<4, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, dm, first, acc); break;
     }
     // the wave's 64 x 16 NCG integer sums into its table
     int* mine = tab + (ks * NH + h) * 64 * TW;
@@ -388,9 +396,11 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
         const int e = a.exps[chunk * slots + r];
         const int mr = __shfl(m_all, r & 63);
         const double v = mr == 0 ? 0.0 : (e == kBadExp ? __builtin_nan("") : ldexp(d, e - kFrac));
-        if (!split)
-            a.y[(int64_t)r * a.N + (int64_t)b * kRows + row] = (float)(sc * v);
-        else   // split K: publish the partial with a device-scope write-through store
+        if (!split) {
+            float* yo = &a.y[(int64_t)r * a.N + (int64_t)b * kRows + row];
+            if constexpr (!REFINE) *yo = (float)(sc * v);
+            else if (mr != 0) *yo = (float)((double)*yo + sc * v);
+        } else   // split K: publish the partial with a device-scope write-through store
             __hip_atomic_store(&a.partials[((int64_t)chunk * B + r) * a.N + (int64_t)b * kRows + row], v,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -410,7 +420,9 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
         for (int cc = 0; cc < a.n_chunks; ++cc)
             sum += __hip_atomic_load(&a.partials[((int64_t)cc * B + r) * a.N + (int64_t)b * kRows + row],
                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        a.y[(int64_t)r * a.N + (int64_t)b * kRows + row] = (float)(sc * sum);
+        float* yo = &a.y[(int64_t)r * a.N + (int64_t)b * kRows + row];
+        if constexpr (!REFINE) *yo = (float)(sc * sum);
+        else if (__shfl(m_all, r & 63) != 0) *yo = (float)((double)*yo + sc * sum);
     }
     if (threadIdx.x == 0) __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -638,10 +650,16 @@ static void launch_product(const MItem& it, const MCommon& c, bool per_req, int6
     }
     const dim3 blk(64 * c.NH * c.KS);
     const size_t lds = ((size_t)c.KS * c.NH * 64 * (16 * NCG + 1) + 4) * sizeof(int);
-    if (per_req)
-        hipLaunchKernelGGL((qmm_kernel<NCG, true, GROUPED>), dim3((unsigned)grid), blk, lds, s, it, c);
-    else
-        hipLaunchKernelGGL((qmm_kernel<NCG, false, GROUPED>), dim3((unsigned)grid), blk, lds, s, it, c);
+    if (c.first > 0) {
+        if (per_req)
+            hipLaunchKernelGGL((qmm_kernel<NCG, true, GROUPED, true>), dim3((unsigned)grid), blk, lds, s, it, c);
+        else
+            hipLaunchKernelGGL((qmm_kernel<NCG, false, GROUPED, true>), dim3((unsigned)grid), blk, lds, s, it, c);
+    } else if (per_req) {
+        hipLaunchKernelGGL((qmm_kernel<NCG, true, GROUPED, false>), dim3((unsigned)grid), blk, lds, s, it, c);
+    } else {
+        hipLaunchKernelGGL((qmm_kernel<NCG, false, GROUPED, false>), dim3((unsigned)grid), blk, lds, s, it, c);
+    }
 }
 
 template <bool GROUPED>
@@ -904,7 +922,8 @@ int mfma_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dt
     return QAM_OK;
 }
 
-int mfma_group_run(const qam_group* g, hipStream_t s) {
+// first > 0: a refinement launch (slices first.. of each request's depth added to y).
+static int mfma_group_run_from(const qam_group* g, int first, hipStream_t s) {
     if (g->sets < 1 || g->sets > 4 || g->set_size < 1 || g->set_size > 16 || (int64_t)g->sets * g->set_size < g->B ||
         g->col_groups < 1 || g->col_groups > 3 || 3 * g->set_size > 16 * g->col_groups)
         QAM_FAIL(QAM_ERR_ARG, "qmatvec_group: corrupt group descriptor");
@@ -917,19 +936,35 @@ int mfma_group_run(const qam_group* g, hipStream_t s) {
     c.SS = g->set_size;
     c.NCG = g->col_groups;
     c.KS = std::max(1, std::min(g_mfma_ksplit, 4 / c.NH));
+    c.first = first;
     MItem dummy{};
     launch_mfma<true>(dummy, c, g->x_dtype == QAM_X_BF16, g->per_request_maps != 0, g->n_pre_workgroups,
                       g->n_workgroups, s);
     QAM_HIP_CHECK(hipGetLastError());
     char v[128];
-    snprintf(v, sizeof(v), "qmatvec_mfma_group items=%d B=%lld maps=%s form=%s wg=%lld", g->n_items, (long long)g->B,
+    snprintf(v, sizeof(v), "qmatvec_mfma_group%s items=%d B=%lld maps=%s form=%s wg=%lld", first ? "_refine" : "",
+             g->n_items, (long long)g->B,
              g->per_request_maps ? "per-request" : "shared",
              per_slice_form(g->B, g->per_request_maps != 0, g->sets) ? "slice" : "depth", (long long)g->n_workgroups);
     set_variant(v);
     return QAM_OK;
 }
 
+int mfma_group_run(const qam_group* g, hipStream_t s) { return mfma_group_run_from(g, 0, s); }
+
 }  // namespace qam
+
+extern "C" int qam_qmatvec_group_refine(const qam_group* group, int first_slice, hipStream_t s) {
+    qam::clear_error();
+    if (!group || !group->table || !group->wg_map || !group->pre_map)
+        QAM_FAIL(QAM_ERR_NULL, "qmatvec_group_refine: uninitialised group");
+    if (group->route != 1 || group->B < 2 || group->B > QAM_MAX_BATCH_MFMA || group->n_workgroups < 1)
+        QAM_FAIL(QAM_ERR_ARG, "qmatvec_group_refine: the group must take the pre-pass route");
+    if (first_slice < 1 || first_slice > 3) QAM_FAIL(QAM_ERR_ARG, "qmatvec_group_refine: first_slice %d outside [1, 3]", first_slice);
+    if (qam::per_slice_form(group->B, group->per_request_maps != 0, group->sets))
+        QAM_FAIL(QAM_ERR_ARG, "qmatvec_group_refine: not available in the per-slice form");
+    return qam::mfma_group_run_from(group, first_slice, s);
+}
 
 extern "C" int qam_set_mfma_per_slice_max(int b) {
     qam::clear_error();

@@ -143,12 +143,14 @@ def test_layer_decides_end_to_end(qam, B):
         assert np.all(err <= O.qmatvec_tolerance(W, sc, x, lv, per_request=True)), rule_kw
 
 
-@pytest.mark.parametrize("B", [1, 8])
-def test_layer_decides_group(qam, B):
+@pytest.mark.parametrize("B,refine", [(1, False), (8, False), (8, True), (3, True), (32, True)])
+def test_layer_decides_group(qam, B, refine):
     """The grouped form over three matrices of different shapes: every map
     between the oracle's maps at the score bounds, every output within the
-    tolerance of the oracle's product at that map; a second run repeats the
-    first bit for bit."""
+    tolerance of the oracle's product at that map (with the refinement, the
+    tolerance of the base read plus that of the product at the map: y is the
+    base product plus the lifted blocks' slices above the glass); a second
+    run repeats the first bit for bit."""
     shapes = [(64 * 40, 512), (64 * 17, 1024), (64 * 64, 256)]
     mats, items, xs = [], [], []
     for i, (N, K) in enumerate(shapes):
@@ -163,7 +165,8 @@ def test_layer_decides_group(qam, B):
             W, sc = mats[0]
             y_ref = O.qmatvec_ref(W, sc, xs[0], np.full(W.shape[0] // 64, glass, np.uint8))
             rule_kw = dict(lam=float(np.median(O.layer_scores(y_ref, sc, W.shape[1]))) / 16)
-        grp = qam.LayerDecidesGroup(items, qam.LayerRule(glass=glass, **rule_kw))
+        grp = qam.LayerDecidesGroup(items, qam.LayerRule(glass=glass, **rule_kw), refine=refine)
+        assert grp.refine == refine
         grp.run()
         first = [it[2].cpu().numpy().copy() for it in items]
         for i, ((W, sc), x) in enumerate(zip(mats, xs)):
@@ -182,8 +185,10 @@ def test_layer_decides_group(qam, B):
                     assert risen.sum() == k and (risen | stay).all()
                     assert s_hi[r][risen].min() >= s_lo[r][stay].max()
             ref = O.qmatvec_ref(W, sc, x, lv, per_request=True)
-            assert np.all(np.abs(first[i].astype(np.float64) - ref)
-                          <= O.qmatvec_tolerance(W, sc, x, lv, per_request=True)), (i, rule_kw)
+            tol = O.qmatvec_tolerance(W, sc, x, lv, per_request=True)
+            if refine:
+                tol = tol + O.qmatvec_tolerance(W, sc, x, uni)
+            assert np.all(np.abs(first[i].astype(np.float64) - ref) <= tol), (i, rule_kw)
         grp.run()
         for i, it in enumerate(items):
             assert np.array_equal(it[2].cpu().numpy(), first[i]), i
@@ -258,3 +263,34 @@ def test_group_step_graph_replays_match_eager(qam):
             assert np.array_equal(grp.levels[i].cpu().numpy(), want_lv[i]), (rep, i)
         grp.second.run()                       # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_refinement_and_full_second_product_agree_on_the_maps(qam):
+    """Both forms of the grouped step take their maps from the same base
+    product, so the maps are the same bits; a block no request lifts keeps
+    its base outputs exactly under the refinement."""
+    B = 6
+    items_r, items_f, mats = [], [], []
+    for i, (N, K) in enumerate([(64 * 50, 256), (64 * 30, 512)]):
+        W, sc, pm = packed(qam, 900 + i, N, K)
+        x = dev(WL.activations(WL.stream(900 + i, TAG, 3), B, K))
+        items_r.append((pm, x, torch.empty((B, N), dtype=torch.float32, device="cuda")))
+        items_f.append((pm, x, torch.empty((B, N), dtype=torch.float32, device="cuda")))
+        mats.append((W, sc))
+    rule = qam.LayerRule(share=0.2, glass=1)
+    gr = qam.LayerDecidesGroup(items_r, rule, refine=True)
+    gf = qam.LayerDecidesGroup(items_f, rule, refine=False)
+    gr.base.run()
+    torch.cuda.synchronize()
+    base = [it[2].cpu().numpy().copy() for it in items_r]
+    gr.decide()
+    gr.refine_run()
+    gf.run()
+    torch.cuda.synchronize()
+    for i, ((W, sc), it) in enumerate(zip(mats, items_r)):
+        lv = gr.levels[i].cpu().numpy()
+        assert np.array_equal(lv, gf.levels[i].cpu().numpy()), i
+        y = it[2].cpu().numpy()
+        kept = np.repeat(lv == 1, 64, axis=1)           # blocks left at the glass
+        assert np.array_equal(y[kept], base[i][kept]), i
+        assert not np.array_equal(y[~kept], base[i][~kept]), i
