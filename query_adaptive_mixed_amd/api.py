@@ -486,10 +486,9 @@ class LayerDecidesGroup:
             self.parts.append((pm, y_base, shat, lv))
         self.base = GroupedQmatvec(base_items, device=device)
         self.second = GroupedQmatvec(second_items, device=device)
+        # on the staged route (a tuning hook can send 3+ requests there) the
+        # second product is a full one at the maps, which overwrites y
         self.refine = refine and self.second.route == "prepass"
-        if refine and not self.refine:
-            # the second product runs on the staged route: a full product at the maps, into y
-            raise ValueError("refinement needs the pre-pass route for the second product")
         self.levels = [p[3] for p in self.parts]
         # one launch for every matrix when each has at most 512 blocks
         self._table = None

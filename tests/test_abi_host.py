@@ -449,3 +449,16 @@ def test_layer_levels_group_rejects_before_any_launch(lib):
     assert call([item()], glass=5) == -4
     assert call([item()], r=L.QamLayerRule(mode=L.QAM_LAYER_SHARE, reserved=0, lam=1.0, share=2.0, g=1.0)) == -3
     assert call([item(y=None, shat=None, out=None)], B=0) == 0      # nothing to do, nothing launched
+
+
+def test_group_refine_rejects_before_any_launch(lib):
+    FAKEW = 0x20000000
+    assert lib.qam_qmatvec_group_refine(None, 1, None) == -1
+    g = L.QamGroup()
+    assert lib.qam_qmatvec_group_refine(C.byref(g), 1, None) == -1          # uninitialised
+    g.table, g.wg_map, g.pre_map = FAKEW, FAKEW, FAKEW
+    g.route, g.B, g.n_workgroups = 0, 4, 10
+    assert lib.qam_qmatvec_group_refine(C.byref(g), 1, None) == -3          # staged route
+    g.route = 1
+    assert lib.qam_qmatvec_group_refine(C.byref(g), 0, None) == -3
+    assert lib.qam_qmatvec_group_refine(C.byref(g), 4, None) == -3
