@@ -71,20 +71,24 @@ __device__ __forceinline__ bool ranks_ahead(double v, int64_t b, double key, int
     return v > key || (v == key && b < c);
 }
 
-// Blocks of sc[0, nb) ahead of (key, c), nb <= kLayerFusedMax: four
+// Blocks of sc[lo, hi) ahead of (key, c), hi <= kLayerFusedMax: four
 // independent counts (integer, so their order does not matter), so that
 // several LDS reads are in flight at once.
-__device__ __forceinline__ int64_t count_ahead(const double* sc, int nb, double key, int c) {
+__device__ __forceinline__ int count_ahead_range(const double* sc, int lo, int hi, double key, int c) {
     int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
-    int b = 0;
-    for (; b + 4 <= nb; b += 4) {
+    int b = lo;
+    for (; b + 4 <= hi; b += 4) {
         r0 += ranks_ahead(sc[b], b, key, c);
         r1 += ranks_ahead(sc[b + 1], b + 1, key, c);
         r2 += ranks_ahead(sc[b + 2], b + 2, key, c);
         r3 += ranks_ahead(sc[b + 3], b + 3, key, c);
     }
-    for (; b < nb; ++b) r0 += ranks_ahead(sc[b], b, key, c);
-    return (int64_t)r0 + r1 + r2 + r3;
+    for (; b < hi; ++b) r0 += ranks_ahead(sc[b], b, key, c);
+    return r0 + r1 + r2 + r3;
+}
+
+__device__ __forceinline__ int64_t count_ahead(const double* sc, int nb, double key, int c) {
+    return count_ahead_range(sc, 0, nb, key, c);
 }
 
 // One thread per (request, block): the score and, in threshold mode, the rung.
@@ -166,15 +170,19 @@ struct LayerGroupArgs {
     double lambda;
 };
 
+constexpr int kLayerGroupThreads = 1024;
+
 // Every matrix of a group in one launch: a workgroup per (item, request),
 // each scoring that request's blocks (at most kLayerFusedMax) and, in share
-// mode, ranking them in LDS; the same arithmetic as the single-matrix kernels.
-__global__ void __launch_bounds__(kLayerThreads) layer_group_kernel(LayerGroupArgs g) {
+// mode, ranking them in LDS, four adjacent lanes per block each counting a
+// quarter of the blocks (integer counts, summed by two lane shuffles); the
+// same arithmetic as the single-matrix kernels.
+__global__ void __launch_bounds__(kLayerGroupThreads) layer_group_kernel(LayerGroupArgs g) {
     __shared__ double sc[kLayerFusedMax];
     const int64_t item = blockIdx.x / g.B, r = blockIdx.x - item * g.B;
     const LayerItem& it = g.items[item];
     const int64_t nb = it.nb;
-    for (int64_t c = threadIdx.x; c < nb; c += kLayerThreads) {
+    for (int64_t c = threadIdx.x; c < nb; c += kLayerGroupThreads) {
         const double score = block_score(it.y, it.scales, r, c, it.N, it.w);
         it.shat[r * nb + c] = score;
         if (g.mode == QAM_LAYER_THRESHOLD) it.level[r * nb + c] = (uint8_t)threshold_rung(score, g.lambda, g.glass, g.lifts);
@@ -182,10 +190,17 @@ __global__ void __launch_bounds__(kLayerThreads) layer_group_kernel(LayerGroupAr
     }
     if (g.mode == QAM_LAYER_THRESHOLD) return;
     __syncthreads();
-    for (int64_t c = threadIdx.x; c < nb; c += kLayerThreads) {
-        const double key = sc[c];
-        const int64_t rank = count_ahead(sc, (int)nb, key, (int)c);
-        it.level[r * nb + c] = (uint8_t)((!isnan(key) && rank < it.k) ? g.kappa : g.glass);
+    const int n = (int)nb;
+    // 4 n (block, quarter) pairs; the trip count is the same for every lane
+    for (int base = 0; base < 4 * n; base += kLayerGroupThreads) {
+        const int idx = base + (int)threadIdx.x;
+        const bool on = idx < 4 * n;
+        const int c = idx >> 2, q = idx & 3;
+        const double key = on ? sc[c] : 0.0;
+        int part = on ? count_ahead_range(sc, (q * n) >> 2, ((q + 1) * n) >> 2, key, c) : 0;
+        part += __shfl_xor(part, 1);
+        part += __shfl_xor(part, 2);
+        if (on && q == 0) it.level[r * nb + c] = (uint8_t)((!isnan(key) && part < it.k) ? g.kappa : g.glass);
     }
 }
 
@@ -288,7 +303,7 @@ extern "C" int qam_layer_levels_group(const qam_layer_item* items, int n_items, 
     g.kappa = kappa;
     g.lambda = rule->lambda;
     if (B > 0) {
-        hipLaunchKernelGGL(layer_group_kernel, dim3((unsigned)(n_items * B)), dim3(kLayerThreads), 0, s, g);
+        hipLaunchKernelGGL(layer_group_kernel, dim3((unsigned)(n_items * B)), dim3(kLayerGroupThreads), 0, s, g);
         QAM_HIP_CHECK(hipGetLastError());
     }
     set_variant("layer_levels_group");
