@@ -294,3 +294,44 @@ def test_refinement_and_full_second_product_agree_on_the_maps(qam):
         kept = np.repeat(lv == 1, 64, axis=1)           # blocks left at the glass
         assert np.array_equal(y[kept], base[i][kept]), i
         assert not np.array_equal(y[~kept], base[i][~kept]), i
+
+
+def test_layer_decides_batched_layer_full_size(qam):
+    """The benchmark's configuration: the batched layer's three matrices
+    (4096x4096, 14336x4096, 4096x14336), 32 requests, the top third of each
+    request's blocks to D8 over a D2 glass, refinement above the glass.
+    Every block's map is checked against the oracle's score bounds; outputs
+    on sampled blocks against the oracle's product at the map."""
+    fld = WL.batched_layer(0)
+    B, glass = 32, 1
+    items, mats = [], []
+    for i, m in enumerate(fld.matrices):
+        W, sc = fld.codes(i), fld.scales(i)
+        pm = qam.pack_slices(dev(W), dev(sc))
+        x = fld.x(i, B)
+        items.append((pm, dev(x), torch.empty((B, m.N), dtype=torch.float32, device="cuda")))
+        mats.append((W, sc, x))
+    grp = qam.LayerDecidesGroup(items, qam.LayerRule(share=1.0 / 3.0, glass=glass))
+    assert grp.refine
+    grp.run()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    for i, ((W, sc, x), it) in enumerate(zip(mats, items)):
+        N, K = W.shape
+        nb = N // 64
+        lv = grp.levels[i].cpu().numpy()
+        uni = np.full(nb, glass, np.uint8)
+        y_ref = O.qmatvec_ref(W, sc, x, uni)
+        tol_base = O.qmatvec_tolerance(W, sc, x, uni)
+        s_lo, s_hi = score_bounds(y_ref, tol_base, sc, K)
+        k = int(np.floor(nb / 3.0))
+        for r in range(B):
+            risen, stay = lv[r] == 4, lv[r] == glass
+            assert risen.sum() == k and (risen | stay).all(), (i, r)
+            assert s_hi[r][risen].min() >= s_lo[r][stay].max(), (i, r)
+        blocks = np.sort(rng.choice(nb, 12, replace=False))
+        rows = np.concatenate([np.arange(64 * b, 64 * b + 64) for b in blocks])
+        ref = O.qmatvec_ref(W[rows], sc[rows], x, lv[:, blocks], per_request=True)
+        tol = O.qmatvec_tolerance(W[rows], sc[rows], x, lv[:, blocks], per_request=True) + tol_base[:, rows]
+        y = it[2].cpu().numpy()[:, rows].astype(np.float64)
+        assert np.all(np.abs(y - ref) <= tol), i
