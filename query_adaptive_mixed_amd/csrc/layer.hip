@@ -24,8 +24,8 @@ namespace qam {
 constexpr int kLayerThreads = 256;
 
 // Requests of at most this many blocks are scored and ranked by one workgroup
-// in one launch (nb^2 / 256 comparisons per thread); larger ones rank over
-// many workgroups after the score launch.
+// of layer_group_kernel in one launch (nb^2 / 1024 comparisons per thread);
+// larger ones rank over many workgroups after the score launch.
 constexpr int64_t kLayerFusedMax = 512;
 
 // The reduced score of block c of request r: its 64 outputs and 64 scales
@@ -87,9 +87,6 @@ __device__ __forceinline__ int count_ahead_range(const double* sc, int lo, int h
     return r0 + r1 + r2 + r3;
 }
 
-__device__ __forceinline__ int64_t count_ahead(const double* sc, int nb, double key, int c) {
-    return count_ahead_range(sc, 0, nb, key, c);
-}
 
 // One thread per (request, block): the score and, in threshold mode, the rung.
 __global__ void __launch_bounds__(kLayerThreads)
@@ -102,28 +99,6 @@ layer_score_kernel(const float* __restrict__ y, const float* __restrict__ scales
     const double score = block_score(y, scales, r, c, N, w);
     shat[idx] = score;
     if (mode == QAM_LAYER_THRESHOLD) level[idx] = (uint8_t)threshold_rung(score, lambda, glass, lifts);
-}
-
-// Share rule for a request of at most kLayerFusedMax blocks, one workgroup
-// per request: the scores go to LDS (and shat), then each block's rank is
-// counted there.
-__global__ void __launch_bounds__(kLayerThreads)
-layer_share_fused_kernel(const float* __restrict__ y, const float* __restrict__ scales, int64_t nb, int64_t N,
-                         double w, int64_t k, int glass, int kappa, double* __restrict__ shat,
-                         uint8_t* __restrict__ level) {
-    __shared__ double sc[kLayerFusedMax];
-    const int64_t r = blockIdx.x;
-    for (int64_t c = threadIdx.x; c < nb; c += kLayerThreads) {
-        const double score = block_score(y, scales, r, c, N, w);
-        shat[r * nb + c] = score;
-        sc[c] = score;
-    }
-    __syncthreads();
-    for (int64_t c = threadIdx.x; c < nb; c += kLayerThreads) {
-        const double key = sc[c];
-        const int64_t rank = count_ahead(sc, (int)nb, key, (int)c);
-        level[r * nb + c] = (uint8_t)((!isnan(key) && rank < k) ? kappa : glass);
-    }
 }
 
 // Share rule: one thread per (request, block); its rank is the number of
@@ -245,9 +220,24 @@ extern "C" int qam_layer_levels(const float* y_base, int64_t B, const qam_packed
     }
     const double wc = (double)(64 * K);
     if (rule->mode == QAM_LAYER_SHARE && nb <= kLayerFusedMax) {
-        const int64_t k = (int64_t)floor(rule->share * (double)nb);
-        hipLaunchKernelGGL(layer_share_fused_kernel, dim3((unsigned)B), dim3(kLayerThreads), 0, s, y_base,
-                           w->scales, nb, N, wc, k, glass, kappa, shat_out, level_out);
+        // one workgroup per request scores and ranks its blocks: the grouped kernel with one item
+        LayerGroupArgs g{};
+        LayerItem& it = g.items[0];
+        it.y = y_base;
+        it.scales = w->scales;
+        it.shat = shat_out;
+        it.level = level_out;
+        it.N = N;
+        it.nb = nb;
+        it.w = wc;
+        it.k = (int64_t)floor(rule->share * (double)nb);
+        g.B = B;
+        g.mode = rule->mode;
+        g.glass = glass;
+        g.lifts = kappa - glass;
+        g.kappa = kappa;
+        g.lambda = rule->lambda;
+        hipLaunchKernelGGL(layer_group_kernel, dim3((unsigned)B), dim3(kLayerGroupThreads), 0, s, g);
         QAM_HIP_CHECK(hipGetLastError());
         set_variant("layer_levels_share_fused");
         return QAM_OK;
