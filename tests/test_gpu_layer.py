@@ -335,3 +335,42 @@ def test_layer_decides_batched_layer_full_size(qam):
         tol = O.qmatvec_tolerance(W[rows], sc[rows], x, lv[:, blocks], per_request=True) + tol_base[:, rows]
         y = it[2].cpu().numpy()[:, rows].astype(np.float64)
         assert np.all(np.abs(y - ref) <= tol), i
+
+
+@pytest.mark.parametrize("per_req", [False, True])
+def test_group_refine_shared_and_per_request_maps(qam, per_req):
+    """qam_qmatvec_group_refine on a group of either map kind: y holds the
+    product at a uniform glass, the refinement takes each block to
+    max(its rung, the glass); rungs at or below the glass leave y as it is."""
+    from query_adaptive_mixed_amd import _lib as L
+    import ctypes as C
+    B, glass = 5, 2
+    rng = WL.stream(1234, TAG, 4)
+    mats, base_items, ref_items = [], [], []
+    for i, (N, K) in enumerate([(64 * 9, 320), (64 * 21, 1024)]):
+        W, sc, pm = packed(qam, 1100 + i, N, K)
+        x = WL.activations(WL.stream(1100 + i, TAG, 3), B, K)
+        nb = N // 64
+        lv = rng.integers(0, 5, (B, nb) if per_req else nb).astype(np.uint8)
+        y = torch.empty((B, N), dtype=torch.float32, device="cuda")
+        xd = dev(x)
+        base_items.append((pm, xd, y, dev(np.full(nb, glass, np.uint8))))
+        ref_items.append((pm, xd, y, dev(lv)))
+        mats.append((W, sc, x, lv))
+    gb, gr = qam.GroupedQmatvec(base_items), qam.GroupedQmatvec(ref_items)
+    assert gr.route == "prepass"
+    gb.run()
+    torch.cuda.synchronize()
+    base = [it[2].cpu().numpy().copy() for it in ref_items]
+    L.check(L.lib().qam_qmatvec_group_refine(C.byref(gr.desc), glass, None))
+    torch.cuda.synchronize()
+    for (W, sc, x, lv), it, y0 in zip(mats, ref_items, base):
+        nb = W.shape[0] // 64
+        eff = np.broadcast_to(np.maximum(lv, glass), (B, nb))
+        uni = np.full(nb, glass, np.uint8)
+        ref = O.qmatvec_ref(W, sc, x, eff, per_request=True)
+        tol = O.qmatvec_tolerance(W, sc, x, eff, per_request=True) + O.qmatvec_tolerance(W, sc, x, uni)
+        y = it[2].cpu().numpy()
+        assert np.all(np.abs(y.astype(np.float64) - ref) <= tol)
+        kept = np.repeat(np.broadcast_to(lv <= glass, (B, nb)), 64, axis=1)
+        assert np.array_equal(y[kept], y0[kept])
