@@ -606,3 +606,31 @@ def test_layer_levels_share_invariants():
                     assert s[r, a] > s[r, b] or (s[r, a] == s[r, b] and a < b)
     lv = O.layer_levels_share(s, 5, 2, 0.5, 0.3)        # kappa = 2 + floor(0.5 * 2) = 3
     assert set(np.unique(lv).tolist()) == {2, 3}
+
+
+def test_tolerance_hand_computed_read_depth():
+    """The bound's |w| is taken at the block's read depth (hand-computed
+    sums in tests/golden/tolerance_examples.json): codes 0..63 read as 0 at
+    D2, so row 1 has a zero bound there; untruncated codes at D2 would give
+    row 0 a sum of 47, not 136."""
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tolerance_examples.json")))
+    K = g["K"]
+    W = np.zeros((64, K), dtype=np.int8)
+    sc = np.ones(64)
+    for r in g["rows"]:
+        W[r["row"]] = r["codes"]
+        sc[r["row"]] = r["scale"]
+    x = np.array(g["x"])
+    listed = [r["row"] for r in g["rows"]]
+    for lev, want in g["by_level_request0"].items():
+        t = O.qmatvec_tolerance(W, sc, x[:1], np.array([int(lev)]), rel=1.0)
+        assert t.shape == (1, 64)
+        assert t[0, listed].tolist() == want, (lev, t[0, listed])
+        assert np.all(np.delete(t[0], listed) == 0.0)
+    # per-request maps: request 0 at D2, request 1 at D4
+    t = O.qmatvec_tolerance(W, sc, x, np.array([[1], [2]]), per_request=True, rel=1.0)
+    assert t[0, listed].tolist() == g["by_level_request0"]["1"]
+    assert t[1, listed].tolist() == g["by_level_request1"]["2"]
+    # the default rel is the 1e-4 of the bound
+    assert np.allclose(O.qmatvec_tolerance(W, sc, x[:1], np.array([2]))[0, listed],
+                       1e-4 * np.array(g["by_level_request0"]["2"]), rtol=1e-15, atol=0)
