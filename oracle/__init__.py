@@ -18,6 +18,8 @@ from .qam_oracle import (  # noqa: F401
     ceiling,
     profile_stops,
     lens_radius,
+    zone_radius,
+    field_width,
     level_map,
     mean_bits,
     weight_bytes,

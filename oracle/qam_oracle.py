@@ -137,8 +137,31 @@ def lens_radius(r, f: float) -> np.ndarray:
     return (r * f) / (np.float64(1.0) - f)
 
 
+def zone_radius(f: float, width: float) -> np.float64:
+    """Rule 1 of the zone form ([FoQLens] "FoQZones, the mechanism"): the
+    zone radius is R = f D, with D the width of the network; f = 0 leaves
+    only the centre, f = 1 takes the whole network.  One fp64 product, the
+    same R for every zone."""
+    return np.float64(f) * np.float64(width)
+
+
+def field_width(coords) -> np.float64:
+    """D for the zone radius: the width of the network, read as the largest
+    Euclidean distance between two blocks of the field (its diameter), so
+    that at f = 1 a zone around any block reaches every block.  The largest
+    squared distance dx*dx + dy*dy over all pairs (fp64, elementwise, no
+    fused multiply-add), then one correctly rounded square root."""
+    c = np.asarray(coords, dtype=np.float64).reshape(-1, 2)
+    best = np.float64(0.0)
+    for i in range(c.shape[0] - 1):
+        dx = c[i + 1:, 0] - c[i, 0]
+        dy = c[i + 1:, 1] - c[i, 1]
+        best = max(best, np.max(dx * dx + dy * dy))
+    return np.sqrt(best)
+
+
 def level_map(coords, centres, radii, f: float, g: float, combine: str,
-              n_rungs: int, glass: int, stops=None) -> np.ndarray:
+              n_rungs: int, glass: int, stops=None, radius: str = "lens", width=None) -> np.ndarray:
     """Per-block rung index from the lens rules (rules 1-6).
 
     [Lens] "The mechanism" and [FoQLens] "FoQZones, the mechanism":
@@ -160,6 +183,10 @@ def level_map(coords, centres, radii, f: float, g: float, combine: str,
 
     All arithmetic is fp64, elementwise, in the order written (no fused
     multiply-add); numpy's sqrt and division are correctly rounded.
+
+    With ``radius='zone'`` rule 1 is the zone form R = f D of [FoQLens]
+    "FoQZones, the mechanism" (``width`` = D, see ``field_width``) for every
+    centre, the per-lens r_i unused; rules 2-6 are the same.
 
     Parameters: ``coords`` [n_blocks, 2] fp64; ``centres`` [n_lenses, 2];
     ``radii`` [n_lenses] (the per-lens r_i); ``combine`` 'sum' or 'max';
@@ -183,7 +210,12 @@ def level_map(coords, centres, radii, f: float, g: float, combine: str,
         return np.full(nb, glass, dtype=np.uint8)
     s = profile_stops(n, stops)
     s_last = s[0]
-    R = lens_radius(radii, f)
+    if radius == "lens":
+        R = lens_radius(radii, f)
+    elif radius == "zone":
+        R = np.full(centres.shape[0], zone_radius(f, width))
+    else:
+        raise ValueError("radius must be 'lens' or 'zone'")
     acc = np.zeros(nb, dtype=np.float64)
     for i in range(centres.shape[0]):
         dx = coords[:, 0] - centres[i, 0]

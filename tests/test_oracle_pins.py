@@ -634,3 +634,68 @@ def test_tolerance_hand_computed_read_depth():
     # the default rel is the 1e-4 of the bound
     assert np.allclose(O.qmatvec_tolerance(W, sc, x[:1], np.array([2]))[0, listed],
                        1e-4 * np.array(g["by_level_request0"]["2"]), rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------------------------ zone radius
+
+def test_zone_radius_hand_examples():
+    g = json.load(open(os.path.join(GOLD, "zone_hand_examples.json")))
+    c = np.array(g["coords"])
+    assert O.field_width(c) == g["width"]
+    for f, want in g["maps"].items():
+        got = O.level_map(c, [g["centre"]], [0.123], float(f), g["g"], "sum", 5, g["glass"],
+                          radius="zone", width=g["width"])
+        assert got.tolist() == want, (f, got)
+
+
+def test_field_width_closed_forms():
+    assert O.field_width(np.array([[0.0, 0.0], [1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])) == math.sqrt(2.0)
+    assert O.field_width(np.array([[0.3, 0.7]])) == 0.0
+    xs = np.array([0.5, -1.25, 3.0, 0.0, 2.75])
+    assert O.field_width(np.stack([xs, np.full(5, 0.1)], axis=1)) == 4.25     # collinear: max - min
+    ang = np.arange(6) * (np.pi / 3)                                          # hexagon of radius 2
+    hexa = np.stack([2 * np.cos(ang), 2 * np.sin(ang)], axis=1)
+    assert abs(O.field_width(hexa) - 4.0) <= 4 * np.finfo(float).eps
+
+
+def test_field_width_is_the_largest_pairwise_distance():
+    rng = np.random.default_rng(21)
+    for n in (2, 3, 9, 40):
+        c = rng.uniform(-3, 3, size=(n, 2))
+        D = O.field_width(c)
+        pair = [math.dist(a, b) for a, b in itertools.combinations(c.tolist(), 2)]
+        assert abs(D - max(pair)) <= 2 * np.finfo(float).eps * max(pair)
+        # permutation and power-of-two translation change nothing
+        assert O.field_width(c[rng.permutation(n)]) == D
+        assert O.field_width(c + 4.0) == D or abs(O.field_width(c + 4.0) - D) <= 8 * np.finfo(float).eps * D
+
+
+def test_zone_ends_centre_only_and_whole_network():
+    """f = 0: only a block at the centre is lifted; f = 1 (R = D): a block is
+    lifted exactly when it is nearer the centre than D."""
+    rng = np.random.default_rng(22)
+    for trial in range(6):
+        c = rng.uniform(0, 1, size=(30, 2))
+        D = O.field_width(c)
+        k = int(rng.integers(0, 30))
+        for glass in (0, 1):
+            z0 = O.level_map(c, c[k:k + 1], [0.2], 0.0, 1.0, "sum", 5, glass, radius="zone", width=D)
+            assert z0[k] == 4 and np.all(np.delete(z0, k) == glass)
+            z1 = O.level_map(c, c[k:k + 1], [0.2], 1.0, 1.0, "sum", 5, glass, radius="zone", width=D)
+            d = np.sqrt(((c - c[k]) ** 2).sum(axis=1))
+            assert np.array_equal(z1 > glass, d < D)
+
+
+def test_zone_monotone_in_f_and_ignores_lens_sizes():
+    rng = np.random.default_rng(23)
+    c = rng.uniform(0, 1, size=(60, 2))
+    D = O.field_width(c)
+    cen = c[rng.choice(60, 3, replace=False)]
+    prev = None
+    for f in np.linspace(0, 1, 21):
+        a = O.level_map(c, cen, [0.05, 0.2, 0.3], f, 0.75, "sum", 5, 1, radius="zone", width=D)
+        b = O.level_map(c, cen, [9.0, 0.0, 1.0], f, 0.75, "sum", 5, 1, radius="zone", width=D)
+        assert np.array_equal(a, b)
+        if prev is not None:
+            assert np.all(a >= prev)
+        prev = a
