@@ -33,10 +33,14 @@
  *     qam_last_error() describes the problem.  Nothing aborts or throws across
  *     the ABI, and no call falls back silently to another kernel variant:
  *     qam_last_variant() names the variant the last successful call ran.
- *   - Calls are reentrant; the library's state is the thread-local error and
- *     variant strings, plus the process-wide launch parameters that the
- *     library's tuning hooks set (qam_set_*, exported for benchmarks and not
- *     declared here): a call racing with a tuning hook is undefined.
+ *   - Calls are reentrant: the library keeps no state but the thread-local
+ *     error and variant strings.  Launch plans are fixed per call (defaults)
+ *     or per group at qam_group_init_tuned, never process-wide.
+ *   - Device-side errors (a level map holding a rung that is not a depth of
+ *     the product) do not fault: the kernel raises a bit in the status word
+ *     of the call's workspace (qam_status reads and clears it) and writes NaN
+ *     for the outputs it could not compute.  Nothing is read silently at
+ *     another depth.
  */
 #ifndef QAM_H
 #define QAM_H
@@ -63,10 +67,19 @@ extern "C" {
 #define QAM_MAX_K          65536      /* keeps every exact integer sum in range */
 #define QAM_MAX_LENSES     64
 #define QAM_MAX_RUNGS      16
-#define QAM_MAX_BATCH      8          /* requests per call on the staged-limb route   */
+#define QAM_MAX_BATCH      1          /* requests per call on the staged-limb route   */
 #define QAM_MAX_BATCH_MFMA 32         /* requests per qam_qmatvec call (matrix cores) */
 #define QAM_MAX_BLOCKS     65536      /* blocks per matrix (N <= 4,194,304)         */
-#define QAM_WS_COUNTER_BYTES (QAM_MAX_BLOCKS * 4)  /* workspace counter region      */
+#define QAM_MAX_FIELD_BLOCKS 262144   /* blocks of a field for qam_field_width       */
+/* Every workspace (and a group's or a decoder's device memory) starts with a
+ * counter region: per-block arrival counters, then the status word. */
+#define QAM_WS_STATUS_OFFSET (QAM_MAX_BLOCKS * 4)
+#define QAM_WS_COUNTER_BYTES (QAM_MAX_BLOCKS * 4 + 256)
+
+/* Status bits (qam_status). */
+#define QAM_STATUS_BAD_RUNG 1u        /* a level map held a rung above 4: the blocks
+                                         concerned were not read and their outputs
+                                         are NaN */
 
 #define QAM_X_F32  0
 #define QAM_X_BF16 1
@@ -145,12 +158,20 @@ typedef struct qam_lens {
 #define QAM_COMBINE_MAX 1
 #define QAM_MAX_STOPS   (QAM_MAX_RUNGS - 1)
 
+#define QAM_RADIUS_LENS 0   /* R_i = r_i f / (1 - f)     ([Lens] "The mechanism") */
+#define QAM_RADIUS_ZONE 1   /* R = f D, D the field width ([FoQLens] "FoQZones, the
+                               mechanism", rule 1: f = 0 the centre only, f = 1 the
+                               whole network); every lens the same R, r_i unused */
+
 typedef struct qam_lens_params {
     double f;           /* focus_area, in [0, 1]                        */
     double g;           /* focus_strength, in [0, 1]                    */
     int    combine;     /* QAM_COMBINE_SUM or QAM_COMBINE_MAX           */
     int    n_stops;     /* 0: default stops; else must equal kappa - glass */
     double stops[QAM_MAX_STOPS]; /* s_(glass+1) > s_(glass+2) > ... > s_kappa > 0, in radii */
+    int    radius_mode; /* QAM_RADIUS_LENS (0) or QAM_RADIUS_ZONE       */
+    int    reserved;
+    double width;       /* zone mode: the field width D >= 0 (e.g. qam_field_width) */
 } qam_lens_params;
 
 /*
@@ -168,13 +189,19 @@ typedef struct qam_lens_params {
  *   rounded sqrt and division: the map is bit-identical to the same rules run
  *   in IEEE fp64 on a CPU.
  *
+ *   With params->radius_mode == QAM_RADIUS_ZONE the radius is the zone
+ *   rule R = f D of [FoQLens] "FoQZones, the mechanism" (rule 1), D =
+ *   params->width, the same for every lens; the other rules are unchanged.
+ *
  *   coords      (device) fp64 [n_blocks][2], finite.
  *   n_blocks    >= 0 (0 enqueues nothing).
  *   lenses      (host) [n_lenses], n_lenses in [0, QAM_MAX_LENSES]; r >= 0.
- *   params      (host) f, g in [0, 1]; explicit stops strictly decreasing, > 0.
- *   ladder_bits (host) [n_rungs], ladder_bits[0] == 0, strictly increasing,
- *               2 <= n_rungs <= QAM_MAX_RUNGS.  Only the rung count enters
- *               the rules; the bits matter to the memory formula.
+ *   params      (host) f, g in [0, 1]; explicit stops strictly decreasing, > 0;
+ *               radius_mode and, for zones, a finite width >= 0.
+ *   ladder_bits (host) [n_rungs]: the product ladder {0, 2, 4, 6, 8}
+ *               (n_rungs = 5), so that a rung index is the number of slices
+ *               qam_qmatvec reads; QAM_ERR_LADDER otherwise (the rules on
+ *               other ladders: qam_build_rung_map).
  *   glass       rung index gamma in [0, n_rungs - 1].
  *   level_out   (device) uint8 [n_blocks].
  * A uniform map (every block at one rung, e.g. the all-D4 pass and its D8
@@ -186,6 +213,35 @@ int qam_build_level_map(const double* coords, int64_t n_blocks,
                         uint8_t* level_out, hipStream_t s);
 
 /*
+ * qam_build_rung_map -- the same rules on any ladder ([FoQLens] "FoQZones,
+ *   the mechanism": the ladder is set by the model and its storage, the rules
+ *   are generic): ladder_bits[0] == 0, strictly increasing, 2 <= n_rungs <=
+ *   QAM_MAX_RUNGS; only the rung count enters the rules.  rung_out holds rung
+ *   indices of that ladder, which are not read depths of qam_qmatvec unless
+ *   the ladder is {0, 2, 4, 6, 8}.  Other arguments as qam_build_level_map.
+ */
+int qam_build_rung_map(const double* coords, int64_t n_blocks,
+                       const qam_lens* lenses, int n_lenses, const qam_lens_params* params,
+                       const uint8_t* ladder_bits, int n_rungs, int glass,
+                       uint8_t* rung_out, hipStream_t s);
+
+/*
+ * qam_field_width -- the width D of a block field for the zone radius: the
+ *   largest Euclidean distance between two blocks (its diameter), so that at
+ *   f = 1 a zone around any block reaches every block ([FoQLens] "FoQZones,
+ *   the mechanism", rule 1: f = 1 takes the whole network).  The maximum of
+ *   the squared distances dx*dx + dy*dy (fp64, no contraction) is exact in
+ *   any order; D = sqrt of it, correctly rounded.
+ *   coords     (device) fp64 [n_blocks][2], finite, 8-byte aligned.
+ *   n_blocks   1 .. QAM_MAX_FIELD_BLOCKS (one block gives D = 0).
+ *   workspace  (device) 256 bytes, 256-byte aligned.
+ *   width_out  (host) D.
+ *   Host-synchronous.
+ */
+int qam_field_width(const double* coords, int64_t n_blocks, void* workspace, size_t workspace_bytes,
+                    double* width_out, hipStream_t s);
+
+/*
  * qam_build_level_maps -- one level map per request, n_maps of them, each by
  *   the rules of qam_build_level_map with its own lenses and parameters (the
  *   per-request maps of a batch).  Maps are computed in launches of up to 8
@@ -194,8 +250,9 @@ int qam_build_level_map(const double* coords, int64_t n_blocks,
  *   params     (host) [n_maps].
  *   n_maps     1 .. QAM_MAX_BATCH_MFMA.
  *   level_out  (device) uint8 [n_maps][n_blocks].
- *   Other arguments and the numerics as qam_build_level_map; each map is
- *   bit-identical to a qam_build_level_map call with its lenses and params.
+ *   Other arguments (the product ladder) and the numerics as
+ *   qam_build_level_map; each map is bit-identical to a qam_build_level_map
+ *   call with its lenses and params.
  */
 int qam_build_level_maps(const double* coords, int64_t n_blocks, const qam_lens* lenses, int n_lenses,
                          const qam_lens_params* params, const uint8_t* ladder_bits, int n_rungs,
@@ -314,42 +371,38 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   the pass; [PoD]: cost counted in weight bytes read).  A ZERO block loads
  *   nothing and writes y = 0.
  *
- *   Arithmetic: x is walked in sub-chunks of columns (at most 1024 for
- *   B <= 2, 512 for B <= 5, 256 for B <= 8); each is put on
- *   a fixed-point grid, x~ = round(x * 2^(22-e)) * 2^(e-22) with
- *   2^(e-1) <= max|x| < 2^e over the sub-chunk, held as three signed int8
- *   limbs; c . x~ is accumulated exactly in integers (int8 dot products),
- *   sub-chunks and column chunks are summed in fp64 in a fixed order, and
- *   y = fl32(scale * sum).  Hence
- *     |y - y_exact| <= 2^-22 sum_sub max_sub|x| sum_sub|w| + 2^-24|y| (+ fp64),
- *   which meets 1e-4 sum|w||x| unless the |w|-weighted mean of |x| in a
- *   sub-chunk falls below about 2.4e-3 of that sub-chunk's largest |x|;
- *   results are bit-reproducible run to run.  Integer-valued x with
- *   |x| < 2^22 and scale 1 gives exact integer outputs; a D8 map gives the
- *   untruncated int8 product.  A non-finite x makes that request's
- *   non-ZERO outputs NaN.
+ *   Arithmetic (exact integer products on a fixed-point x): x is taken in
+ *   chunks of columns per request (sub-chunks of 1024 columns at B = 1, the
+ *   column chunks of the pre-pass at B > 1).  With 2^(e-1) <= max|x| < 2^e
+ *   over the chunk,
+ *     q1 = round(x 2^(22-e)),  r1 = x - q1 2^(e-22),
+ *     q2 = round(r1 2^(45-e)), r2 = r1 - q2 2^(e-45)       (r1, r2 exact),
+ *   each q held as three signed int8 limbs; c . q1 and c . q2 are accumulated
+ *   exactly in int32 (v_mfma_i32_16x16x64_i8) and scaled into an fp64 row
+ *   sum.  |r2| <= 2^(e-46); an element with |r2| > 2^-15 |x| (possible only
+ *   for |x| < 2^(e-31)) has c * r2 added exactly in fp64 afterwards.  Every
+ *   element therefore enters the sum with relative error at most 2^-15, and
+ *   for every finite x and every code
+ *     |y - y_exact| <= 2^-15 sum_k |w_k||x_k| + 2^-24 |y_exact| (+ fp64 sums),
+ *   inside 1e-4 sum|w||x|.  Chunks are summed in fp64 in a fixed order and
+ *   y = fl32(scale * sum): results are bit-reproducible run to run.
+ *   Integer-valued x with |x| < 2^22 and scale 1 gives exact integer
+ *   outputs; a D8 map gives the untruncated int8 product.  A non-finite x
+ *   makes that request's non-ZERO outputs NaN.
  *
- *   Routes.  The staged-limb route (batch 1, and shared-map batches up to
- *   QAM_MAX_BATCH below a tunable threshold) stages each sub-chunk's limbs
- *   in LDS inside the product kernel and multiplies the rebuilt codes (four
- *   int8x4 words per 16-byte slice word, 16 rows x 64 columns per lane
- *   group) by them with v_mfma_i32_16x16x64_i8, B-operand column 3 r + l
- *   holding limb l of request r (one group of 16 columns up to 5 requests,
- *   two up to 8); its dot4 form on the vector ALUs (qam_set_staged_mfma(0))
- *   reaches the same integers, so the same bits.  The pre-pass route (batches of
- *   QAM_MAX_BATCH+1 .. 32, per-request maps, and shared-map batches from
- *   the threshold, 3 by default) runs a pre-pass that writes the limbs of x
- *   per column chunk as MFMA B operands, then v_mfma_i32_16x16x64_i8
- *   multiplies the codes with 16 requests of one limb at a time.  With
- *   per-request maps a block is read once, to the deepest slice any request
- *   needs, and each request gets the codes at its own depth, built from the
- *   same words (the residual slices make the code at depth d the sum of the
- *   first d/2 slices): the codes at each depth present are multiplied by
- *   the limbs of the requests at that depth (or, selected by a tuning hook,
- *   each slice plane by every request's limbs, each request adding the
- *   planes it reads: the same integers).  Both routes have the
- *   arithmetic and bound above (the pre-pass route's fixed point is per
- *   column chunk).
+ *   Routes.  B = 1, the staged-limb route: each wavefront stages its
+ *   sub-chunk's limbs in LDS inside the product kernel and multiplies the
+ *   rebuilt codes (four int8x4 words per 16-byte slice word, 16 rows x 64
+ *   columns per lane group) by them, B-operand column l holding limb l.
+ *   B = 2 .. 32, the pre-pass route: a pre-pass writes the limbs of x per
+ *   column chunk as MFMA B operands (six columns per request, up to 16
+ *   requests per set) and lists each chunk's uncovered elements, then the
+ *   product kernel multiplies the codes by them.  With per-request maps a
+ *   block is read once, to the deepest slice any request needs, and each
+ *   request gets the codes at its own depth, built from the same words (the
+ *   residual slices make the code at depth d the sum of the first d/2
+ *   slices): the codes at each depth present are multiplied by the limbs of
+ *   the requests at that depth.
  *
  *   x          (device) [B][K] row-major, fp32 (x_dtype QAM_X_F32) or bf16
  *              (QAM_X_BF16); 16-byte aligned.
@@ -358,16 +411,17 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   level_map  (device) uint8 rung indices of the ladder {0,2,4,6,8}
  *              (rung index = slices read): [n_blocks] shared by all requests
  *              (per_request_maps = 0) or [B][n_blocks], one map per request
- *              (per_request_maps = 1).
+ *              (per_request_maps = 1).  A rung above 4 raises
+ *              QAM_STATUS_BAD_RUNG; its outputs are NaN.
  *   y          (device) fp32 [B][N], must not overlap x.
- *   workspace  (device) qam_qmatvec_workspace_bytes(N, K, B) bytes (enough
- *              for either route; 0 when no route needs any, NULL is then
- *              accepted), 256-byte aligned.  Its first QAM_WS_COUNTER_BYTES
- *              hold per-block arrival counters: they must be zero before the
- *              first use, and every call leaves them zero again, whatever
- *              the shape, so one buffer serves calls of any shape.  The rest
- *              holds fp64 partial sums and limbs that each call writes before
- *              it reads.  Calls that share a workspace must be ordered (same
+ *   workspace  (device) qam_qmatvec_workspace_bytes(N, K, B) bytes (at least
+ *              QAM_WS_COUNTER_BYTES), 256-byte aligned.  Its first
+ *              QAM_WS_COUNTER_BYTES hold per-block arrival counters and the
+ *              status word: they must be zero before the first use; every
+ *              call leaves the counters zero again, whatever the shape, so
+ *              one buffer serves calls of any shape.  The rest holds fp64
+ *              partial sums, limbs and lists that each call writes before it
+ *              reads.  Calls that share a workspace must be ordered (same
  *              stream or synchronised).
  *   N          at most QAM_MAX_BLOCKS blocks of 64 rows (half that for
  *              B > 16 on the pre-pass route).
@@ -378,6 +432,14 @@ int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_packed* packed,
                 const uint8_t* level_map, int per_request_maps, float* y,
                 void* workspace, size_t workspace_bytes, hipStream_t s);
 
+/*
+ * qam_status -- read the status word of a workspace (or of a group's or a
+ *   decoder's device memory: the dev_mem given at init), optionally clearing
+ *   it.  Bits QAM_STATUS_*; 0 when every launch since the last clear ran as
+ *   documented.  Host-synchronous; a debugging aid, not needed for results.
+ */
+int qam_status(const void* workspace, int clear, uint32_t* status_out, hipStream_t s);
+
 /* ---------------------------------------------------------------- fused epilogues */
 /*
  * qam_qmatvec_ep -- qam_qmatvec with the glue of a decode step folded into
@@ -386,7 +448,7 @@ int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_packed* packed,
  *   normalisation and gated activation around the weight reads of the
  *   decoder-only model the [PoD] abstract decodes (Qwen3-0.6B), so that a
  *   decode step can be timed as tokens/s with no kernel other than the
- *   mixed-depth product.
+ *   mixed-depth product.  One request (B = 1).
  *
  *   With v[r][n] = scale[n] * sum_k c[n][k] x'[r][k], where
  *     x' = x                                 (ep->rms_norm == 0)
@@ -402,8 +464,7 @@ int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_packed* packed,
  *   A ZERO block reads nothing: v = 0 for its rows (QAM_OUT_ADD leaves y as
  *   it is, QAM_OUT_GLU writes 0).  Other arguments, the workspace and the
  *   error bound (on v) are those of qam_qmatvec's staged-limb route; y must
- *   not overlap x.  B <= QAM_MAX_BATCH, shared map; ep == NULL is that route
- *   of qam_qmatvec.
+ *   not overlap x.  B = 1; ep == NULL is qam_qmatvec at B = 1.
  */
 #define QAM_OUT_STORE 0
 #define QAM_OUT_ADD   1
@@ -443,6 +504,8 @@ typedef struct qam_gemv_item {
 } qam_gemv_item;
 
 typedef struct qam_group {     /* filled by qam_group_init; treat as opaque          */
+    void*   dev_mem;           /* (device) the dev_mem given at init (counters, status) */
+    int     ksplit;            /* pre-pass route: waves per request set on a chunk    */
     int     n_items;
     int64_t B;
     int     x_dtype;
@@ -461,8 +524,27 @@ typedef struct qam_group {     /* filled by qam_group_init; treat as opaque     
 } qam_group;
 
 /* Device bytes qam_group_init needs (0 if the items are invalid).  The route
- * is chosen as by qam_qmatvec from B and per_request_maps. */
+ * is chosen as by qam_qmatvec from B. */
 size_t qam_group_bytes(const qam_gemv_item* items, int n_items, int64_t B, int per_request_maps);
+
+/*
+ * Launch-plan settings of a group: how the work is cut into workgroups, never
+ * the results (every setting gives the same bits).  0 in a field takes the
+ * library's default.
+ */
+typedef struct qam_tuning {
+    int target_waves;      /* wavefronts aimed for per launch (64 .. 2^20)           */
+    int max_chunk_tiles;   /* B = 1: longest column chunk, in 64-column tiles        */
+    int tail_pct;          /* B = 1: share of the block tiles planned with short chunks
+                              (-1: none)                                              */
+    int tail_div;          /* B = 1: how much shorter (1 .. 64)                      */
+    int ksplit;            /* B > 1: waves per request set splitting a chunk (1, 2, 4) */
+    int set_max;           /* B > 1: most requests per set (8 .. 16)                 */
+    int tiles_per_request; /* B > 1: shortest chunk, in tiles per request (1 .. 64)  */
+} qam_tuning;
+
+size_t qam_group_bytes_tuned(const qam_gemv_item* items, int n_items, int64_t B, int per_request_maps,
+                             const qam_tuning* tuning);
 
 /*
  * qam_group_init -- validate the items (as qam_qmatvec does for each), lay
@@ -476,6 +558,13 @@ size_t qam_group_bytes(const qam_gemv_item* items, int n_items, int64_t B, int p
 int qam_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dtype,
                    int per_request_maps, void* dev_mem, size_t dev_bytes, qam_group* group_out,
                    hipStream_t s);
+
+/* qam_group_init with a launch plan of the caller's (tuning may be NULL:
+ * defaults); the plan is stored in the group and used by every launch of it.
+ * dev_bytes from qam_group_bytes_tuned with the same tuning. */
+int qam_group_init_tuned(const qam_gemv_item* items, int n_items, int64_t B, int x_dtype,
+                         int per_request_maps, const qam_tuning* tuning, void* dev_mem, size_t dev_bytes,
+                         qam_group* group_out, hipStream_t s);
 
 /*
  * qam_qmatvec_group -- one launch (two on the pre-pass route: the limb
@@ -495,12 +584,10 @@ int qam_qmatvec_group(const qam_group* group, hipStream_t s);
  *   product at the group's maps ([FoQLens] "FoQZones, the mechanism": the
  *   layer read once, its lifted blocks read deeper after it decides).  The
  *   sum is formed in fp64 from the fp32 y and rounded once.
- *   group        initialised by qam_group_init on the pre-pass route (B >= 2,
- *                the route qam_group_init takes from 3 requests by default)
- *                and not in the per-slice form.
+ *   group        initialised by qam_group_init on the pre-pass route (B >= 2).
  *   first_slice  1 .. 3.
  *   Errors: QAM_ERR_NULL (uninitialised group), QAM_ERR_ARG (another route,
- *   the per-slice form, first_slice out of range).  Asynchronous on `s`.
+ *   first_slice out of range).  Asynchronous on `s`.
  */
 int qam_qmatvec_group_refine(const qam_group* group, int first_slice, hipStream_t s);
 
@@ -513,9 +600,9 @@ int qam_qmatvec_group_refine(const qam_group* group, int first_slice, hipStream_
  *   wavefront computes the rung of its own block, one lane per lens, before
  *   reading the block's planes: the map costs no launch of its own and the
  *   planes read are those of the map.
- *   group      from qam_group_init on the staged-limb route with B <= 2
- *              and a shared map, every item's coords bound
- *              (group->lens_ready); else QAM_ERR_ARG, nothing enqueued.
+ *   group      from qam_group_init with B = 1 (the staged-limb route),
+ *              every item's coords bound (group->lens_ready); else
+ *              QAM_ERR_ARG, nothing enqueued.
  *   lenses, n_lenses, params, glass   as qam_build_level_map; one map rule
  *              set for every item (the items are blocks of one field).
  *   ladder_bits/n_rungs  must be the product ladder {0, 2, 4, 6, 8}

@@ -21,7 +21,9 @@ from .api import (  # noqa: F401
     Workspace,
     build_level_map,
     build_level_maps,
+    build_rung_map,
     escalation_schedule,
+    field_width,
     fit_focus_area,
     last_variant,
     layer_levels,
@@ -29,6 +31,7 @@ from .api import (  # noqa: F401
     pack_slices,
     packed_bytes,
     qmatvec,
+    status,
     unpack_codes,
     workspace_bytes,
 )

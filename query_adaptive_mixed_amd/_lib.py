@@ -17,12 +17,18 @@ ERRORS = {-1: "QAM_ERR_NULL", -2: "QAM_ERR_SHAPE", -3: "QAM_ERR_ARG", -4: "QAM_E
           -5: "QAM_ERR_ALIGN", -6: "QAM_ERR_HIP", -7: "QAM_ERR_WORKSPACE"}
 QAM_MAX_LENSES = 64
 QAM_MAX_STOPS = 15
-QAM_MAX_BATCH = 8
+QAM_MAX_BATCH = 1
 QAM_MAX_BATCH_MFMA = 32
 QAM_MAX_K = 65536
 QAM_X_F32, QAM_X_BF16 = 0, 1
 QAM_COMBINE_SUM, QAM_COMBINE_MAX = 0, 1
 QAM_OUT_STORE, QAM_OUT_ADD, QAM_OUT_GLU = 0, 1, 2
+QAM_RADIUS_LENS, QAM_RADIUS_ZONE = 0, 1
+QAM_MAX_BLOCKS = 65536
+QAM_MAX_FIELD_BLOCKS = 262144
+QAM_WS_STATUS_OFFSET = QAM_MAX_BLOCKS * 4
+QAM_WS_COUNTER_BYTES = QAM_MAX_BLOCKS * 4 + 256
+QAM_STATUS_BAD_RUNG = 1
 
 
 class QamPacked(C.Structure):
@@ -36,7 +42,8 @@ class QamLens(C.Structure):
 
 class QamLensParams(C.Structure):
     _fields_ = [("f", C.c_double), ("g", C.c_double), ("combine", C.c_int), ("n_stops", C.c_int),
-                ("stops", C.c_double * QAM_MAX_STOPS)]
+                ("stops", C.c_double * QAM_MAX_STOPS), ("radius_mode", C.c_int), ("reserved", C.c_int),
+                ("width", C.c_double)]
 
 
 QAM_LAYER_THRESHOLD = 0
@@ -60,8 +67,14 @@ class QamGemvItem(C.Structure):
                 ("level_stride", C.c_int64), ("coords", C.c_void_p)]
 
 
+class QamTuning(C.Structure):
+    _fields_ = [("target_waves", C.c_int), ("max_chunk_tiles", C.c_int), ("tail_pct", C.c_int),
+                ("tail_div", C.c_int), ("ksplit", C.c_int), ("set_max", C.c_int), ("tiles_per_request", C.c_int)]
+
+
 class QamGroup(C.Structure):
-    _fields_ = [("n_items", C.c_int), ("B", C.c_int64), ("x_dtype", C.c_int), ("n_workgroups", C.c_int64),
+    _fields_ = [("dev_mem", C.c_void_p), ("ksplit", C.c_int), ("n_items", C.c_int), ("B", C.c_int64),
+                ("x_dtype", C.c_int), ("n_workgroups", C.c_int64),
                 ("lds_bytes", C.c_size_t), ("table", C.c_void_p), ("wg_map", C.c_void_p), ("route", C.c_int),
                 ("per_request_maps", C.c_int), ("n_pre_workgroups", C.c_int64), ("pre_map", C.c_void_p),
                 ("lens_ready", C.c_int), ("sets", C.c_int), ("set_size", C.c_int), ("col_groups", C.c_int)]
@@ -101,6 +114,9 @@ SIGNATURES = [
     ("qam_describe_packed", _I, [_P, _I64, _I64, C.POINTER(QamPacked)]),
     ("qam_unpack_codes", _I, [C.POINTER(QamPacked), _P, _P, _P]),
     ("qam_build_level_map", _I, [_P, _I64, C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I, _I, _P, _P]),
+    ("qam_build_rung_map", _I, [_P, _I64, C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I, _I, _P, _P]),
+    ("qam_field_width", _I, [_P, _I64, _P, _SZ, C.POINTER(_D), _P]),
+    ("qam_status", _I, [_P, _I, C.POINTER(C.c_uint32), _P]),
     ("qam_build_level_maps", _I, [_P, _I64, C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I, _I, _I, _P,
                                   _P]),
     ("qam_map_weight_bytes", _I, [_P, _I64, _I64, _P, _I, C.POINTER(_D), C.POINTER(_I64)]),
@@ -118,6 +134,9 @@ SIGNATURES = [
     ("qam_escalation_schedule", _I, [_P, _I64, _D, _P, C.POINTER(_I64)]),
     ("qam_group_bytes", C.c_size_t, [C.POINTER(QamGemvItem), _I, _I64, _I]),
     ("qam_group_init", _I, [C.POINTER(QamGemvItem), _I, _I64, _I, _I, _P, _SZ, C.POINTER(QamGroup), _P]),
+    ("qam_group_bytes_tuned", C.c_size_t, [C.POINTER(QamGemvItem), _I, _I64, _I, C.POINTER(QamTuning)]),
+    ("qam_group_init_tuned", _I, [C.POINTER(QamGemvItem), _I, _I64, _I, _I, C.POINTER(QamTuning), _P, _SZ,
+                                  C.POINTER(QamGroup), _P]),
     ("qam_qmatvec_group", _I, [C.POINTER(QamGroup), _P]),
     ("qam_qmatvec_group_lens", _I, [C.POINTER(QamGroup), C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I,
                                     _I, _P]),
@@ -133,21 +152,11 @@ SIGNATURES = [
     ("qam_last_variant", C.c_char_p, []),
     ("qam_version", C.c_char_p, []),
 ]
-# tuning hooks that are not part of the product ABI contract
+# benchmark hooks (kernel-side launch timing), not part of the product ABI contract
 EXTRA_SIGNATURES = [
-    ("qam_set_target_waves", _I, [_I]),
-    ("qam_set_max_chunk_tiles", _I, [_I]),
-    ("qam_set_mfma_target_waves", _I, [_I]),
-    ("qam_set_mfma_min_batch", _I, [_I]),
-    ("qam_set_staged_mfma", _I, [_I]),
     ("qam_group_launch_times", _I, [C.POINTER(QamGroup), _I, _P, _P]),
     ("qam_group_lens_launch_times", _I, [C.POINTER(QamGroup), C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P,
                                          _I, _I, _I, _P, _P]),
-    ("qam_set_tail_split", _I, [_I, _I]),
-    ("qam_set_mfma_tiles_per_request", _I, [_I]),
-    ("qam_set_mfma_ksplit", _I, [_I]),
-    ("qam_set_mfma_set_max", _I, [_I]),
-    ("qam_set_mfma_per_slice_max", _I, [_I]),
 ]
 
 

@@ -87,10 +87,12 @@ class LensRules:
     """One map's lens-rule arguments, marshalled once for the C ABI:
     ``centres`` [n_lenses, 2] and ``radii`` [n_lenses] (host sequences), the
     focus area ``f`` and strength ``g``, ``combine`` ('sum' or 'max'), the
-    ``glass`` rung, optional explicit ``stops`` and the ladder."""
+    ``glass`` rung, optional explicit ``stops`` and the ladder.  ``radius``
+    is "lens" (R_i = r_i f / (1 - f)) or "zone" (R = f width for every lens,
+    ``width`` the field's, e.g. from ``field_width``)."""
 
     def __init__(self, centres, radii, f: float, g: float, combine: str = "sum", glass: int = 1, stops=None,
-                 ladder_bits: Sequence[int] = LADDER_BITS):
+                 ladder_bits: Sequence[int] = LADDER_BITS, radius: str = "lens", width: float = 0.0):
         centres = np.asarray(centres, dtype=np.float64).reshape(-1, 2)
         radii = np.asarray(radii, dtype=np.float64).reshape(-1)
         if centres.shape[0] != radii.shape[0]:
@@ -112,6 +114,8 @@ class LensRules:
                 raise ValueError("too many stops")
             for j, v in enumerate(st):
                 p.stops[j] = float(v)
+        p.radius_mode = {"lens": L.QAM_RADIUS_LENS, "zone": L.QAM_RADIUS_ZONE}[radius]
+        p.width = float(width)
         self.params = p
         self.n_rungs = len(ladder_bits)
         self.ladder = (C.c_uint8 * self.n_rungs)(*ladder_bits)
@@ -120,21 +124,56 @@ class LensRules:
 
 def build_level_map(coords: torch.Tensor, centres, radii, f: float, g: float, combine: str = "sum",
                     glass: int = 1, ladder_bits: Sequence[int] = LADDER_BITS, stops=None,
-                    out: Optional[torch.Tensor] = None, rules: Optional[LensRules] = None) -> torch.Tensor:
-    """Per-block rung indices (uint8 [n_blocks]) from the lens rules.
+                    out: Optional[torch.Tensor] = None, rules: Optional[LensRules] = None,
+                    radius: str = "lens", width: float = 0.0) -> torch.Tensor:
+    """Per-block rung indices (uint8 [n_blocks]) from the lens rules, on the
+    product's ladder {0, 2, 4, 6, 8} (a rung index is the slices qmatvec reads).
 
     ``coords`` is a device fp64 [n_blocks, 2] tensor; ``centres`` [n_lenses, 2]
     and ``radii`` [n_lenses] are host sequences (or pass ``rules``, a
     LensRules, with centres = radii = None)."""
+    return _build_map(coords, centres, radii, f, g, combine, glass, ladder_bits, stops, out, rules, radius, width,
+                      "qam_build_level_map")
+
+
+def build_rung_map(coords: torch.Tensor, centres, radii, f: float, g: float, combine: str = "sum",
+                   glass: int = 1, ladder_bits: Sequence[int] = LADDER_BITS, stops=None,
+                   out: Optional[torch.Tensor] = None, rules: Optional[LensRules] = None,
+                   radius: str = "lens", width: float = 0.0) -> torch.Tensor:
+    """The same rules on any ladder (rung indices of ``ladder_bits``, not read
+    depths of qmatvec unless the ladder is {0, 2, 4, 6, 8})."""
+    return _build_map(coords, centres, radii, f, g, combine, glass, ladder_bits, stops, out, rules, radius, width,
+                      "qam_build_rung_map")
+
+
+def _build_map(coords, centres, radii, f, g, combine, glass, ladder_bits, stops, out, rules, radius, width, fn):
     _require_cuda(coords, "coords", torch.float64)
     n_blocks = coords.shape[0]
-    r = rules if rules is not None else LensRules(centres, radii, f, g, combine, glass, stops, ladder_bits)
+    r = rules if rules is not None else LensRules(centres, radii, f, g, combine, glass, stops, ladder_bits, radius,
+                                                  width)
     if out is None:
         out = torch.empty(n_blocks, dtype=torch.uint8, device=coords.device)
-    L.check(L.lib().qam_build_level_map(_ptr(coords), n_blocks, r.lenses, r.n_lenses, C.byref(r.params),
-                                        C.cast(r.ladder, C.c_void_p), r.n_rungs, r.glass, _ptr(out),
-                                        _stream_handle()))
+    L.check(getattr(L.lib(), fn)(_ptr(coords), n_blocks, r.lenses, r.n_lenses, C.byref(r.params),
+                                 C.cast(r.ladder, C.c_void_p), r.n_rungs, r.glass, _ptr(out), _stream_handle()))
     return out
+
+
+def field_width(coords: torch.Tensor) -> float:
+    """The width D of a block field (its largest distance between two
+    blocks), computed on the device; the zone radius is R = f D."""
+    _require_cuda(coords, "coords", torch.float64)
+    ws = torch.zeros(256, dtype=torch.uint8, device=coords.device)
+    d = C.c_double()
+    L.check(L.lib().qam_field_width(_ptr(coords), coords.shape[0], _ptr(ws), 256, C.byref(d), _stream_handle()))
+    return d.value
+
+
+def status(mem: torch.Tensor, clear: bool = True) -> int:
+    """The status word (QAM_STATUS_* bits) of a workspace or of a group's or a
+    decoder's device memory; 0 when every launch ran as documented."""
+    out = C.c_uint32()
+    L.check(L.lib().qam_status(_ptr(mem), int(bool(clear)), C.byref(out), _stream_handle()))
+    return int(out.value)
 
 
 def fit_focus_area(coords: torch.Tensor, block_weights: torch.Tensor, centres, radii, g: float, budget_bytes: int,
@@ -265,8 +304,8 @@ def qmatvec(x: torch.Tensor, packed: PackedMatrix, level_map: torch.Tensor, y: O
     [B, n_blocks] (one map per request).  ``rms_norm`` multiplies in
     1 / sqrt(mean(x^2) + eps); ``out_mode`` is "store" (y [B, N]), "add"
     (y += product, y given) or "glu" (gate/up rows interleaved 32/32 per
-    block, y [B, N/2] = silu(gate) * up); the last two and ``rms_norm`` take a
-    shared map and B <= 8."""
+    block, y [B, N/2] = silu(gate) * up); the last two and ``rms_norm`` take
+    one request (B = 1)."""
     _require_cuda(level_map, "level_map", torch.uint8)
     if x.dim() == 1:
         x = x.unsqueeze(0)
@@ -298,7 +337,9 @@ def qmatvec(x: torch.Tensor, packed: PackedMatrix, level_map: torch.Tensor, y: O
             raise ValueError(f"y must hold {B} x {n_out} values")
     ws = workspace or default_workspace(x.device)
     need = workspace_bytes(packed.N, packed.K, B)
-    wbuf = ws.get(max(need, 1))
+    if need == 0:
+        raise L.QamError(-2, f"no workspace size for N={packed.N} K={packed.K} B={B}")
+    wbuf = ws.get(need)
     if rms_norm or mode != L.QAM_OUT_STORE:
         if per_request:
             raise ValueError("fused epilogues take a shared level map")
@@ -321,9 +362,10 @@ class GroupedQmatvec:
     and update them in place), and every ``run()`` recomputes all the y from
     the bound buffers.  A fifth element, the item's block coordinates (device
     fp64 [n_blocks, 2]), lets ``run_lens`` build the maps in the product
-    launch (staged route, shared maps)."""
+    launch (one request).  ``tuning`` (a dict of qam_tuning fields) sets the
+    group's launch plan; the results do not depend on it."""
 
-    def __init__(self, items, device="cuda"):
+    def __init__(self, items, device="cuda", tuning: Optional[dict] = None):
         n = len(items)
         arr = (L.QamGemvItem * n)()
         B = None
@@ -363,13 +405,20 @@ class GroupedQmatvec:
                     raise ValueError("coords must be a contiguous fp64 [n_blocks, 2] tensor")
                 arr[i].coords = cd.data_ptr()
             self._keep.append((pm, x, y, lv, cd))
-        nbytes = int(L.lib().qam_group_bytes(arr, n, B, int(per_request)))
+        tun = L.QamTuning()
+        for k, v in (tuning or {}).items():
+            setattr(tun, k, int(v))
+        nbytes = int(L.lib().qam_group_bytes_tuned(arr, n, B, int(per_request), C.byref(tun)))
         if nbytes == 0:
-            raise L.QamError(-2, "invalid group items")
+            raise L.QamError(-2, "invalid group items or tuning")
         self.mem = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         self.desc = L.QamGroup()
-        L.check(L.lib().qam_group_init(arr, n, B, xdt, int(per_request), _ptr(self.mem), nbytes, C.byref(self.desc),
-                                       _stream_handle()))
+        L.check(L.lib().qam_group_init_tuned(arr, n, B, xdt, int(per_request), C.byref(tun), _ptr(self.mem), nbytes,
+                                             C.byref(self.desc), _stream_handle()))
+
+    def status(self, clear: bool = True) -> int:
+        """The group's status word (QAM_STATUS_* bits, 0 if all is well)."""
+        return status(self.mem, clear)
 
     @property
     def route(self) -> str:
@@ -463,7 +512,7 @@ class LayerDecidesGroup:
     ``levels[i]`` holds matrix i's maps [B, n_blocks] afterwards.  Up to 16
     matrices of at most 512 blocks each share one level launch.  With
     ``refine`` (taken where the second product runs on the pre-pass route,
-    from 3 requests, and the glass is D2-D6), the base product is written
+    from 2 requests, and the glass is D2-D6), the base product is written
     into y and the second product only adds the lifted blocks' slices above
     the glass (``qam_qmatvec_group_refine``): every block is read once to
     the glass and the lifted ones on from there; ``self.refine`` says which
@@ -472,7 +521,7 @@ class LayerDecidesGroup:
     def __init__(self, items, rule: LayerRule, device="cuda", refine: bool = True):
         self.rule = rule
         B0 = items[0][1].shape[0] if items[0][1].dim() == 2 else 1
-        refine = bool(refine) and B0 >= 3 and 1 <= rule.glass <= 3 and rule.n_rungs == len(LADDER_BITS)
+        refine = bool(refine) and B0 >= 2 and 1 <= rule.glass <= 3 and rule.n_rungs == len(LADDER_BITS)
         base_items, second_items, self.parts = [], [], []
         for pm, x, y in items:
             B = x.shape[0] if x.dim() == 2 else 1
@@ -486,8 +535,8 @@ class LayerDecidesGroup:
             self.parts.append((pm, y_base, shat, lv))
         self.base = GroupedQmatvec(base_items, device=device)
         self.second = GroupedQmatvec(second_items, device=device)
-        # on the staged route (a tuning hook can send 3+ requests there) the
-        # second product is a full one at the maps, which overwrites y
+        # at one request (the staged route) the second product is a full one
+        # at the maps, which overwrites y
         self.refine = refine and self.second.route == "prepass"
         self.levels = [p[3] for p in self.parts]
         # one launch for every matrix when each has at most 512 blocks
@@ -585,6 +634,7 @@ class Decoder:
         h = C.c_void_p()
         L.check(L.lib().qam_decoder_create(C.byref(d), _ptr(self.mem), nbytes, C.byref(h), _stream_handle()))
         self._h = h
+        self._destroy = L.lib().qam_decoder_destroy   # held here: module globals may be gone at interpreter exit
         self.n_layers = n
         self.n_ops = 4 * n + 1
         self.hidden = self._buffer(0, hidden)
@@ -634,11 +684,15 @@ class Decoder:
             esc.ctypes.data_as(C.c_void_p), _stream_handle()))
         return esc
 
+    def status(self, clear: bool = True) -> int:
+        """The decoder's status word (QAM_STATUS_* bits, 0 if all is well)."""
+        return status(self.mem, clear)
+
     def __del__(self):
-        h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            L.lib().qam_decoder_destroy(h)
-            self._h = None
+        h, destroy = getattr(self, "_h", None), getattr(self, "_destroy", None)
+        self._h = None
+        if h is not None and h.value and callable(destroy):
+            destroy(h)
 
 
 def escalation_schedule(scores, rate: float) -> np.ndarray:

@@ -59,7 +59,7 @@ std::vector<Op> chain(const qam_decoder& dec) {
 Plan plan_of(const qam_packed& w, int64_t target_waves) {
     // chunks of whole D8 rings (2 tiles) so that small matrices spread over
     // many wavefronts: a decode step is a chain of short, latency-bound launches
-    return make_plan(w.N, w.K, 1, chunk_goal(w.n_blocks * (w.K / kTileCols), target_waves), 2);
+    return make_plan(w.N, w.K, chunk_goal(w.n_blocks * (w.K / kTileCols), target_waves, 0), 2);
 }
 
 bool same_shape(const qam_packed& w, int64_t N, int64_t K) {
@@ -119,6 +119,7 @@ int enqueue(qam_decoder* dec, int rung, int first, int count, hipStream_t s) {
     Common c{};
     c.B = 1;
     c.x_bf16 = 0;
+    c.status = status_word(dec->ws);
     for (int i = first; i < first + count; ++i) {
         const Op& op = ops[(size_t)i];
         const Plan p = plan_of(*op.w, dec->target_waves);
@@ -132,7 +133,8 @@ int enqueue(qam_decoder* dec, int rung, int first, int count, hipStream_t s) {
             it.counters = reinterpret_cast<uint32_t*>(dec->ws);
             it.partials = reinterpret_cast<double*>(dec->ws + QAM_WS_COUNTER_BYTES);
         }
-        launch_single(1, it, c, (int64_t)p.n_chunks * p.n_quads, s);
+        it.counters = reinterpret_cast<uint32_t*>(dec->ws);
+        launch_single(it, c, (int64_t)p.n_chunks * p.n_quads, s);
     }
     QAM_HIP_CHECK(hipGetLastError());
     return QAM_OK;

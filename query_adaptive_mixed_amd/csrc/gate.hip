@@ -180,11 +180,19 @@ __global__ __launch_bounds__(kGateThreads) void gate_kernel(const float* __restr
         __hip_atomic_store(&pp->i1, i1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&pp->i2, i2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&pp->bad, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);   // the partial is stored before it is counted
+        // the partial is stored before it is counted: the signal fences keep
+        // the compiler from moving the stores past the wait or the counter
+        // update (they emit no instruction), and the wait holds the hardware
+        // to it (device-scope stores are written through to L2 in order of
+        // completion, and the counter update is issued after they complete)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         last = (int)(__hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                      gridDim.x - 1);
     }
     __syncthreads();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // no partial load moves ahead of the count
     if (!last) return;
 
     // the last workgroup: every partial is in; thread k takes partial k

@@ -7,7 +7,9 @@
 // same rung for a block bit for bit.
 //
 // Rules, with the readings taken where the pages are open:
-//   1 radius   R_i = r_i f / (1 - f), +inf at f = 1
+//   1 radius   R_i = r_i f / (1 - f), +inf at f = 1 (the lens rule); or the
+//              zone rule R = f D of "FoQLens", "FoQZones, the mechanism", with
+//              D the width of the field, the same R for every lens
 //   2 ceiling  kappa = gamma + floor(g (m - gamma)); n = kappa - gamma
 //   3 stops    s_(gamma+1) > ... > s_kappa, default (n - j) / n, j = 0..n-1
 //   4 lift     rho_i = d(b, c_i) / R_i (Euclidean d; R = 0 lifts only a block
@@ -111,13 +113,15 @@ __device__ __forceinline__ int lens_block_rung(const double* coords, int64_t b, 
 }
 
 // ---------------------------------------------------------------- host side
-// Ladder checks of a map call (error text names `who`).
+// Ladder checks of a map call (error text names `who`): any ladder, or the
+// product's ladder {0,2,4,6,8} (rung index = slices read).
 int lens_check_ladder(const uint8_t* ladder_bits, int n_rungs, int glass, const char* who);
+int lens_check_product_ladder(const uint8_t* ladder_bits, int n_rungs, int glass, const char* who);
 // Checks of one map's parameters and lenses; fills mp's rules 2-3, combine
 // and lens count (mp.first = 0).
 int lens_check_map(const qam_lens* lenses, int n_lenses, const qam_lens_params* params, int n_rungs, int glass,
                    MapParams& mp, const char* who);
-// Rule 1: (r f) / (1 - f), +inf at f = 1.
-double lens_radius(double r, double f);
+// Rule 1 at focus area f: (r f) / (1 - f), +inf at f = 1; in zone mode f D.
+double lens_radius(const qam_lens_params& p, double r, double f);
 
 }  // namespace qam

@@ -71,6 +71,10 @@ int lens_check_map(const qam_lens* lenses, int n_lenses, const qam_lens_params* 
     if (n_lenses > 0 && !lenses) QAM_FAIL(QAM_ERR_NULL, "%s: null lenses", who);
     const double f = params->f, g = params->g;
     if (!(f >= 0.0 && f <= 1.0)) QAM_FAIL(QAM_ERR_ARG, "%s: f outside [0, 1]", who);
+    if (params->radius_mode != QAM_RADIUS_LENS && params->radius_mode != QAM_RADIUS_ZONE)
+        QAM_FAIL(QAM_ERR_ARG, "%s: unknown radius_mode %d", who, params->radius_mode);
+    if (params->radius_mode == QAM_RADIUS_ZONE && !(params->width >= 0.0 && isfinite(params->width)))
+        QAM_FAIL(QAM_ERR_ARG, "%s: zone radius needs a finite width >= 0", who);
     if (!(g >= 0.0 && g <= 1.0)) QAM_FAIL(QAM_ERR_ARG, "%s: g outside [0, 1]", who);
     if (params->combine != QAM_COMBINE_SUM && params->combine != QAM_COMBINE_MAX)
         QAM_FAIL(QAM_ERR_ARG, "%s: combine must be SUM or MAX", who);
@@ -100,7 +104,10 @@ int lens_check_map(const qam_lens* lenses, int n_lenses, const qam_lens_params* 
     return QAM_OK;
 }
 
-double lens_radius(double r, double f) { return f == 1.0 ? INFINITY : (r * f) / (1.0 - f); }
+double lens_radius(const qam_lens_params& p, double r, double f) {
+    if (p.radius_mode == QAM_RADIUS_ZONE) return f * p.width;   // R = f D, every lens alike
+    return f == 1.0 ? INFINITY : (r * f) / (1.0 - f);
+}
 
 int lens_check_ladder(const uint8_t* ladder_bits, int n_rungs, int glass, const char* who) {
     if (n_rungs < 2 || n_rungs > QAM_MAX_RUNGS)
@@ -110,6 +117,14 @@ int lens_check_ladder(const uint8_t* ladder_bits, int n_rungs, int glass, const 
         if (ladder_bits[i] <= ladder_bits[i - 1]) QAM_FAIL(QAM_ERR_LADDER, "%s: ladder not increasing", who);
     if (glass < 0 || glass >= n_rungs) QAM_FAIL(QAM_ERR_ARG, "%s: glass=%d not a rung", who, glass);
     return QAM_OK;
+}
+
+int lens_check_product_ladder(const uint8_t* ladder_bits, int n_rungs, int glass, const char* who) {
+    static const uint8_t kProduct[5] = {0, 2, 4, 6, 8};
+    if (n_rungs != 5) QAM_FAIL(QAM_ERR_LADDER, "%s: the product ladder {0,2,4,6,8} has 5 rungs, got %d", who, n_rungs);
+    for (int i = 0; i < 5; ++i)
+        if (ladder_bits[i] != kProduct[i]) QAM_FAIL(QAM_ERR_LADDER, "%s: ladder must be {0,2,4,6,8}", who);
+    return lens_check_ladder(ladder_bits, n_rungs, glass, who);
 }
 
 // Lanes per block: the least power of two holding the launch's lens count.
@@ -152,7 +167,7 @@ extern "C" int qam_build_level_maps(const double* coords, int64_t n_blocks, cons
     if (n_maps < 1 || n_maps > QAM_MAX_BATCH_MFMA)
         QAM_FAIL(QAM_ERR_ARG, "build_level_maps: n_maps=%d outside [1, %d]", n_maps, QAM_MAX_BATCH_MFMA);
     if (n_blocks > 0 && (!coords || !level_out)) QAM_FAIL(QAM_ERR_NULL, "build_level_maps: null coords/output");
-    if (int rc = lens_check_ladder(ladder_bits, n_rungs, glass, "build_level_maps")) return rc;
+    if (int rc = lens_check_product_ladder(ladder_bits, n_rungs, glass, "build_level_maps")) return rc;
     if (n_lenses < 0 || n_lenses > QAM_MAX_LENSES)
         QAM_FAIL(QAM_ERR_ARG, "build_level_maps: n_lenses=%d outside [0, %d]", n_lenses, QAM_MAX_LENSES);
     std::vector<MapParams> mps((size_t)n_maps);
@@ -176,7 +191,7 @@ extern "C" int qam_build_level_maps(const double* coords, int64_t n_blocks, cons
                 const qam_lens& l = lenses[(int64_t)(k0 + k) * n_lenses + i];
                 a.t.cx[k * n_lenses + i] = l.cx;
                 a.t.cy[k * n_lenses + i] = l.cy;
-                a.t.R[k * n_lenses + i] = lens_radius(l.r, params[k0 + k].f);
+                a.t.R[k * n_lenses + i] = lens_radius(params[k0 + k], l.r, params[k0 + k].f);
             }
         }
         a.glass = glass;
@@ -189,26 +204,27 @@ extern "C" int qam_build_level_maps(const double* coords, int64_t n_blocks, cons
     return QAM_OK;
 }
 
-extern "C" int qam_build_level_map(const double* coords, int64_t n_blocks, const qam_lens* lenses, int n_lenses,
-                                   const qam_lens_params* params, const uint8_t* ladder_bits, int n_rungs,
-                                   int glass, uint8_t* level_out, hipStream_t s) {
+static int build_map(const double* coords, int64_t n_blocks, const qam_lens* lenses, int n_lenses,
+                     const qam_lens_params* params, const uint8_t* ladder_bits, int n_rungs, int glass,
+                     uint8_t* level_out, hipStream_t s, bool product, const char* who) {
     clear_error();
-    if (n_blocks < 0) QAM_FAIL(QAM_ERR_SHAPE, "build_level_map: n_blocks < 0");
-    if (!params || !ladder_bits) QAM_FAIL(QAM_ERR_NULL, "build_level_map: null params/ladder");
-    if (n_blocks > 0 && (!coords || !level_out)) QAM_FAIL(QAM_ERR_NULL, "build_level_map: null coords/output");
-    if (int rc = lens_check_ladder(ladder_bits, n_rungs, glass, "build_level_map")) return rc;
+    if (n_blocks < 0) QAM_FAIL(QAM_ERR_SHAPE, "%s: n_blocks < 0", who);
+    if (!params || !ladder_bits) QAM_FAIL(QAM_ERR_NULL, "%s: null params/ladder", who);
+    if (n_blocks > 0 && (!coords || !level_out)) QAM_FAIL(QAM_ERR_NULL, "%s: null coords/output", who);
+    if (int rc = product ? lens_check_product_ladder(ladder_bits, n_rungs, glass, who)
+                         : lens_check_ladder(ladder_bits, n_rungs, glass, who))
+        return rc;
     MapParams mp;
-    if (int rc = lens_check_map(lenses, n_lenses, params, n_rungs, glass, mp, "build_level_map")) return rc;
+    if (int rc = lens_check_map(lenses, n_lenses, params, n_rungs, glass, mp, who)) return rc;
     if (n_blocks == 0) return QAM_OK;
     if (n_blocks > (INT64_C(1) << 31) >> lanes_log2_for(n_lenses))
-        QAM_FAIL(QAM_ERR_SHAPE, "build_level_map: %lld blocks of %d lenses exceed one launch", (long long)n_blocks,
-                 n_lenses);
+        QAM_FAIL(QAM_ERR_SHAPE, "%s: %lld blocks of %d lenses exceed one launch", who, (long long)n_blocks, n_lenses);
     LensArgs a = {};
     a.maps[0] = mp;
     for (int i = 0; i < n_lenses; ++i) {
         a.t.cx[i] = lenses[i].cx;
         a.t.cy[i] = lenses[i].cy;
-        a.t.R[i] = lens_radius(lenses[i].r, params->f);
+        a.t.R[i] = lens_radius(*params, lenses[i].r, params->f);
     }
     a.glass = glass;
     a.lanes_log2 = lanes_log2_for(n_lenses);
@@ -216,6 +232,68 @@ extern "C" int qam_build_level_map(const double* coords, int64_t n_blocks, const
     launch_maps(coords, n_blocks, a, 1, level_out, s);
     QAM_HIP_CHECK(hipGetLastError());
     set_variant("levelmap_fp64");
+    return QAM_OK;
+}
+
+extern "C" int qam_build_level_map(const double* coords, int64_t n_blocks, const qam_lens* lenses, int n_lenses,
+                                   const qam_lens_params* params, const uint8_t* ladder_bits, int n_rungs,
+                                   int glass, uint8_t* level_out, hipStream_t s) {
+    return build_map(coords, n_blocks, lenses, n_lenses, params, ladder_bits, n_rungs, glass, level_out, s, true,
+                     "build_level_map");
+}
+
+extern "C" int qam_build_rung_map(const double* coords, int64_t n_blocks, const qam_lens* lenses, int n_lenses,
+                                  const qam_lens_params* params, const uint8_t* ladder_bits, int n_rungs, int glass,
+                                  uint8_t* rung_out, hipStream_t s) {
+    return build_map(coords, n_blocks, lenses, n_lenses, params, ladder_bits, n_rungs, glass, rung_out, s, false,
+                     "build_rung_map");
+}
+
+// The largest squared distance between two blocks, exactly (a max of fp64
+// values, order-free), into *acc as its bit pattern (non-negative doubles
+// order as their bits).  One thread per block i against every block j > i.
+__global__ __launch_bounds__(256) void width_kernel(const double* __restrict__ coords, int64_t n,
+                                                    unsigned long long* acc) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    double best = 0.0;
+    if (i < n) {
+        const double xi = coords[2 * i], yi = coords[2 * i + 1];
+        for (int64_t j = i + 1; j < n; ++j) {
+            const double dx = coords[2 * j] - xi;
+            const double dy = coords[2 * j + 1] - yi;
+            const double d2 = dx * dx + dy * dy;
+            best = d2 > best ? d2 : best;
+        }
+    }
+    unsigned long long u = __builtin_bit_cast(unsigned long long, best);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long v = __shfl_xor(u, o);
+        u = v > u ? v : u;
+    }
+    if ((threadIdx.x & 63) == 0 && u) atomicMax(acc, u);
+}
+
+extern "C" int qam_field_width(const double* coords, int64_t n_blocks, void* workspace, size_t workspace_bytes,
+                               double* width_out, hipStream_t s) {
+    clear_error();
+    if (!coords || !workspace || !width_out) QAM_FAIL(QAM_ERR_NULL, "field_width: null pointer");
+    if (n_blocks < 1 || n_blocks > QAM_MAX_FIELD_BLOCKS)
+        QAM_FAIL(QAM_ERR_SHAPE, "field_width: n_blocks=%lld outside [1, %d]", (long long)n_blocks, QAM_MAX_FIELD_BLOCKS);
+    if (workspace_bytes < 256) QAM_FAIL(QAM_ERR_WORKSPACE, "field_width: workspace %zu < 256 bytes", workspace_bytes);
+    if (!aligned(workspace, 256) || !aligned(coords, 8))
+        QAM_FAIL(QAM_ERR_ALIGN, "field_width: workspace 256-byte and coords 8-byte aligned");
+    unsigned long long* acc = static_cast<unsigned long long*>(workspace);
+    unsigned long long host = 0;
+    QAM_HIP_CHECK(hipMemsetAsync(acc, 0, sizeof(unsigned long long), s));
+    hipLaunchKernelGGL(width_kernel, dim3((unsigned)((n_blocks + 255) / 256)), dim3(256), 0, s, coords, n_blocks, acc);
+    QAM_HIP_CHECK(hipGetLastError());
+    QAM_HIP_CHECK(hipMemcpyAsync(&host, acc, sizeof(host), hipMemcpyDeviceToHost, s));
+    QAM_HIP_CHECK(hipStreamSynchronize(s));
+    const double d2 = __builtin_bit_cast(double, host);
+    if (!isfinite(d2)) QAM_FAIL(QAM_ERR_ARG, "field_width: coordinates not finite");
+    *width_out = sqrt(d2);
+    set_variant("field_width_fp64");
     return QAM_OK;
 }
 
@@ -233,7 +311,7 @@ extern "C" int qam_fit_focus_area(const double* coords, int64_t n_blocks, const 
     if (workspace_bytes < 256) QAM_FAIL(QAM_ERR_WORKSPACE, "fit_focus_area: workspace %zu < 256 bytes", workspace_bytes);
     if (!aligned(workspace, 256) || !aligned(block_weights, 8) || !aligned(coords, 8))
         QAM_FAIL(QAM_ERR_ALIGN, "fit_focus_area: workspace 256-byte, weights and coords 8-byte aligned");
-    if (int rc = lens_check_ladder(ladder_bits, n_rungs, glass, "fit_focus_area")) return rc;
+    if (int rc = lens_check_product_ladder(ladder_bits, n_rungs, glass, "fit_focus_area")) return rc;
     if (n_blocks > (INT64_C(1) << 31) >> lanes_log2_for(n_lenses))
         QAM_FAIL(QAM_ERR_SHAPE, "fit_focus_area: %lld blocks of %d lenses exceed one launch", (long long)n_blocks,
                  n_lenses);
@@ -250,7 +328,7 @@ extern "C" int qam_fit_focus_area(const double* coords, int64_t n_blocks, const 
         for (int i = 0; i < n_lenses; ++i) {
             a.t.cx[i] = lenses[i].cx;
             a.t.cy[i] = lenses[i].cy;
-            a.t.R[i] = lens_radius(lenses[i].r, f);
+            a.t.R[i] = lens_radius(p, lenses[i].r, f);
         }
         a.glass = glass;
         a.lanes_log2 = lanes_log2_for(n_lenses);

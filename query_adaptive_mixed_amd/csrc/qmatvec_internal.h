@@ -52,25 +52,76 @@ __device__ __forceinline__ int level_of(const uint8_t* level, int b) {
     return (int)((word >> (8 * (addr & 3))) & 0xFFu);
 }
 
-// Activations are held as three signed int8 limbs of a 24-bit fixed point
-// per sub-chunk: v = rint(x * 2^(kFrac - e)), |v| <= 2^22.
-constexpr int kLimbs = 3;
-constexpr int kFrac = 22;
+// ---------------------------------------------------------------- x in fixed point
+//
+// The products are exact integer arithmetic on a fixed-point x.  For a chunk
+// of columns of one request with largest |x| in [2^(e-1), 2^e):
+//   q1 = rint(x 2^(22-e)),   r1 = x - q1 2^(e-22)     (|q1| <= 2^22, r1 exact)
+//   q2 = rint(r1 2^(45-e)),  r2 = r1 - q2 2^(e-45)    (|q2| <= 2^22, r2 exact)
+// so x = q1 2^(e-22) + q2 2^(e-45) + r2 with |r2| <= 2^(e-46).  Each q is held
+// as three signed int8 limbs (balanced base-256 digits): six B-operand columns
+// per request, hi limbs 0..2 then lo limbs 0..2.  An element with
+// |r2| > 2^-15 |x| (possible only when |x| < 2^(e-31)) is "uncovered": its r2
+// times its code is added to the row sum in fp64 afterwards, so every element
+// enters the sum with relative error at most 2^-15 and every output meets
+// |y - y_exact| <= 2^-15 sum|w||x| + fl32 rounding, for any finite x.
+// A chunk whose largest |x| is below 2^-82 is first scaled by 2^100 (exact),
+// so that every constant below is a normal float; the digits are unchanged.
+constexpr int kLimbCols = 6;       // B-operand columns per request
+constexpr int kHiShift = 22;       // q1 = x 2^(22-e)
+constexpr int kLoShift = 45;       // q2 = r1 2^(45-e)
+constexpr int kSmallExp = -81;     // below this exponent the chunk is prescaled
+constexpr int kPrescale = 100;     // by 2^100
 
-// Balanced base-256 digits of the fixed-point value of one element, as three
-// signed bytes (byte l = digit l; the top byte is unused).
-__device__ __forceinline__ uint32_t limbs_of(float v, int sh) {
-    const int q = (int)rintf(ldexpf(v, sh));            // |q| <= 2^22
-    return ((uint32_t)q + 0x808080u) ^ 0x808080u;
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+struct XSplit {
+    float pre;                     // 1 or 2^100
+    float scale_hi, step_hi;       // 2^(22-e'), 2^(e'-22)
+    float scale_lo, step_lo;       // 2^(45-e'), 2^(e'-45)
+};
+
+__device__ __forceinline__ XSplit xsplit_of(int e) {
+    XSplit s;
+    const bool small = e < kSmallExp;
+    const int ep = small ? e + kPrescale : e;
+    s.pre = small ? pow2f(kPrescale) : 1.0f;
+    s.scale_hi = pow2f(kHiShift - ep);
+    s.step_hi = pow2f(ep - kHiShift);
+    s.scale_lo = pow2f(kLoShift - ep);
+    s.step_lo = pow2f(ep - kLoShift);
+    return s;
 }
 
-// The same digits when 2^sh is a normal float (sh <= 126, the usual case):
-// fma(v, 2^sh, 1.5 * 2^23) rounds v * 2^sh to the nearest integer q (ties to
-// even, as rintf) because the sum's ulp is 1 for |q| <= 2^22, and the float's
-// bits are 0x4B400000 + q.
-__device__ __forceinline__ uint32_t limbs_fast(float v, float scale) {
-    const uint32_t bits = __float_as_uint(__builtin_fmaf(v, scale, 12582912.0f));
-    return (bits + (0x808080u - 0x4B400000u)) ^ 0x808080u;
+// fma(v, 2^k, 1.5 * 2^23) rounds v 2^k to the nearest integer q (ties to even)
+// for |v 2^k| <= 2^22, and its bits are 0x4B400000 + q; the limb word holds
+// q's balanced base-256 digits in bytes 0..2 (byte 3 unused).
+__device__ __forceinline__ uint32_t limb_word_of(float t) {
+    return (__float_as_uint(t) + (0x808080u - 0x4B400000u)) ^ 0x808080u;
+}
+
+// One element: its hi and lo limb words, its residual r2 (in the prescaled
+// unit) and whether it is uncovered.
+__device__ __forceinline__ void split_elem(float v, const XSplit& s, uint32_t& w_hi, uint32_t& w_lo, float& r2,
+                                           bool& unc) {
+    constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
+    v = v * s.pre;
+    const float t1 = __builtin_fmaf(v, s.scale_hi, kMagic);
+    w_hi = limb_word_of(t1);
+    const float r1 = __builtin_fmaf(-(t1 - kMagic), s.step_hi, v);
+    const float t2 = __builtin_fmaf(r1, s.scale_lo, kMagic);
+    w_lo = limb_word_of(t2);
+    r2 = __builtin_fmaf(-(t2 - kMagic), s.step_lo, r1);
+    unc = fabsf(r2) > fabsf(v) * 0x1p-15f;
+}
+
+// The fp64 value of one request's six column sums (hi limbs s[0..2], lo
+// limbs s[3..5]) for a chunk of exponent e.
+__device__ __forceinline__ double limb_value(int64_t h0, int64_t h1, int64_t h2, int64_t l0, int64_t l1, int64_t l2,
+                                             int e) {
+    const double hi = (double)(h2 * 65536 + h1 * 256 + h0);
+    const double lo = (double)(l2 * 65536 + l1 * 256 + l0);
+    return ldexp(hi, e - kHiShift) + ldexp(lo, e - kLoShift);
 }
 
 // Limb words of four consecutive elements (digit words w0..w3): word l holds
@@ -87,6 +138,28 @@ __device__ __forceinline__ int4 limb_words(uint32_t w0, uint32_t w1, uint32_t w2
     out.z = (int)__builtin_amdgcn_perm(hi2, lo2, 0x05040100u);
     out.w = 0;
     return out;
+}
+
+// The int8 code of row `row` (0..63) of block b, column k, read from planes
+// first .. ns-1 (the code at depth 2 ns less the code at depth 2 first): one
+// 4-byte load per plane from the packed layout.  For the exact corrections of
+// uncovered elements (a slow path taken for them alone).
+__device__ __forceinline__ int code_at(const uint8_t* planes, int64_t pb, int64_t K, int b, int row, int64_t k,
+                                       int first, int ns) {
+    const int64_t t = k >> 6;
+    const int kc = (int)(k & 63);
+    const int lane = (row & 15) + 16 * (kc >> 4);
+    const int u = (kc >> 2) & 3, i = kc & 3;
+    const uint8_t* base = planes + (int64_t)b * 16 * K + t * 1024 + lane * 16 + 4 * (row >> 4);
+    uint32_t acc = 0;
+    for (int p = first; p < ns; ++p) {
+        const uint32_t w = *(const uint32_t*)(base + p * pb);
+        const uint32_t m = 0x03030303u << (2 * (3 - p));                 // slice 3 - p, before rotation
+        const uint32_t mk = u == 0 ? m : ((m >> (2 * u)) | (m << (32 - 2 * u)));
+        acc |= w & mk;
+    }
+    if (u != 0) acc = (acc << (2 * u)) | (acc >> (32 - 2 * u));
+    return (int)(int8_t)(uint8_t)(acc >> (8 * i));
 }
 
 // ---------------------------------------------------------------- launch descriptors
@@ -118,9 +191,10 @@ struct Item {
 struct Common {
     const Item* items;         // grouped launches: the descriptor table
     const int* wg_item;        // grouped launches: item index of every workgroup
+    uint32_t* status;          // the call's status word (QAM_STATUS_*), or null
     int B;
     int x_bf16;
-    int KS;                    // waves per (block, chunk), 1..8 (batch 1, single launches)
+    int KS;                    // waves per (block, chunk), 1..8
 };
 
 // Chunking of one matrix: tiles per chunk, chunks, workgroups per chunk and
@@ -130,29 +204,34 @@ struct Plan {
     size_t partial_bytes;
 };
 
-int tpc_align_for(int64_t B);
-int stage_tiles_for(int64_t B);
-size_t lds_bytes_for(int64_t B);
+int tpc_align();
+size_t lds_bytes_staged();
 // Chunk length goal for a launch of `block_tiles` block x tile pairs aiming at
-// `target_waves` wavefronts (<= 0: the library default).
-int chunk_goal(int64_t block_tiles, int64_t target_waves);
+// `target_waves` wavefronts, at most `cap` tiles (cap <= 0: no cap).
+int chunk_goal(int64_t block_tiles, int64_t target_waves, int cap);
+// The staged-limb route's goal under a group's tuning (null: defaults).
+int staged_goal(int64_t block_tiles, const qam_tuning* t);
 // align: chunk lengths are rounded up to a multiple of it (<= 0: a whole
-// number of prefetch rings for batch B).
-Plan make_plan(int64_t N, int64_t K, int64_t B, int goal, int align = 0);
+// number of prefetch rings).
+Plan make_plan(int64_t N, int64_t K, int goal, int align = 0);
 Item make_item(const void* x, const qam_packed* packed, const uint8_t* level_map, float* y, const Plan& p);
 int check_item(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map, float* y,
                const char* who, int out_mode);
-// Matrix-core route of qam_qmatvec (batches up to 32, per-request maps).
+int check_workspace(void* workspace, size_t workspace_bytes, size_t need, const char* who);
+// The status word inside a counter region (a workspace, a group's or a
+// decoder's device memory).
+uint32_t* status_word(void* counter_region);
+// Matrix-core route of qam_qmatvec (batches of 2 to 32, per-request maps).
+bool mfma_route(int64_t B);
 size_t qam_mfma_workspace_bytes(int64_t N, int64_t K, int64_t B);
 int qmatvec_mfma(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
                  int per_request_maps, float* y, void* workspace, size_t workspace_bytes, hipStream_t s);
-size_t mfma_group_bytes(const qam_gemv_item* items, int n_items, int64_t B);
+size_t mfma_group_bytes(const qam_gemv_item* items, int n_items, int64_t B, const qam_tuning* t);
 int mfma_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dtype, int per_request_maps,
-                    void* dev_mem, size_t dev_bytes, qam_group* out, hipStream_t s);
+                    const qam_tuning* t, void* dev_mem, size_t dev_bytes, qam_group* out, hipStream_t s);
 int mfma_group_run(const qam_group* g, hipStream_t s);
-bool mfma_route(int64_t B, int per_request_maps);
-// Enqueues one single-matrix product launch (grid = n_chunks * n_quads
-// workgroups of c.KS wavefronts; c.KS > 1 only for B == 1).
-void launch_single(int64_t B, const Item& it, const Common& c, int64_t grid, hipStream_t s);
+// Enqueues one single-matrix product launch of the staged-limb route (grid =
+// n_chunks * n_quads workgroups of c.KS wavefronts).
+void launch_single(const Item& it, const Common& c, int64_t grid, hipStream_t s);
 
 }  // namespace qam

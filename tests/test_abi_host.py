@@ -93,6 +93,43 @@ def test_level_map_rejects_bad_ladders_and_glass(lib):
     assert lib.qam_build_level_map(FAKE, 8, lens, 1, C.byref(ps), lad, 5, 1, FAKE, None) == -3
     # zero blocks: nothing to do, success without a launch
     assert lib.qam_build_level_map(None, 0, lens, 1, C.byref(p), lad, 5, 1, None, None) == 0
+    # the product's maps take the ladder {0,2,4,6,8} only (a rung index is the
+    # slices the product reads); other valid ladders go to qam_build_rung_map
+    for bits in [(0, 4, 8), (0, 2, 4, 6, 10), (0, 1, 2, 3, 4, 5, 6, 7, 8)]:
+        lad2, keep2 = _ladder(bits)
+        assert lib.qam_build_level_map(FAKE, 8, lens, 1, C.byref(p), lad2, len(bits), 1, FAKE, None) == -4
+        assert lib.qam_build_rung_map(None, 8, lens, 1, C.byref(p), lad2, len(bits), 1, FAKE, None) == -1
+        assert lib.qam_build_rung_map(None, 0, lens, 1, C.byref(p), lad2, len(bits), 1, None, None) == 0
+    lad3, keep3 = _ladder((1, 2, 4))
+    assert lib.qam_build_rung_map(FAKE, 8, lens, 1, C.byref(p), lad3, 3, 0, FAKE, None) == -4
+
+
+def test_zone_radius_params_are_checked(lib):
+    lad, keep = _ladder()
+    lens = (L.QamLens * 1)()
+    lens[0].cx, lens[0].cy, lens[0].r = 0.5, 0.5, 0.2
+    for mode, width in [(2, 1.0), (-1, 1.0), (L.QAM_RADIUS_ZONE, -1.0), (L.QAM_RADIUS_ZONE, float("nan")),
+                        (L.QAM_RADIUS_ZONE, float("inf"))]:
+        p = _params()
+        p.radius_mode, p.width = mode, width
+        assert lib.qam_build_level_map(FAKE, 8, lens, 1, C.byref(p), lad, 5, 1, FAKE, None) == -3
+        assert lib.qam_build_rung_map(FAKE, 8, lens, 1, C.byref(p), lad, 5, 1, FAKE, None) == -3
+
+
+def test_field_width_and_status_reject_before_any_launch(lib):
+    FAKEW = C.c_void_p(0x20000000)
+    d = C.c_double()
+    assert lib.qam_field_width(None, 8, FAKEW, 256, C.byref(d), None) == -1
+    assert lib.qam_field_width(FAKEW, 8, None, 256, C.byref(d), None) == -1
+    assert lib.qam_field_width(FAKEW, 8, FAKEW, 256, None, None) == -1
+    assert lib.qam_field_width(FAKEW, 0, FAKEW, 256, C.byref(d), None) == -2
+    assert lib.qam_field_width(FAKEW, L.QAM_MAX_FIELD_BLOCKS + 1, FAKEW, 256, C.byref(d), None) == -2
+    assert lib.qam_field_width(FAKEW, 8, FAKEW, 255, C.byref(d), None) == -7
+    assert lib.qam_field_width(FAKEW, 8, C.c_void_p(0x20000008), 256, C.byref(d), None) == -5
+    st = C.c_uint32()
+    assert lib.qam_status(None, 1, C.byref(st), None) == -1
+    assert lib.qam_status(FAKEW, 1, None, None) == -1
+    assert lib.qam_status(FAKEW, 2, C.byref(st), None) == -3
 
 
 def test_pack_rejects_bad_shapes_and_alignment(lib):
@@ -136,9 +173,30 @@ def test_workspace_size_is_zero_for_bad_shapes_and_grows_with_batch(lib):
     assert lib.qam_qmatvec_workspace_bytes(8192, 28672, 8) >= lib.qam_qmatvec_workspace_bytes(8192, 28672, 1)
     assert lib.qam_qmatvec_workspace_bytes(8192, 28672, 32) > 0
     assert lib.qam_qmatvec_workspace_bytes(8192, 28672, 33) == 0
-    # pre-pass route: the limb operands of every tile of x for 16 (32) request slots
-    assert lib.qam_qmatvec_workspace_bytes(64, 4096, 16) >= 64 * 3 * 1024
-    assert lib.qam_qmatvec_workspace_bytes(64, 4096, 32) >= 64 * 6 * 1024
+    # every workspace holds the counters and the status word
+    assert lib.qam_qmatvec_workspace_bytes(64, 64, 1) >= L.QAM_WS_COUNTER_BYTES
+    # pre-pass route: the six limb columns of every tile of x for 16 (32) request slots
+    assert lib.qam_qmatvec_workspace_bytes(64, 4096, 16) >= 64 * 6 * 1024
+    assert lib.qam_qmatvec_workspace_bytes(64, 4096, 32) >= 64 * 12 * 1024
+
+
+def test_group_tuning_is_checked(lib):
+    items = (L.QamGemvItem * 1)()
+    items[0].w = _fake_packed(128, 256)
+    for field, bad in [("target_waves", 10), ("target_waves", -1), ("max_chunk_tiles", 2000), ("tail_pct", 101),
+                       ("tail_div", 65), ("ksplit", 3), ("set_max", 4), ("set_max", 17), ("tiles_per_request", 65)]:
+        t = L.QamTuning()
+        setattr(t, field, bad)
+        assert lib.qam_group_bytes_tuned(items, 1, 1, 0, C.byref(t)) == 0, field
+        assert lib.qam_group_bytes_tuned(items, 1, 4, 1, C.byref(t)) == 0, field
+        g = L.QamGroup()
+        assert lib.qam_group_init_tuned(items, 1, 4, 0, 1, C.byref(t), FAKE, 1 << 30, C.byref(g), None) == -3
+    assert lib.qam_group_bytes_tuned(items, 1, 1, 0, None) == lib.qam_group_bytes(items, 1, 1, 0) > 0
+    t = L.QamTuning()
+    t.set_max = 8
+    # sets of 8 for 16 requests: two sets, the same column groups per set
+    assert lib.qam_group_bytes_tuned(items, 1, 16, 1, C.byref(t)) > 0
+    assert lib.qam_group_bytes_tuned(items, 1, 33, 1, C.byref(t)) == 0
 
 
 def test_map_weight_bytes_matches_the_oracle_memory_formula(lib):
@@ -296,12 +354,14 @@ def test_group_calls_reject_bad_descriptors_before_any_launch(lib):
     assert lib.qam_group_launch_times(None, 4, C.cast(out, C.c_void_p), None) == -1
     assert lib.qam_group_launch_times(C.byref(g), 4, C.cast(out, C.c_void_p), None) == -1
     g.table, g.wg_map, g.n_workgroups, g.B = 0x10000000, 0x10001000, 8, 1
+    assert lib.qam_group_launch_times(C.byref(g), 4, C.cast(out, C.c_void_p), None) == -1   # no device memory
+    g.dev_mem = 0x10002000
     g.route = 1               # the timing hook serves staged-limb groups only
     assert lib.qam_group_launch_times(C.byref(g), 4, C.cast(out, C.c_void_p), None) == -3
     g.route = 0
     assert lib.qam_group_launch_times(C.byref(g), 0, C.cast(out, C.c_void_p), None) == -3
     assert lib.qam_group_launch_times(C.byref(g), 4, None, None) == -1
-    g.B = 9                   # beyond the staged-limb route
+    g.B = 2                   # the staged-limb route takes one request
     assert lib.qam_qmatvec_group(C.byref(g), None) == -3
 
 
@@ -324,14 +384,14 @@ def test_group_lens_rejects_before_any_launch(lib):
     g = L.QamGroup()                      # zeroed: no table, no map
     assert run(g) == -1
     g.table, g.wg_map, g.n_workgroups, g.B = 0x10000000, 0x10001000, 8, 1
+    assert run(g) == -1                   # no device memory
+    g.dev_mem = 0x10002000
     assert run(g) == -3                   # no coordinates bound
     g.lens_ready = 1
     g.route = 1                           # pre-pass route: maps are not built in its launch
     assert run(g) == -3
-    g.route, g.per_request_maps = 0, 1
-    assert run(g) == -3
-    g.per_request_maps = 0
-    g.B = 3                               # the fused launch serves B <= 2
+    g.route = 0
+    g.B = 2                               # the fused launch serves one request
     assert run(g) == -3
     g.B = 1
     assert run(g, ladder=None) == -1

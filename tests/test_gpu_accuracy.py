@@ -1,0 +1,227 @@
+"""The accuracy bound on activations with outliers, on every product route.
+
+Bar: |y - y_ref| <= 1e-4 * sum_k |w_nk| |x_k| per output (w = scale * code at
+the block's read depth), for any finite x.  The kernels carry x as two 24-bit
+fixed-point parts relative to the largest |x| of a chunk of columns and add
+the exact residual of every element those parts do not carry to 2^-15
+relative error; these cases put that to work: outlier channels 1e3 to 1e5
+times the rest (their weights read as zero or not), at every depth, on the
+batch-1 route, its fused epilogues, the pre-pass route with shared and
+per-request maps, and its refinement launch; and inputs whose range within a
+chunk exceeds what the two parts carry, so that the exact residuals decide
+the result.  A level map holding a rung that is no depth is flagged in the
+status word and gives NaN outputs for its blocks, nothing else.
+"""
+
+import ctypes as C
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+LADDER = (0, 2, 4, 6, 8)
+
+
+@pytest.fixture(scope="module")
+def qam():
+    import query_adaptive_mixed_amd as Q
+    return Q
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def check(y, W, sc, x, lv, per_request, what):
+    ref = O.qmatvec_ref(W, sc, x, lv, per_request=per_request)
+    tol = O.qmatvec_tolerance(W, sc, x, lv, per_request=per_request)
+    err = np.abs(y.astype(np.float64) - ref)
+    bad = ~(err <= tol)
+    assert not bad.any(), (what, int(bad.sum()), float(np.nanmax(err / np.maximum(tol, 1e-300))))
+
+
+def outlier_problem(seed, N, K, B, factor, channels, zero_weights):
+    """Codes uniform in [-127, 127], scales U(0.001, 0.02), x ~ N(0, 1) with
+    `channels` columns scaled by `factor` (the same columns in every request,
+    as outlier channels of a model are); with zero_weights their codes are 0
+    in every row, so the outliers enter no output and the bound is set by
+    the O(1) entries alone."""
+    rng = np.random.default_rng(seed)
+    W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+    x = rng.standard_normal((B, K)).astype(np.float32)
+    cols = rng.choice(K, channels, replace=False)
+    x[:, cols] *= np.float32(factor)
+    if zero_weights:
+        W[:, cols] = 0
+    return rng, W, sc, x
+
+
+@pytest.mark.parametrize("zero_weights", [True, False])
+@pytest.mark.parametrize("factor", [1e3, 1e4, 1e5])
+@pytest.mark.parametrize("B", [1, 2, 8, 16, 32])
+def test_outlier_channels_every_depth(qam, B, factor, zero_weights):
+    N, K = 512, 4160          # 65 tiles: several chunks and sub-chunks, a ragged last one
+    rng, W, sc, x = outlier_problem(int(factor) % 997 + 10 * B + zero_weights, N, K, B, factor, 5, zero_weights)
+    pm = qam.pack_slices(dev(W), dev(sc))
+    xd = dev(x)
+    for d in range(1, 5):                                    # D2 .. D8, every block alike
+        lv = np.full(N // 64, d, np.uint8)
+        y = host(qam.qmatvec(xd, pm, dev(lv)))
+        check(y, W, sc, x, lv, False, (B, factor, zero_weights, d))
+    lv = rng.integers(0, 5, size=N // 64).astype(np.uint8)   # mixed depths, ZERO blocks too
+    y = host(qam.qmatvec(xd, pm, dev(lv)))
+    check(y, W, sc, x, lv, False, (B, factor, zero_weights, "mixed"))
+    if B > 1:                                                # a map per request
+        lvr = rng.integers(0, 5, size=(B, N // 64)).astype(np.uint8)
+        y = host(qam.qmatvec(xd, pm, dev(lvr)))
+        assert "per-request" in qam.last_variant()
+        check(y, W, sc, x, lvr, True, (B, factor, zero_weights, "per-request"))
+
+
+@pytest.mark.parametrize("B", [1, 2, 16])
+def test_outliers_bf16_and_grouped(qam, B):
+    """bf16 activations with outliers, and the grouped launch of both routes."""
+    N, K = 256, 2048
+    rng, W, sc, x = outlier_problem(77 + B, N, K, B, 3e4, 3, True)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    x32 = xb.float().numpy()
+    pm = qam.pack_slices(dev(W), dev(sc))
+    lv = rng.integers(1, 5, size=N // 64).astype(np.uint8)
+    y = host(qam.qmatvec(xb.cuda(), pm, dev(lv)))
+    check(y, W, sc, x32, lv, False, ("bf16", B))
+    yg = torch.full((B, N), float("nan"), device="cuda")
+    g = qam.GroupedQmatvec([(pm, dev(x), yg, dev(lv))])
+    g.run()
+    check(host(yg), W, sc, x, lv, False, ("group", B))
+
+
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_range_beyond_the_two_parts(qam, B):
+    """x whose entries span far more than the two fixed-point parts carry:
+    a huge entry whose weights are zero next to tiny ones, and entries
+    spread over thirty decades; the tiny entries' exact residuals set the
+    outputs."""
+    N, K = 256, 2112
+    rng = np.random.default_rng(600 + B)
+    W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+    pm = qam.pack_slices(dev(W), dev(sc))
+    lv = np.array([4, 3, 2, 1], np.uint8)
+    # 1e30 with zero weights among entries of order 1e-10
+    W2 = W.copy()
+    W2[:, 100] = 0
+    pm2 = qam.pack_slices(dev(W2), dev(sc))
+    x = (rng.standard_normal((B, K)) * 1e-10).astype(np.float32)
+    x[:, 100] = 1e30
+    y = host(qam.qmatvec(dev(x), pm2, dev(lv)))
+    check(y, W2, sc, x, lv, False, ("1e30 vs 1e-10", B))
+    # magnitudes spread over 1e-20 .. 1e10, signs random
+    xr = (rng.choice([-1.0, 1.0], size=(B, K)) * 10.0 ** rng.uniform(-20, 10, size=(B, K))).astype(np.float32)
+    y = host(qam.qmatvec(dev(xr), pm, dev(lv)))
+    check(y, W, sc, xr, lv, False, ("thirty decades", B))
+    # subnormal entries next to a normal one
+    xs = np.zeros((B, K), np.float32)
+    xs[:, ::3] = np.float32(3e-39)
+    xs[:, 1] = np.float32(1e-3)
+    W3 = W.copy()
+    W3[:, 1] = 0
+    pm3 = qam.pack_slices(dev(W3), dev(sc))
+    y = host(qam.qmatvec(dev(xs), pm3, dev(lv)))
+    check(y, W3, sc, xs, lv, False, ("subnormals", B))
+
+
+def test_outliers_fused_epilogues(qam):
+    """The decode step's fused epilogues (RMS-normalised input, residual add,
+    gated pairs) on an input with outlier channels."""
+    N, K = 512, 1024
+    rng, W, sc, x = outlier_problem(91, N, K, 1, 1e4, 4, True)
+    pm = qam.pack_slices(dev(W), dev(sc))
+    lv = rng.integers(1, 5, size=N // 64).astype(np.uint8)
+    xd, ld = dev(x), dev(lv)
+    eps = 1e-6
+    r = 1.0 / np.sqrt(np.mean(x.astype(np.float64) ** 2) + eps)
+    y = host(qam.qmatvec(xd, pm, ld, rms_norm=True, eps=eps))
+    ref = O.qmatvec_ref(W, sc, x, lv) * r
+    tol = O.qmatvec_tolerance(W, sc, x, lv) * r
+    assert np.all(np.abs(y.astype(np.float64) - ref) <= tol)
+    y0 = rng.standard_normal((1, N)).astype(np.float32)
+    yd = dev(y0)
+    qam.qmatvec(xd, pm, ld, y=yd, out_mode="add")
+    ref = y0.astype(np.float64) + O.qmatvec_ref(W, sc, x, lv)
+    tol = O.qmatvec_tolerance(W, sc, x, lv) + 2.0 ** -24 * np.abs(ref)
+    assert np.all(np.abs(host(yd).astype(np.float64) - ref) <= tol)
+
+
+@pytest.mark.parametrize("B", [2, 8, 32])
+def test_outliers_refinement(qam, B):
+    """The refinement launch (the slices above the glass added to a product
+    at the glass) on outlier activations: within the base read's bound plus
+    the bound of the product at the final maps."""
+    import query_adaptive_mixed_amd._lib as L
+    N, K = 1024, 3072
+    rng, W, sc, x = outlier_problem(120 + B, N, K, B, 1e5, 6, False)
+    pm = qam.pack_slices(dev(W), dev(sc))
+    glass = 1
+    lv = rng.integers(glass, 5, size=(B, N // 64)).astype(np.uint8)
+    uni = np.full(N // 64, glass, np.uint8)
+    xd, lvd = dev(x), dev(lv)
+    y = torch.full((B, N), float("nan"), device="cuda")
+    base = qam.GroupedQmatvec([(pm, xd, y, dev(uni))])      # y = the product at the glass
+    second = qam.GroupedQmatvec([(pm, xd, y, lvd)])         # the same y, refined to the maps
+    assert second.route == "prepass"
+    base.run()
+    L.check(L.lib().qam_qmatvec_group_refine(C.byref(second.desc), glass, None))
+    second_y = y
+    got = host(second_y)
+    ref = O.qmatvec_ref(W, sc, x, lv, per_request=True)
+    tol = O.qmatvec_tolerance(W, sc, x, lv, per_request=True) + O.qmatvec_tolerance(W, sc, x, uni)
+    err = np.abs(got.astype(np.float64) - ref)
+    assert np.all(err <= tol), float((err / tol).max())
+
+
+@pytest.mark.parametrize("B", [1, 3, 16])
+def test_bad_rung_is_flagged_not_read(qam, B):
+    """A rung above 4 is no depth of the product: its block's outputs are NaN,
+    the status word says so (and clears), every other block is computed as
+    usual; the same map without the bad rungs leaves the status clear."""
+    import query_adaptive_mixed_amd._lib as L
+    N, K = 512, 1024
+    rng = np.random.default_rng(700 + B)
+    W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+    x = rng.standard_normal((B, K)).astype(np.float32)
+    pm = qam.pack_slices(dev(W), dev(sc))
+    lv = np.array([4, 5, 2, 0, 9, 1, 255, 3], np.uint8)
+    ws = qam.Workspace("cuda")
+    assert qam.status(ws.get(qam.workspace_bytes(N, K, B))) == 0
+    y = host(qam.qmatvec(dev(x), pm, dev(lv), workspace=ws))
+    assert qam.status(ws.buf) == L.QAM_STATUS_BAD_RUNG
+    assert qam.status(ws.buf) == 0                          # read and cleared
+    bad = np.repeat(lv > 4, 64)
+    assert np.all(np.isnan(y[:, bad]))
+    good = np.where(lv > 4, 0, lv).astype(np.uint8)
+    check(y[:, ~bad], W[~bad], sc[~bad], x, good[lv <= 4], False, ("good blocks", B))
+    y2 = host(qam.qmatvec(dev(x), pm, dev(good), workspace=ws))
+    assert qam.status(ws.buf) == 0
+    check(y2, W, sc, x, good, False, ("clean", B))
+    if B > 1:                                               # per-request maps: only that request's outputs
+        lvr = np.tile(good, (B, 1))
+        lvr[B - 1, 2] = 6
+        y3 = host(qam.qmatvec(dev(x), pm, dev(lvr), workspace=ws))
+        assert qam.status(ws.buf) == L.QAM_STATUS_BAD_RUNG
+        assert np.all(np.isnan(y3[B - 1, 128:192]))
+        ok = np.ones((B, N), bool)
+        ok[B - 1, 128:192] = False
+        ref = O.qmatvec_ref(W, sc, x, np.tile(good, (B, 1)), per_request=True)
+        tol = O.qmatvec_tolerance(W, sc, x, np.tile(good, (B, 1)), per_request=True)
+        assert np.all(np.abs(y3[ok].astype(np.float64) - ref[ok]) <= tol[ok])

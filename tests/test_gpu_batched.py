@@ -207,65 +207,42 @@ def test_grouped_matrix_cores(qam, B, per_request):
 @pytest.mark.parametrize("set_max", [8, 10, 13])
 def test_request_set_sizes(qam, set_max):
     """Requests split into sets of at most `set_max` (fewer limb columns per
-    set): single and grouped launches give the same bits as sets of 16, and
-    the oracle's values; a group keeps the sets it was built with."""
-    from query_adaptive_mixed_amd import _lib as L
-    lib = L.lib()
-    try:
-        L.check(lib.qam_set_mfma_tiles_per_request(4))   # the same column chunks whatever the sets
-        for B, per_request in ((16, True), (20, True), (32, True), (24, False)):
-            rng, W, sc, x = problem(900 + B + set_max, 512, 4096, B)
-            lv = rng.integers(0, 5, size=(B, 8) if per_request else 8).astype(np.uint8)
-            pm = qam.pack_slices(dev(W), dev(sc))
-            L.check(lib.qam_set_mfma_set_max(0))
-            y16 = host(qam.qmatvec(dev(x), pm, dev(lv)))
-            g16 = qam.GroupedQmatvec([(pm, dev(x), torch.empty((B, 512), device="cuda"), dev(lv))])
-            L.check(lib.qam_set_mfma_set_max(set_max))
-            y = host(qam.qmatvec(dev(x), pm, dev(lv)))
-            assert f"sets={-(-B // set_max)}" in qam.last_variant(), qam.last_variant()
-            assert np.array_equal(y.view(np.uint32), y16.view(np.uint32)), (B, set_max)
-            check(y, W, sc, x, lv, per_request, (B, set_max))
-            yg = torch.full((B, 512), float("nan"), device="cuda")
-            g = qam.GroupedQmatvec([(pm, dev(x), yg, dev(lv))])
-            assert g.desc.sets == -(-B // set_max)
-            g.run()
-            assert np.array_equal(host(yg).view(np.uint32), y16.view(np.uint32)), (B, set_max, "group")
-            g16.run()   # built with sets of 16: still runs them, whatever the setting now
-            assert np.array_equal(host(g16._keep[0][2]).view(np.uint32), y16.view(np.uint32)), (B, "g16")
-    finally:
-        L.check(lib.qam_set_mfma_set_max(0))
-        L.check(lib.qam_set_mfma_tiles_per_request(0))
+    set), a group's own launch plan: the same bits as sets of 16 with the
+    same column chunks, and the oracle's values; groups built with other
+    plans keep their own."""
+    for B, per_request in ((16, True), (20, True), (32, True), (24, False)):
+        rng, W, sc, x = problem(900 + B + set_max, 512, 4096, B)
+        lv = rng.integers(0, 5, size=(B, 8) if per_request else 8).astype(np.uint8)
+        pm = qam.pack_slices(dev(W), dev(sc))
+        xd, lvd = dev(x), dev(lv)
+        y16 = torch.full((B, 512), float("nan"), device="cuda")
+        g16 = qam.GroupedQmatvec([(pm, xd, y16, lvd)], tuning={"tiles_per_request": 4})
+        ys = torch.full((B, 512), float("nan"), device="cuda")
+        gs = qam.GroupedQmatvec([(pm, xd, ys, lvd)], tuning={"tiles_per_request": 4, "set_max": set_max})
+        assert g16.desc.sets == -(-B // 16) and gs.desc.sets == -(-B // set_max)
+        gs.run()
+        assert f"sets={-(-B // set_max)}" in qam.last_variant(), qam.last_variant()
+        g16.run()
+        assert f"sets={-(-B // 16)}" in qam.last_variant(), qam.last_variant()
+        a, b = host(ys), host(y16)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (B, set_max)
+        check(a, W, sc, x, lv, per_request, (B, set_max))
+        gs.run()   # still its own plan, whatever ran in between
+        assert np.array_equal(host(ys).view(np.uint32), b.view(np.uint32)), (B, set_max, "again")
 
 
-@pytest.mark.parametrize("B", [3, 8, 16, 32])
-def test_per_slice_and_per_depth_forms_agree(qam, B):
-    """Per-request maps: the per-slice form (each plane times every request's
-    limbs, then each request adds the planes it reads) and the per-depth form
-    (codes at each depth times the limbs of the requests at that depth) sum
-    the same integers, so with the same column chunks (the fixed point of x is
-    per chunk) their outputs agree bit for bit, single and grouped."""
-    from query_adaptive_mixed_amd import _lib as L
-    lib = L.lib()
-    rng, W, sc, x = problem(1200 + B, 768, 6144, B)
-    lv = rng.integers(0, 5, size=(B, 12)).astype(np.uint8)
+@pytest.mark.parametrize("tuning", [{"ksplit": 1}, {"ksplit": 2}, {"target_waves": 2048},
+                                    {"tiles_per_request": 64}])
+def test_group_plans_give_oracle_values(qam, tuning):
+    """Other launch plans (waves per set, launch width, chunk length) on a
+    per-request batch still give the oracle's values."""
+    rng, W, sc, x = problem(1300 + len(str(tuning)), 768, 6144, 16)
+    lv = rng.integers(0, 5, size=(16, 12)).astype(np.uint8)
     lv[:, 1] = 0
-    lv[:, 2] = 1
-    lv[0, 3] = 4
     pm = qam.pack_slices(dev(W), dev(sc))
-    out = {}
-    try:
-        L.check(lib.qam_set_mfma_tiles_per_request(4))   # the same chunks for both forms
-        for form, mx in (("slice", 32), ("depth", 0)):
-            L.check(lib.qam_set_mfma_per_slice_max(mx))
-            out[form] = host(qam.qmatvec(dev(x), pm, dev(lv)))
-            assert f"form={form}" in qam.last_variant(), qam.last_variant()
-            yg = torch.full((B, 768), float("nan"), device="cuda")
-            g = qam.GroupedQmatvec([(pm, dev(x), yg, dev(lv))])
-            g.run()
-            assert f"form={form}" in qam.last_variant(), qam.last_variant()
-            assert np.array_equal(host(yg).view(np.uint32), out[form].view(np.uint32)), (form, "group")
-    finally:
-        L.check(lib.qam_set_mfma_per_slice_max(0))
-        L.check(lib.qam_set_mfma_tiles_per_request(0))
-    assert np.array_equal(out["slice"].view(np.uint32), out["depth"].view(np.uint32))
-    check(out["slice"], W, sc, x, lv, True, B)
+    y = torch.full((16, 768), float("nan"), device="cuda")
+    g = qam.GroupedQmatvec([(pm, dev(x), y, dev(lv))], tuning=tuning)
+    g.run()
+    if "ksplit" in tuning:
+        assert g.desc.ksplit == tuning["ksplit"]
+    check(host(y), W, sc, x, lv, True, tuning)

@@ -61,7 +61,18 @@ def glu_ref(W, sc, x, lv):
     return m, tol
 
 
-@pytest.mark.parametrize("N,K,B", [(256, 1024, 1), (512, 6144, 1), (192, 1536, 2), (128, 28672, 1)])
+def test_epilogues_take_one_request(qam):
+    """The fused epilogues serve the batch-1 decode step: two requests are
+    rejected on the host, nothing launched."""
+    rng = np.random.default_rng(3)
+    W = rng.integers(-127, 128, size=(192, 1536), dtype=np.int64).astype(np.int8)
+    pm = qam.pack_slices(dev(W), dev(np.ones(192, np.float32)))
+    x = dev(rng.standard_normal((2, 1536)).astype(np.float32))
+    with pytest.raises(qam.QamError):
+        qam.qmatvec(x, pm, dev(np.full(3, 2, np.uint8)), rms_norm=True)
+
+
+@pytest.mark.parametrize("N,K,B", [(256, 1024, 1), (512, 6144, 1), (192, 1536, 1), (128, 28672, 1)])
 def test_epilogue_modes_match_oracle(qam, N, K, B):
     rng = np.random.default_rng(N + K + B)
     W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)

@@ -143,7 +143,7 @@ def test_layer_decides_end_to_end(qam, B):
         assert np.all(err <= O.qmatvec_tolerance(W, sc, x, lv, per_request=True)), rule_kw
 
 
-@pytest.mark.parametrize("B,refine", [(1, False), (8, False), (8, True), (3, True), (32, True)])
+@pytest.mark.parametrize("B,refine", [(1, False), (2, True), (8, False), (8, True), (3, True), (32, True)])
 def test_layer_decides_group(qam, B, refine):
     """The grouped form over three matrices of different shapes: every map
     between the oracle's maps at the score bounds, every output within the

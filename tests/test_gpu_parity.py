@@ -87,8 +87,11 @@ def test_identity_batch_probe_reads_the_codes(qam):
 # ------------------------------------------------------------------ level maps
 
 def _gpu_map(qam, coords, centres, radii, f, g, combine, glass, stops=None, ladder=LADDER):
-    return host(qam.build_level_map(dev(coords.astype(np.float64)), centres, radii, f, g, combine, glass,
-                                    ladder_bits=ladder, stops=stops))
+    """The product's map call on the product ladder; the rules on any other
+    ladder through the rung-map call (the same kernel)."""
+    fn = qam.build_level_map if tuple(ladder) == LADDER else qam.build_rung_map
+    return host(fn(dev(coords.astype(np.float64)), centres, radii, f, g, combine, glass, ladder_bits=ladder,
+                   stops=stops))
 
 
 def test_level_map_hand_examples(qam):
@@ -239,27 +242,13 @@ def test_qmatvec_shape_battery(qam, N, K, B):
     lv = rng.integers(0, 5, size=N // 64).astype(np.uint8)
     pm = pack(qam, W, sc)
     y = host(qam.qmatvec(dev(x), pm, dev(lv)))
+    assert ("qmatvec_staged" if B == 1 else "qmatvec_mfma") in qam.last_variant()
     check_y(y, W, sc, x, lv, (N, K, B))
-    from query_adaptive_mixed_amd import _lib as L
-    # the staged-limb route (batch 1 by default; every batch up to 8 once the
-    # pre-pass threshold is raised): matrix cores, then its dot4 form, which
-    # reaches the same integers, so the same bits
-    assert L.lib().qam_set_mfma_min_batch(9) == 0
-    try:
-        ys = host(qam.qmatvec(dev(x), pm, dev(lv)))
-        assert "staged_mfma" in qam.last_variant()
-        assert L.lib().qam_set_staged_mfma(0) == 0
-        try:
-            yd = host(qam.qmatvec(dev(x), pm, dev(lv)))
-            assert "staged_dot4" in qam.last_variant()
-        finally:
-            assert L.lib().qam_set_staged_mfma(1) == 0
-    finally:
-        assert L.lib().qam_set_mfma_min_batch(3) == 0
-    check_y(ys, W, sc, x, lv, ("staged", N, K, B))
-    assert np.array_equal(yd.view(np.uint32), ys.view(np.uint32)), (N, K, B)
-    if B == 1:
-        assert np.array_equal(ys.view(np.uint32), y.view(np.uint32)), (N, K)
+    # the same map given once per request takes the per-request form, which
+    # sums the same integers: the same bits
+    lvr = np.ascontiguousarray(np.broadcast_to(lv, (B, lv.size)))
+    yr = host(qam.qmatvec(dev(x), pm, dev(lvr)))
+    assert np.array_equal(yr.view(np.uint32), y.view(np.uint32)), (N, K, B)
 
 
 def test_qmatvec_exact_integer_cases(qam):
@@ -293,26 +282,6 @@ def test_qmatvec_large_integer_x_rounds_once(qam):
         codes = np.concatenate([O.truncate(W[64 * b:64 * b + 64], LADDER[lv[b]]) for b in range(N // 64)])
         want = (x.astype(np.int64) @ codes.T).astype(np.float32)
         assert np.array_equal(y, want), (N, K, B)
-
-
-def test_qmatvec_error_within_fixed_point_bound(qam):
-    """Adversarial x (one huge element per row of x whose weight is zero, the
-    rest O(1)) still obeys the kernel's stated fixed-point bound
-    2^-22 max|x| sum|w| + 2^-24 |y|, the bound that holds for any x."""
-    rng = np.random.default_rng(23)
-    N, K = 128, 1024
-    W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
-    W[:, 7] = 0
-    sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
-    x = rng.standard_normal((2, K)).astype(np.float32)
-    x[:, 7] = 3.0e4
-    lv = np.array([4, 4], np.uint8)
-    pm = pack(qam, W, sc)
-    y = host(qam.qmatvec(dev(x), pm, dev(lv)))
-    ref = O.qmatvec_ref(W, sc, x, lv)
-    aw = np.abs(W.astype(np.float64)) * sc[:, None].astype(np.float64)
-    bound = 2.0 ** -22 * np.abs(x).max(axis=1)[:, None] * aw.sum(axis=1)[None, :] + 2.0 ** -24 * np.abs(ref)
-    assert np.all(np.abs(y - ref) <= bound)
 
 
 def test_qmatvec_edge_cases(qam):
@@ -472,7 +441,7 @@ def _lens_group(qam, coords, mats, bf16=False):
     return qam.GroupedQmatvec(items), items, lv, cd
 
 
-@pytest.mark.parametrize("B,bf16", [(1, False), (2, False), (1, True)])
+@pytest.mark.parametrize("B,bf16", [(1, False), (1, True)])
 def test_group_lens_builds_the_maps_in_the_launch(qam, B, bf16):
     """The launch that builds the level maps writes every item's map
     bit-identical to the oracle's lens rules over the whole field, and its
