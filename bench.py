@@ -489,6 +489,7 @@ def run_decode(args, torch, Q, WL):
     t0 = time.time()
     dec = build_decoder(fld, c["n_layers"], c["hidden"], c["q_dim"], c["kv_dim"], c["ffn"], eps=1e-6,
                         target_waves=args.decode_waves, waves_per_block=args.decode_ksplit,
+                        max_chunk_tiles=args.decode_max_chunk,
                         progress=lambda l: log(f"  packed layer {l + 1}/28 ({time.time() - t0:.1f} s)") if l % 7 == 6 else None)
     xs = torch.from_numpy(WL.decode_inputs(0, T, c["hidden"])).cuda()
     esc = Q.escalation_schedule(WL.escalation_scores(0, T), 0.16)
@@ -758,6 +759,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-waves", type=int, default=0, help="decoder launch width goal (0 = library default)")
     ap.add_argument("--decode-ksplit", type=int, default=0, help="waves per block in the decoder (0 = default)")
+    ap.add_argument("--decode-max-chunk", type=int, default=0,
+                    help="decoder: longest column chunk in tiles (0 = default)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

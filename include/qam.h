@@ -647,6 +647,8 @@ typedef struct qam_decoder_desc {
     int                      target_waves;  /* launch width goal per matrix (workgroups); 0 = 16 */
     int                      waves_per_block; /* 1, 2, 4 or 8 wavefronts split each block's chunk
                                                of columns inside a workgroup; 0 = 4 */
+    int                      max_chunk_tiles; /* longest column chunk of a product, in 64-column
+                                               tiles; 0 = the library's default */
 } qam_decoder_desc;
 
 typedef struct qam_decoder qam_decoder;     /* opaque host object */

@@ -346,7 +346,8 @@ def qmatvec_tolerance(W, scales, x, level, ladder_bits=LADDER_BITS, per_request=
 
 
 def fit_focus_area(coords, centres, radii, g: float, combine: str, n_rungs: int, glass: int,
-                   block_weights, budget_bytes: int, iters: int = 40, ladder_bits=LADDER_BITS, stops=None):
+                   block_weights, budget_bytes: int, iters: int = 40, ladder_bits=LADDER_BITS, stops=None,
+                   radius: str = "lens", width=None):
     """The byte-budget regulator: the largest focus area f in [0, 1] whose
     lens map reads at most ``budget_bytes`` of weights.
 
@@ -356,12 +357,14 @@ def fit_focus_area(coords, centres, radii, g: float, combine: str, n_rungs: int,
     decrease as f grows (a wider lens lifts no block less), so f is found by
     bisection on [0, 1], ``iters`` halvings, keeping the end that fits.  If
     f = 1 fits, f = 1; if not even f = 0 fits, f = 0 (and the returned
-    bytes exceed the budget).  Exact integers decide every step.
+    bytes exceed the budget).  Exact integers decide every step.  The same
+    holds for zones, R = f D ([FoQLens] "FoQZones, the mechanism": the
+    budget sets the zone radius), with ``radius='zone'`` and ``width`` = D.
 
     Returns (f, bytes at f, level map at f).
     """
     def at(f):
-        lv = level_map(coords, centres, radii, f, g, combine, n_rungs, glass, stops)
+        lv = level_map(coords, centres, radii, f, g, combine, n_rungs, glass, stops, radius, width)
         return weight_bytes(lv, block_weights, ladder_bits), lv
 
     b1, lv1 = at(1.0)

@@ -178,7 +178,8 @@ def status(mem: torch.Tensor, clear: bool = True) -> int:
 
 def fit_focus_area(coords: torch.Tensor, block_weights: torch.Tensor, centres, radii, g: float, budget_bytes: int,
                    combine: str = "sum", glass: int = 1, iters: int = 40, stops=None,
-                   ladder_bits: Sequence[int] = LADDER_BITS, out: Optional[torch.Tensor] = None):
+                   ladder_bits: Sequence[int] = LADDER_BITS, out: Optional[torch.Tensor] = None,
+                   radius: str = "lens", width: float = 0.0):
     """The byte-budget regulator: the largest focus area f whose lens map
     reads at most ``budget_bytes`` of weights (bisection, ``iters`` halvings).
     ``block_weights`` is a device int64 [n_blocks] tensor of w_b.  Returns
@@ -188,7 +189,7 @@ def fit_focus_area(coords: torch.Tensor, block_weights: torch.Tensor, centres, r
     n_blocks = coords.shape[0]
     if block_weights.numel() != n_blocks:
         raise ValueError("one weight per block")
-    r = LensRules(centres, radii, 0.0, g, combine, glass, stops, ladder_bits)
+    r = LensRules(centres, radii, 0.0, g, combine, glass, stops, ladder_bits, radius, width)
     if out is None:
         out = torch.empty(n_blocks, dtype=torch.uint8, device=coords.device)
     ws = torch.zeros(256, dtype=torch.uint8, device=coords.device)
@@ -611,7 +612,8 @@ class Decoder:
     ``step(rung)`` (eager) or ``capture(rung)`` once and ``replay(rung)``."""
 
     def __init__(self, layers, lm_head: PackedMatrix, hidden: int, q_dim: int, kv_dim: int, ffn: int,
-                 eps: float = 1e-6, target_waves: int = 0, waves_per_block: int = 0, device="cuda"):
+                 eps: float = 1e-6, target_waves: int = 0, waves_per_block: int = 0, max_chunk_tiles: int = 0,
+                 device="cuda"):
         n = len(layers)
         self._layers = (L.QamDecoderLayer * n)()
         self._keep = [lm_head]
@@ -626,6 +628,7 @@ class Decoder:
         d.eps = float(eps)
         d.target_waves = int(target_waves)
         d.waves_per_block = int(waves_per_block)
+        d.max_chunk_tiles = int(max_chunk_tiles)
         self._desc = d
         nbytes = int(L.lib().qam_decoder_bytes(C.byref(d)))
         if nbytes == 0:

@@ -26,6 +26,7 @@ struct qam_decoder {
     char* ws = nullptr;            // counters, then fp64 partials
     int64_t target_waves = 16;
     int ksplit = 4;
+    int max_chunk = 0;             // longest column chunk in tiles (0: no cap)
     hipGraph_t graph[5] = {};
     hipGraphExec_t exec[5] = {};
 };
@@ -33,6 +34,10 @@ struct qam_decoder {
 namespace {
 
 constexpr size_t kAlign = 256;
+// Longest column chunk of a step's products, in tiles: a product with few
+// row blocks and many columns (the down projection) is cut into several
+// chunks so that its waves stay short.
+constexpr int kDefaultMaxChunk = 16;
 size_t up256(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 // The five launches of one layer (or the lm_head) in chain order.
@@ -56,10 +61,10 @@ std::vector<Op> chain(const qam_decoder& dec) {
     return ops;
 }
 
-Plan plan_of(const qam_packed& w, int64_t target_waves) {
+Plan plan_of(const qam_packed& w, int64_t target_waves, int max_chunk) {
     // chunks of whole D8 rings (2 tiles) so that small matrices spread over
     // many wavefronts: a decode step is a chain of short, latency-bound launches
-    return make_plan(w.N, w.K, chunk_goal(w.n_blocks * (w.K / kTileCols), target_waves, 0), 2);
+    return make_plan(w.N, w.K, chunk_goal(w.n_blocks * (w.K / kTileCols), target_waves, max_chunk), 2);
 }
 
 bool same_shape(const qam_packed& w, int64_t N, int64_t K) {
@@ -84,11 +89,14 @@ int layout(const qam_decoder_desc* d, Layout& lo) {
     if (d->waves_per_block != 0 && d->waves_per_block != 1 && d->waves_per_block != 2 && d->waves_per_block != 4 &&
         d->waves_per_block != 8)
         QAM_FAIL(QAM_ERR_ARG, "decoder: waves_per_block must be 0, 1, 2, 4 or 8");
+    if (d->max_chunk_tiles < 0 || d->max_chunk_tiles > QAM_MAX_K / 64)
+        QAM_FAIL(QAM_ERR_ARG, "decoder: max_chunk_tiles %d outside [0, %d]", d->max_chunk_tiles, QAM_MAX_K / 64);
     const int64_t tw = d->target_waves ? d->target_waves : 16;
+    const int mc = d->max_chunk_tiles ? d->max_chunk_tiles : kDefaultMaxChunk;
     size_t partial = 0;
     auto need = [&](const qam_packed& w) {
         lo.max_blocks = std::max<int64_t>(lo.max_blocks, w.n_blocks);
-        partial = std::max(partial, plan_of(w, tw).partial_bytes);
+        partial = std::max(partial, plan_of(w, tw, mc).partial_bytes);
     };
     for (int l = 0; l < d->n_layers; ++l) {
         const qam_decoder_layer& L = d->layers[l];
@@ -122,7 +130,7 @@ int enqueue(qam_decoder* dec, int rung, int first, int count, hipStream_t s) {
     c.status = status_word(dec->ws);
     for (int i = first; i < first + count; ++i) {
         const Op& op = ops[(size_t)i];
-        const Plan p = plan_of(*op.w, dec->target_waves);
+        const Plan p = plan_of(*op.w, dec->target_waves, dec->max_chunk);
         c.KS = dec->ksplit;   // waves per (block, chunk)
         Item it = make_item(op.x, op.w, dec->maps[rung], op.y, p);
         it.fixed_level = rung;   // the map is uniform: the kernel takes the rung, not the map bytes
@@ -164,6 +172,7 @@ extern "C" int qam_decoder_create(const qam_decoder_desc* d, void* dev_mem, size
     dec->d.layers = dec->layers.data();
     dec->target_waves = d->target_waves ? d->target_waves : 16;
     dec->ksplit = d->waves_per_block ? d->waves_per_block : 4;
+    dec->max_chunk = d->max_chunk_tiles ? d->max_chunk_tiles : kDefaultMaxChunk;
     char* base = static_cast<char*>(dev_mem);
     dec->ws = base + lo.ws;
     dec->h = reinterpret_cast<float*>(base + lo.h);

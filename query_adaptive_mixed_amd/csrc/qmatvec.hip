@@ -18,9 +18,13 @@
 // per four codes) and multiplied into the limbs exactly, in int32, with
 // v_mfma_i32_16x16x64_i8 on the matrix cores: the rebuilt words are the A
 // operand as they stand, and B-operand column l holds limb l (hi 0..2, lo
-// 0..2).  The six column sums are combined into a per-row fp64 sum; the few
-// elements the two parts do not carry to 2^-15 relative error are added
-// exactly at the end of the chunk.  The row sums are either written as the
+// 0..2).  The six column sums are combined into a per-row fp64 sum.  A
+// sub-chunk holding an element that the two parts do not carry to 2^-15
+// relative error (its range within the sub-chunk exceeds 2^31, e.g. the
+// exponentially small tail of a gated activation) is instead staged as fp32
+// and multiplied on the vector ALUs in fp32 (per-element exponents; at most
+// 256 sequential terms per lane and row, so within 2^-16 of sum|w||x|).  The
+// row sums are either written as the
 // output (one chunk) or stored as partials; the last wavefront of a block to
 // finish sums the partials in chunk order and writes y = fl32(scale * sum).
 // No floating-point atomics: results are bit-reproducible.
@@ -58,7 +62,9 @@ struct Ring {
 
 // B operand in LDS: per tile, one 16-byte slot per (limb column c < 6, lane
 // group k) at 4 c + k, then 4 zero slots that columns 6..15 read.  After the
-// sub-chunk's slots, the [6][64] int32 table of its column sums.
+// sub-chunk's slots, the [6][64] int32 table of its column sums.  A sub-chunk
+// staged as fp32 keeps x of tile t, columns 16 k .. 16 k + 15, in slots
+// t * 28 + 4 k .. + 3 (clear of the zero slots).
 constexpr int kSlotsPerTile = 4 * (kLimbCols + 1);
 constexpr int kZeroSlot = 4 * kLimbCols;
 constexpr int kRegionInt4 = kStageTiles * kSlotsPerTile + kLimbCols * 16;   // int4 per wave
@@ -85,6 +91,46 @@ __device__ __forceinline__ void tile_mfma(const u32x4* buf, const int4* __restri
         const v4i A = v4i{(int)assemble<NS, 0>(w[j]), (int)assemble<NS, 1>(w[j]), (int)assemble<NS, 2>(w[j]),
                           (int)assemble<NS, 3>(w[j])};
         acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bm, acc[j], 0, 0, 0);
+    }
+}
+
+// One tile in fp32 on the vector ALUs: lane L accumulates, for rows
+// 16j + (L & 15), its 16 columns 16(L >> 4) + 4u + i: code (byte i of the
+// rebuilt word u) times x, in fp32.  xt: this lane group's four slots of x.
+__device__ __forceinline__ float code_byte(uint32_t P, int i) {
+    return (float)((int)(P << (24 - 8 * i)) >> 24);
+}
+
+template <int NS>
+__device__ __forceinline__ void tile_float(const u32x4* buf, const int4* __restrict__ xt, float (&facc)[4]) {
+    uint32_t w[4][NS];
+#pragma unroll
+    for (int p = 0; p < NS; ++p) {
+        w[0][p] = buf[p].x;
+        w[1][p] = buf[p].y;
+        w[2][p] = buf[p].z;
+        w[3][p] = buf[p].w;
+    }
+    // one group of four columns at a time: four x values live, not sixteen
+#pragma unroll 1
+    for (int u = 0; u < 4; ++u) {
+        const int4 v = xt[u];
+        const float x0 = __int_as_float(v.x), x1 = __int_as_float(v.y), x2 = __int_as_float(v.z),
+                    x3 = __int_as_float(v.w);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t acc = 0;
+#pragma unroll
+            for (int p = 0; p < NS; ++p) {
+                const uint32_t m = 0x03030303u << (2 * (3 - p));
+                acc |= w[j][p] & (u == 0 ? m : ((m >> (2 * u)) | (m << (32 - 2 * u))));
+            }
+            const uint32_t P = u == 0 ? acc : ((acc << (2 * u)) | (acc >> (32 - 2 * u)));
+            facc[j] = __builtin_fmaf(code_byte(P, 0), x0, facc[j]);
+            facc[j] = __builtin_fmaf(code_byte(P, 1), x1, facc[j]);
+            facc[j] = __builtin_fmaf(code_byte(P, 2), x2, facc[j]);
+            facc[j] = __builtin_fmaf(code_byte(P, 3), x3, facc[j]);
+        }
     }
 }
 
@@ -139,8 +185,10 @@ __device__ __forceinline__ int exp_of(float m) {
 
 // Turn this wave's sub-chunk of x into limb words in LDS.  xraw[i] holds the
 // x values of group L + 64 i (four columns).  The limb words of limb column
-// c and the tile's columns 16k + 4u .. +3 go to word u of slot 4 c + k.
-// Returns whether some element of the sub-chunk is uncovered.
+// c and the tile's columns 16k + 4u .. +3 go to word u of slot 4 c + k.  If
+// some element of the sub-chunk is uncovered, x is staged as fp32 instead
+// (slot t * 28 + (g & 15) for group g of tile t) and the return value is
+// true: the sub-chunk runs in fp32.
 template <bool XBF16>
 __device__ __forceinline__ bool stage_limbs(const u32x4 (&xraw)[kStageGroups], int ngroups, int L,
                                             int4* __restrict__ lds, int& exp, bool& bad, bool want_ssq,
@@ -183,56 +231,20 @@ __device__ __forceinline__ bool stage_limbs(const u32x4 (&xraw)[kStageGroups], i
         wl[64] = lw.y;
         wl[80] = lw.z;
     }
-    lds_order();   // the writes come before the tile loop's reads
-    return __builtin_amdgcn_readfirstlane((int)(__ballot(unc) != 0)) != 0;
-}
-
-// The exact corrections of a chunk's uncovered elements for the row of lane
-// L: the wave's tiles are walked again sub-chunk by sub-chunk, each element's
-// split recomputed exactly as when it was staged, and for every uncovered one
-// code(row, k) * r2 is added in fp64.  Only chunks holding such an element
-// come here.
-template <bool XBF16>
-__device__ double uncovered_correction(const uint8_t* planes, int64_t pb, int64_t K, const void* x, int b,
-                                       int tile0, int ks, int KS, int ntile, int ns, int L) {
-    double corr = 0.0;
-    for (int sub = 0; sub * kStageTiles < ntile; ++sub) {
-        const int ngroups = min(kStageTiles, ntile - sub * kStageTiles) * 16;
-        float4 xv[kStageGroups];
-        int64_t col[kStageGroups];
+    const bool fp32 = __builtin_amdgcn_readfirstlane((int)(__ballot(unc) != 0)) != 0;
+    if (fp32) {
+        lds_order();   // the limb writes above come first
 #pragma unroll
         for (int i = 0; i < kStageGroups; ++i) {
-            const int g = min(L + 64 * i, ngroups - 1);
-            col[i] = (int64_t)(tile0 + ks + KS * (sub * kStageTiles + (g >> 4))) * kTileCols + 4 * (g & 15);
-            xv[i] = x4_value<XBF16>(load_x4_raw<XBF16>(x, col[i]));
+            const int g = L + 64 * i;
+            if (g >= ngroups) continue;
+            const float4 v = xv[i];
+            lds[(g >> 4) * kSlotsPerTile + (g & 15)] =
+                int4{__float_as_int(v.x), __float_as_int(v.y), __float_as_int(v.z), __float_as_int(v.w)};
         }
-        bool bad;
-        const int e = exp_of(sub_max(xv, bad));
-        const XSplit sp = xsplit_of(e);
-        double part = 0.0;
-#pragma unroll
-        for (int i = 0; i < kStageGroups; ++i) {
-            const bool live = L + 64 * i < ngroups;
-            const float vv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint32_t wh, wl;
-                float r2;
-                bool u;
-                split_elem(vv[q], sp, wh, wl, r2, u);
-                uint64_t mask = __ballot(live && u);
-                while (mask) {
-                    const int src = __builtin_ctzll(mask);
-                    mask &= mask - 1;
-                    const int64_t k = (int64_t)__shfl(col[i], src) + q;
-                    const float rv = __shfl(r2, src);
-                    part += (double)code_at(planes, pb, K, b, L, k, 0, ns) * (double)rv;
-                }
-            }
-        }
-        corr += sp.pre == 1.0f ? part : ldexp(part, -kPrescale);
     }
-    return corr;
+    lds_order();   // the writes come before the tile loop's reads
+    return fp32;
 }
 
 // ------------------------------------------------------------------ epilogue
@@ -317,7 +329,8 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     int* tab = reinterpret_cast<int*>(lds + S * kSlotsPerTile);   // [6][64 rows] sums of a sub-chunk
 
     double mine = 0.0;
-    bool any_bad = false, any_unc = false;
+    bool any_bad = false;
+    bool fmode = false;   // this sub-chunk runs in fp32
     double ssq = 0.0;
     // an unsplit RMS-normalised product sees all of x while staging it
     const bool want_ssq = EPI && a.rms && a.n_chunks == 1;
@@ -337,27 +350,48 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     int exp = 0;
     bool bad = false;
     auto stage = [&](int sub) {
-        any_unc |= stage_limbs<XBF16>(xraw, min(S, ntile - sub * S) * 16, L, lds, exp, bad, want_ssq, ssq);
+        fmode = stage_limbs<XBF16>(xraw, min(S, ntile - sub * S) * 16, L, lds, exp, bad, want_ssq, ssq);
     };
     v4i macc[4];
+    float facc[4];
     auto clear_acc = [&]() {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) macc[j] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < 4; ++j) {
+            macc[j] = v4i{0, 0, 0, 0};
+            facc[j] = 0.0f;
+        }
     };
     // The sub-chunk's exact per-row integers, scaled by its exponent into the
     // row's fp64 sum: the six limb columns of every row meet in LDS, then row
     // L's value forms on lane L.
+    // In fp32: the four lane groups' partial sums of rows 16j + (L & 15) meet
+    // by lane shuffles (in fp64) and lane L keeps row L's.
     auto flush = [&]() {
-        const int gc = L & 15;
-        if (gc < kLimbCols) {
+        if (fmode) {
+            double d[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(tab + gc * 64 + 16 * j + 4 * kg) = macc[j];
+            for (int j = 0; j < 4; ++j) {
+                d[j] = (double)facc[j];
+                d[j] += __shfl_xor(d[j], 16);
+                d[j] += __shfl_xor(d[j], 32);
+            }
+            mine += kg == 0 ? d[0] : (kg == 1 ? d[1] : (kg == 2 ? d[2] : d[3]));
+        } else {
+            const int gc = L & 15;
+            if (gc < kLimbCols) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) *reinterpret_cast<v4i*>(tab + gc * 64 + 16 * j + 4 * kg) = macc[j];
+            }
+            lds_order();
+            mine += limb_value(tab[L], tab[64 + L], tab[128 + L], tab[192 + L], tab[256 + L], tab[320 + L], exp);
         }
-        lds_order();
-        mine += limb_value(tab[L], tab[64 + L], tab[128 + L], tab[192 + L], tab[256 + L], tab[320 + L], exp);
         any_bad = any_bad || bad;
     };
-#define QAM_TILE(BUF, TT) tile_mfma<NS>(BUF, lds + (TT) * kSlotsPerTile, bslot, macc)
+#define QAM_TILE(BUF, TT)                                                                  \
+    do {                                                                                   \
+        if (fmode) tile_float<NS>(BUF, lds + (TT) * kSlotsPerTile + 4 * kg, facc);         \
+        else tile_mfma<NS>(BUF, lds + (TT) * kSlotsPerTile, bslot, macc);                  \
+    } while (0)
 
     // One prefetch ring runs through the whole chunk: two halves of H tiles,
     // each reloaded PF tiles ahead right after it is used.  A round that ends
@@ -413,7 +447,6 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
         for (int u = 0; u < H; ++u)
             if (t + H + u < ntile) QAM_TILE(Bh[u], tl + H + u);
         flush();
-        if (any_unc) mine += uncovered_correction<XBF16>(a.planes, pb, a.K, a.x, b, tile0, ks, KS, ntile, NS, L);
     }
 #undef QAM_TILE
 

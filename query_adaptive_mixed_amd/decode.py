@@ -41,7 +41,8 @@ def _pack(codes: np.ndarray, scales: np.ndarray, device) -> PackedMatrix:
 
 
 def build_decoder(field, n_layers: int, hidden: int, q_dim: int, kv_dim: int, ffn: int, eps: float = 1e-6,
-                  target_waves: int = 0, waves_per_block: int = 0, device="cuda", progress=None) -> Decoder:
+                  target_waves: int = 0, waves_per_block: int = 0, max_chunk_tiles: int = 0, device="cuda",
+                  progress=None) -> Decoder:
     """Pack a field made by ``workloads.decoder_field`` (per layer q, k, v, o,
     gate, up, down, then the head) and create the decoder over it."""
     layers = []
@@ -58,7 +59,7 @@ def build_decoder(field, n_layers: int, hidden: int, q_dim: int, kv_dim: int, ff
             progress(l)
     lm = _pack(field.codes(7 * n_layers), field.scales(7 * n_layers), device)
     return Decoder(layers, lm, hidden, q_dim, kv_dim, ffn, eps=eps, target_waves=target_waves,
-                   waves_per_block=waves_per_block, device=device)
+                   waves_per_block=waves_per_block, max_chunk_tiles=max_chunk_tiles, device=device)
 
 
 def decoder_matrices(dec: Decoder) -> Sequence:

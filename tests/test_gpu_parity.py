@@ -568,3 +568,67 @@ def test_qmatvec_extreme_magnitudes(qam, scale, B):
     pm = pack(qam, W, sc)
     y = host(qam.qmatvec(dev(x), pm, dev(lv)))
     check_y(y, W, sc, x, lv, (scale, B))
+
+
+# ------------------------------------------------------------------ zone radius
+
+def test_field_width_bit_exact(qam):
+    """The field width on the device equals the oracle's, bit for bit."""
+    rng = np.random.default_rng(800)
+    for n in (1, 2, 7, 300, 4608):
+        c = rng.uniform(-1, 2, size=(n, 2))
+        assert qam.field_width(dev(c)) == O.field_width(c), n
+    fld = WL.e2b_field(0)
+    assert qam.field_width(dev(fld.coords)) == O.field_width(fld.coords)
+
+
+def test_zone_radius_maps_bit_exact(qam):
+    """Level maps with the zone radius R = f D: the hand examples, and random
+    and workload fields at every kind of f, bit-identical to the oracle."""
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "zone_hand_examples.json")))
+    c = np.array(g["coords"])
+    for f, want in g["maps"].items():
+        got = host(qam.build_level_map(dev(c), [g["centre"]], [0.123], float(f), g["g"], "sum", g["glass"],
+                                       radius="zone", width=g["width"]))
+        assert got.tolist() == want, f
+    rng = np.random.default_rng(801)
+    for trial in range(12):
+        n = int(rng.integers(1, 4000))
+        coords = rng.uniform(0, 1, size=(n, 2)) if trial % 2 else WL.clustered_coords(rng, n)
+        D = qam.field_width(dev(coords))
+        nl = int(rng.integers(0, 9))
+        cen = coords[rng.choice(n, min(nl, n), replace=False)] if nl else np.zeros((0, 2))
+        rad = rng.uniform(0.0, 0.4, size=cen.shape[0])
+        f = float(rng.choice([0.0, 1.0, rng.uniform(0, 1)]))
+        gg = float(rng.choice([1.0, 0.75, rng.uniform(0, 1)]))
+        glass = int(rng.integers(0, 5))
+        combine = "sum" if trial % 3 else "max"
+        want = O.level_map(coords, cen, rad, f, gg, combine, 5, glass, radius="zone", width=D)
+        got = host(qam.build_level_map(dev(coords), cen, rad, f, gg, combine, glass, radius="zone", width=D))
+        assert np.array_equal(got, want), trial
+    # the E2B-shaped field, one map rule set per f; the launch that builds the
+    # map inside the product takes the zone rule too
+    fld = WL.e2b_field(0)
+    lp = WL.e2b_lenses(fld)
+    D = qam.field_width(dev(fld.coords))
+    for f in (0.0, 0.05, 0.2, 1.0):
+        want = O.level_map(fld.coords, lp.centres, lp.radii, f, lp.g, "sum", 5, 1, radius="zone", width=D)
+        got = host(qam.build_level_map(dev(fld.coords), lp.centres, lp.radii, f, lp.g, "sum", 1,
+                                       radius="zone", width=D))
+        assert np.array_equal(got, want), f
+    rng2 = np.random.default_rng(802)
+    shapes = [(256, 512), (192, 1024), (128, 256)]
+    coords, mats = _lens_field(rng2, shapes, 1)
+    grp, items, lv, cd = _lens_group(qam, coords, mats)
+    D = qam.field_width(cd)
+    cen = coords[[1, 5]]
+    rules = qam.LensRules(cen, [0.3, 0.1], 0.4, 1.0, "sum", 1, radius="zone", width=D)
+    grp.run_lens(rules)
+    want = O.level_map(coords, cen, [0.3, 0.1], 0.4, 1.0, "sum", 5, 1, radius="zone", width=D)
+    assert np.array_equal(host(lv), want)
+    o = 0
+    for (W, sc, x), it in zip(mats, items):
+        N = W.shape[0]
+        check_y(host(it[2]), W, sc, x, want[o:o + N // 64], ("zone", W.shape))
+        o += N // 64

@@ -19,10 +19,12 @@ def qam():
     return Q
 
 
-def both(qam, coords, w, cen, rad, g, combine, glass, budget, iters, stops=None):
-    want = O.fit_focus_area(coords, cen, rad, g, combine, 5, glass, w, budget, iters=iters, stops=stops)
+def both(qam, coords, w, cen, rad, g, combine, glass, budget, iters, stops=None, radius="lens", width=0.0):
+    want = O.fit_focus_area(coords, cen, rad, g, combine, 5, glass, w, budget, iters=iters, stops=stops,
+                            radius=radius, width=width)
     f, b, lv = qam.fit_focus_area(torch.from_numpy(coords).cuda(), torch.from_numpy(np.asarray(w, np.int64)).cuda(),
-                                  cen, rad, g, budget, combine=combine, glass=glass, iters=iters, stops=stops)
+                                  cen, rad, g, budget, combine=combine, glass=glass, iters=iters, stops=stops,
+                                  radius=radius, width=width)
     torch.cuda.synchronize()
     assert f == want[0], (f, want[0])
     assert b == want[1]
@@ -62,3 +64,18 @@ def test_regulator_small_fields_and_ends(qam):
         hi = O.weight_bytes(O.level_map(coords, cen, rad, 1.0, g, combine, 5, glass, stops), w)
         for budget in (max(0, lo - 1), lo, (lo + hi) // 2, hi, hi + 64):
             both(qam, coords, w, cen, rad, g, combine, glass, budget, int(rng.integers(0, 45)), stops)
+
+
+def test_regulator_zone_radius(qam):
+    """The regulator on zones (R = f D, D the field width from the device):
+    the same f, bytes and map as the oracle's bisection."""
+    fld = WL.e2b_field(0)
+    lp = WL.e2b_lenses(fld)
+    w = fld.block_weights().astype(np.int64)
+    D = qam.field_width(torch.from_numpy(fld.coords).cuda())
+    assert D == O.field_width(fld.coords)
+    four_bits = int(np.sum(w)) * 4 // 8
+    for budget in (four_bits, four_bits // 2 + four_bits // 4):
+        f, b = both(qam, fld.coords, w, lp.centres, lp.radii, lp.g, "sum", lp.glass, budget, 40,
+                    radius="zone", width=D)
+        assert b <= budget

@@ -699,3 +699,25 @@ def test_zone_monotone_in_f_and_ignores_lens_sizes():
         if prev is not None:
             assert np.all(a >= prev)
         prev = a
+
+
+def test_regulator_zone_radius_edge():
+    """The regulator on zones: its f fits and a fine scan finds nothing
+    above it that fits (bytes never decrease as f grows)."""
+    rng = np.random.default_rng(24)
+    c = rng.uniform(0, 1, size=(80, 2))
+    D = O.field_width(c)
+    cen = c[rng.choice(80, 2, replace=False)]
+    w = np.full(80, 64 * 256, dtype=np.int64)
+    full = O.weight_bytes(np.full(80, 4), w)
+    floor = O.weight_bytes(np.full(80, 1), w)            # every block at the glass (D2)
+    assert O.fit_focus_area(c, cen, [0.1, 0.2], 1.0, "sum", 5, 1, w, floor - 1, radius="zone", width=D)[0] == 0.0
+    for budget in (floor + full // 16, full // 2, (3 * full) // 4):
+        f, b, lv = O.fit_focus_area(c, cen, [0.1, 0.2], 1.0, "sum", 5, 1, w, budget, iters=30,
+                                    radius="zone", width=D)
+        assert b <= budget and b == O.weight_bytes(lv, w)
+        for f2 in np.linspace(f + 2.0 ** -29, 1.0, 60):
+            lv2 = O.level_map(c, cen, [0.1, 0.2], f2, 1.0, "sum", 5, 1, radius="zone", width=D)
+            assert O.weight_bytes(lv2, w) >= b
+        above = O.level_map(c, cen, [0.1, 0.2], f + 2.0 ** -30, 1.0, "sum", 5, 1, radius="zone", width=D)
+        assert O.weight_bytes(above, w) > budget or f == 1.0
