@@ -22,7 +22,8 @@
  *   - Pointers marked (device) are HIP device pointers owned by the caller;
  *     pointers marked (host) are host memory owned by the caller and only
  *     read during the call.  The library never allocates or frees device
- *     memory.
+ *     memory; the one static device array it holds is the scratch of
+ *     qam_qmatvec_noalloc.
  *   - Work is enqueued on the caller's stream `s` (0 = the null stream) and
  *     is asynchronous: outputs are ready once the stream has reached that
  *     point (calls whose description says they synchronise `s` return with
@@ -34,7 +35,8 @@
  *     the ABI, and no call falls back silently to another kernel variant:
  *     qam_last_variant() names the variant the last successful call ran.
  *   - Calls are reentrant: the library keeps no state but the thread-local
- *     error and variant strings.  Launch plans are fixed per call (defaults)
+ *     error and variant strings (and, for qam_qmatvec_noalloc alone, one
+ *     scratch array per GPU).  Launch plans are fixed per call (defaults)
  *     or per group at qam_group_init_tuned, never process-wide.
  *   - Device-side errors (a level map holding a rung that is not a depth of
  *     the product) do not fault: the kernel raises a bit in the status word
@@ -80,6 +82,9 @@ extern "C" {
 #define QAM_STATUS_BAD_RUNG 1u        /* a level map held a rung above 4: the blocks
                                          concerned were not read and their outputs
                                          are NaN */
+
+/* Size of the static scratch array of qam_qmatvec_noalloc (per GPU). */
+#define QAM_SCRATCH_BYTES (32 * 1024 * 1024)
 
 #define QAM_X_F32  0
 #define QAM_X_BF16 1
@@ -439,6 +444,29 @@ int qam_qmatvec(const void* x, int x_dtype, int64_t B, const qam_packed* packed,
  *   documented.  Host-synchronous; a debugging aid, not needed for results.
  */
 int qam_status(const void* workspace, int clear, uint32_t* status_out, hipStream_t s);
+
+/*
+ * qam_qmatvec_noalloc -- qam_qmatvec for callers that cannot allocate device
+ *   memory (code under HIP graph capture, tight serving loops, harnesses that
+ *   forbid hipMalloc).  Same arguments and the same result, bit for bit, as
+ *   qam_qmatvec, with no workspace argument: the workspace is a static
+ *   256-byte aligned device array of QAM_SCRATCH_BYTES bytes built into the
+ *   library, one copy per GPU, held until the process ends.  The call never
+ *   allocates or frees memory.
+ *
+ *   A shape whose qam_qmatvec_workspace_bytes(N, K, B) exceeds
+ *   QAM_SCRATCH_BYTES is rejected with QAM_ERR_WORKSPACE before anything is
+ *   enqueued (use qam_qmatvec with a workspace of that size).  The first
+ *   call on a device also enqueues, on `s`, a clear of the array's counter
+ *   region.  Every call on one GPU shares that GPU's array, which keeps the
+ *   last call's contents: calls that overlap on one GPU (different streams
+ *   without ordering, or different threads) race and give wrong results.
+ *   The array's status word is not exposed; a rung above 4 still yields NaN
+ *   outputs.  Errors as qam_qmatvec, plus QAM_ERR_HIP when the array's
+ *   device address cannot be looked up.
+ */
+int qam_qmatvec_noalloc(const void* x, int x_dtype, int64_t B, const qam_packed* packed,
+                        const uint8_t* level_map, int per_request_maps, float* y, hipStream_t s);
 
 /* ---------------------------------------------------------------- fused epilogues */
 /*

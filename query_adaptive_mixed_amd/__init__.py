@@ -31,6 +31,7 @@ from .api import (  # noqa: F401
     pack_slices,
     packed_bytes,
     qmatvec,
+    qmatvec_noalloc,
     status,
     unpack_codes,
     workspace_bytes,

@@ -29,6 +29,7 @@ QAM_MAX_FIELD_BLOCKS = 262144
 QAM_WS_STATUS_OFFSET = QAM_MAX_BLOCKS * 4
 QAM_WS_COUNTER_BYTES = QAM_MAX_BLOCKS * 4 + 256
 QAM_STATUS_BAD_RUNG = 1
+QAM_SCRATCH_BYTES = 32 * 1024 * 1024
 
 
 class QamPacked(C.Structure):
@@ -122,6 +123,7 @@ SIGNATURES = [
     ("qam_map_weight_bytes", _I, [_P, _I64, _I64, _P, _I, C.POINTER(_D), C.POINTER(_I64)]),
     ("qam_qmatvec_workspace_bytes", C.c_size_t, [_I64, _I64, _I64]),
     ("qam_qmatvec", _I, [_P, _I, _I64, C.POINTER(QamPacked), _P, _I, _P, _P, _SZ, _P]),
+    ("qam_qmatvec_noalloc", _I, [_P, _I, _I64, C.POINTER(QamPacked), _P, _I, _P, _P]),
     ("qam_qmatvec_ep", _I, [_P, _I, _I64, C.POINTER(QamPacked), _P, C.POINTER(QamEpilogue), _P, _P, _SZ, _P]),
     ("qam_decoder_bytes", C.c_size_t, [C.POINTER(QamDecoderDesc)]),
     ("qam_decoder_create", _I, [C.POINTER(QamDecoderDesc), _P, _SZ, C.POINTER(_P), _P]),

@@ -353,6 +353,38 @@ def qmatvec(x: torch.Tensor, packed: PackedMatrix, level_map: torch.Tensor, y: O
     return y
 
 
+def qmatvec_noalloc(x: torch.Tensor, packed: PackedMatrix, level_map: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+    """``qmatvec`` (plain store, no epilogue) through the library's static
+    per-GPU scratch: the call allocates no device memory, so ``y`` must be
+    given.  Shapes whose workspace exceeds QAM_SCRATCH_BYTES are rejected;
+    calls that overlap on one GPU share the scratch and race."""
+    _require_cuda(level_map, "level_map", torch.uint8)
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    _require_cuda(x, "x")
+    if x.dtype == torch.float32:
+        xdt = L.QAM_X_F32
+    elif x.dtype == torch.bfloat16:
+        xdt = L.QAM_X_BF16
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    B, K = x.shape
+    if K != packed.K:
+        raise ValueError(f"x has {K} columns, matrix has {packed.K}")
+    per_request = level_map.dim() == 2
+    if per_request:
+        if tuple(level_map.shape) != (B, packed.n_blocks):
+            raise ValueError("a per-request level_map must be [B, n_blocks]")
+    elif level_map.numel() != packed.n_blocks:
+        raise ValueError("level_map must have one entry per block")
+    _require_cuda(y, "y", torch.float32)
+    if y.numel() != B * packed.N:
+        raise ValueError(f"y must hold {B} x {packed.N} values")
+    L.check(L.lib().qam_qmatvec_noalloc(_ptr(x), xdt, B, C.byref(packed.desc), _ptr(level_map), int(per_request),
+                                        _ptr(y), _stream_handle()))
+    return y
+
+
 class GroupedQmatvec:
     """Many matrices with their own x, y and level map, one launch per call
     (two on the pre-pass route).

@@ -167,6 +167,28 @@ def test_qmatvec_rejects_bad_arguments(lib):
     assert lib.qam_qmatvec(X, 0, 1, C.byref(bad), M, 0, Y, None, 0, None) == -2
 
 
+def test_qmatvec_noalloc_rejects_before_touching_the_device(lib):
+    """Argument errors and shapes beyond the static scratch are returned by
+    host checks alone (no device here)."""
+    d = L.QamPacked()
+    assert lib.qam_describe_packed(C.c_void_p(0x100000), 128, 256, C.byref(d)) == 0
+    X, Y, M = C.c_void_p(0x200000), C.c_void_p(0x300000), C.c_void_p(0x400000)
+    assert lib.qam_qmatvec_noalloc(X, 0, 0, C.byref(d), M, 0, Y, None) == -3        # B = 0
+    assert lib.qam_qmatvec_noalloc(X, 0, 33, C.byref(d), M, 0, Y, None) == -3       # B > 32
+    assert lib.qam_qmatvec_noalloc(X, 0, 1, C.byref(d), M, 2, Y, None) == -3        # per_request_maps flag
+    assert lib.qam_qmatvec_noalloc(X, 7, 1, C.byref(d), M, 0, Y, None) == -3        # dtype
+    assert lib.qam_qmatvec_noalloc(None, 0, 1, C.byref(d), M, 0, Y, None) == -1
+    assert lib.qam_qmatvec_noalloc(X, 0, 1, None, M, 0, Y, None) == -1
+    assert lib.qam_qmatvec_noalloc(C.c_void_p(0x200004), 0, 1, C.byref(d), M, 0, Y, None) == -5
+    # 2048 blocks x 65536 columns at 32 requests needs ~92 MiB of workspace
+    big = L.QamPacked()
+    assert lib.qam_describe_packed(C.c_void_p(0x10000000), 131072, 65536, C.byref(big)) == 0
+    assert lib.qam_qmatvec_workspace_bytes(131072, 65536, 32) > L.QAM_SCRATCH_BYTES
+    X2 = C.c_void_p(0x8000000000)
+    assert lib.qam_qmatvec_noalloc(X2, 0, 32, C.byref(big), M, 0, Y, None) == -7
+    assert b"scratch" in lib.qam_last_error()
+
+
 def test_workspace_size_is_zero_for_bad_shapes_and_grows_with_batch(lib):
     assert lib.qam_qmatvec_workspace_bytes(100, 64, 1) == 0
     assert lib.qam_qmatvec_workspace_bytes(64, 64, 0) == 0
