@@ -64,6 +64,8 @@ extern "C" {
 #define QAM_ERR_ALIGN     -5   /* a pointer is not aligned as required            */
 #define QAM_ERR_HIP       -6   /* a HIP runtime call failed                       */
 #define QAM_ERR_WORKSPACE -7   /* workspace missing or too small                  */
+#define QAM_ERR_IO        -8   /* a stack file cannot be opened, read or written,
+                                  or is not a well-formed stack file            */
 
 #define QAM_ROWS_PER_BLOCK 64
 #define QAM_MAX_K          65536      /* keeps every exact integer sum in range */
@@ -152,6 +154,100 @@ int qam_describe_packed(void* packed_buf, int64_t N, int64_t K, qam_packed* desc
  */
 int qam_unpack_codes(const qam_packed* packed, const uint8_t* level_map, int8_t* codes_out,
                      hipStream_t s);
+
+/* ---------------------------------------------------------------- stored stack */
+/*
+ * One stored stack on disk ([FoQLens] "Progress": one stored copy, a base
+ * with refinements over it, read at 2, 4, 6 or 8 bits without repacking).
+ * The file holds the packed planes of many matrices, plane-major, so that a
+ * read at depth d is the first d/2 plane sections of the file plus the
+ * scales: one contiguous prefix and one tail, no repacking on load.
+ *
+ * Layout (all integers little-endian; every offset a multiple of 256):
+ *   [0, 128)                   qam_stack_header
+ *   [128, 128 + 64 n)          n qam_stack_entry, one per matrix, in order
+ *   zero bytes up to data_offset = round_up(128 + 64 n, 4096)
+ *   plane sections p = 0 .. 3, each plane_section_bytes long, starting at
+ *                              data_offset + p * plane_section_bytes; inside
+ *                              section p, matrix m's plane p (N K / 4 bytes,
+ *                              the packed layout above) at entry.plane_offset
+ *                              = sum of N K / 4 over the matrices before m
+ *   scales section at scales_offset = data_offset + 4 plane_section_bytes:
+ *                              matrix m's N fp32 scales at scales_offset +
+ *                              entry.scales_offset, = sum of 4 N over the
+ *                              matrices before m
+ *   file_bytes = scales_offset + scales_bytes.
+ */
+#define QAM_STACK_VERSION       1
+#define QAM_STACK_NAME_BYTES    32
+#define QAM_STACK_MAX_MATRICES  65536
+#define QAM_STACK_ALIGN         4096
+
+typedef struct qam_stack_header {        /* 128 bytes */
+    char     magic[8];                   /* "QAMSTACK" (no terminator)            */
+    uint32_t version;                    /* QAM_STACK_VERSION                     */
+    uint32_t n_matrices;                 /* 1 .. QAM_STACK_MAX_MATRICES           */
+    uint32_t n_rungs;                    /* 5                                     */
+    uint8_t  ladder_bits[16];            /* {0, 2, 4, 6, 8}, then zeros           */
+    uint32_t rows_per_block;             /* 64                                    */
+    uint64_t data_offset;                /* start of plane section 0              */
+    uint64_t plane_section_bytes;        /* sum of N K / 4                        */
+    uint64_t scales_offset;              /* start of the scales section           */
+    uint64_t scales_bytes;               /* sum of 4 N                            */
+    uint64_t file_bytes;                 /* total length                          */
+    uint8_t  reserved[48];               /* zeros                                 */
+} qam_stack_header;
+
+typedef struct qam_stack_entry {         /* 64 bytes */
+    int64_t  N, K;                       /* shape, as in qam_packed               */
+    uint64_t plane_offset;               /* offset inside every plane section     */
+    uint64_t scales_offset;              /* offset inside the scales section      */
+    char     name[QAM_STACK_NAME_BYTES]; /* NUL-padded; may be all NUL            */
+} qam_stack_entry;
+
+/*
+ * qam_stack_write -- write packed matrices to a stack file (created or
+ *   truncated).  Synchronises `s` first (the planes must be complete), then
+ *   copies the planes and scales out of device memory through pinned host
+ *   staging buffers that the call allocates and frees.
+ *   path       (host) file name.
+ *   mats       (host) n_matrices descriptors from qam_pack_slices.
+ *   names      (host) NULL, or n_matrices C strings (NULL entries allowed) of
+ *              at most QAM_STACK_NAME_BYTES - 1 characters.
+ *   Returns QAM_ERR_IO when the file cannot be written (a partial file may be
+ *   left behind).
+ */
+int qam_stack_write(const char* path, const qam_packed* mats, const char* const* names, int n_matrices,
+                    hipStream_t s);
+
+/*
+ * qam_stack_info -- read and check a stack file's header and table.
+ *   hdr_out     (host) the header.
+ *   entries_out (host, may be NULL) room for max_entries entries; the first
+ *               min(n_matrices, max_entries) are written.
+ *   Every field is checked against the layout above (magic, version, ladder,
+ *   offsets, shapes, and the file's length); QAM_ERR_IO names the first
+ *   mismatch.  Host only: no device call.
+ */
+int qam_stack_info(const char* path, qam_stack_header* hdr_out, qam_stack_entry* entries_out, int max_entries);
+
+/*
+ * qam_stack_read -- load matrices [first, first + count) of a stack file at
+ *   depth 2 * slices bits into caller device buffers.
+ *   slices      1 .. 4: planes 0 .. slices-1 are read; planes slices .. 3
+ *               of each destination are zero-filled, so any deeper read of
+ *               the loaded matrix returns the codes at depth 2 * slices.
+ *   dst         (host) count descriptors (qam_describe_packed on caller
+ *               buffers of qam_packed_bytes(N, K)), shapes equal to the
+ *               file's entries.
+ *   bytes_read  (host, may be NULL) bytes read from the file:
+ *               slices * sum(N K / 4) + sum(4 N) over the matrices loaded.
+ *   The file is read with large sequential reads into pinned host staging
+ *   buffers (allocated and freed by the call), double-buffered against the
+ *   host-to-device copies on `s`; returns after `s` has been synchronised.
+ */
+int qam_stack_read(const char* path, int slices, int first, int count, const qam_packed* dst, hipStream_t s,
+                   uint64_t* bytes_read);
 
 /* ---------------------------------------------------------------- level maps */
 typedef struct qam_lens {

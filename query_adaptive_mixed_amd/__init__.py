@@ -34,6 +34,9 @@ from .api import (  # noqa: F401
     qmatvec_noalloc,
     status,
     unpack_codes,
+    stack_write,
+    stack_info,
+    stack_read,
     workspace_bytes,
 )
 from ._lib import QamError  # noqa: F401

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libqam.so")
 
 QAM_OK = 0
 ERRORS = {-1: "QAM_ERR_NULL", -2: "QAM_ERR_SHAPE", -3: "QAM_ERR_ARG", -4: "QAM_ERR_LADDER",
-          -5: "QAM_ERR_ALIGN", -6: "QAM_ERR_HIP", -7: "QAM_ERR_WORKSPACE"}
+          -5: "QAM_ERR_ALIGN", -6: "QAM_ERR_HIP", -7: "QAM_ERR_WORKSPACE", -8: "QAM_ERR_IO"}
 QAM_MAX_LENSES = 64
 QAM_MAX_STOPS = 15
 QAM_MAX_BATCH = 1
@@ -35,6 +35,23 @@ QAM_SCRATCH_BYTES = 32 * 1024 * 1024
 class QamPacked(C.Structure):
     _fields_ = [("N", C.c_int64), ("K", C.c_int64), ("n_blocks", C.c_int64),
                 ("planes", C.c_void_p), ("scales", C.c_void_p)]
+
+
+QAM_STACK_VERSION = 1
+QAM_STACK_NAME_BYTES = 32
+QAM_STACK_MAX_MATRICES = 65536
+
+
+class QamStackHeader(C.Structure):
+    _fields_ = [("magic", C.c_char * 8), ("version", C.c_uint32), ("n_matrices", C.c_uint32),
+                ("n_rungs", C.c_uint32), ("ladder_bits", C.c_uint8 * 16), ("rows_per_block", C.c_uint32),
+                ("data_offset", C.c_uint64), ("plane_section_bytes", C.c_uint64), ("scales_offset", C.c_uint64),
+                ("scales_bytes", C.c_uint64), ("file_bytes", C.c_uint64), ("reserved", C.c_uint8 * 48)]
+
+
+class QamStackEntry(C.Structure):
+    _fields_ = [("N", C.c_int64), ("K", C.c_int64), ("plane_offset", C.c_uint64), ("scales_offset", C.c_uint64),
+                ("name", C.c_char * QAM_STACK_NAME_BYTES)]
 
 
 class QamLens(C.Structure):
@@ -114,6 +131,9 @@ SIGNATURES = [
     ("qam_pack_slices", _I, [_P, _P, _I64, _I64, _P, _SZ, C.POINTER(QamPacked), _P]),
     ("qam_describe_packed", _I, [_P, _I64, _I64, C.POINTER(QamPacked)]),
     ("qam_unpack_codes", _I, [C.POINTER(QamPacked), _P, _P, _P]),
+    ("qam_stack_write", _I, [C.c_char_p, C.POINTER(QamPacked), C.POINTER(C.c_char_p), _I, _P]),
+    ("qam_stack_info", _I, [C.c_char_p, C.POINTER(QamStackHeader), C.POINTER(QamStackEntry), _I]),
+    ("qam_stack_read", _I, [C.c_char_p, _I, _I, _I, C.POINTER(QamPacked), _P, C.POINTER(C.c_uint64)]),
     ("qam_build_level_map", _I, [_P, _I64, C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I, _I, _P, _P]),
     ("qam_build_rung_map", _I, [_P, _I64, C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I, _I, _P, _P]),
     ("qam_field_width", _I, [_P, _I64, _P, _SZ, C.POINTER(_D), _P]),

@@ -9,6 +9,7 @@ helpers ``unpack_codes``, ``map_weight_bytes`` and ``workspace_bytes``.
 from __future__ import annotations
 
 import ctypes as C
+import os
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
@@ -81,6 +82,60 @@ def unpack_codes(packed: PackedMatrix, level_map: torch.Tensor, out: Optional[to
         out = torch.empty((packed.N, packed.K), dtype=torch.int8, device=packed.buf.device)
     L.check(L.lib().qam_unpack_codes(C.byref(packed.desc), _ptr(level_map), _ptr(out), _stream_handle()))
     return out
+
+
+def _fspath(path) -> bytes:
+    return os.fsencode(os.fspath(path))
+
+
+def stack_write(path, mats: Sequence[PackedMatrix], names: Optional[Sequence[Optional[str]]] = None) -> None:
+    """Write packed matrices to a stack file (plane-major: a read at depth d
+    is the first d/2 plane sections plus the scales)."""
+    n = len(mats)
+    descs = (L.QamPacked * n)(*[m.desc for m in mats])
+    cnames = None
+    if names is not None:
+        if len(names) != n:
+            raise ValueError("one name per matrix")
+        cnames = (C.c_char_p * n)(*[None if v is None else v.encode() for v in names])
+    L.check(L.lib().qam_stack_write(_fspath(path), descs, cnames, n, _stream_handle()))
+
+
+def stack_info(path):
+    """(header, entries) of a stack file, as ctypes structures."""
+    hdr = L.QamStackHeader()
+    L.check(L.lib().qam_stack_info(_fspath(path), C.byref(hdr), None, 0))
+    n = int(hdr.n_matrices)
+    ents = (L.QamStackEntry * n)()
+    L.check(L.lib().qam_stack_info(_fspath(path), C.byref(hdr), ents, n))
+    return hdr, list(ents)
+
+
+def stack_read(path, bits: int, first: int = 0, count: Optional[int] = None, device=None,
+               out: Optional[Sequence[PackedMatrix]] = None):
+    """Load matrices [first, first + count) at ``bits`` (2, 4, 6 or 8) into
+    device buffers (new ones, or ``out``); planes below that depth are zero.
+    Returns (list of PackedMatrix, bytes read from the file)."""
+    if bits not in (2, 4, 6, 8):
+        raise ValueError("bits must be 2, 4, 6 or 8")
+    hdr, ents = stack_info(path)
+    if count is None:
+        count = len(ents) - first
+    if out is None:
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        out = []
+        for e in ents[first:first + count]:
+            buf = torch.empty(packed_bytes(e.N, e.K), dtype=torch.uint8, device=dev)
+            d = L.QamPacked()
+            L.check(L.lib().qam_describe_packed(_ptr(buf), e.N, e.K, C.byref(d)))
+            out.append(PackedMatrix(buf, d))
+    if len(out) != count:
+        raise ValueError(f"out holds {len(out)} matrices, {count} requested")
+    descs = (L.QamPacked * count)(*[m.desc for m in out])
+    nread = C.c_uint64(0)
+    L.check(L.lib().qam_stack_read(_fspath(path), bits // 2, first, count, descs, _stream_handle(),
+                                    C.byref(nread)))
+    return list(out), int(nread.value)
 
 
 class LensRules:
