@@ -568,6 +568,7 @@ def run_decode(args, torch, Q, WL):
     pywall = time.perf_counter() - t0
     if py_fired != fired:
         raise RuntimeError(f"gated decode: the library loop escalated {fired} steps, the Python loop {py_fired}")
+    spec = run_speculation(args, torch, Q, WL, dec, wb) if args.spec_tokens > 0 else None
     return {
         "workload": "qwen_decode",
         "description": "Qwen3-0.6B-shaped decode: 28 x {q|k|v 4096x1024, o 1024x2048, gate|up 6144x1024, "
@@ -597,8 +598,58 @@ def run_decode(args, torch, Q, WL):
                       "fired; wall clock over the call. python_loop_tokens_per_s: the same steps driven from "
                       "Python",
         },
+        "speculation": spec,
         "_fld": fld, "_esc": esc, "_wb": wb,
     }
+
+
+def run_speculation(args, torch, Q, WL, dec, wb):
+    """Greedy draft-and-verify on the same decoder ([PoD] abstract: verified
+    speculation): k D4 draft steps, then one batched D8 verify pass over the
+    k + 1 positions; the token-feedback stand-in feeds back a seeded
+    embedding row of each emitted token.  Bytes per token against one D8
+    step, beside the gated schedule's ratio."""
+    c = QWEN
+    E = torch.from_numpy(WL.embedding_table(0, c["vocab"], c["hidden"])).cuda()
+    ks = [int(v) for v in args.spec_k.split(",") if v]
+    ver = Q.Verifier(dec, max(ks) + 1)
+    n = args.spec_tokens
+    out = {"tokens": n, "first_token": 0, "draft_rung": 2, "verify_rung": 4,
+           "feedback": "embedding row of the emitted token, N(0,1) fp32 [151936, 1024] seeded table",
+           "timing": "qam_decoder_speculate, one call; per round the D4 draft graphs, a device argmax and "
+                     "embedding copy per draft, one batched D8 verify pass (graph replay), a device argmax and "
+                     "accept kernel, "
+                     "and one read of the round's tokens; wall clock over the call", "by_k": {}}
+    for k in ks:
+        ver.capture(4, k + 1)
+        Q.speculate(dec, ver, E, 0, 4, k)                      # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks, st = Q.speculate(dec, ver, E, 0, n, k)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        # one verify pass alone, timed with events on the launch stream
+        ev = []
+        for i in range(6):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            ver.replay(4, k + 1)
+            b.record()
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        vms = float(np.median([a.elapsed_time(b) for a, b in ev[1:]]))
+        nbytes = st["draft_steps"] * wb[2] + st["rounds"] * wb[4]
+        out["by_k"][str(k)] = {
+            "rounds": st["rounds"], "accepted_of_drafted": f"{st['accepted']}/{st['drafted']}",
+            "acceptance": round(st["accepted"] / max(1, st["drafted"]), 4),
+            "tokens_per_round": round(st["emitted"] / max(1, st["rounds"]), 4),
+            "weight_bytes_per_token": int(nbytes // n),
+            "byte_ratio_vs_all_8bit": round(nbytes / (n * wb[4]), 6),
+            "tokens_per_s": round(n / wall, 2), "ms_per_token": round(wall * 1e3 / n, 5),
+            "verify_pass_ms": round(vms, 5),
+        }
+    del ver, E
+    return out
 
 
 def decode_cpu_baseline(res, args):
@@ -761,6 +812,8 @@ def main():
     ap.add_argument("--decode-ksplit", type=int, default=0, help="waves per block in the decoder (0 = default)")
     ap.add_argument("--decode-max-chunk", type=int, default=0,
                     help="decoder: longest column chunk in tiles (0 = default)")
+    ap.add_argument("--spec-tokens", type=int, default=64, help="draft-and-verify leg: tokens (0 = skip)")
+    ap.add_argument("--spec-k", default="1,2,3", help="draft-and-verify leg: drafts per round, comma-separated")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

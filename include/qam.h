@@ -891,6 +891,120 @@ int qam_decoder_decode_gated(qam_decoder* dec, const float* inputs, int64_t T, i
                              size_t gate_workspace_bytes, qam_uncertainty* gate_out,
                              qam_uncertainty* host_result, uint8_t* escalated_out, hipStream_t s);
 
+/* ---------------------------------------------------------------- draft and verify */
+/*
+ * Verified speculation ([PoD] abstract: speculation verified at full depth
+ * reaches the full-depth output at a similar weight-byte cost).  Reading
+ * taken: greedy decoding; the draft model is the stored stack read at the
+ * draft rung (D4), the target the same stack read at the verify rung (D8).
+ * A round drafts k tokens one step at a time at the draft rung, then runs
+ * ONE batched step at the verify rung over the k + 1 inputs (the current
+ * token and the k drafts), so the verify pass reads every weight block once
+ * for all k + 1 positions.  With t_i the target's token after input i and
+ * d_i the i-th draft, the round keeps d_1 .. d_j for the longest prefix with
+ * t_{i-1} = d_i, then emits t_j: every emitted token is the target's greedy
+ * token, whatever the draft.
+ *
+ * The decode step here has no attention: a step's output depends on its
+ * input alone.  The token-feedback stand-in feeds back the embedding row of
+ * the emitted token (a caller table E [vocab][hidden] fp32) as the next
+ * step's input.
+ *
+ * A verifier holds the batched step's buffers over a decoder's weights.
+ * Its step is the decoder's chain for B requests at once:
+ *   h_r = x_r;  x'_r = rms(h_r)
+ *   per layer: qkv = W_qkv x';  x' = qkv[:, :q_dim];  h += W_o x';
+ *              x' = rms(h);  u = W_gate_up x';  m = silu(u_gate) * u_up;
+ *              h += W_down m;  x' = rms(h)
+ *   logits = W_lm x'
+ * each product a qam_qmatvec call at B (the pre-pass route for B >= 2,
+ * every request's result independent of the others and of its slot), each
+ * glue step one small row kernel: rms in fp64 over the row (x' = fl32(h /
+ * sqrt(mean h^2 + eps))), h + y rounded once to fp32, silu(g) u in fp64
+ * rounded once.
+ */
+typedef struct qam_verifier qam_verifier;   /* opaque host object */
+
+/* Device bytes of a verifier for batches up to max_batch (1 .. 16). */
+size_t qam_verifier_bytes(const qam_decoder_desc* d, int max_batch);
+
+/* qam_verifier_create -- lay out the batched buffers in dev_mem (caller-owned,
+ *   256-byte aligned, kept alive with the verifier), zero the workspace
+ *   counters on `s` and synchronise.  The decoder must outlive it. */
+int qam_verifier_create(qam_decoder* dec, int max_batch, void* dev_mem, size_t dev_bytes, qam_verifier** out,
+                        hipStream_t s);
+
+/* (device) the verifier's buffers, row-major with B rows in use:
+ *   QAM_VER_X [max_batch][hidden] inputs (read by op 0), QAM_VER_H [..][hidden],
+ *   QAM_VER_QKV [..][q_dim + 2 kv_dim], QAM_VER_M [..][ffn],
+ *   QAM_VER_XN [..][max(hidden, q_dim, ffn)] the next product's input,
+ *   QAM_VER_LOGITS [..][vocab]; NULL for an unknown id. */
+#define QAM_VER_X      0
+#define QAM_VER_H      1
+#define QAM_VER_QKV    2
+#define QAM_VER_M      3
+#define QAM_VER_XN     4
+#define QAM_VER_LOGITS 5
+float* qam_verifier_buffer(qam_verifier* v, int which);
+
+/* qam_verifier_run -- enqueue ops first .. first+count-1 of the batched
+ *   chain for B requests (1 <= B <= max_batch) at `rung`: op 0 loads the
+ *   inputs (h = x, x' = rms h), then per layer the four products with their
+ *   glue (qkv, o, gate_up, down), then the head: 4 n_layers + 2 ops.
+ *   qam_verifier_step runs them all. */
+int qam_verifier_run(qam_verifier* v, int rung, int B, int first, int count, hipStream_t s);
+int qam_verifier_step(qam_verifier* v, int rung, int B, hipStream_t s);
+
+/* qam_verifier_capture -- capture qam_verifier_step(v, rung, B) on `s` (not
+ *   the null stream) as a HIP graph kept by the verifier, one per (rung, B);
+ *   qam_verifier_replay launches it, and qam_decoder_speculate replays the
+ *   graph of (verify_rung, k + 1) when there is one. */
+int qam_verifier_capture(qam_verifier* v, int rung, int B, hipStream_t s);
+int qam_verifier_replay(qam_verifier* v, int rung, int B, hipStream_t s);
+
+/* Frees the host object and its graphs (not dev_mem). */
+void qam_verifier_destroy(qam_verifier* v);
+
+/*
+ * qam_argmax_rows -- idx[r] = the first index of the largest of
+ *   v[r*ld .. r*ld + n-1] (fp32 order; -0 < +0 as bit patterns; rows must
+ *   hold no NaN), for r < rows.
+ *   v        (device) fp32, ld >= n >= 1, 1 <= rows <= 65535, n < 2^31.
+ *   idx_out  (device) int32 [rows].
+ *   workspace (device) 8 * rows bytes, 8-byte aligned, zero before the
+ *            first use; left zero.  Two launches.
+ */
+int qam_argmax_rows(const float* v, int64_t rows, int64_t n, int64_t ld, int32_t* idx_out, void* workspace,
+                    hipStream_t s);
+
+typedef struct qam_spec_stats {
+    int64_t rounds;         /* verify passes                                  */
+    int64_t draft_steps;    /* steps at the draft rung (k per round)          */
+    int64_t drafted;        /* tokens drafted (= draft_steps)                 */
+    int64_t accepted;       /* drafts kept                                    */
+    int64_t emitted;        /* tokens emitted (>= n_tokens; the last round's  */
+                            /* surplus is dropped from tokens_out)            */
+} qam_spec_stats;
+
+/*
+ * qam_decoder_speculate -- n_tokens greedy tokens after first_token by
+ *   draft-and-verify (above), k drafts per round (1 .. max_batch - 1).
+ *   embed       (device) fp32 [vocab][hidden], the feedback table.
+ *   draft_rung, verify_rung  rungs 0..4 of {0,2,4,6,8}; the draft steps
+ *               replay the decoder's graph of draft_rung when captured.
+ *   tokens_out  (host) int32 [n_tokens].
+ *   stats       (host, may be NULL).
+ *   Per round: k draft steps, each one graph replay, a device argmax and an
+ *   embedding-row copy chosen on the device; one batched verify step (a
+ *   graph replay when captured); a
+ *   device argmax of its k + 1 rows; one kernel that accepts and feeds the
+ *   next input; then a read of the round's tokens (one synchronisation of
+ *   `s`).  The decoder's own buffers hold the last draft step.
+ */
+int qam_decoder_speculate(qam_decoder* dec, qam_verifier* v, const float* embed, int32_t first_token,
+                          int n_tokens, int k, int draft_rung, int verify_rung, int32_t* tokens_out,
+                          qam_spec_stats* stats, hipStream_t s);
+
 /* ---------------------------------------------------------------- diagnostics */
 const char* qam_last_error(void);     /* thread-local, "" if none           */
 const char* qam_last_variant(void);   /* kernel variant of the last call     */

@@ -548,6 +548,61 @@ def escalation_byte_ratio(mask, low_bits: int = 4, high_bits: int = 8) -> float:
     return float((T * low_bits + int(mask.sum()) * high_bits) / (T * high_bits))
 
 
+def speculative_decode(draft_next, target_next, first_token: int, n_tokens: int, k: int):
+    """Greedy draft-and-verify decoding ([PoD] abstract: speculation verified
+    at 8 bits reaches the 8-bit output at similar bytes).
+
+    Readings taken where the abstract is open: greedy decoding; a step's next
+    token depends on the current token alone (``draft_next(t)`` and
+    ``target_next(t)`` give the draft's and the target's next token after
+    ``t``).  A round drafts ``k`` tokens with the draft, d_1 = draft(cur),
+    d_i = draft(d_{i-1}); the target gives t_0 = target(cur) and
+    t_i = target(d_i) (in the method one batched pass over the k + 1
+    inputs); the round keeps d_1 .. d_j for the longest run with
+    t_{i-1} = d_i, then emits t_j.  The emitted sequence is the target's
+    greedy sequence whatever the draft does.
+
+    Returns (the first ``n_tokens`` emitted tokens, stats) with stats
+    rounds, draft_steps, drafted, accepted, emitted (the last round's surplus
+    counted in ``emitted`` but not returned).
+    """
+    if k < 1:
+        raise ValueError("k must be at least 1")
+    out = []
+    st = dict(rounds=0, draft_steps=0, drafted=0, accepted=0, emitted=0)
+    cur = int(first_token)
+    while len(out) < n_tokens:
+        drafts = []
+        t = cur
+        for _ in range(k):
+            t = int(draft_next(t))
+            drafts.append(t)
+        targets = [int(target_next(x)) for x in [cur] + drafts]
+        j = 0
+        while j < k and targets[j] == drafts[j]:
+            j += 1
+        emitted = drafts[:j] + [targets[j]]
+        out.extend(emitted)
+        cur = emitted[-1]
+        st["rounds"] += 1
+        st["draft_steps"] += k
+        st["drafted"] += k
+        st["accepted"] += j
+        st["emitted"] += j + 1
+    return out[:n_tokens], st
+
+
+def speculation_byte_ratio(stats, n_tokens: int, draft_bits: int = 4, verify_bits: int = 8) -> float:
+    """Weight bytes per emitted token over those of one full-depth step.
+
+    Each draft step reads every weight at ``draft_bits``, each verify pass
+    reads every weight once at ``verify_bits`` for all its positions
+    ([PoD]: cost counted in weight bytes read per token).  Per token:
+    (draft_steps draft_bits + rounds verify_bits) / (n_tokens verify_bits).
+    """
+    return float((stats["draft_steps"] * draft_bits + stats["rounds"] * verify_bits) / (n_tokens * verify_bits))
+
+
 # --------------------------------------------------------------------------
 # Glue around the chained decode step (shape stand-ins, not the method)
 # --------------------------------------------------------------------------

@@ -37,6 +37,9 @@ from .api import (  # noqa: F401
     stack_write,
     stack_info,
     stack_read,
+    Verifier,
+    argmax_rows,
+    speculate,
     workspace_bytes,
 )
 from ._lib import QamError  # noqa: F401

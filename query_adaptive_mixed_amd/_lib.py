@@ -118,6 +118,14 @@ class QamDecoderDesc(C.Structure):
                 ("waves_per_block", C.c_int), ("max_chunk_tiles", C.c_int)]
 
 
+class QamSpecStats(C.Structure):
+    _fields_ = [("rounds", C.c_int64), ("draft_steps", C.c_int64), ("drafted", C.c_int64), ("accepted", C.c_int64),
+                ("emitted", C.c_int64)]
+
+
+QAM_VER_X, QAM_VER_H, QAM_VER_QKV, QAM_VER_M, QAM_VER_XN, QAM_VER_LOGITS = range(6)
+
+
 class QamError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__(f"{ERRORS.get(code, code)}: {msg}")
@@ -170,6 +178,16 @@ SIGNATURES = [
     ("qam_decoder_decode_gated", _I, [_P, _P, _I64, _I, _I, C.c_double, C.c_double, _P, _SZ, _P, _P, _P, _P]),
     ("qam_gate_workspace_bytes", C.c_size_t, [_I64]),
     ("qam_gate", _I, [_P, _I64, C.c_double, C.c_double, _P, _P, _SZ, _P]),
+    ("qam_verifier_bytes", C.c_size_t, [C.POINTER(QamDecoderDesc), _I]),
+    ("qam_verifier_create", _I, [_P, _I, _P, _SZ, C.POINTER(_P), _P]),
+    ("qam_verifier_buffer", _P, [_P, _I]),
+    ("qam_verifier_run", _I, [_P, _I, _I, _I, _I, _P]),
+    ("qam_verifier_step", _I, [_P, _I, _I, _P]),
+    ("qam_verifier_capture", _I, [_P, _I, _I, _P]),
+    ("qam_verifier_replay", _I, [_P, _I, _I, _P]),
+    ("qam_verifier_destroy", None, [_P]),
+    ("qam_argmax_rows", _I, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    ("qam_decoder_speculate", _I, [_P, _P, _P, C.c_int32, _I, _I, _I, _I, _P, C.POINTER(QamSpecStats), _P]),
     ("qam_last_error", C.c_char_p, []),
     ("qam_last_variant", C.c_char_p, []),
     ("qam_version", C.c_char_p, []),

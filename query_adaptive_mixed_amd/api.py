@@ -785,6 +785,95 @@ class Decoder:
             destroy(h)
 
 
+class Verifier:
+    """Batched decode steps over a Decoder's weights (the verify pass of
+    draft-and-verify).  Write B inputs into ``x[:B]`` and call
+    ``step(rung, B)``; ``logits[:B]`` holds the result.  ``run`` enqueues
+    single ops of the chain (op 0 loads the inputs, then qkv, o, gate_up,
+    down per layer, then the head)."""
+
+    def __init__(self, dec: Decoder, max_batch: int):
+        nbytes = int(L.lib().qam_verifier_bytes(C.byref(dec._desc), int(max_batch)))
+        if nbytes == 0:
+            raise L.QamError(-3, f"no verifier for max_batch={max_batch}")
+        self.dec = dec
+        self.max_batch = int(max_batch)
+        self.mem = torch.empty(nbytes, dtype=torch.uint8, device=dec.mem.device)
+        h = C.c_void_p()
+        L.check(L.lib().qam_verifier_create(dec._h, self.max_batch, _ptr(self.mem), nbytes, C.byref(h),
+                                            _stream_handle()))
+        self._h = h
+        self._destroy = L.lib().qam_verifier_destroy
+        d = dec._desc
+        H, Q, KV, F, V = int(d.hidden), int(d.q_dim), int(d.kv_dim), int(d.ffn), int(d.vocab)
+        self.n_ops = 4 * dec.n_layers + 2
+        self.x = self._buffer(L.QAM_VER_X, H)
+        self.hidden = self._buffer(L.QAM_VER_H, H)
+        self.qkv = self._buffer(L.QAM_VER_QKV, Q + 2 * KV)
+        self.m = self._buffer(L.QAM_VER_M, F)
+        self.xn_flat = self._buffer(L.QAM_VER_XN, max(H, Q, F)).reshape(-1)
+        self.logits = self._buffer(L.QAM_VER_LOGITS, V)
+
+    def _buffer(self, which: int, n: int) -> torch.Tensor:
+        off = L.lib().qam_verifier_buffer(self._h, which) - self.mem.data_ptr()
+        return self.mem[off:off + 4 * n * self.max_batch].view(torch.float32).view(self.max_batch, n)
+
+    def xn(self, B: int, n: int) -> torch.Tensor:
+        """The next product's input as [B, n] (rows packed with stride n)."""
+        return self.xn_flat[:B * n].view(B, n)
+
+    def run(self, rung: int, B: int, first: int, count: int = 1) -> None:
+        L.check(L.lib().qam_verifier_run(self._h, int(rung), int(B), int(first), int(count), _stream_handle()))
+
+    def step(self, rung: int, B: int) -> None:
+        L.check(L.lib().qam_verifier_step(self._h, int(rung), int(B), _stream_handle()))
+
+    def capture(self, rung: int, B: int) -> None:
+        if getattr(self, "_capture_stream", None) is None:
+            self._capture_stream = torch.cuda.Stream(device=self.mem.device)
+        s = self._capture_stream
+        s.wait_stream(torch.cuda.current_stream())
+        L.check(L.lib().qam_verifier_capture(self._h, int(rung), int(B), C.c_void_p(s.cuda_stream)))
+        torch.cuda.current_stream().wait_stream(s)
+
+    def replay(self, rung: int, B: int) -> None:
+        L.check(L.lib().qam_verifier_replay(self._h, int(rung), int(B), _stream_handle()))
+
+    def __del__(self):
+        h, destroy = getattr(self, "_h", None), getattr(self, "_destroy", None)
+        self._h = None
+        if h is not None and h.value and callable(destroy):
+            destroy(h)
+
+
+def argmax_rows(v: torch.Tensor, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int32 [rows]: first index of the row maximum of fp32 v [rows, n] (no NaN)."""
+    _require_cuda(v, "v", torch.float32)
+    if v.dim() == 1:
+        v = v.unsqueeze(0)
+    rows, n = v.shape
+    if workspace is None:
+        workspace = torch.zeros(rows, dtype=torch.int64, device=v.device)
+    out = torch.empty(rows, dtype=torch.int32, device=v.device)
+    L.check(L.lib().qam_argmax_rows(_ptr(v), rows, n, n, _ptr(out), _ptr(workspace), _stream_handle()))
+    return out
+
+
+def speculate(dec: Decoder, ver: Verifier, embed: torch.Tensor, first_token: int, n_tokens: int, k: int,
+              draft_rung: int = 2, verify_rung: int = 4):
+    """Greedy draft-and-verify decoding: (tokens int32 [n_tokens], stats dict)."""
+    _require_cuda(embed, "embed", torch.float32)
+    if embed.dim() != 2 or tuple(embed.shape) != (int(dec._desc.vocab), int(dec._desc.hidden)):
+        raise ValueError("embed must be [vocab, hidden]")
+    out = np.zeros(max(1, int(n_tokens)), dtype=np.int32)
+    st = L.QamSpecStats()
+    L.check(L.lib().qam_decoder_speculate(dec._h, ver._h, _ptr(embed), int(first_token), int(n_tokens), int(k),
+                                          int(draft_rung), int(verify_rung), out.ctypes.data_as(C.c_void_p),
+                                          C.byref(st), _stream_handle()))
+    stats = {f: int(getattr(st, f)) for f, _ in L.QamSpecStats._fields_}
+    return out[:int(n_tokens)], stats
+
+
 def escalation_schedule(scores, rate: float) -> np.ndarray:
     """bool [T]: the steps re-run at 8 bits (the round(rate T) largest scores, ties to the earlier step)."""
     sc = np.ascontiguousarray(np.asarray(scores, dtype=np.float64).reshape(-1))

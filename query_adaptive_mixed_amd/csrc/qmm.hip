@@ -356,12 +356,74 @@ __device__ __forceinline__ double listed_correction(const MItem& a, int b, int c
     return e < kSmallExp ? ldexp(part, -kPrescale) : part;
 }
 
+// The same corrections for a chunk with many listed elements: the list,
+// sorted by column, is spread tile by tile into the wave's LDS row `r2d`
+// (64 residuals, zero where nothing is listed), and the lane of row `row`
+// multiplies the row's 64 codes of the tile by it.  Terms are added in
+// column order, as in listed_correction (the extra terms are exact zeros), so
+// both forms give the same bits; this one reads each tile's words once
+// instead of gathering one code per listed element.
+constexpr int kDenseListed = 16;
+
+__device__ __forceinline__ void row_tile_words(const uint8_t* tb, int64_t pb, int first, int depth,
+                                               uint32_t (&w)[4][4]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            w[g][q] = (q >= first && q < depth) ? *reinterpret_cast<const uint32_t*>(tb + 256 * g + q * pb) : 0u;
+}
+
+__device__ double dense_correction(const MItem& a, int b, int chunk, int slot, int n, int row, int first, int depth,
+                                   int e, float* r2d) {
+    const int2* list = a.unc + (int64_t)slot * a.tpc * 64;
+    const int L = (int)threadIdx.x & 63;
+    const int t0 = chunk * a.tpc;
+    const int t1 = min(a.n_tiles, t0 + a.tpc);
+    // row `row` of tile t: word row >> 4 of lanes (row & 15) + 16 g, g = 0..3
+    const uint8_t* rowbase = a.planes + (int64_t)b * 16 * a.K + 16 * (row & 15) + 4 * (row >> 4);
+    double part = 0.0;
+    int p = 0;
+    uint32_t cur[4][4], nxt[4][4];
+    row_tile_words(rowbase + (int64_t)t0 * kTileBytes, a.plane_bytes, first, depth, cur);
+    for (int t = t0; t < t1 && p < n; ++t) {
+        if (t + 1 < t1) row_tile_words(rowbase + (int64_t)(t + 1) * kTileBytes, a.plane_bytes, first, depth, nxt);
+        const int lo = (t - t0) * 64;
+        int2 ent = make_int2(0x7fffffff, 0);
+        if (p + L < n) ent = list[p + L];
+        const bool in = ent.x < lo + 64;   // every earlier entry is consumed: these are the tile's
+        const int cnt = __popcll(__ballot(in));
+        if (cnt > 0) {
+            r2d[L] = 0.0f;
+            if (in) r2d[ent.x - lo] = __int_as_float(ent.y);
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    uint32_t acc = 0u;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc |= cur[g][q] & rotr_const(0x03030303u << (2 * (3 - q)), 2 * u);
+                    if (u != 0) acc = rotl32(acc, 2 * u);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        part += (double)(int8_t)(uint8_t)(acc >> (8 * i)) * (double)r2d[16 * g + 4 * u + i];
+                }
+            p += cnt;
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) cur[g][q] = nxt[g][q];
+    }
+    return e < kSmallExp ? ldexp(part, -kPrescale) : part;
+}
+
 // One workgroup = KS x NH wavefronts = one (block, column chunk).
 // REFINE: a refinement launch (c.first > 0); without it `first` is the
 // constant 0 and the code is that of the plain product.
 template <int NCG, bool PER_REQ, bool GROUPED, bool REFINE>
 __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
-    extern __shared__ int tab[];   // [NH][64 rows][16 NCG + 1] integer sums, then one flag
+    extern __shared__ int tab[];   // [NH][64 rows][16 NCG + 1] integer sums, one flag, then r2d rows
     constexpr int TW = 16 * NCG + 1;
     MItem a;
     int local;
@@ -454,6 +516,7 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
     // request r are columns 6 (r mod SS) + l of set r / SS, then scaled into
     // fp64, with the chunk's listed corrections
     const int row = L;
+    float* r2d = reinterpret_cast<float*>(tab + NH * 64 * TW + 4) + 64 * wave;   // this wave's residual row
     const double sc = (double)a.scales[b * kRows + row];
     const int slots = SS * NH;
     const bool split = a.n_chunks > 1;
@@ -469,7 +532,10 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
             } else {
                 v = limb_value(t2[0], t2[1], t2[2], t2[3], t2[4], t2[5], e);
                 const int n = a.unc_count[slot];
-                if (n > 0) v += listed_correction(a, b, chunk, slot, n, row, first, mr, e);
+                if (n > kDenseListed)
+                    v += dense_correction(a, b, chunk, slot, n, row, first, mr, e, r2d);
+                else if (n > 0)
+                    v += listed_correction(a, b, chunk, slot, n, row, first, mr, e);
             }
         }
         if ((bad_mask >> r) & 1) v = __builtin_nan("");
@@ -514,7 +580,7 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
 template <int NCG, bool GROUPED>
 static void launch_product(const MItem& it, const MCommon& c, bool per_req, int64_t grid, hipStream_t s) {
     const dim3 blk(64 * c.NH * c.KS);
-    const size_t lds = ((size_t)c.NH * 64 * (16 * NCG + 1) + 4) * sizeof(int);
+    const size_t lds = ((size_t)c.NH * 64 * (16 * NCG + 1) + 4 + 4 * 64) * sizeof(int);   // + 4 waves' r2d rows
     if (c.first > 0) {
         if (per_req)
             hipLaunchKernelGGL((qmm_kernel<NCG, true, GROUPED, true>), dim3((unsigned)grid), blk, lds, s, it, c);

@@ -225,3 +225,55 @@ def test_bad_rung_is_flagged_not_read(qam, B):
         ref = O.qmatvec_ref(W, sc, x, np.tile(good, (B, 1)), per_request=True)
         tol = O.qmatvec_tolerance(W, sc, x, np.tile(good, (B, 1)), per_request=True)
         assert np.all(np.abs(y3[ok].astype(np.float64) - ref[ok]) <= tol[ok])
+
+
+def silu_tail_problem(seed, N, K, B):
+    """Inputs shaped like a gated activation silu(g) u with |g| up to ~100:
+    most entries are O(1..1e3), the negative-g ones fall to 1e-40 and below,
+    so nearly every chunk lists many elements (the dense form of the exact
+    residuals) while a few requests list none or a handful (the listed form)."""
+    rng = np.random.default_rng(seed)
+    W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+    g = rng.standard_normal((B, K)) * 25.0
+    u = rng.standard_normal((B, K)) * 25.0
+    x = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+    x[0] = rng.standard_normal(K).astype(np.float32)            # request 0: nothing listed
+    if B > 2:
+        x[1] = rng.standard_normal(K).astype(np.float32)
+        x[1, rng.choice(K, 5, replace=False)] = 1e-30          # request 1: a handful listed per chunk
+    return rng, W, sc, x
+
+
+@pytest.mark.parametrize("B", [2, 5, 16, 32])
+def test_gated_activation_tails(qam, B):
+    """Every pre-pass form on silu-shaped inputs: shared and per-request
+    maps, bf16 input, the grouped launch and the refinement launch."""
+    import query_adaptive_mixed_amd._lib as L
+    N, K = 512, 3136            # 49 tiles: several chunks, a ragged last one
+    rng, W, sc, x = silu_tail_problem(700 + B, N, K, B)
+    pm = qam.pack_slices(dev(W), dev(sc))
+    xd = dev(x)
+    lv = rng.integers(0, 5, size=N // 64).astype(np.uint8)
+    check(host(qam.qmatvec(xd, pm, dev(lv))), W, sc, x, lv, False, ("shared", B))
+    lvr = rng.integers(0, 5, size=(B, N // 64)).astype(np.uint8)
+    check(host(qam.qmatvec(xd, pm, dev(lvr))), W, sc, x, lvr, True, ("per-request", B))
+    xbf = torch.from_numpy(x).to(torch.bfloat16)
+    xb = xbf.to(torch.float32).numpy()
+    check(host(qam.qmatvec(xbf.cuda(), pm, dev(lv))), W, sc, xb, lv, False, ("bf16", B))
+    y = torch.zeros((B, N), device="cuda")
+    grp = qam.GroupedQmatvec([(pm, xd, y, dev(lvr))])
+    grp.run()
+    check(host(y), W, sc, x, lvr, True, ("group", B))
+    glass = 1
+    lvg = rng.integers(glass, 5, size=(B, N // 64)).astype(np.uint8)
+    uni = np.full(N // 64, glass, np.uint8)
+    yr = torch.full((B, N), float("nan"), device="cuda")
+    base = qam.GroupedQmatvec([(pm, xd, yr, dev(uni))])
+    second = qam.GroupedQmatvec([(pm, xd, yr, dev(lvg))])
+    base.run()
+    L.check(L.lib().qam_qmatvec_group_refine(C.byref(second.desc), glass, None))
+    ref = O.qmatvec_ref(W, sc, x, lvg, per_request=True)
+    tol = O.qmatvec_tolerance(W, sc, x, lvg, per_request=True) + O.qmatvec_tolerance(W, sc, x, uni)
+    err = np.abs(host(yr).astype(np.float64) - ref)
+    assert np.all(err <= tol), ("refine", B, float((err / tol).max()))

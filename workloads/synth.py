@@ -27,7 +27,7 @@ import numpy as np
 ROWS_PER_BLOCK = 64
 
 # stream tags for multi-matrix workloads
-TAG_CODES, TAG_SCALES, TAG_X, TAG_COORDS, TAG_LENSES, TAG_SCORES, TAG_REQ_LENSES = range(1, 8)
+TAG_CODES, TAG_SCALES, TAG_X, TAG_COORDS, TAG_LENSES, TAG_SCORES, TAG_REQ_LENSES, TAG_EMBED = range(1, 9)
 
 
 def stream(seed: int, tag: int, index: int = 0) -> np.random.Generator:
@@ -219,6 +219,11 @@ def qwen_decode_field(seed: int = 0, n_layers: int = 28) -> Field:
     """28 layers (hidden 1024; 16 Q heads / 8 KV heads of dim 128; FFN 3072)
     plus the tied 151936x1024 head, int8 weights."""
     return decoder_field(seed, n_layers, QWEN_HIDDEN, 2048, 1024, 3072, QWEN_VOCAB, "qwen_decode")
+
+
+def embedding_table(seed: int, vocab: int, hidden: int) -> np.ndarray:
+    """Token-feedback stand-in: one N(0, 1) fp32 row per token, [vocab, hidden]."""
+    return stream(seed, TAG_EMBED).standard_normal((vocab, hidden), dtype=np.float32)
 
 
 def decode_inputs(seed: int, n_steps: int, hidden: int = QWEN_HIDDEN) -> np.ndarray:
