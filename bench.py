@@ -568,6 +568,32 @@ def run_decode(args, torch, Q, WL):
     pywall = time.perf_counter() - t0
     if py_fired != fired:
         raise RuntimeError(f"gated decode: the library loop escalated {fired} steps, the Python loop {py_fired}")
+    # ... and with the decision kept on the device: the D8 step as a graph of
+    # products predicated on the gate's flag, no synchronisation per step
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dec.decode_gated_async(xs[:min(T, 8)], gate, tau)
+        side.synchronize()
+        t0 = time.perf_counter()
+        aflags = dec.decode_gated_async(xs, gate, tau)
+        side.synchronize()
+        awall = time.perf_counter() - t0
+        # the predicated D8 graph alone when it does not fire: its floor cost per step
+        gate.run(dec.logits, math.inf)
+        never = []
+        for i in range(12):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dec.decode_gated_async(xs[:1], gate, math.inf)
+            b.record()
+            never.append((a, b))
+        side.synchronize()
+    torch.cuda.current_stream().wait_stream(side)
+    a_fired = int(aflags.sum().item())
+    if a_fired != fired:
+        raise RuntimeError(f"gated decode: the device-decided loop escalated {a_fired} steps, the synchronising one {fired}")
+    never_ms = float(np.median([a.elapsed_time(b) for a, b in never[2:]]))
     spec = run_speculation(args, torch, Q, WL, dec, wb) if args.spec_tokens > 0 else None
     return {
         "workload": "qwen_decode",
@@ -593,6 +619,15 @@ def run_decode(args, torch, Q, WL):
             "weight_bytes_per_token": int(gtotal // T),
             "gate_cost_ms_per_token": round((gwall - wall) * 1e3 / T, 5),
             "python_loop_tokens_per_s": round(T / pywall, 2),
+            "no_sync": {
+                "tokens_per_s": round(T / awall, 2), "ms_per_token": round(awall * 1e3 / T, 5),
+                "escalated_steps": a_fired,
+                "step_ms_when_not_fired": round(never_ms, 5),
+                "timing": "qam_decoder_decode_gated_async, one call for all steps, one synchronisation at the "
+                          "end; per step: D4 graph, gate, flag byte, predicated copy, then the D8 graph whose "
+                          "113 products each read the gate's flag and exit at once when it is 0. "
+                          "step_ms_when_not_fired: one such step with the gate forced off (events)",
+            },
             "timing": "qam_decoder_decode_gated, one call for all steps; per step: D4 graph replay, gate launch, "
                       "device-to-host read of its result (a stream synchronisation), D8 graph replay when it "
                       "fired; wall clock over the call. python_loop_tokens_per_s: the same steps driven from "

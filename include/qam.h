@@ -891,6 +891,26 @@ int qam_decoder_decode_gated(qam_decoder* dec, const float* inputs, int64_t T, i
                              size_t gate_workspace_bytes, qam_uncertainty* gate_out,
                              qam_uncertainty* host_result, uint8_t* escalated_out, hipStream_t s);
 
+/*
+ * qam_decoder_decode_gated_async -- the same T gated steps with the decision
+ *   left on the device: no host synchronisation per step (HIP graphs have no
+ *   conditional nodes here, so the branch is a predicate).  Per step t:
+ *   h <- inputs[t]; replay the rung_low graph; qam_gate into gate_out;
+ *   escalated_dev[t] = gate_out->escalate; h <- inputs[t] again if it fired
+ *   (a predicated copy kernel); then a graph of the rung_high step whose
+ *   every product kernel reads gate_out->escalate first and exits at once
+ *   when it is 0.  That graph is captured on `s` on the first call (and again
+ *   when gate_out changes), so `s` must not be the null stream and the call
+ *   must not itself be captured.  Everything is enqueued on `s`; the call
+ *   returns without waiting.  rung_low must have been captured.
+ *   escalated_dev  (device) uint8 [T].
+ *   Each step pays the rung_high graph's launches whether or not it fired.
+ */
+int qam_decoder_decode_gated_async(qam_decoder* dec, const float* inputs, int64_t T, int rung_low, int rung_high,
+                                   double tau_entropy, double tau_margin, void* gate_workspace,
+                                   size_t gate_workspace_bytes, qam_uncertainty* gate_out, uint8_t* escalated_dev,
+                                   hipStream_t s);
+
 /* ---------------------------------------------------------------- draft and verify */
 /*
  * Verified speculation ([PoD] abstract: speculation verified at full depth

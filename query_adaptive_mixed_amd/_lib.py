@@ -176,6 +176,7 @@ SIGNATURES = [
     ("qam_fit_focus_area", _I, [_P, _I64, _P, C.POINTER(QamLens), _I, C.POINTER(QamLensParams), _P, _I, _I, _I64,
                                 _I, _P, _P, _SZ, C.POINTER(C.c_double), C.POINTER(C.c_int64), _P]),
     ("qam_decoder_decode_gated", _I, [_P, _P, _I64, _I, _I, C.c_double, C.c_double, _P, _SZ, _P, _P, _P, _P]),
+    ("qam_decoder_decode_gated_async", _I, [_P, _P, _I64, _I, _I, C.c_double, C.c_double, _P, _SZ, _P, _P, _P]),
     ("qam_gate_workspace_bytes", C.c_size_t, [_I64]),
     ("qam_gate", _I, [_P, _I64, C.c_double, C.c_double, _P, _P, _SZ, _P]),
     ("qam_verifier_bytes", C.c_size_t, [C.POINTER(QamDecoderDesc), _I]),

@@ -774,6 +774,28 @@ class Decoder:
             esc.ctypes.data_as(C.c_void_p), _stream_handle()))
         return esc
 
+    def decode_gated_async(self, inputs: torch.Tensor, gate: "Gate", tau_entropy: float = float("inf"),
+                           tau_margin: float = float("-inf"), rung_low: int = 2, rung_high: int = 4,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """The gated steps with the decision kept on the device (predicated
+        high-rung graph, no per-step synchronisation); ``rung_low`` must be
+        captured.  Returns uint8 [T] on the device (ready when the stream is)."""
+        _require_cuda(inputs, "inputs", torch.float32)
+        T = inputs.shape[0]
+        if inputs.dim() != 2 or inputs.shape[1] != self.hidden.numel():
+            raise ValueError("inputs must be [T, hidden]")
+        if gate.V != self.logits.numel():
+            raise ValueError("the gate must take the vocabulary's logits")
+        if out is None:
+            out = torch.zeros(max(1, T), dtype=torch.uint8, device=self.mem.device)
+        s = torch.cuda.current_stream()
+        if s.cuda_stream == 0:
+            raise ValueError("decode_gated_async needs a stream other than the null stream")
+        L.check(L.lib().qam_decoder_decode_gated_async(
+            self._h, _ptr(inputs), T, int(rung_low), int(rung_high), float(tau_entropy), float(tau_margin),
+            _ptr(gate.ws), gate.ws.numel(), _ptr(gate.out), _ptr(out), C.c_void_p(s.cuda_stream)))
+        return out[:T]
+
     def status(self, clear: bool = True) -> int:
         """The decoder's status word (QAM_STATUS_* bits, 0 if all is well)."""
         return status(self.mem, clear)

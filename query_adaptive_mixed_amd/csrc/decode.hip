@@ -106,7 +106,7 @@ int layout(const qam_decoder_desc* d, Layout& lo) {
     return QAM_OK;
 }
 
-int enqueue(qam_decoder* dec, int rung, int first, int count, hipStream_t s) {
+int enqueue(qam_decoder* dec, int rung, int first, int count, hipStream_t s, const int* run_if = nullptr) {
     if (rung < 0 || rung > 4) QAM_FAIL(QAM_ERR_ARG, "decoder: rung %d outside 0..4", rung);
     const std::vector<Op> ops = chain(*dec);
     if (first < 0 || count < 0 || first > (int)ops.size() || count > (int)ops.size() - first)
@@ -129,9 +129,45 @@ int enqueue(qam_decoder* dec, int rung, int first, int count, hipStream_t s) {
             it.partials = reinterpret_cast<double*>(dec->ws + QAM_WS_COUNTER_BYTES);
         }
         it.counters = reinterpret_cast<uint32_t*>(dec->ws);
+        it.run_if = run_if;
         launch_single(it, c, (int64_t)p.n_chunks * p.n_quads, s);
     }
     QAM_HIP_CHECK(hipGetLastError());
+    return QAM_OK;
+}
+
+// h = x when *flag (the re-run of an escalated step starts from its input).
+__global__ void __launch_bounds__(256) copy_if_kernel(const int* flag, const float* x, float* h, int64_t n) {
+    if (*flag == 0) return;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        h[i] = x[i];
+}
+
+// out = (*flag != 0), one byte.
+__global__ void flag_byte_kernel(const int* flag, uint8_t* out) { *out = *flag != 0 ? 1 : 0; }
+
+// Capture the step at `rung` with every product predicated on *flag.
+int capture_predicated(qam_decoder* dec, int rung, const int* flag, hipStream_t s) {
+    QAM_HIP_CHECK(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    const int rc = enqueue(dec, rung, 0, 4 * dec->d.n_layers + 1, s, flag);
+    hipGraph_t g = nullptr;
+    const hipError_t e = hipStreamEndCapture(s, &g);
+    if (rc != QAM_OK) {
+        if (g) (void)hipGraphDestroy(g);
+        return rc;
+    }
+    if (e != hipSuccess) QAM_FAIL(QAM_ERR_HIP, "decoder: predicated capture: %s", hipGetErrorString(e));
+    hipGraphExec_t x = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    if (ei != hipSuccess) {
+        (void)hipGraphDestroy(g);
+        QAM_FAIL(QAM_ERR_HIP, "decoder: predicated capture: instantiate: %s", hipGetErrorString(ei));
+    }
+    if (dec->pexec[rung]) (void)hipGraphExecDestroy(dec->pexec[rung]);
+    if (dec->pgraph[rung]) (void)hipGraphDestroy(dec->pgraph[rung]);
+    dec->pgraph[rung] = g;
+    dec->pexec[rung] = x;
+    dec->pflag[rung] = flag;
     return QAM_OK;
 }
 
@@ -277,11 +313,51 @@ extern "C" int qam_decoder_decode_gated(qam_decoder* dec, const float* inputs, i
     return QAM_OK;
 }
 
+extern "C" int qam_decoder_decode_gated_async(qam_decoder* dec, const float* inputs, int64_t T, int rung_low,
+                                              int rung_high, double tau_entropy, double tau_margin,
+                                              void* gate_workspace, size_t gate_workspace_bytes,
+                                              qam_uncertainty* gate_out, uint8_t* escalated_dev, hipStream_t s) {
+    clear_error();
+    if (!dec || !gate_out || ((!inputs || !escalated_dev) && T > 0))
+        QAM_FAIL(QAM_ERR_NULL, "decoder_decode_gated_async: null pointer");
+    if (T < 0) QAM_FAIL(QAM_ERR_ARG, "decoder_decode_gated_async: T < 0");
+    if (!s) QAM_FAIL(QAM_ERR_ARG, "decoder_decode_gated_async: needs a stream other than the null stream");
+    if (rung_low < 0 || rung_low > 4 || !dec->exec[rung_low])
+        QAM_FAIL(QAM_ERR_ARG, "decoder_decode_gated_async: rung %d was not captured", rung_low);
+    if (rung_high < 0 || rung_high > 4) QAM_FAIL(QAM_ERR_ARG, "decoder_decode_gated_async: rung %d", rung_high);
+    if (!aligned(inputs, 4) || !aligned(gate_out, 8))
+        QAM_FAIL(QAM_ERR_ALIGN, "decoder_decode_gated_async: misaligned inputs or gate_out");
+    const int64_t H = dec->d.hidden, V = dec->d.vocab;
+    if (gate_workspace_bytes < qam_gate_workspace_bytes(V))
+        QAM_FAIL(QAM_ERR_WORKSPACE, "decoder_decode_gated_async: gate workspace %zu < %zu bytes", gate_workspace_bytes,
+                 qam_gate_workspace_bytes(V));
+    const int* flag = &gate_out->escalate;
+    if (!dec->pexec[rung_high] || dec->pflag[rung_high] != flag)
+        if (int rc = capture_predicated(dec, rung_high, flag, s)) return rc;
+    const unsigned cgrid = (unsigned)std::min<int64_t>(64, (H + 255) / 256);
+    for (int64_t t = 0; t < T; ++t) {
+        const float* x = inputs + t * H;
+        QAM_HIP_CHECK(hipMemcpyAsync(dec->h, x, H * sizeof(float), hipMemcpyDeviceToDevice, s));
+        QAM_HIP_CHECK(hipGraphLaunch(dec->exec[rung_low], s));
+        if (int rc = qam_gate(dec->logits, V, tau_entropy, tau_margin, gate_out, gate_workspace,
+                              gate_workspace_bytes, s))
+            return rc;
+        hipLaunchKernelGGL(flag_byte_kernel, dim3(1), dim3(1), 0, s, flag, escalated_dev + t);
+        hipLaunchKernelGGL(copy_if_kernel, dim3(cgrid), dim3(256), 0, s, flag, x, dec->h, H);
+        QAM_HIP_CHECK(hipGetLastError());
+        QAM_HIP_CHECK(hipGraphLaunch(dec->pexec[rung_high], s));
+    }
+    set_variant("decoder_decode_gated_async");
+    return QAM_OK;
+}
+
 extern "C" void qam_decoder_destroy(qam_decoder* dec) {
     if (!dec) return;
     for (int r = 0; r < 5; ++r) {
         if (dec->exec[r]) (void)hipGraphExecDestroy(dec->exec[r]);
         if (dec->graph[r]) (void)hipGraphDestroy(dec->graph[r]);
+        if (dec->pexec[r]) (void)hipGraphExecDestroy(dec->pexec[r]);
+        if (dec->pgraph[r]) (void)hipGraphDestroy(dec->pgraph[r]);
     }
     delete dec;
 }

@@ -17,4 +17,8 @@ struct qam_decoder {
     int max_chunk = 0;             // longest column chunk in tiles (0: no cap)
     hipGraph_t graph[5] = {};
     hipGraphExec_t exec[5] = {};
+    // steps whose products run only when a device flag is nonzero, by rung
+    hipGraph_t pgraph[5] = {};
+    hipGraphExec_t pexec[5] = {};
+    const int* pflag[5] = {};      // the flag each predicated graph reads
 };

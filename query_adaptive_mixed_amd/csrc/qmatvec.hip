@@ -572,6 +572,7 @@ __global__ __launch_bounds__(64 * MAXW) void qmatvec_kernel(Item single, Common 
         const Item a = unit_item(c, (int)blockIdx.x);
         run_unit<XBF16, MAXW, false>(a, c, (int)blockIdx.x - a.wg_begin, lds, (int)threadIdx.x);
     } else {
+        if (single.run_if != nullptr && *single.run_if == 0) return;   // predicated launch, not taken
         run_unit<XBF16, MAXW, true>(single, c, (int)blockIdx.x, lds, (int)threadIdx.x);
     }
 }

@@ -186,6 +186,7 @@ struct Item {
     int rms;                   // 1: y uses x / sqrt(mean(x^2) + eps)
     int out_mode;              // QAM_OUT_STORE / _ADD / _GLU
     double eps;
+    const int* run_if;         // single launches: when set and *run_if == 0, every workgroup exits at once
 };
 
 struct Common {

@@ -302,3 +302,57 @@ def test_decode_gated_matches_step_by_step_loop(qam):
         dec.decode_gated(xs, qam.Gate(SMALL["vocab"] + 1), tau)
     with pytest.raises(qam.QamError):
         dec.decode_gated(xs, gate, tau, rung_low=1)
+
+
+def test_decode_gated_async_matches_the_synchronising_loop(qam):
+    """The gated steps with the decision left on the device (predicated
+    high-rung graph, no per-step synchronisation) take the same decisions and
+    leave the same bits as qam_decoder_decode_gated."""
+    fld, dec = _make_decoder(qam, SMALL)
+    T = 12
+    xs = dev(WL.decode_inputs(6, T, SMALL["hidden"]))
+    gate = qam.Gate(SMALL["vocab"])
+    dec.capture(2)
+    dec.capture(4)
+    ent = []
+    for t in range(T):
+        dec.hidden.copy_(xs[t])
+        dec.replay(2)
+        gate.run(dec.logits)
+        ent.append(gate.result()["entropy"])
+    srt = sorted(ent)
+    tau = 0.5 * (srt[T // 2 - 1] + srt[T // 2])
+    want = dec.decode_gated(xs, gate, tau)
+    last = (host(dec.logits).copy(), host(dec.hidden).copy())
+    assert 0 < int(want.sum()) < T
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for rep in range(2):
+            dec.hidden.zero_()
+            got = dec.decode_gated_async(xs, gate, tau)
+            side.synchronize()
+            assert got.cpu().numpy().tolist() == want.tolist(), rep
+            assert np.array_equal(dec.logits.cpu().numpy(), last[0]), rep
+            assert np.array_equal(dec.hidden.cpu().numpy(), last[1]), rep
+        # a second gate: the predicated graph is captured again for its flag
+        gate2 = qam.Gate(SMALL["vocab"])
+        got = dec.decode_gated_async(xs, gate2, -1.0)          # always fires
+        side.synchronize()
+        assert int(got.sum()) == T
+        fired_last = dec.logits.cpu().numpy().copy()
+        got = dec.decode_gated_async(xs, gate2, float("inf"))   # never fires
+        side.synchronize()
+        assert int(got.sum()) == 0
+        never_last = dec.logits.cpu().numpy().copy()
+        for rung, ref in ((4, fired_last), (2, never_last)):
+            dec.hidden.copy_(xs[T - 1])
+            dec.replay(rung)
+            side.synchronize()
+            assert np.array_equal(dec.logits.cpu().numpy(), ref), rung
+    torch.cuda.current_stream().wait_stream(side)
+    import query_adaptive_mixed_amd._lib as L
+    from query_adaptive_mixed_amd.api import _ptr
+    rc = L.lib().qam_decoder_decode_gated_async(dec._h, _ptr(xs), T, 2, 4, 1.0, -1.0, _ptr(gate.ws), gate.ws.numel(),
+                                                 _ptr(gate.out), _ptr(xs), None)
+    assert rc == -3                                               # the null stream is refused
