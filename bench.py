@@ -46,21 +46,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as fh:
+def kernel_hash(src: str = KERNEL_SRC) -> str:
+    with open(src, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
 def measured_traffic(key: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source (else None)."""
+    taken on the current source of the kernel they measure (else None)."""
     try:
         with open(COUNTERS) as fh:
             d = json.load(fh)
     except (OSError, ValueError):
         return None
     ent = d.get(key)
-    if not ent or ent.get("kernel_sha") != kernel_hash():
+    if not ent:
+        return None
+    src = os.path.join(ROOT, "query_adaptive_mixed_amd", "csrc", ent.get("kernel_src", "qmatvec.hip"))
+    if ent.get("kernel_sha") != kernel_hash(src):
         return None
     return ent.get("bytes_per_launch")
 
@@ -337,7 +340,7 @@ def run_batched(args, torch, Q, WL):
         for i, m in enumerate(fld.matrices):
             pm = Q.pack_slices(torch.from_numpy(fld.codes(i)).to(dev), torch.from_numpy(fld.scales(i)).to(dev))
             items.append((pm, xs[i], ys[i], maps[:, offs[i]:offs[i] + m.n_blocks]))   # rows of the [B, 352] maps
-        groups.append(Q.GroupedQmatvec(items, device=dev))
+        groups.append(Q.GroupedQmatvec(items, device=dev, tuning=json.loads(args.tuning) if args.tuning else None))
     torch.cuda.synchronize()
     run = Rotate([g.run for g in groups])
     for _ in range(args.warmup):
@@ -847,6 +850,8 @@ def main():
     ap.add_argument("--decode-ksplit", type=int, default=0, help="waves per block in the decoder (0 = default)")
     ap.add_argument("--decode-max-chunk", type=int, default=0,
                     help="decoder: longest column chunk in tiles (0 = default)")
+    ap.add_argument("--tuning", default="", help="batched_layer: launch plan of the group as JSON "
+                    "(qam_tuning fields, e.g. '{\"set_max\": 8}'); empty = the library's defaults")
     ap.add_argument("--spec-tokens", type=int, default=64, help="draft-and-verify leg: tokens (0 = skip)")
     ap.add_argument("--spec-k", default="1,2,3", help="draft-and-verify leg: drafts per round, comma-separated")
     args = ap.parse_args()
