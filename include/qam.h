@@ -481,9 +481,13 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   each q held as three signed int8 limbs; c . q1 and c . q2 are accumulated
  *   exactly in int32 (v_mfma_i32_16x16x64_i8) and scaled into an fp64 row
  *   sum.  |r2| <= 2^(e-46); an element with |r2| > 2^-15 |x| (possible only
- *   for |x| < 2^(e-31)) has c * r2 added exactly in fp64 afterwards.  Every
- *   element therefore enters the sum with relative error at most 2^-15, and
- *   for every finite x and every code
+ *   for |x| < 2^(e-31)) is "uncovered": on the pre-pass route (B > 1) its
+ *   c * r2 is added exactly in fp64 afterwards; at B = 1 a sub-chunk holding
+ *   one is computed instead in fp32 on the vector ALUs (each lane sums at
+ *   most 256 products c x, one rounding per fused multiply-add, and the lane
+ *   sums meet in fp64: relative error at most 2^-16 of that sub-chunk's
+ *   sum |w||x|).  Every element therefore enters the sum with relative error
+ *   at most 2^-15, and for every finite x and every code
  *     |y - y_exact| <= 2^-15 sum_k |w_k||x_k| + 2^-24 |y_exact| (+ fp64 sums),
  *   inside 1e-4 sum|w||x|.  Chunks are summed in fp64 in a fixed order and
  *   y = fl32(scale * sum): results are bit-reproducible run to run.
