@@ -107,3 +107,32 @@ def test_noalloc_repeated_calls_stay_exact(qam):
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.cpu().numpy().view(np.uint32)), j
         check_oracle(y.cpu().numpy(), W, sc, x, lv)
+
+
+def test_noalloc_replays_from_a_captured_graph(qam):
+    """The call as a caller under HIP graph capture uses it: captured once
+    (after a first eager call has set the scratch up), replayed several
+    times with eager work in between, every replay equal bit for bit to
+    qam_qmatvec on the same inputs."""
+    for (N, K, B, per_req) in [(1024, 4096, 1, False), (512, 2048, 8, True)]:
+        print(f"noalloc graph N={N} K={K} B={B}", flush=True)
+        W, sc, x, lv, pm = make_case(qam, N, K, B, per_req, seed=77 + B)
+        xt, lvt = dev(x), dev(lv)
+        y = torch.zeros((B, N), dtype=torch.float32, device="cuda")
+        qam.qmatvec_noalloc(xt, pm, lvt, y)
+        want = qam.qmatvec(xt, pm, lvt)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            qam.qmatvec_noalloc(xt, pm, lvt, y)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            y.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), want.cpu().numpy().view(np.uint32)), rep
+            other = torch.zeros_like(y)
+            qam.qmatvec_noalloc(dev(np.ones_like(x)), pm, lvt, other)   # eager work on the same scratch
+            torch.cuda.synchronize()
