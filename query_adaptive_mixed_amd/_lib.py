@@ -10,7 +10,8 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqam.so")
+# QAM_LIBRARY names another build of the same library (the host-sanitizer build)
+LIB_PATH = os.environ.get("QAM_LIBRARY") or os.path.join(HERE, "libqam.so")
 
 QAM_OK = 0
 ERRORS = {-1: "QAM_ERR_NULL", -2: "QAM_ERR_SHAPE", -3: "QAM_ERR_ARG", -4: "QAM_ERR_LADDER",

@@ -49,9 +49,18 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *CFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+# Host code under AddressSanitizer (device code unchanged): a separate
+# library, libqam_host_asan.so, for running the CPU tests against the
+# host-side checks, layouts and file parsing with the sanitizer preloaded.
+HOST_ASAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+OBJDIR_ASAN = os.path.join(HERE, "_build_asan")
+LIB_ASAN = os.path.join(HERE, "libqam_host_asan.so")
+
+
+def _compile(src: str, verbose: bool, asan: bool = False) -> str:
+    obj = os.path.join(OBJDIR_ASAN if asan else OBJDIR, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *CFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), *(HOST_ASAN if asan else []), "-c", src,
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,22 +69,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every csrc/*.hip and link libqam.so; returns the library path."""
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose: bool = False, jobs: int = 8, host_asan: bool = False) -> str:
+    """Compile every csrc/*.hip and link libqam.so (host_asan: the host code
+    under AddressSanitizer, into libqam_host_asan.so); returns the path."""
+    os.makedirs(OBJDIR_ASAN if host_asan else OBJDIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, host_asan), srcs))
+    out = LIB_ASAN if host_asan else LIB
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    if host_asan:
+        cmd += ["-Xarch_host", "-fsanitize=address", "-shared-libasan"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, host_asan="--host-asan" in sys.argv))

@@ -174,3 +174,35 @@ def test_library_read_rejects_bad_arguments_before_device_work(lib, tmp_path):
     w = (L.QamPacked * 1)()
     assert lib.qam_stack_write(p, w, None, 0, None) == -3
     assert lib.qam_stack_write(p, w, None, 1, None) == -2                  # empty descriptor
+
+
+def test_library_header_check_survives_random_corruption(lib, tmp_path):
+    """Seeded byte flips and truncations of the header and table: every call
+    returns OK (a flip the layout does not reject: a name byte) or
+    QAM_ERR_IO, and never reads outside the file (run this under the
+    host-sanitizer build to check the last part)."""
+    from query_adaptive_mixed_amd import _lib as L
+    rng = np.random.default_rng(2024)
+    data = S.stack_bytes(_mats())
+    hdr, ents = S.read_header(data)
+    h = L.QamStackHeader()
+    e = (L.QamStackEntry * 4)()
+    table_end = S.HEADER_BYTES + S.ENTRY_BYTES * len(ents)
+    name_bytes = set()
+    for m in range(len(ents)):
+        base = S.HEADER_BYTES + S.ENTRY_BYTES * m + 32
+        name_bytes.update(range(base, base + S.NAME_BYTES))
+    for case in range(300):
+        b = bytearray(data)
+        for _ in range(int(rng.integers(1, 4))):
+            pos = int(rng.integers(0, table_end))
+            b[pos] ^= int(rng.integers(1, 256))
+        if case % 7 == 0:
+            b = b[:int(rng.integers(0, len(b)))]
+        p = _write(tmp_path, bytes(b), f"c{case}")
+        rc = lib.qam_stack_info(p.encode(), C.byref(h), e, 4)
+        changed = [i for i in range(min(len(b), len(data))) if b[i] != data[i]]
+        if len(b) == len(data) and all(i in name_bytes for i in changed):
+            assert rc == 0, case
+        else:
+            assert rc in (0, -8), (case, rc)
