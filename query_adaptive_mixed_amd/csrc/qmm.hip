@@ -82,10 +82,16 @@ __device__ __forceinline__ int rung_of(const MItem& a, int r, int b) {
 
 // ------------------------------------------------------------------ x -> limbs
 
-// One workgroup of four wavefronts per (column chunk, request slot
+// One workgroup of sixteen wavefronts per (column chunk, request slot
 // r < SS NH): the chunk's largest |x| sets the exponent; slots r >= B get zero
-// limbs.  The uncovered elements are listed in column order.
-constexpr int kPreThreads = 256;
+// limbs.  The uncovered elements are listed in column order.  Columns go in
+// rounds of kPreRound, each thread holding kPreVec groups of four (thread T:
+// columns 4T and 4T + 4 kPreThreads of the round); the first round's values
+// stay in registers from the maximum to the split.
+constexpr int kPreThreads = 1024;
+constexpr int kPreVec = 2;
+constexpr int kPreRound = 4 * kPreThreads * kPreVec;
+static_assert(kPreVec == 2 && 4 * kPreThreads < 65536, "two 16-bit count fields per thread");
 
 template <bool XBF16, bool GROUPED>
 __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommon c) {
@@ -113,15 +119,24 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
     const bool live = r < B;
     float m = 0.0f;
     float poison = 0.0f;   // 0 * x summed: NaN exactly when some x is not finite
+    float4 keep[kPreVec];
+#pragma unroll
+    for (int j = 0; j < kPreVec; ++j) keep[j] = float4{0.0f, 0.0f, 0.0f, 0.0f};
     if (live)
-        for (int k = 4 * T; k < ncol; k += 4 * kPreThreads) {
-            const float4 v = x4_value<XBF16>(load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + k));
-            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-            poison = __builtin_fmaf(v.x, 0.0f, poison);
-            poison = __builtin_fmaf(v.y, 0.0f, poison);
-            poison = __builtin_fmaf(v.z, 0.0f, poison);
-            poison = __builtin_fmaf(v.w, 0.0f, poison);
-        }
+        for (int base = 0; base < ncol; base += kPreRound)
+#pragma unroll
+            for (int j = 0; j < kPreVec; ++j) {
+                const int k = base + 4 * T + 4 * kPreThreads * j;
+                if (k < ncol) {
+                    const float4 v = x4_value<XBF16>(load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + k));
+                    if (base == 0) keep[j] = v;
+                    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+                    poison = __builtin_fmaf(v.x, 0.0f, poison);
+                    poison = __builtin_fmaf(v.y, 0.0f, poison);
+                    poison = __builtin_fmaf(v.z, 0.0f, poison);
+                    poison = __builtin_fmaf(v.w, 0.0f, poison);
+                }
+            }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         m = fmaxf(m, __shfl_xor(m, o));
@@ -147,38 +162,51 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
     uint8_t* lb = reinterpret_cast<uint8_t*>(a.limbs);
     int2* list = a.unc + (int64_t)(chunk * slots + r) * a.tpc * 64;
     int listed = 0;
-    for (int k = 4 * T; k - 4 * T < ncol; k += 4 * kPreThreads) {
-        const bool in = k < ncol;
-        uint32_t wh[4] = {0, 0, 0, 0}, wl[4] = {0, 0, 0, 0};
-        float r2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        bool u[4] = {false, false, false, false};
-        if (in && live && !nonfinite) {
-            const float4 v = x4_value<XBF16>(load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + k));
-            split_elem(v.x, sp, wh[0], wl[0], r2[0], u[0]);
-            split_elem(v.y, sp, wh[1], wl[1], r2[1], u[1]);
-            split_elem(v.z, sp, wh[2], wl[2], r2[2], u[2]);
-            split_elem(v.w, sp, wh[3], wl[3], r2[3], u[3]);
-        }
-        if (in) {
-            const int64_t kk = col0 + k;   // columns kk .. kk+3: one tile, one 16-column slice
-            const int64_t t = kk >> 6;
-            const int kg = (int)((kk & 63) >> 4);
-            const int byte = (int)(kk & 15);
+    for (int base = 0; base < ncol; base += kPreRound) {
+        float r2[kPreVec][4];
+        bool u[kPreVec][4];
+        int packed = 0;   // uncovered counts of this thread's groups, 16 bits each
 #pragma unroll
-            for (int l = 0; l < kLimbCols; ++l) {
-                const int col = kLimbCols * rr + l;   // B-operand column of this limb
-                const int sh = 8 * (l % 3);
-                const uint32_t* w = l < 3 ? wh : wl;
-                const uint32_t word = ((w[0] >> sh) & 0xFFu) | (((w[1] >> sh) & 0xFFu) << 8) |
-                                      (((w[2] >> sh) & 0xFFu) << 16) | (((w[3] >> sh) & 0xFFu) << 24);
-                const int64_t unit = ((t * NH + h) * NCG + (col >> 4)) * 64 + kg * 16 + (col & 15);
-                *reinterpret_cast<uint32_t*>(lb + unit * 16 + byte) = word;
+        for (int j = 0; j < kPreVec; ++j) {
+            const int k = base + 4 * T + 4 * kPreThreads * j;
+            const bool in = k < ncol;
+            uint32_t wh[4] = {0, 0, 0, 0}, wl[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                r2[j][q] = 0.0f;
+                u[j][q] = false;
             }
+            if (in && live && !nonfinite) {
+                const float4 v = base == 0 ? keep[j]
+                                           : x4_value<XBF16>(load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + k));
+                split_elem(v.x, sp, wh[0], wl[0], r2[j][0], u[j][0]);
+                split_elem(v.y, sp, wh[1], wl[1], r2[j][1], u[j][1]);
+                split_elem(v.z, sp, wh[2], wl[2], r2[j][2], u[j][2]);
+                split_elem(v.w, sp, wh[3], wl[3], r2[j][3], u[j][3]);
+            }
+            if (in) {
+                const int64_t kk = col0 + k;   // columns kk .. kk+3: one tile, one 16-column slice
+                const int64_t t = kk >> 6;
+                const int kg = (int)((kk & 63) >> 4);
+                const int byte = (int)(kk & 15);
+#pragma unroll
+                for (int l = 0; l < kLimbCols; ++l) {
+                    const int col = kLimbCols * rr + l;   // B-operand column of this limb
+                    const int sh = 8 * (l % 3);
+                    const uint32_t* w = l < 3 ? wh : wl;
+                    const uint32_t word = ((w[0] >> sh) & 0xFFu) | (((w[1] >> sh) & 0xFFu) << 8) |
+                                          (((w[2] >> sh) & 0xFFu) << 16) | (((w[3] >> sh) & 0xFFu) << 24);
+                    const int64_t unit = ((t * NH + h) * NCG + (col >> 4)) * 64 + kg * 16 + (col & 15);
+                    *reinterpret_cast<uint32_t*>(lb + unit * 16 + byte) = word;
+                }
+            }
+            packed |= ((int)u[j][0] + (int)u[j][1] + (int)u[j][2] + (int)u[j][3]) << (16 * j);
         }
-        // uncovered elements of this round, appended in column order
-        const int cnt = (int)u[0] + (int)u[1] + (int)u[2] + (int)u[3];
-        if (__syncthreads_or(cnt)) {
-            int incl = cnt;
+        // uncovered elements of this round, appended in column order: the
+        // first groups of all threads, then the second ones (16-bit fields:
+        // a round holds at most 4 kPreThreads of each)
+        if (__syncthreads_or(packed)) {
+            int incl = packed;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
                 const int v = __shfl_up(incl, o);
@@ -186,17 +214,24 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
             }
             if (lane == 63) wave_n[wave] = incl;
             __syncthreads();
-            int pos = listed + incl - cnt;
-            int total = 0;
+            int before = 0, total = 0;
 #pragma unroll
             for (int w = 0; w < kPreThreads / 64; ++w) {
-                if (w < wave) pos += wave_n[w];
-                total += wave_n[w];
+                const int n = wave_n[w];
+                if (w < wave) before += n;
+                total += n;
             }
+            const int excl = before + incl - packed;
+            const int total0 = total & 0xFFFF;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (u[q]) list[pos++] = int2{k + q, __float_as_int(r2[q])};
-            listed += total;
+            for (int j = 0; j < kPreVec; ++j) {
+                int pos = listed + (j == 0 ? (excl & 0xFFFF) : total0 + ((excl >> 16) & 0xFFFF));
+                const int k = base + 4 * T + 4 * kPreThreads * j;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (u[j][q]) list[pos++] = int2{k + q, __float_as_int(r2[j][q])};
+            }
+            listed += total0 + ((total >> 16) & 0xFFFF);
             __syncthreads();   // wave_n is read before the next round writes it
         }
     }
@@ -498,6 +533,15 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
         case 3: mproduct<3, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
         default: mproduct<4, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
     }
+    // the chunk's exponent and listed count of every request (lane r: request r) and this
+    // lane's row scale, requested now so that their latency passes during the table sums
+    const int slots = SS * NH;
+    int e_all = 0, n_all = 0;
+    if (L < slots) {
+        e_all = a.exps[chunk * slots + L];
+        n_all = a.unc_count[chunk * slots + L];
+    }
+    const float sc32 = a.scales[b * kRows + L];
     __syncthreads();   // the tables are clear
     // the wave's 64 x 16 NCG integer sums added into its set's table
     int* mine = tab + h * 64 * TW;
@@ -517,13 +561,12 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
     // fp64, with the chunk's listed corrections
     const int row = L;
     float* r2d = reinterpret_cast<float*>(tab + NH * 64 * TW + 4) + 64 * wave;   // this wave's residual row
-    const double sc = (double)a.scales[b * kRows + row];
-    const int slots = SS * NH;
+    const double sc = (double)sc32;
     const bool split = a.n_chunks > 1;
     for (int r = wave; r < B; r += nw) {
         const int* t2 = tab + (r / SS) * 64 * TW + row * TW + kLimbCols * (r % SS);
         const int slot = chunk * slots + r;
-        const int e = a.exps[slot];
+        const int e = __shfl(e_all, r & 63);
         const int mr = __shfl(m_all, r & 63);
         double v = 0.0;
         if (mr != 0) {
@@ -531,7 +574,7 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
                 v = __builtin_nan("");
             } else {
                 v = limb_value(t2[0], t2[1], t2[2], t2[3], t2[4], t2[5], e);
-                const int n = a.unc_count[slot];
+                const int n = __shfl(n_all, r & 63);
                 if (n > kDenseListed)
                     v += dense_correction(a, b, chunk, slot, n, row, first, mr, e, r2d);
                 else if (n > 0)
