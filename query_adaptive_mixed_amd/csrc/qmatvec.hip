@@ -392,6 +392,19 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
         if (fmode) tile_float<NS>(BUF, lds + (TT) * kSlotsPerTile + 4 * kg, facc);         \
         else tile_mfma<NS>(BUF, lds + (TT) * kSlotsPerTile, bslot, macc);                  \
     } while (0)
+    // A half ring of H tiles, the sub-chunk's mode tested once: straight-line
+    // matrix-core tiles accumulate in place (a test per tile made the compiler
+    // copy the accumulators back after every tile)
+#define QAM_HALF(BUF, TT)                                                                  \
+    do {                                                                                   \
+        if (fmode) {                                                                       \
+            _Pragma("unroll") for (int u = 0; u < H; ++u)                                  \
+                tile_float<NS>(BUF[u], lds + ((TT) + u) * kSlotsPerTile + 4 * kg, facc);   \
+        } else {                                                                           \
+            _Pragma("unroll") for (int u = 0; u < H; ++u)                                  \
+                tile_mfma<NS>(BUF[u], lds + ((TT) + u) * kSlotsPerTile, bslot, macc);      \
+        }                                                                                  \
+    } while (0)
 
     // One prefetch ring runs through the whole chunk: two halves of H tiles,
     // each reloaded PF tiles ahead right after it is used.  A round that ends
@@ -422,13 +435,11 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
             const bool ends_sub = tl + PF == S;
             if (ends_sub) load_x((t + PF) / S);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < H; ++u) QAM_TILE(A[u], tl + u);
+            QAM_HALF(A, tl);
             __builtin_amdgcn_sched_barrier(0);
             load_half<NS, H>(A, base0, pb, tstride, t + PF, last);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < H; ++u) QAM_TILE(Bh[u], tl + H + u);
+            QAM_HALF(Bh, tl + H);
             __builtin_amdgcn_sched_barrier(0);
             if (ends_sub) {
                 flush();
@@ -448,6 +459,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
             if (t + H + u < ntile) QAM_TILE(Bh[u], tl + H + u);
         flush();
     }
+#undef QAM_HALF
 #undef QAM_TILE
 
     const int row = b * kRows + L;   // the row this lane writes
