@@ -277,3 +277,25 @@ def test_gated_activation_tails(qam, B):
     tol = O.qmatvec_tolerance(W, sc, x, lvg, per_request=True) + O.qmatvec_tolerance(W, sc, x, uni)
     err = np.abs(host(yr).astype(np.float64) - ref)
     assert np.all(err <= tol), ("refine", B, float((err / tol).max()))
+
+
+@pytest.mark.parametrize("per_request", [False, True])
+def test_long_chunks_with_residuals_in_every_round(qam, per_request):
+    """One column chunk of 20,480 columns per request (the pre-pass walks it
+    in three rounds of up to 8,192 columns, the first kept in registers, the
+    later ones loaded again), x spread over thirty decades so that every
+    round and both column halves of a round list uncovered elements; the
+    lists must stay in column order and complete for the corrections to
+    match the oracle."""
+    N, K, B = 128, 20480, 5
+    rng = np.random.default_rng(4400 + per_request)
+    W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+    x = (rng.choice([-1.0, 1.0], size=(B, K)) * 10.0 ** rng.uniform(-20, 10, size=(B, K))).astype(np.float32)
+    lv = (rng.integers(1, 5, size=(B, N // 64)) if per_request else np.array([4, 2])).astype(np.uint8)
+    pm = qam.pack_slices(dev(W), dev(sc))
+    y = torch.full((B, N), float("nan"), device="cuda")
+    g = qam.GroupedQmatvec([(pm, dev(x), y, dev(lv))], tuning={"tiles_per_request": K // 64 // B})   # one chunk
+    g.run()
+    assert g.desc.n_workgroups == N // 64, (g.desc.n_workgroups, qam.last_variant())
+    check(host(y), W, sc, x, lv, per_request, ("long chunk", per_request))
