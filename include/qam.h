@@ -774,9 +774,12 @@ typedef struct qam_decoder_desc {
     double                   eps;           /* RMS epsilon, >= 0 */
     int                      target_waves;  /* launch width goal per matrix (workgroups); 0 = 16 */
     int                      waves_per_block; /* 1, 2, 4 or 8 wavefronts split each block's chunk
-                                               of columns inside a workgroup; 0 = 4 */
-    int                      max_chunk_tiles; /* longest column chunk of a product, in 64-column
-                                               tiles; 0 = the library's default */
+                                               of columns inside a workgroup, for every
+                                               product; 0 = per product: 8 for o, 1 for the
+                                               head, 4 for the others */
+    int                      max_chunk_tiles; /* longest column chunk of every product, in
+                                               64-column tiles; 0 = per product: 32 for o,
+                                               16 for the others */
 } qam_decoder_desc;
 
 typedef struct qam_decoder qam_decoder;     /* opaque host object */

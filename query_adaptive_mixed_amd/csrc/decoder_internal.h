@@ -13,8 +13,6 @@ struct qam_decoder {
     uint8_t* maps[5] = {};
     char* ws = nullptr;            // counters, then fp64 partials
     int64_t target_waves = 16;
-    int ksplit = 4;
-    int max_chunk = 0;             // longest column chunk in tiles (0: no cap)
     hipGraph_t graph[5] = {};
     hipGraphExec_t exec[5] = {};
     // steps whose products run only when a device flag is nonzero, by rung
