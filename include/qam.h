@@ -1033,6 +1033,34 @@ int qam_decoder_speculate(qam_decoder* dec, qam_verifier* v, const float* embed,
                           qam_spec_stats* stats, hipStream_t s);
 
 /* ---------------------------------------------------------------- diagnostics */
+
+/*
+ * Timeline of the batch-1 product (a tracing aid for short, latency-bound
+ * launches such as a decode step's).  Only the library built with
+ * QAM_TIMELINE (python -m query_adaptive_mixed_amd.build --timeline, giving
+ * libqam_timeline.so) records anything; in the product library both calls
+ * return QAM_ERR_ARG.
+ *
+ * qam_timeline_select -- choose up to QAM_TIMELINE_SLOTS matrices by their
+ *   planes pointer (slot i: planes[i]) and clear the stamps (synchronous).
+ *   Every later single-matrix launch of the batch-1 kernel on a chosen
+ *   matrix writes, for each of its first QAM_TIMELINE_GROUPS workgroups and
+ *   each wave, the 100 MHz wall clock (wall_clock64) at QAM_TIMELINE_POINTS
+ *   points: 0 kernel entry, 1 start of the wave's work, 2 first x sub-chunk
+ *   staged, 3 last tile multiplied, 4 row sums formed, 5 the block's waves'
+ *   sums combined, 6 split-K arrival counted, 7 wave exit (0 where a wave
+ *   never reaches a point).  A later launch on the same matrix overwrites.
+ *   n in [0, QAM_TIMELINE_SLOTS]; planes may be NULL when n = 0.
+ * qam_timeline_read -- copy the stamps, uint64
+ *   [QAM_TIMELINE_SLOTS][QAM_TIMELINE_GROUPS][8 waves][QAM_TIMELINE_POINTS],
+ *   to host memory `out` (synchronous); n_words must be at least that count.
+ */
+#define QAM_TIMELINE_SLOTS  8
+#define QAM_TIMELINE_GROUPS 512
+#define QAM_TIMELINE_POINTS 8
+int qam_timeline_select(const void* const* planes, int n);
+int qam_timeline_read(uint64_t* out, size_t n_words);
+
 const char* qam_last_error(void);     /* thread-local, "" if none           */
 const char* qam_last_variant(void);   /* kernel variant of the last call     */
 const char* qam_version(void);

@@ -10,7 +10,8 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# QAM_LIBRARY names another build of the same library (the host-sanitizer build)
+# QAM_LIBRARY names another build of the same library (the host-sanitizer or
+# the timeline build)
 LIB_PATH = os.environ.get("QAM_LIBRARY") or os.path.join(HERE, "libqam.so")
 
 QAM_OK = 0
@@ -37,6 +38,10 @@ class QamPacked(C.Structure):
     _fields_ = [("N", C.c_int64), ("K", C.c_int64), ("n_blocks", C.c_int64),
                 ("planes", C.c_void_p), ("scales", C.c_void_p)]
 
+
+QAM_TIMELINE_SLOTS = 8
+QAM_TIMELINE_GROUPS = 512
+QAM_TIMELINE_POINTS = 8
 
 QAM_STACK_VERSION = 1
 QAM_STACK_NAME_BYTES = 32
@@ -190,6 +195,8 @@ SIGNATURES = [
     ("qam_verifier_destroy", None, [_P]),
     ("qam_argmax_rows", _I, [_P, _I64, _I64, _I64, _P, _P, _P]),
     ("qam_decoder_speculate", _I, [_P, _P, _P, C.c_int32, _I, _I, _I, _I, _P, C.POINTER(QamSpecStats), _P]),
+    ("qam_timeline_select", _I, [_P, _I]),
+    ("qam_timeline_read", _I, [_P, _SZ]),
     ("qam_last_error", C.c_char_p, []),
     ("qam_last_variant", C.c_char_p, []),
     ("qam_version", C.c_char_p, []),

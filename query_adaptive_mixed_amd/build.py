@@ -55,12 +55,17 @@ def hipcc() -> str:
 HOST_ASAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
 OBJDIR_ASAN = os.path.join(HERE, "_build_asan")
 LIB_ASAN = os.path.join(HERE, "libqam_host_asan.so")
+# the timeline build: the batch-1 kernel stamps chosen launches (qam_timeline_*)
+TIMELINE = ["-DQAM_TIMELINE"]
+OBJDIR_TIMELINE = os.path.join(HERE, "_build_timeline")
+LIB_TIMELINE = os.path.join(HERE, "libqam_timeline.so")
 
 
-def _compile(src: str, verbose: bool, asan: bool = False) -> str:
-    obj = os.path.join(OBJDIR_ASAN if asan else OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *CFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), *(HOST_ASAN if asan else []), "-c", src,
-           "-o", obj]
+def _compile(src: str, verbose: bool, asan: bool = False, timeline: bool = False) -> str:
+    objdir = OBJDIR_ASAN if asan else (OBJDIR_TIMELINE if timeline else OBJDIR)
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *CFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), *(HOST_ASAN if asan else []),
+           *(TIMELINE if timeline else []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -69,14 +74,27 @@ def _compile(src: str, verbose: bool, asan: bool = False) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8, host_asan: bool = False) -> str:
+def build(verbose: bool = False, jobs: int = 8, host_asan: bool = False, timeline: bool = False) -> str:
     """Compile every csrc/*.hip and link libqam.so (host_asan: the host code
-    under AddressSanitizer, into libqam_host_asan.so); returns the path."""
-    os.makedirs(OBJDIR_ASAN if host_asan else OBJDIR, exist_ok=True)
+    under AddressSanitizer, into libqam_host_asan.so; timeline: the batch-1
+    kernel with its timeline stamps, into libqam_timeline.so); returns the
+    path."""
+    if host_asan and timeline:
+        raise ValueError("one variant at a time")
+    objdir = OBJDIR_ASAN if host_asan else (OBJDIR_TIMELINE if timeline else OBJDIR)
+    os.makedirs(objdir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, host_asan), srcs))
-    out = LIB_ASAN if host_asan else LIB
+    if timeline:
+        # only the batch-1 source carries stamps; the rest is the product build's
+        stamped = [s for s in srcs if os.path.basename(s) == "qmatvec.hip"]
+        rest = [os.path.join(OBJDIR, os.path.basename(s) + ".o") for s in srcs if s not in stamped]
+        if any(not os.path.exists(o) for o in rest):
+            build(verbose=verbose, jobs=jobs)
+        objs = [_compile(stamped[0], verbose, timeline=True)] + rest
+    else:
+        with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
+            objs = list(ex.map(lambda s: _compile(s, verbose, host_asan), srcs))
+    out = LIB_ASAN if host_asan else (LIB_TIMELINE if timeline else LIB)
     tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if host_asan:
@@ -91,4 +109,4 @@ def build(verbose: bool = False, jobs: int = 8, host_asan: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, host_asan="--host-asan" in sys.argv))
+    print(build(verbose="-v" in sys.argv, host_asan="--host-asan" in sys.argv, timeline="--timeline" in sys.argv))

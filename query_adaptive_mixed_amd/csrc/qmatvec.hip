@@ -43,6 +43,23 @@
 
 namespace qam {
 
+// ------------------------------------------------------------------ timeline
+
+// The timeline build (QAM_TIMELINE) stamps chosen single-matrix launches;
+// elsewhere the stamps compile to nothing.
+#ifdef QAM_TIMELINE
+__constant__ const void* tl_select[QAM_TIMELINE_SLOTS];
+__device__ unsigned long long tl_stamps[QAM_TIMELINE_SLOTS][QAM_TIMELINE_GROUPS][8][QAM_TIMELINE_POINTS];
+#define QAM_STAMP(P)                                                                                    \
+    do {                                                                                                \
+        if (tl_row != nullptr && L == 0) tl_row[ks * QAM_TIMELINE_POINTS + (P)] = (unsigned long long)wall_clock64(); \
+    } while (0)
+#else
+#define QAM_STAMP(P) \
+    do {             \
+    } while (0)
+#endif
+
 // ------------------------------------------------------------------ layout
 
 // Sub-chunks of S tiles: each lane loads G = S / 4 groups of four x values.
@@ -308,7 +325,9 @@ __device__ __forceinline__ void finish_zero(const Item& a, int b, int L) {
 // rounding across sub-chunks, in a fixed order).
 template <int NS, bool XBF16, bool EPI>
 __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* __restrict__ lds, int b, int chunk,
-                                          int L, int ks, int KS, double* red) {
+                                          int L, int ks, int KS, double* red, unsigned long long* tl_row) {
+    (void)tl_row;
+    QAM_STAMP(1);
     constexpr int H = Ring<NS>::H;
     constexpr int PF = Ring<NS>::PF;
     constexpr int S = kStageTiles;
@@ -425,6 +444,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
         load_half<NS, H>(A, base0, pb, tstride, 0, last);
         __builtin_amdgcn_sched_barrier(0);   // ... then half a ring, and only then is x used
         stage(0);
+        QAM_STAMP(2);
         load_half<NS, H>(Bh, base0, pb, tstride, H, last);
         __builtin_amdgcn_sched_barrier(0);
         clear_acc();
@@ -457,7 +477,9 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
 #pragma unroll
         for (int u = 0; u < H; ++u)
             if (t + H + u < ntile) QAM_TILE(Bh[u], tl + H + u);
+        QAM_STAMP(3);
         flush();
+        QAM_STAMP(4);
     }
 #undef QAM_HALF
 #undef QAM_TILE
@@ -470,6 +492,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
             red[(ks * 2 + 1) * 64 + L] = ssq;
         }
         __syncthreads();
+        QAM_STAMP(5);
         if (ks > 0) return;
         for (int k2 = 1; k2 < KS; ++k2) {
             part += red[(k2 * 2 + 0) * 64 + L];
@@ -501,6 +524,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     uint32_t prev = 0;
     if (L == 0) prev = __hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = __shfl(prev, 0);
+    QAM_STAMP(6);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (prev != (uint32_t)(a.n_chunks - 1)) return;
     double sum = 0.0;
@@ -520,7 +544,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
 // writes NaN outputs (no read of its planes).
 template <bool XBF16, int MAXW, bool EPI, bool LENS = false>
 __device__ __forceinline__ void run_unit(const Item& a, const Common& c, int local, int4* lds, int tid,
-                                         const LensMap* lm = nullptr) {
+                                         const LensMap* lm = nullptr, unsigned long long* tl_row = nullptr) {
     // per wave: kRegionInt4 int4 (the sub-chunk's limb words, then its column
     // sums); then, with several waves, [KS][2][64] fp64 row sums handed to wave 0
     const int KS = MAXW == 1 ? 1 : c.KS;
@@ -543,10 +567,10 @@ __device__ __forceinline__ void run_unit(const Item& a, const Common& c, int loc
         case 0:   // ZERO: nothing read, y = 0 (written once, by the first chunk's first wave)
             if (chunk == 0 && ks == 0) finish_zero<EPI>(a, b, L);
             return;
-        case 1: wave_body<1, XBF16, EPI>(a, c, mylds, b, chunk, L, ks, KS, red); return;
-        case 2: wave_body<2, XBF16, EPI>(a, c, mylds, b, chunk, L, ks, KS, red); return;
-        case 3: wave_body<3, XBF16, EPI>(a, c, mylds, b, chunk, L, ks, KS, red); return;
-        case 4: wave_body<4, XBF16, EPI>(a, c, mylds, b, chunk, L, ks, KS, red); return;
+        case 1: wave_body<1, XBF16, EPI>(a, c, mylds, b, chunk, L, ks, KS, red, tl_row); return;
+        case 2: wave_body<2, XBF16, EPI>(a, c, mylds, b, chunk, L, ks, KS, red, tl_row); return;
+        case 3: wave_body<3, XBF16, EPI>(a, c, mylds, b, chunk, L, ks, KS, red, tl_row); return;
+        case 4: wave_body<4, XBF16, EPI>(a, c, mylds, b, chunk, L, ks, KS, red, tl_row); return;
         default:   // not a rung of {0,2,4,6,8}: flag it, and write NaN once (no planes read)
             if (chunk == 0 && ks == 0) {
                 if (L == 0 && c.status) __hip_atomic_fetch_or(c.status, (uint32_t)QAM_STATUS_BAD_RUNG, __ATOMIC_RELAXED,
@@ -584,8 +608,23 @@ __global__ __launch_bounds__(64 * MAXW) void qmatvec_kernel(Item single, Common 
         const Item a = unit_item(c, (int)blockIdx.x);
         run_unit<XBF16, MAXW, false>(a, c, (int)blockIdx.x - a.wg_begin, lds, (int)threadIdx.x);
     } else {
+#ifdef QAM_TIMELINE
+        const unsigned long long t_entry = (unsigned long long)wall_clock64();
+#endif
         if (single.run_if != nullptr && *single.run_if == 0) return;   // predicated launch, not taken
-        run_unit<XBF16, MAXW, true>(single, c, (int)blockIdx.x, lds, (int)threadIdx.x);
+        unsigned long long* tl_row = nullptr;
+#ifdef QAM_TIMELINE
+        for (int i = 0; i < QAM_TIMELINE_SLOTS; ++i)
+            if (tl_select[i] != nullptr && tl_select[i] == (const void*)single.planes && blockIdx.x < QAM_TIMELINE_GROUPS)
+                tl_row = &tl_stamps[i][blockIdx.x][0][0];
+        const int tl_wave = (int)threadIdx.x >> 6;
+        if (tl_row != nullptr && (threadIdx.x & 63) == 0) tl_row[tl_wave * QAM_TIMELINE_POINTS] = t_entry;
+#endif
+        run_unit<XBF16, MAXW, true>(single, c, (int)blockIdx.x, lds, (int)threadIdx.x, nullptr, tl_row);
+#ifdef QAM_TIMELINE
+        if (tl_row != nullptr && (threadIdx.x & 63) == 0)
+            tl_row[tl_wave * QAM_TIMELINE_POINTS + 7] = (unsigned long long)wall_clock64();
+#endif
     }
 }
 
@@ -1088,4 +1127,40 @@ extern "C" int qam_qmatvec_group(const qam_group* group, hipStream_t s) {
     snprintf(v, sizeof(v), "qmatvec_staged_group items=%d B=1 wg=%lld", group->n_items, (long long)group->n_workgroups);
     set_variant(v);
     return QAM_OK;
+}
+
+extern "C" int qam_timeline_select(const void* const* planes, int n) {
+    clear_error();
+#ifdef QAM_TIMELINE
+    if (n < 0 || n > QAM_TIMELINE_SLOTS) QAM_FAIL(QAM_ERR_ARG, "timeline_select: n=%d outside [0, %d]", n, QAM_TIMELINE_SLOTS);
+    if (n > 0 && !planes) QAM_FAIL(QAM_ERR_NULL, "timeline_select: null planes");
+    const void* h[QAM_TIMELINE_SLOTS] = {};
+    for (int i = 0; i < n; ++i) h[i] = planes[i];
+    QAM_HIP_CHECK(hipDeviceSynchronize());
+    QAM_HIP_CHECK(hipMemcpyToSymbol(HIP_SYMBOL(qam::tl_select), h, sizeof h));
+    static const unsigned long long zero[QAM_TIMELINE_GROUPS * 8 * QAM_TIMELINE_POINTS] = {};
+    for (int i = 0; i < QAM_TIMELINE_SLOTS; ++i)
+        QAM_HIP_CHECK(hipMemcpyToSymbol(HIP_SYMBOL(qam::tl_stamps), zero, sizeof zero, i * sizeof zero));
+    return QAM_OK;
+#else
+    (void)planes;
+    (void)n;
+    QAM_FAIL(QAM_ERR_ARG, "timeline_select: this library was built without the timeline (QAM_TIMELINE)");
+#endif
+}
+
+extern "C" int qam_timeline_read(uint64_t* out, size_t n_words) {
+    clear_error();
+#ifdef QAM_TIMELINE
+    const size_t words = (size_t)QAM_TIMELINE_SLOTS * QAM_TIMELINE_GROUPS * 8 * QAM_TIMELINE_POINTS;
+    if (!out) QAM_FAIL(QAM_ERR_NULL, "timeline_read: null output");
+    if (n_words < words) QAM_FAIL(QAM_ERR_ARG, "timeline_read: %zu words < %zu", n_words, words);
+    QAM_HIP_CHECK(hipDeviceSynchronize());
+    QAM_HIP_CHECK(hipMemcpyFromSymbol(out, HIP_SYMBOL(qam::tl_stamps), words * sizeof(uint64_t)));
+    return QAM_OK;
+#else
+    (void)out;
+    (void)n_words;
+    QAM_FAIL(QAM_ERR_ARG, "timeline_read: this library was built without the timeline (QAM_TIMELINE)");
+#endif
 }

@@ -544,3 +544,23 @@ def test_group_refine_rejects_before_any_launch(lib):
     g.route = 1
     assert lib.qam_qmatvec_group_refine(C.byref(g), 0, None) == -3
     assert lib.qam_qmatvec_group_refine(C.byref(g), 4, None) == -3
+
+
+def test_timeline_calls_refuse_in_the_product_library(lib):
+    assert lib.qam_timeline_select(None, 0) == -3
+    assert lib.qam_timeline_read(None, 0) == -3
+    assert "without the timeline" in lib.qam_last_error().decode()
+
+
+def test_timeline_library_exports_and_checks_arguments():
+    path = os.path.join(ROOT, "query_adaptive_mixed_amd", "libqam_timeline.so")
+    if not os.path.exists(path):
+        pytest.skip("the timeline library is not built")
+    tl = L.load(path)
+    assert not [n for n in declared_functions() if not hasattr(tl, n)]
+    assert tl.qam_timeline_select(None, -1) == -3
+    assert tl.qam_timeline_select(None, L.QAM_TIMELINE_SLOTS + 1) == -3
+    assert tl.qam_timeline_select(None, 2) == -1
+    assert tl.qam_timeline_read(None, 1 << 30) == -1
+    small = (C.c_uint64 * 4)()
+    assert tl.qam_timeline_read(C.cast(small, C.c_void_p), 4) == -3
