@@ -38,7 +38,8 @@ CFLAGS = [
 # through copies on every ring step of the unrolled loop.
 EXTRA_FLAGS = {
     "qmm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-    "qmatvec.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # the single-matrix kernel's first 12 argument dwords arrive in scalar registers
+    "qmatvec.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-kernarg-preload-count=12"],
 }
 
 

@@ -598,34 +598,56 @@ __device__ __forceinline__ Item unit_item(const Common& c, int u) {
     return a;
 }
 
-// One workgroup per unit: a single matrix (descriptor by value; with its
-// epilogue) or a group (descriptor table, one lookup per workgroup; plain
-// stores, the only output a group's items have).
-template <bool GROUPED, bool XBF16, int MAXW>
-__global__ __launch_bounds__(64 * MAXW) void qmatvec_kernel(Item single, Common c) {
+// One workgroup per unit of a group (descriptor table, one lookup per
+// workgroup; plain stores, the only output a group's items have).
+template <bool XBF16, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void qmatvec_kernel(Common c) {
     extern __shared__ int4 lds[];
-    if constexpr (GROUPED) {
-        const Item a = unit_item(c, (int)blockIdx.x);
-        run_unit<XBF16, MAXW, false>(a, c, (int)blockIdx.x - a.wg_begin, lds, (int)threadIdx.x);
-    } else {
+    const Item a = unit_item(c, (int)blockIdx.x);
+    run_unit<XBF16, MAXW, false>(a, c, (int)blockIdx.x - a.wg_begin, lds, (int)threadIdx.x);
+}
+
+// One workgroup per unit of a single matrix, with its epilogue.  The fields
+// the first loads depend on come first, as scalars (the rest of the
+// descriptor follows by value): the compiler preloads them into scalar
+// registers at wave launch (-amdgpu-kernarg-preload-count), so a short,
+// dependent launch such as a decode step's issues its first loads without
+// waiting for the argument segment.  tiles_tpc = n_tiles | tpc << 16;
+// chunks_level_ks = n_chunks | (fixed_level + 1) << 16 | KS << 24.
+template <bool XBF16, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void qmatvec_single_kernel(const void* x, const uint8_t* planes, int64_t K,
+                                                                   int64_t plane_bytes, const int* run_if,
+                                                                   uint32_t tiles_tpc, uint32_t chunks_level_ks,
+                                                                   Item single, Common c) {
+    extern __shared__ int4 lds[];
 #ifdef QAM_TIMELINE
-        const unsigned long long t_entry = (unsigned long long)wall_clock64();
+    const unsigned long long t_entry = (unsigned long long)wall_clock64();
 #endif
-        if (single.run_if != nullptr && *single.run_if == 0) return;   // predicated launch, not taken
-        unsigned long long* tl_row = nullptr;
+    if (run_if != nullptr && *run_if == 0) return;   // predicated launch, not taken
+    Item a = single;
+    a.x = x;
+    a.planes = planes;
+    a.K = K;
+    a.plane_bytes = plane_bytes;
+    a.n_tiles = (int)(tiles_tpc & 0xFFFFu);
+    a.tpc = (int)(tiles_tpc >> 16);
+    a.n_chunks = (int)(chunks_level_ks & 0xFFFFu);
+    a.fixed_level = (int)((chunks_level_ks >> 16) & 0xFFu) - 1;
+    Common cc = c;
+    cc.KS = (int)(chunks_level_ks >> 24);
+    unsigned long long* tl_row = nullptr;
 #ifdef QAM_TIMELINE
-        for (int i = 0; i < QAM_TIMELINE_SLOTS; ++i)
-            if (tl_select[i] != nullptr && tl_select[i] == (const void*)single.planes && blockIdx.x < QAM_TIMELINE_GROUPS)
-                tl_row = &tl_stamps[i][blockIdx.x][0][0];
-        const int tl_wave = (int)threadIdx.x >> 6;
-        if (tl_row != nullptr && (threadIdx.x & 63) == 0) tl_row[tl_wave * QAM_TIMELINE_POINTS] = t_entry;
+    for (int i = 0; i < QAM_TIMELINE_SLOTS; ++i)
+        if (tl_select[i] != nullptr && tl_select[i] == (const void*)planes && blockIdx.x < QAM_TIMELINE_GROUPS)
+            tl_row = &tl_stamps[i][blockIdx.x][0][0];
+    const int tl_wave = (int)threadIdx.x >> 6;
+    if (tl_row != nullptr && (threadIdx.x & 63) == 0) tl_row[tl_wave * QAM_TIMELINE_POINTS] = t_entry;
 #endif
-        run_unit<XBF16, MAXW, true>(single, c, (int)blockIdx.x, lds, (int)threadIdx.x, nullptr, tl_row);
+    run_unit<XBF16, MAXW, true>(a, cc, (int)blockIdx.x, lds, (int)threadIdx.x, nullptr, tl_row);
 #ifdef QAM_TIMELINE
-        if (tl_row != nullptr && (threadIdx.x & 63) == 0)
-            tl_row[tl_wave * QAM_TIMELINE_POINTS + 7] = (unsigned long long)wall_clock64();
+    if (tl_row != nullptr && (threadIdx.x & 63) == 0)
+        tl_row[tl_wave * QAM_TIMELINE_POINTS + 7] = (unsigned long long)wall_clock64();
 #endif
-    }
 }
 
 // A group whose maps are built in the same launch: every unit computes its
@@ -684,30 +706,46 @@ Plan make_plan(int64_t N, int64_t K, int goal, int align) {
 
 // With events, the launch records them at the kernel's own start and end
 // (hipExtLaunchKernel), which times the kernel alone.
-template <bool GROUPED, int MAXW>
-static void launch_k(const Item& it, const Common& c, int64_t grid, int threads, size_t lds, hipStream_t s,
-                     hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
+template <int MAXW>
+static void launch_group_k(const Common& c, int64_t grid, int threads, size_t lds, hipStream_t s,
+                           hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr) {
     const dim3 g((unsigned)grid), b((unsigned)threads);
     if (e0 || e1) {
         if (c.x_bf16)
-            hipExtLaunchKernelGGL((qmatvec_kernel<GROUPED, true, MAXW>), g, b, (uint32_t)lds, s, e0, e1, 0u, it, c);
+            hipExtLaunchKernelGGL((qmatvec_kernel<true, MAXW>), g, b, (uint32_t)lds, s, e0, e1, 0u, c);
         else
-            hipExtLaunchKernelGGL((qmatvec_kernel<GROUPED, false, MAXW>), g, b, (uint32_t)lds, s, e0, e1, 0u, it, c);
+            hipExtLaunchKernelGGL((qmatvec_kernel<false, MAXW>), g, b, (uint32_t)lds, s, e0, e1, 0u, c);
         return;
     }
     if (c.x_bf16)
-        hipLaunchKernelGGL((qmatvec_kernel<GROUPED, true, MAXW>), g, b, lds, s, it, c);
+        hipLaunchKernelGGL((qmatvec_kernel<true, MAXW>), g, b, lds, s, c);
     else
-        hipLaunchKernelGGL((qmatvec_kernel<GROUPED, false, MAXW>), g, b, lds, s, it, c);
+        hipLaunchKernelGGL((qmatvec_kernel<false, MAXW>), g, b, lds, s, c);
+}
+
+template <int MAXW>
+static void launch_single_k(const Item& it, const Common& c, int64_t grid, int threads, size_t lds, hipStream_t s) {
+    const uint32_t tiles_tpc = (uint32_t)it.n_tiles | ((uint32_t)it.tpc << 16);
+    const uint32_t chunks_level_ks =
+        (uint32_t)it.n_chunks | ((uint32_t)(it.fixed_level + 1) << 16) | ((uint32_t)c.KS << 24);
+    const dim3 g((unsigned)grid), b((unsigned)threads);
+    if (c.x_bf16)
+        hipLaunchKernelGGL((qmatvec_single_kernel<true, MAXW>), g, b, lds, s, it.x, it.planes, it.K, it.plane_bytes,
+                           it.run_if, tiles_tpc, chunks_level_ks, it, c);
+    else
+        hipLaunchKernelGGL((qmatvec_single_kernel<false, MAXW>), g, b, lds, s, it.x, it.planes, it.K, it.plane_bytes,
+                           it.run_if, tiles_tpc, chunks_level_ks, it, c);
 }
 
 void launch_single(const Item& it, const Common& c, int64_t grid, hipStream_t s) {
+    // the packed launch fields (16 bits each for tiles, tpc and chunks: K <= QAM_MAX_K)
+    static_assert(QAM_MAX_K / kTileCols < 65536, "tile counts fit 16 bits");
     if (c.KS > 1) {   // several waves per (block, chunk)
         const size_t lds = (size_t)c.KS * lds_bytes_staged() + (size_t)c.KS * 2 * 64 * sizeof(double);
-        launch_k<false, 8>(it, c, grid, 64 * c.KS, lds, s);
+        launch_single_k<8>(it, c, grid, 64 * c.KS, lds, s);
         return;
     }
-    launch_k<false, 1>(it, c, grid, 64, lds_bytes_staged(), s);
+    launch_single_k<1>(it, c, grid, 64, lds_bytes_staged(), s);
 }
 
 // Host checks shared by the single and grouped entry points.
@@ -1104,9 +1142,8 @@ extern "C" int qam_group_launch_times(const qam_group* group, int n, float* ms_o
     clear_error();
     if (int rc = staged_group_ok(group, "group_launch_times")) return rc;
     const Common c = staged_common(group);
-    const Item none{};
     return time_launches(n, ms_out, s, [&](hipEvent_t e0, hipEvent_t e1) {
-        launch_k<true, 1>(none, c, group->n_workgroups, 64, group->lds_bytes, s, e0, e1);
+        launch_group_k<1>(c, group->n_workgroups, 64, group->lds_bytes, s, e0, e1);
     }, "group_launch_times");
 }
 
@@ -1120,8 +1157,7 @@ extern "C" int qam_qmatvec_group(const qam_group* group, hipStream_t s) {
     }
     if (int rc = staged_group_ok(group, "qmatvec_group")) return rc;
     const Common c = staged_common(group);
-    const Item none{};
-    launch_k<true, 1>(none, c, group->n_workgroups, 64, group->lds_bytes, s);
+    launch_group_k<1>(c, group->n_workgroups, 64, group->lds_bytes, s);
     QAM_HIP_CHECK(hipGetLastError());
     char v[128];
     snprintf(v, sizeof(v), "qmatvec_staged_group items=%d B=1 wg=%lld", group->n_items, (long long)group->n_workgroups);
