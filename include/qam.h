@@ -944,11 +944,14 @@ int qam_decoder_decode_gated_async(qam_decoder* dec, const float* inputs, int64_
  *              x' = rms(h);  u = W_gate_up x';  m = silu(u_gate) * u_up;
  *              h += W_down m;  x' = rms(h)
  *   logits = W_lm x'
- * each product a qam_qmatvec call at B (the pre-pass route for B >= 2,
- * every request's result independent of the others and of its slot), each
- * glue step one small row kernel: rms in fp64 over the row (x' = fl32(h /
- * sqrt(mean h^2 + eps))), h + y rounded once to fp32, silu(g) u in fp64
- * rounded once.
+ * each product a qam_qmatvec product at B (the pre-pass route for B >= 2,
+ * every request's result independent of the others and of its slot): rms in
+ * fp64 over the row (x' = fl32(h / sqrt(mean h^2 + eps))), h + y rounded
+ * once to fp32, silu(g) u in fp64 rounded once.  For B >= 2 the elementwise
+ * steps run inside the pre-pass of the product that consumes them (the
+ * residual add and norm, the q columns read in place, the gated product),
+ * so a layer is four products of two launches each; for B = 1 each is one
+ * small row kernel before its product.
  */
 typedef struct qam_verifier qam_verifier;   /* opaque host object */
 
@@ -964,20 +967,29 @@ int qam_verifier_create(qam_decoder* dec, int max_batch, void* dev_mem, size_t d
 /* (device) the verifier's buffers, row-major with B rows in use:
  *   QAM_VER_X [max_batch][hidden] inputs (read by op 0), QAM_VER_H [..][hidden],
  *   QAM_VER_QKV [..][q_dim + 2 kv_dim], QAM_VER_M [..][ffn],
- *   QAM_VER_XN [..][max(hidden, q_dim, ffn)] the next product's input,
- *   QAM_VER_LOGITS [..][vocab]; NULL for an unknown id. */
+ *   QAM_VER_XN [..][hidden] the last rms output,
+ *   QAM_VER_LOGITS [..][vocab],
+ *   QAM_VER_Y [..][max(hidden, 2 ffn)] the o, gate|up and down products'
+ *   output (rows packed with the product's row count as stride);
+ *   NULL for an unknown id. */
 #define QAM_VER_X      0
 #define QAM_VER_H      1
 #define QAM_VER_QKV    2
 #define QAM_VER_M      3
 #define QAM_VER_XN     4
 #define QAM_VER_LOGITS 5
+#define QAM_VER_Y      6
 float* qam_verifier_buffer(qam_verifier* v, int which);
 
 /* qam_verifier_run -- enqueue ops first .. first+count-1 of the batched
- *   chain for B requests (1 <= B <= max_batch) at `rung`: op 0 loads the
- *   inputs (h = x, x' = rms h), then per layer the four products with their
- *   glue (qkv, o, gate_up, down), then the head: 4 n_layers + 2 ops.
+ *   chain for B requests (1 <= B <= max_batch) at `rung`: 4 n_layers + 2
+ *   ops, each forming its product's input from the previous op's output:
+ *     op 0         h = x; x' = rms h
+ *     op 1 + 4l    (l > 0: h += y; x' = rms h) qkv = W_qkv x'
+ *     op 2 + 4l    y = W_o qkv[:, :q_dim]
+ *     op 3 + 4l    h += y; x' = rms h; y = W_gate_up x'
+ *     op 4 + 4l    m = silu(y_gate) y_up; y = W_down m
+ *     last         h += y; x' = rms h; logits = W_lm x'
  *   qam_verifier_step runs them all. */
 int qam_verifier_run(qam_verifier* v, int rung, int B, int first, int count, hipStream_t s);
 int qam_verifier_step(qam_verifier* v, int rung, int B, hipStream_t s);

@@ -129,7 +129,7 @@ class QamSpecStats(C.Structure):
                 ("emitted", C.c_int64)]
 
 
-QAM_VER_X, QAM_VER_H, QAM_VER_QKV, QAM_VER_M, QAM_VER_XN, QAM_VER_LOGITS = range(6)
+QAM_VER_X, QAM_VER_H, QAM_VER_QKV, QAM_VER_M, QAM_VER_XN, QAM_VER_LOGITS, QAM_VER_Y = range(7)
 
 
 class QamError(RuntimeError):

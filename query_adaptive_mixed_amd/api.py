@@ -812,7 +812,9 @@ class Verifier:
     draft-and-verify).  Write B inputs into ``x[:B]`` and call
     ``step(rung, B)``; ``logits[:B]`` holds the result.  ``run`` enqueues
     single ops of the chain (op 0 loads the inputs, then qkv, o, gate_up,
-    down per layer, then the head)."""
+    down per layer, then the head; each op forms its product's input from
+    the previous op's output: residual add and norm, the q columns, the
+    gated product)."""
 
     def __init__(self, dec: Decoder, max_batch: int):
         nbytes = int(L.lib().qam_verifier_bytes(C.byref(dec._desc), int(max_batch)))
@@ -833,7 +835,8 @@ class Verifier:
         self.hidden = self._buffer(L.QAM_VER_H, H)
         self.qkv = self._buffer(L.QAM_VER_QKV, Q + 2 * KV)
         self.m = self._buffer(L.QAM_VER_M, F)
-        self.xn_flat = self._buffer(L.QAM_VER_XN, max(H, Q, F)).reshape(-1)
+        self.xn_flat = self._buffer(L.QAM_VER_XN, H).reshape(-1)
+        self.y_flat = self._buffer(L.QAM_VER_Y, max(H, 2 * F)).reshape(-1)
         self.logits = self._buffer(L.QAM_VER_LOGITS, V)
 
     def _buffer(self, which: int, n: int) -> torch.Tensor:
@@ -841,8 +844,12 @@ class Verifier:
         return self.mem[off:off + 4 * n * self.max_batch].view(torch.float32).view(self.max_batch, n)
 
     def xn(self, B: int, n: int) -> torch.Tensor:
-        """The next product's input as [B, n] (rows packed with stride n)."""
+        """The last rms output as [B, n] (rows packed with stride n)."""
         return self.xn_flat[:B * n].view(B, n)
+
+    def y(self, B: int, n: int) -> torch.Tensor:
+        """The last o, gate|up or down product's output as [B, n]."""
+        return self.y_flat[:B * n].view(B, n)
 
     def run(self, rung: int, B: int, first: int, count: int = 1) -> None:
         L.check(L.lib().qam_verifier_run(self._h, int(rung), int(B), int(first), int(count), _stream_handle()))

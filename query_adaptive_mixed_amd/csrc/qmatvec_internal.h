@@ -227,6 +227,32 @@ bool mfma_route(int64_t B);
 size_t qam_mfma_workspace_bytes(int64_t N, int64_t K, int64_t B);
 int qmatvec_mfma(const void* x, int x_dtype, int64_t B, const qam_packed* packed, const uint8_t* level_map,
                  int per_request_maps, float* y, void* workspace, size_t workspace_bytes, hipStream_t s);
+// A transform the pre-pass route's pre-pass applies to fp32 x before
+// splitting it (the product itself reads only the limbs), so that a chain of
+// products needs no separate elementwise launches:
+//   kXStrided  row r of x starts at r ld;
+//   kXAddNorm  x is a residual h: v = h + add (fp32), written back into res
+//              (res may be x itself), then the RMS-normalised
+//              x' = fl32(v / sqrt(mean_k v^2 + eps)) (fp64), written to side;
+//              the row is taken in one column chunk;
+//   kXGated    x is a gate|up product's output, rows interleaved 32 gate / 32
+//              up per 64-row block, row stride ld:
+//              x'_j = fl32(silu(g_j) u_j) (fp64), written to side.
+// add, res and side rows have stride K.  The output y may be add, or x in
+// kXGated: the pre-pass has read them before the product writes y.
+enum XMode { kXPlain = 0, kXStrided = 1, kXAddNorm = 2, kXGated = 3 };
+struct XIn {
+    int mode = kXPlain;
+    int64_t ld = 0;
+    const float* add = nullptr;
+    float* res = nullptr;
+    float* side = nullptr;
+    double eps = 0.0;
+};
+// qam_qmatvec's pre-pass route with a shared map and an input transform
+// (x fp32; B in [2, 32]); workspace: at least qam_mfma_workspace_bytes.
+int qmatvec_mfma_in(const float* x, int64_t B, const qam_packed* packed, const uint8_t* level_map, float* y,
+                    const XIn& in, void* workspace, size_t workspace_bytes, hipStream_t s);
 size_t mfma_group_bytes(const qam_gemv_item* items, int n_items, int64_t B, const qam_tuning* t);
 int mfma_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dtype, int per_request_maps,
                     const qam_tuning* t, void* dev_mem, size_t dev_bytes, qam_group* out, hipStream_t s);

@@ -58,6 +58,13 @@ struct MItem {
     int n_blocks, n_tiles, tpc, n_chunks;
     int wg_begin;              // grouped launches: first product workgroup of this item
     int pre_begin;             // grouped launches: first pre-pass workgroup of this item
+    // the pre-pass's input transform (XMode; fp32 x; zero: plain x)
+    int x_mode;
+    int64_t x_ld;
+    const float* x_add;
+    float* x_res;
+    float* x_side;
+    double x_eps;
 };
 
 struct MCommon {
@@ -82,6 +89,36 @@ __device__ __forceinline__ int rung_of(const MItem& a, int r, int b) {
 
 // ------------------------------------------------------------------ x -> limbs
 
+// Columns c .. c+3 of request r's input, after the item's transform (for
+// kXAddNorm the values before scaling, v = h + add).
+template <bool XBF16>
+__device__ __forceinline__ float4 input4(const MItem& a, int r, int64_t c) {
+    if constexpr (XBF16) return x4_value<true>(load_x4_raw<true>(a.x, (int64_t)r * a.K + c));   // plain only
+    const float* xf = static_cast<const float*>(a.x);
+    switch (a.x_mode) {
+        case kXStrided:
+            return *reinterpret_cast<const float4*>(xf + (int64_t)r * a.x_ld + c);
+        case kXAddNorm: {
+            const float4 h = *reinterpret_cast<const float4*>(xf + (int64_t)r * a.K + c);
+            const float4 d = *reinterpret_cast<const float4*>(a.x_add + (int64_t)r * a.K + c);
+            return float4{h.x + d.x, h.y + d.y, h.z + d.z, h.w + d.w};
+        }
+        case kXGated: {
+            // x' = silu(g) u of gate|up rows 64 (c / 32) + c % 32 and + 32 (c % 4 == 0: one block)
+            const float* row = xf + (int64_t)r * a.x_ld + 64 * (c / 32) + c % 32;
+            const float4 g4 = *reinterpret_cast<const float4*>(row);
+            const float4 u4 = *reinterpret_cast<const float4*>(row + 32);
+            const double g[4] = {g4.x, g4.y, g4.z, g4.w}, u[4] = {u4.x, u4.y, u4.z, u4.w};
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (float)(g[i] / (1.0 + exp(-g[i])) * u[i]);
+            return float4{o[0], o[1], o[2], o[3]};
+        }
+        default:
+            return x4_value<XBF16>(load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + c));
+    }
+}
+
 // One workgroup of sixteen wavefronts per (column chunk, request slot
 // r < SS NH): the chunk's largest |x| sets the exponent; slots r >= B get zero
 // limbs.  The uncovered elements are listed in column order.  Columns go in
@@ -97,6 +134,7 @@ template <bool XBF16, bool GROUPED>
 __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommon c) {
     __shared__ float red_m[kPreThreads / 64];
     __shared__ float red_p[kPreThreads / 64];
+    __shared__ double red_s[kPreThreads / 64];
     __shared__ int wave_n[kPreThreads / 64];
     MItem a;
     int local;
@@ -117,8 +155,11 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
     const int ncol = min(a.tpc, a.n_tiles - t0) * 64;
     const int64_t col0 = (int64_t)t0 * 64;
     const bool live = r < B;
+    const int mode = a.x_mode;
+    const bool norm = mode == kXAddNorm;
     float m = 0.0f;
     float poison = 0.0f;   // 0 * x summed: NaN exactly when some x is not finite
+    double ssq = 0.0;      // norm transforms: sum of v^2 over the row
     float4 keep[kPreVec];
 #pragma unroll
     for (int j = 0; j < kPreVec; ++j) keep[j] = float4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -128,33 +169,47 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
             for (int j = 0; j < kPreVec; ++j) {
                 const int k = base + 4 * T + 4 * kPreThreads * j;
                 if (k < ncol) {
-                    const float4 v = x4_value<XBF16>(load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + k));
+                    const float4 v = input4<XBF16>(a, r, col0 + k);
                     if (base == 0) keep[j] = v;
                     m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
                     poison = __builtin_fmaf(v.x, 0.0f, poison);
                     poison = __builtin_fmaf(v.y, 0.0f, poison);
                     poison = __builtin_fmaf(v.z, 0.0f, poison);
                     poison = __builtin_fmaf(v.w, 0.0f, poison);
+                    if (norm)
+                        ssq += (double)v.x * (double)v.x + (double)v.y * (double)v.y + (double)v.z * (double)v.z +
+                               (double)v.w * (double)v.w;
                 }
             }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         m = fmaxf(m, __shfl_xor(m, o));
         poison += __shfl_xor(poison, o);
+        if (norm) ssq += __shfl_xor(ssq, o);
     }
     if (lane == 0) {
         red_m[wave] = m;
         red_p[wave] = poison;
+        red_s[wave] = ssq;
     }
     __syncthreads();
     m = red_m[0];
     poison = red_p[0];
+    ssq = red_s[0];
 #pragma unroll
     for (int w = 1; w < kPreThreads / 64; ++w) {
         m = fmaxf(m, red_m[w]);
         poison += red_p[w];
+        ssq += red_s[w];
     }
-    const bool nonfinite = poison != 0.0f;   // NaN compares unequal
+    // kXAddNorm: every value is scaled by inv (a positive factor, so the
+    // largest |x'| is the largest |v| scaled and rounded alike)
+    double inv = 1.0;
+    if (norm) {
+        inv = 1.0 / sqrt(ssq / (double)a.K + a.x_eps);
+        m = (float)((double)m * inv);
+    }
+    const bool nonfinite = poison != 0.0f || (norm && !(inv <= 1.7976931348623157e308));   // NaN compares unequal
     int e = 0;
     if (m > 0.0f) frexpf(m, &e);
     const XSplit sp = xsplit_of(e);
@@ -176,9 +231,19 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
                 r2[j][q] = 0.0f;
                 u[j][q] = false;
             }
+            float4 v = float4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (in && live) {
+                v = base == 0 ? keep[j] : input4<XBF16>(a, r, col0 + k);
+                const int64_t o = (int64_t)r * a.K + col0 + k;
+                if (norm) {   // the residual row, then the normalised input (each element is read
+                              // before it is written, by the same thread: res may be x)
+                    *reinterpret_cast<float4*>(a.x_res + o) = v;
+                    v = float4{(float)((double)v.x * inv), (float)((double)v.y * inv), (float)((double)v.z * inv),
+                               (float)((double)v.w * inv)};
+                }
+                if (mode == kXAddNorm || mode == kXGated) *reinterpret_cast<float4*>(a.x_side + o) = v;
+            }
             if (in && live && !nonfinite) {
-                const float4 v = base == 0 ? keep[j]
-                                           : x4_value<XBF16>(load_x4_raw<XBF16>(a.x, (int64_t)r * a.K + col0 + k));
                 split_elem(v.x, sp, wh[0], wl[0], r2[j][0], u[j][0]);
                 split_elem(v.y, sp, wh[1], wl[1], r2[j][1], u[j][1]);
                 split_elem(v.z, sp, wh[2], wl[2], r2[j][2], u[j][2]);
@@ -789,6 +854,54 @@ int qmatvec_mfma(const void* x, int x_dtype, int64_t B, const qam_packed* packed
     snprintf(v, sizeof(v), "qmatvec_mfma B=%lld maps=%s tpc=%d chunks=%d sets=%d colgroups=%d ksplit=%d",
              (long long)B, per_request_maps ? "per-request" : "shared", p.tpc, p.n_chunks, p.NH, p.NCG, p.KS);
     set_variant(v);
+    return QAM_OK;
+}
+
+// The pre-pass route with an input transform (internal: the verify chain).
+int qmatvec_mfma_in(const float* x, int64_t B, const qam_packed* packed, const uint8_t* level_map, float* y,
+                    const XIn& in, void* workspace, size_t workspace_bytes, hipStream_t s) {
+    if (!x || !packed || !packed->planes || !level_map || !y) QAM_FAIL(QAM_ERR_NULL, "qmatvec_in: null pointer");
+    if (B < 2 || B > QAM_MAX_BATCH_MFMA) QAM_FAIL(QAM_ERR_ARG, "qmatvec_in: B=%lld outside [2, %d]", (long long)B,
+                                                  QAM_MAX_BATCH_MFMA);
+    const int64_t N = packed->N, K = packed->K;
+    if (N <= 0 || K <= 0 || N % kRows || K % kTileCols || K > QAM_MAX_K || packed->n_blocks != N / kRows)
+        QAM_FAIL(QAM_ERR_SHAPE, "qmatvec_in: bad packed shape N=%lld K=%lld", (long long)N, (long long)K);
+    const bool norm = in.mode == kXAddNorm;
+    switch (in.mode) {
+        case kXPlain: break;
+        case kXStrided:
+            if (in.ld < K || in.ld % 4) QAM_FAIL(QAM_ERR_ARG, "qmatvec_in: row stride %lld", (long long)in.ld);
+            break;
+        case kXAddNorm:
+            if (!in.add || !in.res || !in.side) QAM_FAIL(QAM_ERR_NULL, "qmatvec_in: add-norm needs add, res, side");
+            if (!(in.eps >= 0.0)) QAM_FAIL(QAM_ERR_ARG, "qmatvec_in: eps must be >= 0");
+            break;
+        case kXGated:
+            if (!in.side) QAM_FAIL(QAM_ERR_NULL, "qmatvec_in: gated input needs side");
+            if (in.ld < 2 * K || in.ld % 4) QAM_FAIL(QAM_ERR_ARG, "qmatvec_in: row stride %lld", (long long)in.ld);
+            break;
+        default: QAM_FAIL(QAM_ERR_ARG, "qmatvec_in: unknown input mode %d", in.mode);
+    }
+    if (!aligned(x, 16) || !aligned(in.add, 16) || !aligned(in.res, 16) || !aligned(in.side, 16) || !aligned(y, 4))
+        QAM_FAIL(QAM_ERR_ALIGN, "qmatvec_in: inputs must be 16-byte aligned");
+    // the whole row in one chunk for the norm (its sum of squares comes first)
+    const MPlan p = norm ? mplan_goal(N, K, B, (int)(K / kTileCols), false, nullptr) : mplan(N, K, B, false);
+    if (norm && p.n_chunks != 1) QAM_FAIL(QAM_ERR_SHAPE, "qmatvec_in: the norm's row spans %d chunks", p.n_chunks);
+    if (int rc = check_workspace(workspace, workspace_bytes, p.total, "qmatvec_in")) return rc;
+    char* ws = static_cast<char*>(workspace);
+    char* limbs = ws + p.counters + p.partials;
+    MItem it = make_mitem(x, packed, level_map, y, 0, p, limbs, limbs + p.limbs, limbs + p.limbs + p.exps);
+    it.counters = reinterpret_cast<uint32_t*>(ws);
+    it.partials = p.partials ? reinterpret_cast<double*>(ws + p.counters) : nullptr;
+    it.x_mode = in.mode;
+    it.x_ld = in.ld;
+    it.x_add = in.add;
+    it.x_res = in.res;
+    it.x_side = in.side;
+    it.x_eps = in.eps;
+    const MCommon c = mcommon(B, p.NH, p.SS, p.NCG, p.KS, status_word(ws));
+    launch_mfma<false>(it, c, false, false, (int64_t)p.n_chunks * p.SS * p.NH, (int64_t)it.n_blocks * p.n_chunks, s);
+    QAM_HIP_CHECK(hipGetLastError());
     return QAM_OK;
 }
 

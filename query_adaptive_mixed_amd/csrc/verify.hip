@@ -59,12 +59,12 @@ __device__ double block_sum(double v, double* red) {
     return t;
 }
 
-enum GlueMode { kInit = 0, kCopyQ = 1, kAddNorm = 2, kGlu = 3 };
+enum GlueMode { kInit = 0, kAddNorm = 1, kGlu = 2 };
 
 struct GlueArgs {
-    const float* x;    // kInit: inputs [B][n]; kCopyQ: qkv [B][ld]; kAddNorm, kGlu: y [B][ld]
+    const float* x;    // kInit: inputs [B][n]; kAddNorm, kGlu: y [B][ld]
     float* h;          // residual [B][n] (kInit, kAddNorm)
-    float* out;        // kInit, kAddNorm, kCopyQ: x' [B][n]; kGlu: m [B][n]
+    float* out;        // kInit, kAddNorm: x' [B][n]; kGlu: m [B][n]
     int64_t n;         // row length written
     int64_t ld;        // row stride of x
     double eps;
@@ -76,10 +76,7 @@ __global__ void __launch_bounds__(kGlueThreads) glue_kernel(GlueArgs a) {
     __shared__ double red[kGlueThreads / 64];
     const int64_t r = blockIdx.x;
     const int64_t n = a.n;
-    if constexpr (MODE == kCopyQ) {
-        for (int64_t i = threadIdx.x; i < n; i += kGlueThreads) a.out[r * n + i] = a.x[r * a.ld + i];
-        return;
-    } else if constexpr (MODE == kGlu) {
+    if constexpr (MODE == kGlu) {
         // block b of the gate|up product: rows 64b..64b+31 gate, 64b+32..64b+63 up
         for (int64_t j = threadIdx.x; j < n; j += kGlueThreads) {
             const int64_t b = j / 32, i = j % 32;
@@ -199,7 +196,6 @@ int vlayout(const qam_decoder_desc* d, int max_batch, VLayout& lo) {
                                     (long long)sh[1]);
             ws = std::max(ws, need);
         }
-    const int64_t XW = std::max(std::max(H, Q), F);
     size_t off = 0;
     lo.ws = off;      off += up256(ws);
     lo.ws_bytes = up256(ws);
@@ -207,7 +203,7 @@ int vlayout(const qam_decoder_desc* d, int max_batch, VLayout& lo) {
     lo.h = off;       off += up256((size_t)B * H * 4);
     lo.qkv = off;     off += up256((size_t)B * (Q + 2 * KV) * 4);
     lo.m = off;       off += up256((size_t)B * F * 4);
-    lo.xn = off;      off += up256((size_t)B * XW * 4);
+    lo.xn = off;      off += up256((size_t)B * H * 4);
     lo.y = off;       off += up256((size_t)B * std::max(H, 2 * F) * 4);
     lo.logits = off;  off += up256((size_t)B * V * 4);
     lo.keys = off;    off += up256((size_t)(B + 1) * 8);
@@ -229,6 +225,38 @@ int product(qam_verifier* v, int rung, int B, const qam_packed& w, const float* 
     return qam_qmatvec(x, QAM_X_F32, B, &w, v->dec->maps[rung], 0, y, v->ws, v->ws_bytes, s);
 }
 
+// A product of the chain with its input's elementwise step: at B = 1 a glue
+// kernel and the staged product, from two requests on the pre-pass route's
+// pre-pass, which forms the product's input itself.
+int product_in(qam_verifier* v, int rung, int B, const qam_packed& w, const XIn& in, const float* x, float* y,
+               hipStream_t s) {
+    if (B > 1) return qmatvec_mfma_in(x, B, &w, v->dec->maps[rung], y, in, v->ws, v->ws_bytes, s);
+    const int64_t K = w.K;
+    int rc = QAM_OK;
+    switch (in.mode) {
+        case kXStrided:   // row stride is moot for one row
+            return product(v, rung, B, w, x, y, s);
+        case kXAddNorm:
+            rc = glue<kAddNorm>(v, B, in.add, in.res, in.side, K, K, s);
+            break;
+        case kXGated:
+            rc = glue<kGlu>(v, B, x, nullptr, in.side, K, in.ld, s);
+            break;
+        default:
+            return product(v, rung, B, w, x, y, s);
+    }
+    return rc ? rc : product(v, rung, B, w, in.side, y, s);
+}
+
+// The chain, op by op (n_layers L):
+//   op 0            h = x; xn = rmsnorm(h)
+//   op 1 + 4l       layer l > 0: h += y, xn = rmsnorm(h); then qkv = Wqkv xn
+//   op 2 + 4l       y = Wo q (q: the first q_dim columns of qkv)
+//   op 3 + 4l       h += y, xn = rmsnorm(h); y = Wgu xn
+//   op 4 + 4l       m = silu(gate) up of y; y = Wdown m
+//   op 4L + 1       h += y, xn = rmsnorm(h); logits = Whead xn
+// Each op forms its own input from the previous op's output, so the
+// elementwise steps ride in the products' pre-passes.
 int run_ops(qam_verifier* v, int rung, int B, int first, int count, hipStream_t s) {
     const int n_ops = 4 * v->dec->d.n_layers + 2;
     if (rung < 0 || rung > 4) QAM_FAIL(QAM_ERR_ARG, "verifier: rung %d outside 0..4", rung);
@@ -236,31 +264,35 @@ int run_ops(qam_verifier* v, int rung, int B, int first, int count, hipStream_t 
     if (first < 0 || count < 0 || first > n_ops || count > n_ops - first)
         QAM_FAIL(QAM_ERR_ARG, "verifier: ops [%d, %d) outside the chain of %d", first, first + count, n_ops);
     const int64_t H = v->H, Q = v->Q, KV = v->KV, F = v->F;
+    XIn add_norm;   // h += y, xn = rmsnorm(h)
+    add_norm.mode = kXAddNorm;
+    add_norm.add = v->y;
+    add_norm.res = v->h;
+    add_norm.side = v->xn;
+    add_norm.eps = v->dec->d.eps;
+    XIn strided_q;
+    strided_q.mode = kXStrided;
+    strided_q.ld = Q + 2 * KV;
+    XIn gated;
+    gated.mode = kXGated;
+    gated.ld = 2 * F;
+    gated.side = v->m;
     for (int op = first; op < first + count; ++op) {
         int rc = QAM_OK;
         if (op == 0) {
             rc = glue<kInit>(v, B, v->x, v->h, v->xn, H, H, s);
         } else if (op == n_ops - 1) {
-            rc = product(v, rung, B, v->dec->d.lm_head, v->xn, v->logits, s);
+            rc = product_in(v, rung, B, v->dec->d.lm_head, add_norm, v->h, v->logits, s);
         } else {
             const qam_decoder_layer& L = v->dec->layers[(size_t)(op - 1) / 4];
             switch ((op - 1) % 4) {
                 case 0:
-                    rc = product(v, rung, B, L.qkv, v->xn, v->qkv, s);
-                    if (!rc) rc = glue<kCopyQ>(v, B, v->qkv, nullptr, v->xn, Q, Q + 2 * KV, s);
+                    rc = op == 1 ? product(v, rung, B, L.qkv, v->xn, v->qkv, s)
+                                 : product_in(v, rung, B, L.qkv, add_norm, v->h, v->qkv, s);
                     break;
-                case 1:
-                    rc = product(v, rung, B, L.o, v->xn, v->y, s);
-                    if (!rc) rc = glue<kAddNorm>(v, B, v->y, v->h, v->xn, H, H, s);
-                    break;
-                case 2:
-                    rc = product(v, rung, B, L.gate_up, v->xn, v->y, s);
-                    if (!rc) rc = glue<kGlu>(v, B, v->y, nullptr, v->m, F, 2 * F, s);
-                    break;
-                default:
-                    rc = product(v, rung, B, L.down, v->m, v->y, s);
-                    if (!rc) rc = glue<kAddNorm>(v, B, v->y, v->h, v->xn, H, H, s);
-                    break;
+                case 1: rc = product_in(v, rung, B, L.o, strided_q, v->qkv, v->y, s); break;
+                case 2: rc = product_in(v, rung, B, L.gate_up, add_norm, v->h, v->y, s); break;
+                default: rc = product_in(v, rung, B, L.down, gated, v->y, v->y, s); break;
             }
         }
         if (rc) return rc;
@@ -330,6 +362,7 @@ extern "C" float* qam_verifier_buffer(qam_verifier* v, int which) {
         case QAM_VER_M: return v->m;
         case QAM_VER_XN: return v->xn;
         case QAM_VER_LOGITS: return v->logits;
+        case QAM_VER_Y: return v->y;
         default: return nullptr;
     }
 }

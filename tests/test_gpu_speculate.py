@@ -60,24 +60,19 @@ def rms_tol(ref):
     return 2.0 ** -23 * np.abs(ref) + 1e-30
 
 
-def glu_check(m_gpu, W, sc, x, lv, what):
-    """silu(g) u from the two fp32-rounded halves: each half carries its
-    product bound plus its own fp32 rounding into silu(g) u (|silu'| <= 1.1)."""
-    idx = np.arange(W.shape[0]).reshape(-1, 64)
-    gr, ur = idx[:, :32].reshape(-1), idx[:, 32:].reshape(-1)
-    v = O.qmatvec_ref(W, sc, x, lv)
-    t = O.qmatvec_tolerance(W, sc, x, lv)
-    g, u = v[:, gr], v[:, ur]
-    tg = t[:, gr] + 2.0 ** -24 * np.abs(g)
-    tu = t[:, ur] + 2.0 ** -24 * np.abs(u)
-    m = O.silu_mul_ref(g, u)
-    silu = g / (1.0 + np.exp(-g))
-    tol = 1.1 * tg * (np.abs(u) + tu) + np.abs(silu) * tu + 2.0 ** -23 * np.abs(m) + 1e-30
-    within(m_gpu, m, tol, what)
+def add_norm_check(ver, B, H, h, y, what):
+    """h += y and xn = rmsnorm(h), the step that opens a product's input."""
+    hn = host(ver.hidden[:B])
+    assert np.array_equal(hn, (h.astype(np.float32) + y.astype(np.float32))), (what, "residual")
+    within(host(ver.xn(B, H)), O.rmsnorm_ref(hn.astype(np.float64), EPS), rms_tol(O.rmsnorm_ref(hn, EPS)),
+           (what, "norm"))
+    return host(ver.xn(B, H)).astype(np.float64)
 
 
 def check_chain(qam, ver, fld, cfg, rung, B, X, head_rows=None):
-    """Run the batched chain one op at a time; check every op on its actual inputs."""
+    """Run the batched chain one op at a time; check every op on its actual
+    inputs: each op forms its input (residual add and norm, the q columns,
+    the gated product) from the previous op's output, then multiplies."""
     H, Q, F = cfg["hidden"], cfg["q_dim"], cfg["ffn"]
     mats, (Wl, sl) = fused_weights(fld, cfg["n_layers"])
     lv_of = lambda W: np.full(W.shape[0] // 64, rung, np.uint8)
@@ -85,36 +80,36 @@ def check_chain(qam, ver, fld, cfg, rung, B, X, head_rows=None):
     ver.run(rung, B, 0)
     assert np.array_equal(host(ver.hidden[:B]), X)
     within(host(ver.xn(B, H)), O.rmsnorm_ref(X.astype(np.float64), EPS), rms_tol(O.rmsnorm_ref(X, EPS)), "init")
+    xn = host(ver.xn(B, H)).astype(np.float64)
     op = 1
     for l in range(cfg["n_layers"]):
         (Wqkv, sqkv), (Wo, so), (Wgu, sgu), (Wd, sd) = mats[l]
-        xn = host(ver.xn(B, H)).astype(np.float64)
+        if l > 0:
+            h, y = host(ver.hidden[:B]), host(ver.y(B, H))
         ver.run(rung, B, op); op += 1
+        if l > 0:
+            xn = add_norm_check(ver, B, H, h, y, (l, "down residual"))
         within(host(ver.qkv[:B]), O.qmatvec_ref(Wqkv, sqkv, xn, lv_of(Wqkv)),
                O.qmatvec_tolerance(Wqkv, sqkv, xn, lv_of(Wqkv)), (l, "qkv"))
-        q = host(ver.xn(B, Q))
-        assert np.array_equal(q, host(ver.qkv[:B])[:, :Q]), (l, "q copy")
-        h = host(ver.hidden[:B]).astype(np.float64)
+        q = host(ver.qkv[:B])[:, :Q].astype(np.float64)
         ver.run(rung, B, op); op += 1
-        v = O.qmatvec_ref(Wo, so, q.astype(np.float64), lv_of(Wo))
-        hn = host(ver.hidden[:B])
-        within(hn, h + v, O.qmatvec_tolerance(Wo, so, q, lv_of(Wo)) + 2.0 ** -23 * (np.abs(h) + np.abs(v)), (l, "o"))
-        within(host(ver.xn(B, H)), O.rmsnorm_ref(hn.astype(np.float64), EPS), rms_tol(O.rmsnorm_ref(hn, EPS)),
-               (l, "o norm"))
-        xn = host(ver.xn(B, H)).astype(np.float64)
+        within(host(ver.y(B, H)), O.qmatvec_ref(Wo, so, q, lv_of(Wo)), O.qmatvec_tolerance(Wo, so, q, lv_of(Wo)),
+               (l, "o"))
+        h, y = host(ver.hidden[:B]), host(ver.y(B, H))
         ver.run(rung, B, op); op += 1
-        glu_check(host(ver.m[:B]), Wgu, sgu, xn, lv_of(Wgu), (l, "gate_up"))
+        xn = add_norm_check(ver, B, H, h, y, (l, "o residual"))
+        within(host(ver.y(B, 2 * F)), O.qmatvec_ref(Wgu, sgu, xn, lv_of(Wgu)),
+               O.qmatvec_tolerance(Wgu, sgu, xn, lv_of(Wgu)), (l, "gate_up"))
+        gu = host(ver.y(B, 2 * F)).astype(np.float64).reshape(B, -1, 2, 32)
+        ver.run(rung, B, op); op += 1
+        m_ref = O.silu_mul_ref(gu[:, :, 0, :], gu[:, :, 1, :]).reshape(B, F)
+        within(host(ver.m[:B]), m_ref, 2.0 ** -23 * np.abs(m_ref) + 1e-30, (l, "gated"))
         mm = host(ver.m[:B]).astype(np.float64)
-        h = host(ver.hidden[:B]).astype(np.float64)
-        ver.run(rung, B, op); op += 1
-        v = O.qmatvec_ref(Wd, sd, mm, lv_of(Wd))
-        hn = host(ver.hidden[:B])
-        within(hn, h + v, O.qmatvec_tolerance(Wd, sd, mm, lv_of(Wd)) + 2.0 ** -23 * (np.abs(h) + np.abs(v)),
+        within(host(ver.y(B, H)), O.qmatvec_ref(Wd, sd, mm, lv_of(Wd)), O.qmatvec_tolerance(Wd, sd, mm, lv_of(Wd)),
                (l, "down"))
-        within(host(ver.xn(B, H)), O.rmsnorm_ref(hn.astype(np.float64), EPS), rms_tol(O.rmsnorm_ref(hn, EPS)),
-               (l, "down norm"))
-    xn = host(ver.xn(B, H)).astype(np.float64)
+    h, y = host(ver.hidden[:B]), host(ver.y(B, H))
     ver.run(rung, B, op)
+    xn = add_norm_check(ver, B, H, h, y, "head residual")
     rows = np.arange(Wl.shape[0]) if head_rows is None else head_rows
     blocks = np.unique(rows // 64)
     sub = np.concatenate([np.arange(64 * b, 64 * b + 64) for b in blocks])
@@ -124,7 +119,7 @@ def check_chain(qam, ver, fld, cfg, rung, B, X, head_rows=None):
     return host(ver.logits[:B]).copy()
 
 
-@pytest.mark.parametrize("B", [1, 3, 8])
+@pytest.mark.parametrize("B", [1, 2, 3, 8])
 @pytest.mark.parametrize("rung", [2, 4])
 def test_verifier_chain_matches_oracle(qam, rung, B):
     fld, dec, ver = make(qam, SMALL)
