@@ -486,11 +486,17 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   one is computed instead in fp32 on the vector ALUs (each lane sums at
  *   most 256 products c x, one rounding per fused multiply-add, and the lane
  *   sums meet in fp64: relative error at most 2^-16 of that sub-chunk's
- *   sum |w||x|).  Every element therefore enters the sum with relative error
- *   at most 2^-15, and for every finite x and every code
+ *   sum |w||x|).  On the pre-pass route a (chunk, request) whose coarse split
+ *   (q1, then one digit q2c = round(r1 2^(29-e)), r2c = r1 - q2c 2^(e-29),
+ *   |r2c| <= 2^(e-30)) leaves at most 4 elements with |r2c| > 2^-15 |x|
+ *   multiplies four limb columns instead of six, and those elements' c * r2c
+ *   are added exactly instead.  Every element therefore enters the sum with
+ *   relative error at most 2^-15, and for every finite x and every code
  *     |y - y_exact| <= 2^-15 sum_k |w_k||x_k| + 2^-24 |y_exact| (+ fp64 sums),
  *   inside 1e-4 sum|w||x|.  Chunks are summed in fp64 in a fixed order and
- *   y = fl32(scale * sum): results are bit-reproducible run to run.
+ *   y = fl32(scale * sum): results are bit-reproducible run to run (for one
+ *   launch plan: x's split is per column chunk, so plans that chunk K
+ *   differently can differ in the last bits).
  *   Integer-valued x with |x| < 2^22 and scale 1 gives exact integer
  *   outputs; a D8 map gives the untruncated int8 product.  A non-finite x
  *   makes that request's non-ZERO outputs NaN.
@@ -500,7 +506,7 @@ int qam_map_weight_bytes(const uint8_t* level, int64_t n_blocks, int64_t K,
  *   rebuilt codes (four int8x4 words per 16-byte slice word, 16 rows x 64
  *   columns per lane group) by them, B-operand column l holding limb l.
  *   B = 2 .. 32, the pre-pass route: a pre-pass writes the limbs of x per
- *   column chunk as MFMA B operands (six columns per request, up to 16
+ *   column chunk as MFMA B operands (four or six columns per request, up to 16
  *   requests per set) and lists each chunk's uncovered elements, then the
  *   product kernel multiplies the codes by them.  With per-request maps a
  *   block is read once, to the deepest slice any request needs, and each

@@ -70,6 +70,7 @@ __device__ __forceinline__ int level_of(const uint8_t* level, int b) {
 constexpr int kLimbCols = 6;       // B-operand columns per request
 constexpr int kHiShift = 22;       // q1 = x 2^(22-e)
 constexpr int kLoShift = 45;       // q2 = r1 2^(45-e)
+constexpr int kCoarseShift = 29;   // coarse lo digit: q2c = r1 2^(29-e), |q2c| <= 64
 constexpr int kSmallExp = -81;     // below this exponent the chunk is prescaled
 constexpr int kPrescale = 100;     // by 2^100
 
@@ -79,6 +80,7 @@ struct XSplit {
     float pre;                     // 1 or 2^100
     float scale_hi, step_hi;       // 2^(22-e'), 2^(e'-22)
     float scale_lo, step_lo;       // 2^(45-e'), 2^(e'-45)
+    float scale_c, step_c;         // 2^(29-e'), 2^(e'-29): the coarse lo digit
 };
 
 __device__ __forceinline__ XSplit xsplit_of(int e) {
@@ -90,6 +92,8 @@ __device__ __forceinline__ XSplit xsplit_of(int e) {
     s.step_hi = pow2f(ep - kHiShift);
     s.scale_lo = pow2f(kLoShift - ep);
     s.step_lo = pow2f(ep - kLoShift);
+    s.scale_c = pow2f(kCoarseShift - ep);
+    s.step_c = pow2f(ep - kCoarseShift);
     return s;
 }
 
@@ -113,6 +117,36 @@ __device__ __forceinline__ void split_elem(float v, const XSplit& s, uint32_t& w
     w_lo = limb_word_of(t2);
     r2 = __builtin_fmaf(-(t2 - kMagic), s.step_lo, r1);
     unc = fabsf(r2) > fabsf(v) * 0x1p-15f;
+}
+
+// The coarse split of one element (the pre-pass route's common case): the
+// same hi part, then ONE lo digit q2c = rint(r1 2^(29-e)) (|q2c| <= 64, so a
+// single balanced int8 digit), r2c = r1 - q2c 2^(e-29) exact, |r2c| <= 2^(e-30).
+// w_lo holds q2c in byte 2 and zeros in bytes 0 and 1, so that the six-column
+// arithmetic below reads it as the lo part 65536 q2c 2^(e-45) = q2c 2^(e-29).
+// An element with |r2c| > 2^-15 |x| (possible only when |x| < 2^(e-15)) is
+// uncovered.
+__device__ __forceinline__ void split_coarse(float v, const XSplit& s, uint32_t& w_hi, uint32_t& w_lo, float& r2,
+                                             bool& unc) {
+    constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
+    v = v * s.pre;
+    const float t1 = __builtin_fmaf(v, s.scale_hi, kMagic);
+    w_hi = limb_word_of(t1);
+    const float r1 = __builtin_fmaf(-(t1 - kMagic), s.step_hi, v);
+    const float tc = __builtin_fmaf(r1, s.scale_c, kMagic);
+    w_lo = limb_word_of(tc) << 16;
+    r2 = __builtin_fmaf(-(tc - kMagic), s.step_c, r1);
+    unc = fabsf(r2) > fabsf(v) * 0x1p-15f;
+}
+
+// Whether the coarse split leaves one element uncovered (the count decides a
+// chunk's columns before any is written).
+__device__ __forceinline__ bool coarse_uncovered(float v, const XSplit& s) {
+    uint32_t wh, wl;
+    float r2;
+    bool unc;
+    split_coarse(v, s, wh, wl, r2, unc);
+    return unc;
 }
 
 // The fp64 value of one request's six column sums (hi limbs s[0..2], lo

@@ -11,17 +11,22 @@
 // of the requests at that depth.
 //
 // Arithmetic (exact, as in the batch-1 kernel; qmatvec_internal.h): a
-// pre-pass turns each request's x, per column chunk, into the hi and lo
-// 24-bit fixed-point parts, three int8 limbs each, laid out as B operands of
-// v_mfma_i32_16x16x64_i8: column c = 6 rr + l of a request set (16 requests
-// at most) holds limb l of request rr (hi 0..2, lo 0..2), 16 columns per
-// MFMA (NCG column groups per set, up to 6); it also lists the chunk's
-// uncovered elements (relative error above 2^-15 after the two parts) with
-// their exact residuals.  Codes are the A operands (16 rows x 64 columns,
-// exactly the words a lane loads); i32 accumulation is exact; the six
-// columns of a request are combined in fp64 after the chunk, through an LDS
-// table of the block's 64 x 16 NCG integer sums, and the listed residuals
-// are added with their codes in fp64.
+// pre-pass turns each request's x, per column chunk, into int8 limbs laid out
+// as B operands of v_mfma_i32_16x16x64_i8, 16 columns per MFMA, and lists the
+// chunk's uncovered elements (relative error above 2^-15) with their exact
+// residuals.  A (chunk, request) is "coarse" when the coarse split (the hi
+// part's three limbs and one lo digit, 32 bits of fixed point) leaves at most
+// kCoarseListMax elements uncovered, else "fine" (the hi part and the full
+// 24-bit lo part, 48 bits).  A set of SS requests has NCGC coarse column
+// groups (column 4 rr + l: hi limbs 0..2, then the lo digit of weight 2^16,
+// which is the coarse digit or the fine part's top digit) and NCGF fine ones
+// (column 2 rr + l: the fine part's low digits 0 and 1, zero for a coarse
+// request).  A (chunk, set) whose requests are all coarse multiplies only its
+// coarse groups: 4 columns per request instead of 6.  Codes are the A
+// operands (16 rows x 64 columns, exactly the words a lane loads); i32
+// accumulation is exact; a request's columns are combined in fp64 after the
+// chunk, through an LDS table of the block's 64 x 16 NCG integer sums, and the
+// listed residuals are added with their codes in fp64.
 //
 // A workgroup is one (block, column chunk): wave (ks, h) serves request set h
 // on the chunk's tiles ks, ks + KS, ...; the KS waves of a set add their sums
@@ -38,7 +43,19 @@ namespace qam {
 typedef __attribute__((address_space(1))) const v4i global_v4i;
 
 constexpr int kBadExp = 0x7FFFFFFF;   // exponent marker of a chunk of x with a non-finite value
-constexpr int kMaxNCG = 6;            // 16 requests x 6 limb columns
+constexpr int kMaxNCG = 6;            // 16 requests: 4 coarse + 2 fine column groups
+constexpr int kCoarseCols = 4;        // coarse B-operand columns per request
+constexpr int kFineCols = 2;          // fine B-operand columns per request
+constexpr int kCoarseListMax = 4;     // most coarse-uncovered elements a coarse (chunk, request) lists
+constexpr int kFineFlag = 1 << 30;    // unc_count bit: the (chunk, request) is fine
+
+// Column groups of a set of SS requests: coarse, fine, both.
+__host__ __device__ constexpr int ncgc_of_ss(int ss) { return (kCoarseCols * ss + 15) / 16; }
+__host__ __device__ constexpr int ncgf_of_ss(int ss) { return (kFineCols * ss + 15) / 16; }
+__host__ __device__ constexpr int ncg_of_ss(int ss) { return ncgc_of_ss(ss) + ncgf_of_ss(ss); }
+// The coarse groups of a total of NCG (every set size gives a distinct total:
+// 1-4 requests 1 + 1, 5-8 2 + 1, 9-12 3 + 2, 13-16 4 + 2).
+__host__ __device__ constexpr int ncgc_of_ncg(int ncg) { return ncg == 2 ? 1 : ncg == 3 ? 2 : ncg == 5 ? 3 : 4; }
 
 struct MItem {
     const uint8_t* planes;
@@ -74,9 +91,10 @@ struct MCommon {
     uint32_t* status;          // the call's status word
     int B;
     int NH;                    // request sets per workgroup
-    int SS;                    // requests per set (<= 16; 6 SS limb columns in NCG groups of 16)
+    int SS;                    // requests per set (<= 16)
     int KS;                    // waves per request set splitting a chunk's tiles
-    int NCG;                   // 16-column groups per request set
+    int NCG;                   // 16-column groups per request set (coarse, then fine)
+    int NCGC;                  // coarse groups among them
     int first;                 // refinement launches: slices below this are not read, and y is added to
 };
 
@@ -213,7 +231,34 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
     int e = 0;
     if (m > 0.0f) frexpf(m, &e);
     const XSplit sp = xsplit_of(e);
+    // Coarse or fine: count the elements the coarse split leaves uncovered
+    // (the first round's values are still in registers).
+    int ccount = 0;
+    if (live && !nonfinite)
+        for (int base = 0; base < ncol; base += kPreRound)
+#pragma unroll
+            for (int j = 0; j < kPreVec; ++j) {
+                const int k = base + 4 * T + 4 * kPreThreads * j;
+                if (k < ncol) {
+                    float4 v = base == 0 ? keep[j] : input4<XBF16>(a, r, col0 + k);
+                    if (norm)
+                        v = float4{(float)((double)v.x * inv), (float)((double)v.y * inv),
+                                   (float)((double)v.z * inv), (float)((double)v.w * inv)};
+                    ccount += (int)coarse_uncovered(v.x, sp) + (int)coarse_uncovered(v.y, sp) +
+                              (int)coarse_uncovered(v.z, sp) + (int)coarse_uncovered(v.w, sp);
+                }
+            }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ccount += __shfl_xor(ccount, o);
+    if (lane == 0) wave_n[wave] = ccount;
+    __syncthreads();
+    ccount = 0;
+#pragma unroll
+    for (int w = 0; w < kPreThreads / 64; ++w) ccount += wave_n[w];
+    __syncthreads();   // wave_n is written again by the listing
+    const bool fine = ccount > kCoarseListMax;
     const int h = r / SS, rr = r % SS;
+    const int NCGC = c.NCGC;
     uint8_t* lb = reinterpret_cast<uint8_t*>(a.limbs);
     int2* list = a.unc + (int64_t)(chunk * slots + r) * a.tpc * 64;
     int listed = 0;
@@ -244,24 +289,33 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
                 if (mode == kXAddNorm || mode == kXGated) *reinterpret_cast<float4*>(a.x_side + o) = v;
             }
             if (in && live && !nonfinite) {
-                split_elem(v.x, sp, wh[0], wl[0], r2[j][0], u[j][0]);
-                split_elem(v.y, sp, wh[1], wl[1], r2[j][1], u[j][1]);
-                split_elem(v.z, sp, wh[2], wl[2], r2[j][2], u[j][2]);
-                split_elem(v.w, sp, wh[3], wl[3], r2[j][3], u[j][3]);
+                if (fine) {
+                    split_elem(v.x, sp, wh[0], wl[0], r2[j][0], u[j][0]);
+                    split_elem(v.y, sp, wh[1], wl[1], r2[j][1], u[j][1]);
+                    split_elem(v.z, sp, wh[2], wl[2], r2[j][2], u[j][2]);
+                    split_elem(v.w, sp, wh[3], wl[3], r2[j][3], u[j][3]);
+                } else {
+                    split_coarse(v.x, sp, wh[0], wl[0], r2[j][0], u[j][0]);
+                    split_coarse(v.y, sp, wh[1], wl[1], r2[j][1], u[j][1]);
+                    split_coarse(v.z, sp, wh[2], wl[2], r2[j][2], u[j][2]);
+                    split_coarse(v.w, sp, wh[3], wl[3], r2[j][3], u[j][3]);
+                }
             }
             if (in) {
                 const int64_t kk = col0 + k;   // columns kk .. kk+3: one tile, one 16-column slice
                 const int64_t t = kk >> 6;
                 const int kg = (int)((kk & 63) >> 4);
                 const int byte = (int)(kk & 15);
+                // digits: hi 0..2 and lo 2 to coarse columns 4 rr + 0..3, lo 0..1 to fine columns 2 rr + 0..1
 #pragma unroll
-                for (int l = 0; l < kLimbCols; ++l) {
-                    const int col = kLimbCols * rr + l;   // B-operand column of this limb
-                    const int sh = 8 * (l % 3);
+                for (int l = 0; l < kCoarseCols + kFineCols; ++l) {
                     const uint32_t* w = l < 3 ? wh : wl;
+                    const int sh = l < 3 ? 8 * l : l == 3 ? 16 : 8 * (l - 4);
+                    const int col = l < kCoarseCols ? kCoarseCols * rr + l : kFineCols * rr + (l - kCoarseCols);
+                    const int grp = l < kCoarseCols ? col >> 4 : NCGC + (col >> 4);
                     const uint32_t word = ((w[0] >> sh) & 0xFFu) | (((w[1] >> sh) & 0xFFu) << 8) |
                                           (((w[2] >> sh) & 0xFFu) << 16) | (((w[3] >> sh) & 0xFFu) << 24);
-                    const int64_t unit = ((t * NH + h) * NCG + (col >> 4)) * 64 + kg * 16 + (col & 15);
+                    const int64_t unit = ((t * NH + h) * NCG + grp) * 64 + kg * 16 + (col & 15);
                     *reinterpret_cast<uint32_t*>(lb + unit * 16 + byte) = word;
                 }
             }
@@ -302,22 +356,22 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
     }
     if (T == 0) {
         a.exps[chunk * slots + r] = nonfinite ? kBadExp : e;
-        a.unc_count[chunk * slots + r] = live && !nonfinite ? listed : 0;
+        a.unc_count[chunk * slots + r] = live && !nonfinite ? (listed | (fine ? kFineFlag : 0)) : 0;
     }
 }
 
 // ------------------------------------------------------------------ product
 
-// Tiles in flight: two halves of H tiles, each tile NS weight loads and NCG
-// limb loads per lane.
-template <int NS, int NCG>
+// Tiles in flight: two halves of H tiles, each tile NS weight loads and NG
+// limb loads per lane (NG: the column groups multiplied, coarse or all).
+template <int NS, int NG>
 struct MRing {
-    static constexpr int H = NS + NCG <= 4 ? 2 : 1;
+    static constexpr int H = NS + NG <= 4 ? 2 : 1;
     static constexpr int PF = 2 * H;
 };
 
-template <int NS, int NCG, int H>
-__device__ __forceinline__ void mload(u32x4 (&w)[H][NS], v4i (&x)[H][NCG], const uint8_t* wbase, int64_t pb,
+template <int NS, int NG, int H>
+__device__ __forceinline__ void mload(u32x4 (&w)[H][NS], v4i (&x)[H][NG], const uint8_t* wbase, int64_t pb,
                                       int64_t wstride, const v4i* xbase, int64_t xstride, int tile, int last,
                                       int first) {
 #pragma unroll
@@ -327,16 +381,18 @@ __device__ __forceinline__ void mload(u32x4 (&w)[H][NS], v4i (&x)[H][NCG], const
         for (int p = 0; p < NS; ++p)
             w[u][p] = p < first ? u32x4{0u, 0u, 0u, 0u} : load_plane(wbase + p * pb + (int64_t)t * wstride);
 #pragma unroll
-        for (int g = 0; g < NCG; ++g) x[u][g] = *(global_v4i*)(xbase + t * xstride + g * 64);
+        for (int g = 0; g < NG; ++g) x[u][g] = *(global_v4i*)(xbase + t * xstride + g * 64);
     }
 }
 
 // One tile: for each depth d present among the set's requests, the codes at
 // depth d times the limbs of the requests reading d (mcol[g]: depth of the
 // request owning this lane's column in group g; gmask[g]: the depths present
-// in group g, so a group with no request at d costs no MFMA there).
-template <int NS, int NCG, bool PER_REQ>
-__device__ __forceinline__ void mtile(const u32x4 (&w)[NS], const v4i (&xl)[NCG], const int (&mcol)[NCG],
+// in group g, so a group with no request at d costs no MFMA there); with a
+// shared map, the codes at the block's depth NS times every limb.  The first
+// NG column groups are multiplied (the coarse ones, or all).
+template <int NS, int NCG, int NG, bool PER_REQ>
+__device__ __forceinline__ void mtile(const u32x4 (&w)[NS], const v4i (&xl)[NG], const int (&mcol)[NCG],
                                       const uint32_t (&gmask)[NCG], uint32_t dmask, v4i (&acc)[4][NCG]) {
     uint32_t q[4][4];   // [j][u]: masked slice bits so far, unrotated
 #pragma unroll
@@ -363,7 +419,7 @@ __device__ __forceinline__ void mtile(const u32x4 (&w)[NS], const v4i (&xl)[NCG]
             for (int j = 0; j < 4; ++j)
                 A[j] = v4i{(int)q[j][0], (int)rotl32(q[j][1], 2), (int)rotl32(q[j][2], 4), (int)rotl32(q[j][3], 6)};
 #pragma unroll
-            for (int g = 0; g < NCG; ++g) {
+            for (int g = 0; g < NG; ++g) {
                 if (PER_REQ && ((gmask[g] >> (p + 1)) & 1u) == 0) continue;
                 v4i bm;
                 if constexpr (PER_REQ) {
@@ -379,13 +435,14 @@ __device__ __forceinline__ void mtile(const u32x4 (&w)[NS], const v4i (&xl)[NCG]
     }
 }
 
-// The product over this wave's tiles of the chunk: tiles ks, ks + KS, ...
-template <int NS, int NCG, bool PER_REQ>
+// The product over this wave's tiles of the chunk: tiles ks, ks + KS, ...,
+// multiplying the first NG column groups (the coarse ones, or all).
+template <int NS, int NCG, int NG, bool PER_REQ>
 __device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, int chunk, int h, int ks, int L,
                                          const int (&mcol)[NCG], const uint32_t (&gmask)[NCG], uint32_t dmask,
                                          int first, v4i (&acc)[4][NCG]) {
-    constexpr int H = MRing<NS, NCG>::H;
-    constexpr int PF = MRing<NS, NCG>::PF;
+    constexpr int H = MRing<NS, NG>::H;
+    constexpr int PF = MRing<NS, NG>::PF;
     const int t0 = chunk * a.tpc + ks;
     const int nt_all = min(a.tpc, a.n_tiles - chunk * a.tpc);
     const int nt = nt_all > ks ? (nt_all - ks + KS - 1) / KS : 0;
@@ -400,22 +457,22 @@ __device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, 
 
     __builtin_amdgcn_s_waitcnt(0);
     u32x4 wa[H][NS], wb[H][NS];
-    v4i xa[H][NCG], xb[H][NCG];
-    mload<NS, NCG, H>(wa, xa, wbase, pb, wstride, xbase, xstride, 0, last, first);
+    v4i xa[H][NG], xb[H][NG];
+    mload<NS, NG, H>(wa, xa, wbase, pb, wstride, xbase, xstride, 0, last, first);
     __builtin_amdgcn_sched_barrier(0);
-    mload<NS, NCG, H>(wb, xb, wbase, pb, wstride, xbase, xstride, H, last, first);
+    mload<NS, NG, H>(wb, xb, wbase, pb, wstride, xbase, xstride, H, last, first);
     __builtin_amdgcn_sched_barrier(0);
     int t = 0;
     for (; t + PF < nt; t += PF) {
 #pragma unroll
-        for (int u = 0; u < H; ++u) mtile<NS, NCG, PER_REQ>(wa[u], xa[u], mcol, gmask, dmask, acc);
+        for (int u = 0; u < H; ++u) mtile<NS, NCG, NG, PER_REQ>(wa[u], xa[u], mcol, gmask, dmask, acc);
         __builtin_amdgcn_sched_barrier(0);
-        mload<NS, NCG, H>(wa, xa, wbase, pb, wstride, xbase, xstride, t + PF, last, first);
+        mload<NS, NG, H>(wa, xa, wbase, pb, wstride, xbase, xstride, t + PF, last, first);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < H; ++u) mtile<NS, NCG, PER_REQ>(wb[u], xb[u], mcol, gmask, dmask, acc);
+        for (int u = 0; u < H; ++u) mtile<NS, NCG, NG, PER_REQ>(wb[u], xb[u], mcol, gmask, dmask, acc);
         __builtin_amdgcn_sched_barrier(0);
-        mload<NS, NCG, H>(wb, xb, wbase, pb, wstride, xbase, xstride, t + PF + H, last, first);
+        mload<NS, NG, H>(wb, xb, wbase, pb, wstride, xbase, xstride, t + PF + H, last, first);
         __builtin_amdgcn_sched_barrier(0);
     }
     // Drain: the last ring, whose tail may run past the wave's tiles.  Tiles
@@ -425,18 +482,18 @@ __device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, 
 #pragma unroll
     for (int u = 0; u < H; ++u) {
         const bool in = t + u < nt;
-        v4i z[NCG];
+        v4i z[NG];
 #pragma unroll
-        for (int g = 0; g < NCG; ++g) z[g] = in ? xa[u][g] : v4i{0, 0, 0, 0};
-        mtile<NS, NCG, PER_REQ>(wa[u], z, mcol, gmask, dmask, acc);
+        for (int g = 0; g < NG; ++g) z[g] = in ? xa[u][g] : v4i{0, 0, 0, 0};
+        mtile<NS, NCG, NG, PER_REQ>(wa[u], z, mcol, gmask, dmask, acc);
     }
 #pragma unroll
     for (int u = 0; u < H; ++u) {
         const bool in = t + H + u < nt;
-        v4i z[NCG];
+        v4i z[NG];
 #pragma unroll
-        for (int g = 0; g < NCG; ++g) z[g] = in ? xb[u][g] : v4i{0, 0, 0, 0};
-        mtile<NS, NCG, PER_REQ>(wb[u], z, mcol, gmask, dmask, acc);
+        for (int g = 0; g < NG; ++g) z[g] = in ? xb[u][g] : v4i{0, 0, 0, 0};
+        mtile<NS, NCG, NG, PER_REQ>(wb[u], z, mcol, gmask, dmask, acc);
     }
 }
 
@@ -474,20 +531,23 @@ __device__ __forceinline__ void row_tile_words(const uint8_t* tb, int64_t pb, in
             w[g][q] = (q >= first && q < depth) ? *reinterpret_cast<const uint32_t*>(tb + 256 * g + q * pb) : 0u;
 }
 
-__device__ double dense_correction(const MItem& a, int b, int chunk, int slot, int n, int row, int first, int depth,
+// (The item's fields come by value: a reference to the item would keep the
+// caller's copy of it in scratch memory when this is not inlined.)
+__device__ double dense_correction(const uint8_t* planes, int64_t plane_bytes, int64_t K, const int2* unc, int tpc,
+                                   int n_tiles, int b, int chunk, int slot, int n, int row, int first, int depth,
                                    int e, float* r2d) {
-    const int2* list = a.unc + (int64_t)slot * a.tpc * 64;
+    const int2* list = unc + (int64_t)slot * tpc * 64;
     const int L = (int)threadIdx.x & 63;
-    const int t0 = chunk * a.tpc;
-    const int t1 = min(a.n_tiles, t0 + a.tpc);
+    const int t0 = chunk * tpc;
+    const int t1 = min(n_tiles, t0 + tpc);
     // row `row` of tile t: word row >> 4 of lanes (row & 15) + 16 g, g = 0..3
-    const uint8_t* rowbase = a.planes + (int64_t)b * 16 * a.K + 16 * (row & 15) + 4 * (row >> 4);
+    const uint8_t* rowbase = planes + (int64_t)b * 16 * K + 16 * (row & 15) + 4 * (row >> 4);
     double part = 0.0;
     int p = 0;
     uint32_t cur[4][4], nxt[4][4];
-    row_tile_words(rowbase + (int64_t)t0 * kTileBytes, a.plane_bytes, first, depth, cur);
+    row_tile_words(rowbase + (int64_t)t0 * kTileBytes, plane_bytes, first, depth, cur);
     for (int t = t0; t < t1 && p < n; ++t) {
-        if (t + 1 < t1) row_tile_words(rowbase + (int64_t)(t + 1) * kTileBytes, a.plane_bytes, first, depth, nxt);
+        if (t + 1 < t1) row_tile_words(rowbase + (int64_t)(t + 1) * kTileBytes, plane_bytes, first, depth, nxt);
         const int lo = (t - t0) * 64;
         int2 ent = make_int2(0x7fffffff, 0);
         if (p + L < n) ent = list[p + L];
@@ -525,6 +585,7 @@ template <int NCG, bool PER_REQ, bool GROUPED, bool REFINE>
 __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
     extern __shared__ int tab[];   // [NH][64 rows][16 NCG + 1] integer sums, one flag, then r2d rows
     constexpr int TW = 16 * NCG + 1;
+    constexpr int NCGC = ncgc_of_ncg(NCG);
     MItem a;
     int local;
     if constexpr (GROUPED) {
@@ -543,6 +604,14 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
     const int ks = wave / NH;
     const int L = (int)threadIdx.x & 63;
     const int nw = NH * KS;
+    // the chunk's exponent and listed count (with the fine flag) of every
+    // request (lane r: request r), requested with the rungs
+    const int slots = SS * NH;
+    int e_all = 0, n_all = 0;
+    if (L < slots) {
+        e_all = a.exps[chunk * slots + L];
+        n_all = a.unc_count[chunk * slots + L];
+    }
     // rung of request L (lanes < B); a rung above 4 is flagged, read as
     // nothing and its outputs are NaN; then the depths of the set's requests
     // and columns.  A refinement launch reads nothing for a request at or
@@ -577,7 +646,8 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
     uint32_t gmask[NCG];
 #pragma unroll
     for (int g = 0; g < NCG; ++g) {
-        const int rr = (16 * g + (L & 15)) / kLimbCols;          // request (within the set) owning this column
+        // request (within the set) owning this lane's column of group g
+        const int rr = g < NCGC ? (16 * g + (L & 15)) / kCoarseCols : (16 * (g - NCGC) + (L & 15)) / kFineCols;
         const int md = __shfl(m_set, rr & 15);                   // its depth (lane rr holds it)
         mcol[g] = (rr < SS && SS * h + rr < B) ? md : 0;
         uint32_t gm = 1u << mcol[g];
@@ -585,27 +655,27 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
         for (int o = 1; o < 16; o <<= 1) gm |= __shfl_xor(gm, o);
         gmask[g] = __builtin_amdgcn_readfirstlane(gm);
     }
+    // the set multiplies its fine column groups only if one of its requests is fine
+    const uint64_t fine_bits = __ballot(L < slots && (n_all & kFineFlag) != 0);
+    const int fine = __builtin_amdgcn_readfirstlane((int)(((fine_bits >> (SS * h)) & ((1ull << SS) - 1)) != 0));
     for (int i = (int)threadIdx.x; i < NH * 64 * TW; i += (int)blockDim.x) tab[i] = 0;
     v4i acc[4][NCG];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int g = 0; g < NCG; ++g) acc[j][g] = v4i{0, 0, 0, 0};
-    switch (ns) {
-        case 0: break;   // no request of this set reads the block
-        case 1: mproduct<1, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
-        case 2: mproduct<2, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
-        case 3: mproduct<3, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
-        default: mproduct<4, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+    switch (ns + 5 * fine) {
+        case 0: case 5: break;   // no request of this set reads the block
+        case 1: mproduct<1, NCG, NCGC, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+        case 2: mproduct<2, NCG, NCGC, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+        case 3: mproduct<3, NCG, NCGC, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+        case 4: mproduct<4, NCG, NCGC, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+        case 6: mproduct<1, NCG, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+        case 7: mproduct<2, NCG, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+        case 8: mproduct<3, NCG, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+        default: mproduct<4, NCG, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
     }
-    // the chunk's exponent and listed count of every request (lane r: request r) and this
-    // lane's row scale, requested now so that their latency passes during the table sums
-    const int slots = SS * NH;
-    int e_all = 0, n_all = 0;
-    if (L < slots) {
-        e_all = a.exps[chunk * slots + L];
-        n_all = a.unc_count[chunk * slots + L];
-    }
+    // this lane's row scale, requested now so that its latency passes during the table sums
     const float sc32 = a.scales[b * kRows + L];
     __syncthreads();   // the tables are clear
     // the wave's 64 x 16 NCG integer sums added into its set's table
@@ -615,21 +685,24 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int g = 0; g < NCG; ++g)
+                if (g < NCGC || fine)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     atomicAdd(&mine[(16 * j + 4 * (L >> 4) + i) * TW + 16 * g + (L & 15)], acc[j][g][i]);
     }
     __syncthreads();
 
-    // outputs: one row per lane, requests spread over the waves; the limbs of
-    // request r are columns 6 (r mod SS) + l of set r / SS, then scaled into
-    // fp64, with the chunk's listed corrections
+    // outputs: one row per lane, requests spread over the waves; the sums of
+    // request r are its coarse columns 4 (r mod SS) + l and fine columns
+    // 16 NCGC + 2 (r mod SS) + l of set r / SS, combined and scaled into fp64,
+    // with the chunk's listed corrections
     const int row = L;
     float* r2d = reinterpret_cast<float*>(tab + NH * 64 * TW + 4) + 64 * wave;   // this wave's residual row
     const double sc = (double)sc32;
     const bool split = a.n_chunks > 1;
     for (int r = wave; r < B; r += nw) {
-        const int* t2 = tab + (r / SS) * 64 * TW + row * TW + kLimbCols * (r % SS);
+        const int* t2 = tab + (r / SS) * 64 * TW + row * TW + kCoarseCols * (r % SS);
+        const int* t2f = tab + (r / SS) * 64 * TW + row * TW + 16 * NCGC + kFineCols * (r % SS);
         const int slot = chunk * slots + r;
         const int e = __shfl(e_all, r & 63);
         const int mr = __shfl(m_all, r & 63);
@@ -638,10 +711,11 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
             if (e == kBadExp) {
                 v = __builtin_nan("");
             } else {
-                v = limb_value(t2[0], t2[1], t2[2], t2[3], t2[4], t2[5], e);
-                const int n = __shfl(n_all, r & 63);
+                v = limb_value(t2[0], t2[1], t2[2], t2f[0], t2f[1], t2[3], e);
+                const int n = __shfl(n_all, r & 63) & ~kFineFlag;
                 if (n > kDenseListed)
-                    v += dense_correction(a, b, chunk, slot, n, row, first, mr, e, r2d);
+                    v += dense_correction(a.planes, a.plane_bytes, a.K, a.unc, a.tpc, a.n_tiles, b, chunk, slot, n, row,
+                                          first, mr, e, r2d);
                 else if (n > 0)
                     v += listed_correction(a, b, chunk, slot, n, row, first, mr, e);
             }
@@ -708,11 +782,9 @@ static void launch_mfma(const MItem& it, const MCommon& c, bool xbf16, bool per_
         hipLaunchKernelGGL((limbs_kernel<true, GROUPED>), dim3((unsigned)pre_grid), dim3(kPreThreads), 0, s, it, c);
     else
         hipLaunchKernelGGL((limbs_kernel<false, GROUPED>), dim3((unsigned)pre_grid), dim3(kPreThreads), 0, s, it, c);
-    switch (c.NCG) {
-        case 1: launch_product<1, GROUPED>(it, c, per_req, grid, s); break;
+    switch (c.NCG) {   // the totals ncg_of_ss gives
         case 2: launch_product<2, GROUPED>(it, c, per_req, grid, s); break;
         case 3: launch_product<3, GROUPED>(it, c, per_req, grid, s); break;
-        case 4: launch_product<4, GROUPED>(it, c, per_req, grid, s); break;
         case 5: launch_product<5, GROUPED>(it, c, per_req, grid, s); break;
         default: launch_product<6, GROUPED>(it, c, per_req, grid, s); break;
     }
@@ -742,7 +814,7 @@ static MShape mshape(int64_t B, const qam_tuning* t) {
     const int set_max = t && t->set_max > 0 ? t->set_max : kMfmaSetMax;
     m.NH = (int)((B + set_max - 1) / set_max);              // request sets, as even as possible
     m.SS = (int)((B + m.NH - 1) / m.NH);
-    m.NCG = (kLimbCols * m.SS + 15) / 16;                     // 16-column groups per set
+    m.NCG = ncg_of_ss(m.SS);                                  // 16-column groups per set
     const int ks = t && t->ksplit > 0 ? t->ksplit : kMfmaKsplit;
     m.KS = std::max(1, std::min(ks, 4 / m.NH));               // at most four waves per workgroup
     return m;
@@ -823,6 +895,7 @@ static MCommon mcommon(int64_t B, int NH, int SS, int NCG, int KS, uint32_t* sta
     c.NH = NH;
     c.SS = SS;
     c.NCG = NCG;
+    c.NCGC = ncgc_of_ncg(NCG);
     c.KS = KS;
     c.status = status;
     return c;
@@ -1029,8 +1102,8 @@ int mfma_group_init(const qam_gemv_item* items, int n_items, int64_t B, int x_dt
 // first > 0: a refinement launch (slices first.. of each request's depth added to y).
 static int mfma_group_run_from(const qam_group* g, int first, hipStream_t s) {
     if (!g->dev_mem || g->sets < 1 || g->sets > 4 || g->set_size < 1 || g->set_size > 16 ||
-        (int64_t)g->sets * g->set_size < g->B || g->col_groups < 1 || g->col_groups > kMaxNCG ||
-        kLimbCols * g->set_size > 16 * g->col_groups || g->ksplit < 1 || g->ksplit * g->sets > 4)
+        (int64_t)g->sets * g->set_size < g->B || g->col_groups != ncg_of_ss(g->set_size) || g->ksplit < 1 ||
+        g->ksplit * g->sets > 4)
         QAM_FAIL(QAM_ERR_ARG, "qmatvec_group: corrupt group descriptor");
     MCommon c = mcommon(g->B, g->sets, g->set_size, g->col_groups, g->ksplit, status_word(g->dev_mem));
     c.items = static_cast<const MItem*>(g->table);

@@ -244,11 +244,15 @@ def test_qmatvec_shape_battery(qam, N, K, B):
     y = host(qam.qmatvec(dev(x), pm, dev(lv)))
     assert ("qmatvec_staged" if B == 1 else "qmatvec_mfma") in qam.last_variant()
     check_y(y, W, sc, x, lv, (N, K, B))
-    # the same map given once per request takes the per-request form, which
-    # sums the same integers: the same bits
+    # the same map given once per request: at B = 1 the same route and bits;
+    # above, the per-request form, whose column chunks can differ from the
+    # shared form's (x is split into fixed point per chunk), so it meets the
+    # same bound rather than the same bits
     lvr = np.ascontiguousarray(np.broadcast_to(lv, (B, lv.size)))
     yr = host(qam.qmatvec(dev(x), pm, dev(lvr)))
-    assert np.array_equal(yr.view(np.uint32), y.view(np.uint32)), (N, K, B)
+    if B == 1:
+        assert np.array_equal(yr.view(np.uint32), y.view(np.uint32)), (N, K, B)
+    check_y(yr, W, sc, x, lv, (N, K, B, "per-request"))
 
 
 def test_qmatvec_exact_integer_cases(qam):
