@@ -299,3 +299,39 @@ def test_long_chunks_with_residuals_in_every_round(qam, per_request):
     g.run()
     assert g.desc.n_workgroups == N // 64, (g.desc.n_workgroups, qam.last_variant())
     check(host(y), W, sc, x, lv, per_request, ("long chunk", per_request))
+
+
+@pytest.mark.parametrize("per_request", [True, False])
+@pytest.mark.parametrize("B", [3, 16, 20, 32])
+def test_coarse_and_fine_chunks_in_one_set(qam, B, per_request):
+    """A request set mixing chunks that keep the 32-bit split with a few
+    listed elements and chunks that need the 48-bit one.  Requests r % 3 == 0
+    hold one large value on a column whose weights are all zero and 1-4 small
+    ones (below 2^-15 of the large one, so the coarse split leaves them to the
+    exact listed corrections, which then carry the whole output); r % 3 == 1
+    hold the large value and 40 small ones (too many to list: the chunk takes
+    the fine columns); r % 3 == 2 are N(0, 1)."""
+    N, K = 512, 4160
+    rng = np.random.default_rng(700 + B + per_request)
+    W = rng.integers(-127, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    sc = rng.uniform(0.001, 0.02, size=N).astype(np.float32)
+    zc = int(rng.integers(K))
+    W[:, zc] = 0
+    x = np.zeros((B, K), np.float32)
+    for r in range(B):
+        if r % 3 == 2:
+            x[r] = rng.standard_normal(K).astype(np.float32)
+            continue
+        x[r, zc] = np.float32(4.0 + r)
+        n_small = int(rng.integers(1, 5)) if r % 3 == 0 else 40
+        cols = rng.choice(np.setdiff1d(np.arange(K), [zc]), n_small, replace=False)
+        x[r, cols] = (rng.uniform(1e-6, 1e-4, n_small) * rng.choice([-1.0, 1.0], n_small)).astype(np.float32)
+    pm = qam.pack_slices(dev(W), dev(sc))
+    xd = dev(x)
+    lv = rng.integers(1, 5, size=(B, N // 64) if per_request else N // 64).astype(np.uint8)
+    y = host(qam.qmatvec(xd, pm, dev(lv)))
+    assert "qmatvec_mfma" in qam.last_variant()
+    check(y, W, sc, x, lv, per_request, (B, per_request))
+    # the small values decide these outputs: they are far from zero
+    small = [r for r in range(B) if r % 3 != 2]
+    assert np.all(np.abs(y[small]).max(axis=1) > 0), small
