@@ -49,13 +49,21 @@ constexpr int kFineCols = 2;          // fine B-operand columns per request
 constexpr int kCoarseListMax = 4;     // most coarse-uncovered elements a coarse (chunk, request) lists
 constexpr int kFineFlag = 1 << 30;    // unc_count bit: the (chunk, request) is fine
 
-// Column groups of a set of SS requests: coarse, fine, both.
+// Column groups of a set of SS requests: coarse, fine, both.  Sets of one or
+// two requests keep all six columns of a request in one group (the coarse
+// block, then the fine block at column 4 SS): there is no MFMA to save.
 __host__ __device__ constexpr int ncgc_of_ss(int ss) { return (kCoarseCols * ss + 15) / 16; }
 __host__ __device__ constexpr int ncgf_of_ss(int ss) { return (kFineCols * ss + 15) / 16; }
-__host__ __device__ constexpr int ncg_of_ss(int ss) { return ncgc_of_ss(ss) + ncgf_of_ss(ss); }
+__host__ __device__ constexpr int ncg_of_ss(int ss) {
+    return (kCoarseCols + kFineCols) * ss <= 16 ? 1 : ncgc_of_ss(ss) + ncgf_of_ss(ss);
+}
 // The coarse groups of a total of NCG (every set size gives a distinct total:
-// 1-4 requests 1 + 1, 5-8 2 + 1, 9-12 3 + 2, 13-16 4 + 2).
-__host__ __device__ constexpr int ncgc_of_ncg(int ncg) { return ncg == 2 ? 1 : ncg == 3 ? 2 : ncg == 5 ? 3 : 4; }
+// 1-2 requests 1 (shared), 3-4 1 + 1, 5-8 2 + 1, 9-12 3 + 2, 13-16 4 + 2).
+__host__ __device__ constexpr int ncgc_of_ncg(int ncg) {
+    return ncg <= 2 ? 1 : ncg == 3 ? 2 : ncg == 5 ? 3 : 4;
+}
+// First column of the fine block in a set's columns.
+__host__ __device__ constexpr int fine_base(int ncg, int ss) { return ncg == 1 ? kCoarseCols * ss : 16 * ncgc_of_ncg(ncg); }
 
 struct MItem {
     const uint8_t* planes;
@@ -154,6 +162,8 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
     __shared__ float red_p[kPreThreads / 64];
     __shared__ double red_s[kPreThreads / 64];
     __shared__ int wave_n[kPreThreads / 64];
+    __shared__ int clist_n;                    // coarse chunks: elements listed so far ...
+    __shared__ int2 clist[kCoarseListMax];     // ... and the list, in no order until sorted
     MItem a;
     int local;
     if constexpr (GROUPED) {
@@ -232,9 +242,13 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
     if (m > 0.0f) frexpf(m, &e);
     const XSplit sp = xsplit_of(e);
     // Coarse or fine: count the elements the coarse split leaves uncovered
-    // (the first round's values are still in registers).
+    // (the first round's values are still in registers).  Sets of up to four
+    // requests (one or two column groups) always take the fine split: the
+    // coarse one would save them at most one group of MFMAs, less than the
+    // count costs these small launches.
+    const bool one_group = NCG <= 2;
     int ccount = 0;
-    if (live && !nonfinite)
+    if (live && !nonfinite && !one_group)
         for (int base = 0; base < ncol; base += kPreRound)
 #pragma unroll
             for (int j = 0; j < kPreVec; ++j) {
@@ -248,17 +262,20 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
                               (int)coarse_uncovered(v.z, sp) + (int)coarse_uncovered(v.w, sp);
                 }
             }
+    if (!one_group) {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ccount += __shfl_xor(ccount, o);
-    if (lane == 0) wave_n[wave] = ccount;
-    __syncthreads();
-    ccount = 0;
+        for (int o = 32; o > 0; o >>= 1) ccount += __shfl_xor(ccount, o);
+        if (lane == 0) wave_n[wave] = ccount;
+        if (T == 0) clist_n = 0;
+        __syncthreads();
+        ccount = 0;
 #pragma unroll
-    for (int w = 0; w < kPreThreads / 64; ++w) ccount += wave_n[w];
-    __syncthreads();   // wave_n is written again by the listing
-    const bool fine = ccount > kCoarseListMax;
+        for (int w = 0; w < kPreThreads / 64; ++w) ccount += wave_n[w];
+        __syncthreads();   // wave_n is written again by the listing
+    }
+    const bool fine = one_group || ccount > kCoarseListMax;
     const int h = r / SS, rr = r % SS;
-    const int NCGC = c.NCGC;
+    const int FB = fine_base(NCG, SS);
     uint8_t* lb = reinterpret_cast<uint8_t*>(a.limbs);
     int2* list = a.unc + (int64_t)(chunk * slots + r) * a.tpc * 64;
     int listed = 0;
@@ -306,16 +323,16 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
                 const int64_t t = kk >> 6;
                 const int kg = (int)((kk & 63) >> 4);
                 const int byte = (int)(kk & 15);
-                // digits: hi 0..2 and lo 2 to coarse columns 4 rr + 0..3, lo 0..1 to fine columns 2 rr + 0..1
+                // digits: hi 0..2 and lo 2 to coarse columns 4 rr + 0..3, lo 0..1 to fine
+                // columns FB + 2 rr + 0..1
 #pragma unroll
                 for (int l = 0; l < kCoarseCols + kFineCols; ++l) {
                     const uint32_t* w = l < 3 ? wh : wl;
                     const int sh = l < 3 ? 8 * l : l == 3 ? 16 : 8 * (l - 4);
-                    const int col = l < kCoarseCols ? kCoarseCols * rr + l : kFineCols * rr + (l - kCoarseCols);
-                    const int grp = l < kCoarseCols ? col >> 4 : NCGC + (col >> 4);
+                    const int col = l < kCoarseCols ? kCoarseCols * rr + l : FB + kFineCols * rr + (l - kCoarseCols);
                     const uint32_t word = ((w[0] >> sh) & 0xFFu) | (((w[1] >> sh) & 0xFFu) << 8) |
                                           (((w[2] >> sh) & 0xFFu) << 16) | (((w[3] >> sh) & 0xFFu) << 24);
-                    const int64_t unit = ((t * NH + h) * NCG + grp) * 64 + kg * 16 + (col & 15);
+                    const int64_t unit = ((t * NH + h) * NCG + (col >> 4)) * 64 + kg * 16 + (col & 15);
                     *reinterpret_cast<uint32_t*>(lb + unit * 16 + byte) = word;
                 }
             }
@@ -324,7 +341,17 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
         // uncovered elements of this round, appended in column order: the
         // first groups of all threads, then the second ones (16-bit fields:
         // a round holds at most 4 kPreThreads of each)
-        if (__syncthreads_or(packed)) {
+        if (!fine) {
+            // a coarse chunk lists at most kCoarseListMax elements (counted
+            // above): each takes a slot, and the list is sorted at the end
+#pragma unroll
+            for (int j = 0; j < kPreVec; ++j) {
+                const int k = base + 4 * T + 4 * kPreThreads * j;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (u[j][q]) clist[atomicAdd(&clist_n, 1)] = int2{k + q, __float_as_int(r2[j][q])};
+            }
+        } else if (__syncthreads_or(packed)) {
             int incl = packed;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
@@ -352,6 +379,19 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
             }
             listed += total0 + ((total >> 16) & 0xFFFF);
             __syncthreads();   // wave_n is read before the next round writes it
+        }
+    }
+    if (!fine) {   // the coarse list in column order, as the scan would have placed it
+        __syncthreads();
+        if (T == 0) {
+            listed = clist_n;
+            for (int i = 1; i < listed; ++i)
+                for (int m = i; m > 0 && clist[m - 1].x > clist[m].x; --m) {
+                    const int2 t = clist[m - 1];
+                    clist[m - 1] = clist[m];
+                    clist[m] = t;
+                }
+            for (int i = 0; i < listed; ++i) list[i] = clist[i];
         }
     }
     if (T == 0) {
@@ -391,7 +431,7 @@ __device__ __forceinline__ void mload(u32x4 (&w)[H][NS], v4i (&x)[H][NG], const 
 // in group g, so a group with no request at d costs no MFMA there); with a
 // shared map, the codes at the block's depth NS times every limb.  The first
 // NG column groups are multiplied (the coarse ones, or all).
-template <int NS, int NCG, int NG, bool PER_REQ>
+template <int NS, int NCG, int G0, int NG, bool PER_REQ>
 __device__ __forceinline__ void mtile(const u32x4 (&w)[NS], const v4i (&xl)[NG], const int (&mcol)[NCG],
                                       const uint32_t (&gmask)[NCG], uint32_t dmask, v4i (&acc)[4][NCG]) {
     uint32_t q[4][4];   // [j][u]: masked slice bits so far, unrotated
@@ -420,24 +460,25 @@ __device__ __forceinline__ void mtile(const u32x4 (&w)[NS], const v4i (&xl)[NG],
                 A[j] = v4i{(int)q[j][0], (int)rotl32(q[j][1], 2), (int)rotl32(q[j][2], 4), (int)rotl32(q[j][3], 6)};
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                if (PER_REQ && ((gmask[g] >> (p + 1)) & 1u) == 0) continue;
+                if (PER_REQ && ((gmask[G0 + g] >> (p + 1)) & 1u) == 0) continue;
                 v4i bm;
                 if constexpr (PER_REQ) {
-                    const bool mine = mcol[g] == p + 1;
+                    const bool mine = mcol[G0 + g] == p + 1;
                     bm = v4i{mine ? xl[g].x : 0, mine ? xl[g].y : 0, mine ? xl[g].z : 0, mine ? xl[g].w : 0};
                 } else {
                     bm = xl[g];
                 }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], bm, acc[j][g], 0, 0, 0);
+                for (int j = 0; j < 4; ++j)
+                    acc[j][G0 + g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], bm, acc[j][G0 + g], 0, 0, 0);
             }
         }
     }
 }
 
 // The product over this wave's tiles of the chunk: tiles ks, ks + KS, ...,
-// multiplying the first NG column groups (the coarse ones, or all).
-template <int NS, int NCG, int NG, bool PER_REQ>
+// multiplying column groups G0 .. G0 + NG - 1.
+template <int NS, int NCG, int G0, int NG, bool PER_REQ>
 __device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, int chunk, int h, int ks, int L,
                                          const int (&mcol)[NCG], const uint32_t (&gmask)[NCG], uint32_t dmask,
                                          int first, v4i (&acc)[4][NCG]) {
@@ -451,7 +492,7 @@ __device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, 
     const uint8_t* wbase = a.planes + (int64_t)b * 16 * a.K + (int64_t)t0 * kTileBytes + L * 16;
     const int64_t wstride = (int64_t)KS * kTileBytes;
     const int64_t xunit = (int64_t)NH * NCG * 64;        // v4i units per tile
-    const v4i* xbase = a.limbs + (int64_t)t0 * xunit + (int64_t)h * NCG * 64 + L;
+    const v4i* xbase = a.limbs + (int64_t)t0 * xunit + ((int64_t)h * NCG + G0) * 64 + L;
     const int64_t xstride = xunit * KS;
     const int64_t pb = a.plane_bytes;
 
@@ -465,12 +506,12 @@ __device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, 
     int t = 0;
     for (; t + PF < nt; t += PF) {
 #pragma unroll
-        for (int u = 0; u < H; ++u) mtile<NS, NCG, NG, PER_REQ>(wa[u], xa[u], mcol, gmask, dmask, acc);
+        for (int u = 0; u < H; ++u) mtile<NS, NCG, G0, NG, PER_REQ>(wa[u], xa[u], mcol, gmask, dmask, acc);
         __builtin_amdgcn_sched_barrier(0);
         mload<NS, NG, H>(wa, xa, wbase, pb, wstride, xbase, xstride, t + PF, last, first);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < H; ++u) mtile<NS, NCG, NG, PER_REQ>(wb[u], xb[u], mcol, gmask, dmask, acc);
+        for (int u = 0; u < H; ++u) mtile<NS, NCG, G0, NG, PER_REQ>(wb[u], xb[u], mcol, gmask, dmask, acc);
         __builtin_amdgcn_sched_barrier(0);
         mload<NS, NG, H>(wb, xb, wbase, pb, wstride, xbase, xstride, t + PF + H, last, first);
         __builtin_amdgcn_sched_barrier(0);
@@ -485,7 +526,7 @@ __device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, 
         v4i z[NG];
 #pragma unroll
         for (int g = 0; g < NG; ++g) z[g] = in ? xa[u][g] : v4i{0, 0, 0, 0};
-        mtile<NS, NCG, NG, PER_REQ>(wa[u], z, mcol, gmask, dmask, acc);
+        mtile<NS, NCG, G0, NG, PER_REQ>(wa[u], z, mcol, gmask, dmask, acc);
     }
 #pragma unroll
     for (int u = 0; u < H; ++u) {
@@ -493,7 +534,7 @@ __device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, 
         v4i z[NG];
 #pragma unroll
         for (int g = 0; g < NG; ++g) z[g] = in ? xb[u][g] : v4i{0, 0, 0, 0};
-        mtile<NS, NCG, NG, PER_REQ>(wb[u], z, mcol, gmask, dmask, acc);
+        mtile<NS, NCG, G0, NG, PER_REQ>(wb[u], z, mcol, gmask, dmask, acc);
     }
 }
 
@@ -596,6 +637,7 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
         local = (int)blockIdx.x;
     }
     const int B = c.B, NH = c.NH, KS = c.KS, SS = c.SS;
+    const int FB = fine_base(NCG, SS);   // first column of the fine block
     const int first = REFINE ? c.first : 0;
     const int chunk = local % a.n_chunks;
     const int b = local / a.n_chunks;
@@ -604,14 +646,7 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
     const int ks = wave / NH;
     const int L = (int)threadIdx.x & 63;
     const int nw = NH * KS;
-    // the chunk's exponent and listed count (with the fine flag) of every
-    // request (lane r: request r), requested with the rungs
     const int slots = SS * NH;
-    int e_all = 0, n_all = 0;
-    if (L < slots) {
-        e_all = a.exps[chunk * slots + L];
-        n_all = a.unc_count[chunk * slots + L];
-    }
     // rung of request L (lanes < B); a rung above 4 is flagged, read as
     // nothing and its outputs are NaN; then the depths of the set's requests
     // and columns.  A refinement launch reads nothing for a request at or
@@ -647,7 +682,9 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
 #pragma unroll
     for (int g = 0; g < NCG; ++g) {
         // request (within the set) owning this lane's column of group g
-        const int rr = g < NCGC ? (16 * g + (L & 15)) / kCoarseCols : (16 * (g - NCGC) + (L & 15)) / kFineCols;
+        const int cc = 16 * g + (L & 15);                       // the column in the set
+        const bool coarse = NCG == 1 ? cc < kCoarseCols * SS : g < NCGC;
+        const int rr = coarse ? cc / kCoarseCols : (cc - FB) / kFineCols;
         const int md = __shfl(m_set, rr & 15);                   // its depth (lane rr holds it)
         mcol[g] = (rr < SS && SS * h + rr < B) ? md : 0;
         uint32_t gm = 1u << mcol[g];
@@ -655,27 +692,34 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
         for (int o = 1; o < 16; o <<= 1) gm |= __shfl_xor(gm, o);
         gmask[g] = __builtin_amdgcn_readfirstlane(gm);
     }
-    // the set multiplies its fine column groups only if one of its requests is fine
-    const uint64_t fine_bits = __ballot(L < slots && (n_all & kFineFlag) != 0);
-    const int fine = __builtin_amdgcn_readfirstlane((int)(((fine_bits >> (SS * h)) & ((1ull << SS) - 1)) != 0));
     for (int i = (int)threadIdx.x; i < NH * 64 * TW; i += (int)blockDim.x) tab[i] = 0;
     v4i acc[4][NCG];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int g = 0; g < NCG; ++g) acc[j][g] = v4i{0, 0, 0, 0};
-    switch (ns + 5 * fine) {
-        case 0: case 5: break;   // no request of this set reads the block
-        case 1: mproduct<1, NCG, NCGC, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
-        case 2: mproduct<2, NCG, NCGC, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
-        case 3: mproduct<3, NCG, NCGC, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
-        case 4: mproduct<4, NCG, NCGC, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
-        case 6: mproduct<1, NCG, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
-        case 7: mproduct<2, NCG, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
-        case 8: mproduct<3, NCG, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
-        default: mproduct<4, NCG, NCG, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+    // Sets of up to four requests always take the fine split: one pass over
+    // every group.  Larger sets multiply their coarse groups first and the
+    // fine ones in a second pass when a request of the set is fine for the
+    // chunk, so no launch waits for the pre-pass's mode before its first loads.
+    constexpr bool ALWAYS_FINE = NCG <= 2;
+    constexpr int NG1 = ALWAYS_FINE ? NCG : NCGC;
+    switch (ns) {
+        case 0: break;   // no request of this set reads the block
+        case 1: mproduct<1, NCG, 0, NG1, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+        case 2: mproduct<2, NCG, 0, NG1, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+        case 3: mproduct<3, NCG, 0, NG1, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+        default: mproduct<4, NCG, 0, NG1, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
     }
-    // this lane's row scale, requested now so that its latency passes during the table sums
+    // the chunk's exponent and listed count (with the fine flag) of every
+    // request (lane r: request r) and this lane's row scale, read once the
+    // first pass is done (the product's loads wait for nothing the pre-pass
+    // wrote), so that their latency passes during the table sums
+    int e_all = 0, n_all = 0;
+    if (L < slots) {
+        e_all = a.exps[chunk * slots + L];
+        n_all = a.unc_count[chunk * slots + L];
+    }
     const float sc32 = a.scales[b * kRows + L];
     __syncthreads();   // the tables are clear
     // the wave's 64 x 16 NCG integer sums added into its set's table
@@ -684,11 +728,31 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int g = 0; g < NCG; ++g)
-                if (g < NCGC || fine)
+            for (int g = 0; g < NG1; ++g)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     atomicAdd(&mine[(16 * j + 4 * (L >> 4) + i) * TW + 16 * g + (L & 15)], acc[j][g][i]);
+    }
+    if constexpr (!ALWAYS_FINE) {
+        // the set's mode: a fine request of the set brings the fine groups in
+        const uint64_t fine_bits = __ballot(L < slots && (n_all & kFineFlag) != 0);
+        const bool fine = __builtin_amdgcn_readfirstlane(
+                              (int)(((fine_bits >> (SS * h)) & ((1ull << SS) - 1)) != 0)) != 0;
+        if (fine && ns > 0) {
+            switch (ns) {
+                case 1: mproduct<1, NCG, NCGC, NCG - NCGC, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+                case 2: mproduct<2, NCG, NCGC, NCG - NCGC, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+                case 3: mproduct<3, NCG, NCGC, NCG - NCGC, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+                default: mproduct<4, NCG, NCGC, NCG - NCGC, PER_REQ>(a, NH, KS, b, chunk, h, ks, L, mcol, gmask, dm, first, acc); break;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = NCGC; g < NCG; ++g)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        atomicAdd(&mine[(16 * j + 4 * (L >> 4) + i) * TW + 16 * g + (L & 15)], acc[j][g][i]);
+        }
     }
     __syncthreads();
 
@@ -702,7 +766,7 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
     const bool split = a.n_chunks > 1;
     for (int r = wave; r < B; r += nw) {
         const int* t2 = tab + (r / SS) * 64 * TW + row * TW + kCoarseCols * (r % SS);
-        const int* t2f = tab + (r / SS) * 64 * TW + row * TW + 16 * NCGC + kFineCols * (r % SS);
+        const int* t2f = tab + (r / SS) * 64 * TW + row * TW + FB + kFineCols * (r % SS);
         const int slot = chunk * slots + r;
         const int e = __shfl(e_all, r & 63);
         const int mr = __shfl(m_all, r & 63);
@@ -783,6 +847,7 @@ static void launch_mfma(const MItem& it, const MCommon& c, bool xbf16, bool per_
     else
         hipLaunchKernelGGL((limbs_kernel<false, GROUPED>), dim3((unsigned)pre_grid), dim3(kPreThreads), 0, s, it, c);
     switch (c.NCG) {   // the totals ncg_of_ss gives
+        case 1: launch_product<1, GROUPED>(it, c, per_req, grid, s); break;
         case 2: launch_product<2, GROUPED>(it, c, per_req, grid, s); break;
         case 3: launch_product<3, GROUPED>(it, c, per_req, grid, s); break;
         case 5: launch_product<5, GROUPED>(it, c, per_req, grid, s); break;
