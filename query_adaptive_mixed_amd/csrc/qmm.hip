@@ -349,7 +349,10 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
                 const int k = base + 4 * T + 4 * kPreThreads * j;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    if (u[j][q]) clist[atomicAdd(&clist_n, 1)] = int2{k + q, __float_as_int(r2[j][q])};
+                    if (u[j][q]) {
+                        const int pos = atomicAdd(&clist_n, 1);   // < kCoarseListMax: the count above saw these
+                        if (pos < kCoarseListMax) clist[pos] = int2{k + q, __float_as_int(r2[j][q])};
+                    }
             }
         } else if (__syncthreads_or(packed)) {
             int incl = packed;
@@ -384,7 +387,7 @@ __global__ __launch_bounds__(kPreThreads) void limbs_kernel(MItem single, MCommo
     if (!fine) {   // the coarse list in column order, as the scan would have placed it
         __syncthreads();
         if (T == 0) {
-            listed = clist_n;
+            listed = min(clist_n, kCoarseListMax);
             for (int i = 1; i < listed; ++i)
                 for (int m = i; m > 0 && clist[m - 1].x > clist[m].x; --m) {
                     const int2 t = clist[m - 1];
