@@ -21,8 +21,12 @@
 // groups (column 4 rr + l: hi limbs 0..2, then the lo digit of weight 2^16,
 // which is the coarse digit or the fine part's top digit) and NCGF fine ones
 // (column 2 rr + l: the fine part's low digits 0 and 1, zero for a coarse
-// request).  A (chunk, set) whose requests are all coarse multiplies only its
-// coarse groups: 4 columns per request instead of 6.  Codes are the A
+// request); sets of one or two requests keep both blocks in one group (the
+// fine block from column 4 SS).  Sets of more than four requests multiply
+// their coarse groups first and their fine groups in a second pass only when
+// a request of the set is fine for the chunk: 4 columns per request instead
+// of 6 in the common case.  Sets of up to four always take the fine split (the
+// coarse one would save them at most one group).  Codes are the A
 // operands (16 rows x 64 columns, exactly the words a lane loads); i32
 // accumulation is exact; a request's columns are combined in fp64 after the
 // chunk, through an LDS table of the block's 64 x 16 NCG integer sums, and the
