@@ -527,9 +527,18 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     QAM_STAMP(6);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (prev != (uint32_t)(a.n_chunks - 1)) return;
+    // eight partial loads in flight at a time, added in chunk order
     double sum = 0.0;
-    for (int cc = 0; cc < a.n_chunks; ++cc)
-        sum += __hip_atomic_load(&a.partials[(int64_t)cc * a.N + row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int c0 = 0; c0 < a.n_chunks; c0 += 8) {
+        double pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            pv[j] = __hip_atomic_load(&a.partials[(int64_t)min(c0 + j, a.n_chunks - 1) * a.N + row], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (c0 + j < a.n_chunks) sum += pv[j];
+    }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (L == 0) __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     finish<XBF16, EPI>(a, b, L, sum, false, ssq);

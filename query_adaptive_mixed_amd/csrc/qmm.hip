@@ -547,16 +547,48 @@ __device__ __forceinline__ void mproduct(const MItem& a, int NH, int KS, int b, 
 
 // Request r's exact corrections for the uncovered elements of its chunk, for
 // the row of lane `row`: code(row, k) at the request's read (slices
-// first .. depth-1) times the listed residual, in fp64.
+// first .. depth-1) times the listed residual, in fp64.  The list (at most
+// kDenseListed entries) comes in with one load, lane i holding entry i, and
+// the plane words of four elements are in flight together; the terms are
+// still added one by one in list order.
 __device__ __forceinline__ double listed_correction(const MItem& a, int b, int chunk, int slot, int n, int row,
                                                     int first, int depth, int e) {
     const int2* list = a.unc + (int64_t)slot * a.tpc * 64;
     const int64_t col0 = (int64_t)chunk * a.tpc * 64;
+    const int L = (int)threadIdx.x & 63;
+    const int2 mine = L < n ? list[L] : make_int2(0, 0);
+    // row `row` of tile t: word row >> 4 of lanes (row & 15) + 16 g, g = 0..3
+    const uint8_t* rowbase = a.planes + (int64_t)b * 16 * a.K + 16 * (row & 15) + 4 * (row >> 4);
     double part = 0.0;
-    for (int i = 0; i < n; ++i) {
-        const int2 ent = list[i];
-        part += (double)code_at(a.planes, a.plane_bytes, a.K, b, row, col0 + ent.x, first, depth) *
-                (double)__int_as_float(ent.y);
+    for (int i0 = 0; i0 < n; i0 += 4) {
+        uint32_t w[4][4];
+        int kc[4];
+        float res[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = min(i0 + j, n - 1);
+            const int64_t k = col0 + __builtin_amdgcn_readlane(mine.x, i);
+            res[j] = __int_as_float(__builtin_amdgcn_readlane(mine.y, i));
+            kc[j] = (int)(k & 63);
+            const uint8_t* wp = rowbase + (k >> 6) * kTileBytes + 256 * (kc[j] >> 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                w[j][q] = (q >= first && q < depth) ? *reinterpret_cast<const uint32_t*>(wp + q * a.plane_bytes) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (i0 + j >= n) break;
+            // slice 3 - q of the element's byte, before the rotation by 2u
+            const int u = (kc[j] >> 2) & 3;
+            uint32_t acc = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t m = 0x03030303u << (2 * (3 - q));
+                acc |= w[j][q] & ((m >> (2 * u)) | (m << ((32 - 2 * u) & 31)));
+            }
+            acc = (acc << (2 * u)) | (acc >> ((32 - 2 * u) & 31));
+            part += (double)(int)(int8_t)(uint8_t)(acc >> (8 * (kc[j] & 3))) * (double)res[j];
+        }
     }
     return e < kSmallExp ? ldexp(part, -kPrescale) : part;
 }
@@ -815,14 +847,35 @@ __global__ __launch_bounds__(256) void qmm_kernel(MItem single, MCommon c) {
     __syncthreads();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (*flag != a.n_chunks - 1) return;
-    for (int r = wave; r < B; r += nw) {
-        double sum = 0.0;
-        for (int cc = 0; cc < a.n_chunks; ++cc)
-            sum += __hip_atomic_load(&a.partials[((int64_t)cc * B + r) * a.N + (int64_t)b * kRows + row],
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        float* yo = &a.y[(int64_t)r * a.N + (int64_t)b * kRows + row];
-        if constexpr (!REFINE) *yo = (float)(sc * sum);
-        else if (__shfl(m_all, r & 63) != 0 || ((bad_mask >> r) & 1)) *yo = (float)((double)*yo + sc * sum);
+    // The wave's (request, chunk) pairs in request-major order, eight
+    // partial loads in flight at a time; each request's sum still runs over
+    // its chunks in order.
+    const int nc = a.n_chunks;
+    const int n_pairs = (B - wave + nw - 1) / nw * nc;
+    const double* pbase = a.partials + (int64_t)b * kRows + row;
+    double sum = 0.0;
+    for (int f0 = 0; f0 < n_pairs; f0 += 8) {
+        double pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int f = min(f0 + j, n_pairs - 1);
+            const int jr = f / nc, cc = f - jr * nc;
+            pv[j] = __hip_atomic_load(pbase + ((int64_t)cc * B + wave + jr * nw) * a.N, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int f = f0 + j;
+            if (f >= n_pairs) break;
+            sum += pv[j];
+            const int jr = f / nc;
+            if (f - jr * nc != nc - 1) continue;
+            const int r = wave + jr * nw;
+            float* yo = &a.y[(int64_t)r * a.N + (int64_t)b * kRows + row];
+            if constexpr (!REFINE) *yo = (float)(sc * sum);
+            else if (__shfl(m_all, r & 63) != 0 || ((bad_mask >> r) & 1)) *yo = (float)((double)*yo + sc * sum);
+            sum = 0.0;
+        }
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (threadIdx.x == 0) __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
