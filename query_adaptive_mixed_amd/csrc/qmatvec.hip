@@ -290,9 +290,12 @@ __device__ double sum_squares(const void* x, int64_t K, int L) {
 // interleaved 32 gate / 32 up per block, one output per pair:
 // fl32(silu(gate) * up) with silu(t) = t / (1 + e^-t), all in fp64.
 template <bool XBF16, bool EPI>
-__device__ __forceinline__ void finish(const Item& a, int b, int L, double sum, bool have_ssq, double ssq) {
+// `scale` and `y_old` are the row's scale and, when adding, its y before the
+// launch (loaded by the caller, ahead of the split-K hand-off where it has one).
+__device__ __forceinline__ void finish(const Item& a, int b, int L, double sum, bool have_ssq, double ssq, float scale,
+                                       float y_old) {
     const int row = b * kRows + L;
-    double v = (double)a.scales[row] * sum;
+    double v = (double)scale * sum;
     if (EPI && a.rms) {
         const double ss = have_ssq ? ssq : sum_squares<XBF16>(a.x, a.K, L);
         v = v / sqrt(ss / (double)a.K + a.eps);
@@ -301,7 +304,7 @@ __device__ __forceinline__ void finish(const Item& a, int b, int L, double sum, 
         const double up = __shfl(v, (L + 32) & 63);
         if (L < 32) a.y[b * 32 + L] = (float)(v / (1.0 + exp(-v)) * up);
     } else if (EPI && a.out_mode == QAM_OUT_ADD) {
-        a.y[row] = (float)((double)a.y[row] + v);
+        a.y[row] = (float)((double)y_old + v);
     } else {
         a.y[row] = (float)v;
     }
@@ -505,7 +508,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) ssq += __shfl_xor(ssq, o);
         }
-        finish<XBF16, EPI>(a, b, L, part, want_ssq, ssq);
+        finish<XBF16, EPI>(a, b, L, part, want_ssq, ssq, a.scales[row], EPI && a.out_mode == QAM_OUT_ADD ? a.y[row] : 0.0f);
         return;
     }
     // Split K: publish this chunk's partials, then count the arrival; the last
@@ -518,6 +521,10 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     // partial stores past the counter update, and the partial loads ahead of
     // it (they emit no instruction).
     __hip_atomic_store(&a.partials[(int64_t)chunk * a.N + row], part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the row's scale and old y, in flight while the stores complete (no
+    // other wave writes this row of y before the last arriver)
+    const float scale = a.scales[row];
+    const float y_old = EPI && a.out_mode == QAM_OUT_ADD ? a.y[row] : 0.0f;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);   // the partial stores are complete before the arrival is counted
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -541,7 +548,7 @@ __device__ __forceinline__ void wave_body(const Item& a, const Common& c, int4* 
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (L == 0) __hip_atomic_store(&a.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    finish<XBF16, EPI>(a, b, L, sum, false, ssq);
+    finish<XBF16, EPI>(a, b, L, sum, false, ssq, scale, y_old);
 }
 
 // One (block, column chunk) unit of item a, `local` being its index within
